@@ -1,0 +1,30 @@
+"""Plain, slow, float64 CPU reference for one self-speculative decoding round.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library path imports, calls or links
+this package; only the tests, the package's smoke check and the bench's
+CPU-baseline leg use it. It shares no code with the HIP path: it re-implements
+paging from the page table, the intra-block masks, the softmax and the
+acceptance rule from the pages' definitions, in float64 NumPy.
+
+Modules:
+  prepare   -- block ids / positions / cache slots of one round's block
+  attention -- block-query attention over a paged KV cache, two forms:
+               a per-row loop and a dense masked-softmax matrix form
+  accept    -- speculative accept: p/q rejection test, longest accepted
+               prefix, residual (or bonus) sample, committed length; the greedy
+               special case; argmax with the lowest index winning
+
+Parity status: every function here is pinned by CPU tests against closed
+forms, library routines, brute force or exact enumeration (see the tests
+named test_oracle_*). None is "parity unpinned".
+"""
+from .prepare import prepare_block
+from .attention import (BIDIR, CAUSAL, MIXED, visible, block_attn_rows,
+                        block_attn_dense, attn_row, unpage_kv)
+from .accept import accept_request, accept_batch, greedy_accept_request, argmax_lowest
+
+__all__ = [
+    "prepare_block", "BIDIR", "CAUSAL", "MIXED", "visible", "block_attn_rows",
+    "block_attn_dense", "attn_row", "unpage_kv", "accept_request", "accept_batch",
+    "greedy_accept_request", "argmax_lowest",
+]

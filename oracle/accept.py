@@ -1,0 +1,133 @@
+"""Speculative accept / bonus epilogue (reference form, float64).
+
+What is computed:
+
+* "Unlocking Lossless Speedups in LLMs via Discrete Diffusion", prerequisite
+  "speculative decoding and rejection sampling" and the Psi-Spec Linear
+  sampler: a block of draft tokens is scored by the target in one pass; the
+  longest prefix that passes rejection sampling is kept and the rejected slot
+  is re-drawn from the residual distribution, which leaves the output
+  distribution equal to the target's.
+* "From DFlash to dLLM Self-Spec (4)", section 4.3 / 4.3.1 (I-DLM p/q verify):
+  q is the draft probability of the speculative token, p the anchor (causal
+  view) probability; a token is accepted with probability min(1, p/q), and a
+  reject emits a correction from the anchor side.
+* "From DFlash to dLLM Self-Spec (2)", section 2.2.5: the greedy rule (accept
+  while the draft equals the target's argmax at the previous position; bonus =
+  target argmax at the accept length; commit = accept + 1) and the outputs
+  accept_len, commit_len, bonus, out_tokens, new_seq_lens.
+* "From DFlash to dLLM Self-Spec (4)", section 4.4.1 (LinearSpec verify):
+  count matching positions, add one, crop the cache to length + accepted, and
+  carry the last emitted token into the next round.
+
+Readings where the pages are silent:
+* Row alignment: target row i (0-based, i = 0..K) scores block token i+1, so
+  test i uses p[i, d_i], q[i, d_i] with d_i = draft[i]; row K is the bonus row.
+* The test is u_i * q < p in float64 (exact for float32 inputs), which is
+  u_i < min(1, p/q) without a division; p = 0 is never accepted.
+* u[0..K-1] drive the tests, u[K] drives the one final draw.
+* Residual r = max(p_j - q_j, 0) (float64, one rounding per entry) after a
+  reject at j, else r = p_K; S = sum r; the token is the smallest t with
+  C_t > u_K * S (C = running sum in vocabulary order). If S <= 0 the draw
+  falls back to p_j and flags it; if rounding leaves no C_t above the
+  threshold the last index with r > 0 is taken.
+"""
+import numpy as np
+
+ERR_TOKEN = 4          # a draft token id is outside [0, V)
+ERR_ZERO_RESIDUAL = 8  # residual mass was zero; the draw used p_j instead
+TIE_EPS = 1e-6
+
+
+def argmax_lowest(x):
+    """Index of the maximum; the lowest index wins among equal maxima."""
+    x = np.asarray(x)
+    m = x.max()
+    return int(np.flatnonzero(x == m)[0])
+
+
+def _inverse_cdf(r, u):
+    """Smallest t with C_t > u * S, C the running sum of r. Returns
+    (t, S, thr, C) with a fallback to the last positive entry."""
+    C = np.cumsum(r)
+    S = C[-1]
+    thr = np.float64(u) * S
+    t = int(np.searchsorted(C, thr, side="right"))
+    if t >= len(r):
+        t = int(np.flatnonzero(r > 0)[-1])
+    return t, S, thr, C
+
+
+def accept_request(p, q, draft, u, seq_len):
+    """One request. p [K+1, V], q [K, V] float32 rows; draft [K]; u [K+1].
+
+    Returns a dict with accept_len, commit_len, bonus, out_tokens [K+1]
+    (accepted drafts, then the bonus, then -1), new_seq_len, err, and
+    tie (True when a decision lies within 1e-6 of its threshold)."""
+    K, V = q.shape
+    err = 0
+    tie = False
+    n_acc = 0
+    for i in range(K):
+        d = int(draft[i])
+        if d < 0 or d >= V:
+            err |= ERR_TOKEN
+            break
+        pd = np.float64(p[i, d])
+        qd = np.float64(q[i, d])
+        ui = np.float64(u[i])
+        if qd > 0 and abs(ui - min(1.0, pd / qd)) < TIE_EPS:
+            tie = True
+        if ui * qd < pd:
+            n_acc += 1
+        else:
+            break
+    j = n_acc
+    if j < K:
+        r = np.maximum(p[j].astype(np.float64) - q[j].astype(np.float64), 0.0)
+    else:
+        r = p[K].astype(np.float64)
+    if not r.sum() > 0:
+        err |= ERR_ZERO_RESIDUAL
+        r = p[j].astype(np.float64)
+    t, S, thr, C = _inverse_cdf(r, u[K])
+    lo = C[t - 1] if t > 0 else 0.0
+    if abs(thr - C[t]) < TIE_EPS * S or abs(thr - lo) < TIE_EPS * S:
+        tie = True
+    out = np.full(K + 1, -1, np.int64)
+    out[:n_acc] = draft[:n_acc]
+    out[n_acc] = t
+    return dict(accept_len=n_acc, commit_len=n_acc + 1, bonus=t, out_tokens=out,
+                new_seq_len=int(seq_len) + n_acc + 1, err=err, tie=tie)
+
+
+def greedy_accept_request(p, draft, seq_len):
+    """Greedy special case: accept while draft[i] == argmax p[i]; the bonus is
+    argmax p[accept_len]; commit = accept_len + 1."""
+    K = len(draft)
+    n_acc = 0
+    while n_acc < K and int(draft[n_acc]) == argmax_lowest(p[n_acc]):
+        n_acc += 1
+    bonus = argmax_lowest(p[n_acc])
+    out = np.full(K + 1, -1, np.int64)
+    out[:n_acc] = draft[:n_acc]
+    out[n_acc] = bonus
+    return dict(accept_len=n_acc, commit_len=n_acc + 1, bonus=bonus, out_tokens=out,
+                new_seq_len=int(seq_len) + n_acc + 1, err=0, tie=False)
+
+
+def accept_batch(p, q, draft, u, seq_lens, greedy=False, requests=None):
+    """Every request (or the listed ones) of a batch; returns stacked arrays
+    plus the per-request tie flags."""
+    bs, K = draft.shape
+    reqs = range(bs) if requests is None else requests
+    res = dict(accept_len=[], commit_len=[], bonus=[], out_tokens=[], new_seq_len=[],
+               err=[], tie=[])
+    for b in reqs:
+        if greedy:
+            r = greedy_accept_request(p[b], draft[b], seq_lens[b])
+        else:
+            r = accept_request(p[b], q[b], draft[b], u[b], seq_lens[b])
+        for key in res:
+            res[key].append(r[key])
+    return {k: np.array(v) for k, v in res.items()}

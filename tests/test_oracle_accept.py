@@ -1,0 +1,248 @@
+"""Pins for the float64 accept reference (CPU only).
+
+The central pin is exact: on a tiny vocabulary the reference is treated as a
+black box, every draft sequence is enumerated with its probability, and the
+uniforms are integrated exactly (the outputs are piecewise constant in each
+uniform, so the pieces are located by scanning and bisection). The resulting
+distribution must satisfy the losslessness the pages state for rejection
+sampling: the token emitted at a reached position is distributed as the target
+row, and the per-position acceptance probability is sum_v min(p, q)
+(Leviathan et al., Corollary 3.6, cited by the Uno summary).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from verify_attention_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _dist(rng, V, floor=0.05):
+    w = rng.random(V) + floor
+    return w / w.sum()
+
+
+def _rows(seed, K, V):
+    """Full-support p [K+1, V] and q [K, V] whose residual pieces are all
+    either empty or wider than 1/200 of their row's mass."""
+    rng = np.random.default_rng(seed)
+    while True:
+        p = np.stack([_dist(rng, V) for _ in range(K + 1)])
+        q = np.stack([_dist(rng, V) for _ in range(K)])
+        ok = True
+        for i in range(K):
+            r = np.maximum(p[i] - q[i], 0)
+            nz = r[r > 0]
+            if len(nz) == 0 or nz.min() / nz.sum() < 5e-3 or np.min(np.abs(p[i] - q[i])) < 1e-3:
+                ok = False
+        if ok:
+            return p, q
+
+
+def _scan_last_uniform(call, grid=1024):
+    """Pieces of [0, 1) on which call(u_last) is constant: (length, output)."""
+    us = (np.arange(grid) + 0.5) / grid
+    outs = [call(u) for u in us]
+    cuts = [0.0]
+    for a in range(grid - 1):
+        if outs[a] != outs[a + 1]:
+            lo, hi = us[a], us[a + 1]
+            for _ in range(60):
+                mid = 0.5 * (lo + hi)
+                if call(mid) == outs[a]:
+                    lo = mid
+                else:
+                    hi = mid
+            cuts.append(hi)
+    cuts.append(1.0)
+    vals = [outs[0]] + [outs[a + 1] for a in range(grid - 1) if outs[a] != outs[a + 1]]
+    return [(cuts[n + 1] - cuts[n], vals[n]) for n in range(len(vals))]
+
+
+def exact_distribution(p, q):
+    """{(accept_len, out_tokens...): probability} of the reference's output
+    when d_i ~ q_i independently and every uniform ~ U[0, 1)."""
+    K, V = q.shape
+    dist = {}
+    for d in np.ndindex(*([V] * K)):
+        d = np.array(d)
+        wd = np.prod([q[i, d[i]] for i in range(K)])
+        a = [min(1.0, p[i, d[i]] / q[i, d[i]]) for i in range(K)]
+        # the accept threshold sits exactly at min(1, p/q)
+        for i in range(K):
+            if a[i] < 1:
+                for u_i, want in ((a[i] * (1 - 1e-9), True), (a[i] * (1 + 1e-9), False)):
+                    u = np.zeros(K + 1)
+                    u[i] = u_i
+                    r = oracle.accept_request(p, q, d, u, 0)
+                    assert (r["accept_len"] > i) == want
+        for j in range(K + 1):
+            w = wd
+            u = np.zeros(K + 1)
+            for i in range(j):
+                w *= a[i]
+                u[i] = a[i] / 2
+            if j < K:
+                w *= 1 - a[j]
+                u[j] = (a[j] + 1) / 2
+            if w == 0:
+                continue
+
+            def call(ul, u=u):
+                uu = u.copy()
+                uu[K] = ul
+                r = oracle.accept_request(p, q, d, uu, 0)
+                return (r["accept_len"],) + tuple(r["out_tokens"])
+
+            for length, out in _scan_last_uniform(call):
+                assert out[0] == j
+                dist[out] = dist.get(out, 0.0) + w * length
+    return dist
+
+
+@pytest.mark.parametrize("K,V,seed", [(3, 3, 0), (2, 5, 1), (1, 7, 2)])
+def test_exact_losslessness_on_tiny_vocab(K, V, seed):
+    p, q = _rows(seed, K, V)
+    dist = exact_distribution(p, q)
+    assert abs(sum(dist.values()) - 1) < 1e-12
+    reach = np.zeros(K + 2)
+    emit = np.zeros((K + 1, V))
+    for out, w in dist.items():
+        n_acc, toks = out[0], out[1:]
+        for i in range(n_acc + 1):
+            reach[i] += w
+            emit[i, toks[i]] += w
+        # outputs are the accepted drafts, then one sampled token, then -1
+        assert all(t == -1 for t in toks[n_acc + 1:])
+    for i in range(K + 1):
+        # the token emitted at a reached position is distributed as p_i
+        assert np.max(np.abs(emit[i] - reach[i] * p[i])) < 1e-10
+        if i < K:
+            # acceptance probability at position i is sum_v min(p_i, q_i)
+            assert abs(reach[i + 1] - reach[i] * np.minimum(p[i], q[i]).sum()) < 1e-10
+
+
+def test_planted_residual_sign_error_breaks_losslessness(monkeypatch):
+    """Discrimination check: the same exact test fails when the reference's
+    residual is max(q - p, 0) instead of max(p - q, 0)."""
+    real_max = np.maximum
+
+    def swapped(a, b, *args, **kw):
+        if isinstance(a, np.ndarray) and a.ndim == 1 and np.isscalar(b) and b == 0.0:
+            return real_max(-a, b)
+        return real_max(a, b, *args, **kw)
+
+    p, q = _rows(3, 1, 4)
+    monkeypatch.setattr(oracle.accept.np, "maximum", swapped)
+    dist = exact_distribution(p, q)
+    monkeypatch.undo()
+    emit = np.zeros(4)
+    for out, w in dist.items():
+        emit[out[1]] += w
+    assert np.max(np.abs(emit - p[0])) > 1e-3
+
+
+def test_acceptance_rate_at_full_vocab_is_one_minus_tv():
+    """Statistical form of the same corollary at V = 151936: the mean of the
+    first test's accept indicator matches the mean of sum_v min(p, q)."""
+    cfg = synth.config(2, k_spec=1)
+    n = 300
+    x = synth.make_accept_inputs(cfg, seed=123, bs=n)
+    hits = 0
+    expect = 0.0
+    var = 0.0
+    for b in range(n):
+        r = oracle.accept_request(x.p[b], x.q[b], x.draft[b], x.u[b], 0)
+        hits += r["accept_len"] >= 1
+        a = np.minimum(x.p[b, 0].astype(np.float64), x.q[b, 0]).sum()
+        expect += a
+        var += a * (1 - a)
+    assert abs(hits - expect) < 4.5 * np.sqrt(var) + 1
+
+
+def test_one_hot_rows_reduce_to_greedy_rule():
+    rng = np.random.default_rng(5)
+    K, V = 6, 20
+    for trial in range(50):
+        tgt = rng.integers(0, V, K + 1)
+        draft = np.where(rng.random(K) < 0.7, tgt[:K], rng.integers(0, V, K))
+        p = np.zeros((K + 1, V), np.float32)
+        p[np.arange(K + 1), tgt] = 1
+        q = np.zeros((K, V), np.float32)
+        q[np.arange(K), draft] = 1
+        u = rng.random(K + 1).astype(np.float32)
+        s = oracle.accept_request(p, q, draft, u, 50)
+        g = oracle.greedy_accept_request(p, draft, 50)
+        for key in ("accept_len", "commit_len", "bonus", "new_seq_len"):
+            assert s[key] == g[key]
+        assert np.array_equal(s["out_tokens"], g["out_tokens"])
+
+
+def test_greedy_golden_dflash_example():
+    fx = json.load(open(os.path.join(GOLDEN, "greedy_accept_dflash.json")))
+    V = fx["vocab"]
+    for c in fx["cases"]:
+        tp = np.array(c["target_predict"])
+        p = np.zeros((len(tp), V), np.float32)
+        p[np.arange(len(tp)), tp] = 1
+        r = oracle.greedy_accept_request(p, np.array(c["drafts"]), c["seq_len"])
+        assert r["accept_len"] == c["accept_len"]
+        assert r["bonus"] == c["bonus"]
+        assert r["commit_len"] == c["commit_len"]
+        assert r["new_seq_len"] == c["new_seq_len"]
+        assert list(r["out_tokens"]) == c["out_tokens"]
+
+
+def test_linear_spec_golden_nemotron_loop():
+    fx = json.load(open(os.path.join(GOLDEN, "linear_spec_nemotron.json")))
+    V = fx["vocab"]
+    for c in fx["cases"]:
+        ar = np.array(c["ar_tokens"])
+        block = np.array(c["block"])
+        p = np.zeros((len(ar), V), np.float32)
+        p[np.arange(len(ar)), ar] = 1
+        r = oracle.greedy_accept_request(p, block[1:], c["cache_len"])
+        assert r["commit_len"] == c["accepted"]
+        assert r["new_seq_len"] == c["cropped_len"]
+        assert r["bonus"] == c["next_token"]
+        assert list(r["out_tokens"][:r["commit_len"]]) == c["accepted_toks"]
+
+
+def test_bounds_and_identity_draft():
+    cfg = synth.config(1)
+    x = synth.make_accept_inputs(cfg, seed=9, bs=40)
+    for b in range(40):
+        r = oracle.accept_request(x.p[b], x.q[b], x.draft[b], x.u[b], 17)
+        K = cfg.k_spec
+        assert 1 <= r["commit_len"] <= K + 1
+        assert r["new_seq_len"] == 17 + r["commit_len"]
+        n = r["accept_len"]
+        assert np.array_equal(r["out_tokens"][:n], x.draft[b, :n])
+        assert 0 <= r["bonus"] < cfg.vocab
+        # q == p accepts every draft (u < 1)
+        pp = x.p[b]
+        rr = oracle.accept_request(pp, pp[:K], x.draft[b], x.u[b], 0)
+        assert rr["accept_len"] == K
+
+
+def test_invalid_draft_token_is_rejected_and_flagged():
+    cfg = synth.config(1)
+    x = synth.make_accept_inputs(cfg, seed=10, bs=1)
+    d = x.draft[0].copy()
+    d[2] = cfg.vocab + 5
+    r = oracle.accept_request(x.p[0], x.q[0], d, np.zeros(cfg.k_spec + 1, np.float32), 0)
+    assert r["accept_len"] == 2 and r["err"] & oracle.accept.ERR_TOKEN
+
+
+def test_argmax_lowest_index_matches_numpy():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        x = rng.integers(-5, 5, size=rng.integers(1, 64)).astype(np.float32)
+        assert oracle.argmax_lowest(x) == int(np.argmax(x))
+    x = np.zeros(10)
+    x[[3, 7]] = 1
+    assert oracle.argmax_lowest(x) == 3

@@ -1,0 +1,220 @@
+"""Pins for the float64 attention reference (CPU only).
+
+Each test checks the reference against something other than itself: a
+library routine (torch's scaled_dot_product_attention, scipy's logsumexp),
+closed forms, the two independent forms against each other, or invariances
+that the pages' mask definition implies.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle
+from oracle import BIDIR, CAUSAL, MIXED
+from verify_attention_amd import synth
+
+MODES = [(BIDIR, 0), (CAUSAL, 0), (MIXED, 3), (MIXED, 0), (MIXED, 6)]
+
+
+def tiny(bs=2, hq=4, hkv=2, d=16, page=4, block=6, ctx=(3, 13), dtype="f32", seed=0):
+    cfg = synth.RoundConfig("tiny", bs=bs, hq=hq, hkv=hkv, d=d, page=page, block=block,
+                            modes=(BIDIR,), dtype=dtype, ctx_lo=ctx[0], ctx_hi=ctx[1])
+    return synth.make_attn_inputs(cfg, seed)
+
+
+def run_dense(x, mode, nc):
+    return oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                   x.page_table, x.seq_lens, mode, nc)
+
+
+def run_rows(x, mode, nc):
+    return oracle.block_attn_rows(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                  x.page_table, x.seq_lens, mode, nc)
+
+
+def gather_torch(x):
+    """Logical K/V [bs, Hkv, Lmax+B, D] by tensor indexing (independent of the
+    reference's per-token loop)."""
+    cfg = x.cfg
+    P = cfg.page
+    kp = torch.from_numpy(x.as_f64("k_pool"))
+    vp = torch.from_numpy(x.as_f64("v_pool")).transpose(2, 3)   # -> [pages, Hkv, P, D]
+    out_k, out_v = [], []
+    for b in range(cfg.bs):
+        n = int(x.seq_lens[b]) + cfg.block
+        pos = torch.arange(n)
+        pages = torch.from_numpy(x.page_table[b].astype(np.int64))[pos // P]
+        out_k.append(kp[pages, :, pos % P, :].transpose(0, 1))   # [Hkv, n, D]
+        out_v.append(vp[pages, :, pos % P, :].transpose(0, 1))
+    return out_k, out_v
+
+
+@pytest.mark.parametrize("mode,nc", MODES)
+def test_rows_and_dense_forms_agree(mode, nc):
+    x = tiny(seed=1)
+    o1, l1 = run_rows(x, mode, nc)
+    o2, l2 = run_dense(x, mode, nc)
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs(l1 - l2)) < 1e-12
+
+
+@pytest.mark.parametrize("mode,nc", MODES)
+def test_matches_torch_sdpa_with_explicit_mask(mode, nc):
+    """Library routine: torch SDPA in float64 on CPU, fed the mask the pages
+    draw (context columns all visible; rectangle / triangle / mixed block)."""
+    x = tiny(seed=2, block=5, ctx=(0, 9))
+    o, _ = run_dense(x, mode, nc)
+    ks, vs = gather_torch(x)
+    cfg = x.cfg
+    g = cfg.hq // cfg.hkv
+    q = torch.from_numpy(x.as_f64("q"))
+    for b in range(cfg.bs):
+        L = int(x.seq_lens[b])
+        B = cfg.block
+        allow = torch.ones(B, L + B, dtype=torch.bool)
+        for i in range(B):
+            for jb in range(B):
+                if mode == CAUSAL:
+                    allow[i, L + jb] = jb <= i
+                elif mode == MIXED:
+                    allow[i, L + jb] = (i >= nc) or (jb <= i)
+        qb = q[b].transpose(0, 1)                        # [Hq, B, D]
+        kb = ks[b].repeat_interleave(g, dim=0)           # [Hq, n, D]
+        vb = vs[b].repeat_interleave(g, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=allow)
+        got = torch.from_numpy(o[b]).transpose(0, 1)
+        assert torch.max(torch.abs(ref - got)).item() < 1e-12
+
+
+def test_lse_matches_scipy_logsumexp():
+    x = tiny(seed=3)
+    _, lse = run_rows(x, CAUSAL, 0)
+    ks, _ = gather_torch(x)
+    cfg = x.cfg
+    g = cfg.hq // cfg.hkv
+    q = x.as_f64("q")
+    for b in range(cfg.bs):
+        L = int(x.seq_lens[b])
+        for h in range(cfg.hq):
+            K = ks[b][h // g].numpy()
+            for i in range(cfg.block):
+                s = K[:L + i + 1] @ q[b, i, h] / np.sqrt(cfg.d)
+                assert abs(logsumexp(s) - lse[b, i, h]) < 1e-12
+
+
+@pytest.mark.parametrize("mode,nc", MODES)
+def test_zero_query_gives_mean_of_visible_values(mode, nc):
+    """Q = 0: every visible key scores 0, so each output row is the plain mean
+    of the V rows it may see -- a different set per mode and row."""
+    x = tiny(seed=4)
+    x.q[...] = 0
+    o, lse = run_dense(x, mode, nc)
+    _, vs = gather_torch(x)
+    cfg = x.cfg
+    g = cfg.hq // cfg.hkv
+    B = cfg.block
+    for b in range(cfg.bs):
+        L = int(x.seq_lens[b])
+        for h in range(cfg.hq):
+            V = vs[b][h // g].numpy()
+            for i in range(B):
+                if mode == BIDIR or (mode == MIXED and i >= nc):
+                    n_vis = L + B
+                else:
+                    n_vis = L + i + 1
+                want = V[:n_vis].mean(axis=0)
+                assert np.max(np.abs(o[b, i, h] - want)) < 1e-13
+                assert abs(lse[b, i, h] - np.log(n_vis)) < 1e-13
+
+
+def test_single_token_no_context_returns_its_value():
+    x = tiny(seed=5, block=1, ctx=(0, 0))
+    for mode in (BIDIR, CAUSAL, MIXED):
+        o, lse = run_rows(x, mode, 0)
+        _, vs = gather_torch(x)
+        g = x.cfg.hq // x.cfg.hkv
+        for b in range(x.cfg.bs):
+            for h in range(x.cfg.hq):
+                assert np.array_equal(o[b, 0, h], vs[b][h // g][0].numpy())
+
+
+def test_rank_one_keys_give_uniform_weights():
+    """All keys equal: scores are equal, weights uniform, O = mean of V."""
+    x = tiny(seed=6)
+    x.k_pool[...] = x.k_pool[0, 0, 0, :]
+    o, _ = run_dense(x, BIDIR, 0)
+    _, vs = gather_torch(x)
+    g = x.cfg.hq // x.cfg.hkv
+    for b in range(x.cfg.bs):
+        for h in range(x.cfg.hq):
+            want = vs[b][h // g].numpy().mean(axis=0)
+            assert np.max(np.abs(o[b, :, h] - want)) < 1e-12
+
+
+def test_mode_special_cases():
+    x = tiny(seed=7, block=6)
+    B = x.cfg.block
+    ob, _ = run_dense(x, BIDIR, 0)
+    oc, _ = run_dense(x, CAUSAL, 0)
+    # the last block row sees the whole block under both masks
+    assert np.array_equal(ob[:, B - 1], oc[:, B - 1])
+    # every other row differs between the rectangle and the triangle
+    assert np.min(np.abs(ob[:, :B - 1] - oc[:, :B - 1]).max(axis=-1)) > 0
+    # MIXED with every position clean is CAUSAL; with none clean it is BIDIR
+    om_all, _ = run_dense(x, MIXED, B)
+    om_none, _ = run_dense(x, MIXED, 0)
+    assert np.array_equal(om_all, oc)
+    assert np.array_equal(om_none, ob)
+    # MIXED with 3 clean rows: clean rows follow CAUSAL, MASK rows follow BIDIR
+    om3, _ = run_dense(x, MIXED, 3)
+    assert np.array_equal(om3[:, :3], oc[:, :3])
+    assert np.array_equal(om3[:, 3:], ob[:, 3:])
+    # a single-token block is ordinary decode under every mask
+    y = tiny(seed=8, block=1)
+    outs = [run_dense(y, m, 0)[0] for m in (BIDIR, CAUSAL, MIXED)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_page_permutation_changes_nothing():
+    """The same logical KV placed in two different physical page orders."""
+    cfg = synth.RoundConfig("perm", bs=3, hq=4, hkv=2, d=8, page=4, block=5,
+                            modes=(CAUSAL,), dtype="f32", ctx_lo=2, ctx_hi=17)
+    a = synth.make_attn_inputs(cfg, 11, shuffle=False)
+    b = synth.make_attn_inputs(cfg, 11, shuffle=True)
+    # move a's pages to b's physical ids
+    for r in range(cfg.bs):
+        for n in range(a.page_table.shape[1]):
+            pa, pb = a.page_table[r, n], b.page_table[r, n]
+            if pa >= 0:
+                b.k_pool[pb] = a.k_pool[pa]
+                b.v_pool[pb] = a.v_pool[pa]
+    oa, la = run_rows(a, CAUSAL, 0)
+    ob, lb = run_rows(b, CAUSAL, 0)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_rows_subset_matches_full():
+    x = tiny(seed=9)
+    full, fl = run_rows(x, CAUSAL, 0)
+    rows = [(1, 2, 3), (0, 5, 0)]
+    part, pl = oracle.block_attn_rows(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                      x.page_table, x.seq_lens, CAUSAL, 0, rows=rows)
+    for b, i, h in rows:
+        assert np.array_equal(part[b, i, h], full[b, i, h])
+        assert pl[b, i, h] == fl[b, i, h]
+
+
+def test_planted_mask_mistake_is_caught(monkeypatch):
+    """Discrimination check: a triangle that drops its diagonal (jb < i) in the
+    reference must fail the zero-query closed form."""
+    x = tiny(seed=10)
+    x.q[...] = 0
+    monkeypatch.setattr(oracle.attention, "visible",
+                        lambda mode, i, jb, nc: jb < i if mode == CAUSAL else True)
+    o, _ = oracle.block_attn_rows(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                  x.page_table, x.seq_lens, CAUSAL, 0, rows=[(0, 2, 0)])
+    _, vs = gather_torch(x)
+    L = int(x.seq_lens[0])
+    want = vs[0][0].numpy()[:L + 3].mean(axis=0)
+    assert np.max(np.abs(o[0, 2, 0] - want)) > 1e-6

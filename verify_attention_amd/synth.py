@@ -1,0 +1,288 @@
+"""Seeded synthetic inputs for one self-speculative decoding round.
+
+This module only draws random numbers and lays them out in the library's
+buffer formats. It holds none of the method's arithmetic (no masking, no
+attention, no acceptance test, no residual sampling): the tests, the bench and
+the CPU reference all take their inputs from here, and nothing here imports
+either side.
+
+Workload shapes follow the five round configurations of the DFlash / I-DLM /
+block-diffusion pages (SGLang Spec V2 verify block, I-DLM Block-N mixed layout,
+LLaDA-style draft block). Where a page leaves a distribution open the choice is
+stated next to the field.
+
+Buffer formats (the library's contract):
+  q        [bs, B, Hq, D]              query rows of the block (bf16 or fp32)
+  k_pool   [num_pages, Hkv, P, D]      K pages, token-major inside a page
+  v_pool   [num_pages, Hkv, D, P]      V pages, dim-major inside a page
+  page_table [bs, max_pages] int32     physical page of logical page n; -1 unused
+  seq_lens [bs] int32                  committed context length L_b; the block
+                                       occupies positions L_b .. L_b+B-1 and its
+                                       K/V are already in the pages
+  p [bs, K+1, V] f32, q_probs [bs, K, V] f32, draft [bs, K] i32, u [bs, K+1] f32
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+BIDIR, CAUSAL, MIXED = 0, 1, 2
+MODE_NAMES = {BIDIR: "BIDIR", CAUSAL: "CAUSAL", MIXED: "MIXED"}
+
+
+@dataclasses.dataclass(frozen=True)
+class RoundConfig:
+    """One round's shapes. `ctx_lo/ctx_hi` give the committed-context range;
+    `commit_hi` > 0 adds the previous round's commit length ~ U{1..commit_hi}."""
+    name: str
+    bs: int
+    hq: int
+    hkv: int
+    d: int
+    page: int
+    block: int
+    modes: tuple
+    dtype: str                 # "bf16" | "f32"
+    ctx_lo: int
+    ctx_hi: int
+    commit_hi: int = 0
+    n_causal: int = 0          # MIXED: clean (causal) positions at the block head
+    vocab: int = 0             # 0: no accept step in this round
+    k_spec: int = 0            # draft tokens checked by the accept step
+    logit_sigma: float = 3.0
+    q_noise_sigma: float = 0.0  # >0: q-logits = p-logits + N(0, s^2); 0: independent
+    argmax_vocab: int = 0      # draft pass: argmax of bf16 logits over this vocab
+
+
+# The five round configurations. Sizes are the workloads the pages describe:
+#  1 tiny fp32 correctness round (both intra-block masks, vocab 512)
+#  2 Qwen3-8B-shaped verify at concurrency 32 (page size 16, block 16)
+#  3 block-diffusion draft pass, ragged contexts, block 32, greedy draft ids
+#  4 high-concurrency ragged verify (batch 256)
+#  5 I-DLM style mixed layout: 8 clean causal + 8 MASK bidirectional positions
+CONFIGS = {
+    1: RoundConfig("tiny_f32", bs=1, hq=2, hkv=1, d=64, page=16, block=8,
+                   modes=(BIDIR, CAUSAL), dtype="f32", ctx_lo=256, ctx_hi=256,
+                   vocab=512, k_spec=7, logit_sigma=2.0, q_noise_sigma=0.0),
+    2: RoundConfig("qwen3_8b_verify_bs32", bs=32, hq=32, hkv=8, d=128, page=16,
+                   block=16, modes=(CAUSAL,), dtype="bf16", ctx_lo=1024,
+                   ctx_hi=1024, vocab=151936, k_spec=15, logit_sigma=3.0,
+                   q_noise_sigma=0.5),
+    3: RoundConfig("draft_bidir_bs64", bs=64, hq=16, hkv=4, d=128, page=32,
+                   block=32, modes=(BIDIR,), dtype="bf16", ctx_lo=1024,
+                   ctx_hi=9216, argmax_vocab=157184, logit_sigma=3.0),
+    4: RoundConfig("ragged_verify_bs256", bs=256, hq=32, hkv=8, d=128, page=16,
+                   block=16, modes=(CAUSAL,), dtype="bf16", ctx_lo=1024,
+                   ctx_hi=9216, commit_hi=16, vocab=151936, k_spec=15,
+                   logit_sigma=3.0, q_noise_sigma=0.5),
+    5: RoundConfig("idlm_mixed_bs128", bs=128, hq=32, hkv=8, d=128, page=16,
+                   block=16, modes=(MIXED,), dtype="bf16", ctx_lo=4096,
+                   ctx_hi=4096, n_causal=8, vocab=151936, k_spec=8,
+                   logit_sigma=3.0, q_noise_sigma=0.5),
+}
+
+
+def config(cid: int, **overrides) -> RoundConfig:
+    """A round configuration, optionally with fields replaced (smaller test
+    variants keep the shape family but shrink bs, vocab or contexts)."""
+    return dataclasses.replace(CONFIGS[cid], **overrides)
+
+
+# Independent child streams, one per drawn item, so that resizing one item
+# never shifts the numbers of another.
+_STREAMS = dict(pages=1, ctx=2, commit=3, q=4, k=5, v=6, plogit=7, qnoise=8,
+                draft=9, uniform=10, argmax=11, ncausal=12, poison=13)
+
+
+def rng_for(seed: int, item: str) -> np.random.Generator:
+    return np.random.default_rng([int(seed), _STREAMS[item]])
+
+
+# ---------------------------------------------------------------- bf16 values
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest even) and return the
+    16-bit patterns as uint16."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 values of bf16 bit patterns."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_bf16(rng, shape, sigma=1.0, chunk=1 << 26):
+    """N(0, sigma^2) drawn in float32 and rounded once to bf16 -> uint16 bits."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = rng.standard_normal(e - s, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out[s:e] = bf16_bits(x)
+    return out.reshape(shape)
+
+
+def _normal_f32(rng, shape, sigma=1.0):
+    x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
+
+
+# ------------------------------------------------------------ attention round
+@dataclasses.dataclass
+class AttnInputs:
+    cfg: RoundConfig
+    seq_lens: np.ndarray       # [bs] int32
+    page_table: np.ndarray     # [bs, max_pages] int32
+    num_pages: int
+    q: np.ndarray              # [bs, B, Hq, D] uint16 (bf16 bits) or float32
+    k_pool: np.ndarray         # [num_pages, Hkv, P, D]
+    v_pool: np.ndarray         # [num_pages, Hkv, D, P]
+    n_causal: np.ndarray       # [bs] int32 (MIXED clean-prefix lengths)
+
+    @property
+    def max_pages(self):
+        return self.page_table.shape[1]
+
+    def as_f64(self, name):
+        """Exact float64 values of a stored tensor."""
+        a = getattr(self, name)
+        if a.dtype == np.uint16:
+            return bf16_to_f32(a).astype(np.float64)
+        return a.astype(np.float64)
+
+
+def context_lengths(cfg: RoundConfig, seed: int) -> np.ndarray:
+    """Committed lengths L_b: context ~ U{ctx_lo..ctx_hi}, plus the previous
+    round's commit ~ U{1..commit_hi} when the workload has one."""
+    ctx = rng_for(seed, "ctx").integers(cfg.ctx_lo, cfg.ctx_hi + 1, size=cfg.bs)
+    if cfg.commit_hi:
+        ctx = ctx + rng_for(seed, "commit").integers(1, cfg.commit_hi + 1, size=cfg.bs)
+    return ctx.astype(np.int32)
+
+
+def page_layout(cfg: RoundConfig, seq_lens: np.ndarray, seed: int, shuffle=True,
+                spare_pages: int = 0):
+    """Each request owns ceil((L_b + 2B) / P) pages (the over-allocation rule
+    of the Spec V2 page: reserved = committed + 2 * block). Physical page ids
+    come from a random permutation of the pool; unused table entries are -1."""
+    P, B = cfg.page, cfg.block
+    need = (seq_lens.astype(np.int64) + 2 * B + P - 1) // P
+    total = int(need.sum()) + spare_pages
+    max_pages = int(need.max())
+    ids = np.arange(total, dtype=np.int32)
+    if shuffle:
+        ids = rng_for(seed, "pages").permutation(total).astype(np.int32)
+    table = np.full((cfg.bs, max_pages), -1, dtype=np.int32)
+    o = 0
+    for b in range(cfg.bs):
+        n = int(need[b])
+        table[b, :n] = ids[o:o + n]
+        o += n
+    return table, total
+
+
+def make_attn_inputs(cfg: RoundConfig, seed: int, shuffle=True,
+                     n_causal_per_req=False, poison_tail=False) -> AttnInputs:
+    """Q/K/V ~ N(0,1) (bf16: drawn in float32, rounded once). Every pool slot
+    holds a value, including slots past a request's end. With `poison_tail`,
+    slots at positions >= L_b + B are overwritten with NaN so that any read
+    of them shows up in the output."""
+    seq = context_lengths(cfg, seed)
+    table, num_pages = page_layout(cfg, seq, seed, shuffle=shuffle)
+    shp_q = (cfg.bs, cfg.block, cfg.hq, cfg.d)
+    shp_k = (num_pages, cfg.hkv, cfg.page, cfg.d)
+    shp_v = (num_pages, cfg.hkv, cfg.d, cfg.page)
+    if cfg.dtype == "bf16":
+        q = _normal_bf16(rng_for(seed, "q"), shp_q)
+        k = _normal_bf16(rng_for(seed, "k"), shp_k)
+        v = _normal_bf16(rng_for(seed, "v"), shp_v)
+        nan = np.uint16(0x7FC0)
+    else:
+        q = _normal_f32(rng_for(seed, "q"), shp_q)
+        k = _normal_f32(rng_for(seed, "k"), shp_k)
+        v = _normal_f32(rng_for(seed, "v"), shp_v)
+        nan = np.float32(np.nan)
+    if poison_tail:
+        P = cfg.page
+        for b in range(cfg.bs):
+            end = int(seq[b]) + cfg.block
+            for n in range(table.shape[1]):
+                pg = table[b, n]
+                if pg < 0:
+                    continue
+                lo = max(end - n * P, 0)
+                if lo < P:
+                    k[pg, :, lo:, :] = nan
+                    v[pg, :, :, lo:] = nan
+    if n_causal_per_req:
+        nc = rng_for(seed, "ncausal").integers(0, cfg.block + 1, size=cfg.bs)
+    else:
+        nc = np.full(cfg.bs, cfg.n_causal, dtype=np.int64)
+    return AttnInputs(cfg, seq, table, num_pages, q, k, v, nc.astype(np.int32))
+
+
+# --------------------------------------------------------------- accept step
+@dataclasses.dataclass
+class AcceptInputs:
+    p: np.ndarray       # [bs, K+1, V] float32 target rows (row i scores block token i+1)
+    q: np.ndarray       # [bs, K, V]   float32 draft rows
+    draft: np.ndarray   # [bs, K] int32 draft tokens, d_i ~ q_i
+    u: np.ndarray       # [bs, K+1] float32 uniforms in [0, 1)
+
+
+def _softmax_rows64(x):
+    x = x.astype(np.float64)
+    x -= x.max(axis=-1, keepdims=True)
+    np.exp(x, out=x)
+    x /= x.sum(axis=-1, keepdims=True)
+    return x
+
+
+def make_accept_inputs(cfg: RoundConfig, seed: int, bs: int | None = None) -> AcceptInputs:
+    """p = softmax(l), l ~ N(0, sigma^2) per row. q = softmax(l + N(0, s^2))
+    when the workload ties the draft to the target (the verify configs), or
+    softmax of independent logits (the tiny config). Distributions are built in
+    float64 one request at a time and stored as float32. Draft tokens are drawn
+    from the stored q rows with numpy's categorical sampler; the accept step's
+    own uniforms come from a separate stream."""
+    bs = cfg.bs if bs is None else bs
+    K, V = cfg.k_spec, cfg.vocab
+    p = np.empty((bs, K + 1, V), np.float32)
+    q = np.empty((bs, K, V), np.float32)
+    draft = np.empty((bs, K), np.int32)
+    rp, rq, rd = rng_for(seed, "plogit"), rng_for(seed, "qnoise"), rng_for(seed, "draft")
+    for b in range(bs):
+        lp = rp.standard_normal((K + 1, V)) * cfg.logit_sigma
+        p[b] = _softmax_rows64(lp)
+        if cfg.q_noise_sigma > 0:
+            lq = lp[:K] + rq.standard_normal((K, V)) * cfg.q_noise_sigma
+        else:
+            lq = rq.standard_normal((K, V)) * cfg.logit_sigma
+        q[b] = _softmax_rows64(lq)
+        for i in range(K):
+            w = q[b, i].astype(np.float64)
+            draft[b, i] = rd.choice(V, p=w / w.sum())
+    u = rng_for(seed, "uniform").random((bs, K + 1), dtype=np.float32)
+    return AcceptInputs(p, q, draft, u)
+
+
+def make_argmax_logits(cfg: RoundConfig, seed: int, rows: int | None = None) -> np.ndarray:
+    """Draft-pass logits [bs * (B-1), V] as bf16 bits, N(0, sigma^2) rounded to
+    bf16 (equal maxima occur; the lowest index is the defined winner)."""
+    rows = cfg.bs * (cfg.block - 1) if rows is None else rows
+    return _normal_bf16(rng_for(seed, "argmax"), (rows, cfg.argmax_vocab), cfg.logit_sigma)
+
+
+def make_round_state(cfg: RoundConfig, seed: int, vocab: int | None = None):
+    """verified_id [bs] (previous round's bonus token) and the verify pass's
+    draft tokens [bs, B-1], uniform over the vocabulary."""
+    vocab = vocab or cfg.vocab or cfg.argmax_vocab or 32000
+    r = rng_for(seed, "draft")
+    verified = r.integers(0, vocab, size=cfg.bs).astype(np.int32)
+    drafts = r.integers(0, vocab, size=(cfg.bs, cfg.block - 1)).astype(np.int32)
+    return verified, drafts
