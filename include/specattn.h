@@ -1,0 +1,220 @@
+/*
+ * specattn.h -- C ABI of the block draft/verify attention + speculative accept
+ * library for MI355X (gfx950).
+ *
+ * One decode round of block-diffusion self-speculative decoding runs, on one
+ * HIP stream and without any host/device synchronisation:
+ *
+ *   spec_prepare_block  (draft pass)  -> block ids / positions / KV slots
+ *   [caller writes the block's K/V at the slots]
+ *   block_attn(SPEC_BIDIR)            -> draft-pass attention
+ *   spec_draft_argmax                 -> greedy draft tokens
+ *   spec_prepare_block  (verify pass, with the draft tokens)
+ *   block_attn(SPEC_CAUSAL | SPEC_MIXED)
+ *   [caller produces target rows p]
+ *   spec_accept                       -> accepted prefix, bonus, new lengths
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array argument is a DEVICE pointer to memory owned by the caller
+ *   (the library never keeps a pointer past the call). Arrays are dense and
+ *   row-major with the shapes given below.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *   only enqueue work on it: no allocation, no free, no host<->device copy, no
+ *   synchronisation. Outputs are valid once the stream reaches that point.
+ * - Return value: SPEC_OK when the work was queued; a negative status when a
+ *   host-detectable argument error was found, in which case nothing was
+ *   launched and no output was touched.
+ * - `err_flags` (nullable, one int32 on the device): data errors found by the
+ *   kernels are OR-ed into it (SPEC_ERR_* bits). The caller clears it and
+ *   reads it whenever convenient; the library never reads it back.
+ * - Token ids, positions, lengths and slots are int32.
+ *
+ * KV cache format (the pages leave it open; chosen for 16-byte MFMA operand
+ * loads on both contractions):
+ *   k_pool [num_pages][Hkv][P][D]   K rows token-major inside a page
+ *   v_pool [num_pages][Hkv][D][P]   V columns dim-major inside a page
+ *   page_table [bs][max_pages]      physical page of logical page n of request b
+ *   The token at logical position n of request b lives in physical page
+ *   page_table[b][n / P] at offset n % P; its slot id is page * P + n % P.
+ */
+#ifndef SPECATTN_H
+#define SPECATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SPEC_OK 0
+#define SPEC_EINVAL (-1)  /* null pointer, bad shape or count              */
+#define SPEC_ENOTSUP (-2) /* dtype, head_dim or page size not supported    */
+#define SPEC_ENOSPC (-3)  /* workspace smaller than the *_workspace_bytes  */
+#define SPEC_EHIP (-4)    /* the HIP runtime refused the launch            */
+
+/* err_flags bits, set by kernels */
+#define SPEC_ERR_SLOT 1           /* a page-table entry the call needed is outside [0, num_pages) */
+#define SPEC_ERR_CAPACITY 2       /* seq_len < 0 or seq_len + B > max_pages * P                 */
+#define SPEC_ERR_TOKEN 4          /* a draft token id is outside [0, V)                          */
+#define SPEC_ERR_ZERO_RESIDUAL 8  /* residual mass was zero; the draw used the target row        */
+
+typedef enum { SPEC_BIDIR = 0, SPEC_CAUSAL = 1, SPEC_MIXED = 2 } spec_mode;
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int spec_version(void);
+
+/* Text for a status code. Static string, never NULL. */
+const char* spec_status_string(int status);
+
+/*
+ * spec_prepare_block -- the block of one round, for every request.
+ *
+ * Follows "From DFlash to dLLM Self-Spec (2): SGLang Spec V2", section 2.2.2
+ * (block token 0 = the previous round's verified id, tokens 1..B-1 = the mask
+ * token; positions and KV locations built in the same step) and section 2.2.4
+ * (the verify pass feeds the draft tokens instead of the mask token). Slots
+ * follow the request -> token map of section 2.3.5, whose over-allocation
+ * rule (committed + 2 * block reserved) is what makes seq_len + B fit.
+ *
+ *   bs, B           requests and block length (B >= 1)
+ *   page_size       P, tokens per page (> 0)
+ *   max_pages       columns of page_table
+ *   num_pages       pages in the pool (page ids must be < num_pages)
+ *   mask_token_id   id written at block positions 1..B-1 on the draft pass
+ *   verified_id     [bs]      token 0 of each block
+ *   seq_lens        [bs]      committed length L_b (the block starts there)
+ *   page_table      [bs, max_pages]
+ *   draft_tokens    [bs, B-1] verify pass tokens, or NULL for the draft pass
+ * Outputs:
+ *   block_ids [bs, B], positions [bs, B] (= L_b + i),
+ *   cache_loc [bs, B] (= page_table[b][pos / P] * P + pos % P, or -1 with
+ *   SPEC_ERR_SLOT / SPEC_ERR_CAPACITY set when it cannot be formed).
+ * Errors: SPEC_EINVAL for bs <= 0, B <= 0, P <= 0, max_pages <= 0,
+ *   num_pages <= 0 or a NULL required pointer.
+ */
+int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_pages,
+                       int32_t mask_token_id, const int32_t* verified_id,
+                       const int32_t* seq_lens, const int32_t* page_table,
+                       const int32_t* draft_tokens, int32_t* block_ids, int32_t* positions,
+                       int32_t* cache_loc, int32_t* err_flags, void* stream);
+
+/*
+ * block_attn -- block-query attention over the paged KV cache.
+ *
+ * Follows "SGLang strengthens diffusion LLMs: LLaDA 2.0", section "Attention
+ * Mask": the block's queries attend to the whole cached context (as chunked
+ * prefill) and to the block's own K/V with a rectangular mask (block
+ * diffusion, SPEC_BIDIR) or a triangular one (AR chunked prefill,
+ * SPEC_CAUSAL); "From DFlash to dLLM Self-Spec (4)", sections 4.4-4.4.1
+ * (bidirectional draft pass, causal verify pass of one model) and 4.3.1
+ * (I-DLM layout: clean positions, then MASK positions) for SPEC_MIXED: block
+ * rows i < n_c are causal, rows i >= n_c see the context and the whole block.
+ *
+ * For request b with L = seq_lens[b], block row i (query token at position
+ * L + i) and query head h (KV head h / (Hq / Hkv)):
+ *   o[b,i,h,:] = sum_j softmax_j(s_j) v_j over visible keys j in [0, L + B),
+ *   s_j = sm_scale * <q[b,i,h,:], k_j>; key j < L is always visible; block key
+ *   j = L + j' is visible iff BIDIR, or j' <= i (CAUSAL), or i >= n_c or
+ *   j' <= i (MIXED). lse[b,i,h] = natural log of sum_j exp(s_j).
+ * The block's own K/V must already be in the cache at positions L..L+B-1.
+ *
+ *   mode              SPEC_BIDIR / SPEC_CAUSAL / SPEC_MIXED
+ *   n_causal          MIXED: clean rows per request (0..B) when
+ *   n_causal_per_req  is NULL, else per-request counts [bs] (device)
+ *   dtype             SPEC_BF16 (q, pools, o in bf16) or SPEC_F32
+ *   bs, B, Hq, Hkv    Hq % Hkv == 0; g = Hq / Hkv; g * B <= 128
+ *   D                 head dim: 64 or 128
+ *   page_size         16 or 32
+ *   max_pages, num_pages   page-table columns, pages in the pool
+ *   max_kv_len        host upper bound of L_b + B over the batch; sizes the
+ *                     split-KV plan only (a request longer than it is still
+ *                     computed correctly, more slowly)
+ *   q [bs, B, Hq, D]; k_pool, v_pool as in the file header; page_table;
+ *   seq_lens [bs]; sm_scale (0 -> 1/sqrt(D))
+ * Outputs: o [bs, B, Hq, D] (dtype), lse [bs, B, Hq] float (nullable).
+ * Workspace: at least block_attn_workspace_bytes(...) bytes of device memory,
+ *   16-byte aligned, ZERO-FILLED before its first use; every completed call
+ *   leaves it ready for the next one. Calls that share a workspace must not
+ *   overlap in time.
+ * Errors: SPEC_EINVAL (bad counts, Hq % Hkv != 0, g * B > 128, mode, n_causal
+ *   outside [0, B], NULL pointers), SPEC_ENOTSUP (D, P, dtype), SPEC_ENOSPC.
+ *   Kernels set SPEC_ERR_SLOT for a page id outside [0, num_pages) (that page
+ *   is read as zeros) and SPEC_ERR_CAPACITY for L_b < 0 or L_b + B >
+ *   max_pages * P (the request is clamped to the table).
+ */
+size_t block_attn_workspace_bytes(int bs, int B, int Hq, int Hkv, int D, int max_kv_len);
+
+int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req, int dtype, int bs,
+               int B, int Hq, int Hkv, int D, int page_size, int max_pages, int num_pages,
+               int max_kv_len, const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* page_table, const int32_t* seq_lens, float sm_scale, void* o,
+               float* lse, void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream);
+
+/*
+ * spec_draft_argmax -- greedy draft tokens from the draft pass's logits.
+ *
+ * Follows "From DFlash to dLLM Self-Spec (2)", section 2.2.3: the draft
+ * tokens are the greedy choice of the target lm_head over the draft hidden
+ * states at block positions 1..B-1 (the vocab projection itself is outside
+ * this library). tokens[r] = smallest index among the maxima of logits[r, :].
+ *
+ *   rows, V   logits is [rows, V] (for a draft pass, rows = bs * (B - 1))
+ *   dtype     SPEC_BF16 or SPEC_F32
+ * Output: tokens [rows]. Rows holding NaN give an unspecified id in [0, V).
+ * Errors: SPEC_EINVAL (rows <= 0, V <= 0, NULL), SPEC_ENOTSUP (dtype).
+ */
+int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* tokens,
+                      void* stream);
+
+/*
+ * spec_accept -- speculative accept / bonus epilogue.
+ *
+ * Follows "Unlocking Lossless Speedups in LLMs via Discrete Diffusion"
+ * (prerequisite on speculative decoding and rejection sampling; the Psi-Spec
+ * linear sampler keeps the longest accepted prefix and re-draws the rejected
+ * slot from the residual, leaving the target distribution unchanged), "From
+ * DFlash to dLLM Self-Spec (4)", section 4.3.1 (accept with probability
+ * min(1, p/q); a reject emits a correction from the anchor side), and "From
+ * DFlash to dLLM Self-Spec (2)", section 2.2.5 (outputs accept_len,
+ * commit_len = accept_len + 1, bonus, out_tokens, new_seq_lens; the greedy rule).
+ *
+ * Per request b with K draft tokens d_0..d_{K-1} (block tokens 1..K):
+ *   target row i of p scores block token i + 1; row K is the bonus row.
+ *   test i: accept iff u[b,i] * q[b,i,d_i] < p[b,i,d_i] (exact, in double);
+ *   accept_len = number of leading accepted tests (a token id outside [0, V)
+ *   ends the prefix and sets SPEC_ERR_TOKEN);
+ *   j = accept_len; r = max(p[b,j,:] - q[b,j,:], 0) if j < K else p[b,K,:]
+ *   (double); bonus = smallest t with sum_{v<=t} r_v > u[b,K] * sum_v r_v;
+ *   if sum r is zero the draw uses p[b,j,:] and sets SPEC_ERR_ZERO_RESIDUAL.
+ *   commit_len = accept_len + 1; new_seq_lens = seq_lens + commit_len;
+ *   out_tokens[b] = d_0..d_{j-1}, bonus, then -1 up to K + 1 entries.
+ * greedy != 0: test i is d_i == argmax p[b,i,:] and bonus = argmax p[b,j,:]
+ *   (lowest index on ties; p may hold logits); q and u are not read.
+ *
+ *   bs, K, V      requests, draft tokens per request (1..63), vocabulary
+ *   p [bs, K+1, V] float, q [bs, K, V] float, draft [bs, K], u [bs, K+1] float
+ *   in [0, 1), seq_lens [bs]
+ * Outputs: accept_len, commit_len, bonus, new_seq_lens [bs]; out_tokens [bs, K+1].
+ * Workspace: spec_accept_workspace_bytes(bs, K, V, greedy) bytes of device
+ *   memory, 16-byte aligned, ZERO-FILLED before its first use; every
+ *   completed call leaves it ready for the next one. Calls that share a
+ *   workspace must not overlap in time.
+ * Errors: SPEC_EINVAL (bs <= 0, K outside 1..63, V <= 0, NULL), SPEC_ENOSPC.
+ */
+size_t spec_accept_workspace_bytes(int bs, int K, int V, int greedy);
+
+int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q,
+                const int32_t* draft, const float* u, const int32_t* seq_lens,
+                int32_t* accept_len, int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
+                int32_t* new_seq_lens, void* workspace, size_t ws_bytes, int32_t* err_flags,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECATTN_H */

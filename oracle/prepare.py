@@ -34,7 +34,7 @@ def prepare_block(verified_id, seq_lens, page_table, page_size, block, mask_toke
     err = 0
     for b in range(bs):
         L = int(seq_lens[b])
-        if L + block > max_pages * page_size:
+        if L < 0 or L + block > max_pages * page_size:
             err |= ERR_CAPACITY
         for i in range(block):
             if i == 0:
@@ -46,7 +46,7 @@ def prepare_block(verified_id, seq_lens, page_table, page_size, block, mask_toke
             pos = L + i
             positions[b, i] = pos
             n = pos // page_size
-            page = int(page_table[b, n]) if n < max_pages else -1
+            page = int(page_table[b, n]) if 0 <= pos and n < max_pages else -1
             if page < 0 or (num_pages is not None and page >= num_pages):
                 err |= ERR_SLOT
                 cache_loc[b, i] = -1

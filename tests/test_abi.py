@@ -1,0 +1,135 @@
+"""CPU checks of the C ABI: the library loads, exports exactly the functions
+include/specattn.h declares, and rejects bad arguments on the host before
+any launch (no compute calls here; this container has no GPU)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import verify_attention_amd as va
+from verify_attention_amd import binding as b
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(b.lib_path()):
+        from verify_attention_amd import build
+        build.build()
+    return va.load()
+
+
+def test_exports_match_header(lib):
+    declared = set(b.header_functions())
+    out = subprocess.run(["nm", "-D", "--defined-only", b.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[2] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    assert exported == declared
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert lib.spec_version() == 100
+    for s in (0, -1, -2, -3, -4):
+        assert len(lib.spec_status_string(s)) > 0
+    assert lib.spec_status_string(-99) == b"unknown status"
+
+
+def _prep(lib, **kw):
+    args = dict(bs=2, B=4, P=16, max_pages=4, num_pages=8, mask=0, vid=FAKE, seq=FAKE, tab=FAKE,
+                draft=None, ids=FAKE, pos=FAKE, loc=FAKE, err=None)
+    args.update(kw)
+    return lib.spec_prepare_block(args["bs"], args["B"], args["P"], args["max_pages"],
+                                  args["num_pages"], args["mask"], args["vid"], args["seq"],
+                                  args["tab"], args["draft"], args["ids"], args["pos"],
+                                  args["loc"], args["err"], None)
+
+
+def test_prepare_block_rejects_bad_arguments(lib):
+    assert _prep(lib, bs=0) == b.SPEC_EINVAL
+    assert _prep(lib, B=0) == b.SPEC_EINVAL
+    assert _prep(lib, P=0) == b.SPEC_EINVAL
+    assert _prep(lib, max_pages=0) == b.SPEC_EINVAL
+    assert _prep(lib, num_pages=0) == b.SPEC_EINVAL
+    assert _prep(lib, vid=None) == b.SPEC_EINVAL
+    assert _prep(lib, loc=None) == b.SPEC_EINVAL
+
+
+def _attn(lib, **kw):
+    a = dict(mode=1, nc=0, ncr=None, dt=1, bs=2, B=16, hq=32, hkv=8, d=128, P=16, max_pages=80,
+             num_pages=200, max_kv=1040, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, seq=FAKE, scale=0.0,
+             o=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, err=None)
+    a.update(kw)
+    return lib.block_attn(a["mode"], a["nc"], a["ncr"], a["dt"], a["bs"], a["B"], a["hq"],
+                          a["hkv"], a["d"], a["P"], a["max_pages"], a["num_pages"], a["max_kv"],
+                          a["q"], a["k"], a["v"], a["tab"], a["seq"], a["scale"], a["o"],
+                          a["lse"], a["ws"], a["ws_bytes"], a["err"], None)
+
+
+def test_block_attn_rejects_bad_arguments(lib):
+    assert _attn(lib, d=96) == b.SPEC_ENOTSUP
+    assert _attn(lib, P=8) == b.SPEC_ENOTSUP
+    assert _attn(lib, dt=7) == b.SPEC_ENOTSUP
+    assert _attn(lib, mode=3) == b.SPEC_EINVAL
+    assert _attn(lib, hq=30) == b.SPEC_EINVAL           # Hq % Hkv != 0
+    assert _attn(lib, B=40) == b.SPEC_EINVAL            # g * B = 160 > 128
+    assert _attn(lib, bs=0) == b.SPEC_EINVAL
+    assert _attn(lib, max_pages=0) == b.SPEC_EINVAL
+    assert _attn(lib, mode=2, nc=17) == b.SPEC_EINVAL   # n_causal > B
+    assert _attn(lib, mode=2, nc=-1) == b.SPEC_EINVAL
+    assert _attn(lib, q=None) == b.SPEC_EINVAL
+    assert _attn(lib, o=None) == b.SPEC_EINVAL
+    assert _attn(lib, scale=float("nan")) == b.SPEC_EINVAL
+    assert _attn(lib, max_pages=1, B=32, hq=8, hkv=8) == b.SPEC_EINVAL  # table shorter than B
+
+
+def test_block_attn_workspace_planning(lib):
+    # few (request, KV head) units and a long context -> split-KV workspace
+    small = lib.block_attn_workspace_bytes(2, 16, 32, 8, 128, 8192)
+    assert small > 0
+    assert _attn(lib, bs=2, max_kv=8192, ws_bytes=small - 1) == b.SPEC_ENOSPC
+    assert _attn(lib, bs=2, max_kv=8192, ws=None, ws_bytes=small) == b.SPEC_ENOSPC
+    # enough units to fill the chip -> no workspace at all
+    assert lib.block_attn_workspace_bytes(256, 16, 32, 8, 128, 9232) == 0
+    assert lib.block_attn_workspace_bytes(0, 16, 32, 8, 128, 9232) == 0
+
+
+def _acc(lib, **kw):
+    a = dict(bs=4, K=15, V=151936, greedy=0, p=FAKE, q=FAKE, d=FAKE, u=FAKE, seq=FAKE, al=FAKE,
+             cl=FAKE, bon=FAKE, out=FAKE, nsl=FAKE, ws=FAKE, ws_bytes=1 << 30, err=None)
+    a.update(kw)
+    return lib.spec_accept(a["bs"], a["K"], a["V"], a["greedy"], a["p"], a["q"], a["d"], a["u"],
+                           a["seq"], a["al"], a["cl"], a["bon"], a["out"], a["nsl"], a["ws"],
+                           a["ws_bytes"], a["err"], None)
+
+
+def test_accept_rejects_bad_arguments(lib):
+    assert _acc(lib, bs=0) == b.SPEC_EINVAL
+    assert _acc(lib, K=0) == b.SPEC_EINVAL
+    assert _acc(lib, K=64) == b.SPEC_EINVAL
+    assert _acc(lib, V=0) == b.SPEC_EINVAL
+    assert _acc(lib, q=None) == b.SPEC_EINVAL
+    assert _acc(lib, u=None) == b.SPEC_EINVAL
+    assert _acc(lib, out=None) == b.SPEC_EINVAL
+    need = lib.spec_accept_workspace_bytes(4, 15, 151936, 0)
+    assert need > 0
+    assert _acc(lib, ws_bytes=need - 1) == b.SPEC_ENOSPC
+    assert _acc(lib, ws=None) == b.SPEC_ENOSPC
+    assert lib.spec_accept_workspace_bytes(4, 15, 151936, 1) == 4 * 16 * 4
+
+
+def test_argmax_rejects_bad_arguments(lib):
+    assert lib.spec_draft_argmax(0, 10, 1, FAKE, FAKE, None) == b.SPEC_EINVAL
+    assert lib.spec_draft_argmax(4, 0, 1, FAKE, FAKE, None) == b.SPEC_EINVAL
+    assert lib.spec_draft_argmax(4, 10, 5, FAKE, FAKE, None) == b.SPEC_ENOTSUP
+    assert lib.spec_draft_argmax(4, 10, 1, None, FAKE, None) == b.SPEC_EINVAL
+
+
+def test_binding_fails_loudly_without_gpu_tensors(lib):
+    import torch
+    x = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(b.SpecError):
+        va.prepare_block(x, x, torch.zeros((3, 2), dtype=torch.int32), 16, 4, 0, 8)

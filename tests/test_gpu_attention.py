@@ -1,0 +1,171 @@
+"""GPU parity of block_attn against the float64 CPU reference.
+
+Agreement required: max abs error <= 1e-2 for bf16 inputs, <= 1e-5 for fp32
+inputs (outputs written in the input dtype); lse within 1e-3 (bf16) / 1e-5.
+Small cases compare every output row with the dense reference; full-size
+workloads compare sampled rows computed one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import verify_attention_amd as va
+from verify_attention_amd import synth
+from _support import AttnCase, print_case, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}
+
+
+def run(case, mode, max_kv=None, nc_per_req=False, err=None):
+    x = case.x
+    lse = torch.empty((x.cfg.bs, x.cfg.block, x.cfg.hq), dtype=torch.float32, device="cuda")
+    o = va.block_attn(mode, case.q, case.k, case.v, case.table, case.seq,
+                      max_kv or case.max_kv, n_causal=x.cfg.n_causal,
+                      n_causal_per_req=case.nc if nc_per_req else None, lse=lse, err=err)
+    torch.cuda.synchronize()
+    return to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def ref_dense(x, mode, nc):
+    return oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                   x.page_table, x.seq_lens, mode, nc)
+
+
+def check_all(x, got_o, got_lse, mode, nc):
+    ro, rl = ref_dense(x, mode, nc)
+    eo = np.max(np.abs(got_o - ro))
+    el = np.max(np.abs(got_lse - rl))
+    assert eo <= TOL[x.cfg.dtype], f"max abs error {eo}"
+    assert el <= LSE_TOL[x.cfg.dtype], f"lse error {el}"
+    return eo
+
+
+SMALL = [
+    # (name, config id, overrides, mode)
+    ("tiny_f32_bidir", 1, {}, synth.BIDIR),
+    ("tiny_f32_causal", 1, {}, synth.CAUSAL),
+    ("tiny_f32_mixed", 1, dict(n_causal=3), synth.MIXED),
+    ("verify_bs2", 2, dict(bs=2), synth.CAUSAL),
+    ("verify_bs3_bidir", 2, dict(bs=3), synth.BIDIR),
+    ("draft_b32_p32_ragged", 3, dict(bs=3, ctx_lo=700, ctx_hi=1500), synth.BIDIR),
+    ("ragged_verify_bs5", 4, dict(bs=5, ctx_lo=30, ctx_hi=1300), synth.CAUSAL),
+    ("mixed_bs2", 5, dict(bs=2, ctx_lo=900, ctx_hi=1100), synth.MIXED),
+    ("no_context", 2, dict(bs=2, ctx_lo=0, ctx_hi=0), synth.CAUSAL),
+    ("short_ctx_mixed", 5, dict(bs=3, ctx_lo=1, ctx_hi=40), synth.MIXED),
+    ("single_token_block", 2, dict(bs=3, block=1, ctx_lo=5, ctx_hi=300), synth.CAUSAL),
+    ("g1_b8_d64", 1, dict(bs=4, hq=4, hkv=4, dtype="bf16", ctx_lo=100, ctx_hi=700), synth.BIDIR),
+    ("g2_b40_d128", 2, dict(bs=2, hq=4, hkv=2, block=40, ctx_lo=50, ctx_hi=400), synth.CAUSAL),
+    ("f32_d128_m64", 2, dict(bs=2, dtype="f32", ctx_lo=200, ctx_hi=600), synth.CAUSAL),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,mode", SMALL, ids=[s[0] for s in SMALL])
+def test_small_all_rows(gpu_lib, name, cid, over, mode):
+    cfg = synth.config(cid, **over)
+    print_case("block_attn", name, cfg)
+    x = synth.make_attn_inputs(cfg, seed=100 + cid)
+    case = AttnCase(x)
+    o, lse = run(case, mode)
+    check_all(x, o, lse, mode, cfg.n_causal)
+
+
+def test_mixed_per_request_clean_counts(gpu_lib):
+    """I-DLM batches mix verify rows (N clean positions) with cold starts (1
+    clean position): n_causal differs per request."""
+    cfg = synth.config(5, bs=6, ctx_lo=64, ctx_hi=700)
+    print_case("block_attn mixed per-request", cfg)
+    x = synth.make_attn_inputs(cfg, seed=7, n_causal_per_req=True)
+    case = AttnCase(x)
+    o, lse = run(case, synth.MIXED, nc_per_req=True)
+    ro = np.empty_like(o)
+    rl = np.empty_like(lse)
+    for b in range(cfg.bs):
+        one = synth.AttnInputs(cfg, x.seq_lens[b:b + 1], x.page_table[b:b + 1], x.num_pages,
+                               x.q[b:b + 1], x.k_pool, x.v_pool, x.n_causal[b:b + 1])
+        r = ref_dense(one, synth.MIXED, int(x.n_causal[b]))
+        ro[b], rl[b] = r[0][0], r[1][0]
+    assert np.max(np.abs(o - ro)) <= TOL["bf16"]
+    assert np.max(np.abs(lse - rl)) <= LSE_TOL["bf16"]
+
+
+def test_poisoned_tail_slots_never_read(gpu_lib):
+    """Slots past L_b + B hold NaN; no output may change or turn NaN."""
+    cfg = synth.config(4, bs=4, ctx_lo=17, ctx_hi=900)
+    print_case("block_attn poisoned tail", cfg)
+    x = synth.make_attn_inputs(cfg, seed=3, poison_tail=True)
+    o, lse = run(AttnCase(x), synth.CAUSAL)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    check_all(x, o, lse, synth.CAUSAL, 0)
+
+
+def test_split_kv_plans_agree(gpu_lib):
+    """A loose host upper bound on the context length makes the planner split
+    every (request, KV head) many ways (most splits then hold no key): the
+    result must not change beyond fp32 rounding."""
+    cfg = synth.config(2, bs=2, ctx_lo=1500, ctx_hi=2600)
+    print_case("block_attn split plans", cfg)
+    x = synth.make_attn_inputs(cfg, seed=5)
+    case = AttnCase(x)
+    o1, l1 = run(case, synth.CAUSAL)
+    o2, l2 = run(case, synth.CAUSAL, max_kv=9216)
+    o3, l3 = run(case, synth.CAUSAL, max_kv=65536)
+    assert va.attn_workspace_bytes(2, 16, 32, 8, 128, 65536) > va.attn_workspace_bytes(2, 16, 32, 8, 128, 2616)
+    assert np.max(np.abs(o1 - o2)) <= 2 ** -7 and np.max(np.abs(o1 - o3)) <= 2 ** -7
+    assert np.max(np.abs(l1 - l3)) <= 1e-4
+    check_all(x, o3, l3, synth.CAUSAL, 0)
+    # a second call on the same workspace (counters were reset by the first)
+    ws = va.workspace(va.attn_workspace_bytes(2, 16, 32, 8, 128, 65536))
+    for _ in range(2):
+        o = va.block_attn(synth.CAUSAL, case.q, case.k, case.v, case.table, case.seq, 65536, ws=ws)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(to_f64(o) - o3)) == 0.0
+
+
+def test_bad_page_id_is_flagged(gpu_lib):
+    cfg = synth.config(2, bs=2, ctx_lo=300, ctx_hi=300)
+    print_case("block_attn bad page id", cfg)
+    x = synth.make_attn_inputs(cfg, seed=9)
+    x.page_table[1, 3] = x.num_pages + 5
+    case = AttnCase(x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, _ = run(case, synth.CAUSAL, err=err)
+    assert int(err.item()) & va.ERR_SLOT
+    # request 0 is untouched by request 1's bad entry
+    good = synth.AttnInputs(cfg, x.seq_lens[:1], x.page_table[:1], x.num_pages, x.q[:1],
+                            x.k_pool, x.v_pool, x.n_causal[:1])
+    ro, _ = ref_dense(good, synth.CAUSAL, 0)
+    assert np.max(np.abs(o[:1] - ro)) <= TOL["bf16"]
+
+
+def sampled_rows(x, n, rng):
+    rows = set()
+    B, hq = x.cfg.block, x.cfg.hq
+    while len(rows) < n:
+        rows.add((int(rng.integers(x.cfg.bs)), int(rng.integers(B)), int(rng.integers(hq))))
+    # always the first and last block rows of the longest and shortest request
+    for b in (int(np.argmax(x.seq_lens)), int(np.argmin(x.seq_lens))):
+        rows.update({(b, 0, 0), (b, B - 1, hq - 1)})
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_full_size_sampled_rows(gpu_lib, cid):
+    """Full workload shapes in the bench's launch configuration; the reference
+    computes sampled rows one at a time."""
+    cfg = synth.config(cid)
+    print_case("block_attn full size", cid, cfg.name)
+    x = synth.make_attn_inputs(cfg, seed=cid)
+    case = AttnCase(x)
+    mode = cfg.modes[0]
+    o, lse = run(case, mode)
+    assert np.isfinite(o).all()
+    rows = sampled_rows(x, 40, np.random.default_rng(cid))
+    ro, rl = oracle.block_attn_rows(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                    x.page_table, x.seq_lens, mode, cfg.n_causal, rows=rows)
+    for (b, i, h) in rows:
+        assert np.max(np.abs(o[b, i, h] - ro[b, i, h])) <= TOL[cfg.dtype], (b, i, h)
+        assert abs(lse[b, i, h] - rl[b, i, h]) <= LSE_TOL[cfg.dtype], (b, i, h)

@@ -1,12 +1,238 @@
-"""ctypes binding of libspecattn.so (filled in with the C ABI)."""
+"""ctypes binding of libspecattn.so (include/specattn.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape
+and contiguity, their data pointers and the current HIP stream are handed to
+the C ABI, and a negative status raises. Every step of the computation runs in
+the library's HIP kernels; there is no other implementation behind these
+names, so a missing library or device is an error, never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes
 import os
+import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+_LIB = None
+
+SPEC_OK, SPEC_EINVAL, SPEC_ENOTSUP, SPEC_ENOSPC, SPEC_EHIP = 0, -1, -2, -3, -4
+ERR_SLOT, ERR_CAPACITY, ERR_TOKEN, ERR_ZERO_RESIDUAL = 1, 2, 4, 8
+BIDIR, CAUSAL, MIXED = 0, 1, 2
+F32, BF16 = 0, 1
+
+_c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+_SIGS = {
+    "spec_version": (_c_int, []),
+    "spec_status_string": (ctypes.c_char_p, [_c_int]),
+    "spec_prepare_block": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_int32,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "block_attn_workspace_bytes": (_c_size, [_c_int] * 6),
+    "block_attn": (_c_int, [_c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                            _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _f, _vp,
+                            _vp, _vp, _c_size, _vp, _vp]),
+    "spec_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "spec_accept_workspace_bytes": (_c_size, [_c_int] * 4),
+    "spec_accept": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
+}
 
 
-def lib_path():
+class SpecError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
     return os.path.join(_HERE, "libspecattn.so")
 
 
+def header_path() -> str:
+    return os.path.join(_ROOT, "include", "specattn.h")
+
+
+def header_functions() -> list:
+    """Names of the functions include/specattn.h declares."""
+    txt = open(header_path()).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", txt, flags=re.M)))
+
+
 def load():
-    raise RuntimeError("libspecattn.so binding not built yet")
+    """Load the built library (raises when it is missing)."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise SpecError(f"{path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(status: int, what: str):
+    if status != SPEC_OK:
+        msg = load().spec_status_string(status).decode()
+        raise SpecError(f"{what} failed with status {status}: {msg}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, shape=None, device=True):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if device and not t.is_cuda:
+        raise SpecError(f"{name} must live on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------- workspaces
+def attn_workspace_bytes(bs, B, hq, hkv, d, max_kv_len) -> int:
+    return int(load().block_attn_workspace_bytes(bs, B, hq, hkv, d, max_kv_len))
+
+
+def accept_workspace_bytes(bs, K, V, greedy=False) -> int:
+    return int(load().spec_accept_workspace_bytes(bs, K, V, int(bool(greedy))))
+
+
+def workspace(nbytes, device="cuda"):
+    """A zero-filled device workspace (the library needs zeros before first use)."""
+    torch = _torch()
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# -------------------------------------------------------------------- calls
+def prepare_block(verified_id, seq_lens, page_table, page_size, block, mask_token_id, num_pages,
+                  draft_tokens=None, out=None, err=None, stream=None):
+    """Block ids, positions and KV slots of one round (spec_prepare_block)."""
+    torch = _torch()
+    bs = verified_id.shape[0]
+    _need(verified_id, "verified_id", torch.int32, (bs,))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need(page_table, "page_table", torch.int32)
+    if draft_tokens is not None:
+        _need(draft_tokens, "draft_tokens", torch.int32, (bs, block - 1))
+    if out is None:
+        out = tuple(torch.empty((bs, block), dtype=torch.int32, device=verified_id.device)
+                    for _ in range(3))
+    for t, nm in zip(out, ("block_ids", "positions", "cache_loc")):
+        _need(t, nm, torch.int32, (bs, block))
+    st = load().spec_prepare_block(bs, block, page_size, page_table.shape[1], num_pages,
+                                   mask_token_id, _ptr(verified_id), _ptr(seq_lens),
+                                   _ptr(page_table), _ptr(draft_tokens), _ptr(out[0]),
+                                   _ptr(out[1]), _ptr(out[2]), _ptr(err), _stream(stream))
+    _check(st, "spec_prepare_block")
+    return out
+
+
+def block_attn(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n_causal=0,
+               n_causal_per_req=None, sm_scale=0.0, out=None, lse=None, ws=None, err=None,
+               stream=None):
+    """Block-query attention over the paged cache (block_attn).
+
+    q [bs, B, Hq, D]; k_pool [pages, Hkv, P, D]; v_pool [pages, Hkv, D, P]."""
+    torch = _torch()
+    bs, B, hq, d = q.shape
+    num_pages, hkv, P, d2 = k_pool.shape
+    _need(q, "q")
+    dt = _dtype_code(q)
+    _need(k_pool, "k_pool", q.dtype)
+    _need(v_pool, "v_pool", q.dtype, (num_pages, hkv, d, P))
+    if d2 != d:
+        raise ValueError("k_pool head dim differs from q")
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    if n_causal_per_req is not None:
+        _need(n_causal_per_req, "n_causal_per_req", torch.int32, (bs,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (bs, B, hq))
+    need = attn_workspace_bytes(bs, B, hq, hkv, d, max_kv_len)
+    if ws is None and need > 0:
+        ws = workspace(need, q.device)
+    st = load().block_attn(mode, n_causal, _ptr(n_causal_per_req), dt, bs, B, hq, hkv, d, P,
+                           page_table.shape[1], num_pages, max_kv_len, _ptr(q), _ptr(k_pool),
+                           _ptr(v_pool), _ptr(page_table), _ptr(seq_lens), sm_scale, _ptr(out),
+                           _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _ptr(err),
+                           _stream(stream))
+    _check(st, "block_attn")
+    return out
+
+
+def draft_argmax(logits, out=None, stream=None):
+    """Greedy draft tokens: lowest-index argmax of each row of logits [rows, V]."""
+    torch = _torch()
+    _need(logits, "logits")
+    rows, V = logits.shape
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _need(out, "tokens", torch.int32, (rows,))
+    st = load().spec_draft_argmax(rows, V, _dtype_code(logits), _ptr(logits), _ptr(out),
+                                  _stream(stream))
+    _check(st, "spec_draft_argmax")
+    return out
+
+
+def accept(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, stream=None):
+    """Speculative accept / bonus (spec_accept). Returns a dict of int32 tensors:
+    accept_len, commit_len, bonus, out_tokens [bs, K+1], new_seq_lens."""
+    torch = _torch()
+    bs, K1, V = p.shape
+    K = K1 - 1
+    _need(p, "p", torch.float32)
+    _need(draft, "draft", torch.int32, (bs, K))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    if not greedy:
+        _need(q, "q", torch.float32, (bs, K, V))
+        _need(u, "u", torch.float32, (bs, K + 1))
+    dev = p.device
+    if out is None:
+        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((bs, K + 1), dtype=torch.int32, device=dev),
+                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = workspace(accept_workspace_bytes(bs, K, V, greedy), dev)
+    st = load().spec_accept(bs, K, V, int(bool(greedy)), _ptr(p), _ptr(q), _ptr(draft), _ptr(u),
+                            _ptr(seq_lens), _ptr(out["accept_len"]), _ptr(out["commit_len"]),
+                            _ptr(out["bonus"]), _ptr(out["out_tokens"]),
+                            _ptr(out["new_seq_lens"]), _ptr(ws), ws.numel(), _ptr(err),
+                            _stream(stream))
+    _check(st, "spec_accept")
+    return out

@@ -1,0 +1,254 @@
+// Host side of the C ABI declared in include/specattn.h: argument checks,
+// split-KV / vocabulary-chunk planning, workspace layout and kernel launches.
+// Every entry point only enqueues work on the caller's stream.
+#include <climits>
+#include <cmath>
+#include <cstdlib>
+
+#include "specattn.h"
+#include "kernels.h"
+
+#define SPEC_API extern "C" __attribute__((visibility("default")))
+
+using namespace specattn;
+
+namespace {
+
+constexpr int kStepKeys = 32;
+constexpr int kMaxSplits = 64;  // the merge weights (M x (splits+1) floats) fit the LDS output tile
+constexpr int kMaxChunks = 256;
+constexpr int kCUs = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int ilog2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return (1 << s) == x ? s : -1;
+}
+
+// Optional override of the split count, read once (tuning knob).
+int env_splits() {
+  static int v = [] {
+    const char* s = std::getenv("SPECATTN_SPLITS");
+    return s ? std::atoi(s) : 0;
+  }();
+  return v;
+}
+
+struct AttnPlan {
+  int M = 0, units = 0, splits = 1, steps_per_split = 1;
+  size_t off_counters = 0, off_ml = 0, off_o = 0, ws_bytes = 0;
+};
+
+// Splits per (request, KV head): enough workgroups to cover the chip when the
+// batch has few (request, KV head) units, while every wave keeps several
+// 32-key steps. A split runs 4 key waves, so 16 steps = 4 per wave minimum.
+AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
+  AttnPlan p;
+  p.M = (Hq / Hkv) * B;
+  p.units = bs * Hkv;
+  const int max_steps = std::max(1, (max_kv_len + kStepKeys - 1) / kStepKeys);
+  int splits = env_splits();
+  if (splits <= 0) {
+    splits = (kCUs + p.units - 1) / p.units;
+    splits = std::min(splits, std::max(1, max_steps / 16));
+  }
+  splits = std::max(1, std::min(splits, std::min(kMaxSplits, max_steps)));
+  p.steps_per_split = (max_steps + splits - 1) / splits;
+  p.splits = (max_steps + p.steps_per_split - 1) / p.steps_per_split;
+  if (p.splits > 1) {
+    p.off_counters = 0;
+    p.off_ml = align_up((size_t)p.units * sizeof(int32_t), 256);
+    p.off_o = p.off_ml + align_up((size_t)p.units * p.splits * p.M * 2 * sizeof(float), 256);
+    p.ws_bytes = p.off_o + (size_t)p.units * p.splits * p.M * D * sizeof(float);
+  }
+  return p;
+}
+
+struct AccPlan {
+  int nchunk = 1, chunk = 0;
+  size_t off_counters = 0, off_partial = 0, off_ids = 0, ws_bytes = 0;
+};
+
+// Vocabulary chunks per request: about 2048 workgroups over the batch, chunks a
+// multiple of 1024 entries (256 threads x one float4), at most 256 chunks.
+AccPlan plan_accept(int bs, int K, int V, int greedy) {
+  AccPlan p;
+  if (greedy) {
+    p.off_ids = 0;
+    p.ws_bytes = (size_t)bs * (K + 1) * sizeof(int32_t);
+    return p;
+  }
+  int want = std::max(1, std::min(kMaxChunks, (2048 + bs - 1) / bs));
+  int chunk = (V + want - 1) / want;
+  chunk = (int)align_up((size_t)chunk, 1024);
+  p.chunk = chunk;
+  p.nchunk = (V + chunk - 1) / chunk;
+  p.off_counters = 0;
+  p.off_partial = align_up((size_t)bs * sizeof(int32_t), 256);
+  p.ws_bytes = p.off_partial + (size_t)bs * p.nchunk * sizeof(double);
+  return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_EHIP; }
+
+}  // namespace
+
+SPEC_API int spec_version(void) { return 100; }
+
+SPEC_API const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument (null pointer, count or shape)";
+    case SPEC_ENOTSUP: return "unsupported dtype, head dim or page size";
+    case SPEC_ENOSPC: return "workspace too small";
+    case SPEC_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+SPEC_API int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_pages,
+                                int32_t mask_token_id, const int32_t* verified_id,
+                                const int32_t* seq_lens, const int32_t* page_table,
+                                const int32_t* draft_tokens, int32_t* block_ids,
+                                int32_t* positions, int32_t* cache_loc, int32_t* err_flags,
+                                void* stream) {
+  if (bs <= 0 || B <= 0 || page_size <= 0 || max_pages <= 0 || num_pages <= 0) return SPEC_EINVAL;
+  if ((long long)bs * B > INT_MAX) return SPEC_EINVAL;
+  if (!verified_id || !seq_lens || !page_table || !block_ids || !positions || !cache_loc)
+    return SPEC_EINVAL;
+  PrepareArgs a;
+  a.verified_id = verified_id;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.draft = B > 1 ? draft_tokens : nullptr;
+  a.block_ids = block_ids;
+  a.positions = positions;
+  a.cache_loc = cache_loc;
+  a.err = err_flags;
+  a.bs = bs;
+  a.B = B;
+  a.P = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.mask_token_id = mask_token_id;
+  return hip_status(launch_prepare_block(a, static_cast<hipStream_t>(stream)));
+}
+
+SPEC_API size_t block_attn_workspace_bytes(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
+  if (bs <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || max_kv_len <= 0) return 0;
+  return plan_attn(bs, B, Hq, Hkv, D, max_kv_len).ws_bytes;
+}
+
+SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req, int dtype, int bs,
+                        int B, int Hq, int Hkv, int D, int page_size, int max_pages,
+                        int num_pages, int max_kv_len, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+                        float sm_scale, void* o, float* lse, void* workspace, size_t ws_bytes,
+                        int32_t* err_flags, void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (D != 64 && D != 128) return SPEC_ENOTSUP;
+  if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
+  if (mode < SPEC_BIDIR || mode > SPEC_MIXED) return SPEC_EINVAL;
+  if (bs <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return SPEC_EINVAL;
+  if ((Hq / Hkv) * B > 128) return SPEC_EINVAL;
+  if (max_pages <= 0 || num_pages <= 0 || max_kv_len <= 0) return SPEC_EINVAL;
+  if ((long long)max_pages * page_size < B) return SPEC_EINVAL;
+  if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
+  if (mode == SPEC_MIXED && !n_causal_per_req && (n_causal < 0 || n_causal > B)) return SPEC_EINVAL;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return SPEC_EINVAL;
+  if (!(std::isfinite(sm_scale))) return SPEC_EINVAL;
+  const AttnPlan plan = plan_attn(bs, B, Hq, Hkv, D, max_kv_len);
+  if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes)) return SPEC_ENOSPC;
+
+  AttnArgs a;
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.nc_per_req = mode == SPEC_MIXED ? n_causal_per_req : nullptr;
+  a.o = o;
+  a.lse = lse;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = plan.splits > 1 ? reinterpret_cast<int32_t*>(ws + plan.off_counters) : nullptr;
+  a.part_ml = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.off_ml) : nullptr;
+  a.part_o = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.off_o) : nullptr;
+  a.err = err_flags;
+  a.bs = bs;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.g = Hq / Hkv;
+  a.M = plan.M;
+  a.P = page_size;
+  a.p_shift = ilog2_exact(page_size);
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.mode = mode;
+  a.n_causal = mode == SPEC_MIXED ? n_causal : (mode == SPEC_CAUSAL ? B : 0);
+  a.splits = plan.splits;
+  a.steps_per_split = plan.steps_per_split;
+  const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt((float)D) : sm_scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(launch_block_attn(a, dtype == SPEC_BF16, D, plan.units * plan.splits,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+SPEC_API int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* tokens,
+                               void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (rows <= 0 || V <= 0 || !logits || !tokens) return SPEC_EINVAL;
+  return hip_status(launch_argmax_rows(logits, dtype == SPEC_BF16, rows, V, tokens,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+SPEC_API size_t spec_accept_workspace_bytes(int bs, int K, int V, int greedy) {
+  if (bs <= 0 || K < 1 || K > 63 || V <= 0) return 0;
+  return plan_accept(bs, K, V, greedy).ws_bytes;
+}
+
+SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q,
+                         const int32_t* draft, const float* u, const int32_t* seq_lens,
+                         int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                         int32_t* out_tokens, int32_t* new_seq_lens, void* workspace,
+                         size_t ws_bytes, int32_t* err_flags, void* stream) {
+  if (bs <= 0 || K < 1 || K > 63 || V <= 0) return SPEC_EINVAL;
+  if ((long long)bs * (K + 1) > INT_MAX) return SPEC_EINVAL;
+  if (!p || !draft || !seq_lens || !accept_len || !commit_len || !bonus || !out_tokens ||
+      !new_seq_lens)
+    return SPEC_EINVAL;
+  if (!greedy && (!q || !u)) return SPEC_EINVAL;
+  const AccPlan plan = plan_accept(bs, K, V, greedy);
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  char* ws = static_cast<char*>(workspace);
+  AcceptArgs a;
+  a.p = p;
+  a.q = q;
+  a.draft = draft;
+  a.u = u;
+  a.seq_lens = seq_lens;
+  a.accept_len = accept_len;
+  a.commit_len = commit_len;
+  a.bonus = bonus;
+  a.out_tokens = out_tokens;
+  a.new_seq_lens = new_seq_lens;
+  a.err = err_flags;
+  a.bs = bs;
+  a.K = K;
+  a.V = V;
+  a.nchunk = plan.nchunk;
+  a.chunk = plan.chunk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (greedy) {
+    a.partial = nullptr;
+    a.counters = nullptr;
+    a.greedy_ids = reinterpret_cast<int32_t*>(ws + plan.off_ids);
+    return hip_status(launch_greedy_accept(a, s));
+  }
+  a.counters = reinterpret_cast<int32_t*>(ws + plan.off_counters);
+  a.partial = reinterpret_cast<double*>(ws + plan.off_partial);
+  a.greedy_ids = nullptr;
+  return hip_status(launch_accept(a, s));
+}

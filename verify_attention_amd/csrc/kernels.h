@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI host layer (capi.hip) and the kernels.
+#pragma once
+
+#include "common.h"
+
+namespace specattn {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* nc_per_req;
+  void* o;
+  float* lse;
+  float* part_o;      // [units * splits][M][D] split partial outputs (unnormalised)
+  float* part_ml;     // [units * splits][M][2] split partial (max, sum), log2 domain
+  int32_t* counters;  // [units] splits finished so far; reset by the merging workgroup
+  int32_t* err;
+  int bs, B, Hq, Hkv, g, M;  // M = g * B query rows per KV head
+  int P, p_shift, max_pages, num_pages;
+  int mode, n_causal;
+  int splits, steps_per_split;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks,
+                             hipStream_t stream);
+
+struct PrepareArgs {
+  const int32_t* verified_id;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  const int32_t* draft;
+  int32_t* block_ids;
+  int32_t* positions;
+  int32_t* cache_loc;
+  int32_t* err;
+  int bs, B, P, max_pages, num_pages;
+  int32_t mask_token_id;
+};
+
+hipError_t launch_prepare_block(const PrepareArgs& a, hipStream_t stream);
+
+hipError_t launch_argmax_rows(const void* x, bool bf16, int rows, int V, int32_t* out,
+                              hipStream_t stream);
+
+struct AcceptArgs {
+  const float* p;
+  const float* q;
+  const int32_t* draft;
+  const float* u;
+  const int32_t* seq_lens;
+  int32_t* accept_len;
+  int32_t* commit_len;
+  int32_t* bonus;
+  int32_t* out_tokens;
+  int32_t* new_seq_lens;
+  int32_t* err;
+  double* partial;     // [bs][nchunk] residual mass per vocabulary chunk
+  int32_t* counters;   // [bs] chunks finished so far; reset by the sampling workgroup
+  int32_t* greedy_ids; // [bs][K+1] row argmax (greedy mode)
+  int bs, K, V, nchunk, chunk;
+};
+
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+hipError_t launch_greedy_accept(const AcceptArgs& a, hipStream_t stream);
+
+}  // namespace specattn
