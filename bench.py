@@ -1,0 +1,253 @@
+"""Benchmark of one self-speculative decoding round on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  verify workloads: spec_prepare_block (verify pass) -> block_attn -> spec_accept
+  draft workload:   spec_prepare_block (draft pass)  -> block_attn -> spec_draft_argmax
+Inputs are resident in HBM before the timed region. Several copies of the
+per-step inputs are cycled so that every step reads its KV pages and target
+rows from HBM rather than from the 256 MB last-level cache.
+
+Prints ONE JSON line: verified tokens/s (bs * B per step), the dominant
+kernel's roofline position (block_attn, algorithmic bytes over its event-timed
+average duration) and the float64 CPU reference timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified tokens/s per round (attn+accept) and % HBM roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+F32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="round configuration 1..5")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference leg")
+    return ap.parse_args()
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "verify_attention_amd", "csrc"))):
+        h.update(open(os.path.join(ROOT, "verify_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def attn_alg_bytes_flops(cfg, seq_lens):
+    """Algorithmic bytes / flops of one block_attn launch: K and V of positions
+    [0, L_b + B) read once per KV head, Q read and O written once; 4 * D flops
+    per visible (query row, key) pair."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    keys = (seq_lens.astype(np.int64) + cfg.block).sum()
+    kv = 2 * keys * cfg.hkv * cfg.d * esz
+    qo = 2 * cfg.bs * cfg.block * cfg.hq * cfg.d * esz
+    B = cfg.block
+    i = np.arange(B)
+    if cfg.modes[0] == 0:
+        intra = B * B
+    elif cfg.modes[0] == 1:
+        intra = int((i + 1).sum())
+    else:
+        nc = cfg.n_causal
+        intra = int(np.where(i < nc, i + 1, B).sum())
+    pairs = (seq_lens.astype(np.int64) * B).sum() + cfg.bs * intra
+    flops = 4 * cfg.d * pairs * cfg.hq
+    return int(kv + qo), int(flops)
+
+
+def accept_alg_bytes(cfg, accept_len):
+    """Target / draft rows streamed by spec_accept: the residual pair p_j, q_j
+    (or the bonus row p_K alone) per request, plus 2K gathered floats."""
+    V, K = cfg.vocab, cfg.k_spec
+    rows = np.where(accept_len < K, 2, 1)
+    return int((rows * V * 4).sum() + cfg.bs * (2 * K + 1) * 4)
+
+
+def cpu_baseline(cfg, x, acc, seconds):
+    """The float64 reference, as it stands, on the host cores: dense attention
+    per (request, KV head) plus the sequential accept, request after request,
+    until `seconds` have elapsed (at least one request)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    q, kp, vp = x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool")
+    mode = cfg.modes[0]
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        b = done % cfg.bs
+        sl = slice(b, b + 1)
+        oracle.block_attn_dense(q[sl], kp, vp, x.page_table[sl], x.seq_lens[sl], mode,
+                                cfg.n_causal)
+        if acc is not None:
+            oracle.accept_request(acc.p[b], acc.q[b], acc.draft[b], acc.u[b], x.seq_lens[b])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return dict(value=done * cfg.block / el, unit="verified tokens/s", cores=int(threads),
+                kind="oracle",
+                sample=f"{done} requests of this workload (attention over all {cfg.hq} query "
+                       f"heads + accept), one after another, {el:.1f} s; host has "
+                       f"{len(os.sched_getaffinity(0))} cores")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build runs on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import verify_attention_amd as va
+    from verify_attention_amd import synth
+
+    va.load()
+    dev = torch.device("cuda:0")
+    cfg = synth.config(args.config)
+    mode = cfg.modes[-1]
+    x = synth.make_attn_inputs(cfg, seed=args.seed)
+    acc = synth.make_accept_inputs(cfg, seed=args.seed) if cfg.vocab else None
+    logits = synth.make_argmax_logits(cfg, seed=args.seed) if cfg.argmax_vocab else None
+    verified, drafts = synth.make_round_state(cfg, args.seed)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    step_bytes = x.k_pool.nbytes + x.v_pool.nbytes + x.q.nbytes
+    if acc is not None:
+        step_bytes += acc.p.nbytes + acc.q.nbytes
+    if logits is not None:
+        step_bytes += logits.nbytes
+    copies = args.copies or max(1, int(np.ceil(768e6 / step_bytes)))
+    sets = []
+    for _ in range(copies):
+        s = dict(q=up(x.q), k=up(x.k_pool), v=up(x.v_pool))
+        if acc is not None:
+            s.update(p=up(acc.p), qd=up(acc.q), u=up(acc.u), draft=up(acc.draft))
+        if logits is not None:
+            s["logits"] = up(logits)
+        sets.append(s)
+    table, seq = up(x.page_table), up(x.seq_lens)
+    vid, dr = up(verified), up(drafts)
+    max_kv = int(x.seq_lens.max()) + cfg.block
+    bs, B = cfg.bs, cfg.block
+    o = torch.empty_like(sets[0]["q"])
+    ws_attn = va.workspace(va.attn_workspace_bytes(bs, B, cfg.hq, cfg.hkv, cfg.d, max_kv))
+    prep_out = tuple(torch.empty((bs, B), dtype=torch.int32, device=dev) for _ in range(3))
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    if acc is not None:
+        ws_acc = va.workspace(va.accept_workspace_bytes(bs, cfg.k_spec, cfg.vocab))
+        acc_out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                       commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                       bonus=torch.empty(bs, dtype=torch.int32, device=dev),
+                       out_tokens=torch.empty((bs, cfg.k_spec + 1), dtype=torch.int32, device=dev),
+                       new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
+    else:
+        tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % copies]
+        va.prepare_block(vid, seq, table, cfg.page, B, 0, x.num_pages,
+                         None if mode == synth.BIDIR else dr, out=prep_out, err=err)
+        if ev is not None:
+            ev[0].record(stream)
+        va.block_attn(mode, s["q"], s["k"], s["v"], table, seq, max_kv, n_causal=cfg.n_causal,
+                      out=o, ws=ws_attn, err=err)
+        if ev is not None:
+            ev[1].record(stream)
+        if acc is not None:
+            va.accept(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out, ws=ws_acc, err=err)
+        else:
+            va.draft_argmax(s["logits"], out=tokens)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(err.item()) != 0:
+        raise RuntimeError(f"kernels reported data errors: {int(err.item())}")
+
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    tail_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    alg_bytes, alg_flops = attn_alg_bytes_flops(cfg, x.seq_lens)
+    attn_s = attn_ms.mean() / 1e3
+    achieved = alg_bytes / attn_s / 1e9
+    mfma_peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
+    tokens_per_step = bs * B
+    value = tokens_per_step * args.steps / wall
+    extra = {}
+    if acc is not None:
+        al = acc_out["accept_len"].cpu().numpy()
+        cl = acc_out["commit_len"].cpu().numpy()
+        ab = accept_alg_bytes(cfg, al)
+        extra["accept"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2),
+                               alg_bytes=ab, achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1),
+                               mean_commit_len=float(cl.mean()))
+        extra["committed_tokens_per_s"] = float(cl.sum() * args.steps / wall)
+    else:
+        ab = logits.nbytes
+        extra["draft_argmax"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2), alg_bytes=int(ab),
+                                     achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1))
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, softmax-of-normal target/draft rows)",
+        "config": {"workload": cfg.name, "bs": bs, "block": B, "hq": cfg.hq, "hkv": cfg.hkv,
+                   "head_dim": cfg.d, "page": cfg.page, "mode": synth.MODE_NAMES[mode],
+                   "ctx": [cfg.ctx_lo, cfg.ctx_hi], "vocab": cfg.vocab or cfg.argmax_vocab,
+                   "k_spec": cfg.k_spec, "input_copies": copies},
+        "roofline": {"kernel": "block_attn", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": alg_bytes, "avg_us": round(attn_ms.mean() * 1e3, 2),
+                     "mfma_frac": round(alg_flops / attn_s / 1e12 / mfma_peak, 4)},
+        "kernel_src": kernel_sources_hash(),
+        **extra,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, x, acc, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -136,10 +136,11 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
  *   q [bs, B, Hq, D]; k_pool, v_pool as in the file header; page_table;
  *   seq_lens [bs]; sm_scale (0 -> 1/sqrt(D))
  * Outputs: o [bs, B, Hq, D] (dtype), lse [bs, B, Hq] float (nullable).
- * Workspace: at least block_attn_workspace_bytes(...) bytes of device memory,
- *   16-byte aligned, ZERO-FILLED before its first use; every completed call
- *   leaves it ready for the next one. Calls that share a workspace must not
- *   overlap in time.
+ * Workspace: at least block_attn_workspace_bytes(...) bytes of device memory
+ *   (0 when the plan needs no split-KV partials; then workspace may be NULL),
+ *   16-byte aligned, contents irrelevant. It holds per-split partial outputs
+ *   between the attention kernel and the merge kernel of the same call, so
+ *   calls that share a workspace must be ordered (same stream, or synchronised).
  * Errors: SPEC_EINVAL (bad counts, Hq % Hkv != 0, g * B > 128, mode, n_causal
  *   outside [0, B], NULL pointers), SPEC_ENOTSUP (D, P, dtype), SPEC_ENOSPC.
  *   Kernels set SPEC_ERR_SLOT for a page id outside [0, num_pages) (that page
@@ -200,9 +201,9 @@ int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* t
  *   in [0, 1), seq_lens [bs]
  * Outputs: accept_len, commit_len, bonus, new_seq_lens [bs]; out_tokens [bs, K+1].
  * Workspace: spec_accept_workspace_bytes(bs, K, V, greedy) bytes of device
- *   memory, 16-byte aligned, ZERO-FILLED before its first use; every
- *   completed call leaves it ready for the next one. Calls that share a
- *   workspace must not overlap in time.
+ *   memory, 16-byte aligned, contents irrelevant (per-chunk residual masses
+ *   and accept lengths passed between the call's two kernels). Calls that
+ *   share a workspace must be ordered (same stream, or synchronised).
  * Errors: SPEC_EINVAL (bs <= 0, K outside 1..63, V <= 0, NULL), SPEC_ENOSPC.
  */
 size_t spec_accept_workspace_bytes(int bs, int K, int V, int greedy);

@@ -62,11 +62,13 @@ def accept_request(p, q, draft, u, seq_len):
     """One request. p [K+1, V], q [K, V] float32 rows; draft [K]; u [K+1].
 
     Returns a dict with accept_len, commit_len, bonus, out_tokens [K+1]
-    (accepted drafts, then the bonus, then -1), new_seq_len, err, and
-    tie (True when a decision lies within 1e-6 of its threshold)."""
+    (accepted drafts, then the bonus, then -1), new_seq_len, err, and the
+    tie flags: tie_accept when a reached test has |u - min(1, p/q)| < 1e-6,
+    tie_sample when u_K * S lies within 1e-6 * S of the chosen token's
+    interval ends, tie = either."""
     K, V = q.shape
     err = 0
-    tie = False
+    tie_accept = False
     n_acc = 0
     for i in range(K):
         d = int(draft[i])
@@ -77,7 +79,7 @@ def accept_request(p, q, draft, u, seq_len):
         qd = np.float64(q[i, d])
         ui = np.float64(u[i])
         if qd > 0 and abs(ui - min(1.0, pd / qd)) < TIE_EPS:
-            tie = True
+            tie_accept = True
         if ui * qd < pd:
             n_acc += 1
         else:
@@ -92,13 +94,13 @@ def accept_request(p, q, draft, u, seq_len):
         r = p[j].astype(np.float64)
     t, S, thr, C = _inverse_cdf(r, u[K])
     lo = C[t - 1] if t > 0 else 0.0
-    if abs(thr - C[t]) < TIE_EPS * S or abs(thr - lo) < TIE_EPS * S:
-        tie = True
+    tie_sample = bool(abs(thr - C[t]) < TIE_EPS * S or abs(thr - lo) < TIE_EPS * S)
     out = np.full(K + 1, -1, np.int64)
     out[:n_acc] = draft[:n_acc]
     out[n_acc] = t
     return dict(accept_len=n_acc, commit_len=n_acc + 1, bonus=t, out_tokens=out,
-                new_seq_len=int(seq_len) + n_acc + 1, err=err, tie=tie)
+                new_seq_len=int(seq_len) + n_acc + 1, err=err, tie=tie_accept or tie_sample,
+                tie_accept=tie_accept, tie_sample=tie_sample)
 
 
 def greedy_accept_request(p, draft, seq_len):
@@ -113,7 +115,8 @@ def greedy_accept_request(p, draft, seq_len):
     out[:n_acc] = draft[:n_acc]
     out[n_acc] = bonus
     return dict(accept_len=n_acc, commit_len=n_acc + 1, bonus=bonus, out_tokens=out,
-                new_seq_len=int(seq_len) + n_acc + 1, err=0, tie=False)
+                new_seq_len=int(seq_len) + n_acc + 1, err=0, tie=False, tie_accept=False,
+                tie_sample=False)
 
 
 def accept_batch(p, q, draft, u, seq_lens, greedy=False, requests=None):
@@ -122,7 +125,7 @@ def accept_batch(p, q, draft, u, seq_lens, greedy=False, requests=None):
     bs, K = draft.shape
     reqs = range(bs) if requests is None else requests
     res = dict(accept_len=[], commit_len=[], bonus=[], out_tokens=[], new_seq_len=[],
-               err=[], tie=[])
+               err=[], tie=[], tie_accept=[], tie_sample=[])
     for b in reqs:
         if greedy:
             r = greedy_accept_request(p[b], draft[b], seq_lens[b])

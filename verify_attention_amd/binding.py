@@ -129,9 +129,9 @@ def accept_workspace_bytes(bs, K, V, greedy=False) -> int:
 
 
 def workspace(nbytes, device="cuda"):
-    """A zero-filled device workspace (the library needs zeros before first use)."""
+    """A device workspace of at least nbytes (contents irrelevant to the library)."""
     torch = _torch()
-    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 # -------------------------------------------------------------------- calls

@@ -10,9 +10,10 @@
 //   * the residual row r = max(p_j - q_j, 0) (or the bonus row p_K) is split
 //     into vocabulary chunks, one workgroup per (request, chunk), each
 //     summing its chunk in double;
-//   * the last workgroup of the request (device-scope counter) scans the chunk
-//     sums, finds the chunk where the running mass passes u_K * S, re-reads
-//     only that chunk to locate the token, and writes every output.
+//   * a second kernel, one workgroup per request, scans the chunk sums, finds
+//     the chunk where the running mass passes u_K * S, re-reads only that
+//     chunk to locate the token, and writes every output (a kernel boundary
+//     orders the two phases; no device-scope fences or counters).
 // Only the residual (or bonus) row pair is streamed from HBM; the other target
 // rows are touched at one gathered element each.
 #include "kernels.h"
@@ -20,6 +21,7 @@
 namespace specattn {
 
 constexpr int kAccThreads = 256;
+constexpr int kJTokenErr = 1 << 16;  // jbuf flag: the first reject was an invalid token id
 
 // ------------------------------------------------------------ block scans
 // Inclusive prefix sum of one double per thread over a 256-thread block, in a
@@ -67,6 +69,7 @@ __device__ double range_mass(const float* p, const float* q, int lo, int hi) {
     const int n4 = (hi - lo) / 4;
     const float4* p4 = reinterpret_cast<const float4*>(p + lo);
     const float4* q4 = q ? reinterpret_cast<const float4*>(q + lo) : nullptr;
+#pragma unroll 4
     for (int e = threadIdx.x; e < n4; e += kAccThreads) {
       const float4 pv = p4[e];
       if (q4) {
@@ -130,16 +133,18 @@ __device__ void write_outputs(const AcceptArgs& a, int b, int j, int tok) {
     a.out_tokens[(size_t)b * (K + 1) + i] = i < j ? a.draft[(size_t)b * K + i] : (i == j ? tok : -1);
 }
 
-__global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
+// Kernel 1, one workgroup per (request, vocabulary chunk): accept length,
+// then the residual (or bonus) mass of the chunk.
+__global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs a) {
   const int b = blockIdx.x / a.nchunk;
   const int c = blockIdx.x - b * a.nchunk;
   const int K = a.K, V = a.V;
   const int tid = threadIdx.x, lane = tid & 63;
-  __shared__ int s_j, s_tokerr, s_last;
+  __shared__ int s_j;
   __shared__ double s_wave[4];
-  __shared__ int s_int[2];
 
-  // accept length: lane i runs test i
+  // accept length: lane i runs test i; a ballot of the failures gives the
+  // first reject (an invalid token id counts as a reject and is flagged)
   if (tid < 64) {
     bool fail = false, bad = false;
     if (lane < K) {
@@ -156,42 +161,46 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     }
     const uint64_t fails = __builtin_amdgcn_ballot_w64(fail);
     const int j = fails ? __builtin_ctzll(fails) : K;
+    const uint64_t bads = __builtin_amdgcn_ballot_w64(bad);
     if (lane == 0) {
       s_j = j;
-      s_tokerr = 0;
+      if (c == 0) a.jbuf[b] = j | (((bads >> j) & 1) && j < K ? kJTokenErr : 0);
     }
-    if (lane == j && bad) s_tokerr = 1;
   }
   __syncthreads();
   const int j = s_j;
   const float* prow = a.p + ((size_t)b * (K + 1) + j) * V;
   const float* qrow = j < K ? a.q + ((size_t)b * K + j) * V : nullptr;
-
   const int lo = c * a.chunk, hi = min(V, lo + a.chunk);
   const double part = block_sum(range_mass(prow, qrow, lo, hi), s_wave);
   if (tid == 0) a.partial[(size_t)b * a.nchunk + c] = part;
+}
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[b], 1) == a.nchunk - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // ---- the last workgroup of request b draws the token
+// Kernel 2, one workgroup per request: scan the chunk masses, find the chunk
+// where the running mass passes u_K * S, locate the token inside it, write
+// every output.
+__global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int K = a.K, V = a.V;
+  const int tid = threadIdx.x;
+  __shared__ double s_wave[4];
+  __shared__ int s_int[2];
+  __shared__ double s_tot, s_base;
+  const int jw = a.jbuf[b];
+  const int j = jw & 0xffff;
+  const float* prow = a.p + ((size_t)b * (K + 1) + j) * V;
+  const float* qrow = j < K ? a.q + ((size_t)b * K + j) * V : nullptr;
   const double ub = (double)a.u[(size_t)b * (K + 1) + K];
-  // chunk sums, scanned in chunk order (nchunk <= 256: one per thread)
+  // chunk masses scanned in chunk order (nchunk <= 256: one per thread)
   const double mine = tid < a.nchunk ? a.partial[(size_t)b * a.nchunk + tid] : 0.0;
   const double incl = block_inclusive_scan(mine, s_wave);
-  __shared__ double s_tot;
   if (tid == kAccThreads - 1) s_tot = incl;
   __syncthreads();
   const double S = s_tot;
   int tok = -1;
-  int errs = s_tokerr ? kErrToken : 0;
+  int errs = (jw & kJTokenErr) ? kErrToken : 0;
   if (S > 0.0) {
     const double thr = ub * S;
-    // first chunk whose running mass passes thr (or the last chunk with mass)
     if (tid == 0) {
       s_int[0] = 0x7fffffff;
       s_int[1] = -1;
@@ -201,7 +210,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
     if (tid < a.nchunk && mine > 0.0) atomicMax(&s_int[1], tid);
     __syncthreads();
     const int cstar = s_int[0] != 0x7fffffff ? s_int[0] : s_int[1];
-    __shared__ double s_base;
     if (tid == cstar) s_base = incl - mine;
     __syncthreads();
     const double base = s_base;
@@ -219,10 +227,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_kernel(AcceptArgs a) {
   }
   if (tok < 0) tok = 0;
   write_outputs(a, b, j, tok);
-  if (tid == 0) {
-    if (errs) flag_error(a.err, errs);
-    a.counters[b] = 0;
-  }
+  if (tid == 0 && errs) flag_error(a.err, errs);
 }
 
 // ----------------------------------------------------------------- argmax
@@ -324,7 +329,10 @@ __global__ __launch_bounds__(64) void greedy_commit_kernel(AcceptArgs a) {
 }
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_kernel, dim3(a.bs * a.nchunk), dim3(kAccThreads), 0, stream, a);
+  hipLaunchKernelGGL(accept_partial_kernel, dim3(a.bs * a.nchunk), dim3(kAccThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_select_kernel, dim3(a.bs), dim3(kAccThreads), 0, stream, a);
   return hipGetLastError();
 }
 

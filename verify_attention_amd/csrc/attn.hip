@@ -8,41 +8,41 @@
 // Mask" section of "SGLang strengthens diffusion LLMs: LLaDA 2.0" and in
 // sections 4.3.1 / 4.4.1 of "From DFlash to dLLM Self-Spec (4)".
 //
-// Work decomposition (one workgroup per (request, KV head, split)):
-//   * All g * B query rows that share one KV head (the g query heads of the
-//     GQA group times the B block tokens) form the MFMA N dimension, so each
-//     K/V page is read from HBM once per KV head.
-//   * A row group is 64 rows (4 MFMA tiles of 16); a 4-wave workgroup holds
-//     one row group served by 4 key waves, or two row groups of 2 key waves
-//     each. The key waves of a row group take interleaved 32-key steps of the
-//     split's key range (a flash-decoding style key split inside the
-//     workgroup), so no KV tile is staged or shared through LDS: every wave
-//     loads its own MFMA operands straight from HBM with 16-byte loads and
-//     prefetches the next step into registers. Only the last steps of a
-//     sequence (the block and the ragged end) carry masks and bounds checks.
+// Work decomposition: one 4-wave workgroup per (request, KV head, split).
+//   * All g * B query rows that share a KV head (the GQA group's query heads
+//     times the block tokens) are the MFMA N dimension, so each K/V page is
+//     read from HBM once per KV head. Wave w owns 16 (or 32) of those rows.
+//   * The split's keys stream through in 32-key stages. For each stage the 4
+//     waves together issue the 16-byte loads of every MFMA operand fragment
+//     (each wave a quarter), keep three stages in flight in registers, and
+//     write each fragment to LDS in the lane order its MFMA consumes it, so
+//     every wave then reads whole fragments with conflict-free ds_read_b128.
+//     Three LDS stage buffers, one barrier per stage.
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16
-//     (8 x v_mfma_f32_16x16x4f32 for fp32 inputs). Keys are permuted inside a
-//     32-key step so that the accumulator layout of S^T is directly the B
-//     operand of the PV product and the dim-major V page gives the A operand
-//     as one contiguous 16-byte run: no shuffles between the two products.
+//     (eight v_mfma_f32_16x16x4f32 for fp32 inputs). Keys are permuted inside
+//     a stage so that the accumulator layout of S^T is directly the B operand
+//     of the PV product and the dim-major V page gives the A operand as one
+//     contiguous 16-byte run: no shuffles between the two products.
 //   * Online softmax in fp32 (exp2 domain), row max across the 4 lane groups
 //     via permlane swaps, lazy rescaling (the reference max only moves when a
-//     new max exceeds it by 2^8), masks applied only on steps that reach the
-//     block.
-//   * The 4 waves' partial states are merged through LDS in a fixed order;
-//     with several splits per (request, KV head) the workgroup stores its
-//     partial state and the last workgroup to finish (device-scope counter)
-//     merges all splits: one kernel launch per call.
+//     new max exceeds it by 2^8), masks applied only on stages that reach the
+//     block; keys past the sequence end are zeroed by the loading wave.
+//   * With several splits per (request, KV head) each workgroup stores its
+//     partial state and a second, small kernel merges the splits (a kernel
+//     boundary instead of device-scope fences, which on gfx950 write back and
+//     invalidate the L2 of the issuing XCD).
 #include "kernels.h"
 
 namespace specattn {
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;   // finite start value for running maxima
 constexpr float kRescale = 8.0f;      // lazy rescale threshold, log2 units
-constexpr int kStep = 32;             // keys per step
-constexpr int kRowsPerGroup = 64;
+constexpr int kStep = 32;             // keys per stage
+constexpr int kWaves = 4;             // waves per workgroup
+constexpr int kPageWin = 1024;        // page ids staged in LDS per window
+
+typedef int intx4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- fragments
 // A fragment is the 8 consecutive reduction-dimension elements one lane feeds
@@ -97,82 +97,128 @@ __device__ __forceinline__ bool block_visible(int mode, int i, int jb, int nc) {
   return mode == 0 || jb <= i || (mode == 2 && i >= nc);
 }
 
-// Operand registers of one 32-key step.
+// Fragments of one stage as the MFMAs consume them.
 template <typename T, int D>
 struct StepFrags {
   typename Frag<T>::vec k[2][D / 32];  // A operands of S^T = K Q^T, two 16-key tiles
   typename Frag<T>::vec v[D / 16];     // A operands of O^T += V^T P^T, one per 16-dim tile
 };
 
-// Per-wave geometry of the current (request, KV head).
-template <typename T>
-struct KvView {
-  const T* kbase;        // k_pool + kvh * P * D
-  const T* vbase;        // v_pool + kvh * P * D
-  const int32_t* ptab;   // page_table row of the request
-  size_t page_stride;    // elements per physical page (all KV heads)
+// A stage is NP pieces of 1 KB (64 lanes x 16 bytes): the K fragments first,
+// then the V fragments; a fragment is H = sizeof(T)/2 pieces. Wave w loads
+// K pieces w, w+4, ... and V pieces w, w+4, ... of every stage.
+template <typename T, int D>
+struct StageShape {
+  static constexpr int H = sizeof(T) / 2;
+  static constexpr int KC = D / 32;           // K chunks along D per key tile
+  static constexpr int NKP = 2 * KC * H;      // K pieces
+  static constexpr int NVP = (D / 16) * H;    // V pieces
+  static constexpr int KPW = NKP / kWaves;    // K pieces per wave
+  static constexpr int VPW = NVP / kWaves;    // V pieces per wave
+  static constexpr int PW = KPW + VPW;
+  static constexpr int BYTES = (NKP + NVP) * 1024;
+  typedef intx4 Regs[PW];  // one stage's pieces held by one wave
+  static_assert(NKP % kWaves == 0 && NVP % kWaves == 0, "pieces must split over 4 waves");
 };
 
-// Physical pages of the (at most two) pages of the step at key0; ids outside
-// the pool are flagged and replaced by page 0.
-template <typename T>
-__device__ __forceinline__ void step_pages(const KvView<T>& kv, const AttnArgs& a, int key0,
-                                           bool hi_valid, int& lo, int& hi) {
-  lo = kv.ptab[key0 >> a.p_shift];
-  hi = lo;
-  if (a.P == 16 && hi_valid) hi = kv.ptab[(key0 >> a.p_shift) + 1];
-  if ((unsigned)lo >= (unsigned)a.num_pages || (unsigned)hi >= (unsigned)a.num_pages) {
-    if ((threadIdx.x & 63) == 0) flag_error(a.err, kErrSlot);
-    if ((unsigned)lo >= (unsigned)a.num_pages) lo = 0;
-    if ((unsigned)hi >= (unsigned)a.num_pages) hi = 0;
-  }
-}
+struct KvView {
+  const char* kbase;    // k_pool + kvh * P * D elements
+  const char* vbase;    // v_pool + kvh * P * D elements
+  size_t page_bytes;    // bytes per physical page (all KV heads)
+};
 
-// Loads the K and V operands of the step starting at key0. Lane (n, grp):
-//   K tile T row n  <- key key0 + 8*(n/4) + 4*T + n%4, dims 32c + 8*grp .. +7
-//   V tile dt row n <- dim 16*dt + n, keys key0 + 8*grp .. +7
-// TAIL: keys at or past n_keys are read from a valid slot of the step and
+// Loads this wave's pieces of the stage at key0 (pages page_lo for keys 0..15
+// or all keys when P = 32, page_hi for keys 16..31). Lane (n, grp):
+//   K piece (tile T, chunk c, half h): key key0 + 8*(n/4) + 4*T + n%4,
+//     dims 32c + 8*grp + 4h (bf16: h = 0, 8 dims; fp32: 4 dims per half)
+//   V piece (dim tile dt, half h): dim 16*dt + n, keys key0 + 8*grp + 4h ...
+// TAIL: keys at or past n_keys are read from the stage's first slot and
 // zeroed (their own slots may hold anything, or not exist).
 template <typename T, int D, bool TAIL>
-__device__ __forceinline__ void load_step(StepFrags<T, D>& f, const KvView<T>& kv,
-                                          const AttnArgs& a, int key0, int n_keys, int lane) {
+__device__ __forceinline__ void load_stage(typename StageShape<T, D>::Regs& r, const KvView& kv,
+                                           int P, int key0, int page_lo, int page_hi,
+                                           int n_keys, int wave, int lane) {
+  using SS = StageShape<T, D>;
+  constexpr int E = 16 / sizeof(T);  // elements per piece
   const int n = lane & 15, grp = lane >> 4;
-  const int P = a.P;
-  int page_lo, page_hi;
-  step_pages(kv, a, key0, !TAIL || key0 + 16 < n_keys, page_lo, page_hi);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int kk = 8 * (n >> 2) + 4 * t + (n & 3);  // key inside the step
+  for (int j = 0; j < SS::KPW; ++j) {
+    const int piece = wave + kWaves * j;
+    const int f = piece / SS::H, h = piece % SS::H;
+    const int t2 = f / SS::KC, c = f % SS::KC;
+    const int kk = 8 * (n >> 2) + 4 * t2 + (n & 3);
     const bool ok = !TAIL || key0 + kk < n_keys;
     const int kq = ok ? kk : 0;
     const int page = (P == 16 && kq >= 16) ? page_hi : page_lo;
-    const T* src = kv.kbase + page * kv.page_stride + (size_t)((key0 + kq) & (P - 1)) * D + 8 * grp;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      f.k[t][c] = Frag<T>::load(src + 32 * c);
-      if (TAIL && !ok) f.k[t][c] = Frag<T>::zero();
-    }
+    const size_t off = (size_t)page * kv.page_bytes +
+                       (size_t)(((key0 + kq) & (P - 1)) * D + 32 * c + 8 * grp + 4 * h) * sizeof(T);
+    r[j] = *reinterpret_cast<const intx4*>(kv.kbase + off);
+    if (TAIL && !ok) r[j] = intx4{0, 0, 0, 0};
   }
-  {
-    const int kk = 8 * grp;
+#pragma unroll
+  for (int j = 0; j < SS::VPW; ++j) {
+    const int piece = wave + kWaves * j;
+    const int dt = piece / SS::H, h = piece % SS::H;
+    const int kk = 8 * grp + 4 * h;
     const bool ok = !TAIL || key0 + kk < n_keys;
     const int kq = ok ? kk : 0;
     const int page = (P == 16 && kq >= 16) ? page_hi : page_lo;
-    const T* src = kv.vbase + page * kv.page_stride + (size_t)n * P + ((key0 + kq) & (P - 1));
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = Frag<T>::load(src + (size_t)16 * dt * P);
+    const size_t off = (size_t)page * kv.page_bytes +
+                       (size_t)((16 * dt + n) * P + ((key0 + kq) & (P - 1))) * sizeof(T);
+    intx4 x = *reinterpret_cast<const intx4*>(kv.vbase + off);
     if (TAIL) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (key0 + kk + j >= n_keys) {
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) Frag<T>::clear(f.v[dt], j);
+      for (int e = 0; e < E; ++e) {
+        if (key0 + kk + e >= n_keys) {
+          if (sizeof(T) == 4) x[e] = 0;
+          else x[e / 2] &= (e & 1) ? 0x0000ffff : 0xffff0000;
         }
+      }
     }
+    r[SS::KPW + j] = x;
   }
 }
 
-// One 32-key step: S^T = K Q^T, (mask), online softmax update, O^T += V^T P^T.
+template <typename T, int D>
+__device__ __forceinline__ void store_stage(const typename StageShape<T, D>::Regs& r, char* buf,
+                                            int wave, int lane) {
+  using SS = StageShape<T, D>;
+#pragma unroll
+  for (int j = 0; j < SS::KPW; ++j)
+    *reinterpret_cast<intx4*>(buf + (wave + kWaves * j) * 1024 + lane * 16) = r[j];
+#pragma unroll
+  for (int j = 0; j < SS::VPW; ++j)
+    *reinterpret_cast<intx4*>(buf + (SS::NKP + wave + kWaves * j) * 1024 + lane * 16) = r[SS::KPW + j];
+}
+
+// Fragment starting at piece p0: one 16-byte piece (bf16) or two (fp32).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::vec read_frag(const char* buf, int p0, int lane);
+
+template <>
+__device__ __forceinline__ bf16x8 read_frag<__bf16>(const char* buf, int p0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(buf + p0 * 1024 + lane * 16);
+}
+
+template <>
+__device__ __forceinline__ floatx8 read_frag<float>(const char* buf, int p0, int lane) {
+  const floatx4 lo = *reinterpret_cast<const floatx4*>(buf + p0 * 1024 + lane * 16);
+  const floatx4 hi = *reinterpret_cast<const floatx4*>(buf + (p0 + 1) * 1024 + lane * 16);
+  return floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void read_stage(StepFrags<T, D>& f, const char* buf, int lane) {
+  using SS = StageShape<T, D>;
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+    for (int c = 0; c < SS::KC; ++c) f.k[t2][c] = read_frag<T>(buf, (t2 * SS::KC + c) * SS::H, lane);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = read_frag<T>(buf, SS::NKP + dt * SS::H, lane);
+}
+
+// One stage: S^T = K Q^T, (mask), online softmax update, O^T += V^T P^T.
 // s[T][t][j] is key key0 + 8*grp + 4*T + j against row 16t + n of the wave;
 // softmax runs in the exp2 domain with the scale folded into the exponent.
 template <typename T, int D, int MT, bool MASKED>
@@ -247,17 +293,52 @@ __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
     for (int t = 0; t < MT; ++t) acc[dt][t] = Frag<T>::mma(f.v[dt], pf[t], acc[dt][t]);
 }
 
-// RG row groups of 64 rows, each served by 4 / RG key waves: the workgroup is
-// always 4 waves, so a wave may use the whole 512-entry register file.
-template <typename T, int D, int MT, int RG>
-__global__ __launch_bounds__(kWave * 4, 1) void block_attn_kernel(AttnArgs a) {
-  typedef typename Frag<T>::vec vec;
-  constexpr int KW = 4 / RG;
+template <typename T, int D, int MT>
+struct WaveState {
+  typename Frag<T>::vec qf[MT][D / 32];
+  floatx4 acc[D / 16][MT];
+  float m_run[MT], l_run[MT];
+  int blk_row[MT];
+};
+
+// Consumes stage key0 from LDS buffer buf.
+template <typename T, int D, int MT>
+__device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, const char* buf, const AttnArgs& a,
+                                        int key0, int L, int n_keys, int nc, int lane,
+                                        bool has_rows) {
+  if (!has_rows) return;
+  StepFrags<T, D> f;
+  read_stage<T, D>(f, buf, lane);
+  if (key0 + kStep > L)
+    compute_step<T, D, MT, true>(f, ws.qf, ws.acc, ws.m_run, ws.l_run, ws.blk_row, a, key0, L,
+                                 n_keys, nc, lane >> 4);
+  else
+    compute_step<T, D, MT, false>(f, ws.qf, ws.acc, ws.m_run, ws.l_run, ws.blk_row, a, key0, L,
+                                  n_keys, nc, lane >> 4);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void issue(typename StageShape<T, D>::Regs& r, const KvView& kv,
+                                      const AttnArgs& a, const int* s_pages, int pg0, int key0,
+                                      int n_keys, int wave, int lane) {
+  const int idx = (key0 >> a.p_shift) - pg0;
+  const int page_lo = s_pages[idx];
+  const int page_hi = (a.P == 16 && key0 + 16 < n_keys) ? s_pages[idx + 1] : page_lo;
+  if (key0 + kStep <= n_keys)
+    load_stage<T, D, false>(r, kv, a.P, key0, page_lo, page_hi, n_keys, wave, lane);
+  else
+    load_stage<T, D, true>(r, kv, a.P, key0, page_lo, page_hi, n_keys, wave, lane);
+}
+
+template <typename T, int D, int MT>
+__global__ __launch_bounds__(kWave * kWaves, (MT == 1 ? 2 : 1)) void block_attn_kernel(AttnArgs a) {
+  using SS = StageShape<T, D>;
+  __shared__ __attribute__((aligned(16))) char s_buf[3][SS::BYTES];
+  __shared__ int s_pages[kPageWin];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rg = wave / KW;   // row group
-  const int kw = wave % KW;   // key wave inside the row group
   const int n = lane & 15, grp = lane >> 4;
 
   const int unit = blockIdx.x / a.splits;
@@ -276,166 +357,119 @@ __global__ __launch_bounds__(kWave * 4, 1) void block_attn_kernel(AttnArgs a) {
   const int n_steps = (n_keys + kStep - 1) / kStep;
   const int s_lo = split * a.steps_per_split;
   const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
-  const int s_full = min(s_hi, L / kStep);  // steps [s_lo, s_full) hold context keys only
 
-  KvView<T> kv;
-  kv.kbase = reinterpret_cast<const T*>(a.k) + (size_t)kvh * a.P * D;
-  kv.vbase = reinterpret_cast<const T*>(a.v) + (size_t)kvh * a.P * D;
-  kv.ptab = a.page_table + (size_t)b * a.max_pages;
-  kv.page_stride = (size_t)a.P * D * a.Hkv;
+  KvView kv;
+  kv.kbase = reinterpret_cast<const char*>(a.k) + (size_t)kvh * a.P * D * sizeof(T);
+  kv.vbase = reinterpret_cast<const char*>(a.v) + (size_t)kvh * a.P * D * sizeof(T);
+  kv.page_bytes = (size_t)a.P * D * a.Hkv * sizeof(T);
+  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
 
-  // ---- Q^T operands for this wave's 16*MT rows: lane (n, grp) holds row
-  // 16t + n, dims 32c + 8*grp .. +7. Row r of the group is block token r / g,
-  // query head kvh * g + r % g.
+  // ---- Q^T operands of this wave's rows: lane (n, grp) holds row 16t + n,
+  // dims 32c + 8*grp .. +7. Row r of the group is block token r / g, query
+  // head kvh * g + r % g.
+  WaveState<T, D, MT> ws;
+  const int row0 = wave * 16 * MT;
+  const bool has_rows = row0 < a.M;
   const T* qg = reinterpret_cast<const T*>(a.q);
-  vec qf[MT][D / 32];
-  int blk_row[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const int r = rg * kRowsPerGroup + 16 * t + n;
-    const int i = r / a.g, hl = r - i * a.g;
-    blk_row[t] = i;
+    const int r = row0 + 16 * t + n;
+    ws.blk_row[t] = r / a.g;
     const int rr = r < a.M ? r : 0;
     const int ii = rr / a.g, hh = rr - ii * a.g;
     const T* src = qg + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hh) * D + 8 * grp;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      qf[t][c] = Frag<T>::load(src + 32 * c);
-      if (r >= a.M) qf[t][c] = Frag<T>::zero();
+      ws.qf[t][c] = Frag<T>::load(src + 32 * c);
+      if (r >= a.M) ws.qf[t][c] = Frag<T>::zero();
     }
-    (void)hl;
+    ws.m_run[t] = kNegBig;
+    ws.l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) ws.acc[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  floatx4 acc[D / 16][MT];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run[MT], l_run[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    m_run[t] = kNegBig;
-    l_run[t] = 0.f;
-  }
-
-  // ---- context steps: no mask, no bounds; two per trip so the prefetch
-  // buffers alternate without register copies
-  StepFrags<T, D> fa, fb;
-  int st = s_lo + kw;
-  if (st < s_full) load_step<T, D, false>(fa, kv, a, st * kStep, n_keys, lane);
-  for (; st < s_full; st += 2 * KW) {
-    if (st + KW < s_full) load_step<T, D, false>(fb, kv, a, (st + KW) * kStep, n_keys, lane);
-    compute_step<T, D, MT, false>(fa, qf, acc, m_run, l_run, blk_row, a, st * kStep, L, n_keys,
-                                  nc, grp);
-    if (st + KW >= s_full) {
-      st += KW;
-      break;
-    }
-    if (st + 2 * KW < s_full) load_step<T, D, false>(fa, kv, a, (st + 2 * KW) * kStep, n_keys, lane);
-    compute_step<T, D, MT, false>(fb, qf, acc, m_run, l_run, blk_row, a, (st + KW) * kStep, L,
-                                  n_keys, nc, grp);
-  }
-  // ---- steps that reach the block or the end of the sequence
-  for (; st < s_hi; st += KW) {
-    load_step<T, D, true>(fa, kv, a, st * kStep, n_keys, lane);
-    compute_step<T, D, MT, true>(fa, qf, acc, m_run, l_run, blk_row, a, st * kStep, L, n_keys,
-                                 nc, grp);
-  }
-
-  // ---- merge the key waves of each row group through LDS (fixed order)
-  constexpr int kOStride = D + 4;  // padded row stride (floats)
-  __shared__ float s_ml[RG][KW][kRowsPerGroup][2];
-  __shared__ float s_o[RG][kRowsPerGroup * kOStride];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    l_run[t] = group_sum4(l_run[t]);
-    if (grp == 0) {
-      s_ml[rg][kw][16 * t + n][0] = m_run[t];
-      s_ml[rg][kw][16 * t + n][1] = l_run[t];
-    }
-  }
-  __syncthreads();
-  float m_tot[MT], l_tot[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    float mm = kNegBig;
-#pragma unroll
-    for (int w = 0; w < KW; ++w) mm = fmaxf(mm, s_ml[rg][w][16 * t + n][0]);
-    float ll = 0.f;
-#pragma unroll
-    for (int w = 0; w < KW; ++w)
-      ll += s_ml[rg][w][16 * t + n][1] * __builtin_amdgcn_exp2f(s_ml[rg][w][16 * t + n][0] - mm);
-    m_tot[t] = mm;
-    l_tot[t] = ll;
-    const float f = __builtin_amdgcn_exp2f(m_run[t] - mm);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt][t] *= f;
-  }
-  float* so = s_o[rg];
-#pragma unroll
-  for (int w = KW - 1; w >= 1; --w) {
-    if (kw == w) {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          floatx4* p = reinterpret_cast<floatx4*>(so + (16 * t + n) * kOStride + 16 * dt + 4 * grp);
-          if (w < KW - 1) acc[dt][t] += *p;
-          *p = acc[dt][t];
-        }
+  // ---- stream the split's stages, one window of staged page ids at a time
+  const int win_steps = kPageWin * a.P / kStep;
+  for (int w0 = s_lo; w0 < s_hi; w0 += win_steps) {
+    const int w1 = min(s_hi, w0 + win_steps);
+    const int pg0 = (w0 * kStep) >> a.p_shift;
+    const int npg = ((min(w1 * kStep, n_keys) - 1) >> a.p_shift) - pg0 + 1;
+    __syncthreads();  // the previous window is fully consumed
+    for (int x = tid; x < npg; x += kWave * kWaves) {
+      const int p = ptab[pg0 + x];
+      const bool bad = (unsigned)p >= (unsigned)a.num_pages;
+      if (bad) flag_error(a.err, kErrSlot);
+      s_pages[x] = bad ? 0 : p;
     }
     __syncthreads();
+
+    const int ns = w1 - w0;
+    typename SS::Regs r0, r1, r2;
+    issue<T, D>(r0, kv, a, s_pages, pg0, w0 * kStep, n_keys, wave, lane);
+    if (ns > 1) issue<T, D>(r1, kv, a, s_pages, pg0, (w0 + 1) * kStep, n_keys, wave, lane);
+    if (ns > 2) issue<T, D>(r2, kv, a, s_pages, pg0, (w0 + 2) * kStep, n_keys, wave, lane);
+    store_stage<T, D>(r0, s_buf[0], wave, lane);
+    __syncthreads();
+    // three stages per trip: register set and LDS buffer indices stay static
+    for (int t = 0; t < ns; t += 3) {
+      if (t + 3 < ns) issue<T, D>(r0, kv, a, s_pages, pg0, (w0 + t + 3) * kStep, n_keys, wave, lane);
+      consume<T, D, MT>(ws, s_buf[0], a, (w0 + t) * kStep, L, n_keys, nc, lane, has_rows);
+      if (t + 1 < ns) store_stage<T, D>(r1, s_buf[1], wave, lane);
+      __syncthreads();
+      if (t + 1 >= ns) break;
+      if (t + 4 < ns) issue<T, D>(r1, kv, a, s_pages, pg0, (w0 + t + 4) * kStep, n_keys, wave, lane);
+      consume<T, D, MT>(ws, s_buf[1], a, (w0 + t + 1) * kStep, L, n_keys, nc, lane, has_rows);
+      if (t + 2 < ns) store_stage<T, D>(r2, s_buf[2], wave, lane);
+      __syncthreads();
+      if (t + 2 >= ns) break;
+      if (t + 5 < ns) issue<T, D>(r2, kv, a, s_pages, pg0, (w0 + t + 5) * kStep, n_keys, wave, lane);
+      consume<T, D, MT>(ws, s_buf[2], a, (w0 + t + 2) * kStep, L, n_keys, nc, lane, has_rows);
+      if (t + 3 < ns) store_stage<T, D>(r0, s_buf[0], wave, lane);
+      __syncthreads();
+    }
   }
 
+  // ---- this wave's rows: normalise and write, or store the split's partial state
+  if (!has_rows) return;
   const bool single = a.splits == 1;
-  if (kw == 0) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int r = rg * kRowsPerGroup + 16 * t + n;
-      if (r >= a.M) continue;
-      if (KW > 1) {
+  for (int t = 0; t < MT; ++t) {
+    const float l_tot = group_sum4(ws.l_run[t]);
+    const int r = row0 + 16 * t + n;
+    if (r >= a.M) continue;
+    const int i = r / a.g, hl = r - i * a.g;
+    const size_t orow = (size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl;
+    if (single) {
+      const float inv = 1.0f / l_tot;
+      T* dst = reinterpret_cast<T*>(a.o) + orow * D + 4 * grp;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-          acc[dt][t] += *reinterpret_cast<floatx4*>(so + (16 * t + n) * kOStride + 16 * dt + 4 * grp);
-      }
-      const int i = r / a.g, hl = r - i * a.g;
-      const size_t orow = (size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl;
-      if (single) {
-        const float inv = 1.0f / l_tot[t];
-        T* dst = reinterpret_cast<T*>(a.o) + orow * D + 4 * grp;
+      for (int dt = 0; dt < D / 16; ++dt) Frag<T>::store4(dst + 16 * dt, ws.acc[dt][t] * inv);
+      if (a.lse && grp == 0) a.lse[orow] = (ws.m_run[t] + __log2f(l_tot)) * kLn2;
+    } else {
+      const size_t prow = ((size_t)blockIdx.x * a.M + r);
+      float* dst = a.part_o + prow * D + 4 * grp;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) Frag<T>::store4(dst + 16 * dt, acc[dt][t] * inv);
-        if (a.lse && grp == 0) a.lse[orow] = (m_tot[t] + __log2f(l_tot[t])) * kLn2;
-      } else {
-        const size_t prow = ((size_t)blockIdx.x * a.M + r);
-        float* dst = a.part_o + prow * D + 4 * grp;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(dst + 16 * dt) = acc[dt][t];
-        if (grp == 0) {
-          a.part_ml[prow * 2 + 0] = m_tot[t];
-          a.part_ml[prow * 2 + 1] = l_tot[t];
-        }
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(dst + 16 * dt) = ws.acc[dt][t];
+      if (grp == 0) {
+        a.part_ml[prow * 2 + 0] = ws.m_run[t];
+        a.part_ml[prow * 2 + 1] = l_tot;
       }
     }
   }
-  if (single) return;
+}
 
-  // ---- split-KV merge by the last workgroup of this (request, KV head)
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.counters[unit], 1);
-    s_last = prev == a.splits - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // per-row merge weights in LDS (reuses s_o): w[r][s], then 1/L per row
-  float* wts = &s_o[0][0];
+// Split-KV merge: O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^(m_s - max m),
+// one workgroup per (request, KV head), a separate launch after the splits.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
+  const int unit = blockIdx.x;
+  const int b = unit / a.Hkv;
+  const int kvh = unit - b * a.Hkv;
   const int S = a.splits;
   const size_t part0 = (size_t)unit * S;
-  for (int r = tid; r < a.M; r += blockDim.x) {
+  __shared__ float wts[128 * 65];  // M <= 128 rows x (splits <= 64, + 1/L)
+  for (int r = threadIdx.x; r < a.M; r += blockDim.x) {
     float mm = kNegBig;
     for (int s2 = 0; s2 < S; ++s2) mm = fmaxf(mm, a.part_ml[((part0 + s2) * a.M + r) * 2]);
     float ll = 0.f;
@@ -453,7 +487,7 @@ __global__ __launch_bounds__(kWave * 4, 1) void block_attn_kernel(AttnArgs a) {
   }
   __syncthreads();
   const int n4 = a.M * (D / 4);
-  for (int e = tid; e < n4; e += blockDim.x) {
+  for (int e = threadIdx.x; e < n4; e += blockDim.x) {
     const int r = e / (D / 4), d4 = e - r * (D / 4);
     floatx4 sum = {0.f, 0.f, 0.f, 0.f};
     for (int s2 = 0; s2 < S; ++s2)
@@ -464,27 +498,19 @@ __global__ __launch_bounds__(kWave * 4, 1) void block_attn_kernel(AttnArgs a) {
     T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl) * D + 4 * d4;
     Frag<T>::store4(dst, sum);
   }
-  if (tid == 0) a.counters[unit] = 0;
 }
 
 // ------------------------------------------------------------------ launch
 template <typename T, int D>
 static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t stream) {
-  const int rows_wave = a.M > kRowsPerGroup ? kRowsPerGroup : a.M;
-  const int mt = (rows_wave + 15) / 16;
-  const int rg = (a.M + kRowsPerGroup - 1) / kRowsPerGroup;
-  dim3 grid(total_blocks);
-  if (rg == 2) {
-    hipLaunchKernelGGL((block_attn_kernel<T, D, 4, 2>), grid, dim3(kWave * 4), 0, stream, a);
-  } else {
-    dim3 block(kWave * 4);
-    switch (mt) {
-      case 1: hipLaunchKernelGGL((block_attn_kernel<T, D, 1, 1>), grid, block, 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((block_attn_kernel<T, D, 2, 1>), grid, block, 0, stream, a); break;
-      case 3: hipLaunchKernelGGL((block_attn_kernel<T, D, 3, 1>), grid, block, 0, stream, a); break;
-      default: hipLaunchKernelGGL((block_attn_kernel<T, D, 4, 1>), grid, block, 0, stream, a); break;
-    }
-  }
+  const dim3 grid(total_blocks), block(kWave * kWaves);
+  if (a.M > 64)
+    hipLaunchKernelGGL((block_attn_kernel<T, D, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((block_attn_kernel<T, D, 1>), grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL((block_attn_combine_kernel<T, D>), dim3(a.bs * a.Hkv), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

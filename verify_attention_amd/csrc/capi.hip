@@ -38,12 +38,12 @@ int env_splits() {
 
 struct AttnPlan {
   int M = 0, units = 0, splits = 1, steps_per_split = 1;
-  size_t off_counters = 0, off_ml = 0, off_o = 0, ws_bytes = 0;
+  size_t off_ml = 0, off_o = 0, ws_bytes = 0;
 };
 
-// Splits per (request, KV head): enough workgroups to cover the chip when the
-// batch has few (request, KV head) units, while every wave keeps several
-// 32-key steps. A split runs 4 key waves, so 16 steps = 4 per wave minimum.
+// Splits per (request, KV head): enough workgroups for two per CU when the
+// batch has few (request, KV head) units, while every split keeps at least
+// 8 stages of 32 keys for its pipeline.
 AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   AttnPlan p;
   p.M = (Hq / Hkv) * B;
@@ -51,16 +51,15 @@ AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   const int max_steps = std::max(1, (max_kv_len + kStepKeys - 1) / kStepKeys);
   int splits = env_splits();
   if (splits <= 0) {
-    splits = (kCUs + p.units - 1) / p.units;
-    splits = std::min(splits, std::max(1, max_steps / 16));
+    splits = (2 * kCUs + p.units - 1) / p.units;
+    splits = std::min(splits, std::max(1, max_steps / 8));
   }
   splits = std::max(1, std::min(splits, std::min(kMaxSplits, max_steps)));
   p.steps_per_split = (max_steps + splits - 1) / splits;
   p.splits = (max_steps + p.steps_per_split - 1) / p.steps_per_split;
   if (p.splits > 1) {
-    p.off_counters = 0;
-    p.off_ml = align_up((size_t)p.units * sizeof(int32_t), 256);
-    p.off_o = p.off_ml + align_up((size_t)p.units * p.splits * p.M * 2 * sizeof(float), 256);
+    p.off_ml = 0;
+    p.off_o = align_up((size_t)p.units * p.splits * p.M * 2 * sizeof(float), 256);
     p.ws_bytes = p.off_o + (size_t)p.units * p.splits * p.M * D * sizeof(float);
   }
   return p;
@@ -68,7 +67,7 @@ AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
 
 struct AccPlan {
   int nchunk = 1, chunk = 0;
-  size_t off_counters = 0, off_partial = 0, off_ids = 0, ws_bytes = 0;
+  size_t off_jbuf = 0, off_partial = 0, off_ids = 0, ws_bytes = 0;
 };
 
 // Vocabulary chunks per request: about 2048 workgroups over the batch, chunks a
@@ -85,7 +84,7 @@ AccPlan plan_accept(int bs, int K, int V, int greedy) {
   chunk = (int)align_up((size_t)chunk, 1024);
   p.chunk = chunk;
   p.nchunk = (V + chunk - 1) / chunk;
-  p.off_counters = 0;
+  p.off_jbuf = 0;
   p.off_partial = align_up((size_t)bs * sizeof(int32_t), 256);
   p.ws_bytes = p.off_partial + (size_t)bs * p.nchunk * sizeof(double);
   return p;
@@ -172,7 +171,6 @@ SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req,
   a.o = o;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  a.counters = plan.splits > 1 ? reinterpret_cast<int32_t*>(ws + plan.off_counters) : nullptr;
   a.part_ml = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.off_ml) : nullptr;
   a.part_o = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.off_o) : nullptr;
   a.err = err_flags;
@@ -243,11 +241,11 @@ SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (greedy) {
     a.partial = nullptr;
-    a.counters = nullptr;
+    a.jbuf = nullptr;
     a.greedy_ids = reinterpret_cast<int32_t*>(ws + plan.off_ids);
     return hip_status(launch_greedy_accept(a, s));
   }
-  a.counters = reinterpret_cast<int32_t*>(ws + plan.off_counters);
+  a.jbuf = reinterpret_cast<int32_t*>(ws + plan.off_jbuf);
   a.partial = reinterpret_cast<double*>(ws + plan.off_partial);
   a.greedy_ids = nullptr;
   return hip_status(launch_accept(a, s));

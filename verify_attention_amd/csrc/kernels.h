@@ -16,7 +16,6 @@ struct AttnArgs {
   float* lse;
   float* part_o;      // [units * splits][M][D] split partial outputs (unnormalised)
   float* part_ml;     // [units * splits][M][2] split partial (max, sum), log2 domain
-  int32_t* counters;  // [units] splits finished so far; reset by the merging workgroup
   int32_t* err;
   int bs, B, Hq, Hkv, g, M;  // M = g * B query rows per KV head
   int P, p_shift, max_pages, num_pages;
@@ -59,7 +58,7 @@ struct AcceptArgs {
   int32_t* new_seq_lens;
   int32_t* err;
   double* partial;     // [bs][nchunk] residual mass per vocabulary chunk
-  int32_t* counters;   // [bs] chunks finished so far; reset by the sampling workgroup
+  int32_t* jbuf;       // [bs] accept length (| token-error flag) from the first kernel
   int32_t* greedy_ids; // [bs][K+1] row argmax (greedy mode)
   int bs, K, V, nchunk, chunk;
 };
