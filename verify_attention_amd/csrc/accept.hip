@@ -8,12 +8,12 @@
 //     wave: lane i gathers p[i, d_i], q[i, d_i], u_i and tests u*q < p in
 //     double; a ballot of the failures gives the first reject;
 //   * the residual row r = max(p_j - q_j, 0) (or the bonus row p_K) is split
-//     into vocabulary chunks, one workgroup per (request, chunk), each
-//     summing its chunk in double;
-//   * a second kernel, one workgroup per request, scans the chunk sums, finds
-//     the chunk where the running mass passes u_K * S, re-reads only that
-//     chunk to locate the token, and writes every output (a kernel boundary
-//     orders the two phases; no device-scope fences or counters).
+//     into vocabulary chunks, one workgroup per (request, chunk); each wave
+//     sums 256-entry sub-blocks in double and stores one mass per sub-block;
+//   * a second kernel, one workgroup per request, scans the sub-block masses,
+//     finds the sub-block where the running mass passes u_K * S, re-reads only
+//     that sub-block to locate the token, and writes every output (a kernel
+//     boundary orders the two phases; no device-scope fences or counters).
 // Only the residual (or bonus) row pair is streamed from HBM; the other target
 // rows are touched at one gathered element each.
 #include "kernels.h"
@@ -23,16 +23,30 @@ namespace specattn {
 constexpr int kAccThreads = 256;
 constexpr int kJTokenErr = 1 << 16;  // jbuf flag: the first reject was an invalid token id
 
-// ------------------------------------------------------------ block scans
-// Inclusive prefix sum of one double per thread over a 256-thread block, in a
-// fixed order (wave shuffles, then the wave totals through LDS).
-__device__ __forceinline__ double block_inclusive_scan(double x, double* s_wave) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kSub = 256;  // vocabulary entries per sub-block (one wave, 4 per lane)
+
+// ------------------------------------------------------------ reductions
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ double wave_inclusive_scan(double x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const double y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
+  return x;
+}
+
+// Inclusive prefix sum of one double per thread over a 256-thread block, in a
+// fixed order (wave scans, then the wave totals through LDS).
+__device__ __forceinline__ double block_inclusive_scan(double x, double* s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_inclusive_scan(x);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   double base = 0.0;
@@ -41,84 +55,38 @@ __device__ __forceinline__ double block_inclusive_scan(double x, double* s_wave)
   return base + x;
 }
 
-__device__ __forceinline__ double block_sum(double x, double* s_wave) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  if (lane == 0) s_wave[wave] = x;
-  __syncthreads();
-  const double t = (s_wave[0] + s_wave[1]) + (s_wave[2] + s_wave[3]);
-  __syncthreads();
-  return t;
-}
-
-// residual entry in double: max(p - q, 0), or p alone when q is absent
-__device__ __forceinline__ double resid(float p, const float* q, size_t i) {
-  if (!q) return (double)p;
-  const double r = (double)p - (double)q[i];
-  return r > 0.0 ? r : 0.0;
-}
-
-// Sum of r over [lo, hi) of a row, one double per thread, vectorised when the
-// row pointers are 16-byte aligned.
-__device__ double range_mass(const float* p, const float* q, int lo, int hi) {
-  double s = 0.0;
-  const bool vec = ((reinterpret_cast<uintptr_t>(p + lo) | reinterpret_cast<uintptr_t>(q ? q + lo : p)) & 15) == 0;
-  int t = lo;
-  if (vec) {
-    const int n4 = (hi - lo) / 4;
-    const float4* p4 = reinterpret_cast<const float4*>(p + lo);
-    const float4* q4 = q ? reinterpret_cast<const float4*>(q + lo) : nullptr;
-#pragma unroll 4
-    for (int e = threadIdx.x; e < n4; e += kAccThreads) {
-      const float4 pv = p4[e];
-      if (q4) {
-        const float4 qv = q4[e];
-        const double r0 = (double)pv.x - (double)qv.x, r1 = (double)pv.y - (double)qv.y;
-        const double r2 = (double)pv.z - (double)qv.z, r3 = (double)pv.w - (double)qv.w;
-        s += (r0 > 0.0 ? r0 : 0.0) + (r1 > 0.0 ? r1 : 0.0) + ((r2 > 0.0 ? r2 : 0.0) + (r3 > 0.0 ? r3 : 0.0));
-      } else {
-        s += ((double)pv.x + (double)pv.y) + ((double)pv.z + (double)pv.w);
-      }
+// The 4 residual entries r_v (v = e .. e+3) of one lane, in double:
+// max(p - q, 0), or p alone when q is absent; entries past V are 0.
+__device__ __forceinline__ void resid4(const float* p, const float* q, int e, int V, bool vec,
+                                       double (&r)[4]) {
+  float pv[4], qv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (vec && e + 4 <= V) {
+    const float4 a = *reinterpret_cast<const float4*>(p + e);
+    pv[0] = a.x; pv[1] = a.y; pv[2] = a.z; pv[3] = a.w;
+    if (q) {
+      const float4 b = *reinterpret_cast<const float4*>(q + e);
+      qv[0] = b.x; qv[1] = b.y; qv[2] = b.z; qv[3] = b.w;
     }
-    t = lo + 4 * n4;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = e + i < V ? p[e + i] : 0.f;
+      if (q) qv[i] = e + i < V ? q[e + i] : 0.f;
+    }
   }
-  for (int e = t + threadIdx.x; e < hi; e += kAccThreads) s += resid(p[e], q, e);
-  return s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!q) {
+      r[i] = (double)pv[i];
+    } else {
+      const double d = (double)pv[i] - (double)qv[i];
+      r[i] = d > 0.0 ? d : 0.0;
+    }
+  }
 }
 
-// Smallest index t in [lo, hi) with base + sum_{lo<=v<=t} r_v > thr, found by
-// giving each thread a contiguous sub-range. Returns -1 when no entry passes;
-// *last_pos receives the last index with r > 0 (or -1).
-__device__ int range_search(const float* p, const float* q, int lo, int hi, double base,
-                            double thr, double* s_wave, int* s_int, int* last_pos) {
-  const int n = hi - lo;
-  const int per = (n + kAccThreads - 1) / kAccThreads;
-  const int a0 = lo + min(n, (int)threadIdx.x * per);
-  const int a1 = lo + min(n, ((int)threadIdx.x + 1) * per);
-  double mine = 0.0;
-  for (int e = a0; e < a1; ++e) mine += resid(p[e], q, e);
-  const double incl = block_inclusive_scan(mine, s_wave);
-  double run = base + (incl - mine);
-  if (threadIdx.x == 0) {
-    s_int[0] = 0x7fffffff;
-    s_int[1] = -1;
-  }
-  __syncthreads();
-  int found = -1, lastp = -1;
-  for (int e = a0; e < a1; ++e) {
-    const double r = resid(p[e], q, e);
-    if (r > 0.0) lastp = e;
-    run += r;
-    if (found < 0 && run > thr) found = e;
-  }
-  if (found >= 0) atomicMin(&s_int[0], found);
-  if (lastp >= 0) atomicMax(&s_int[1], lastp);
-  __syncthreads();
-  const int res = s_int[0] == 0x7fffffff ? -1 : s_int[0];
-  *last_pos = s_int[1];
-  __syncthreads();
-  return res;
+__device__ __forceinline__ bool rows_aligned(const float* p, const float* q) {
+  return ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q ? q : p)) & 15) == 0;
 }
 
 __device__ void write_outputs(const AcceptArgs& a, int b, int j, int tok) {
@@ -133,19 +101,19 @@ __device__ void write_outputs(const AcceptArgs& a, int b, int j, int tok) {
     a.out_tokens[(size_t)b * (K + 1) + i] = i < j ? a.draft[(size_t)b * K + i] : (i == j ? tok : -1);
 }
 
-// Kernel 1, one workgroup per (request, vocabulary chunk): accept length,
-// then the residual (or bonus) mass of the chunk.
+// Kernel 1, one workgroup per (request, vocabulary chunk): the accept length,
+// then the residual (or bonus) mass of every 256-entry sub-block of the chunk
+// (one wave per sub-block, 4 entries per lane).
 __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs a) {
   const int b = blockIdx.x / a.nchunk;
   const int c = blockIdx.x - b * a.nchunk;
   const int K = a.K, V = a.V;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int s_j;
-  __shared__ double s_wave[4];
 
   // accept length: lane i runs test i; a ballot of the failures gives the
   // first reject (an invalid token id counts as a reject and is flagged)
-  if (tid < 64) {
+  if (wave == 0) {
     bool fail = false, bad = false;
     if (lane < K) {
       const int d = a.draft[(size_t)b * K + lane];
@@ -164,66 +132,152 @@ __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs 
     const uint64_t bads = __builtin_amdgcn_ballot_w64(bad);
     if (lane == 0) {
       s_j = j;
-      if (c == 0) a.jbuf[b] = j | (((bads >> j) & 1) && j < K ? kJTokenErr : 0);
+      if (c == 0) a.jbuf[b] = j | ((((bads >> j) & 1) && j < K) ? kJTokenErr : 0);
     }
   }
   __syncthreads();
   const int j = s_j;
   const float* prow = a.p + ((size_t)b * (K + 1) + j) * V;
   const float* qrow = j < K ? a.q + ((size_t)b * K + j) * V : nullptr;
-  const int lo = c * a.chunk, hi = min(V, lo + a.chunk);
-  const double part = block_sum(range_mass(prow, qrow, lo, hi), s_wave);
-  if (tid == 0) a.partial[(size_t)b * a.nchunk + c] = part;
+  const bool vec = rows_aligned(prow, qrow);
+  const int nsb = (V + kSub - 1) / kSub;
+  const int sb0 = c * (a.chunk / kSub);
+  const int sb1 = min(nsb, sb0 + a.chunk / kSub);
+  double* out = a.partial + (size_t)b * nsb;
+#pragma unroll 2
+  for (int sb = sb0 + wave; sb < sb1; sb += kAccThreads / 64) {
+    double r[4];
+    resid4(prow, qrow, sb * kSub + 4 * lane, V, vec, r);
+    const double t = wave_sum((r[0] + r[1]) + (r[2] + r[3]));
+    if (lane == 0) out[sb] = t;
+  }
 }
 
-// Kernel 2, one workgroup per request: scan the chunk masses, find the chunk
-// where the running mass passes u_K * S, locate the token inside it, write
-// every output.
+// Smallest index t of sub-block sb with base + sum_{v<=t} r_v > thr, found by
+// wave 0 (4 entries per lane, then a wave scan); -1 when none passes, with
+// *lastp the last index holding mass. Every thread gets the result.
+__device__ int sub_block_search(const float* p, const float* q, int sb, int V, bool vec,
+                                double base, double thr, int* s_int, int* lastp) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    const int e = sb * kSub + 4 * lane;
+    double r[4];
+    resid4(p, q, e, V, vec, r);
+    const double mine = (r[0] + r[1]) + (r[2] + r[3]);
+    double run = base + (wave_inclusive_scan(mine) - mine);
+    int found = -1, lp = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      run += r[i];
+      if (found < 0 && run > thr) found = e + i;
+      if (r[i] > 0.0) lp = e + i;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(found >= 0);
+    const uint64_t pos = __builtin_amdgcn_ballot_w64(lp >= 0);
+    const int first = hit ? __shfl(found, __builtin_ctzll(hit), 64) : -1;
+    const int last = pos ? __shfl(lp, 63 - __builtin_clzll(pos), 64) : -1;
+    if (lane == 0) {
+      s_int[0] = first;
+      s_int[1] = last;
+    }
+  }
+  __syncthreads();
+  const int res = s_int[0];
+  *lastp = s_int[1];
+  __syncthreads();
+  return res;
+}
+
+// Draws the token from sub-block masses m[0..nsb) (one pass over the
+// masses, one sub-block re-read). Returns -1 if the total mass is not > 0.
+__device__ int draw_from_masses(const double* m, int nsb, const float* p, const float* q, int V,
+                                bool vec, double u, double* s_wave, int* s_int) {
+  __shared__ double s_tot, s_base;
+  const int tid = threadIdx.x;
+  const int per = (nsb + kAccThreads - 1) / kAccThreads;
+  const int i0 = min(nsb, tid * per), i1 = min(nsb, i0 + per);
+  double mine = 0.0;
+  for (int i = i0; i < i1; ++i) mine += m[i];
+  const double incl = block_inclusive_scan(mine, s_wave);
+  if (tid == kAccThreads - 1) s_tot = incl;
+  __syncthreads();
+  const double S = s_tot;
+  if (!(S > 0.0)) return -1;
+  const double thr = u * S;
+  if (tid == 0) {
+    s_int[0] = 0x7fffffff;
+    s_int[1] = -1;
+  }
+  __syncthreads();
+  // first sub-block whose running mass passes thr, and the last one with mass
+  double run = incl - mine;
+  int hit = -1, lastm = -1;
+  for (int i = i0; i < i1; ++i) {
+    const double x = m[i];
+    if (hit < 0 && run + x > thr) hit = i;
+    run += x;
+    if (x > 0.0) lastm = i;
+  }
+  if (hit >= 0) atomicMin(&s_int[0], hit);
+  if (lastm >= 0) atomicMax(&s_int[1], lastm);
+  __syncthreads();
+  const int first_hit = s_int[0];
+  int sstar = first_hit != 0x7fffffff ? first_hit : s_int[1];
+  __syncthreads();
+  // base: running mass before sub-block sstar (recomputed by its owner)
+  if (first_hit == 0x7fffffff && tid == 0) {
+    double b0 = 0.0;
+    for (int i = 0; i < sstar; ++i) b0 += m[i];
+    s_base = b0;
+  }
+  if (first_hit != 0x7fffffff && sstar >= i0 && sstar < i1) {
+    double b0 = incl - mine;
+    for (int i = i0; i < sstar; ++i) b0 += m[i];
+    s_base = b0;
+  }
+  __syncthreads();
+  const double base = s_base;
+  int lastp;
+  int tok = sub_block_search(p, q, sstar, V, vec, base, thr, s_int, &lastp);
+  if (tok < 0) tok = lastp;
+  return tok;
+}
+
+// Kernel 2, one workgroup per request: scan the sub-block masses, find the
+// sub-block where the running mass passes u_K * S, locate the token inside it,
+// write every output.
 __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a) {
   const int b = blockIdx.x;
   const int K = a.K, V = a.V;
   const int tid = threadIdx.x;
   __shared__ double s_wave[4];
   __shared__ int s_int[2];
-  __shared__ double s_tot, s_base;
   const int jw = a.jbuf[b];
   const int j = jw & 0xffff;
   const float* prow = a.p + ((size_t)b * (K + 1) + j) * V;
   const float* qrow = j < K ? a.q + ((size_t)b * K + j) * V : nullptr;
+  const bool vec = rows_aligned(prow, qrow);
   const double ub = (double)a.u[(size_t)b * (K + 1) + K];
-  // chunk masses scanned in chunk order (nchunk <= 256: one per thread)
-  const double mine = tid < a.nchunk ? a.partial[(size_t)b * a.nchunk + tid] : 0.0;
-  const double incl = block_inclusive_scan(mine, s_wave);
-  if (tid == kAccThreads - 1) s_tot = incl;
-  __syncthreads();
-  const double S = s_tot;
-  int tok = -1;
+  const int nsb = (V + kSub - 1) / kSub;
   int errs = (jw & kJTokenErr) ? kErrToken : 0;
-  if (S > 0.0) {
-    const double thr = ub * S;
-    if (tid == 0) {
-      s_int[0] = 0x7fffffff;
-      s_int[1] = -1;
-    }
-    __syncthreads();
-    if (tid < a.nchunk && incl > thr) atomicMin(&s_int[0], tid);
-    if (tid < a.nchunk && mine > 0.0) atomicMax(&s_int[1], tid);
-    __syncthreads();
-    const int cstar = s_int[0] != 0x7fffffff ? s_int[0] : s_int[1];
-    if (tid == cstar) s_base = incl - mine;
-    __syncthreads();
-    const double base = s_base;
-    int lastp;
-    const int clo = cstar * a.chunk, chi = min(V, clo + a.chunk);
-    tok = range_search(prow, qrow, clo, chi, base, thr, s_wave, s_int, &lastp);
-    if (tok < 0) tok = lastp;
-  } else {
-    // zero residual mass: draw from the target row itself
+  int tok = draw_from_masses(a.partial + (size_t)b * nsb, nsb, prow, qrow, V, vec, ub, s_wave, s_int);
+  if (tok < 0) {
+    // zero residual mass: draw from the target row itself. Its sub-block
+    // masses replace the residual ones in this request's partial slots (each
+    // wave fills its own sub-blocks, then the block synchronises).
     errs |= kErrZeroResidual;
-    const double S2 = block_sum(range_mass(prow, nullptr, 0, V), s_wave);
-    int lastp;
-    tok = range_search(prow, nullptr, 0, V, 0.0, ub * S2, s_wave, s_int, &lastp);
-    if (tok < 0) tok = lastp;
+    double* m = a.partial + (size_t)b * nsb;
+    const bool pvec = rows_aligned(prow, nullptr);
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int sb = wave; sb < nsb; sb += kAccThreads / 64) {
+      double r[4];
+      resid4(prow, nullptr, sb * kSub + 4 * lane, V, pvec, r);
+      const double t = wave_sum((r[0] + r[1]) + (r[2] + r[3]));
+      if (lane == 0) m[sb] = t;
+    }
+    __threadfence_block();
+    __syncthreads();
+    tok = draw_from_masses(m, nsb, prow, nullptr, V, pvec, ub, s_wave, s_int);
   }
   if (tok < 0) tok = 0;
   write_outputs(a, b, j, tok);

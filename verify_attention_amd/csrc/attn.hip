@@ -132,14 +132,14 @@ struct KvView {
 //   K piece (tile T, chunk c, half h): key key0 + 8*(n/4) + 4*T + n%4,
 //     dims 32c + 8*grp + 4h (bf16: h = 0, 8 dims; fp32: 4 dims per half)
 //   V piece (dim tile dt, half h): dim 16*dt + n, keys key0 + 8*grp + 4h ...
-// TAIL: keys at or past n_keys are read from the stage's first slot and
-// zeroed (their own slots may hold anything, or not exist).
-template <typename T, int D, bool TAIL>
+// Keys at or past n_keys are read from the stage's first slot instead (their
+// own slots may hold anything, or not exist); store_stage zeroes them. One
+// branch-free path, so the loads stay in flight until the data is stored.
+template <typename T, int D>
 __device__ __forceinline__ void load_stage(typename StageShape<T, D>::Regs& r, const KvView& kv,
                                            int P, int key0, int page_lo, int page_hi,
                                            int n_keys, int wave, int lane) {
   using SS = StageShape<T, D>;
-  constexpr int E = 16 / sizeof(T);  // elements per piece
   const int n = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int j = 0; j < SS::KPW; ++j) {
@@ -147,42 +147,54 @@ __device__ __forceinline__ void load_stage(typename StageShape<T, D>::Regs& r, c
     const int f = piece / SS::H, h = piece % SS::H;
     const int t2 = f / SS::KC, c = f % SS::KC;
     const int kk = 8 * (n >> 2) + 4 * t2 + (n & 3);
-    const bool ok = !TAIL || key0 + kk < n_keys;
-    const int kq = ok ? kk : 0;
+    const int kq = key0 + kk < n_keys ? kk : 0;
     const int page = (P == 16 && kq >= 16) ? page_hi : page_lo;
     const size_t off = (size_t)page * kv.page_bytes +
                        (size_t)(((key0 + kq) & (P - 1)) * D + 32 * c + 8 * grp + 4 * h) * sizeof(T);
     r[j] = *reinterpret_cast<const intx4*>(kv.kbase + off);
-    if (TAIL && !ok) r[j] = intx4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int j = 0; j < SS::VPW; ++j) {
     const int piece = wave + kWaves * j;
     const int dt = piece / SS::H, h = piece % SS::H;
     const int kk = 8 * grp + 4 * h;
-    const bool ok = !TAIL || key0 + kk < n_keys;
-    const int kq = ok ? kk : 0;
+    const int kq = key0 + kk < n_keys ? kk : 0;
     const int page = (P == 16 && kq >= 16) ? page_hi : page_lo;
     const size_t off = (size_t)page * kv.page_bytes +
                        (size_t)((16 * dt + n) * P + ((key0 + kq) & (P - 1))) * sizeof(T);
-    intx4 x = *reinterpret_cast<const intx4*>(kv.vbase + off);
-    if (TAIL) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (key0 + kk + e >= n_keys) {
-          if (sizeof(T) == 4) x[e] = 0;
-          else x[e / 2] &= (e & 1) ? 0x0000ffff : 0xffff0000;
-        }
-      }
-    }
-    r[SS::KPW + j] = x;
+    r[SS::KPW + j] = *reinterpret_cast<const intx4*>(kv.vbase + off);
   }
 }
 
+// Writes this wave's pieces to an LDS stage buffer at the positions the MFMA
+// lanes read them from; on the stage that crosses n_keys the pieces (or
+// elements) of keys past the end are zeroed first.
 template <typename T, int D>
-__device__ __forceinline__ void store_stage(const typename StageShape<T, D>::Regs& r, char* buf,
-                                            int wave, int lane) {
+__device__ __forceinline__ void store_stage(typename StageShape<T, D>::Regs& r, char* buf, int key0,
+                                            int n_keys, int wave, int lane) {
   using SS = StageShape<T, D>;
+  constexpr int E = 16 / sizeof(T);  // elements per piece
+  const int n = lane & 15, grp = lane >> 4;
+  if (key0 + kStep > n_keys) {
+#pragma unroll
+    for (int j = 0; j < SS::KPW; ++j) {
+      const int piece = wave + kWaves * j;
+      const int t2 = (piece / SS::H) / SS::KC;
+      if (key0 + 8 * (n >> 2) + 4 * t2 + (n & 3) >= n_keys) r[j] = intx4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < SS::VPW; ++j) {
+      const int h = (wave + kWaves * j) % SS::H;
+      const int k0 = key0 + 8 * grp + 4 * h;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (k0 + e >= n_keys) {
+          if (sizeof(T) == 4) r[SS::KPW + j][e] = 0;
+          else r[SS::KPW + j][e / 2] &= (e & 1) ? 0x0000ffff : (int)0xffff0000;
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < SS::KPW; ++j)
     *reinterpret_cast<intx4*>(buf + (wave + kWaves * j) * 1024 + lane * 16) = r[j];
@@ -324,10 +336,7 @@ __device__ __forceinline__ void issue(typename StageShape<T, D>::Regs& r, const 
   const int idx = (key0 >> a.p_shift) - pg0;
   const int page_lo = s_pages[idx];
   const int page_hi = (a.P == 16 && key0 + 16 < n_keys) ? s_pages[idx + 1] : page_lo;
-  if (key0 + kStep <= n_keys)
-    load_stage<T, D, false>(r, kv, a.P, key0, page_lo, page_hi, n_keys, wave, lane);
-  else
-    load_stage<T, D, true>(r, kv, a.P, key0, page_lo, page_hi, n_keys, wave, lane);
+  load_stage<T, D>(r, kv, a.P, key0, page_lo, page_hi, n_keys, wave, lane);
 }
 
 template <typename T, int D, int MT>
@@ -406,28 +415,34 @@ __global__ __launch_bounds__(kWave * kWaves, (MT == 1 ? 2 : 1)) void block_attn_
 
     const int ns = w1 - w0;
     typename SS::Regs r0, r1, r2;
+    // one pipeline step: load stage t + 3, consume stage t, stage t + 1 to LDS
+    auto step = [&](typename SS::Regs& r_issue, char* b_cons, typename SS::Regs& r_store,
+                    char* b_store, int t, bool do_issue, bool do_store) {
+      if (do_issue) issue<T, D>(r_issue, kv, a, s_pages, pg0, (w0 + t + 3) * kStep, n_keys, wave, lane);
+      consume<T, D, MT>(ws, b_cons, a, (w0 + t) * kStep, L, n_keys, nc, lane, has_rows);
+      if (do_store) store_stage<T, D>(r_store, b_store, (w0 + t + 1) * kStep, n_keys, wave, lane);
+      __syncthreads();
+    };
     issue<T, D>(r0, kv, a, s_pages, pg0, w0 * kStep, n_keys, wave, lane);
     if (ns > 1) issue<T, D>(r1, kv, a, s_pages, pg0, (w0 + 1) * kStep, n_keys, wave, lane);
     if (ns > 2) issue<T, D>(r2, kv, a, s_pages, pg0, (w0 + 2) * kStep, n_keys, wave, lane);
-    store_stage<T, D>(r0, s_buf[0], wave, lane);
+    store_stage<T, D>(r0, s_buf[0], w0 * kStep, n_keys, wave, lane);
     __syncthreads();
-    // three stages per trip: register set and LDS buffer indices stay static
-    for (int t = 0; t < ns; t += 3) {
-      if (t + 3 < ns) issue<T, D>(r0, kv, a, s_pages, pg0, (w0 + t + 3) * kStep, n_keys, wave, lane);
-      consume<T, D, MT>(ws, s_buf[0], a, (w0 + t) * kStep, L, n_keys, nc, lane, has_rows);
-      if (t + 1 < ns) store_stage<T, D>(r1, s_buf[1], wave, lane);
-      __syncthreads();
-      if (t + 1 >= ns) break;
-      if (t + 4 < ns) issue<T, D>(r1, kv, a, s_pages, pg0, (w0 + t + 4) * kStep, n_keys, wave, lane);
-      consume<T, D, MT>(ws, s_buf[1], a, (w0 + t + 1) * kStep, L, n_keys, nc, lane, has_rows);
-      if (t + 2 < ns) store_stage<T, D>(r2, s_buf[2], wave, lane);
-      __syncthreads();
-      if (t + 2 >= ns) break;
-      if (t + 5 < ns) issue<T, D>(r2, kv, a, s_pages, pg0, (w0 + t + 5) * kStep, n_keys, wave, lane);
-      consume<T, D, MT>(ws, s_buf[2], a, (w0 + t + 2) * kStep, L, n_keys, nc, lane, has_rows);
-      if (t + 3 < ns) store_stage<T, D>(r0, s_buf[0], wave, lane);
-      __syncthreads();
+    // steady state: three stages per trip with static register-set / buffer
+    // indices and no conditions, so every load stays in flight until its
+    // data is written to LDS two steps later
+    int t = 0;
+    for (; t + 6 <= ns; t += 3) {
+      step(r0, s_buf[0], r1, s_buf[1], t, true, true);
+      step(r1, s_buf[1], r2, s_buf[2], t + 1, true, true);
+      step(r2, s_buf[2], r0, s_buf[0], t + 2, true, true);
     }
+    // the last (at most five) stages
+    if (t < ns) step(r0, s_buf[0], r1, s_buf[1], t, t + 3 < ns, t + 1 < ns);
+    if (t + 1 < ns) step(r1, s_buf[1], r2, s_buf[2], t + 1, t + 4 < ns, t + 2 < ns);
+    if (t + 2 < ns) step(r2, s_buf[2], r0, s_buf[0], t + 2, false, t + 3 < ns);
+    if (t + 3 < ns) step(r0, s_buf[0], r1, s_buf[1], t + 3, false, t + 4 < ns);
+    if (t + 4 < ns) step(r1, s_buf[1], r2, s_buf[2], t + 4, false, false);
   }
 
   // ---- this wave's rows: normalise and write, or store the split's partial state

@@ -86,7 +86,7 @@ AccPlan plan_accept(int bs, int K, int V, int greedy) {
   p.nchunk = (V + chunk - 1) / chunk;
   p.off_jbuf = 0;
   p.off_partial = align_up((size_t)bs * sizeof(int32_t), 256);
-  p.ws_bytes = p.off_partial + (size_t)bs * p.nchunk * sizeof(double);
+  p.ws_bytes = p.off_partial + (size_t)bs * ((V + 255) / 256) * sizeof(double);
   return p;
 }
 

@@ -57,7 +57,7 @@ struct AcceptArgs {
   int32_t* out_tokens;
   int32_t* new_seq_lens;
   int32_t* err;
-  double* partial;     // [bs][nchunk] residual mass per vocabulary chunk
+  double* partial;     // [bs][ceil(V / 256)] residual mass per 256-entry sub-block
   int32_t* jbuf;       // [bs] accept length (| token-error flag) from the first kernel
   int32_t* greedy_ids; // [bs][K+1] row argmax (greedy mode)
   int bs, K, V, nchunk, chunk;
