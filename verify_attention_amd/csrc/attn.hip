@@ -13,11 +13,14 @@
 //     times the block tokens) are the MFMA N dimension, so each K/V page is
 //     read from HBM once per KV head. Wave w owns 16 (or 32) of those rows.
 //   * The split's keys stream through in 32-key stages. For each stage the 4
-//     waves together issue the 16-byte loads of every MFMA operand fragment
-//     (each wave a quarter), keep three stages in flight in registers, and
-//     write each fragment to LDS in the lane order its MFMA consumes it, so
+//     waves together issue the 16-byte global->LDS DMA loads
+//     (global_load_lds_dwordx4) of every MFMA operand fragment, each wave a
+//     quarter, placing each fragment in the lane order its MFMA consumes it;
 //     every wave then reads whole fragments with conflict-free ds_read_b128.
-//     Three LDS stage buffers, one barrier per stage.
+//     An LDS ring of 64 KB (two workgroups per CU, 3 stages in flight each)
+//     or 128 KB (one workgroup, 7 stages) keeps stages in flight without
+//     holding them in registers; hand-counted vmcnt waits and one barrier per
+//     stage.
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16
 //     (eight v_mfma_f32_16x16x4f32 for fp32 inputs). Keys are permuted inside
 //     a stage so that the accumulator layout of S^T is directly the B operand
@@ -127,19 +130,41 @@ struct KvView {
   size_t page_bytes;    // bytes per physical page (all KV heads)
 };
 
-// Loads this wave's pieces of the stage at key0 (pages page_lo for keys 0..15
-// or all keys when P = 32, page_hi for keys 16..31). Lane (n, grp):
-//   K piece (tile T, chunk c, half h): key key0 + 8*(n/4) + 4*T + n%4,
-//     dims 32c + 8*grp + 4h (bf16: h = 0, 8 dims; fp32: 4 dims per half)
-//   V piece (dim tile dt, half h): dim 16*dt + n, keys key0 + 8*grp + 4h ...
-// Keys at or past n_keys are read from the stage's first slot instead (their
-// own slots may hold anything, or not exist); store_stage zeroes them. One
-// branch-free path, so the loads stay in flight until the data is stored.
+// 16 zero bytes: the DMA source for lanes whose key lies past the sequence end.
+__device__ __attribute__((aligned(64))) int g_zero16[16];
+
+constexpr int wait_vm_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+// s_waitcnt vmcnt(per * m) for a small runtime m (the immediate must be static).
+template <int PER>
+__device__ __forceinline__ void wait_stages(int m) {
+  switch (m) {
+    case 0: __builtin_amdgcn_s_waitcnt(wait_vm_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vm_imm(PER)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vm_imm(2 * PER)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_vm_imm(3 * PER)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(wait_vm_imm(4 * PER)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(wait_vm_imm(5 * PER)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vm_imm(6 * PER)); break;
+  }
+}
+
+// Per-lane constants of this wave's DMA pieces. A stage starts on a page
+// boundary (32 keys, P in {16, 32}), so the slot of a lane's key inside its
+// page, and whether that page is the stage's first or second, never change.
 template <typename T, int D>
-__device__ __forceinline__ void load_stage(typename StageShape<T, D>::Regs& r, const KvView& kv,
-                                           int P, int key0, int page_lo, int page_hi,
-                                           int n_keys, int wave, int lane) {
+struct DmaLanes {
   using SS = StageShape<T, D>;
+  uint32_t off[SS::PW];  // byte offset inside the (page, KV head) tile
+  int key[SS::PW];       // first key of the piece inside the stage
+  bool hi[SS::PW];       // the key lies in the stage's second page (P = 16)
+  uint32_t lds[SS::PW];  // piece offset inside a ring slot
+};
+
+template <typename T, int D>
+__device__ __forceinline__ DmaLanes<T, D> dma_lanes(int P, int wave, int lane) {
+  using SS = StageShape<T, D>;
+  DmaLanes<T, D> d;
   const int n = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int j = 0; j < SS::KPW; ++j) {
@@ -147,99 +172,164 @@ __device__ __forceinline__ void load_stage(typename StageShape<T, D>::Regs& r, c
     const int f = piece / SS::H, h = piece % SS::H;
     const int t2 = f / SS::KC, c = f % SS::KC;
     const int kk = 8 * (n >> 2) + 4 * t2 + (n & 3);
-    const int kq = key0 + kk < n_keys ? kk : 0;
-    const int page = (P == 16 && kq >= 16) ? page_hi : page_lo;
-    const size_t off = (size_t)page * kv.page_bytes +
-                       (size_t)(((key0 + kq) & (P - 1)) * D + 32 * c + 8 * grp + 4 * h) * sizeof(T);
-    r[j] = *reinterpret_cast<const intx4*>(kv.kbase + off);
+    d.key[j] = kk;
+    d.hi[j] = P == 16 && kk >= 16;
+    d.off[j] = (uint32_t)(((kk & (P - 1)) * D + 32 * c + 8 * grp + 4 * h) * sizeof(T));
+    d.lds[j] = piece * 1024;
   }
 #pragma unroll
   for (int j = 0; j < SS::VPW; ++j) {
     const int piece = wave + kWaves * j;
     const int dt = piece / SS::H, h = piece % SS::H;
     const int kk = 8 * grp + 4 * h;
-    const int kq = key0 + kk < n_keys ? kk : 0;
-    const int page = (P == 16 && kq >= 16) ? page_hi : page_lo;
-    const size_t off = (size_t)page * kv.page_bytes +
-                       (size_t)((16 * dt + n) * P + ((key0 + kq) & (P - 1))) * sizeof(T);
-    r[SS::KPW + j] = *reinterpret_cast<const intx4*>(kv.vbase + off);
+    d.key[SS::KPW + j] = kk;
+    d.hi[SS::KPW + j] = P == 16 && kk >= 16;
+    d.off[SS::KPW + j] = (uint32_t)(((16 * dt + n) * P + (kk & (P - 1))) * sizeof(T));
+    d.lds[SS::KPW + j] = (SS::NKP + piece) * 1024;
   }
+  return d;
 }
 
-// Writes this wave's pieces to an LDS stage buffer at the positions the MFMA
-// lanes read them from; on the stage that crosses n_keys the pieces (or
-// elements) of keys past the end are zeroed first.
-template <typename T, int D>
-__device__ __forceinline__ void store_stage(typename StageShape<T, D>::Regs& r, char* buf, int key0,
-                                            int n_keys, int wave, int lane) {
+// Issues this wave's pieces of one stage as LDS DMA loads into a ring slot:
+// the K/V tiles of the stage's two pages (one when P = 32) start at k_lo/k_hi
+// and v_lo/v_hi. Each piece lands at slot + piece * 1024 + lane * 16, the
+// position from which the MFMA lane that consumes it reads. TAIL: lanes whose
+// first key lies at or past n_keys load zeros instead; a V piece that
+// straddles n_keys is masked by its reader.
+template <typename T, int D, bool TAIL>
+__device__ __forceinline__ void issue_dma(char* slot, const DmaLanes<T, D>& dl, const char* k_lo,
+                                          const char* k_hi, const char* v_lo, const char* v_hi,
+                                          int key0, int n_keys) {
   using SS = StageShape<T, D>;
-  constexpr int E = 16 / sizeof(T);  // elements per piece
-  const int n = lane & 15, grp = lane >> 4;
-  if (key0 + kStep > n_keys) {
 #pragma unroll
-    for (int j = 0; j < SS::KPW; ++j) {
-      const int piece = wave + kWaves * j;
-      const int t2 = (piece / SS::H) / SS::KC;
-      if (key0 + 8 * (n >> 2) + 4 * t2 + (n & 3) >= n_keys) r[j] = intx4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < SS::VPW; ++j) {
-      const int h = (wave + kWaves * j) % SS::H;
-      const int k0 = key0 + 8 * grp + 4 * h;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (k0 + e >= n_keys) {
-          if (sizeof(T) == 4) r[SS::KPW + j][e] = 0;
-          else r[SS::KPW + j][e / 2] &= (e & 1) ? 0x0000ffff : (int)0xffff0000;
-        }
-      }
-    }
+  for (int j = 0; j < SS::PW; ++j) {
+    const bool is_k = j < SS::KPW;
+    const char* base = is_k ? (dl.hi[j] ? k_hi : k_lo) : (dl.hi[j] ? v_hi : v_lo);
+    const char* src = base + dl.off[j];
+    if (TAIL && key0 + dl.key[j] >= n_keys) src = reinterpret_cast<const char*>(g_zero16);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(slot + dl.lds[j]), 16, 0, 0);
   }
-#pragma unroll
-  for (int j = 0; j < SS::KPW; ++j)
-    *reinterpret_cast<intx4*>(buf + (wave + kWaves * j) * 1024 + lane * 16) = r[j];
-#pragma unroll
-  for (int j = 0; j < SS::VPW; ++j)
-    *reinterpret_cast<intx4*>(buf + (SS::NKP + wave + kWaves * j) * 1024 + lane * 16) = r[SS::KPW + j];
 }
 
-// Fragment starting at piece p0: one 16-byte piece (bf16) or two (fp32).
+// Sixteen 16-byte pieces P0 .. P0+15 of a ring slot (lane-relative address
+// `addr`) behind one s_waitcnt. Inline asm keeps the compiler's LDS-DMA
+// tracking from inserting a wait for every DMA still in flight.
+template <int P0>
+__device__ __forceinline__ void read16(intx4* o, unsigned addr) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:%17\n\t"
+      "ds_read_b128 %1, %16 offset:%18\n\t"
+      "ds_read_b128 %2, %16 offset:%19\n\t"
+      "ds_read_b128 %3, %16 offset:%20\n\t"
+      "ds_read_b128 %4, %16 offset:%21\n\t"
+      "ds_read_b128 %5, %16 offset:%22\n\t"
+      "ds_read_b128 %6, %16 offset:%23\n\t"
+      "ds_read_b128 %7, %16 offset:%24\n\t"
+      "ds_read_b128 %8, %16 offset:%25\n\t"
+      "ds_read_b128 %9, %16 offset:%26\n\t"
+      "ds_read_b128 %10, %16 offset:%27\n\t"
+      "ds_read_b128 %11, %16 offset:%28\n\t"
+      "ds_read_b128 %12, %16 offset:%29\n\t"
+      "ds_read_b128 %13, %16 offset:%30\n\t"
+      "ds_read_b128 %14, %16 offset:%31\n\t"
+      "ds_read_b128 %15, %16 offset:%32\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]),
+        "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+      : "v"(addr), "i"(P0 * 1024), "i"((P0 + 1) * 1024), "i"((P0 + 2) * 1024),
+        "i"((P0 + 3) * 1024), "i"((P0 + 4) * 1024), "i"((P0 + 5) * 1024), "i"((P0 + 6) * 1024),
+        "i"((P0 + 7) * 1024), "i"((P0 + 8) * 1024), "i"((P0 + 9) * 1024),
+        "i"((P0 + 10) * 1024), "i"((P0 + 11) * 1024), "i"((P0 + 12) * 1024),
+        "i"((P0 + 13) * 1024), "i"((P0 + 14) * 1024), "i"((P0 + 15) * 1024)
+      : "memory");
+}
+
+// Eight pieces, for stages of eight pieces (bf16, 64 dims).
+template <int P0>
+__device__ __forceinline__ void read8(intx4* o, unsigned addr) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(addr), "i"(P0 * 1024), "i"((P0 + 1) * 1024), "i"((P0 + 2) * 1024),
+        "i"((P0 + 3) * 1024), "i"((P0 + 4) * 1024), "i"((P0 + 5) * 1024), "i"((P0 + 6) * 1024),
+        "i"((P0 + 7) * 1024)
+      : "memory");
+}
+
 template <typename T>
-__device__ __forceinline__ typename Frag<T>::vec read_frag(const char* buf, int p0, int lane);
+__device__ __forceinline__ typename Frag<T>::vec frag_of(const intx4* pc);
 
 template <>
-__device__ __forceinline__ bf16x8 read_frag<__bf16>(const char* buf, int p0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(buf + p0 * 1024 + lane * 16);
+__device__ __forceinline__ bf16x8 frag_of<__bf16>(const intx4* pc) {
+  return __builtin_bit_cast(bf16x8, pc[0]);
 }
 
 template <>
-__device__ __forceinline__ floatx8 read_frag<float>(const char* buf, int p0, int lane) {
-  const floatx4 lo = *reinterpret_cast<const floatx4*>(buf + p0 * 1024 + lane * 16);
-  const floatx4 hi = *reinterpret_cast<const floatx4*>(buf + (p0 + 1) * 1024 + lane * 16);
+__device__ __forceinline__ floatx8 frag_of<float>(const intx4* pc) {
+  const floatx4 lo = __builtin_bit_cast(floatx4, pc[0]);
+  const floatx4 hi = __builtin_bit_cast(floatx4, pc[1]);
   return floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// All fragments of a ring slot; on the stage that crosses n_keys the V
+// elements of keys past the end are zeroed (their slots may hold anything).
 template <typename T, int D>
-__device__ __forceinline__ void read_stage(StepFrags<T, D>& f, const char* buf, int lane) {
+__device__ __forceinline__ void read_stage(StepFrags<T, D>& f, unsigned addr, int key0,
+                                           int n_keys, int lane) {
   using SS = StageShape<T, D>;
+  constexpr int NP = SS::NKP + SS::NVP;
+  static_assert(NP == 8 || NP == 16 || NP == 32, "stage piece counts");
+  intx4 pc[NP];
+  if constexpr (NP == 8) {
+    read8<0>(pc, addr);
+  } else {
+    read16<0>(pc, addr);
+    if constexpr (NP == 32) read16<16>(pc + 16, addr);
+  }
+  if (key0 + kStep > n_keys) {
+    const int grp = lane >> 4;
+    constexpr int E = 16 / sizeof(T);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int h = 0; h < SS::H; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (key0 + 8 * grp + 4 * h + e >= n_keys) {
+            intx4& x = pc[SS::NKP + dt * SS::H + h];
+            if (sizeof(T) == 4) x[e] = 0;
+            else x[e / 2] &= (e & 1) ? 0x0000ffff : (int)0xffff0000;
+          }
+        }
+  }
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-    for (int c = 0; c < SS::KC; ++c) f.k[t2][c] = read_frag<T>(buf, (t2 * SS::KC + c) * SS::H, lane);
+    for (int c = 0; c < SS::KC; ++c) f.k[t2][c] = frag_of<T>(pc + (t2 * SS::KC + c) * SS::H);
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = read_frag<T>(buf, SS::NKP + dt * SS::H, lane);
+  for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = frag_of<T>(pc + SS::NKP + dt * SS::H);
 }
 
 // One stage: S^T = K Q^T, (mask), online softmax update, O^T += V^T P^T.
 // s[T][t][j] is key key0 + 8*grp + 4*T + j against row 16t + n of the wave;
 // softmax runs in the exp2 domain with the scale folded into the exponent.
-template <typename T, int D, int MT, bool MASKED>
+template <typename T, int D, int MT>
 __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
                                              const typename Frag<T>::vec (&qf)[MT][D / 32],
                                              floatx4 (&acc)[D / 16][MT], float (&m_run)[MT],
                                              float (&l_run)[MT], const int (&blk_row)[MT],
                                              const AttnArgs& a, int key0, int L, int n_keys,
-                                             int nc, int grp) {
+                                             int nc, int grp, bool masked) {
   floatx4 s[2][MT];
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2)
@@ -251,7 +341,7 @@ __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
       s[t2][t] = c;
     }
 
-  if (MASKED) {
+  if (masked) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -259,9 +349,9 @@ __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int key = key0 + 8 * grp + 4 * t2 + j;
-          const bool vis = key < L ||
-                           (key < n_keys && block_visible(a.mode, blk_row[t], key - L, nc));
-          if (!vis) s[t2][t][j] = -__builtin_inff();
+          const int jb = key - L, i = blk_row[t];
+          const bool vis = (key < L) | ((key < n_keys) & ((a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc))));
+          s[t2][t][j] = vis ? s[t2][t][j] : -__builtin_inff();
         }
   }
 
@@ -313,37 +403,27 @@ struct WaveState {
   int blk_row[MT];
 };
 
-// Consumes stage key0 from LDS buffer buf.
+// Consumes the stage at key0 from the ring slot at lane-relative LDS address addr.
 template <typename T, int D, int MT>
-__device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, const char* buf, const AttnArgs& a,
+__device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned addr, const AttnArgs& a,
                                         int key0, int L, int n_keys, int nc, int lane,
                                         bool has_rows) {
   if (!has_rows) return;
   StepFrags<T, D> f;
-  read_stage<T, D>(f, buf, lane);
-  if (key0 + kStep > L)
-    compute_step<T, D, MT, true>(f, ws.qf, ws.acc, ws.m_run, ws.l_run, ws.blk_row, a, key0, L,
-                                 n_keys, nc, lane >> 4);
-  else
-    compute_step<T, D, MT, false>(f, ws.qf, ws.acc, ws.m_run, ws.l_run, ws.blk_row, a, key0, L,
-                                  n_keys, nc, lane >> 4);
+  read_stage<T, D>(f, addr, key0, n_keys, lane);
+  compute_step<T, D, MT>(f, ws.qf, ws.acc, ws.m_run, ws.l_run, ws.blk_row, a, key0, L, n_keys,
+                         nc, lane >> 4, key0 + kStep > L);
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void issue(typename StageShape<T, D>::Regs& r, const KvView& kv,
-                                      const AttnArgs& a, const int* s_pages, int pg0, int key0,
-                                      int n_keys, int wave, int lane) {
-  const int idx = (key0 >> a.p_shift) - pg0;
-  const int page_lo = s_pages[idx];
-  const int page_hi = (a.P == 16 && key0 + 16 < n_keys) ? s_pages[idx + 1] : page_lo;
-  load_stage<T, D>(r, kv, a.P, key0, page_lo, page_hi, n_keys, wave, lane);
-}
-
-template <typename T, int D, int MT>
+// RING_KB: LDS for the stage ring; its depth NS = RING_KB KB / stage bytes
+// (at most 8) sets how many stages are in flight (NS - 1).
+template <typename T, int D, int MT, int RING_KB>
 __global__ __launch_bounds__(kWave * kWaves, (MT == 1 ? 2 : 1)) void block_attn_kernel(AttnArgs a) {
   using SS = StageShape<T, D>;
-  __shared__ __attribute__((aligned(16))) char s_buf[3][SS::BYTES];
-  __shared__ int s_pages[kPageWin];
+  constexpr int NS = RING_KB * 1024 / SS::BYTES < 8 ? RING_KB * 1024 / SS::BYTES : 8;
+  static_assert(NS >= 3, "the ring needs at least three stages");
+  __shared__ __attribute__((aligned(16))) char s_ring[NS * SS::BYTES];
+  __shared__ __attribute__((aligned(8))) int s_pages[kPageWin];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -399,50 +479,59 @@ __global__ __launch_bounds__(kWave * kWaves, (MT == 1 ? 2 : 1)) void block_attn_
   }
 
   // ---- stream the split's stages, one window of staged page ids at a time
-  const int win_steps = kPageWin * a.P / kStep;
+  const int win_steps = kPageWin / 2;  // (lo, hi) page pairs per window
+  const DmaLanes<T, D> dl = dma_lanes<T, D>(a.P, wave, lane);
   for (int w0 = s_lo; w0 < s_hi; w0 += win_steps) {
     const int w1 = min(s_hi, w0 + win_steps);
-    const int pg0 = (w0 * kStep) >> a.p_shift;
-    const int npg = ((min(w1 * kStep, n_keys) - 1) >> a.p_shift) - pg0 + 1;
     __syncthreads();  // the previous window is fully consumed
-    for (int x = tid; x < npg; x += kWave * kWaves) {
-      const int p = ptab[pg0 + x];
+    // (lo, hi) physical pages of every stage of the window; hi = lo when the
+    // stage has one page (P = 32) or its second page lies past the sequence
+    for (int x = tid; x < 2 * (w1 - w0); x += kWave * kWaves) {
+      const int key = (w0 + (x >> 1)) * kStep + (x & 1) * 16;
+      const bool second = (x & 1) && a.P == 16 && key < n_keys;
+      const int p = ptab[(second ? key : (key & ~31)) >> a.p_shift];
       const bool bad = (unsigned)p >= (unsigned)a.num_pages;
       if (bad) flag_error(a.err, kErrSlot);
       s_pages[x] = bad ? 0 : p;
     }
+    // Q and the page ids are in: from here on the only vector-memory loads in
+    // flight are the ring's DMAs, which the waits below count by hand
+    __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
     __syncthreads();
 
     const int ns = w1 - w0;
-    typename SS::Regs r0, r1, r2;
-    // one pipeline step: load stage t + 3, consume stage t, stage t + 1 to LDS
-    auto step = [&](typename SS::Regs& r_issue, char* b_cons, typename SS::Regs& r_store,
-                    char* b_store, int t, bool do_issue, bool do_store) {
-      if (do_issue) issue<T, D>(r_issue, kv, a, s_pages, pg0, (w0 + t + 3) * kStep, n_keys, wave, lane);
-      consume<T, D, MT>(ws, b_cons, a, (w0 + t) * kStep, L, n_keys, nc, lane, has_rows);
-      if (do_store) store_stage<T, D>(r_store, b_store, (w0 + t + 1) * kStep, n_keys, wave, lane);
-      __syncthreads();
+    const unsigned ring_lane = (unsigned)(size_t)s_ring + (unsigned)lane * 16;
+    // pages of stage t: s_pages[2t'] / [2t'+1] hold (lo, hi) of window stage t'
+    auto issue = [&](int t, int2 pg) {
+      const int key0 = (w0 + t) * kStep;
+      const char* k_lo = kv.kbase + (size_t)pg.x * kv.page_bytes;
+      const char* k_hi = kv.kbase + (size_t)pg.y * kv.page_bytes;
+      const char* v_lo = kv.vbase + (size_t)pg.x * kv.page_bytes;
+      const char* v_hi = kv.vbase + (size_t)pg.y * kv.page_bytes;
+      char* slot = s_ring + (t % NS) * SS::BYTES;
+      if (key0 + kStep <= n_keys)
+        issue_dma<T, D, false>(slot, dl, k_lo, k_hi, v_lo, v_hi, key0, n_keys);
+      else
+        issue_dma<T, D, true>(slot, dl, k_lo, k_hi, v_lo, v_hi, key0, n_keys);
     };
-    issue<T, D>(r0, kv, a, s_pages, pg0, w0 * kStep, n_keys, wave, lane);
-    if (ns > 1) issue<T, D>(r1, kv, a, s_pages, pg0, (w0 + 1) * kStep, n_keys, wave, lane);
-    if (ns > 2) issue<T, D>(r2, kv, a, s_pages, pg0, (w0 + 2) * kStep, n_keys, wave, lane);
-    store_stage<T, D>(r0, s_buf[0], w0 * kStep, n_keys, wave, lane);
-    __syncthreads();
-    // steady state: three stages per trip with static register-set / buffer
-    // indices and no conditions, so every load stays in flight until its
-    // data is written to LDS two steps later
-    int t = 0;
-    for (; t + 6 <= ns; t += 3) {
-      step(r0, s_buf[0], r1, s_buf[1], t, true, true);
-      step(r1, s_buf[1], r2, s_buf[2], t + 1, true, true);
-      step(r2, s_buf[2], r0, s_buf[0], t + 2, true, true);
+    auto stage_pages = [&](int t) {
+      const int2 pg = reinterpret_cast<const int2*>(s_pages)[t];
+      return int2{__builtin_amdgcn_readfirstlane(pg.x), __builtin_amdgcn_readfirstlane(pg.y)};
+    };
+    // NS - 1 stages in flight; stage t lands in ring slot t % NS. Each wave
+    // waits for its own DMA share of stage t (vmcnt counts this wave's
+    // loads in issue order), the barrier publishes all shares, and the slot
+    // consumed one step earlier is refilled with stage t + NS - 1.
+    for (int t = 0; t < NS - 1 && t < ns; ++t) issue(t, stage_pages(t));
+    int2 next_pg = stage_pages(min(NS - 1, ns - 1));
+    for (int t = 0; t < ns; ++t) {
+      wait_stages<SS::PW>(min(NS - 2, ns - 1 - t));
+      asm volatile("s_barrier" ::: "memory");
+      if (t + NS - 1 < ns) issue(t + NS - 1, next_pg);
+      next_pg = stage_pages(min(t + NS, ns - 1));
+      consume<T, D, MT>(ws, ring_lane + (t % NS) * SS::BYTES, a, (w0 + t) * kStep, L, n_keys, nc,
+                        lane, has_rows);
     }
-    // the last (at most five) stages
-    if (t < ns) step(r0, s_buf[0], r1, s_buf[1], t, t + 3 < ns, t + 1 < ns);
-    if (t + 1 < ns) step(r1, s_buf[1], r2, s_buf[2], t + 1, t + 4 < ns, t + 2 < ns);
-    if (t + 2 < ns) step(r2, s_buf[2], r0, s_buf[0], t + 2, false, t + 3 < ns);
-    if (t + 3 < ns) step(r0, s_buf[0], r1, s_buf[1], t + 3, false, t + 4 < ns);
-    if (t + 4 < ns) step(r1, s_buf[1], r2, s_buf[2], t + 4, false, false);
   }
 
   // ---- this wave's rows: normalise and write, or store the split's partial state
@@ -516,27 +605,40 @@ __global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ launch
+template <typename T, int D, int MT>
+static void launch_mt(const AttnArgs& a, dim3 grid, dim3 block, int ring_kb, hipStream_t stream) {
+  // fp32 stages of 128 dims are 32 KB: only the large ring holds 3 of them
+  if constexpr (sizeof(T) == 4 && D == 128) {
+    hipLaunchKernelGGL((block_attn_kernel<T, D, MT, 128>), grid, block, 0, stream, a);
+  } else {
+    if (ring_kb >= 128)
+      hipLaunchKernelGGL((block_attn_kernel<T, D, MT, 128>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((block_attn_kernel<T, D, MT, 64>), grid, block, 0, stream, a);
+  }
+}
+
 template <typename T, int D>
-static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t stream) {
+static hipError_t launch_dt(const AttnArgs& a, int total_blocks, int ring_kb, hipStream_t stream) {
   const dim3 grid(total_blocks), block(kWave * kWaves);
   if (a.M > 64)
-    hipLaunchKernelGGL((block_attn_kernel<T, D, 2>), grid, block, 0, stream, a);
+    launch_mt<T, D, 2>(a, grid, block, ring_kb, stream);
   else
-    hipLaunchKernelGGL((block_attn_kernel<T, D, 1>), grid, block, 0, stream, a);
+    launch_mt<T, D, 1>(a, grid, block, ring_kb, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL((block_attn_combine_kernel<T, D>), dim3(a.bs * a.Hkv), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks,
+hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks, int ring_kb,
                              hipStream_t stream) {
   if (bf16) {
-    return D == 64 ? launch_dt<__bf16, 64>(a, total_blocks, stream)
-                   : launch_dt<__bf16, 128>(a, total_blocks, stream);
+    return D == 64 ? launch_dt<__bf16, 64>(a, total_blocks, ring_kb, stream)
+                   : launch_dt<__bf16, 128>(a, total_blocks, ring_kb, stream);
   }
-  return D == 64 ? launch_dt<float, 64>(a, total_blocks, stream)
-                 : launch_dt<float, 128>(a, total_blocks, stream);
+  return D == 64 ? launch_dt<float, 64>(a, total_blocks, ring_kb, stream)
+                 : launch_dt<float, 128>(a, total_blocks, ring_kb, stream);
 }
 
 }  // namespace specattn

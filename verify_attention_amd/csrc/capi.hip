@@ -27,13 +27,18 @@ int ilog2_exact(int x) {
   return (1 << s) == x ? s : -1;
 }
 
-// Optional override of the split count, read once (tuning knob).
+// Optional overrides read once (tuning knobs): split count, LDS ring size (KB).
+int env_int(const char* name) {
+  const char* s = std::getenv(name);
+  return s ? std::atoi(s) : 0;
+}
 int env_splits() {
-  static int v = [] {
-    const char* s = std::getenv("SPECATTN_SPLITS");
-    return s ? std::atoi(s) : 0;
-  }();
+  static int v = env_int("SPECATTN_SPLITS");
   return v;
+}
+int env_ring_kb() {
+  static int v = env_int("SPECATTN_RING_KB");
+  return v > 0 ? v : 64;
 }
 
 struct AttnPlan {
@@ -41,9 +46,9 @@ struct AttnPlan {
   size_t off_ml = 0, off_o = 0, ws_bytes = 0;
 };
 
-// Splits per (request, KV head): enough workgroups for two per CU when the
-// batch has few (request, KV head) units, while every split keeps at least
-// 8 stages of 32 keys for its pipeline.
+// Splits per (request, KV head): enough workgroups for one per CU when the
+// batch has few (request, KV head) units, while every split keeps at least 8
+// stages of 32 keys.
 AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   AttnPlan p;
   p.M = (Hq / Hkv) * B;
@@ -51,7 +56,7 @@ AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   const int max_steps = std::max(1, (max_kv_len + kStepKeys - 1) / kStepKeys);
   int splits = env_splits();
   if (splits <= 0) {
-    splits = (2 * kCUs + p.units - 1) / p.units;
+    splits = (kCUs + p.units - 1) / p.units;
     splits = std::min(splits, std::max(1, max_steps / 8));
   }
   splits = std::max(1, std::min(splits, std::min(kMaxSplits, max_steps)));
@@ -191,7 +196,7 @@ SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req,
   const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt((float)D) : sm_scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(launch_block_attn(a, dtype == SPEC_BF16, D, plan.units * plan.splits,
-                                      static_cast<hipStream_t>(stream)));
+                                      env_ring_kb(), static_cast<hipStream_t>(stream)));
 }
 
 SPEC_API int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* tokens,
