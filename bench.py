@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference leg")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="before warmup, run one plain device copy of this many MB (a known-size "
+                         "kernel for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -50,6 +53,19 @@ def kernel_sources_hash():
     for f in sorted(os.listdir(os.path.join(ROOT, "verify_attention_amd", "csrc"))):
         h.update(open(os.path.join(ROOT, "verify_attention_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, src_hash):
+    """HBM bytes per block_attn launch from the committed counter runs
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE, each scaled by a plain
+    copy of known size), or None when they were taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_src") != src_hash or workload not in t.get("workloads", {}):
+        return None
+    return int(t["workloads"][workload]["traffic_bytes"])
 
 
 def attn_alg_bytes_flops(cfg, seq_lens):
@@ -185,6 +201,14 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    if args.copy_calib_mb:
+        n = args.copy_calib_mb << 20
+        src_c = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst_c = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -238,7 +262,9 @@ def main():
                    "k_spec": cfg.k_spec, "input_copies": copies},
         "roofline": {"kernel": "block_attn", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name, kernel_sources_hash()),
+                     "traffic_unit": "bytes per launch",
                      "alg_bytes_per_launch": alg_bytes, "avg_us": round(attn_ms.mean() * 1e3, 2),
                      "mfma_frac": round(alg_flops / attn_s / 1e12 / mfma_peak, 4)},
         "kernel_src": kernel_sources_hash(),
