@@ -8,19 +8,24 @@
 // Mask" section of "SGLang strengthens diffusion LLMs: LLaDA 2.0" and in
 // sections 4.3.1 / 4.4.1 of "From DFlash to dLLM Self-Spec (4)".
 //
-// Work decomposition: one 4-wave workgroup per (request, KV head, split).
+// Work decomposition: one 8-wave workgroup per (request, KV head, split).
 //   * All g * B query rows that share a KV head (the GQA group's query heads
 //     times the block tokens) are the MFMA N dimension, so each K/V page is
-//     read from HBM once per KV head. Wave w owns 16 (or 32) of those rows.
-//   * The split's keys stream through in 32-key stages. For each stage the 4
-//     waves together issue the 16-byte global->LDS DMA loads
-//     (global_load_lds_dwordx4) of every MFMA operand fragment, each wave a
-//     quarter, placing each fragment in the lane order its MFMA consumes it;
-//     every wave then reads whole fragments with conflict-free ds_read_b128.
-//     An LDS ring of 64 KB (two workgroups per CU, 3 stages in flight each)
-//     or 128 KB (one workgroup, 7 stages) keeps stages in flight without
-//     holding them in registers; hand-counted vmcnt waits and one barrier per
-//     stage.
+//     read from HBM once per KV head. The rows are cut into 4 row slots of 16
+//     (or 32 when g * B > 64) rows; each row slot has two waves, one per key
+//     half: the split's keys stream through in 32-key stages taken in pairs,
+//     wave set 0 consuming the even stage of a pair and set 1 the odd one.
+//     The two sets' softmax states are merged through LDS at the end, so two
+//     waves share every SIMD and one wave's MFMAs overlap the other's VALU.
+//   * For each stage the 4 waves of its set issue the 16-byte global->LDS DMA
+//     loads (global_load_lds_dwordx4) of every MFMA operand fragment, each a
+//     quarter. A DMA instruction's 64 lanes all read from one page (the key
+//     order inside a stage is chosen so that this holds for P = 16), so its
+//     address is an SGPR page base plus a per-lane offset fixed for the whole
+//     kernel. Each fragment lands where the MFMA lane that consumes it reads
+//     it with one conflict-free ds_read_b128. A 128 KB ring of stage pairs
+//     keeps three pairs in flight; vmcnt waits are counted by hand and one
+//     barrier per pair publishes a pair to both sets.
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16
 //     (eight v_mfma_f32_16x16x4f32 for fp32 inputs). Keys are permuted inside
 //     a stage so that the accumulator layout of S^T is directly the B operand
@@ -29,7 +34,8 @@
 //   * Online softmax in fp32 (exp2 domain), row max across the 4 lane groups
 //     via permlane swaps, lazy rescaling (the reference max only moves when a
 //     new max exceeds it by 2^8), masks applied only on stages that reach the
-//     block; keys past the sequence end are zeroed by the loading wave.
+//     block; keys past the sequence end load zeros (K) or are zeroed by the
+//     reader (V).
 //   * With several splits per (request, KV head) each workgroup stores its
 //     partial state and a second, small kernel merges the splits (a kernel
 //     boundary instead of device-scope fences, which on gfx950 write back and
@@ -42,8 +48,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;   // finite start value for running maxima
 constexpr float kRescale = 8.0f;      // lazy rescale threshold, log2 units
 constexpr int kStep = 32;             // keys per stage
-constexpr int kWaves = 4;             // waves per workgroup
-constexpr int kPageWin = 1024;        // page ids staged in LDS per window
+constexpr int kRowSlots = 4;          // row slots per workgroup
+constexpr int kSets = 2;              // key halves (stage parity) per row slot
+constexpr int kWaves = kRowSlots * kSets;
+constexpr int kRingBytes = 128 * 1024;
+constexpr int kPageWin = 512;         // stages whose page offsets are staged at once
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
 
@@ -64,7 +73,6 @@ template <> struct Frag<__bf16> {
   static __device__ __forceinline__ vec pack(const floatx8& x) {
     return __builtin_convertvector(x, bf16x8);  // v_cvt_pk_bf16_f32, round to nearest even
   }
-  static __device__ __forceinline__ void clear(vec& v, int j) { v[j] = (__bf16)0.0f; }
   static __device__ __forceinline__ void store4(__bf16* p, floatx4 x) {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     bf16x4 r;
@@ -88,49 +96,46 @@ template <> struct Frag<float> {
     return c;
   }
   static __device__ __forceinline__ vec pack(const floatx8& x) { return x; }
-  static __device__ __forceinline__ void clear(vec& v, int j) { v[j] = 0.0f; }
   static __device__ __forceinline__ void store4(float* p, floatx4 x) {
     *reinterpret_cast<floatx4*>(p) = x;
   }
 };
 
-__device__ __forceinline__ bool block_visible(int mode, int i, int jb, int nc) {
-  // mode 0 BIDIR (rectangle), 1 CAUSAL (triangle), 2 MIXED (causal clean rows,
-  // all-visible MASK rows)
-  return mode == 0 || jb <= i || (mode == 2 && i >= nc);
-}
-
-// Fragments of one stage as the MFMAs consume them.
-template <typename T, int D>
-struct StepFrags {
-  typename Frag<T>::vec k[2][D / 32];  // A operands of S^T = K Q^T, two 16-key tiles
-  typename Frag<T>::vec v[D / 16];     // A operands of O^T += V^T P^T, one per 16-dim tile
-};
-
-// A stage is NP pieces of 1 KB (64 lanes x 16 bytes): the K fragments first,
-// then the V fragments; a fragment is H = sizeof(T)/2 pieces. Wave w loads
-// K pieces w, w+4, ... and V pieces w, w+4, ... of every stage.
+// One stage of 32 keys as LDS pieces of 1 KB (64 lanes x 16 bytes).
+//
+// Key order. Inside a stage, S^T tile T (T = 0, 1) row n is key
+// 8 * (n / 4) + 4 * T + n % 4, so the S^T accumulator lane (n, grp) holds keys
+// 8 * grp .. 8 * grp + 7: exactly the B operand of the PV MFMA, whose A
+// operand is then 8 consecutive keys of one dim-major V row. Keys 0..15 of a
+// stage form half 0 and keys 16..31 half 1 (with P = 16 the two pages).
+//
+// K pieces. A K fragment (tile T, 32-dim chunk c, 16-byte part h2) has 64
+// lanes; the 32 lanes with n < 8 read half 0 and the 32 with n >= 8 half 1.
+// Fragment q = (T * KC + c) * H + h2 puts its half-h lanes into K piece
+// h * NKP / 2 + q / 2, lanes 32 * (q % 2) + 8 * (grp ^ h) + n % 8, so every
+// piece reads a single half. V pieces likewise: V fragment q = dt * H + h2
+// (16 dims 16 dt .., 16-byte part h2) puts lane (n, grp) into V piece
+// (grp / 2) * NVP / 2 + q / 2, lane 32 * (q % 2) + 16 * (grp % 2) + n. In both
+// cases fragment q of a lane sits 512 * q bytes after that lane's first one.
 template <typename T, int D>
 struct StageShape {
-  static constexpr int H = sizeof(T) / 2;
-  static constexpr int KC = D / 32;           // K chunks along D per key tile
-  static constexpr int NKP = 2 * KC * H;      // K pieces
-  static constexpr int NVP = (D / 16) * H;    // V pieces
-  static constexpr int KPW = NKP / kWaves;    // K pieces per wave
-  static constexpr int VPW = NVP / kWaves;    // V pieces per wave
+  static constexpr int H = sizeof(T) / 2;        // 16-byte parts per fragment
+  static constexpr int E = 16 / sizeof(T);       // elements per part
+  static constexpr int KC = D / 32;              // 32-dim chunks per key
+  static constexpr int NKP = 2 * KC * H;         // K pieces (= K fragments)
+  static constexpr int NVP = (D / 16) * H;       // V pieces (= V fragments)
+  static constexpr int KPW = NKP / kRowSlots;    // K pieces issued per wave
+  static constexpr int VPW = NVP / kRowSlots;    // V pieces issued per wave
   static constexpr int PW = KPW + VPW;
   static constexpr int BYTES = (NKP + NVP) * 1024;
-  typedef intx4 Regs[PW];  // one stage's pieces held by one wave
-  static_assert(NKP % kWaves == 0 && NVP % kWaves == 0, "pieces must split over 4 waves");
+  static constexpr int PAIR = 2 * BYTES;
+  static constexpr int NSP = kRingBytes / PAIR < 4 ? kRingBytes / PAIR : 4;  // ring depth (pairs)
+  static_assert(NKP % kRowSlots == 0 && NVP % kRowSlots == 0 && KPW > 0 && VPW > 0,
+                "pieces must split over the 4 waves of a set");
+  static_assert(NSP >= 2, "the ring holds at least two stage pairs");
 };
 
-struct KvView {
-  const char* kbase;    // k_pool + kvh * P * D elements
-  const char* vbase;    // v_pool + kvh * P * D elements
-  size_t page_bytes;    // bytes per physical page (all KV heads)
-};
-
-// 16 zero bytes: the DMA source for lanes whose key lies past the sequence end.
+// 16 zero bytes: the DMA source for K lanes whose key lies past the sequence end.
 __device__ __attribute__((aligned(64))) int g_zero16[16];
 
 constexpr int wait_vm_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
@@ -141,129 +146,213 @@ __device__ __forceinline__ void wait_stages(int m) {
   switch (m) {
     case 0: __builtin_amdgcn_s_waitcnt(wait_vm_imm(0)); break;
     case 1: __builtin_amdgcn_s_waitcnt(wait_vm_imm(PER)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(wait_vm_imm(2 * PER)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(wait_vm_imm(3 * PER)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(wait_vm_imm(4 * PER)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(wait_vm_imm(5 * PER)); break;
-    default: __builtin_amdgcn_s_waitcnt(wait_vm_imm(6 * PER)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vm_imm(2 * PER)); break;
   }
 }
 
-// Per-lane constants of this wave's DMA pieces. A stage starts on a page
-// boundary (32 keys, P in {16, 32}), so the slot of a lane's key inside its
-// page, and whether that page is the stage's first or second, never change.
+// Per-lane constants of one wave's DMA pieces: the byte offset of the lane's
+// 16 bytes inside the (page, KV head) tile and, for K pieces, the lane's key
+// inside the stage. Stages start on page boundaries, so both are fixed.
 template <typename T, int D>
 struct DmaLanes {
   using SS = StageShape<T, D>;
-  uint32_t off[SS::PW];  // byte offset inside the (page, KV head) tile
-  int key[SS::PW];       // first key of the piece inside the stage
-  bool hi[SS::PW];       // the key lies in the stage's second page (P = 16)
-  uint32_t lds[SS::PW];  // piece offset inside a ring slot
+  uint32_t off[SS::PW];
+  int key[SS::KPW];
 };
 
 template <typename T, int D>
-__device__ __forceinline__ DmaLanes<T, D> dma_lanes(int P, int wave, int lane) {
+__device__ __forceinline__ DmaLanes<T, D> dma_lanes(int P, int r, int lane) {
   using SS = StageShape<T, D>;
   DmaLanes<T, D> d;
-  const int n = lane & 15, grp = lane >> 4;
+  const int wh = lane >> 5;
 #pragma unroll
   for (int j = 0; j < SS::KPW; ++j) {
-    const int piece = wave + kWaves * j;
-    const int f = piece / SS::H, h = piece % SS::H;
-    const int t2 = f / SS::KC, c = f % SS::KC;
-    const int kk = 8 * (n >> 2) + 4 * t2 + (n & 3);
-    d.key[j] = kk;
-    d.hi[j] = P == 16 && kk >= 16;
-    d.off[j] = (uint32_t)(((kk & (P - 1)) * D + 32 * c + 8 * grp + 4 * h) * sizeof(T));
-    d.lds[j] = piece * 1024;
+    const int p = r + kRowSlots * j;
+    const int h = p / (SS::NKP / 2), q = 2 * (p % (SS::NKP / 2)) + wh;
+    const int grp = ((lane >> 3) & 3) ^ h, n8 = lane & 7;
+    const int h2 = q % SS::H, f = q / SS::H, t2 = f / SS::KC, c = f % SS::KC;
+    const int ks = 16 * h + 8 * (n8 >> 2) + 4 * t2 + (n8 & 3);
+    d.key[j] = ks;
+    d.off[j] = (uint32_t)(((ks & (P - 1)) * D + 32 * c + 8 * grp + SS::E * h2) * sizeof(T));
   }
 #pragma unroll
   for (int j = 0; j < SS::VPW; ++j) {
-    const int piece = wave + kWaves * j;
-    const int dt = piece / SS::H, h = piece % SS::H;
-    const int kk = 8 * grp + 4 * h;
-    d.key[SS::KPW + j] = kk;
-    d.hi[SS::KPW + j] = P == 16 && kk >= 16;
-    d.off[SS::KPW + j] = (uint32_t)(((16 * dt + n) * P + (kk & (P - 1))) * sizeof(T));
-    d.lds[SS::KPW + j] = (SS::NKP + piece) * 1024;
+    const int p = r + kRowSlots * j;
+    const int h = p / (SS::NVP / 2), q = 2 * (p % (SS::NVP / 2)) + wh;
+    const int g1 = (lane >> 4) & 1, n = lane & 15;
+    const int dt = q / SS::H, h2 = q % SS::H;
+    const int ks = 16 * h + 8 * g1;
+    d.off[SS::KPW + j] = (uint32_t)(((16 * dt + n) * P + (ks & (P - 1)) + SS::E * h2) * sizeof(T));
   }
   return d;
 }
 
-// Issues this wave's pieces of one stage as LDS DMA loads into a ring slot:
-// the K/V tiles of the stage's two pages (one when P = 32) start at k_lo/k_hi
-// and v_lo/v_hi. Each piece lands at slot + piece * 1024 + lane * 16, the
-// position from which the MFMA lane that consumes it reads. TAIL: lanes whose
-// first key lies at or past n_keys load zeros instead; a V piece that
-// straddles n_keys is masked by its reader.
+// Global base addresses of a stage's two halves for this KV head.
+struct HalfBases {
+  const char* k0;
+  const char* k1;
+  const char* v0;
+  const char* v1;
+};
+
+// Bases from the staged (lo, hi) page byte offsets, made wave-uniform.
+__device__ __forceinline__ HalfBases half_bases(const char* kbase, const char* vbase, uint4 po) {
+  const uint64_t lo = ((uint64_t)__builtin_amdgcn_readfirstlane(po.y) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane(po.x);
+  const uint64_t hi = ((uint64_t)__builtin_amdgcn_readfirstlane(po.w) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane(po.z);
+  return HalfBases{kbase + lo, kbase + hi, vbase + lo, vbase + hi};
+}
+
+// Issues this wave's pieces of one stage into the ring slot `slot`. Piece p of
+// wave r is r + 4 j; its half, hence its page base, is wave-uniform. TAIL:
+// K lanes whose key lies at or past n_keys read zeros instead; V elements past
+// n_keys are zeroed by their reader.
 template <typename T, int D, bool TAIL>
-__device__ __forceinline__ void issue_dma(char* slot, const DmaLanes<T, D>& dl, const char* k_lo,
-                                          const char* k_hi, const char* v_lo, const char* v_hi,
-                                          int key0, int n_keys) {
+__device__ __forceinline__ void issue_dma(char* slot, int r, const DmaLanes<T, D>& dl,
+                                          const HalfBases& hb, int key0, int n_keys) {
   using SS = StageShape<T, D>;
 #pragma unroll
-  for (int j = 0; j < SS::PW; ++j) {
-    const bool is_k = j < SS::KPW;
-    const char* base = is_k ? (dl.hi[j] ? k_hi : k_lo) : (dl.hi[j] ? v_hi : v_lo);
+  for (int j = 0; j < SS::KPW; ++j) {
+    const int p = r + kRowSlots * j;
+    const char* base = p >= SS::NKP / 2 ? hb.k1 : hb.k0;
     const char* src = base + dl.off[j];
     if (TAIL && key0 + dl.key[j] >= n_keys) src = reinterpret_cast<const char*>(g_zero16);
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(slot + dl.lds[j]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(slot + p * 1024),
+                                     16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < SS::VPW; ++j) {
+    const int p = r + kRowSlots * j;
+    const char* base = p >= SS::NVP / 2 ? hb.v1 : hb.v0;
+    __builtin_amdgcn_global_load_lds(base + dl.off[SS::KPW + j],
+                                     (__attribute__((address_space(3))) void*)(slot + (SS::NKP + p) * 1024),
+                                     16, 0, 0);
   }
 }
 
-// Sixteen 16-byte pieces P0 .. P0+15 of a ring slot (lane-relative address
-// `addr`) behind one s_waitcnt. Inline asm keeps the compiler's LDS-DMA
-// tracking from inserting a wait for every DMA still in flight.
-template <int P0>
-__device__ __forceinline__ void read16(intx4* o, unsigned addr) {
+// Issues one stage (when it exists) whose first key is key0; the stage that
+// crosses n_keys takes the zero-filling path.
+template <typename T, int D>
+__device__ __forceinline__ void issue_stage(char* slot, int r, const DmaLanes<T, D>& dl,
+                                            const HalfBases& hb, int key0, int n_keys,
+                                            bool exists) {
+  if (!exists) return;
+  if (key0 + kStep <= n_keys)
+    issue_dma<T, D, false>(slot, r, dl, hb, key0, n_keys);
+  else
+    issue_dma<T, D, true>(slot, r, dl, hb, key0, n_keys);
+}
+
+// ------------------------------------------------------------- LDS reads
+// N 16-byte fragment parts at lane-relative LDS address addr + 512 * i, then
+// one s_waitcnt. Inline asm keeps the compiler's LDS-DMA tracking from
+// inserting a wait for every DMA still in flight.
+__device__ __forceinline__ void lds_read4(intx4* o, unsigned addr) {
   asm volatile(
-      "ds_read_b128 %0, %16 offset:%17\n\t"
-      "ds_read_b128 %1, %16 offset:%18\n\t"
-      "ds_read_b128 %2, %16 offset:%19\n\t"
-      "ds_read_b128 %3, %16 offset:%20\n\t"
-      "ds_read_b128 %4, %16 offset:%21\n\t"
-      "ds_read_b128 %5, %16 offset:%22\n\t"
-      "ds_read_b128 %6, %16 offset:%23\n\t"
-      "ds_read_b128 %7, %16 offset:%24\n\t"
-      "ds_read_b128 %8, %16 offset:%25\n\t"
-      "ds_read_b128 %9, %16 offset:%26\n\t"
-      "ds_read_b128 %10, %16 offset:%27\n\t"
-      "ds_read_b128 %11, %16 offset:%28\n\t"
-      "ds_read_b128 %12, %16 offset:%29\n\t"
-      "ds_read_b128 %13, %16 offset:%30\n\t"
-      "ds_read_b128 %14, %16 offset:%31\n\t"
-      "ds_read_b128 %15, %16 offset:%32\n\t"
+      "ds_read_b128 %0, %4 offset:0\n\t"
+      "ds_read_b128 %1, %4 offset:512\n\t"
+      "ds_read_b128 %2, %4 offset:1024\n\t"
+      "ds_read_b128 %3, %4 offset:1536\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(addr)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_read8(intx4* o, unsigned addr) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:0\n\t"
+      "ds_read_b128 %1, %8 offset:512\n\t"
+      "ds_read_b128 %2, %8 offset:1024\n\t"
+      "ds_read_b128 %3, %8 offset:1536\n\t"
+      "ds_read_b128 %4, %8 offset:2048\n\t"
+      "ds_read_b128 %5, %8 offset:2560\n\t"
+      "ds_read_b128 %6, %8 offset:3072\n\t"
+      "ds_read_b128 %7, %8 offset:3584\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(addr)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_read16(intx4* o, unsigned addr) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:0\n\t"
+      "ds_read_b128 %1, %16 offset:512\n\t"
+      "ds_read_b128 %2, %16 offset:1024\n\t"
+      "ds_read_b128 %3, %16 offset:1536\n\t"
+      "ds_read_b128 %4, %16 offset:2048\n\t"
+      "ds_read_b128 %5, %16 offset:2560\n\t"
+      "ds_read_b128 %6, %16 offset:3072\n\t"
+      "ds_read_b128 %7, %16 offset:3584\n\t"
+      "ds_read_b128 %8, %16 offset:4096\n\t"
+      "ds_read_b128 %9, %16 offset:4608\n\t"
+      "ds_read_b128 %10, %16 offset:5120\n\t"
+      "ds_read_b128 %11, %16 offset:5632\n\t"
+      "ds_read_b128 %12, %16 offset:6144\n\t"
+      "ds_read_b128 %13, %16 offset:6656\n\t"
+      "ds_read_b128 %14, %16 offset:7168\n\t"
+      "ds_read_b128 %15, %16 offset:7680\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
         "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]),
         "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
-      : "v"(addr), "i"(P0 * 1024), "i"((P0 + 1) * 1024), "i"((P0 + 2) * 1024),
-        "i"((P0 + 3) * 1024), "i"((P0 + 4) * 1024), "i"((P0 + 5) * 1024), "i"((P0 + 6) * 1024),
-        "i"((P0 + 7) * 1024), "i"((P0 + 8) * 1024), "i"((P0 + 9) * 1024),
-        "i"((P0 + 10) * 1024), "i"((P0 + 11) * 1024), "i"((P0 + 12) * 1024),
-        "i"((P0 + 13) * 1024), "i"((P0 + 14) * 1024), "i"((P0 + 15) * 1024)
+      : "v"(addr)
       : "memory");
 }
 
-// Eight pieces, for stages of eight pieces (bf16, 64 dims).
-template <int P0>
-__device__ __forceinline__ void read8(intx4* o, unsigned addr) {
+// K and V parts of a whole stage from two lane addresses behind one wait.
+__device__ __forceinline__ void lds_read4_4(intx4* k, intx4* v, unsigned ka, unsigned va) {
   asm volatile(
-      "ds_read_b128 %0, %8 offset:%9\n\t"
-      "ds_read_b128 %1, %8 offset:%10\n\t"
-      "ds_read_b128 %2, %8 offset:%11\n\t"
-      "ds_read_b128 %3, %8 offset:%12\n\t"
-      "ds_read_b128 %4, %8 offset:%13\n\t"
-      "ds_read_b128 %5, %8 offset:%14\n\t"
-      "ds_read_b128 %6, %8 offset:%15\n\t"
-      "ds_read_b128 %7, %8 offset:%16\n\t"
+      "ds_read_b128 %0, %8 offset:0\n\t"
+      "ds_read_b128 %1, %8 offset:512\n\t"
+      "ds_read_b128 %2, %8 offset:1024\n\t"
+      "ds_read_b128 %3, %8 offset:1536\n\t"
+      "ds_read_b128 %4, %9 offset:0\n\t"
+      "ds_read_b128 %5, %9 offset:512\n\t"
+      "ds_read_b128 %6, %9 offset:1024\n\t"
+      "ds_read_b128 %7, %9 offset:1536\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
-        "=&v"(o[6]), "=&v"(o[7])
-      : "v"(addr), "i"(P0 * 1024), "i"((P0 + 1) * 1024), "i"((P0 + 2) * 1024),
-        "i"((P0 + 3) * 1024), "i"((P0 + 4) * 1024), "i"((P0 + 5) * 1024), "i"((P0 + 6) * 1024),
-        "i"((P0 + 7) * 1024)
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
+        "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ka), "v"(va)
       : "memory");
+}
+
+__device__ __forceinline__ void lds_read8_8(intx4* k, intx4* v, unsigned ka, unsigned va) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:0\n\t"
+      "ds_read_b128 %1, %16 offset:512\n\t"
+      "ds_read_b128 %2, %16 offset:1024\n\t"
+      "ds_read_b128 %3, %16 offset:1536\n\t"
+      "ds_read_b128 %4, %16 offset:2048\n\t"
+      "ds_read_b128 %5, %16 offset:2560\n\t"
+      "ds_read_b128 %6, %16 offset:3072\n\t"
+      "ds_read_b128 %7, %16 offset:3584\n\t"
+      "ds_read_b128 %8, %17 offset:0\n\t"
+      "ds_read_b128 %9, %17 offset:512\n\t"
+      "ds_read_b128 %10, %17 offset:1024\n\t"
+      "ds_read_b128 %11, %17 offset:1536\n\t"
+      "ds_read_b128 %12, %17 offset:2048\n\t"
+      "ds_read_b128 %13, %17 offset:2560\n\t"
+      "ds_read_b128 %14, %17 offset:3072\n\t"
+      "ds_read_b128 %15, %17 offset:3584\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+        "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+        "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(ka), "v"(va)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void lds_read(intx4* o, unsigned addr) {
+  static_assert(N == 4 || N == 8 || N == 16, "part counts");
+  if constexpr (N == 4) lds_read4(o, addr);
+  else if constexpr (N == 8) lds_read8(o, addr);
+  else lds_read16(o, addr);
 }
 
 template <typename T>
@@ -281,55 +370,50 @@ __device__ __forceinline__ floatx8 frag_of<float>(const intx4* pc) {
   return floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// All fragments of a ring slot; on the stage that crosses n_keys the V
-// elements of keys past the end are zeroed (their slots may hold anything).
+// Zeroes the V elements of keys at or past n_keys (their slots may hold
+// anything, NaN included) on the stage that crosses the sequence end.
 template <typename T, int D>
-__device__ __forceinline__ void read_stage(StepFrags<T, D>& f, unsigned addr, int key0,
-                                           int n_keys, int lane) {
+__device__ __forceinline__ void zero_v_tail(intx4* vp, int key0, int n_keys, int grp) {
   using SS = StageShape<T, D>;
-  constexpr int NP = SS::NKP + SS::NVP;
-  static_assert(NP == 8 || NP == 16 || NP == 32, "stage piece counts");
-  intx4 pc[NP];
-  if constexpr (NP == 8) {
-    read8<0>(pc, addr);
-  } else {
-    read16<0>(pc, addr);
-    if constexpr (NP == 32) read16<16>(pc + 16, addr);
-  }
-  if (key0 + kStep > n_keys) {
-    const int grp = lane >> 4;
-    constexpr int E = 16 / sizeof(T);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
+  for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int h = 0; h < SS::H; ++h)
+    for (int h2 = 0; h2 < SS::H; ++h2)
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (key0 + 8 * grp + 4 * h + e >= n_keys) {
-            intx4& x = pc[SS::NKP + dt * SS::H + h];
-            if (sizeof(T) == 4) x[e] = 0;
-            else x[e / 2] &= (e & 1) ? 0x0000ffff : (int)0xffff0000;
-          }
+      for (int e = 0; e < SS::E; ++e) {
+        if (key0 + 8 * grp + SS::E * h2 + e >= n_keys) {
+          intx4& x = vp[dt * SS::H + h2];
+          if (sizeof(T) == 4) x[e] = 0;
+          else x[e / 2] &= (e & 1) ? 0x0000ffff : (int)0xffff0000;
         }
-  }
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-    for (int c = 0; c < SS::KC; ++c) f.k[t2][c] = frag_of<T>(pc + (t2 * SS::KC + c) * SS::H);
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = frag_of<T>(pc + SS::NKP + dt * SS::H);
+      }
 }
+
+template <typename T, int D, int MT>
+struct WaveState {
+  typename Frag<T>::vec qf[MT][D / 32];
+  floatx4 acc[D / 16][MT];
+  float m_run[MT], l_run[MT];
+  int blk_row[MT];
+};
 
 // One stage: S^T = K Q^T, (mask), online softmax update, O^T += V^T P^T.
 // s[T][t][j] is key key0 + 8*grp + 4*T + j against row 16t + n of the wave;
 // softmax runs in the exp2 domain with the scale folded into the exponent.
 template <typename T, int D, int MT>
-__device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
-                                             const typename Frag<T>::vec (&qf)[MT][D / 32],
-                                             floatx4 (&acc)[D / 16][MT], float (&m_run)[MT],
-                                             float (&l_run)[MT], const int (&blk_row)[MT],
-                                             const AttnArgs& a, int key0, int L, int n_keys,
-                                             int nc, int grp, bool masked) {
+__device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned kaddr, unsigned vaddr,
+                                        const AttnArgs& a, int key0, int L, int n_keys, int nc,
+                                        int grp) {
+  using SS = StageShape<T, D>;
+  intx4 kp[SS::NKP], vp[SS::NVP];
+  constexpr bool together = MT == 1 && SS::NKP == SS::NVP && SS::NKP <= 8;
+  if constexpr (together) {
+    if constexpr (SS::NKP == 4) lds_read4_4(kp, vp, kaddr, vaddr);
+    else lds_read8_8(kp, vp, kaddr, vaddr);
+  } else {
+    lds_read<SS::NKP>(kp, kaddr);
+  }
+
   floatx4 s[2][MT];
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2)
@@ -337,11 +421,15 @@ __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
     for (int t = 0; t < MT; ++t) {
       floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cc = 0; cc < D / 32; ++cc) c = Frag<T>::mma(f.k[t2][cc], qf[t][cc], c);
+      for (int cc = 0; cc < SS::KC; ++cc)
+        c = Frag<T>::mma(frag_of<T>(kp + (t2 * SS::KC + cc) * SS::H), ws.qf[t][cc], c);
       s[t2][t] = c;
     }
 
-  if (masked) {
+  if constexpr (!together) lds_read<SS::NVP>(vp, vaddr);
+  if (key0 + kStep > n_keys) zero_v_tail<T, D>(vp, key0, n_keys, grp);
+
+  if (key0 + kStep > L) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -349,7 +437,7 @@ __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int key = key0 + 8 * grp + 4 * t2 + j;
-          const int jb = key - L, i = blk_row[t];
+          const int jb = key - L, i = ws.blk_row[t];
           const bool vis = (key < L) | ((key < n_keys) & ((a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc))));
           s[t2][t][j] = vis ? s[t2][t][j] : -__builtin_inff();
         }
@@ -363,18 +451,18 @@ __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
     float mx = fmaxf(fmaxf(fmaxf(s[0][t][0], s[0][t][1]), fmaxf(s[0][t][2], s[0][t][3])),
                      fmaxf(fmaxf(s[1][t][0], s[1][t][1]), fmaxf(s[1][t][2], s[1][t][3])));
     mx = group_max4(mx) * c2;
-    m_new[t] = fmaxf(m_run[t], mx);
-    need_any |= m_new[t] > m_run[t] + kRescale;
+    m_new[t] = fmaxf(ws.m_run[t], mx);
+    need_any |= m_new[t] > ws.m_run[t] + kRescale;
   }
   if (__builtin_amdgcn_ballot_w64(need_any)) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const bool need = m_new[t] > m_run[t] + kRescale;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run[t] - m_new[t]) : 1.0f;
-      m_run[t] = need ? m_new[t] : m_run[t];
-      l_run[t] *= alpha;
+      const bool need = m_new[t] > ws.m_run[t] + kRescale;
+      const float alpha = need ? __builtin_amdgcn_exp2f(ws.m_run[t] - m_new[t]) : 1.0f;
+      ws.m_run[t] = need ? m_new[t] : ws.m_run[t];
+      ws.l_run[t] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[dt][t] *= alpha;
+      for (int dt = 0; dt < D / 16; ++dt) ws.acc[dt][t] *= alpha;
     }
   }
   typename Frag<T>::vec pf[MT];
@@ -385,49 +473,29 @@ __device__ __forceinline__ void compute_step(const StepFrags<T, D>& f,
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pv[4 * t2 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][t][j], c2, -m_run[t]));
-    l_run[t] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        pv[4 * t2 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][t][j], c2, -ws.m_run[t]));
+    ws.l_run[t] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     pf[t] = Frag<T>::pack(pv);
   }
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[dt][t] = Frag<T>::mma(f.v[dt], pf[t], acc[dt][t]);
+    for (int t = 0; t < MT; ++t)
+      ws.acc[dt][t] = Frag<T>::mma(frag_of<T>(vp + dt * SS::H), pf[t], ws.acc[dt][t]);
 }
 
 template <typename T, int D, int MT>
-struct WaveState {
-  typename Frag<T>::vec qf[MT][D / 32];
-  floatx4 acc[D / 16][MT];
-  float m_run[MT], l_run[MT];
-  int blk_row[MT];
-};
-
-// Consumes the stage at key0 from the ring slot at lane-relative LDS address addr.
-template <typename T, int D, int MT>
-__device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned addr, const AttnArgs& a,
-                                        int key0, int L, int n_keys, int nc, int lane,
-                                        bool has_rows) {
-  if (!has_rows) return;
-  StepFrags<T, D> f;
-  read_stage<T, D>(f, addr, key0, n_keys, lane);
-  compute_step<T, D, MT>(f, ws.qf, ws.acc, ws.m_run, ws.l_run, ws.blk_row, a, key0, L, n_keys,
-                         nc, lane >> 4, key0 + kStep > L);
-}
-
-// RING_KB: LDS for the stage ring; its depth NS = RING_KB KB / stage bytes
-// (at most 8) sets how many stages are in flight (NS - 1).
-template <typename T, int D, int MT, int RING_KB>
-__global__ __launch_bounds__(kWave * kWaves, (MT == 1 ? 2 : 1)) void block_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs a) {
   using SS = StageShape<T, D>;
-  constexpr int NS = RING_KB * 1024 / SS::BYTES < 8 ? RING_KB * 1024 / SS::BYTES : 8;
-  static_assert(NS >= 3, "the ring needs at least three stages");
-  __shared__ __attribute__((aligned(16))) char s_ring[NS * SS::BYTES];
-  __shared__ __attribute__((aligned(8))) int s_pages[kPageWin];
+  constexpr int NSP = SS::NSP;
+  __shared__ __attribute__((aligned(1024))) char s_ring[NSP * SS::PAIR];
+  __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((unsigned)tid >> 6);
+  const int set = wave / kRowSlots;
+  const int rs = wave % kRowSlots;
   const int n = lane & 15, grp = lane >> 4;
 
   const int unit = blockIdx.x / a.splits;
@@ -447,17 +515,16 @@ __global__ __launch_bounds__(kWave * kWaves, (MT == 1 ? 2 : 1)) void block_attn_
   const int s_lo = split * a.steps_per_split;
   const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
 
-  KvView kv;
-  kv.kbase = reinterpret_cast<const char*>(a.k) + (size_t)kvh * a.P * D * sizeof(T);
-  kv.vbase = reinterpret_cast<const char*>(a.v) + (size_t)kvh * a.P * D * sizeof(T);
-  kv.page_bytes = (size_t)a.P * D * a.Hkv * sizeof(T);
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)kvh * a.P * D * sizeof(T);
+  const char* vbase = reinterpret_cast<const char*>(a.v) + (size_t)kvh * a.P * D * sizeof(T);
+  const uint64_t page_bytes = (uint64_t)a.P * D * a.Hkv * sizeof(T);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
 
   // ---- Q^T operands of this wave's rows: lane (n, grp) holds row 16t + n,
   // dims 32c + 8*grp .. +7. Row r of the group is block token r / g, query
-  // head kvh * g + r % g.
+  // head kvh * g + r % g. Both waves of a row slot hold the same rows.
   WaveState<T, D, MT> ws;
-  const int row0 = wave * 16 * MT;
+  const int row0 = rs * 16 * MT;
   const bool has_rows = row0 < a.M;
   const T* qg = reinterpret_cast<const T*>(a.q);
 #pragma unroll
@@ -478,64 +545,96 @@ __global__ __launch_bounds__(kWave * kWaves, (MT == 1 ? 2 : 1)) void block_attn_
     for (int dt = 0; dt < D / 16; ++dt) ws.acc[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- stream the split's stages, one window of staged page ids at a time
-  const int win_steps = kPageWin / 2;  // (lo, hi) page pairs per window
-  const DmaLanes<T, D> dl = dma_lanes<T, D>(a.P, wave, lane);
-  for (int w0 = s_lo; w0 < s_hi; w0 += win_steps) {
-    const int w1 = min(s_hi, w0 + win_steps);
+  const DmaLanes<T, D> dl = dma_lanes<T, D>(a.P, rs, lane);
+  // lane-relative LDS addresses of this lane's first K and V fragment parts
+  const int hk = n >> 3, hv = grp >> 1;
+  const unsigned ring = (unsigned)(size_t)s_ring + (unsigned)set * SS::BYTES;
+  const unsigned k_lane = ring + hk * (SS::NKP / 2) * 1024 + (8 * (grp ^ hk) + (n & 7)) * 16;
+  const unsigned v_lane = ring + SS::NKP * 1024 + hv * (SS::NVP / 2) * 1024 + (16 * (grp & 1) + n) * 16;
+
+  // ---- stream the split's stages, one window of staged page offsets at a time
+  for (int w0 = s_lo; w0 < s_hi; w0 += kPageWin) {
+    const int w1 = min(s_hi, w0 + kPageWin);
+    const int ns = w1 - w0;
     __syncthreads();  // the previous window is fully consumed
-    // (lo, hi) physical pages of every stage of the window; hi = lo when the
-    // stage has one page (P = 32) or its second page lies past the sequence
-    for (int x = tid; x < 2 * (w1 - w0); x += kWave * kWaves) {
+    // byte offsets of the (lo, hi) pages of every stage of the window; hi = lo
+    // when the stage has one page (P = 32) or its second page lies past the
+    // sequence end
+    for (int x = tid; x < 2 * ns; x += kWave * kWaves) {
       const int key = (w0 + (x >> 1)) * kStep + (x & 1) * 16;
       const bool second = (x & 1) && a.P == 16 && key < n_keys;
       const int p = ptab[(second ? key : (key & ~31)) >> a.p_shift];
       const bool bad = (unsigned)p >= (unsigned)a.num_pages;
       if (bad) flag_error(a.err, kErrSlot);
-      s_pages[x] = bad ? 0 : p;
+      s_pgoff[x] = (uint64_t)(bad ? 0 : p) * page_bytes;
     }
     // Q and the page ids are in: from here on the only vector-memory loads in
     // flight are the ring's DMAs, which the waits below count by hand
     __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
     __syncthreads();
 
-    const int ns = w1 - w0;
-    const unsigned ring_lane = (unsigned)(size_t)s_ring + (unsigned)lane * 16;
-    // pages of stage t: s_pages[2t'] / [2t'+1] hold (lo, hi) of window stage t'
-    auto issue = [&](int t, int2 pg) {
-      const int key0 = (w0 + t) * kStep;
-      const char* k_lo = kv.kbase + (size_t)pg.x * kv.page_bytes;
-      const char* k_hi = kv.kbase + (size_t)pg.y * kv.page_bytes;
-      const char* v_lo = kv.vbase + (size_t)pg.x * kv.page_bytes;
-      const char* v_hi = kv.vbase + (size_t)pg.y * kv.page_bytes;
-      char* slot = s_ring + (t % NS) * SS::BYTES;
-      if (key0 + kStep <= n_keys)
-        issue_dma<T, D, false>(slot, dl, k_lo, k_hi, v_lo, v_hi, key0, n_keys);
-      else
-        issue_dma<T, D, true>(slot, dl, k_lo, k_hi, v_lo, v_hi, key0, n_keys);
+    // pair u holds window stages 2u (set 0) and 2u + 1 (set 1) in ring slot u % NSP
+    const int npairs = (ns + 1) >> 1;
+    const int mine = (ns - set + 1) >> 1;  // pairs with a stage for this wave's set
+    auto offsets = [&](int u) {
+      const int t = min(2 * u + set, ns - 1);
+      return reinterpret_cast<const uint4*>(s_pgoff)[t];
     };
-    auto stage_pages = [&](int t) {
-      const int2 pg = reinterpret_cast<const int2*>(s_pages)[t];
-      return int2{__builtin_amdgcn_readfirstlane(pg.x), __builtin_amdgcn_readfirstlane(pg.y)};
+    auto issue = [&](int u, uint4 po) {
+      issue_stage<T, D>(s_ring + (u % NSP) * SS::PAIR + set * SS::BYTES, rs, dl,
+                        half_bases(kbase, vbase, po), (w0 + 2 * u + set) * kStep, n_keys,
+                        2 * u + set < ns);
     };
-    // NS - 1 stages in flight; stage t lands in ring slot t % NS. Each wave
-    // waits for its own DMA share of stage t (vmcnt counts this wave's
-    // loads in issue order), the barrier publishes all shares, and the slot
-    // consumed one step earlier is refilled with stage t + NS - 1.
-    for (int t = 0; t < NS - 1 && t < ns; ++t) issue(t, stage_pages(t));
-    int2 next_pg = stage_pages(min(NS - 1, ns - 1));
-    for (int t = 0; t < ns; ++t) {
-      wait_stages<SS::PW>(min(NS - 2, ns - 1 - t));
+    // NSP - 1 pairs in flight. Each wave waits for its own DMA share of pair
+    // u (vmcnt counts this wave's loads in issue order), the barrier
+    // publishes every share, and the slot consumed one pair earlier is
+    // refilled with pair u + NSP - 1.
+    for (int u = 0; u < NSP - 1 && u < npairs; ++u) issue(u, offsets(u));
+    uint4 po_next = offsets(NSP - 1);
+    for (int u = 0; u < npairs; ++u) {
+      wait_stages<SS::PW>(max(0, min(NSP - 2, mine - 1 - u)));
       asm volatile("s_barrier" ::: "memory");
-      if (t + NS - 1 < ns) issue(t + NS - 1, next_pg);
-      next_pg = stage_pages(min(t + NS, ns - 1));
-      consume<T, D, MT>(ws, ring_lane + (t % NS) * SS::BYTES, a, (w0 + t) * kStep, L, n_keys, nc,
-                        lane, has_rows);
+      if (u + NSP - 1 < npairs) issue(u + NSP - 1, po_next);
+      po_next = offsets(u + NSP);
+      const int t = 2 * u + set;
+      if (t < ns && has_rows) {
+        const unsigned so = (u % NSP) * SS::PAIR;
+        consume<T, D, MT>(ws, k_lane + so, v_lane + so, a, (w0 + t) * kStep, L, n_keys, nc, grp);
+      }
     }
   }
 
+  // ---- merge the two key halves of every row slot through LDS
+  static_assert(kRowSlots * (D / 16) * MT * 1024 + kRowSlots * MT * 512 <= NSP * SS::PAIR,
+                "merge buffers fit the ring");
+  __syncthreads();  // every stage consumed: the ring is free
+  floatx4* x_acc = reinterpret_cast<floatx4*>(s_ring) + (size_t)rs * (D / 16) * MT * 64;
+  float2* x_ml = reinterpret_cast<float2*>(s_ring + kRowSlots * (D / 16) * MT * 1024) +
+                 (size_t)rs * MT * 64;
+  if (set == 1 && has_rows) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) x_acc[(dt * MT + t) * 64 + lane] = ws.acc[dt][t];
+      x_ml[t * 64 + lane] = float2{ws.m_run[t], ws.l_run[t]};
+    }
+  }
+  __syncthreads();
+  if (set == 1 || !has_rows) return;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const float2 ml = x_ml[t * 64 + lane];
+    const float m = fmaxf(ws.m_run[t], ml.x);
+    const float a0 = __builtin_amdgcn_exp2f(ws.m_run[t] - m);
+    const float a1 = __builtin_amdgcn_exp2f(ml.x - m);
+    ws.m_run[t] = m;
+    ws.l_run[t] = a0 * ws.l_run[t] + a1 * ml.y;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      ws.acc[dt][t] = a0 * ws.acc[dt][t] + a1 * x_acc[(dt * MT + t) * 64 + lane];
+  }
+
   // ---- this wave's rows: normalise and write, or store the split's partial state
-  if (!has_rows) return;
   const bool single = a.splits == 1;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -605,40 +704,27 @@ __global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ launch
-template <typename T, int D, int MT>
-static void launch_mt(const AttnArgs& a, dim3 grid, dim3 block, int ring_kb, hipStream_t stream) {
-  // fp32 stages of 128 dims are 32 KB: only the large ring holds 3 of them
-  if constexpr (sizeof(T) == 4 && D == 128) {
-    hipLaunchKernelGGL((block_attn_kernel<T, D, MT, 128>), grid, block, 0, stream, a);
-  } else {
-    if (ring_kb >= 128)
-      hipLaunchKernelGGL((block_attn_kernel<T, D, MT, 128>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((block_attn_kernel<T, D, MT, 64>), grid, block, 0, stream, a);
-  }
-}
-
 template <typename T, int D>
-static hipError_t launch_dt(const AttnArgs& a, int total_blocks, int ring_kb, hipStream_t stream) {
+static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t stream) {
   const dim3 grid(total_blocks), block(kWave * kWaves);
   if (a.M > 64)
-    launch_mt<T, D, 2>(a, grid, block, ring_kb, stream);
+    hipLaunchKernelGGL((block_attn_kernel<T, D, 2>), grid, block, 0, stream, a);
   else
-    launch_mt<T, D, 1>(a, grid, block, ring_kb, stream);
+    hipLaunchKernelGGL((block_attn_kernel<T, D, 1>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL((block_attn_combine_kernel<T, D>), dim3(a.bs * a.Hkv), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks, int ring_kb,
+hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks,
                              hipStream_t stream) {
   if (bf16) {
-    return D == 64 ? launch_dt<__bf16, 64>(a, total_blocks, ring_kb, stream)
-                   : launch_dt<__bf16, 128>(a, total_blocks, ring_kb, stream);
+    return D == 64 ? launch_dt<__bf16, 64>(a, total_blocks, stream)
+                   : launch_dt<__bf16, 128>(a, total_blocks, stream);
   }
-  return D == 64 ? launch_dt<float, 64>(a, total_blocks, ring_kb, stream)
-                 : launch_dt<float, 128>(a, total_blocks, ring_kb, stream);
+  return D == 64 ? launch_dt<float, 64>(a, total_blocks, stream)
+                 : launch_dt<float, 128>(a, total_blocks, stream);
 }
 
 }  // namespace specattn

@@ -27,7 +27,7 @@ int ilog2_exact(int x) {
   return (1 << s) == x ? s : -1;
 }
 
-// Optional overrides read once (tuning knobs): split count, LDS ring size (KB).
+// Optional override read once (a tuning knob): the split count.
 int env_int(const char* name) {
   const char* s = std::getenv(name);
   return s ? std::atoi(s) : 0;
@@ -35,10 +35,6 @@ int env_int(const char* name) {
 int env_splits() {
   static int v = env_int("SPECATTN_SPLITS");
   return v;
-}
-int env_ring_kb() {
-  static int v = env_int("SPECATTN_RING_KB");
-  return v > 0 ? v : 64;
 }
 
 struct AttnPlan {
@@ -196,7 +192,7 @@ SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req,
   const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt((float)D) : sm_scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(launch_block_attn(a, dtype == SPEC_BF16, D, plan.units * plan.splits,
-                                      env_ring_kb(), static_cast<hipStream_t>(stream)));
+                                      static_cast<hipStream_t>(stream)));
 }
 
 SPEC_API int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* tokens,

@@ -24,7 +24,7 @@ struct AttnArgs {
   float scale_log2;  // sm_scale * log2(e)
 };
 
-hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks, int ring_kb,
+hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks,
                              hipStream_t stream);
 
 struct PrepareArgs {
