@@ -23,9 +23,11 @@
 //     order inside a stage is chosen so that this holds for P = 16), so its
 //     address is an SGPR page base plus a per-lane offset fixed for the whole
 //     kernel. Each fragment lands where the MFMA lane that consumes it reads
-//     it with one conflict-free ds_read_b128. A 128 KB ring of stage pairs
-//     keeps three pairs in flight; vmcnt waits are counted by hand and one
-//     barrier per pair publishes a pair to both sets.
+//     it with one conflict-free ds_read_b128. A ring of three stage pairs
+//     keeps two pairs (64 KB for bf16, 128 dims) in flight per CU; the loads
+//     carry the non-temporal cache policy (the KV stream is read once), which
+//     measurably raises the HBM read rate. vmcnt waits are counted by hand and
+//     one barrier per pair publishes a pair to both sets.
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16
 //     (eight v_mfma_f32_16x16x4f32 for fp32 inputs). Keys are permuted inside
 //     a stage so that the accumulator layout of S^T is directly the B operand
@@ -51,7 +53,8 @@ constexpr int kStep = 32;             // keys per stage
 constexpr int kRowSlots = 4;          // row slots per workgroup
 constexpr int kSets = 2;              // key halves (stage parity) per row slot
 constexpr int kWaves = kRowSlots * kSets;
-constexpr int kRingBytes = 128 * 1024;
+constexpr int kRingBytes = 128 * 1024;  // ring capacity; at most 3 stage pairs are used
+constexpr int kNonTemporal = 2;       // cache policy of the KV loads: streamed, read once
 constexpr int kPageWin = 512;         // stages whose page offsets are staged at once
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
@@ -129,7 +132,7 @@ struct StageShape {
   static constexpr int PW = KPW + VPW;
   static constexpr int BYTES = (NKP + NVP) * 1024;
   static constexpr int PAIR = 2 * BYTES;
-  static constexpr int NSP = kRingBytes / PAIR < 4 ? kRingBytes / PAIR : 4;  // ring depth (pairs)
+  static constexpr int NSP = kRingBytes / PAIR < 3 ? kRingBytes / PAIR : 3;  // ring depth (pairs)
   static_assert(NKP % kRowSlots == 0 && NVP % kRowSlots == 0 && KPW > 0 && VPW > 0,
                 "pieces must split over the 4 waves of a set");
   static_assert(NSP >= 2, "the ring holds at least two stage pairs");
@@ -219,7 +222,7 @@ __device__ __forceinline__ void issue_dma(char* slot, int r, const DmaLanes<T, D
     const char* src = base + dl.off[j];
     if (TAIL && key0 + dl.key[j] >= n_keys) src = reinterpret_cast<const char*>(g_zero16);
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(slot + p * 1024),
-                                     16, 0, 0);
+                                     16, 0, kNonTemporal);
   }
 #pragma unroll
   for (int j = 0; j < SS::VPW; ++j) {
@@ -227,7 +230,7 @@ __device__ __forceinline__ void issue_dma(char* slot, int r, const DmaLanes<T, D
     const char* base = p >= SS::NVP / 2 ? hb.v1 : hb.v0;
     __builtin_amdgcn_global_load_lds(base + dl.off[SS::KPW + j],
                                      (__attribute__((address_space(3))) void*)(slot + (SS::NKP + p) * 1024),
-                                     16, 0, 0);
+                                     16, 0, kNonTemporal);
   }
 }
 
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
   using SS = StageShape<T, D>;
   constexpr int NSP = SS::NSP;
   __shared__ __attribute__((aligned(1024))) char s_ring[NSP * SS::PAIR];
-  __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];
+  __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];  // (lo, hi) per stage
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -503,26 +506,17 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
   const int b = unit / a.Hkv;
   const int kvh = unit - b * a.Hkv;
 
-  int L = a.seq_lens[b];
-  const int cap = a.max_pages * a.P - a.B;
-  if (L < 0 || L > cap) {
-    if (tid == 0 && split == 0) flag_error(a.err, kErrCapacity);
-    L = L < 0 ? 0 : cap;
-  }
-  const int n_keys = L + a.B;
-  const int nc = a.nc_per_req ? a.nc_per_req[b] : a.n_causal;
-  const int n_steps = (n_keys + kStep - 1) / kStep;
-  const int s_lo = split * a.steps_per_split;
-  const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
-
   const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)kvh * a.P * D * sizeof(T);
   const char* vbase = reinterpret_cast<const char*>(a.v) + (size_t)kvh * a.P * D * sizeof(T);
   const uint64_t page_bytes = (uint64_t)a.P * D * a.Hkv * sizeof(T);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+  const int s_lo = split * a.steps_per_split;
 
-  // ---- Q^T operands of this wave's rows: lane (n, grp) holds row 16t + n,
-  // dims 32c + 8*grp .. +7. Row r of the group is block token r / g, query
-  // head kvh * g + r % g. Both waves of a row slot hold the same rows.
+  // ---- loads that do not depend on the sequence length go out first, so
+  // that their latency overlaps the length's.
+  // Q^T operands of this wave's rows: lane (n, grp) holds row 16t + n, dims
+  // 32c + 8*grp .. +7. Row r of the group is block token r / g, query head
+  // kvh * g + r % g. Both waves of a row slot hold the same rows.
   WaveState<T, D, MT> ws;
   const int row0 = rs * 16 * MT;
   const bool has_rows = row0 < a.M;
@@ -544,6 +538,27 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) ws.acc[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  // Page-table entries of the first window's stage `tid` (thread tid stages
+  // stage tid of each window): the (lo, hi) pages of keys 32 t and 32 t + 16,
+  // read whenever they lie inside the table row; validated once the length
+  // says which stages exist.
+  static_assert(kPageWin == kWave * kWaves, "one thread per staged stage");
+  auto table_pair = [&](int t) {
+    const int i_lo = (t * kStep) >> a.p_shift, i_hi = (t * kStep + 16) >> a.p_shift;
+    return int2{i_lo < a.max_pages ? ptab[i_lo] : 0, i_hi < a.max_pages ? ptab[i_hi] : 0};
+  };
+  const int2 first_pages = table_pair(s_lo + tid);
+
+  int L = a.seq_lens[b];
+  const int cap = a.max_pages * a.P - a.B;
+  if (L < 0 || L > cap) {
+    if (tid == 0 && split == 0) flag_error(a.err, kErrCapacity);
+    L = L < 0 ? 0 : cap;
+  }
+  const int n_keys = L + a.B;
+  const int nc = a.nc_per_req ? a.nc_per_req[b] : a.n_causal;
+  const int n_steps = (n_keys + kStep - 1) / kStep;
+  const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
 
   const DmaLanes<T, D> dl = dma_lanes<T, D>(a.P, rs, lane);
   // lane-relative LDS addresses of this lane's first K and V fragment parts
@@ -560,13 +575,16 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
     // byte offsets of the (lo, hi) pages of every stage of the window; hi = lo
     // when the stage has one page (P = 32) or its second page lies past the
     // sequence end
-    for (int x = tid; x < 2 * ns; x += kWave * kWaves) {
-      const int key = (w0 + (x >> 1)) * kStep + (x & 1) * 16;
-      const bool second = (x & 1) && a.P == 16 && key < n_keys;
-      const int p = ptab[(second ? key : (key & ~31)) >> a.p_shift];
-      const bool bad = (unsigned)p >= (unsigned)a.num_pages;
-      if (bad) flag_error(a.err, kErrSlot);
-      s_pgoff[x] = (uint64_t)(bad ? 0 : p) * page_bytes;
+    if (tid < ns) {
+      const int2 pg = w0 == s_lo ? first_pages : table_pair(w0 + tid);
+      const bool second = a.P == 16 && (w0 + tid) * kStep + 16 < n_keys;
+      const bool bad_lo = (unsigned)pg.x >= (unsigned)a.num_pages;
+      const bool bad_hi = second && (unsigned)pg.y >= (unsigned)a.num_pages;
+      if (bad_lo || bad_hi) flag_error(a.err, kErrSlot);
+      const uint64_t lo = (uint64_t)(bad_lo ? 0 : pg.x) * page_bytes;
+      const uint64_t hi = second ? (uint64_t)(bad_hi ? 0 : pg.y) * page_bytes : lo;
+      reinterpret_cast<uint4*>(s_pgoff)[tid] =
+          uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
     }
     // Q and the page ids are in: from here on the only vector-memory loads in
     // flight are the ring's DMAs, which the waits below count by hand
