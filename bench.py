@@ -183,21 +183,27 @@ def main():
     else:
         tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    # every call is checked once; the timed loop re-enqueues pre-marshalled calls
+    prep_call, _ = va.prepare_block_call(vid, seq, table, cfg.page, B, 0, x.num_pages,
+                                         None if mode == synth.BIDIR else dr, out=prep_out,
+                                         err=err)
+    attn_calls = [va.block_attn_call(mode, s["q"], s["k"], s["v"], table, seq, max_kv,
+                                     n_causal=cfg.n_causal, out=o, ws=ws_attn, err=err)[0]
+                  for s in sets]
+    if acc is not None:
+        tail_calls = [va.accept_call(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out,
+                                     ws=ws_acc, err=err)[0] for s in sets]
+    else:
+        tail_calls = [va.draft_argmax_call(s["logits"], out=tokens)[0] for s in sets]
 
     def step(i, ev=None):
-        s = sets[i % copies]
-        va.prepare_block(vid, seq, table, cfg.page, B, 0, x.num_pages,
-                         None if mode == synth.BIDIR else dr, out=prep_out, err=err)
+        prep_call()
         if ev is not None:
             ev[0].record(stream)
-        va.block_attn(mode, s["q"], s["k"], s["v"], table, seq, max_kv, n_causal=cfg.n_causal,
-                      out=o, ws=ws_attn, err=err)
+        attn_calls[i % copies]()
         if ev is not None:
             ev[1].record(stream)
-        if acc is not None:
-            va.accept(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out, ws=ws_acc, err=err)
-        else:
-            va.draft_argmax(s["logits"], out=tokens)
+        tail_calls[i % copies]()
         if ev is not None:
             ev[2].record(stream)
 

@@ -92,8 +92,15 @@ def test_block_attn_workspace_planning(lib):
     assert small > 0
     assert _attn(lib, bs=2, max_kv=8192, ws_bytes=small - 1) == b.SPEC_ENOSPC
     assert _attn(lib, bs=2, max_kv=8192, ws=None, ws_bytes=small) == b.SPEC_ENOSPC
-    # enough units to fill the chip -> no workspace at all
-    assert lib.block_attn_workspace_bytes(256, 16, 32, 8, 128, 9232) == 0
+    # enough units to fill the chip, short contexts -> one workgroup per unit,
+    # no workspace at all
+    assert lib.block_attn_workspace_bytes(32, 16, 32, 8, 128, 1040) == 0
+    # large batches take the balanced schedule: two partial slots of M x (D + 2)
+    # floats per workgroup (256), whatever the batch size
+    bal = 2 * 256 * 64 * (128 + 2) * 4
+    assert bal <= lib.block_attn_workspace_bytes(256, 16, 32, 8, 128, 9232) <= bal + 256
+    assert lib.block_attn_workspace_bytes(128, 16, 32, 8, 128, 4112) == \
+        lib.block_attn_workspace_bytes(256, 16, 32, 8, 128, 9232)
     assert lib.block_attn_workspace_bytes(0, 16, 32, 8, 128, 9232) == 0
 
 

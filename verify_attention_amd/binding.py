@@ -2,7 +2,10 @@
 
 Argument marshalling only: torch tensors are checked for device, dtype, shape
 and contiguity, their data pointers and the current HIP stream are handed to
-the C ABI, and a negative status raises. Every step of the computation runs in
+the C ABI, and a negative status raises. Each entry point also has a `*_call`
+form that checks once and returns an `enqueue()` closure re-issuing the same
+call with the pre-marshalled pointers (for loops that launch the same round
+many times without re-checking). Every step of the computation runs in
 the library's HIP kernels; there is no other implementation behind these
 names, so a missing library or device is an error, never a fallback.
 """
@@ -135,9 +138,9 @@ def workspace(nbytes, device="cuda"):
 
 
 # -------------------------------------------------------------------- calls
-def prepare_block(verified_id, seq_lens, page_table, page_size, block, mask_token_id, num_pages,
-                  draft_tokens=None, out=None, err=None, stream=None):
-    """Block ids, positions and KV slots of one round (spec_prepare_block)."""
+def prepare_block_call(verified_id, seq_lens, page_table, page_size, block, mask_token_id,
+                       num_pages, draft_tokens=None, out=None, err=None, stream=None):
+    """Checks the arguments of spec_prepare_block once and returns (enqueue, out)."""
     torch = _torch()
     bs = verified_id.shape[0]
     _need(verified_id, "verified_id", torch.int32, (bs,))
@@ -150,20 +153,35 @@ def prepare_block(verified_id, seq_lens, page_table, page_size, block, mask_toke
                     for _ in range(3))
     for t, nm in zip(out, ("block_ids", "positions", "cache_loc")):
         _need(t, nm, torch.int32, (bs, block))
-    st = load().spec_prepare_block(bs, block, page_size, page_table.shape[1], num_pages,
-                                   mask_token_id, _ptr(verified_id), _ptr(seq_lens),
-                                   _ptr(page_table), _ptr(draft_tokens), _ptr(out[0]),
-                                   _ptr(out[1]), _ptr(out[2]), _ptr(err), _stream(stream))
-    _check(st, "spec_prepare_block")
+    args = (bs, block, page_size, page_table.shape[1], num_pages, mask_token_id, _ptr(verified_id),
+            _ptr(seq_lens), _ptr(page_table), _ptr(draft_tokens), _ptr(out[0]), _ptr(out[1]),
+            _ptr(out[2]), _ptr(err), _stream(stream))
+    fn = load().spec_prepare_block
+    keep = (verified_id, seq_lens, page_table, draft_tokens, out, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_prepare_block")
+
+    return enqueue, out
+
+
+def prepare_block(verified_id, seq_lens, page_table, page_size, block, mask_token_id, num_pages,
+                  draft_tokens=None, out=None, err=None, stream=None):
+    """Block ids, positions and KV slots of one round (spec_prepare_block)."""
+    enqueue, out = prepare_block_call(verified_id, seq_lens, page_table, page_size, block,
+                                      mask_token_id, num_pages, draft_tokens, out, err, stream)
+    enqueue()
     return out
 
 
-def block_attn(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n_causal=0,
-               n_causal_per_req=None, sm_scale=0.0, out=None, lse=None, ws=None, err=None,
-               stream=None):
-    """Block-query attention over the paged cache (block_attn).
-
-    q [bs, B, Hq, D]; k_pool [pages, Hkv, P, D]; v_pool [pages, Hkv, D, P]."""
+def block_attn_call(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n_causal=0,
+                    n_causal_per_req=None, sm_scale=0.0, out=None, lse=None, ws=None, err=None,
+                    stream=None):
+    """Checks the arguments of block_attn once and returns (enqueue, out): each
+    enqueue() queues the same call again with the pre-marshalled pointers."""
     torch = _torch()
     bs, B, hq, d = q.shape
     num_pages, hkv, P, d2 = k_pool.shape
@@ -185,32 +203,64 @@ def block_attn(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n_caus
     need = attn_workspace_bytes(bs, B, hq, hkv, d, max_kv_len)
     if ws is None and need > 0:
         ws = workspace(need, q.device)
-    st = load().block_attn(mode, n_causal, _ptr(n_causal_per_req), dt, bs, B, hq, hkv, d, P,
-                           page_table.shape[1], num_pages, max_kv_len, _ptr(q), _ptr(k_pool),
-                           _ptr(v_pool), _ptr(page_table), _ptr(seq_lens), sm_scale, _ptr(out),
-                           _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _ptr(err),
-                           _stream(stream))
-    _check(st, "block_attn")
+    args = (mode, n_causal, _ptr(n_causal_per_req), dt, bs, B, hq, hkv, d, P, page_table.shape[1],
+            num_pages, max_kv_len, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+            _ptr(seq_lens), sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
+            0 if ws is None else ws.numel(), _ptr(err), _stream(stream))
+    fn = load().block_attn
+    keep = (q, k_pool, v_pool, page_table, seq_lens, n_causal_per_req, out, lse, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "block_attn")
+
+    return enqueue, out
+
+
+def block_attn(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n_causal=0,
+               n_causal_per_req=None, sm_scale=0.0, out=None, lse=None, ws=None, err=None,
+               stream=None):
+    """Block-query attention over the paged cache (block_attn).
+
+    q [bs, B, Hq, D]; k_pool [pages, Hkv, P, D]; v_pool [pages, Hkv, D, P]."""
+    enqueue, out = block_attn_call(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len,
+                                   n_causal, n_causal_per_req, sm_scale, out, lse, ws, err, stream)
+    enqueue()
     return out
 
 
-def draft_argmax(logits, out=None, stream=None):
-    """Greedy draft tokens: lowest-index argmax of each row of logits [rows, V]."""
+def draft_argmax_call(logits, out=None, stream=None):
+    """Checks the arguments of spec_draft_argmax once and returns (enqueue, out)."""
     torch = _torch()
     _need(logits, "logits")
     rows, V = logits.shape
     if out is None:
         out = torch.empty(rows, dtype=torch.int32, device=logits.device)
     _need(out, "tokens", torch.int32, (rows,))
-    st = load().spec_draft_argmax(rows, V, _dtype_code(logits), _ptr(logits), _ptr(out),
-                                  _stream(stream))
-    _check(st, "spec_draft_argmax")
+    args = (rows, V, _dtype_code(logits), _ptr(logits), _ptr(out), _stream(stream))
+    fn = load().spec_draft_argmax
+    keep = (logits, out)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_draft_argmax")
+
+    return enqueue, out
+
+
+def draft_argmax(logits, out=None, stream=None):
+    """Greedy draft tokens: lowest-index argmax of each row of logits [rows, V]."""
+    enqueue, out = draft_argmax_call(logits, out, stream)
+    enqueue()
     return out
 
 
-def accept(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, stream=None):
-    """Speculative accept / bonus (spec_accept). Returns a dict of int32 tensors:
-    accept_len, commit_len, bonus, out_tokens [bs, K+1], new_seq_lens."""
+def accept_call(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, stream=None):
+    """Checks the arguments of spec_accept once and returns (enqueue, out)."""
     torch = _torch()
     bs, K1, V = p.shape
     K = K1 - 1
@@ -229,10 +279,25 @@ def accept(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, 
                    new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
     if ws is None:
         ws = workspace(accept_workspace_bytes(bs, K, V, greedy), dev)
-    st = load().spec_accept(bs, K, V, int(bool(greedy)), _ptr(p), _ptr(q), _ptr(draft), _ptr(u),
-                            _ptr(seq_lens), _ptr(out["accept_len"]), _ptr(out["commit_len"]),
-                            _ptr(out["bonus"]), _ptr(out["out_tokens"]),
-                            _ptr(out["new_seq_lens"]), _ptr(ws), ws.numel(), _ptr(err),
-                            _stream(stream))
-    _check(st, "spec_accept")
+    args = (bs, K, V, int(bool(greedy)), _ptr(p), _ptr(q), _ptr(draft), _ptr(u), _ptr(seq_lens),
+            _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
+            _ptr(out["out_tokens"]), _ptr(out["new_seq_lens"]), _ptr(ws), ws.numel(), _ptr(err),
+            _stream(stream))
+    fn = load().spec_accept
+    keep = (p, q, draft, u, seq_lens, out, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_accept")
+
+    return enqueue, out
+
+
+def accept(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, stream=None):
+    """Speculative accept / bonus (spec_accept). Returns a dict of int32 tensors:
+    accept_len, commit_len, bonus, out_tokens [bs, K+1], new_seq_lens."""
+    enqueue, out = accept_call(p, q, draft, u, seq_lens, greedy, out, ws, err, stream)
+    enqueue()
     return out

@@ -400,24 +400,31 @@ struct WaveState {
   int blk_row[MT];
 };
 
-// One stage: S^T = K Q^T, (mask), online softmax update, O^T += V^T P^T.
+// A stage is consumed in two halves so that the two waves sharing a SIMD can
+// run them out of phase:
+//   front: read the stage's K and V fragments from the ring, S^T = K Q^T;
+//   back:  mask, online softmax update, O^T += V^T P^T (registers only).
 // s[T][t][j] is key key0 + 8*grp + 4*T + j against row 16t + n of the wave;
 // softmax runs in the exp2 domain with the scale folded into the exponent.
 template <typename T, int D, int MT>
-__device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned kaddr, unsigned vaddr,
-                                        const AttnArgs& a, int key0, int L, int n_keys, int nc,
-                                        int grp) {
+struct StageRegs {
+  floatx4 s[2][MT];
+  intx4 vp[StageShape<T, D>::NVP];
+  int key0;
+};
+
+template <typename T, int D, int MT>
+__device__ __forceinline__ void stage_front(StageRegs<T, D, MT>& st, const WaveState<T, D, MT>& ws,
+                                            unsigned kaddr, unsigned vaddr, int key0) {
   using SS = StageShape<T, D>;
-  intx4 kp[SS::NKP], vp[SS::NVP];
+  intx4 kp[SS::NKP];
   constexpr bool together = MT == 1 && SS::NKP == SS::NVP && SS::NKP <= 8;
   if constexpr (together) {
-    if constexpr (SS::NKP == 4) lds_read4_4(kp, vp, kaddr, vaddr);
-    else lds_read8_8(kp, vp, kaddr, vaddr);
+    if constexpr (SS::NKP == 4) lds_read4_4(kp, st.vp, kaddr, vaddr);
+    else lds_read8_8(kp, st.vp, kaddr, vaddr);
   } else {
     lds_read<SS::NKP>(kp, kaddr);
   }
-
-  floatx4 s[2][MT];
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -426,11 +433,18 @@ __device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned kaddr,
 #pragma unroll
       for (int cc = 0; cc < SS::KC; ++cc)
         c = Frag<T>::mma(frag_of<T>(kp + (t2 * SS::KC + cc) * SS::H), ws.qf[t][cc], c);
-      s[t2][t] = c;
+      st.s[t2][t] = c;
     }
+  if constexpr (!together) lds_read<SS::NVP>(st.vp, vaddr);
+  st.key0 = key0;
+}
 
-  if constexpr (!together) lds_read<SS::NVP>(vp, vaddr);
-  if (key0 + kStep > n_keys) zero_v_tail<T, D>(vp, key0, n_keys, grp);
+template <typename T, int D, int MT>
+__device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T, D, MT>& ws,
+                                           const AttnArgs& a, int L, int n_keys, int nc, int grp) {
+  using SS = StageShape<T, D>;
+  const int key0 = st.key0;
+  if (key0 + kStep > n_keys) zero_v_tail<T, D>(st.vp, key0, n_keys, grp);
 
   if (key0 + kStep > L) {
 #pragma unroll
@@ -442,7 +456,7 @@ __device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned kaddr,
           const int key = key0 + 8 * grp + 4 * t2 + j;
           const int jb = key - L, i = ws.blk_row[t];
           const bool vis = (key < L) | ((key < n_keys) & ((a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc))));
-          s[t2][t][j] = vis ? s[t2][t][j] : -__builtin_inff();
+          st.s[t2][t][j] = vis ? st.s[t2][t][j] : -__builtin_inff();
         }
   }
 
@@ -451,8 +465,9 @@ __device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned kaddr,
   bool need_any = false;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    float mx = fmaxf(fmaxf(fmaxf(s[0][t][0], s[0][t][1]), fmaxf(s[0][t][2], s[0][t][3])),
-                     fmaxf(fmaxf(s[1][t][0], s[1][t][1]), fmaxf(s[1][t][2], s[1][t][3])));
+    const floatx4 s0 = st.s[0][t], s1 = st.s[1][t];
+    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
     mx = group_max4(mx) * c2;
     m_new[t] = fmaxf(ws.m_run[t], mx);
     need_any |= m_new[t] > ws.m_run[t] + kRescale;
@@ -476,7 +491,7 @@ __device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned kaddr,
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pv[4 * t2 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t2][t][j], c2, -ws.m_run[t]));
+        pv[4 * t2 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[t2][t][j], c2, -ws.m_run[t]));
     ws.l_run[t] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     pf[t] = Frag<T>::pack(pv);
   }
@@ -484,42 +499,43 @@ __device__ __forceinline__ void consume(WaveState<T, D, MT>& ws, unsigned kaddr,
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
     for (int t = 0; t < MT; ++t)
-      ws.acc[dt][t] = Frag<T>::mma(frag_of<T>(vp + dt * SS::H), pf[t], ws.acc[dt][t]);
+      ws.acc[dt][t] = Frag<T>::mma(frag_of<T>(st.vp + dt * SS::H), pf[t], ws.acc[dt][t]);
 }
 
-template <typename T, int D, int MT>
-__global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs a) {
+// Per-wave constants of the stage pipeline.
+template <typename T, int D>
+struct WaveCtx {
+  int tid, lane, set, rs, n, grp;
+  DmaLanes<T, D> dl;
+  unsigned k_lane, v_lane;  // lane-relative LDS addresses of the first K / V fragment parts
+};
+
+template <typename T, int D>
+__device__ __forceinline__ WaveCtx<T, D> wave_ctx(const AttnArgs& a, const char* s_ring) {
   using SS = StageShape<T, D>;
-  constexpr int NSP = SS::NSP;
-  __shared__ __attribute__((aligned(1024))) char s_ring[NSP * SS::PAIR];
-  __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];  // (lo, hi) per stage
+  WaveCtx<T, D> c;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((unsigned)c.tid >> 6);
+  c.set = wave / kRowSlots;
+  c.rs = wave % kRowSlots;
+  c.n = c.lane & 15;
+  c.grp = c.lane >> 4;
+  c.dl = dma_lanes<T, D>(a.P, c.rs, c.lane);
+  const int hk = c.n >> 3, hv = c.grp >> 1;
+  const unsigned ring = (unsigned)(size_t)s_ring + (unsigned)c.set * SS::BYTES;
+  c.k_lane = ring + hk * (SS::NKP / 2) * 1024 + (8 * (c.grp ^ hk) + (c.n & 7)) * 16;
+  c.v_lane = ring + SS::NKP * 1024 + hv * (SS::NVP / 2) * 1024 + (16 * (c.grp & 1) + c.n) * 16;
+  return c;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((unsigned)tid >> 6);
-  const int set = wave / kRowSlots;
-  const int rs = wave % kRowSlots;
-  const int n = lane & 15, grp = lane >> 4;
-
-  const int unit = blockIdx.x / a.splits;
-  const int split = blockIdx.x - unit * a.splits;
-  const int b = unit / a.Hkv;
-  const int kvh = unit - b * a.Hkv;
-
-  const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)kvh * a.P * D * sizeof(T);
-  const char* vbase = reinterpret_cast<const char*>(a.v) + (size_t)kvh * a.P * D * sizeof(T);
-  const uint64_t page_bytes = (uint64_t)a.P * D * a.Hkv * sizeof(T);
-  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
-  const int s_lo = split * a.steps_per_split;
-
-  // ---- loads that do not depend on the sequence length go out first, so
-  // that their latency overlaps the length's.
-  // Q^T operands of this wave's rows: lane (n, grp) holds row 16t + n, dims
-  // 32c + 8*grp .. +7. Row r of the group is block token r / g, query head
-  // kvh * g + r % g. Both waves of a row slot hold the same rows.
-  WaveState<T, D, MT> ws;
+// Q^T operands of this wave's rows of unit (b, kvh): lane (n, grp) holds row
+// 16t + n, dims 32c + 8*grp .. +7. Row r of the group is block token r / g,
+// query head kvh * g + r % g. Both waves of a row slot hold the same rows.
+template <typename T, int D, int MT>
+__device__ __forceinline__ void load_q(WaveState<T, D, MT>& ws, const AttnArgs& a, int b, int kvh,
+                                       int rs, int n, int grp) {
   const int row0 = rs * 16 * MT;
-  const bool has_rows = row0 < a.M;
   const T* qg = reinterpret_cast<const T*>(a.q);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -538,52 +554,63 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) ws.acc[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  // Page-table entries of the first window's stage `tid` (thread tid stages
-  // stage tid of each window): the (lo, hi) pages of keys 32 t and 32 t + 16,
-  // read whenever they lie inside the table row; validated once the length
-  // says which stages exist.
-  static_assert(kPageWin == kWave * kWaves, "one thread per staged stage");
-  auto table_pair = [&](int t) {
-    const int i_lo = (t * kStep) >> a.p_shift, i_hi = (t * kStep + 16) >> a.p_shift;
-    return int2{i_lo < a.max_pages ? ptab[i_lo] : 0, i_hi < a.max_pages ? ptab[i_hi] : 0};
-  };
-  const int2 first_pages = table_pair(s_lo + tid);
+}
 
+// Page-table entries of stage t of a request: the pages of keys 32 t and
+// 32 t + 16, read whenever they lie inside the table row (validated later,
+// once the length says which stages exist).
+__device__ __forceinline__ int2 table_pair(const AttnArgs& a, const int32_t* ptab, int t) {
+  const int i_lo = (t * kStep) >> a.p_shift, i_hi = (t * kStep + 16) >> a.p_shift;
+  return int2{i_lo < a.max_pages ? ptab[i_lo] : 0, i_hi < a.max_pages ? ptab[i_hi] : 0};
+}
+
+// Sequence length of request b clamped to the page-table capacity.
+__device__ __forceinline__ int clamped_len(const AttnArgs& a, int b, bool flag) {
   int L = a.seq_lens[b];
   const int cap = a.max_pages * a.P - a.B;
   if (L < 0 || L > cap) {
-    if (tid == 0 && split == 0) flag_error(a.err, kErrCapacity);
+    if (flag) flag_error(a.err, kErrCapacity);
     L = L < 0 ? 0 : cap;
   }
+  return L;
+}
+
+// Streams stages [s_lo, s_hi) of unit (b, kvh), length L, through the ring
+// into this wave's softmax state. Thread tid stages the page offsets of
+// stage tid of each window (first window: the prefetched `first` entries).
+template <typename T, int D, int MT>
+__device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const AttnArgs& a,
+                                              const WaveCtx<T, D>& c, char* s_ring,
+                                              uint64_t* s_pgoff, int b, int kvh, int L, int s_lo,
+                                              int s_hi, int2 first) {
+  using SS = StageShape<T, D>;
+  constexpr int NSP = SS::NSP;
+  static_assert(kPageWin == kWave * kWaves, "one thread per staged stage");
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)kvh * a.P * D * sizeof(T);
+  const char* vbase = reinterpret_cast<const char*>(a.v) + (size_t)kvh * a.P * D * sizeof(T);
+  const uint64_t page_bytes = (uint64_t)a.P * D * a.Hkv * sizeof(T);
+  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
   const int n_keys = L + a.B;
   const int nc = a.nc_per_req ? a.nc_per_req[b] : a.n_causal;
-  const int n_steps = (n_keys + kStep - 1) / kStep;
-  const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
+  const bool has_rows = c.rs * 16 * MT < a.M;
+  const int set = c.set;
 
-  const DmaLanes<T, D> dl = dma_lanes<T, D>(a.P, rs, lane);
-  // lane-relative LDS addresses of this lane's first K and V fragment parts
-  const int hk = n >> 3, hv = grp >> 1;
-  const unsigned ring = (unsigned)(size_t)s_ring + (unsigned)set * SS::BYTES;
-  const unsigned k_lane = ring + hk * (SS::NKP / 2) * 1024 + (8 * (grp ^ hk) + (n & 7)) * 16;
-  const unsigned v_lane = ring + SS::NKP * 1024 + hv * (SS::NVP / 2) * 1024 + (16 * (grp & 1) + n) * 16;
-
-  // ---- stream the split's stages, one window of staged page offsets at a time
   for (int w0 = s_lo; w0 < s_hi; w0 += kPageWin) {
     const int w1 = min(s_hi, w0 + kPageWin);
     const int ns = w1 - w0;
-    __syncthreads();  // the previous window is fully consumed
+    __syncthreads();  // the previous window (or unit) is fully consumed
     // byte offsets of the (lo, hi) pages of every stage of the window; hi = lo
     // when the stage has one page (P = 32) or its second page lies past the
     // sequence end
-    if (tid < ns) {
-      const int2 pg = w0 == s_lo ? first_pages : table_pair(w0 + tid);
-      const bool second = a.P == 16 && (w0 + tid) * kStep + 16 < n_keys;
+    if (c.tid < ns) {
+      const int2 pg = w0 == s_lo ? first : table_pair(a, ptab, w0 + c.tid);
+      const bool second = a.P == 16 && (w0 + c.tid) * kStep + 16 < n_keys;
       const bool bad_lo = (unsigned)pg.x >= (unsigned)a.num_pages;
       const bool bad_hi = second && (unsigned)pg.y >= (unsigned)a.num_pages;
       if (bad_lo || bad_hi) flag_error(a.err, kErrSlot);
       const uint64_t lo = (uint64_t)(bad_lo ? 0 : pg.x) * page_bytes;
       const uint64_t hi = second ? (uint64_t)(bad_hi ? 0 : pg.y) * page_bytes : lo;
-      reinterpret_cast<uint4*>(s_pgoff)[tid] =
+      reinterpret_cast<uint4*>(s_pgoff)[c.tid] =
           uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
     }
     // Q and the page ids are in: from here on the only vector-memory loads in
@@ -599,7 +626,7 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
       return reinterpret_cast<const uint4*>(s_pgoff)[t];
     };
     auto issue = [&](int u, uint4 po) {
-      issue_stage<T, D>(s_ring + (u % NSP) * SS::PAIR + set * SS::BYTES, rs, dl,
+      issue_stage<T, D>(s_ring + (u % NSP) * SS::PAIR + set * SS::BYTES, c.rs, c.dl,
                         half_bases(kbase, vbase, po), (w0 + 2 * u + set) * kStep, n_keys,
                         2 * u + set < ns);
     };
@@ -609,27 +636,51 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
     // refilled with pair u + NSP - 1.
     for (int u = 0; u < NSP - 1 && u < npairs; ++u) issue(u, offsets(u));
     uint4 po_next = offsets(NSP - 1);
+    // Between two barriers set 0 runs the front then the back half of its
+    // stage; set 1 first finishes the back half of its previous stage (held
+    // in registers across the barrier), then runs the front half of its new
+    // one. The two waves of a SIMD thus work on different halves at once:
+    // one reads LDS and issues S MFMAs while the other runs the softmax.
+    StageRegs<T, D, MT> st;
+    bool pending = false;
     for (int u = 0; u < npairs; ++u) {
       wait_stages<SS::PW>(max(0, min(NSP - 2, mine - 1 - u)));
       asm volatile("s_barrier" ::: "memory");
       if (u + NSP - 1 < npairs) issue(u + NSP - 1, po_next);
       po_next = offsets(u + NSP);
+      if (!has_rows) continue;
+      if (pending) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
+      pending = false;
       const int t = 2 * u + set;
-      if (t < ns && has_rows) {
+      if (t < ns) {
         const unsigned so = (u % NSP) * SS::PAIR;
-        consume<T, D, MT>(ws, k_lane + so, v_lane + so, a, (w0 + t) * kStep, L, n_keys, nc, grp);
+        stage_front<T, D, MT>(st, ws, c.k_lane + so, c.v_lane + so, (w0 + t) * kStep);
+        if (set == 0) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
+        else pending = true;
       }
     }
+    if (pending) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
   }
+}
 
-  // ---- merge the two key halves of every row slot through LDS
-  static_assert(kRowSlots * (D / 16) * MT * 1024 + kRowSlots * MT * 512 <= NSP * SS::PAIR,
+// Merges the two key halves of every row slot through LDS, then writes the
+// unit's rows: normalised output (part < 0) or the unnormalised partial
+// state into partial slot `part`.
+template <typename T, int D, int MT>
+__device__ __forceinline__ void finish_unit(WaveState<T, D, MT>& ws, const AttnArgs& a,
+                                            const WaveCtx<T, D>& c, char* s_ring, int b, int kvh,
+                                            int part) {
+  using SS = StageShape<T, D>;
+  static_assert(kRowSlots * (D / 16) * MT * 1024 + kRowSlots * MT * 512 <= SS::NSP * SS::PAIR,
                 "merge buffers fit the ring");
+  const int row0 = c.rs * 16 * MT;
+  const bool has_rows = row0 < a.M;
+  const int lane = c.lane;
   __syncthreads();  // every stage consumed: the ring is free
-  floatx4* x_acc = reinterpret_cast<floatx4*>(s_ring) + (size_t)rs * (D / 16) * MT * 64;
+  floatx4* x_acc = reinterpret_cast<floatx4*>(s_ring) + (size_t)c.rs * (D / 16) * MT * 64;
   float2* x_ml = reinterpret_cast<float2*>(s_ring + kRowSlots * (D / 16) * MT * 1024) +
-                 (size_t)rs * MT * 64;
-  if (set == 1 && has_rows) {
+                 (size_t)c.rs * MT * 64;
+  if (c.set == 1 && has_rows) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -638,7 +689,7 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
     }
   }
   __syncthreads();
-  if (set == 1 || !has_rows) return;
+  if (c.set == 1 || !has_rows) return;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const float2 ml = x_ml[t * 64 + lane];
@@ -651,32 +702,260 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
     for (int dt = 0; dt < D / 16; ++dt)
       ws.acc[dt][t] = a0 * ws.acc[dt][t] + a1 * x_acc[(dt * MT + t) * 64 + lane];
   }
-
-  // ---- this wave's rows: normalise and write, or store the split's partial state
-  const bool single = a.splits == 1;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const float l_tot = group_sum4(ws.l_run[t]);
-    const int r = row0 + 16 * t + n;
+    const int r = row0 + 16 * t + c.n;
     if (r >= a.M) continue;
     const int i = r / a.g, hl = r - i * a.g;
     const size_t orow = (size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl;
-    if (single) {
+    if (part < 0) {
       const float inv = 1.0f / l_tot;
-      T* dst = reinterpret_cast<T*>(a.o) + orow * D + 4 * grp;
+      T* dst = reinterpret_cast<T*>(a.o) + orow * D + 4 * c.grp;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) Frag<T>::store4(dst + 16 * dt, ws.acc[dt][t] * inv);
-      if (a.lse && grp == 0) a.lse[orow] = (ws.m_run[t] + __log2f(l_tot)) * kLn2;
+      if (a.lse && c.grp == 0) a.lse[orow] = (ws.m_run[t] + __log2f(l_tot)) * kLn2;
     } else {
-      const size_t prow = ((size_t)blockIdx.x * a.M + r);
-      float* dst = a.part_o + prow * D + 4 * grp;
+      const size_t prow = (size_t)part * a.M + r;
+      float* dst = a.part_o + prow * D + 4 * c.grp;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(dst + 16 * dt) = ws.acc[dt][t];
-      if (grp == 0) {
+      if (c.grp == 0) {
         a.part_ml[prow * 2 + 0] = ws.m_run[t];
         a.part_ml[prow * 2 + 1] = l_tot;
       }
     }
+  }
+}
+
+// One workgroup per (request, KV head, split): the split is stages
+// [split * steps_per_split, ...) of the unit. With one split the rows are
+// written normalised, otherwise as partial state for the split merge.
+template <typename T, int D, int MT>
+__global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs a) {
+  using SS = StageShape<T, D>;
+  __shared__ __attribute__((aligned(1024))) char s_ring[SS::NSP * SS::PAIR];
+  __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];  // (lo, hi) per stage
+
+  const WaveCtx<T, D> c = wave_ctx<T, D>(a, s_ring);
+  const int unit = blockIdx.x / a.splits;
+  const int split = blockIdx.x - unit * a.splits;
+  const int b = unit / a.Hkv;
+  const int kvh = unit - b * a.Hkv;
+  const int s_lo = split * a.steps_per_split;
+
+  // loads that do not depend on the sequence length go out first, so that
+  // their latency overlaps the length's
+  WaveState<T, D, MT> ws;
+  load_q<T, D, MT>(ws, a, b, kvh, c.rs, c.n, c.grp);
+  const int2 first = table_pair(a, a.page_table + (size_t)b * a.max_pages, s_lo + c.tid);
+  const int L = clamped_len(a, b, c.tid == 0 && split == 0);
+  const int n_steps = (L + a.B + kStep - 1) / kStep;
+  const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
+  stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, L, s_lo, s_hi, first);
+  finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, a.splits == 1 ? -1 : (int)blockIdx.x);
+}
+
+// ------------------------------------------------------- balanced schedule
+// For batches whose lengths may differ widely, a fixed grid of G workgroups
+// shares the work evenly: the stage pairs of all units, taken in unit order
+// (unit = b * Hkv + kvh, each unit ceil(ceil((L_b + B) / 32) / 2) pairs), are
+// cut into G equal contiguous ranges, workgroup w taking pairs
+// [floor(TP * w / G), floor(TP * (w + 1) / G)). A unit that a range boundary
+// cuts is written as partial states by the workgroups that share it -- into
+// slot 2w when it is workgroup w's first unit, else 2w + 1 -- and merged by
+// the boundary-combine kernel; every other unit is written normalised.
+
+__device__ __forceinline__ int unit_pairs(const AttnArgs& a, int L) {
+  const int n_steps = (L + a.B + kStep - 1) / kStep;
+  return (n_steps + 1) >> 1;
+}
+
+__device__ __forceinline__ int block_exclusive_scan_int(int x, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int v = s_tmp[w];
+    base += w < wave ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - x;
+}
+
+// s_pre[b] = pairs of all units of requests before b (b = 0 .. bs); returns
+// the total. Thread tid covers a contiguous run of requests.
+__device__ int balanced_prefix(const AttnArgs& a, int* s_pre, int* s_tmp, bool flag) {
+  const int nthr = blockDim.x, tid = threadIdx.x;
+  const int per = (a.bs + nthr - 1) / nthr;
+  const int b0 = min(a.bs, tid * per), b1 = min(a.bs, b0 + per);
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += a.Hkv * unit_pairs(a, clamped_len(a, b, flag));
+  int total;
+  int run = block_exclusive_scan_int(sum, s_tmp, &total);
+  for (int b = b0; b < b1; ++b) {
+    s_pre[b] = run;
+    run += a.Hkv * unit_pairs(a, clamped_len(a, b, false));
+  }
+  if (tid == 0) s_pre[a.bs] = total;
+  __syncthreads();
+  return total;
+}
+
+// Request holding global pair x: the largest b with s_pre[b] <= x.
+__device__ __forceinline__ int request_of(const int* s_pre, int bs, int x) {
+  int lo = 0, hi = bs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int range_start(int total, int w, int G) {
+  return (int)((long long)total * w / G);
+}
+
+template <typename T, int D, int MT>
+__global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(AttnArgs a) {
+  using SS = StageShape<T, D>;
+  __shared__ __attribute__((aligned(1024))) char s_ring[SS::NSP * SS::PAIR];
+  __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];
+  __shared__ int s_pre[kMaxBalancedBatch + 1];
+  __shared__ int s_tmp[kWaves];
+
+  const WaveCtx<T, D> c = wave_ctx<T, D>(a, s_ring);
+  const int G = gridDim.x, w = blockIdx.x;
+  const int total = balanced_prefix(a, s_pre, s_tmp, w == 0);
+  const int start = range_start(total, w, G), end = range_start(total, w + 1, G);
+  if (start >= end) return;
+  int b = request_of(s_pre, a.bs, start);
+  int L = clamped_len(a, b, false);
+  int np = unit_pairs(a, L);
+  int kvh = (start - s_pre[b]) / np;
+  int off = start - s_pre[b] - kvh * np;  // first pair inside the unit
+  for (int cur = start; cur < end;) {
+    const int seg = min(np - off, end - cur);
+    const bool whole = off == 0 && seg == np;
+    const int part = whole ? -1 : (cur == start ? 2 * w : 2 * w + 1);
+    const int s_lo = 2 * off;
+    const int s_hi = min((L + a.B + kStep - 1) / kStep, 2 * (off + seg));
+    WaveState<T, D, MT> ws;
+    load_q<T, D, MT>(ws, a, b, kvh, c.rs, c.n, c.grp);
+    const int2 first = table_pair(a, a.page_table + (size_t)b * a.max_pages, s_lo + c.tid);
+    stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, L, s_lo, s_hi, first);
+    finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, part);
+    cur += seg;
+    off += seg;
+    if (off == np) {  // next unit
+      off = 0;
+      if (++kvh == a.Hkv) {
+        kvh = 0;
+        if (++b < a.bs) {
+          L = clamped_len(a, b, false);
+          np = unit_pairs(a, L);
+        }
+      }
+    }
+  }
+}
+
+// Merge of the units cut by range boundaries. Boundary k (k = 1 .. G - 1)
+// merges the unit containing pair start(k) if that unit began inside
+// workgroup k - 1's range (so each cut unit is merged once); each boundary's
+// rows are spread over kCombineRowGroups blocks.
+constexpr int kCombineRowGroups = 4;
+constexpr int kCombineMaxPieces = 256;  // a unit is shared by at most G workgroups
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnArgs a) {
+  __shared__ int s_pre[kMaxBalancedBatch + 1];
+  __shared__ int s_tmp[4];
+  __shared__ int s_slot[kCombineMaxPieces];
+  constexpr int RPB = 128 / kCombineRowGroups;  // rows per block at most
+  __shared__ float s_w[RPB * 33];               // per row: weight of each of <= 32 pieces
+  const int G = a.G, k = blockIdx.x / kCombineRowGroups + 1, rg = blockIdx.x % kCombineRowGroups;
+  const int total = balanced_prefix(a, s_pre, s_tmp, false);
+  const int sk = range_start(total, k, G), sk1 = range_start(total, k - 1, G);
+  if (sk >= total || sk1 >= sk) return;
+  const int b = request_of(s_pre, a.bs, sk);
+  const int np = unit_pairs(a, clamped_len(a, b, false));
+  const int kvh = (sk - s_pre[b]) / np;
+  const int u0 = s_pre[b] + kvh * np, u1 = u0 + np;  // the unit's pairs [u0, u1)
+  if (u0 >= sk || u0 < sk1) return;  // not cut here, or cut at an earlier boundary
+  // pieces: workgroups k - 1 .. wb with a non-empty range; the first one's
+  // piece sits in its second slot unless the unit is that workgroup's first
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int wg = k - 1; wg < G && range_start(total, wg, G) < u1; ++wg) {
+      if (range_start(total, wg, G) >= range_start(total, wg + 1, G)) continue;
+      if (n < kCombineMaxPieces) s_slot[n] = wg == k - 1 && u0 > sk1 ? 2 * wg + 1 : 2 * wg;
+      ++n;
+    }
+    s_tmp[0] = min(n, kCombineMaxPieces);
+  }
+  __syncthreads();
+  const int npc = s_tmp[0];
+  const int rpb = (a.M + kCombineRowGroups - 1) / kCombineRowGroups;
+  const int r0 = rg * rpb, r1 = min(a.M, r0 + rpb);
+  if (r0 >= r1) return;
+  // weights in chunks of 32 pieces: w_i = 2^(m_i - max m) / sum_j 2^(m_j - max m) l_j
+  const int n4 = (r1 - r0) * (D / 4);
+  floatx4 sum[4];
+  for (int j = 0; j < 4; ++j) sum[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < npc; p0 += 32) {
+    const int pn = min(32, npc - p0);
+    __syncthreads();
+    for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
+      float mm = kNegBig;
+      for (int i = 0; i < npc; ++i) mm = fmaxf(mm, a.part_ml[((size_t)s_slot[i] * a.M + r) * 2]);
+      float ll = 0.f;
+      for (int i = 0; i < npc; ++i) {
+        const size_t pr = (size_t)s_slot[i] * a.M + r;
+        ll += __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - mm) * a.part_ml[pr * 2 + 1];
+      }
+      const float inv = 1.0f / ll;
+      for (int i = 0; i < pn; ++i) {
+        const size_t pr = (size_t)s_slot[p0 + i] * a.M + r;
+        s_w[(r - r0) * 33 + i] = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - mm) * inv;
+      }
+      if (p0 == 0 && a.lse) {
+        const int ii = r / a.g, hl = r - ii * a.g;
+        a.lse[(size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hl] = (mm + __log2f(ll)) * kLn2;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = threadIdx.x + j * blockDim.x;
+      if (e >= n4) break;
+      const int rl = e / (D / 4), d4 = e - rl * (D / 4);
+      floatx4 acc = sum[j];
+      for (int i = 0; i < pn; ++i) {
+        const size_t pr = (size_t)s_slot[p0 + i] * a.M + r0 + rl;
+        acc += s_w[rl * 33 + i] * *reinterpret_cast<const floatx4*>(a.part_o + pr * D + 4 * d4);
+      }
+      sum[j] = acc;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = threadIdx.x + j * blockDim.x;
+    if (e >= n4) break;
+    const int rl = e / (D / 4), d4 = e - rl * (D / 4);
+    const int r = r0 + rl, ii = r / a.g, hl = r - ii * a.g;
+    T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hl) * D + 4 * d4;
+    Frag<T>::store4(dst, sum[j]);
   }
 }
 
@@ -724,7 +1003,20 @@ __global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
 // ------------------------------------------------------------------ launch
 template <typename T, int D>
 static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t stream) {
-  const dim3 grid(total_blocks), block(kWave * kWaves);
+  const dim3 block(kWave * kWaves);
+  if (a.balanced) {
+    const dim3 grid(a.G);
+    if (a.M > 64)
+      hipLaunchKernelGGL((block_attn_balanced_kernel<T, D, 2>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((block_attn_balanced_kernel<T, D, 1>), grid, block, 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.G < 2) return e;
+    hipLaunchKernelGGL((block_attn_boundary_combine_kernel<T, D>),
+                       dim3((a.G - 1) * kCombineRowGroups), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(total_blocks);
   if (a.M > 64)
     hipLaunchKernelGGL((block_attn_kernel<T, D, 2>), grid, block, 0, stream, a);
   else

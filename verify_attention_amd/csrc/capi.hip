@@ -27,7 +27,8 @@ int ilog2_exact(int x) {
   return (1 << s) == x ? s : -1;
 }
 
-// Optional override read once (a tuning knob): the split count.
+// Optional overrides read once (tuning knobs): the split count of the
+// per-unit schedule, and the schedule itself (1: per unit, 2: balanced).
 int env_int(const char* name) {
   const char* s = std::getenv(name);
   return s ? std::atoi(s) : 0;
@@ -36,20 +37,44 @@ int env_splits() {
   static int v = env_int("SPECATTN_SPLITS");
   return v;
 }
+int env_schedule() {
+  static int v = env_int("SPECATTN_SCHEDULE");
+  return v;
+}
 
 struct AttnPlan {
   int M = 0, units = 0, splits = 1, steps_per_split = 1;
+  bool balanced = false;
+  int grid = 0;
   size_t off_ml = 0, off_o = 0, ws_bytes = 0;
 };
 
-// Splits per (request, KV head): enough workgroups for one per CU when the
-// batch has few (request, KV head) units, while every split keeps at least 8
-// stages of 32 keys.
+// Two schedules. Large batches (units x stages of the longest request at
+// least kBalancedMinStages) use the balanced schedule: one workgroup per CU,
+// each taking an equal share of all units' stage pairs, so that lengths that
+// differ widely do not leave CUs idle; units cut by a share boundary leave
+// partial states in the workspace (two slots per workgroup). Smaller batches
+// use one workgroup per (request, KV head, split): enough splits for one
+// workgroup per CU when the batch has few units, every split keeping at least
+// 8 stages of 32 keys.
+constexpr long long kBalancedMinStages = 32768;
+
 AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   AttnPlan p;
   p.M = (Hq / Hkv) * B;
   p.units = bs * Hkv;
   const int max_steps = std::max(1, (max_kv_len + kStepKeys - 1) / kStepKeys);
+  const int sched = env_schedule();
+  p.balanced = bs <= kMaxBalancedBatch &&
+               (sched == 2 || (sched != 1 && (long long)p.units * max_steps >= kBalancedMinStages));
+  if (p.balanced) {
+    p.grid = kCUs;
+    const size_t slots = 2 * (size_t)kCUs;
+    p.off_ml = 0;
+    p.off_o = align_up(slots * p.M * 2 * sizeof(float), 256);
+    p.ws_bytes = p.off_o + slots * p.M * D * sizeof(float);
+    return p;
+  }
   int splits = env_splits();
   if (splits <= 0) {
     splits = (kCUs + p.units - 1) / p.units;
@@ -58,6 +83,7 @@ AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   splits = std::max(1, std::min(splits, std::min(kMaxSplits, max_steps)));
   p.steps_per_split = (max_steps + splits - 1) / splits;
   p.splits = (max_steps + p.steps_per_split - 1) / p.steps_per_split;
+  p.grid = p.units * p.splits;
   if (p.splits > 1) {
     p.off_ml = 0;
     p.off_o = align_up((size_t)p.units * p.splits * p.M * 2 * sizeof(float), 256);
@@ -172,8 +198,8 @@ SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req,
   a.o = o;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  a.part_ml = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.off_ml) : nullptr;
-  a.part_o = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.off_o) : nullptr;
+  a.part_ml = plan.ws_bytes > 0 ? reinterpret_cast<float*>(ws + plan.off_ml) : nullptr;
+  a.part_o = plan.ws_bytes > 0 ? reinterpret_cast<float*>(ws + plan.off_o) : nullptr;
   a.err = err_flags;
   a.bs = bs;
   a.B = B;
@@ -189,9 +215,11 @@ SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req,
   a.n_causal = mode == SPEC_MIXED ? n_causal : (mode == SPEC_CAUSAL ? B : 0);
   a.splits = plan.splits;
   a.steps_per_split = plan.steps_per_split;
+  a.balanced = plan.balanced ? 1 : 0;
+  a.G = plan.grid;
   const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt((float)D) : sm_scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(launch_block_attn(a, dtype == SPEC_BF16, D, plan.units * plan.splits,
+  return hip_status(launch_block_attn(a, dtype == SPEC_BF16, D, plan.grid,
                                       static_cast<hipStream_t>(stream)));
 }
 

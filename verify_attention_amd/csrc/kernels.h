@@ -14,15 +14,19 @@ struct AttnArgs {
   const int32_t* nc_per_req;
   void* o;
   float* lse;
-  float* part_o;      // [units * splits][M][D] split partial outputs (unnormalised)
-  float* part_ml;     // [units * splits][M][2] split partial (max, sum), log2 domain
+  float* part_o;      // [slots][M][D] partial outputs (unnormalised): split or cut-unit pieces
+  float* part_ml;     // [slots][M][2] partial (max, sum), log2 domain
   int32_t* err;
   int bs, B, Hq, Hkv, g, M;  // M = g * B query rows per KV head
   int P, p_shift, max_pages, num_pages;
   int mode, n_causal;
   int splits, steps_per_split;
+  int balanced, G;   // balanced schedule: G persistent workgroups
   float scale_log2;  // sm_scale * log2(e)
 };
+
+// Largest batch the balanced schedule handles (its prefix sums live in LDS).
+constexpr int kMaxBalancedBatch = 2048;
 
 hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks,
                              hipStream_t stream);
