@@ -204,7 +204,8 @@ int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* t
  *   memory, 16-byte aligned, contents irrelevant (per-chunk residual masses
  *   and accept lengths passed between the call's two kernels). Calls that
  *   share a workspace must be ordered (same stream, or synchronised).
- * Errors: SPEC_EINVAL (bs <= 0, K outside 1..63, V <= 0, NULL), SPEC_ENOSPC.
+ * Errors: SPEC_EINVAL (bs <= 0, K outside 1..63, V <= 0, NULL), SPEC_ENOSPC,
+ *   SPEC_ENOTSUP (greedy == 0 with V > 524288).
  */
 size_t spec_accept_workspace_bytes(int bs, int K, int V, int greedy);
 

@@ -121,6 +121,7 @@ def test_accept_rejects_bad_arguments(lib):
     assert _acc(lib, q=None) == b.SPEC_EINVAL
     assert _acc(lib, u=None) == b.SPEC_EINVAL
     assert _acc(lib, out=None) == b.SPEC_EINVAL
+    assert _acc(lib, V=524289) == b.SPEC_ENOTSUP              # stochastic accept vocabulary cap
     need = lib.spec_accept_workspace_bytes(4, 15, 151936, 0)
     assert need > 0
     assert _acc(lib, ws_bytes=need - 1) == b.SPEC_ENOSPC

@@ -89,18 +89,6 @@ __device__ __forceinline__ bool rows_aligned(const float* p, const float* q) {
   return ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q ? q : p)) & 15) == 0;
 }
 
-__device__ void write_outputs(const AcceptArgs& a, int b, int j, int tok) {
-  const int K = a.K;
-  if (threadIdx.x == 0) {
-    a.accept_len[b] = j;
-    a.commit_len[b] = j + 1;
-    a.bonus[b] = tok;
-    a.new_seq_lens[b] = a.seq_lens[b] + j + 1;
-  }
-  for (int i = threadIdx.x; i <= K; i += kAccThreads)
-    a.out_tokens[(size_t)b * (K + 1) + i] = i < j ? a.draft[(size_t)b * K + i] : (i == j ? tok : -1);
-}
-
 // Kernel 1, one workgroup per (request, vocabulary chunk): the accept length,
 // then the residual (or bonus) mass of every 256-entry sub-block of the chunk
 // (one wave per sub-block, 4 entries per lane).
@@ -116,6 +104,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs 
   if (wave == 0) {
     bool fail = false, bad = false;
     if (lane < K) {
+      const double ui = a.u[(size_t)b * (K + 1) + lane];
       const int d = a.draft[(size_t)b * K + lane];
       bad = d < 0 || d >= V;
       if (bad) {
@@ -123,7 +112,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs 
       } else {
         const double pd = a.p[((size_t)b * (K + 1) + lane) * V + d];
         const double qd = a.q[((size_t)b * K + lane) * V + d];
-        const double ui = a.u[(size_t)b * (K + 1) + lane];
         fail = !(ui * qd < pd);
       }
     }
@@ -188,55 +176,58 @@ __device__ int sub_block_search(const float* p, const float* q, int sb, int V, b
   return res;
 }
 
-// Draws the token from sub-block masses m[0..nsb) (one pass over the
-// masses, one sub-block re-read). Returns -1 if the total mass is not > 0.
-__device__ int draw_from_masses(const double* m, int nsb, const float* p, const float* q, int V,
-                                bool vec, double u, double* s_wave, int* s_int) {
-  __shared__ double s_tot, s_base;
+// Draws the token from sub-block masses: thread tid holds the masses of
+// sub-blocks [i0, i1) in mv (one pass over them, one sub-block re-read).
+// Returns -1 if the total mass is not > 0.
+constexpr int kMaxPer = kMaxAcceptVocab / (kSub * kAccThreads);  // sub-blocks per thread
+
+__device__ int draw_from_masses(const double (&mv)[kMaxPer], int i0, int i1, const float* p,
+                                const float* q, int V, bool vec, double u, double* s_wave,
+                                int* s_int, double* s_dbl) {
   const int tid = threadIdx.x;
-  const int per = (nsb + kAccThreads - 1) / kAccThreads;
-  const int i0 = min(nsb, tid * per), i1 = min(nsb, i0 + per);
   double mine = 0.0;
-  for (int i = i0; i < i1; ++i) mine += m[i];
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) mine += i0 + k < i1 ? mv[k] : 0.0;
   const double incl = block_inclusive_scan(mine, s_wave);
-  if (tid == kAccThreads - 1) s_tot = incl;
-  __syncthreads();
-  const double S = s_tot;
-  if (!(S > 0.0)) return -1;
-  const double thr = u * S;
+  if (tid == kAccThreads - 1) s_dbl[0] = incl;
   if (tid == 0) {
     s_int[0] = 0x7fffffff;
     s_int[1] = -1;
   }
   __syncthreads();
+  const double S = s_dbl[0];
+  if (!(S > 0.0)) return -1;
+  const double thr = u * S;
   // first sub-block whose running mass passes thr, and the last one with mass
   double run = incl - mine;
   int hit = -1, lastm = -1;
-  for (int i = i0; i < i1; ++i) {
-    const double x = m[i];
-    if (hit < 0 && run + x > thr) hit = i;
+  double hit_base = 0.0;
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    if (i0 + k >= i1) break;
+    const double x = mv[k];
+    if (hit < 0 && run + x > thr) {
+      hit = i0 + k;
+      hit_base = run;
+    }
     run += x;
-    if (x > 0.0) lastm = i;
+    if (x > 0.0) lastm = i0 + k;
   }
   if (hit >= 0) atomicMin(&s_int[0], hit);
   if (lastm >= 0) atomicMax(&s_int[1], lastm);
   __syncthreads();
   const int first_hit = s_int[0];
-  int sstar = first_hit != 0x7fffffff ? first_hit : s_int[1];
-  __syncthreads();
-  // base: running mass before sub-block sstar (recomputed by its owner)
-  if (first_hit == 0x7fffffff && tid == 0) {
-    double b0 = 0.0;
-    for (int i = 0; i < sstar; ++i) b0 += m[i];
-    s_base = b0;
-  }
-  if (first_hit != 0x7fffffff && sstar >= i0 && sstar < i1) {
+  const int sstar = first_hit != 0x7fffffff ? first_hit : s_int[1];
+  // base: running mass before sub-block sstar, from the thread that holds it
+  if (sstar >= i0 && sstar < i1) {
     double b0 = incl - mine;
-    for (int i = i0; i < sstar; ++i) b0 += m[i];
-    s_base = b0;
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k)
+      if (i0 + k < sstar) b0 += mv[k];
+    s_dbl[1] = first_hit != 0x7fffffff ? hit_base : b0;
   }
   __syncthreads();
-  const double base = s_base;
+  const double base = s_dbl[1];
   int lastp;
   int tok = sub_block_search(p, q, sstar, V, vec, base, thr, s_int, &lastp);
   if (tok < 0) tok = lastp;
@@ -245,42 +236,60 @@ __device__ int draw_from_masses(const double* m, int nsb, const float* p, const 
 
 // Kernel 2, one workgroup per request: scan the sub-block masses, find the
 // sub-block where the running mass passes u_K * S, locate the token inside it,
-// write every output.
+// write every output. Every load that does not depend on the accept length
+// goes out first.
 __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a) {
   const int b = blockIdx.x;
   const int K = a.K, V = a.V;
   const int tid = threadIdx.x;
   __shared__ double s_wave[4];
+  __shared__ double s_dbl[2];
   __shared__ int s_int[2];
+  const int nsb = (V + kSub - 1) / kSub;
+  const int per = (nsb + kAccThreads - 1) / kAccThreads;
+  const int i0 = min(nsb, tid * per), i1 = min(nsb, i0 + per);
+  const double* m = a.partial + (size_t)b * nsb;
+  double mv[kMaxPer];
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) mv[k] = i0 + k < i1 ? m[i0 + k] : 0.0;
+  const int dtok = tid < K ? a.draft[(size_t)b * K + tid] : -1;
+  const int L = a.seq_lens[b];
+  const double ub = (double)a.u[(size_t)b * (K + 1) + K];
   const int jw = a.jbuf[b];
   const int j = jw & 0xffff;
   const float* prow = a.p + ((size_t)b * (K + 1) + j) * V;
   const float* qrow = j < K ? a.q + ((size_t)b * K + j) * V : nullptr;
   const bool vec = rows_aligned(prow, qrow);
-  const double ub = (double)a.u[(size_t)b * (K + 1) + K];
-  const int nsb = (V + kSub - 1) / kSub;
   int errs = (jw & kJTokenErr) ? kErrToken : 0;
-  int tok = draw_from_masses(a.partial + (size_t)b * nsb, nsb, prow, qrow, V, vec, ub, s_wave, s_int);
+  int tok = draw_from_masses(mv, i0, i1, prow, qrow, V, vec, ub, s_wave, s_int, s_dbl);
   if (tok < 0) {
-    // zero residual mass: draw from the target row itself. Its sub-block
-    // masses replace the residual ones in this request's partial slots (each
-    // wave fills its own sub-blocks, then the block synchronises).
+    // zero residual mass: draw from the target row itself (its sub-block
+    // masses recomputed into registers, thread by thread)
     errs |= kErrZeroResidual;
-    double* m = a.partial + (size_t)b * nsb;
     const bool pvec = rows_aligned(prow, nullptr);
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int sb = wave; sb < nsb; sb += kAccThreads / 64) {
-      double r[4];
-      resid4(prow, nullptr, sb * kSub + 4 * lane, V, pvec, r);
-      const double t = wave_sum((r[0] + r[1]) + (r[2] + r[3]));
-      if (lane == 0) m[sb] = t;
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+      double t = 0.0;
+      if (i0 + k < i1) {
+        for (int e = (i0 + k) * kSub; e < min(V, (i0 + k + 1) * kSub); e += 4) {
+          double r[4];
+          resid4(prow, nullptr, e, V, pvec, r);
+          t += (r[0] + r[1]) + (r[2] + r[3]);
+        }
+      }
+      mv[k] = t;
     }
-    __threadfence_block();
-    __syncthreads();
-    tok = draw_from_masses(m, nsb, prow, nullptr, V, pvec, ub, s_wave, s_int);
+    tok = draw_from_masses(mv, i0, i1, prow, nullptr, V, pvec, ub, s_wave, s_int, s_dbl);
   }
   if (tok < 0) tok = 0;
-  write_outputs(a, b, j, tok);
+  if (tid == 0) {
+    a.accept_len[b] = j;
+    a.commit_len[b] = j + 1;
+    a.bonus[b] = tok;
+    a.new_seq_lens[b] = L + j + 1;
+  }
+  if (tid <= K)
+    a.out_tokens[(size_t)b * (K + 1) + tid] = tid < j ? dtok : (tid == j ? tok : -1);
   if (tid == 0 && errs) flag_error(a.err, errs);
 }
 

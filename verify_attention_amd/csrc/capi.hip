@@ -247,6 +247,7 @@ SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const
       !new_seq_lens)
     return SPEC_EINVAL;
   if (!greedy && (!q || !u)) return SPEC_EINVAL;
+  if (!greedy && V > kMaxAcceptVocab) return SPEC_ENOTSUP;
   const AccPlan plan = plan_accept(bs, K, V, greedy);
   if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
   char* ws = static_cast<char*>(workspace);

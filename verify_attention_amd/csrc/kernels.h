@@ -67,6 +67,10 @@ struct AcceptArgs {
   int bs, K, V, nchunk, chunk;
 };
 
+// Largest vocabulary of the stochastic accept: its select pass holds each
+// request's sub-block masses (256 entries each) in registers, 8 per thread.
+constexpr int kMaxAcceptVocab = 8 * 256 * 256;
+
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 hipError_t launch_greedy_accept(const AcceptArgs& a, hipStream_t stream);
 
