@@ -8,8 +8,9 @@ acceptance rule from the pages' definitions, in float64 NumPy.
 
 Modules:
   prepare   -- block ids / positions / cache slots of one round's block
-  attention -- block-query attention over a paged KV cache, two forms:
-               a per-row loop and a dense masked-softmax matrix form
+  attention -- block-query attention over a paged KV cache (BIDIR, CAUSAL,
+               MIXED and TREE masks), two forms: a per-row loop and a dense
+               masked-softmax matrix form
   accept    -- speculative accept: p/q rejection test, longest accepted
                prefix, residual (or bonus) sample, committed length; the greedy
                special case; argmax with the lowest index winning
@@ -19,12 +20,12 @@ forms, library routines, brute force or exact enumeration (see the tests
 named test_oracle_*). None is "parity unpinned".
 """
 from .prepare import prepare_block
-from .attention import (BIDIR, CAUSAL, MIXED, visible, block_attn_rows,
-                        block_attn_dense, attn_row, unpage_kv)
+from .attention import (BIDIR, CAUSAL, MIXED, TREE, visible, block_attn_rows,
+                        block_attn_dense, attn_row, unpage_kv, mask_matrix)
 from .accept import accept_request, accept_batch, greedy_accept_request, argmax_lowest
 
 __all__ = [
-    "prepare_block", "BIDIR", "CAUSAL", "MIXED", "visible", "block_attn_rows",
-    "block_attn_dense", "attn_row", "unpage_kv", "accept_request", "accept_batch",
+    "prepare_block", "BIDIR", "CAUSAL", "MIXED", "TREE", "visible", "block_attn_rows",
+    "block_attn_dense", "attn_row", "unpage_kv", "mask_matrix", "accept_request", "accept_batch",
     "greedy_accept_request", "argmax_lowest",
 ]

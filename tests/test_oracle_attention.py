@@ -211,10 +211,94 @@ def test_planted_mask_mistake_is_caught(monkeypatch):
     x = tiny(seed=10)
     x.q[...] = 0
     monkeypatch.setattr(oracle.attention, "visible",
-                        lambda mode, i, jb, nc: jb < i if mode == CAUSAL else True)
+                        lambda mode, i, jb, nc, tree_row=0: jb < i if mode == CAUSAL else True)
     o, _ = oracle.block_attn_rows(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
                                   x.page_table, x.seq_lens, CAUSAL, 0, rows=[(0, 2, 0)])
     _, vs = gather_torch(x)
     L = int(x.seq_lens[0])
     want = vs[0][0].numpy()[:L + 3].mean(axis=0)
     assert np.max(np.abs(o[0, 2, 0] - want)) > 1e-6
+
+
+# ------------------------------------------------------------------ TREE mode
+def test_tree_mode_chain_and_full_masks_reduce_to_causal_and_bidir():
+    """A chain tree (parent[n] = n - 1) gives the causal triangle; all-ones
+    rows give the rectangle."""
+    x = tiny(seed=21, block=7, ctx=(0, 11))
+    B = x.cfg.block
+    chain = synth.tree_row_masks(np.arange(-1, B - 1, dtype=np.int32))
+    full = np.full(B, (1 << B) - 1, dtype=np.uint64)
+    for tree, mode in ((chain, CAUSAL), (full, BIDIR)):
+        o_t, l_t = oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                           x.page_table, x.seq_lens, oracle.TREE, 0, tree=tree)
+        o_m, l_m = run_dense(x, mode, 0)
+        assert np.max(np.abs(o_t - o_m)) < 1e-12 and np.max(np.abs(l_t - l_m)) < 1e-12
+
+
+def test_tree_node_equals_causal_attention_over_its_root_path():
+    """Defining property of tree attention: node n's output equals ordinary
+    causal attention of the last row of a block laid out as the node's root
+    path (ancestors in order, then n) after the same context. The path block
+    is built as a separate paged cache, so this does not go through the tree
+    mask at all."""
+    x = tiny(bs=2, hq=4, hkv=2, d=16, page=4, block=9, ctx=(2, 10), seed=22)
+    cfg = x.cfg
+    B, P = cfg.block, cfg.page
+    par, masks = synth.make_trees(dataclasses_replace(cfg, tree_depth=6), 3)
+    q64, k64, v64 = x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool")
+    o_t, l_t = oracle.block_attn_rows(q64, k64, v64, x.page_table, x.seq_lens, oracle.TREE, 0,
+                                      tree=masks)
+    for b in range(cfg.bs):
+        L = int(x.seq_lens[b])
+        for n in range(B):
+            path = []
+            m = n
+            while m >= 0:
+                path.append(m)
+                m = int(par[b][m])
+            path = path[::-1]
+            Lp = L + len(path)
+            # a fresh identity-paged cache holding context, then the path's block rows
+            npg = (Lp + P - 1) // P
+            kp = np.zeros((npg, cfg.hkv, P, cfg.d))
+            vp = np.zeros((npg, cfg.hkv, cfg.d, P))
+            for t in range(Lp):
+                src = t if t < L else L + path[t - L]
+                pg, off = int(x.page_table[b, src // P]), src % P
+                kp[t // P, :, t % P, :] = k64[pg, :, off, :]
+                vp[t // P, :, :, t % P] = v64[pg, :, :, off]
+            qp = np.zeros((1, len(path), cfg.hq, cfg.d))
+            qp[0, -1] = q64[b, n]
+            o_c, l_c = oracle.block_attn_rows(qp, kp, vp, np.arange(npg)[None, :],
+                                              np.array([L]), CAUSAL, 0,
+                                              rows=[(0, len(path) - 1, h) for h in range(cfg.hq)])
+            assert np.max(np.abs(o_c[0, -1] - o_t[b, n])) < 1e-12, (b, n)
+            assert np.max(np.abs(l_c[0, -1] - l_t[b, n])) < 1e-12, (b, n)
+
+
+def test_tree_rows_and_dense_forms_agree_and_planted_bit_matters():
+    x = tiny(seed=23, block=8, ctx=(1, 12))
+    par, masks = synth.make_trees(dataclasses_replace(x.cfg, tree_depth=5), 4)
+    args = (x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"), x.page_table, x.seq_lens,
+            oracle.TREE, 0)
+    o1, l1 = oracle.block_attn_rows(*args, tree=masks)
+    o2, l2 = oracle.block_attn_dense(*args, tree=masks)
+    assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(l1 - l2)) < 1e-12
+    # a shared [B] tree is the per-request tree broadcast
+    o3, _ = oracle.block_attn_dense(*args, tree=masks[0])
+    o4, _ = oracle.block_attn_dense(*args, tree=np.stack([masks[0]] * x.cfg.bs))
+    assert np.max(np.abs(o3 - o4)) == 0.0
+    # dropping one ancestor bit changes exactly that node's rows
+    bad = masks.copy()
+    n = int(np.argmax([bin(int(v)).count("1") for v in bad[0]]))
+    top = int(bad[0][n]) & ~(1 << n)
+    j = top.bit_length() - 1
+    bad[0][n] = np.uint64(int(bad[0][n]) & ~(1 << j))
+    o5, _ = oracle.block_attn_dense(*args, tree=bad)
+    diff = np.abs(o5 - o2).max(axis=(2, 3))
+    assert diff[0, n] > 1e-6 and np.delete(diff[0], n).max() == 0.0 and diff[1:].max() == 0.0
+
+
+def dataclasses_replace(cfg, **kw):
+    import dataclasses
+    return dataclasses.replace(cfg, **kw)

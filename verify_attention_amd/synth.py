@@ -26,8 +26,8 @@ from __future__ import annotations
 import dataclasses
 import numpy as np
 
-BIDIR, CAUSAL, MIXED = 0, 1, 2
-MODE_NAMES = {BIDIR: "BIDIR", CAUSAL: "CAUSAL", MIXED: "MIXED"}
+BIDIR, CAUSAL, MIXED, TREE = 0, 1, 2, 3
+MODE_NAMES = {BIDIR: "BIDIR", CAUSAL: "CAUSAL", MIXED: "MIXED", TREE: "TREE"}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +52,7 @@ class RoundConfig:
     logit_sigma: float = 3.0
     q_noise_sigma: float = 0.0  # >0: q-logits = p-logits + N(0, s^2); 0: independent
     argmax_vocab: int = 0      # draft pass: argmax of bf16 logits over this vocab
+    tree_depth: int = 0        # TREE: the block is a token tree of this many levels at most
 
 
 # The five round configurations. Sizes are the workloads the pages describe:
@@ -60,6 +61,8 @@ class RoundConfig:
 #  3 block-diffusion draft pass, ragged contexts, block 32, greedy draft ids
 #  4 high-concurrency ragged verify (batch 256)
 #  5 I-DLM style mixed layout: 8 clean causal + 8 MASK bidirectional positions
+#  6 tree verify: the Qwen3-8B-shaped verify of 2 with a 32-node token tree
+#    (at most 16 levels) as the block, one tree per request
 CONFIGS = {
     1: RoundConfig("tiny_f32", bs=1, hq=2, hkv=1, d=64, page=16, block=8,
                    modes=(BIDIR, CAUSAL), dtype="f32", ctx_lo=256, ctx_hi=256,
@@ -79,6 +82,10 @@ CONFIGS = {
                    block=16, modes=(MIXED,), dtype="bf16", ctx_lo=4096,
                    ctx_hi=4096, n_causal=8, vocab=151936, k_spec=8,
                    logit_sigma=3.0, q_noise_sigma=0.5),
+    6: RoundConfig("tree_verify_bs32", bs=32, hq=32, hkv=8, d=128, page=16,
+                   block=32, modes=(TREE,), dtype="bf16", ctx_lo=1024,
+                   ctx_hi=1024, tree_depth=16, vocab=151936, k_spec=31,
+                   logit_sigma=3.0, q_noise_sigma=0.5),
 }
 
 
@@ -91,7 +98,7 @@ def config(cid: int, **overrides) -> RoundConfig:
 # Independent child streams, one per drawn item, so that resizing one item
 # never shifts the numbers of another.
 _STREAMS = dict(pages=1, ctx=2, commit=3, q=4, k=5, v=6, plogit=7, qnoise=8,
-                draft=9, uniform=10, argmax=11, ncausal=12, poison=13)
+                draft=9, uniform=10, argmax=11, ncausal=12, poison=13, tree=14)
 
 
 def rng_for(seed: int, item: str) -> np.random.Generator:
@@ -224,6 +231,46 @@ def make_attn_inputs(cfg: RoundConfig, seed: int, shuffle=True,
     else:
         nc = np.full(cfg.bs, cfg.n_causal, dtype=np.int64)
     return AttnInputs(cfg, seq, table, num_pages, q, k, v, nc.astype(np.int32))
+
+
+# -------------------------------------------------------------- token trees
+def random_tree_parents(rng, n_nodes: int, max_depth: int) -> np.ndarray:
+    """parent[n] of a random token tree in topological order: node 0 is the
+    root (depth 0); every other node extends the previous node with
+    probability 1/2 (a main path with side branches, as a top-candidate tree
+    has) and otherwise picks a uniformly random earlier node; parents are
+    limited to depth below max_depth - 1."""
+    parent = np.full(n_nodes, -1, dtype=np.int32)
+    depth = np.zeros(n_nodes, dtype=np.int32)
+    for n in range(1, n_nodes):
+        ok = np.flatnonzero(depth[:n] < max_depth - 1)
+        chain = rng.random() < 0.5 and depth[n - 1] < max_depth - 1
+        parent[n] = n - 1 if chain else ok[rng.integers(len(ok))]
+        depth[n] = depth[parent[n]] + 1
+    return parent
+
+
+def tree_row_masks(parent: np.ndarray) -> np.ndarray:
+    """uint64 row masks of a tree in topological order: bit j of row n is set
+    iff node j is node n or one of its ancestors."""
+    m = np.zeros(len(parent), dtype=np.uint64)
+    for n in range(len(parent)):
+        m[n] = np.uint64(1) << np.uint64(n)
+        if parent[n] >= 0:
+            m[n] |= m[parent[n]]
+    return m
+
+
+def make_trees(cfg: RoundConfig, seed: int, per_request=True):
+    """Token trees for a TREE round: parents [bs, B] and row masks [bs, B]
+    (per_request), or one tree shared by the batch ([B] each)."""
+    r = rng_for(seed, "tree")
+    depth = cfg.tree_depth or cfg.block
+    if not per_request:
+        par = random_tree_parents(r, cfg.block, depth)
+        return par, tree_row_masks(par)
+    par = np.stack([random_tree_parents(r, cfg.block, depth) for _ in range(cfg.bs)])
+    return par, np.stack([tree_row_masks(p) for p in par])
 
 
 # --------------------------------------------------------------- accept step
