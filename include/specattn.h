@@ -10,7 +10,7 @@
  *   block_attn(SPEC_BIDIR)            -> draft-pass attention
  *   spec_draft_argmax                 -> greedy draft tokens
  *   spec_prepare_block  (verify pass, with the draft tokens)
- *   block_attn(SPEC_CAUSAL | SPEC_MIXED)
+ *   block_attn(SPEC_CAUSAL | SPEC_MIXED), or block_attn_tree for a token tree
  *   [caller produces target rows p]
  *   spec_accept                       -> accepted prefix, bonus, new lengths
  *
@@ -61,7 +61,7 @@ extern "C" {
 #define SPEC_ERR_TOKEN 4          /* a draft token id is outside [0, V)                          */
 #define SPEC_ERR_ZERO_RESIDUAL 8  /* residual mass was zero; the draw used the target row        */
 
-typedef enum { SPEC_BIDIR = 0, SPEC_CAUSAL = 1, SPEC_MIXED = 2 } spec_mode;
+typedef enum { SPEC_BIDIR = 0, SPEC_CAUSAL = 1, SPEC_MIXED = 2, SPEC_TREE = 3 } spec_mode;
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -143,9 +143,9 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
  *   calls that share a workspace must be ordered (same stream, or synchronised).
  * Errors: SPEC_EINVAL (bad counts, Hq % Hkv != 0, g * B > 128, mode, n_causal
  *   outside [0, B], NULL pointers), SPEC_ENOTSUP (D, P, dtype), SPEC_ENOSPC.
- *   Kernels set SPEC_ERR_SLOT for a page id outside [0, num_pages) (that page
- *   is read as zeros) and SPEC_ERR_CAPACITY for L_b < 0 or L_b + B >
- *   max_pages * P (the request is clamped to the table).
+ *   Kernels set SPEC_ERR_SLOT for a page id outside [0, num_pages) (physical
+ *   page 0 is read in its place) and SPEC_ERR_CAPACITY for L_b < 0 or L_b + B
+ *   > max_pages * P (the request is clamped to the table).
  */
 size_t block_attn_workspace_bytes(int bs, int B, int Hq, int Hkv, int D, int max_kv_len);
 
@@ -154,6 +154,32 @@ int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req, int dtyp
                int max_kv_len, const void* q, const void* k_pool, const void* v_pool,
                const int32_t* page_table, const int32_t* seq_lens, float sm_scale, void* o,
                float* lse, void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream);
+
+/*
+ * block_attn_tree -- block_attn for a block that is a token tree.
+ *
+ * Follows the Tree sampler of "Unlocking Lossless Speedups in LLMs via
+ * Discrete Diffusion" (method steps: candidate prefixes verified in parallel
+ * with tree attention): the B block tokens are tree nodes, and a node must see
+ * the context and its own root path only. Row i's visibility over the block
+ * is a bitmask: block key j' (0 <= j' < B) is visible to block row i iff bit
+ * j' of tree_mask[i] (shared tree) or tree_mask[b * B + i] (one tree per
+ * request) is set; context keys are always visible. Callers set, for node i,
+ * the bits of node i and of its ancestors; a row whose mask and context are
+ * both empty has no defined output.
+ *
+ *   tree_mask         uint64 row masks (device): [B] when tree_per_request
+ *                     is 0, else [bs, B]; B <= 64
+ *   other arguments, outputs, workspace (block_attn_workspace_bytes) and
+ *   errors as for block_attn; SPEC_EINVAL also for tree_mask == NULL or
+ *   B > 64.
+ */
+int block_attn_tree(const uint64_t* tree_mask, int tree_per_request, int dtype, int bs, int B,
+                    int Hq, int Hkv, int D, int page_size, int max_pages, int num_pages,
+                    int max_kv_len, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* page_table, const int32_t* seq_lens, float sm_scale, void* o,
+                    float* lse, void* workspace, size_t ws_bytes, int32_t* err_flags,
+                    void* stream);
 
 /*
  * spec_draft_argmax -- greedy draft tokens from the draft pass's logits.

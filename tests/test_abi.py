@@ -86,6 +86,25 @@ def test_block_attn_rejects_bad_arguments(lib):
     assert _attn(lib, max_pages=1, B=32, hq=8, hkv=8) == b.SPEC_EINVAL  # table shorter than B
 
 
+def test_block_attn_tree_rejects_bad_arguments(lib):
+    def tree(**kw):
+        a = dict(tm=FAKE, per=1, dt=1, bs=2, B=32, hq=8, hkv=2, d=128, P=16, max_pages=80,
+                 num_pages=200, max_kv=1040, q=FAKE, k=FAKE, v=FAKE, tab=FAKE, seq=FAKE,
+                 scale=0.0, o=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, err=None)
+        a.update(kw)
+        return lib.block_attn_tree(a["tm"], a["per"], a["dt"], a["bs"], a["B"], a["hq"], a["hkv"],
+                                   a["d"], a["P"], a["max_pages"], a["num_pages"], a["max_kv"],
+                                   a["q"], a["k"], a["v"], a["tab"], a["seq"], a["scale"], a["o"],
+                                   a["lse"], a["ws"], a["ws_bytes"], a["err"], None)
+    assert tree(tm=None) == b.SPEC_EINVAL
+    assert tree(B=65, hq=2, hkv=2) == b.SPEC_EINVAL       # more nodes than mask bits
+    assert tree(B=40) == b.SPEC_EINVAL                    # g * B = 160 > 128
+    assert tree(d=96) == b.SPEC_ENOTSUP
+    assert tree(q=None) == b.SPEC_EINVAL
+    # the mode argument of block_attn itself does not take TREE (no mask pointer)
+    assert _attn(lib, mode=3) == b.SPEC_EINVAL
+
+
 def test_block_attn_workspace_planning(lib):
     # few (request, KV head) units and a long context -> split-KV workspace
     small = lib.block_attn_workspace_bytes(2, 16, 32, 8, 128, 8192)

@@ -181,6 +181,53 @@ def test_balanced_schedule_all_rows(gpu_lib, name, cid, over, mode, nc_req):
         assert np.max(np.abs(lse[b] - rl[0])) <= LSE_TOL[cfg.dtype], b
 
 
+def run_tree(case, masks, max_kv=None):
+    x = case.x
+    tm = torch.from_numpy(masks.view(np.int64)).to("cuda")
+    lse = torch.empty((x.cfg.bs, x.cfg.block, x.cfg.hq), dtype=torch.float32, device="cuda")
+    o = va.block_attn_tree(tm, case.q, case.k, case.v, case.table, case.seq,
+                           max_kv or case.max_kv, lse=lse)
+    torch.cuda.synchronize()
+    return to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+TREES = [
+    # (name, config id, overrides, one tree per request)
+    ("b32_g4_d128_per_request", 6, dict(bs=4, ctx_lo=100, ctx_hi=900), True),
+    ("b64_g2_d64_shared", 6, dict(bs=3, hq=4, hkv=2, d=64, block=64, tree_depth=20, ctx_lo=0,
+                                  ctx_hi=600), False),
+    ("b16_g4_f32_d64", 6, dict(bs=3, hq=8, hkv=2, d=64, block=16, tree_depth=8, dtype="f32",
+                               ctx_lo=40, ctx_hi=500), True),
+    ("b32_p32_balanced", 6, dict(bs=128, hq=8, hkv=2, page=32, ctx_lo=1, ctx_hi=4200), True),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,per_req", TREES, ids=[t[0] for t in TREES])
+def test_tree_mode_all_rows(gpu_lib, name, cid, over, per_req):
+    cfg = synth.config(cid, **over)
+    print_case("block_attn_tree", name, cfg)
+    x = synth.make_attn_inputs(cfg, seed=31)
+    _, masks = synth.make_trees(cfg, 31, per_request=per_req)
+    o, lse = run_tree(AttnCase(x), masks)
+    ro, rl = oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                     x.page_table, x.seq_lens, oracle.TREE, 0, tree=masks)
+    assert np.max(np.abs(o - ro)) <= TOL[cfg.dtype]
+    assert np.max(np.abs(lse - rl)) <= LSE_TOL[cfg.dtype]
+
+
+def test_tree_chain_is_bitwise_causal(gpu_lib):
+    """A chain tree takes the same path through the kernel as the causal
+    mask: outputs must be identical, bit for bit."""
+    cfg = synth.config(2, bs=3, ctx_lo=200, ctx_hi=700)
+    print_case("block_attn_tree chain", cfg)
+    x = synth.make_attn_inputs(cfg, seed=32)
+    case = AttnCase(x)
+    chain = synth.tree_row_masks(np.arange(-1, cfg.block - 1, dtype=np.int32))
+    o_t, l_t = run_tree(case, chain)
+    o_c, l_c = run(case, synth.CAUSAL)
+    assert np.array_equal(o_t, o_c) and np.array_equal(l_t, l_c)
+
+
 def sampled_rows(x, n, rng):
     rows = set()
     B, hq = x.cfg.block, x.cfg.hq
@@ -192,7 +239,7 @@ def sampled_rows(x, n, rng):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6])
 def test_full_size_sampled_rows(gpu_lib, cid):
     """Full workload shapes in the bench's launch configuration; the reference
     computes sampled rows one at a time."""
@@ -201,11 +248,17 @@ def test_full_size_sampled_rows(gpu_lib, cid):
     x = synth.make_attn_inputs(cfg, seed=cid)
     case = AttnCase(x)
     mode = cfg.modes[0]
-    o, lse = run(case, mode)
+    masks = None
+    if mode == synth.TREE:
+        _, masks = synth.make_trees(cfg, cid)
+        o, lse = run_tree(case, masks)
+    else:
+        o, lse = run(case, mode)
     assert np.isfinite(o).all()
     rows = sampled_rows(x, 40, np.random.default_rng(cid))
     ro, rl = oracle.block_attn_rows(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
-                                    x.page_table, x.seq_lens, mode, cfg.n_causal, rows=rows)
+                                    x.page_table, x.seq_lens, mode, cfg.n_causal, rows=rows,
+                                    tree=masks)
     for (b, i, h) in rows:
         assert np.max(np.abs(o[b, i, h] - ro[b, i, h])) <= TOL[cfg.dtype], (b, i, h)
         assert abs(lse[b, i, h] - rl[b, i, h]) <= LSE_TOL[cfg.dtype], (b, i, h)

@@ -21,7 +21,7 @@ _LIB = None
 
 SPEC_OK, SPEC_EINVAL, SPEC_ENOTSUP, SPEC_ENOSPC, SPEC_EHIP = 0, -1, -2, -3, -4
 ERR_SLOT, ERR_CAPACITY, ERR_TOKEN, ERR_ZERO_RESIDUAL = 1, 2, 4, 8
-BIDIR, CAUSAL, MIXED = 0, 1, 2
+BIDIR, CAUSAL, MIXED, TREE = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
 _c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -35,6 +35,9 @@ _SIGS = {
     "block_attn": (_c_int, [_c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _f, _vp,
                             _vp, _vp, _c_size, _vp, _vp]),
+    "block_attn_tree": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _f, _vp,
+                                 _vp, _vp, _c_size, _vp, _vp]),
     "spec_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "spec_accept_workspace_bytes": (_c_size, [_c_int] * 4),
     "spec_accept": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -217,6 +220,59 @@ def block_attn_call(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n
             _check(st, "block_attn")
 
     return enqueue, out
+
+
+def block_attn_tree_call(tree_mask, q, k_pool, v_pool, page_table, seq_lens, max_kv_len,
+                         sm_scale=0.0, out=None, lse=None, ws=None, err=None, stream=None):
+    """Checks the arguments of block_attn_tree once and returns (enqueue, out).
+    tree_mask: int64 tensor of uint64 row bit patterns, [B] (one tree for the
+    batch) or [bs, B] (one tree per request)."""
+    torch = _torch()
+    bs, B, hq, d = q.shape
+    num_pages, hkv, P, d2 = k_pool.shape
+    _need(q, "q")
+    dt = _dtype_code(q)
+    _need(k_pool, "k_pool", q.dtype)
+    _need(v_pool, "v_pool", q.dtype, (num_pages, hkv, d, P))
+    if d2 != d:
+        raise ValueError("k_pool head dim differs from q")
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need(tree_mask, "tree_mask", torch.int64)
+    if tuple(tree_mask.shape) not in ((B,), (bs, B)):
+        raise ValueError(f"tree_mask must have shape ({B},) or ({bs}, {B})")
+    per_request = tree_mask.dim() == 2
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (bs, B, hq))
+    need = attn_workspace_bytes(bs, B, hq, hkv, d, max_kv_len)
+    if ws is None and need > 0:
+        ws = workspace(need, q.device)
+    args = (_ptr(tree_mask), int(per_request), dt, bs, B, hq, hkv, d, P, page_table.shape[1],
+            num_pages, max_kv_len, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+            _ptr(seq_lens), sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
+            0 if ws is None else ws.numel(), _ptr(err), _stream(stream))
+    fn = load().block_attn_tree
+    keep = (tree_mask, q, k_pool, v_pool, page_table, seq_lens, out, lse, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "block_attn_tree")
+
+    return enqueue, out
+
+
+def block_attn_tree(tree_mask, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, sm_scale=0.0,
+                    out=None, lse=None, ws=None, err=None, stream=None):
+    """Tree-block attention over the paged cache (block_attn_tree)."""
+    enqueue, out = block_attn_tree_call(tree_mask, q, k_pool, v_pool, page_table, seq_lens,
+                                        max_kv_len, sm_scale, out, lse, ws, err, stream)
+    enqueue()
+    return out
 
 
 def block_attn(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n_causal=0,

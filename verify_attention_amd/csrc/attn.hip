@@ -6,7 +6,9 @@
 // draft pass, a triangle for the AR verify pass, and the I-DLM mixed layout
 // (causal clean rows, bidirectional MASK rows) -- as drawn in the "Attention
 // Mask" section of "SGLang strengthens diffusion LLMs: LLaDA 2.0" and in
-// sections 4.3.1 / 4.4.1 of "From DFlash to dLLM Self-Spec (4)".
+// sections 4.3.1 / 4.4.1 of "From DFlash to dLLM Self-Spec (4)" -- or a
+// per-row bitmask over the block keys for tree verification (the Tree
+// sampler of "Unlocking Lossless Speedups in LLMs via Discrete Diffusion").
 //
 // Work decomposition: one 8-wave workgroup per (request, KV head, split).
 //   * All g * B query rows that share a KV head (the GQA group's query heads
@@ -398,6 +400,7 @@ struct WaveState {
   floatx4 acc[D / 16][MT];
   float m_run[MT], l_run[MT];
   int blk_row[MT];
+  uint64_t tmask[MT];  // TREE mode: the row's visibility bits over the block keys
 };
 
 // A stage is consumed in two halves so that the two waves sharing a SIMD can
@@ -455,7 +458,9 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
         for (int j = 0; j < 4; ++j) {
           const int key = key0 + 8 * grp + 4 * t2 + j;
           const int jb = key - L, i = ws.blk_row[t];
-          const bool vis = (key < L) | ((key < n_keys) & ((a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc))));
+          const bool intra = a.mode == 3 ? ((ws.tmask[t] >> (jb & 63)) & 1) != 0
+                                         : (a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc));
+          const bool vis = (key < L) | ((key < n_keys) & intra);
           st.s[t2][t][j] = vis ? st.s[t2][t][j] : -__builtin_inff();
         }
   }
@@ -543,6 +548,7 @@ __device__ __forceinline__ void load_q(WaveState<T, D, MT>& ws, const AttnArgs& 
     ws.blk_row[t] = r / a.g;
     const int rr = r < a.M ? r : 0;
     const int ii = rr / a.g, hh = rr - ii * a.g;
+    ws.tmask[t] = a.mode == 3 ? a.tree[(a.tree_per_req ? (size_t)b * a.B : 0) + ii] : 0;
     const T* src = qg + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hh) * D + 8 * grp;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {

@@ -167,22 +167,24 @@ SPEC_API size_t block_attn_workspace_bytes(int bs, int B, int Hq, int Hkv, int D
   return plan_attn(bs, B, Hq, Hkv, D, max_kv_len).ws_bytes;
 }
 
-SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req, int dtype, int bs,
-                        int B, int Hq, int Hkv, int D, int page_size, int max_pages,
-                        int num_pages, int max_kv_len, const void* q, const void* k_pool,
-                        const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
-                        float sm_scale, void* o, float* lse, void* workspace, size_t ws_bytes,
-                        int32_t* err_flags, void* stream) {
+namespace {
+
+int attn_common(int mode, int n_causal, const int32_t* n_causal_per_req, const uint64_t* tree,
+                int tree_per_request, int dtype, int bs, int B, int Hq, int Hkv, int D,
+                int page_size, int max_pages, int num_pages, int max_kv_len, const void* q,
+                const void* k_pool, const void* v_pool, const int32_t* page_table,
+                const int32_t* seq_lens, float sm_scale, void* o, float* lse, void* workspace,
+                size_t ws_bytes, int32_t* err_flags, void* stream) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
   if (D != 64 && D != 128) return SPEC_ENOTSUP;
   if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
-  if (mode < SPEC_BIDIR || mode > SPEC_MIXED) return SPEC_EINVAL;
   if (bs <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return SPEC_EINVAL;
   if ((Hq / Hkv) * B > 128) return SPEC_EINVAL;
   if (max_pages <= 0 || num_pages <= 0 || max_kv_len <= 0) return SPEC_EINVAL;
   if ((long long)max_pages * page_size < B) return SPEC_EINVAL;
   if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
   if (mode == SPEC_MIXED && !n_causal_per_req && (n_causal < 0 || n_causal > B)) return SPEC_EINVAL;
+  if (mode == SPEC_TREE && (!tree || B > 64)) return SPEC_EINVAL;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return SPEC_EINVAL;
   if (!(std::isfinite(sm_scale))) return SPEC_EINVAL;
   const AttnPlan plan = plan_attn(bs, B, Hq, Hkv, D, max_kv_len);
@@ -195,6 +197,8 @@ SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req,
   a.page_table = page_table;
   a.seq_lens = seq_lens;
   a.nc_per_req = mode == SPEC_MIXED ? n_causal_per_req : nullptr;
+  a.tree = mode == SPEC_TREE ? tree : nullptr;
+  a.tree_per_req = tree_per_request ? 1 : 0;
   a.o = o;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
@@ -221,6 +225,32 @@ SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req,
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(launch_block_attn(a, dtype == SPEC_BF16, D, plan.grid,
                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+SPEC_API int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req, int dtype, int bs,
+                        int B, int Hq, int Hkv, int D, int page_size, int max_pages,
+                        int num_pages, int max_kv_len, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+                        float sm_scale, void* o, float* lse, void* workspace, size_t ws_bytes,
+                        int32_t* err_flags, void* stream) {
+  if (mode < SPEC_BIDIR || mode > SPEC_MIXED) return SPEC_EINVAL;
+  return attn_common(mode, n_causal, n_causal_per_req, nullptr, 0, dtype, bs, B, Hq, Hkv, D,
+                     page_size, max_pages, num_pages, max_kv_len, q, k_pool, v_pool, page_table,
+                     seq_lens, sm_scale, o, lse, workspace, ws_bytes, err_flags, stream);
+}
+
+SPEC_API int block_attn_tree(const uint64_t* tree_mask, int tree_per_request, int dtype, int bs,
+                             int B, int Hq, int Hkv, int D, int page_size, int max_pages,
+                             int num_pages, int max_kv_len, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* page_table,
+                             const int32_t* seq_lens, float sm_scale, void* o, float* lse,
+                             void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream) {
+  return attn_common(SPEC_TREE, 0, nullptr, tree_mask, tree_per_request, dtype, bs, B, Hq, Hkv,
+                     D, page_size, max_pages, num_pages, max_kv_len, q, k_pool, v_pool,
+                     page_table, seq_lens, sm_scale, o, lse, workspace, ws_bytes, err_flags,
+                     stream);
 }
 
 SPEC_API int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* tokens,

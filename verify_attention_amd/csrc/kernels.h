@@ -12,6 +12,7 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* seq_lens;
   const int32_t* nc_per_req;
+  const uint64_t* tree;  // TREE mode: row masks over the block keys, [B] or [bs][B]
   void* o;
   float* lse;
   float* part_o;      // [slots][M][D] partial outputs (unnormalised): split or cut-unit pieces
@@ -20,6 +21,7 @@ struct AttnArgs {
   int bs, B, Hq, Hkv, g, M;  // M = g * B query rows per KV head
   int P, p_shift, max_pages, num_pages;
   int mode, n_causal;
+  int tree_per_req;
   int splits, steps_per_split;
   int balanced, G;   // balanced schedule: G persistent workgroups
   float scale_log2;  // sm_scale * log2(e)
