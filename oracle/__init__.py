@@ -13,7 +13,8 @@ Modules:
                masked-softmax matrix form
   accept    -- speculative accept: p/q rejection test, longest accepted
                prefix, residual (or bonus) sample, committed length; the greedy
-               special case; argmax with the lowest index winning
+               special case; argmax with the lowest index winning; the tree
+               walk (recursive rejection over deterministic candidates)
 
 Parity status: every function here is pinned by CPU tests against closed
 forms, library routines, brute force or exact enumeration (see the tests
@@ -22,10 +23,11 @@ named test_oracle_*). None is "parity unpinned".
 from .prepare import prepare_block
 from .attention import (BIDIR, CAUSAL, MIXED, TREE, visible, block_attn_rows,
                         block_attn_dense, attn_row, unpage_kv, mask_matrix)
-from .accept import accept_request, accept_batch, greedy_accept_request, argmax_lowest
+from .accept import (accept_request, accept_batch, greedy_accept_request, argmax_lowest,
+                     tree_accept_request, tree_children)
 
 __all__ = [
     "prepare_block", "BIDIR", "CAUSAL", "MIXED", "TREE", "visible", "block_attn_rows",
     "block_attn_dense", "attn_row", "unpage_kv", "mask_matrix", "accept_request", "accept_batch",
-    "greedy_accept_request", "argmax_lowest",
+    "greedy_accept_request", "argmax_lowest", "tree_accept_request", "tree_children",
 ]

@@ -19,6 +19,11 @@ What is computed:
 * "From DFlash to dLLM Self-Spec (4)", section 4.4.1 (LinearSpec verify):
   count matching positions, add one, crop the cache to length + accepted, and
   carry the last emitted token into the next round.
+* "Unlocking Lossless Speedups in LLMs via Discrete Diffusion", method steps
+  (the Tree sampler: top candidates per position kept as a tree of prefixes,
+  verified in parallel, losslessness from rejection sampling):
+  tree_accept_request walks the tree from the root with the recursive
+  rejection rule for deterministic candidates (see its docstring).
 
 Readings where the pages are silent:
 * Row alignment: target row i (0-based, i = 0..K) scores block token i+1, so
@@ -117,6 +122,89 @@ def greedy_accept_request(p, draft, seq_len):
     return dict(accept_len=n_acc, commit_len=n_acc + 1, bonus=bonus, out_tokens=out,
                 new_seq_len=int(seq_len) + n_acc + 1, err=0, tie=False, tie_accept=False,
                 tie_sample=False)
+
+
+ERR_TREE = 16  # a node's parent is not an earlier node (the node is ignored)
+
+
+def tree_children(parent, x):
+    """Children of node x in increasing node order (nodes whose parent is x;
+    a node n is only a child when 0 <= parent[n] < n)."""
+    return [n for n in range(1, len(parent)) if int(parent[n]) == x and 0 <= x < n]
+
+
+def tree_accept_request(parent, token, p, u, seq_len):
+    """Tree verification of one request by recursive rejection sampling.
+
+    The tree's candidates are deterministic (top candidates), so each child
+    is a draft with a one-hot draft distribution: at node x (starting at the
+    root, node 0) the children c are tried in increasing node order; with T
+    the target mass p_x of the distinct tokens already tried at x, child c is
+    accepted iff u[c] * (1 - T) < p_x(token[c]) (the probability p_x(t) / (1 -
+    T) of the normalised residual; a token already tried has residual 0, an
+    id outside [0, V) is a reject and is flagged). An accepted child becomes
+    the next node. When no child of x is accepted (or x is a leaf) the bonus
+    is drawn from r = p_x with the tried tokens set to 0: the smallest t with
+    C_t > u[0] * S, C the running sum of r in vocabulary order, S = sum r
+    (S <= 0: drawn from p_x itself and flagged).
+
+    parent [N] (parent[0] = -1), token [N] (token[0], the root, is not read),
+    p [N, V] float32 (row n: the target distribution of the token after
+    node n's path), u [N] float32. Returns accept_len (accepted nodes),
+    path_nodes [N] (accepted node ids, then -1), out_tokens [N] (their
+    tokens, then the bonus, then -1), bonus, commit_len, new_seq_len, err and
+    tie flags as accept_request (tie_accept: a test with |u - p/(1 - T)| <
+    1e-6; tie_sample: the final threshold within 1e-6 * S of an interval end).
+    """
+    N, V = p.shape
+    err = 0
+    for n in range(1, N):
+        if not 0 <= int(parent[n]) < n:
+            err |= ERR_TREE
+    path = []
+    tie_accept = False
+    x = 0
+    while True:
+        tried = []
+        nxt = -1
+        T = np.float64(0.0)
+        for c in tree_children(parent, x):
+            d = int(token[c])
+            if d < 0 or d >= V:
+                err |= ERR_TOKEN
+                continue
+            pr = np.float64(0.0) if d in tried else np.float64(p[x, d])
+            uc = np.float64(u[c])
+            if 1.0 - T > 0 and abs(uc - pr / (1.0 - T)) < TIE_EPS:
+                tie_accept = True
+            if uc * (1.0 - T) < pr:
+                nxt = c
+                break
+            if d not in tried:
+                tried.append(d)
+                T += pr
+        if nxt < 0:
+            break
+        path.append(nxt)
+        x = nxt
+    r = p[x].astype(np.float64)
+    for d in tried:
+        r[d] = 0.0
+    if not r.sum() > 0:
+        err |= ERR_ZERO_RESIDUAL
+        r = p[x].astype(np.float64)
+    t, S, thr, C = _inverse_cdf(r, u[0])
+    lo = C[t - 1] if t > 0 else 0.0
+    tie_sample = bool(abs(thr - C[t]) < TIE_EPS * S or abs(thr - lo) < TIE_EPS * S)
+    k = len(path)
+    nodes = np.full(N, -1, np.int64)
+    nodes[:k] = path
+    out = np.full(N, -1, np.int64)
+    out[:k] = [int(token[c]) for c in path]
+    out[k] = t
+    return dict(accept_len=k, commit_len=k + 1, bonus=t, out_tokens=out, path_nodes=nodes,
+                new_seq_len=int(seq_len) + k + 1, err=err, tie=tie_accept or tie_sample,
+                tie_accept=tie_accept, tie_sample=tie_sample)
 
 
 def accept_batch(p, q, draft, u, seq_lens, greedy=False, requests=None):

@@ -246,3 +246,158 @@ def test_argmax_lowest_index_matches_numpy():
     x = np.zeros(10)
     x[[3, 7]] = 1
     assert oracle.argmax_lowest(x) == 3
+
+
+# ------------------------------------------------------------------ tree walk
+def _tree_key(r):
+    return tuple(int(n) for n in r["path_nodes"][:r["accept_len"]]), int(r["bonus"])
+
+
+def exact_tree_distribution(parent, token, p, grid=256):
+    """{(accepted nodes, bonus): probability} of the tree walk under
+    independent U[0, 1) uniforms, integrated exactly with the reference as a
+    black box. Nodes are numbered breadth first, so a decision on u[c] can
+    only depend on uniforms of lower-numbered nodes: the uniforms are scanned
+    in node order (then u[0], the final draw), each one split into the pieces
+    on which the output is constant with the earlier ones fixed inside their
+    pieces."""
+    N = len(parent)
+    order = list(range(1, N)) + [0]
+    dist = {}
+
+    def rec(k, u, w):
+        if k == len(order):
+            key = _tree_key(oracle.tree_accept_request(parent, token, p, u, 0))
+            dist[key] = dist.get(key, 0.0) + w
+            return
+        dim = order[k]
+
+        def call(x):
+            uu = u.copy()
+            uu[dim] = x
+            return _tree_key(oracle.tree_accept_request(parent, token, p, uu, 0))
+
+        pieces = _scan_last_uniform(call, grid)
+        lo = 0.0
+        for length, _ in pieces:
+            uu = u.copy()
+            uu[dim] = lo + length / 2
+            rec(k + 1, uu, w * length)
+            lo += length
+
+    rec(0, np.full(N, 0.5), 1.0)
+    return dist
+
+
+TREES_BFS = [
+    # (parent, V, seed): breadth-first numbered trees
+    ([-1, 0, 0, 1, 1, 2], 5, 0),
+    ([-1, 0, 0, 0, 1, 3], 6, 1),
+    ([-1, 0, 1, 2], 4, 2),        # a chain
+    ([-1, 0, 0, 0], 5, 3),        # one level, three candidates
+]
+
+
+def _tree_case(parent, V, seed):
+    rng = np.random.default_rng(seed)
+    N = len(parent)
+    token = np.zeros(N, np.int64)
+    for x in range(N):
+        kids = oracle.tree_children(parent, x)
+        token[kids] = rng.choice(V, size=len(kids), replace=False)   # distinct siblings
+    p = np.stack([_dist(rng, V) for _ in range(N)])
+    return np.array(parent), token, p
+
+
+@pytest.mark.parametrize("parent,V,seed", TREES_BFS)
+def test_tree_walk_is_lossless_exactly(parent, V, seed):
+    """Losslessness of the tree walk: every (accepted path, bonus) outcome has
+    exactly the target's autoregressive probability of the emitted tokens
+    along the tree, prod p[parent(n)](token n) * p[last](bonus), and a bonus is
+    never one of the last node's child tokens (those are emitted by
+    descending)."""
+    parent, token, p = _tree_case(parent, V, seed)
+    dist = exact_tree_distribution(parent, token, p)
+    assert abs(sum(dist.values()) - 1) < 1e-12
+    seen = 0.0
+    for (path, bonus), w in dist.items():
+        prob, x = 1.0, 0
+        for n in path:
+            assert parent[n] == x
+            prob *= p[x, token[n]]
+            x = n
+        assert bonus not in [token[c] for c in oracle.tree_children(parent, x)]
+        prob *= p[x, bonus]
+        assert abs(w - prob) < 1e-10, (path, bonus, w, prob)
+        seen += prob
+    # every emitted sequence of positive probability occurs
+    assert abs(seen - 1) < 1e-10
+
+
+def test_chain_tree_is_the_linear_accept_with_one_hot_drafts():
+    """A chain tree is a linear block whose draft distributions are one-hot at
+    the draft tokens: the tree walk must agree with the (separately pinned)
+    linear reference fed q = one-hot, test uniforms u[1..K] and final u[0]."""
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        K, V = int(rng.integers(1, 6)), int(rng.integers(2, 9))
+        parent = np.arange(-1, K, dtype=np.int64)
+        token = np.concatenate([[0], rng.integers(0, V, size=K)])
+        p = np.stack([_dist(rng, V, floor=0.01) for _ in range(K + 1)]).astype(np.float32)
+        u = rng.random(K + 1).astype(np.float32)
+        q = np.zeros((K, V), np.float32)
+        q[np.arange(K), token[1:]] = 1.0
+        lin = oracle.accept_request(p, q, token[1:], np.concatenate([u[1:], u[:1]]), 5)
+        tr = oracle.tree_accept_request(parent, token, p, u, 5)
+        for key in ("accept_len", "commit_len", "bonus", "new_seq_len", "err"):
+            assert lin[key] == tr[key], (trial, key)
+        assert np.array_equal(lin["out_tokens"], tr["out_tokens"])
+        assert np.array_equal(tr["path_nodes"][:tr["accept_len"]], np.arange(1, tr["accept_len"] + 1))
+
+
+def test_planted_tree_normaliser_mistake_breaks_losslessness(monkeypatch):
+    """Discrimination check: testing later siblings against p alone (dropping
+    the 1 - T normaliser of the residual) must fail the exact test."""
+    parent, token, p = _tree_case([-1, 0, 0, 0], 5, 3)
+    real = oracle.accept.np.float64
+
+    class NoRenorm:
+        calls = 0
+
+    def fake_tree(parent, token, p, u, seq_len):
+        # same walk with T frozen at 0
+        N, V = p.shape
+        x, path, tried = 0, [], []
+        while True:
+            nxt = -1
+            tried = []
+            for c in oracle.tree_children(parent, x):
+                d = int(token[c])
+                if real(u[c]) < real(p[x, d]) and d not in tried:
+                    nxt = c
+                    break
+                tried.append(d)
+            if nxt < 0:
+                break
+            path.append(nxt)
+            x = nxt
+        r = p[x].astype(real)
+        r[tried] = 0.0
+        t = int(np.searchsorted(np.cumsum(r), real(u[0]) * r.sum(), side="right"))
+        nodes = np.full(N, -1)
+        nodes[:len(path)] = path
+        return dict(accept_len=len(path), path_nodes=nodes, bonus=t)
+
+    monkeypatch.setattr(oracle, "tree_accept_request", fake_tree)
+    with pytest.raises(AssertionError):
+        test_tree_walk_is_lossless_exactly([-1, 0, 0, 0], 5, 3)
+
+
+def test_tree_walk_flags_bad_tokens_and_parents():
+    p = np.full((4, 3), 1 / 3, np.float32)
+    r = oracle.tree_accept_request(np.array([-1, 0, 0, 5]), np.array([0, 7, 1, 2]), p,
+                                   np.zeros(4, np.float32), 10)
+    assert r["err"] & oracle.accept.ERR_TOKEN and r["err"] & oracle.accept.ERR_TREE
+    # u = 0 accepts the first valid child (node 2), a leaf; bonus from p[2]
+    assert r["accept_len"] == 1 and r["path_nodes"][0] == 2 and r["out_tokens"][0] == 1
+    assert r["new_seq_len"] == 12
