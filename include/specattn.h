@@ -12,7 +12,7 @@
  *   spec_prepare_block  (verify pass, with the draft tokens)
  *   block_attn(SPEC_CAUSAL | SPEC_MIXED), or block_attn_tree for a token tree
  *   [caller produces target rows p]
- *   spec_accept                       -> accepted prefix, bonus, new lengths
+ *   spec_accept (or spec_accept_tree) -> accepted prefix, bonus, new lengths
  *
  * Conventions shared by every call
  * --------------------------------
@@ -60,6 +60,7 @@ extern "C" {
 #define SPEC_ERR_CAPACITY 2       /* seq_len < 0 or seq_len + B > max_pages * P                 */
 #define SPEC_ERR_TOKEN 4          /* a draft token id is outside [0, V)                          */
 #define SPEC_ERR_ZERO_RESIDUAL 8  /* residual mass was zero; the draw used the target row        */
+#define SPEC_ERR_TREE 16          /* a tree node's parent is not an earlier node (node ignored)  */
 
 typedef enum { SPEC_BIDIR = 0, SPEC_CAUSAL = 1, SPEC_MIXED = 2, SPEC_TREE = 3 } spec_mode;
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
@@ -240,6 +241,55 @@ int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q
                 int32_t* accept_len, int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
                 int32_t* new_seq_lens, void* workspace, size_t ws_bytes, int32_t* err_flags,
                 void* stream);
+
+/*
+ * spec_accept_tree -- speculative accept for a token tree (tree verify).
+ *
+ * Follows the Tree sampler of "Unlocking Lossless Speedups in LLMs via
+ * Discrete Diffusion" (method steps: top candidates per position kept as a
+ * tree, verified in parallel, lossless through rejection sampling). Its
+ * candidates are deterministic, so every child is a draft whose draft
+ * distribution is one-hot; the rejection rule for such drafts, applied from
+ * the root down, is:
+ *   at node x (start: the root, node 0), try the children c of x in
+ *   increasing node order; with T the target mass p[b,x,.] of the distinct
+ *   tokens already tried at x, child c is accepted iff
+ *   u[b,c] * (1 - T) < p[b,x,token[c]] (double); the first accepted child
+ *   becomes the next node. A child repeating a tried token is never accepted;
+ *   a token id outside [0, V) is a reject and sets SPEC_ERR_TOKEN.
+ *   When no child of x is accepted (or x is a leaf), the bonus is the smallest
+ *   t with C_t > u[b,0] * S, where C is the running sum (double, vocabulary
+ *   order) of r = p[b,x,.] with the tried tokens set to 0 and S = sum r (S <= 0:
+ *   drawn from p[b,x,.] itself, SPEC_ERR_ZERO_RESIDUAL).
+ * Every emitted token is then distributed as the target's next-token
+ * distribution at its position, as for the linear rule.
+ *
+ *   bs, N, V          requests, tree nodes per request (1..64), vocabulary
+ *                     (<= 524288)
+ *   parent [bs, N]    parent node; parent[b,0] = -1 (the root is the last
+ *                     committed token); a node n >= 1 needs 0 <= parent < n
+ *                     (else it is ignored and SPEC_ERR_TREE is set)
+ *   token [bs, N]     candidate token of node n (token[b,0] is not read)
+ *   p [bs, N, V]      float target rows: row n is the distribution of the
+ *                     token that follows node n's root path
+ *   u [bs, N]         float uniforms in [0, 1): u[b,c] drives child c's test,
+ *                     u[b,0] the bonus draw
+ *   seq_lens [bs]
+ * Outputs: accept_len [bs] (accepted nodes), path_nodes [bs, N] (their ids in
+ *   order, then -1), out_tokens [bs, N] (their tokens, the bonus, then -1),
+ *   bonus, commit_len = accept_len + 1, new_seq_lens = seq_lens + commit_len.
+ * Workspace: spec_accept_tree_workspace_bytes(bs, N, V) bytes, 16-byte
+ *   aligned, contents irrelevant; calls sharing it must be ordered.
+ * Errors: SPEC_EINVAL (bs <= 0, N outside 1..64, V <= 0, NULL), SPEC_ENOSPC,
+ *   SPEC_ENOTSUP (V > 524288).
+ */
+size_t spec_accept_tree_workspace_bytes(int bs, int N, int V);
+
+int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const int32_t* token,
+                     const float* p, const float* u, const int32_t* seq_lens,
+                     int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                     int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
+                     void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream);
 
 #ifdef __cplusplus
 }

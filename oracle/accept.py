@@ -35,7 +35,8 @@ Readings where the pages are silent:
   reject at j, else r = p_K; S = sum r; the token is the smallest t with
   C_t > u_K * S (C = running sum in vocabulary order). If S <= 0 the draw
   falls back to p_j and flags it; if rounding leaves no C_t above the
-  threshold the last index with r > 0 is taken.
+  threshold the last index with r > 0 is taken; a row with no positive entry
+  at all (not a distribution) yields token 0.
 """
 import numpy as np
 
@@ -53,13 +54,15 @@ def argmax_lowest(x):
 
 def _inverse_cdf(r, u):
     """Smallest t with C_t > u * S, C the running sum of r. Returns
-    (t, S, thr, C) with a fallback to the last positive entry."""
+    (t, S, thr, C) with a fallback to the last positive entry (token 0 when
+    the row holds no positive entry at all)."""
     C = np.cumsum(r)
     S = C[-1]
     thr = np.float64(u) * S
     t = int(np.searchsorted(C, thr, side="right"))
     if t >= len(r):
-        t = int(np.flatnonzero(r > 0)[-1])
+        pos = np.flatnonzero(r > 0)
+        t = int(pos[-1]) if len(pos) else 0
     return t, S, thr, C
 
 

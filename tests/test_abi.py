@@ -148,6 +148,26 @@ def test_accept_rejects_bad_arguments(lib):
     assert lib.spec_accept_workspace_bytes(4, 15, 151936, 1) == 4 * 16 * 4
 
 
+def test_accept_tree_rejects_bad_arguments(lib):
+    def acc(**kw):
+        a = dict(bs=4, N=32, V=151936, par=FAKE, tok=FAKE, p=FAKE, u=FAKE, seq=FAKE, al=FAKE,
+                 cl=FAKE, bon=FAKE, out=FAKE, path=FAKE, nsl=FAKE, ws=FAKE, ws_bytes=1 << 30,
+                 err=None)
+        a.update(kw)
+        return lib.spec_accept_tree(a["bs"], a["N"], a["V"], a["par"], a["tok"], a["p"], a["u"],
+                                    a["seq"], a["al"], a["cl"], a["bon"], a["out"], a["path"],
+                                    a["nsl"], a["ws"], a["ws_bytes"], a["err"], None)
+    assert acc(bs=0) == b.SPEC_EINVAL
+    assert acc(N=0) == b.SPEC_EINVAL
+    assert acc(N=65) == b.SPEC_EINVAL
+    assert acc(par=None) == b.SPEC_EINVAL
+    assert acc(path=None) == b.SPEC_EINVAL
+    assert acc(V=524289) == b.SPEC_ENOTSUP
+    need = lib.spec_accept_tree_workspace_bytes(4, 32, 151936)
+    assert need > lib.spec_accept_workspace_bytes(4, 31, 151936, 0)   # + the node ids
+    assert acc(ws_bytes=need - 1) == b.SPEC_ENOSPC
+
+
 def test_argmax_rejects_bad_arguments(lib):
     assert lib.spec_draft_argmax(0, 10, 1, FAKE, FAKE, None) == b.SPEC_EINVAL
     assert lib.spec_draft_argmax(4, 0, 1, FAKE, FAKE, None) == b.SPEC_EINVAL

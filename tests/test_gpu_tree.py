@@ -1,0 +1,109 @@
+"""GPU parity of the tree verify path: spec_accept_tree against the float64
+tree walk of the CPU reference (bit-exact outputs for every request whose
+walk has no tie within 1e-6; ties are counted and reported)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import verify_attention_amd as va
+from verify_attention_amd import synth
+from _support import print_case, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_tree_accept(ti, seq, err=None, ws=None, out=None):
+    dev = lambda a: to_dev(np.ascontiguousarray(a))
+    res = va.accept_tree(dev(ti.parent), dev(ti.token), dev(ti.p), dev(ti.u), dev(seq), err=err,
+                         ws=ws, out=out)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def compare(ti, seq, got):
+    bs = ti.parent.shape[0]
+    ties = differ = 0
+    for b in range(bs):
+        r = oracle.tree_accept_request(ti.parent[b], ti.token[b], ti.p[b], ti.u[b], seq[b])
+        same = (got["accept_len"][b] == r["accept_len"] and got["bonus"][b] == r["bonus"] and
+                got["commit_len"][b] == r["commit_len"] and
+                got["new_seq_lens"][b] == r["new_seq_len"] and
+                np.array_equal(got["out_tokens"][b], r["out_tokens"]) and
+                np.array_equal(got["path_nodes"][b], r["path_nodes"]))
+        if r["tie"]:
+            ties += 1
+            differ += not same
+            continue
+        assert same, (b, {k: got[k][b] for k in got}, r)
+    print(f"ties {ties} of {bs} requests ({differ} of them differ)", flush=True)
+    return ties
+
+
+def test_tree_accept_full_vocab(gpu_lib):
+    cfg = synth.config(6, bs=16)
+    print_case("spec_accept_tree full vocab", cfg.name, "bs", cfg.bs)
+    par, _ = synth.make_trees(cfg, 41)
+    ti = synth.make_tree_accept_inputs(cfg, 41, par)
+    seq = np.full(cfg.bs, 1000, np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = run_tree_accept(ti, seq, err=err)
+    assert int(err.item()) == 0
+    assert compare(ti, seq, got) <= 2
+    assert got["accept_len"].max() >= 1   # the workload does accept children
+
+
+@pytest.mark.parametrize("N,V,depth,seed", [(16, 64, 6, 1), (64, 37, 12, 2), (1, 50, 1, 3),
+                                            (33, 4099, 10, 4)])
+def test_tree_accept_small_vocab_many_requests(gpu_lib, N, V, depth, seed):
+    """Small vocabularies make deep acceptance common; N = 64 fills the wave,
+    N = 1 is a root alone (bonus only), V = 4099 leaves a ragged last
+    sub-block."""
+    cfg = synth.config(6, bs=256, block=N, tree_depth=depth, vocab=V, logit_sigma=2.0)
+    print_case("spec_accept_tree small vocab", N, V, depth)
+    par, _ = synth.make_trees(cfg, seed)
+    ti = synth.make_tree_accept_inputs(cfg, seed, par)
+    seq = np.random.default_rng(seed).integers(0, 5000, size=cfg.bs).astype(np.int32)
+    got = run_tree_accept(ti, seq)
+    ties = compare(ti, seq, got)
+    assert ties <= cfg.bs // 20
+    if N > 1:
+        assert got["accept_len"].max() >= 2
+
+
+def test_tree_accept_workspace_reuse_and_error_paths(gpu_lib):
+    cfg = synth.config(6, bs=6, block=8, tree_depth=4, vocab=300, logit_sigma=2.0)
+    print_case("spec_accept_tree error paths", cfg)
+    par, _ = synth.make_trees(cfg, 5)
+    ti = synth.make_tree_accept_inputs(cfg, 5, par)
+    ti.token[1, np.flatnonzero(ti.parent[1] == 0)[0]] = cfg.vocab + 3    # invalid token id
+    ti.parent[2, 5] = 7                                                  # parent not earlier
+    ti.p[3] = 0.0                                                        # rows without mass
+    seq = np.arange(cfg.bs, dtype=np.int32) * 10
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = va.workspace(va.accept_tree_workspace_bytes(cfg.bs, cfg.block, cfg.vocab))
+    first = run_tree_accept(ti, seq, err=err, ws=ws)
+    e = int(err.item())
+    assert e & va.ERR_TREE and e & va.ERR_ZERO_RESIDUAL and e & va.ERR_TOKEN
+    compare(ti, seq, first)
+    second = run_tree_accept(ti, seq, ws=ws)
+    for k in first:
+        assert np.array_equal(first[k], second[k])
+    assert first["bonus"][3] == 0 and first["accept_len"][3] == 0
+
+
+def test_linear_accept_zero_rows(gpu_lib):
+    """A target row with no mass at all (not a distribution): both sides give
+    token 0 and the zero-residual flag."""
+    cfg = synth.config(2, bs=4, vocab=2000, k_spec=3)
+    print_case("spec_accept zero rows", cfg)
+    acc = synth.make_accept_inputs(cfg, 9)
+    acc.p[2] = 0.0
+    dev = lambda a: to_dev(np.ascontiguousarray(a))
+    seq = np.zeros(cfg.bs, np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = va.accept(dev(acc.p), dev(acc.q), dev(acc.draft), dev(acc.u), dev(seq), err=err)
+    torch.cuda.synchronize()
+    r = oracle.accept_request(acc.p[2], acc.q[2], acc.draft[2], acc.u[2], 0)
+    assert int(got["bonus"][2]) == r["bonus"] == 0 and int(got["accept_len"][2]) == r["accept_len"]
+    assert int(err.item()) & va.ERR_ZERO_RESIDUAL

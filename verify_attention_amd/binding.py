@@ -20,7 +20,7 @@ _ROOT = os.path.dirname(_HERE)
 _LIB = None
 
 SPEC_OK, SPEC_EINVAL, SPEC_ENOTSUP, SPEC_ENOSPC, SPEC_EHIP = 0, -1, -2, -3, -4
-ERR_SLOT, ERR_CAPACITY, ERR_TOKEN, ERR_ZERO_RESIDUAL = 1, 2, 4, 8
+ERR_SLOT, ERR_CAPACITY, ERR_TOKEN, ERR_ZERO_RESIDUAL, ERR_TREE = 1, 2, 4, 8, 16
 BIDIR, CAUSAL, MIXED, TREE = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
@@ -40,6 +40,9 @@ _SIGS = {
                                  _vp, _vp, _c_size, _vp, _vp]),
     "spec_draft_argmax": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "spec_accept_workspace_bytes": (_c_size, [_c_int] * 4),
+    "spec_accept_tree_workspace_bytes": (_c_size, [_c_int] * 3),
+    "spec_accept_tree": (_c_int, [_c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "spec_accept": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
 }
@@ -355,5 +358,54 @@ def accept(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, 
     """Speculative accept / bonus (spec_accept). Returns a dict of int32 tensors:
     accept_len, commit_len, bonus, out_tokens [bs, K+1], new_seq_lens."""
     enqueue, out = accept_call(p, q, draft, u, seq_lens, greedy, out, ws, err, stream)
+    enqueue()
+    return out
+
+
+def accept_tree_workspace_bytes(bs, N, V) -> int:
+    return int(load().spec_accept_tree_workspace_bytes(bs, N, V))
+
+
+def accept_tree_call(parent, token, p, u, seq_lens, out=None, ws=None, err=None, stream=None):
+    """Checks the arguments of spec_accept_tree once and returns (enqueue, out).
+    parent, token [bs, N] int32; p [bs, N, V] float32; u [bs, N] float32."""
+    torch = _torch()
+    bs, N, V = p.shape
+    _need(p, "p", torch.float32)
+    _need(parent, "parent", torch.int32, (bs, N))
+    _need(token, "token", torch.int32, (bs, N))
+    _need(u, "u", torch.float32, (bs, N))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    dev = p.device
+    if out is None:
+        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((bs, N), dtype=torch.int32, device=dev),
+                   path_nodes=torch.empty((bs, N), dtype=torch.int32, device=dev),
+                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = workspace(accept_tree_workspace_bytes(bs, N, V), dev)
+    args = (bs, N, V, _ptr(parent), _ptr(token), _ptr(p), _ptr(u), _ptr(seq_lens),
+            _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
+            _ptr(out["out_tokens"]), _ptr(out["path_nodes"]), _ptr(out["new_seq_lens"]),
+            _ptr(ws), ws.numel(), _ptr(err), _stream(stream))
+    fn = load().spec_accept_tree
+    keep = (parent, token, p, u, seq_lens, out, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_accept_tree")
+
+    return enqueue, out
+
+
+def accept_tree(parent, token, p, u, seq_lens, out=None, ws=None, err=None, stream=None):
+    """Tree accept (spec_accept_tree). Returns a dict of int32 tensors:
+    accept_len, commit_len, bonus, out_tokens [bs, N], path_nodes [bs, N],
+    new_seq_lens."""
+    enqueue, out = accept_tree_call(parent, token, p, u, seq_lens, out, ws, err, stream)
     enqueue()
     return out

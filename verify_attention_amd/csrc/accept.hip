@@ -89,6 +89,34 @@ __device__ __forceinline__ bool rows_aligned(const float* p, const float* q) {
   return ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(q ? q : p)) & 15) == 0;
 }
 
+// Residual rows as functors: r(e .. e+3) for one lane.
+// Linear verify: max(p - q, 0), or p alone (bonus row / fallback).
+struct ResidPQ {
+  const float* p;
+  const float* q;
+  int V;
+  bool vec;
+  __device__ __forceinline__ void operator()(int e, double (&r)[4]) const { resid4(p, q, e, V, vec, r); }
+};
+
+// Tree verify: p with the listed tokens (the tried children, in LDS) at 0.
+struct ResidExcl {
+  const float* p;
+  int V;
+  bool vec;
+  const int* excl;
+  int n;
+  __device__ __forceinline__ void operator()(int e, double (&r)[4]) const {
+    resid4(p, nullptr, e, V, vec, r);
+    for (int k = 0; k < n; ++k) {
+      const int t = excl[k];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t == e + i) r[i] = 0.0;
+    }
+  }
+};
+
 // Kernel 1, one workgroup per (request, vocabulary chunk): the accept length,
 // then the residual (or bonus) mass of every 256-entry sub-block of the chunk
 // (one wave per sub-block, 4 entries per lane).
@@ -144,13 +172,14 @@ __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs 
 // Smallest index t of sub-block sb with base + sum_{v<=t} r_v > thr, found by
 // wave 0 (4 entries per lane, then a wave scan); -1 when none passes, with
 // *lastp the last index holding mass. Every thread gets the result.
-__device__ int sub_block_search(const float* p, const float* q, int sb, int V, bool vec,
-                                double base, double thr, int* s_int, int* lastp) {
+template <typename R>
+__device__ int sub_block_search(const R& res, int sb, double base, double thr, int* s_int,
+                                int* lastp) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid < 64) {
     const int e = sb * kSub + 4 * lane;
     double r[4];
-    resid4(p, q, e, V, vec, r);
+    res(e, r);
     const double mine = (r[0] + r[1]) + (r[2] + r[3]);
     double run = base + (wave_inclusive_scan(mine) - mine);
     int found = -1, lp = -1;
@@ -170,10 +199,10 @@ __device__ int sub_block_search(const float* p, const float* q, int sb, int V, b
     }
   }
   __syncthreads();
-  const int res = s_int[0];
+  const int found = s_int[0];
   *lastp = s_int[1];
   __syncthreads();
-  return res;
+  return found;
 }
 
 // Draws the token from sub-block masses: thread tid holds the masses of
@@ -181,9 +210,9 @@ __device__ int sub_block_search(const float* p, const float* q, int sb, int V, b
 // Returns -1 if the total mass is not > 0.
 constexpr int kMaxPer = kMaxAcceptVocab / (kSub * kAccThreads);  // sub-blocks per thread
 
-__device__ int draw_from_masses(const double (&mv)[kMaxPer], int i0, int i1, const float* p,
-                                const float* q, int V, bool vec, double u, double* s_wave,
-                                int* s_int, double* s_dbl) {
+template <typename R>
+__device__ int draw_from_masses(const double (&mv)[kMaxPer], int i0, int i1, const R& res,
+                                double u, double* s_wave, int* s_int, double* s_dbl) {
   const int tid = threadIdx.x;
   double mine = 0.0;
 #pragma unroll
@@ -229,7 +258,7 @@ __device__ int draw_from_masses(const double (&mv)[kMaxPer], int i0, int i1, con
   __syncthreads();
   const double base = s_dbl[1];
   int lastp;
-  int tok = sub_block_search(p, q, sstar, V, vec, base, thr, s_int, &lastp);
+  int tok = sub_block_search(res, sstar, base, thr, s_int, &lastp);
   if (tok < 0) tok = lastp;
   return tok;
 }
@@ -261,7 +290,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a
   const float* qrow = j < K ? a.q + ((size_t)b * K + j) * V : nullptr;
   const bool vec = rows_aligned(prow, qrow);
   int errs = (jw & kJTokenErr) ? kErrToken : 0;
-  int tok = draw_from_masses(mv, i0, i1, prow, qrow, V, vec, ub, s_wave, s_int, s_dbl);
+  int tok = draw_from_masses(mv, i0, i1, ResidPQ{prow, qrow, V, vec}, ub, s_wave, s_int, s_dbl);
   if (tok < 0) {
     // zero residual mass: draw from the target row itself (its sub-block
     // masses recomputed into registers, thread by thread)
@@ -279,7 +308,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a
       }
       mv[k] = t;
     }
-    tok = draw_from_masses(mv, i0, i1, prow, nullptr, V, pvec, ub, s_wave, s_int, s_dbl);
+    tok = draw_from_masses(mv, i0, i1, ResidPQ{prow, nullptr, V, pvec}, ub, s_wave, s_int, s_dbl);
   }
   if (tok < 0) tok = 0;
   if (tid == 0) {
@@ -291,6 +320,203 @@ __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a
   if (tid <= K)
     a.out_tokens[(size_t)b * (K + 1) + tid] = tid < j ? dtok : (tid == j ? tok : -1);
   if (tid == 0 && errs) flag_error(a.err, errs);
+}
+
+// ------------------------------------------------------------- tree verify
+// The walk of the Tree sampler's verification (recursive rejection over
+// deterministic candidates): at node x, children c in increasing node order
+// are accepted iff u[c] * (1 - T) < p_x(token[c]), T the target mass of the
+// distinct tokens already tried at x; the first accepted child becomes the
+// next node; with none (or at a leaf) the bonus is drawn from p_x with the
+// tried tokens set to 0.
+//
+// One wave, lane n = node n (N <= 64). Every value a test may need,
+// p[parent(n)][token(n)], is gathered in one round before the walk, so the
+// walk itself is register work: the children of x are a ballot, T an
+// exclusive wave scan of their target masses, the accepted child the lowest
+// set bit of a second ballot.
+struct TreeWalk {
+  int x;          // final node
+  int depth;      // accepted nodes
+  int errs;       // kErrToken / kErrTree
+};
+
+constexpr int kJTreeTokErr = 1 << 16;
+constexpr int kJTreeErr = 1 << 17;
+
+__device__ __forceinline__ double wave_exclusive_scan(double x) {
+  return wave_inclusive_scan(x) - x;
+}
+
+// Wave 0 only. path[] (LDS) receives the accepted node ids.
+__device__ TreeWalk tree_walk(const AcceptArgs& a, int b, int* path) {
+  const int N = a.K, V = a.V;
+  const int n = threadIdx.x & 63;
+  const bool in = n < N;
+  const int par = in ? a.parent[(size_t)b * N + n] : -2;
+  const int tok = in ? a.token[(size_t)b * N + n] : -1;
+  const double un = in ? (double)a.u[(size_t)b * N + n] : 0.0;
+  const bool vpar = in && n >= 1 && par >= 0 && par < n;
+  const bool vtok = tok >= 0 && tok < V;
+  const double pv = (vpar && vtok) ? (double)a.p[((size_t)b * N + par) * V + tok] : 0.0;
+  TreeWalk w{0, 0, 0};
+  if (__builtin_amdgcn_ballot_w64(in && n >= 1 && !vpar)) w.errs |= kErrTree;
+  for (int level = 0; level < 64; ++level) {
+    const bool kid = vpar && par == w.x;
+    const uint64_t kids = __builtin_amdgcn_ballot_w64(kid);
+    if (!kids) break;
+    // a child repeating an earlier sibling's token has residual 0
+    bool dup = false;
+    for (uint64_t rest = kids; rest; rest &= rest - 1) {
+      const int k = __builtin_ctzll(rest);
+      const int tk = __shfl(tok, k, 64);
+      dup |= kid && n > k && tk == tok;
+    }
+    const double pres = (kid && vtok && !dup) ? pv : 0.0;
+    const double T = wave_exclusive_scan(pres);
+    const bool acc = kid && vtok && !dup && un * (1.0 - T) < pres;
+    const uint64_t accm = __builtin_amdgcn_ballot_w64(acc);
+    const int limit = accm ? __builtin_ctzll(accm) : 64;
+    if (__builtin_amdgcn_ballot_w64(kid && !vtok && n < limit)) w.errs |= kErrToken;
+    if (!accm) break;
+    w.x = limit;
+    if (n == 0) path[w.depth] = limit;
+    ++w.depth;
+  }
+  return w;
+}
+
+// The final node's children tokens (valid ids) into excl[]; returns the count.
+// Wave 0 only.
+__device__ int tree_excluded(const AcceptArgs& a, int b, int x, int* excl) {
+  const int N = a.K, V = a.V;
+  const int n = threadIdx.x & 63;
+  const bool in = n < N;
+  const int par = in ? a.parent[(size_t)b * N + n] : -2;
+  const int tok = in ? a.token[(size_t)b * N + n] : -1;
+  const bool ex = in && n >= 1 && par == x && par < n && tok >= 0 && tok < V;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(ex);
+  if (ex) excl[__builtin_popcountll(m & ((1ull << n) - 1))] = tok;
+  return __builtin_popcountll(m);
+}
+
+// Kernel 1, one workgroup per (request, vocabulary chunk): the walk, then
+// the residual mass of every 256-entry sub-block of the chunk.
+__global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(AcceptArgs a) {
+  const int b = blockIdx.x / a.nchunk;
+  const int c = blockIdx.x - b * a.nchunk;
+  const int N = a.K, V = a.V;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_path[64], s_excl[64], s_fexcl[64];
+  __shared__ int s_x, s_nex, s_nf;
+  if (wave == 0) {
+    const TreeWalk w = tree_walk(a, b, s_path);
+    const int nex = tree_excluded(a, b, w.x, s_excl);
+    if (lane == 0) {
+      s_x = w.x;
+      s_nex = nex;
+      if (c == 0)
+        a.jbuf[b] = w.x | (w.depth << 8) | ((w.errs & kErrToken) ? kJTreeTokErr : 0) |
+                    ((w.errs & kErrTree) ? kJTreeErr : 0);
+    }
+    if (c == 0 && lane < w.depth) a.pathbuf[(size_t)b * N + lane] = s_path[lane];
+  }
+  __syncthreads();
+  const int nsb = (V + kSub - 1) / kSub;
+  const int sb0 = c * (a.chunk / kSub);
+  const int sb1 = min(nsb, sb0 + a.chunk / kSub);
+  // the excluded tokens inside this chunk
+  if (tid == 0) {
+    int nf = 0;
+    for (int k = 0; k < s_nex; ++k)
+      if (s_excl[k] >= sb0 * kSub && s_excl[k] < sb1 * kSub) s_fexcl[nf++] = s_excl[k];
+    s_nf = nf;
+  }
+  __syncthreads();
+  const float* prow = a.p + ((size_t)b * N + s_x) * V;
+  const ResidExcl res{prow, V, rows_aligned(prow, nullptr), s_fexcl, s_nf};
+  double* out = a.partial + (size_t)b * nsb;
+#pragma unroll 2
+  for (int sb = sb0 + wave; sb < sb1; sb += kAccThreads / 64) {
+    double r[4];
+    res(sb * kSub + 4 * lane, r);
+    const double t = wave_sum((r[0] + r[1]) + (r[2] + r[3]));
+    if (lane == 0) out[sb] = t;
+  }
+}
+
+// Kernel 2, one workgroup per request: the bonus from the sub-block masses,
+// then every output.
+__global__ __launch_bounds__(kAccThreads) void accept_tree_select_kernel(AcceptArgs a) {
+  const int b = blockIdx.x;
+  const int N = a.K, V = a.V;
+  const int tid = threadIdx.x;
+  __shared__ double s_wave[4];
+  __shared__ double s_dbl[2];
+  __shared__ int s_int[2];
+  __shared__ int s_excl[64];
+  __shared__ int s_nex;
+  const int nsb = (V + kSub - 1) / kSub;
+  const int per = (nsb + kAccThreads - 1) / kAccThreads;
+  const int i0 = min(nsb, tid * per), i1 = min(nsb, i0 + per);
+  const double* m = a.partial + (size_t)b * nsb;
+  double mv[kMaxPer];
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) mv[k] = i0 + k < i1 ? m[i0 + k] : 0.0;
+  const int L = a.seq_lens[b];
+  const double ub = (double)a.u[(size_t)b * N];
+  const int jw = a.jbuf[b];
+  const int x = jw & 0xff, depth = (jw >> 8) & 0xff;
+  const int pnode = tid < depth ? a.pathbuf[(size_t)b * N + tid] : -1;
+  const int ptok = pnode >= 0 ? a.token[(size_t)b * N + pnode] : -1;
+  if (tid < 64) {
+    const int nex = tree_excluded(a, b, x, s_excl);
+    if (tid == 0) s_nex = nex;
+  }
+  __syncthreads();
+  const float* prow = a.p + ((size_t)b * N + x) * V;
+  const bool vec = rows_aligned(prow, nullptr);
+  int errs = ((jw & kJTreeTokErr) ? kErrToken : 0) | ((jw & kJTreeErr) ? kErrTree : 0);
+  int tok = draw_from_masses(mv, i0, i1, ResidExcl{prow, V, vec, s_excl, s_nex}, ub, s_wave,
+                             s_int, s_dbl);
+  if (tok < 0) {
+    // zero residual mass: draw from the node's target row itself
+    errs |= kErrZeroResidual;
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+      double t = 0.0;
+      if (i0 + k < i1) {
+        for (int e = (i0 + k) * kSub; e < min(V, (i0 + k + 1) * kSub); e += 4) {
+          double r[4];
+          resid4(prow, nullptr, e, V, vec, r);
+          t += (r[0] + r[1]) + (r[2] + r[3]);
+        }
+      }
+      mv[k] = t;
+    }
+    tok = draw_from_masses(mv, i0, i1, ResidPQ{prow, nullptr, V, vec}, ub, s_wave, s_int, s_dbl);
+  }
+  if (tok < 0) tok = 0;
+  if (tid == 0) {
+    a.accept_len[b] = depth;
+    a.commit_len[b] = depth + 1;
+    a.bonus[b] = tok;
+    a.new_seq_lens[b] = L + depth + 1;
+  }
+  if (tid < N) {
+    a.path_nodes[(size_t)b * N + tid] = pnode;
+    a.out_tokens[(size_t)b * N + tid] = tid < depth ? ptok : (tid == depth ? tok : -1);
+  }
+  if (tid == 0 && errs) flag_error(a.err, errs);
+}
+
+hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_tree_partial_kernel, dim3(a.bs * a.nchunk), dim3(kAccThreads), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_tree_select_kernel, dim3(a.bs), dim3(kAccThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------- argmax

@@ -94,7 +94,7 @@ AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
 
 struct AccPlan {
   int nchunk = 1, chunk = 0;
-  size_t off_jbuf = 0, off_partial = 0, off_ids = 0, ws_bytes = 0;
+  size_t off_jbuf = 0, off_partial = 0, off_ids = 0, off_path = 0, ws_bytes = 0;
 };
 
 // Vocabulary chunks per request: about 2048 workgroups over the batch, chunks a
@@ -114,6 +114,14 @@ AccPlan plan_accept(int bs, int K, int V, int greedy) {
   p.off_jbuf = 0;
   p.off_partial = align_up((size_t)bs * sizeof(int32_t), 256);
   p.ws_bytes = p.off_partial + (size_t)bs * ((V + 255) / 256) * sizeof(double);
+  return p;
+}
+
+// Tree verify: the same chunking, plus the accepted node ids [bs][N].
+AccPlan plan_accept_tree(int bs, int N, int V) {
+  AccPlan p = plan_accept(bs, N, V, 0);
+  p.off_path = align_up(p.ws_bytes, 256);
+  p.ws_bytes = p.off_path + (size_t)bs * N * sizeof(int32_t);
   return p;
 }
 
@@ -309,4 +317,51 @@ SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const
   a.partial = reinterpret_cast<double*>(ws + plan.off_partial);
   a.greedy_ids = nullptr;
   return hip_status(launch_accept(a, s));
+}
+
+SPEC_API size_t spec_accept_tree_workspace_bytes(int bs, int N, int V) {
+  if (bs <= 0 || N < 1 || N > 64 || V <= 0) return 0;
+  return plan_accept_tree(bs, N, V).ws_bytes;
+}
+
+SPEC_API int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const int32_t* token,
+                              const float* p, const float* u, const int32_t* seq_lens,
+                              int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                              int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
+                              void* workspace, size_t ws_bytes, int32_t* err_flags,
+                              void* stream) {
+  if (bs <= 0 || N < 1 || N > 64 || V <= 0) return SPEC_EINVAL;
+  if ((long long)bs * N > INT_MAX) return SPEC_EINVAL;
+  if (!parent || !token || !p || !u || !seq_lens || !accept_len || !commit_len || !bonus ||
+      !out_tokens || !path_nodes || !new_seq_lens)
+    return SPEC_EINVAL;
+  if (V > kMaxAcceptVocab) return SPEC_ENOTSUP;
+  const AccPlan plan = plan_accept_tree(bs, N, V);
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  char* ws = static_cast<char*>(workspace);
+  AcceptArgs a{};
+  a.p = p;
+  a.q = nullptr;
+  a.draft = nullptr;
+  a.u = u;
+  a.seq_lens = seq_lens;
+  a.accept_len = accept_len;
+  a.commit_len = commit_len;
+  a.bonus = bonus;
+  a.out_tokens = out_tokens;
+  a.new_seq_lens = new_seq_lens;
+  a.err = err_flags;
+  a.jbuf = reinterpret_cast<int32_t*>(ws + plan.off_jbuf);
+  a.partial = reinterpret_cast<double*>(ws + plan.off_partial);
+  a.greedy_ids = nullptr;
+  a.parent = parent;
+  a.token = token;
+  a.path_nodes = path_nodes;
+  a.pathbuf = reinterpret_cast<int32_t*>(ws + plan.off_path);
+  a.bs = bs;
+  a.K = N;
+  a.V = V;
+  a.nchunk = plan.nchunk;
+  a.chunk = plan.chunk;
+  return hip_status(launch_accept_tree(a, static_cast<hipStream_t>(stream)));
 }

@@ -17,6 +17,7 @@ constexpr int kErrSlot = 1;
 constexpr int kErrCapacity = 2;
 constexpr int kErrToken = 4;
 constexpr int kErrZeroResidual = 8;
+constexpr int kErrTree = 16;
 
 __device__ __forceinline__ void flag_error(int32_t* err, int bits) {
   if (err) atomicOr(err, bits);

@@ -66,6 +66,11 @@ struct AcceptArgs {
   double* partial;     // [bs][ceil(V / 256)] residual mass per 256-entry sub-block
   int32_t* jbuf;       // [bs] accept length (| token-error flag) from the first kernel
   int32_t* greedy_ids; // [bs][K+1] row argmax (greedy mode)
+  // tree verify (K = N nodes): parent, token [bs][N]; accepted node ids out
+  const int32_t* parent;
+  const int32_t* token;
+  int32_t* path_nodes;  // [bs][N] output
+  int32_t* pathbuf;     // [bs][N] accepted nodes passed between the two kernels
   int bs, K, V, nchunk, chunk;
 };
 
@@ -74,6 +79,7 @@ struct AcceptArgs {
 constexpr int kMaxAcceptVocab = 8 * 256 * 256;
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream);
 hipError_t launch_greedy_accept(const AcceptArgs& a, hipStream_t stream);
 
 }  // namespace specattn

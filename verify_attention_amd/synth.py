@@ -62,7 +62,9 @@ class RoundConfig:
 #  4 high-concurrency ragged verify (batch 256)
 #  5 I-DLM style mixed layout: 8 clean causal + 8 MASK bidirectional positions
 #  6 tree verify: the Qwen3-8B-shaped verify of 2 with a 32-node token tree
-#    (at most 16 levels) as the block, one tree per request
+#    (at most 16 levels) as the block, one tree per request; target logits
+#    N(0, 6^2), peaked enough (top-4 mass about 2/3 at this vocabulary) that
+#    top-candidate children are accepted at useful rates
 CONFIGS = {
     1: RoundConfig("tiny_f32", bs=1, hq=2, hkv=1, d=64, page=16, block=8,
                    modes=(BIDIR, CAUSAL), dtype="f32", ctx_lo=256, ctx_hi=256,
@@ -85,7 +87,7 @@ CONFIGS = {
     6: RoundConfig("tree_verify_bs32", bs=32, hq=32, hkv=8, d=128, page=16,
                    block=32, modes=(TREE,), dtype="bf16", ctx_lo=1024,
                    ctx_hi=1024, tree_depth=16, vocab=151936, k_spec=31,
-                   logit_sigma=3.0, q_noise_sigma=0.5),
+                   logit_sigma=6.0, q_noise_sigma=0.5),
 }
 
 
@@ -316,6 +318,41 @@ def make_accept_inputs(cfg: RoundConfig, seed: int, bs: int | None = None) -> Ac
             draft[b, i] = rd.choice(V, p=w / w.sum())
     u = rng_for(seed, "uniform").random((bs, K + 1), dtype=np.float32)
     return AcceptInputs(p, q, draft, u)
+
+
+@dataclasses.dataclass
+class TreeAcceptInputs:
+    parent: np.ndarray  # [bs, N] int32, parent[:, 0] = -1
+    token: np.ndarray   # [bs, N] int32 candidate token of each node (node 0 unused)
+    p: np.ndarray       # [bs, N, V] float32 target rows (row n: the token after node n)
+    u: np.ndarray       # [bs, N] float32 uniforms in [0, 1)
+
+
+def make_tree_accept_inputs(cfg: RoundConfig, seed: int, parents: np.ndarray,
+                            bs: int | None = None) -> TreeAcceptInputs:
+    """Target rows p = softmax(l), l ~ N(0, sigma^2), one per node. The
+    children of node x take the top tokens of a draft distribution q_x =
+    softmax(l_x + N(0, s^2)) (largest first, as a top-candidate tree keeps
+    them), so siblings carry distinct tokens and the first child is the
+    draft's most likely token."""
+    bs = cfg.bs if bs is None else bs
+    N, V = parents.shape[-1], cfg.vocab
+    par = np.broadcast_to(parents, (bs, N)).astype(np.int32)
+    p = np.empty((bs, N, V), np.float32)
+    token = np.zeros((bs, N), np.int32)
+    rp, rq = rng_for(seed, "plogit"), rng_for(seed, "qnoise")
+    for b in range(bs):
+        lp = rp.standard_normal((N, V)) * cfg.logit_sigma
+        p[b] = _softmax_rows64(lp)
+        for x in range(N):
+            kids = np.flatnonzero(par[b] == x)
+            if len(kids) == 0:
+                continue
+            lq = lp[x] + rq.standard_normal(V) * max(cfg.q_noise_sigma, 1e-3)
+            top = np.argsort(-lq, kind="stable")[:len(kids)]
+            token[b, kids] = top
+    u = rng_for(seed, "uniform").random((bs, N), dtype=np.float32)
+    return TreeAcceptInputs(par.copy(), token, p, u)
 
 
 def make_argmax_logits(cfg: RoundConfig, seed: int, rows: int | None = None) -> np.ndarray:
