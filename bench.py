@@ -3,6 +3,7 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
   verify workloads: spec_prepare_block (verify pass) -> block_attn -> spec_accept
   draft workload:   spec_prepare_block (draft pass)  -> block_attn -> spec_draft_argmax
+  tree workload:    block_attn_tree -> spec_accept_tree
 Inputs are resident in HBM before the timed region. Several copies of the
 per-step inputs are cycled so that every step reads its KV pages and target
 rows from HBM rather than from the 256 MB last-level cache.
@@ -68,7 +69,7 @@ def measured_traffic(workload, src_hash):
     return int(t["workloads"][workload]["traffic_bytes"])
 
 
-def attn_alg_bytes_flops(cfg, seq_lens):
+def attn_alg_bytes_flops(cfg, seq_lens, tree_masks=None):
     """Algorithmic bytes / flops of one block_attn launch: K and V of positions
     [0, L_b + B) read once per KV head, Q read and O written once; 4 * D flops
     per visible (query row, key) pair."""
@@ -79,15 +80,23 @@ def attn_alg_bytes_flops(cfg, seq_lens):
     B = cfg.block
     i = np.arange(B)
     if cfg.modes[0] == 0:
-        intra = B * B
+        intra = cfg.bs * B * B
     elif cfg.modes[0] == 1:
-        intra = int((i + 1).sum())
-    else:
+        intra = cfg.bs * int((i + 1).sum())
+    elif cfg.modes[0] == 2:
         nc = cfg.n_causal
-        intra = int(np.where(i < nc, i + 1, B).sum())
-    pairs = (seq_lens.astype(np.int64) * B).sum() + cfg.bs * intra
+        intra = cfg.bs * int(np.where(i < nc, i + 1, B).sum())
+    else:
+        intra = sum(bin(int(m)).count("1") for m in np.asarray(tree_masks).ravel())
+    pairs = (seq_lens.astype(np.int64) * B).sum() + intra
     flops = 4 * cfg.d * pairs * cfg.hq
     return int(kv + qo), int(flops)
+
+
+def tree_accept_alg_bytes(cfg):
+    """Tree accept: the final node's target row streamed once, plus one
+    gathered float per node, per request."""
+    return int(cfg.bs * (cfg.vocab + cfg.block) * 4)
 
 
 def accept_alg_bytes(cfg, accept_len):
@@ -98,10 +107,11 @@ def accept_alg_bytes(cfg, accept_len):
     return int((rows * V * 4).sum() + cfg.bs * (2 * K + 1) * 4)
 
 
-def cpu_baseline(cfg, x, acc, seconds):
+def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None):
     """The float64 reference, as it stands, on the host cores: dense attention
-    per (request, KV head) plus the sequential accept, request after request,
-    until `seconds` have elapsed (at least one request)."""
+    per (request, KV head) plus the sequential accept (or tree accept),
+    request after request, until `seconds` have elapsed (at least one
+    request)."""
     import oracle
     from threadpoolctl import threadpool_info
     q, kp, vp = x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool")
@@ -112,9 +122,12 @@ def cpu_baseline(cfg, x, acc, seconds):
         b = done % cfg.bs
         sl = slice(b, b + 1)
         oracle.block_attn_dense(q[sl], kp, vp, x.page_table[sl], x.seq_lens[sl], mode,
-                                cfg.n_causal)
+                                cfg.n_causal, tree=None if masks is None else masks[sl])
         if acc is not None:
             oracle.accept_request(acc.p[b], acc.q[b], acc.draft[b], acc.u[b], x.seq_lens[b])
+        if tacc is not None:
+            oracle.tree_accept_request(tacc.parent[b], tacc.token[b], tacc.p[b], tacc.u[b],
+                                       x.seq_lens[b])
         done += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -141,8 +154,14 @@ def main():
     dev = torch.device("cuda:0")
     cfg = synth.config(args.config)
     mode = cfg.modes[-1]
+    tree = mode == synth.TREE
     x = synth.make_attn_inputs(cfg, seed=args.seed)
-    acc = synth.make_accept_inputs(cfg, seed=args.seed) if cfg.vocab else None
+    parents = masks = tacc = acc = None
+    if tree:
+        parents, masks = synth.make_trees(cfg, args.seed)
+        tacc = synth.make_tree_accept_inputs(cfg, args.seed, parents)
+    elif cfg.vocab:
+        acc = synth.make_accept_inputs(cfg, seed=args.seed)
     logits = synth.make_argmax_logits(cfg, seed=args.seed) if cfg.argmax_vocab else None
     verified, drafts = synth.make_round_state(cfg, args.seed)
 
@@ -151,17 +170,24 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    # bytes one step streams (KV, Q, and the accept's rows or the logits):
+    # enough input copies are cycled that a copy is not re-read before about
+    # 768 MB have gone by, so no step finds its inputs in the 256 MB LLC
     step_bytes = x.k_pool.nbytes + x.v_pool.nbytes + x.q.nbytes
     if acc is not None:
-        step_bytes += acc.p.nbytes + acc.q.nbytes
+        step_bytes += 2 * cfg.bs * cfg.vocab * 4
+    if tacc is not None:
+        step_bytes += tree_accept_alg_bytes(cfg)
     if logits is not None:
         step_bytes += logits.nbytes
-    copies = args.copies or max(1, int(np.ceil(768e6 / step_bytes)))
+    copies = args.copies or max(2, int(np.ceil(768e6 / step_bytes)))
     sets = []
     for _ in range(copies):
         s = dict(q=up(x.q), k=up(x.k_pool), v=up(x.v_pool))
         if acc is not None:
             s.update(p=up(acc.p), qd=up(acc.q), u=up(acc.u), draft=up(acc.draft))
+        if tacc is not None:
+            s.update(p=up(tacc.p), u=up(tacc.u))
         if logits is not None:
             s["logits"] = up(logits)
         sets.append(s)
@@ -173,6 +199,10 @@ def main():
     ws_attn = va.workspace(va.attn_workspace_bytes(bs, B, cfg.hq, cfg.hkv, cfg.d, max_kv))
     prep_out = tuple(torch.empty((bs, B), dtype=torch.int32, device=dev) for _ in range(3))
     err = torch.zeros(1, dtype=torch.int32, device=dev)
+    if tree:
+        tmask = torch.from_numpy(masks.view(np.int64)).to(dev)
+        tpar, ttok = up(tacc.parent), up(tacc.token)
+        ws_tacc = va.workspace(va.accept_tree_workspace_bytes(bs, B, cfg.vocab))
     if acc is not None:
         ws_acc = va.workspace(va.accept_workspace_bytes(bs, cfg.k_spec, cfg.vocab))
         acc_out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
@@ -180,24 +210,35 @@ def main():
                        bonus=torch.empty(bs, dtype=torch.int32, device=dev),
                        out_tokens=torch.empty((bs, cfg.k_spec + 1), dtype=torch.int32, device=dev),
                        new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
-    else:
+    elif not tree:
         tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     # every call is checked once; the timed loop re-enqueues pre-marshalled calls
-    prep_call, _ = va.prepare_block_call(vid, seq, table, cfg.page, B, 0, x.num_pages,
-                                         None if mode == synth.BIDIR else dr, out=prep_out,
-                                         err=err)
-    attn_calls = [va.block_attn_call(mode, s["q"], s["k"], s["v"], table, seq, max_kv,
-                                     n_causal=cfg.n_causal, out=o, ws=ws_attn, err=err)[0]
-                  for s in sets]
+    # a tree round has no linear block to prepare (node positions follow the
+    # tree depths): its step is the tree attention and the tree accept
+    prep_call = None if tree else va.prepare_block_call(
+        vid, seq, table, cfg.page, B, 0, x.num_pages, None if mode == synth.BIDIR else dr,
+        out=prep_out, err=err)[0]
+    if tree:
+        attn_calls = [va.block_attn_tree_call(tmask, s["q"], s["k"], s["v"], table, seq, max_kv,
+                                              out=o, ws=ws_attn, err=err)[0] for s in sets]
+        tail_calls = [va.accept_tree_call(tpar, ttok, s["p"], s["u"], seq, ws=ws_tacc,
+                                          err=err) for s in sets]
+        acc_out = tail_calls[0][1]
+        tail_calls = [c[0] for c in tail_calls]
+    else:
+        attn_calls = [va.block_attn_call(mode, s["q"], s["k"], s["v"], table, seq, max_kv,
+                                         n_causal=cfg.n_causal, out=o, ws=ws_attn, err=err)[0]
+                      for s in sets]
     if acc is not None:
         tail_calls = [va.accept_call(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out,
                                      ws=ws_acc, err=err)[0] for s in sets]
-    else:
+    elif logits is not None:
         tail_calls = [va.draft_argmax_call(s["logits"], out=tokens)[0] for s in sets]
 
     def step(i, ev=None):
-        prep_call()
+        if prep_call is not None:
+            prep_call()
         if ev is not None:
             ev[0].record(stream)
         attn_calls[i % copies]()
@@ -230,17 +271,17 @@ def main():
 
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     tail_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    alg_bytes, alg_flops = attn_alg_bytes_flops(cfg, x.seq_lens)
+    alg_bytes, alg_flops = attn_alg_bytes_flops(cfg, x.seq_lens, masks)
     attn_s = attn_ms.mean() / 1e3
     achieved = alg_bytes / attn_s / 1e9
     mfma_peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
     tokens_per_step = bs * B
     value = tokens_per_step * args.steps / wall
     extra = {}
-    if acc is not None:
+    if acc is not None or tree:
         al = acc_out["accept_len"].cpu().numpy()
         cl = acc_out["commit_len"].cpu().numpy()
-        ab = accept_alg_bytes(cfg, al)
+        ab = tree_accept_alg_bytes(cfg) if tree else accept_alg_bytes(cfg, al)
         extra["accept"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2),
                                alg_bytes=ab, achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1),
                                mean_commit_len=float(cl.mean()))
@@ -277,7 +318,7 @@ def main():
         **extra,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, x, acc, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(cfg, x, acc, args.cpu_seconds, masks, tacc)
     print(json.dumps(line), flush=True)
 
 
