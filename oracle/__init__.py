@@ -15,6 +15,8 @@ Modules:
                prefix, residual (or bonus) sample, committed length; the greedy
                special case; argmax with the lowest index winning; the tree
                walk (recursive rejection over deterministic candidates)
+  sampling  -- temperature / top-k / top-p processing of logits rows, and the
+               accept on processed target and draft rows
 
 Parity status: every function here is pinned by CPU tests against closed
 forms, library routines, brute force or exact enumeration (see the tests
@@ -25,9 +27,12 @@ from .attention import (BIDIR, CAUSAL, MIXED, TREE, visible, block_attn_rows,
                         block_attn_dense, attn_row, unpage_kv, mask_matrix)
 from .accept import (accept_request, accept_batch, greedy_accept_request, argmax_lowest,
                      tree_accept_request, tree_children)
+from .sampling import (sampling_filter, rank_order, accept_logits_request,
+                       accept_logits_batch)
 
 __all__ = [
     "prepare_block", "BIDIR", "CAUSAL", "MIXED", "TREE", "visible", "block_attn_rows",
     "block_attn_dense", "attn_row", "unpage_kv", "mask_matrix", "accept_request", "accept_batch",
     "greedy_accept_request", "argmax_lowest", "tree_accept_request", "tree_children",
+    "sampling_filter", "rank_order", "accept_logits_request", "accept_logits_batch",
 ]

@@ -63,22 +63,30 @@ def _scan_last_uniform(call, grid=1024):
     return [(cuts[n + 1] - cuts[n], vals[n]) for n in range(len(vals))]
 
 
-def exact_distribution(p, q):
+def exact_distribution(p, q, run=None):
     """{(accept_len, out_tokens...): probability} of the reference's output
-    when d_i ~ q_i independently and every uniform ~ U[0, 1)."""
+    when d_i ~ q_i independently and every uniform ~ U[0, 1). run(d, u)
+    calls the reference under test (default: accept_request on p, q)."""
     K, V = q.shape
+    if run is None:
+        def run(d, u):
+            return oracle.accept_request(p, q, d, u, 0)
     dist = {}
     for d in np.ndindex(*([V] * K)):
         d = np.array(d)
         wd = np.prod([q[i, d[i]] for i in range(K)])
+        if wd == 0:
+            continue
         a = [min(1.0, p[i, d[i]] / q[i, d[i]]) for i in range(K)]
         # the accept threshold sits exactly at min(1, p/q)
         for i in range(K):
-            if a[i] < 1:
+            # (position i is reached with u = 0 before it unless an earlier
+            # draft has target probability 0)
+            if 0 < a[i] < 1 and all(a[s] > 0 for s in range(i)):
                 for u_i, want in ((a[i] * (1 - 1e-9), True), (a[i] * (1 + 1e-9), False)):
                     u = np.zeros(K + 1)
                     u[i] = u_i
-                    r = oracle.accept_request(p, q, d, u, 0)
+                    r = run(d, u)
                     assert (r["accept_len"] > i) == want
         for j in range(K + 1):
             w = wd
@@ -95,7 +103,7 @@ def exact_distribution(p, q):
             def call(ul, u=u):
                 uu = u.copy()
                 uu[K] = ul
-                r = oracle.accept_request(p, q, d, uu, 0)
+                r = run(d, uu)
                 return (r["accept_len"],) + tuple(r["out_tokens"])
 
             for length, out in _scan_last_uniform(call):
