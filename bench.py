@@ -4,12 +4,14 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   verify workloads: spec_prepare_block (verify pass) -> block_attn -> spec_accept
   draft workload:   spec_prepare_block (draft pass)  -> block_attn -> spec_draft_argmax
   tree workload:    block_attn_tree -> spec_accept_tree
+  logits workload:  spec_prepare_block (verify pass) -> block_attn -> spec_accept_logits
 Inputs are resident in HBM before the timed region. Several copies of the
 per-step inputs are cycled so that every step reads its KV pages and target
 rows from HBM rather than from the 256 MB last-level cache.
 
-Prints ONE JSON line: verified tokens/s (bs * B per step), the dominant
-kernel's roofline position (block_attn, algorithmic bytes over its event-timed
+Prints ONE JSON line: verified tokens/s (bs * B per step), the roofline
+position of the call that dominates the step (block_attn, or the accept /
+argmax call when it takes longer: algorithmic bytes over its event-timed
 average duration) and the float64 CPU reference timed on a bounded sample.
 """
 from __future__ import annotations
@@ -38,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="round configuration 1..5")
+    ap.add_argument("--config", type=int, default=2, help="round configuration 1..7")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="the warm-up runs at least this long (after the W steps)")
@@ -58,17 +60,19 @@ def kernel_sources_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, src_hash):
-    """HBM bytes per block_attn launch from the committed counter runs
-    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE, each scaled by a plain
-    copy of known size), or None when they were taken on other kernel sources."""
+def measured_traffic(workload, src_hash, call="block_attn"):
+    """HBM bytes per launch of `call` from the committed counter runs
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE summed over the call's
+    kernels, each scaled by a plain copy of known size), or None when they
+    were taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("kernel_src") != src_hash or workload not in t.get("workloads", {}):
+    key = workload if call == "block_attn" else f"{workload}/{call}"
+    if t.get("kernel_src") != src_hash or key not in t.get("workloads", {}):
         return None
-    return int(t["workloads"][workload]["traffic_bytes"])
+    return int(t["workloads"][key]["traffic_bytes"])
 
 
 def attn_alg_bytes_flops(cfg, seq_lens, tree_masks=None):
@@ -109,7 +113,14 @@ def accept_alg_bytes(cfg, accept_len):
     return int((rows * V * 4).sum() + cfg.bs * (2 * K + 1) * 4)
 
 
-def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None):
+def logits_accept_alg_bytes(cfg, esz=4):
+    """Logits accept: every target and draft logits row streamed once (the
+    top-k needs each row whole); the candidate re-reads, kept sets and the
+    gathered values are overhead."""
+    return int(cfg.bs * (2 * cfg.k_spec + 1) * cfg.vocab * esz)
+
+
+def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None, lacc=None):
     """The float64 reference, as it stands, on the host cores: dense attention
     per (request, KV head) plus the sequential accept (or tree accept),
     request after request, until `seconds` have elapsed (at least one
@@ -130,6 +141,11 @@ def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None):
         if tacc is not None:
             oracle.tree_accept_request(tacc.parent[b], tacc.token[b], tacc.p[b], tacc.u[b],
                                        x.seq_lens[b])
+        if lacc is not None:
+            T, k, top_p = cfg.sampling
+            oracle.accept_logits_request(lacc.target[b], lacc.draft_logits[b], lacc.draft[b],
+                                         lacc.u[b], x.seq_lens[b], float(np.float32(T)), k,
+                                         float(np.float32(top_p)))
         done += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -158,10 +174,12 @@ def main():
     mode = cfg.modes[-1]
     tree = mode == synth.TREE
     x = synth.make_attn_inputs(cfg, seed=args.seed)
-    parents = masks = tacc = acc = None
+    parents = masks = tacc = acc = lacc = None
     if tree:
         parents, masks = synth.make_trees(cfg, args.seed)
         tacc = synth.make_tree_accept_inputs(cfg, args.seed, parents)
+    elif cfg.sampling:
+        lacc = synth.make_logits_accept_inputs(cfg, args.seed)
     elif cfg.vocab:
         acc = synth.make_accept_inputs(cfg, seed=args.seed)
     logits = synth.make_argmax_logits(cfg, seed=args.seed) if cfg.argmax_vocab else None
@@ -180,6 +198,8 @@ def main():
         step_bytes += 2 * cfg.bs * cfg.vocab * 4
     if tacc is not None:
         step_bytes += tree_accept_alg_bytes(cfg)
+    if lacc is not None:
+        step_bytes += logits_accept_alg_bytes(cfg)
     if logits is not None:
         step_bytes += logits.nbytes
     copies = args.copies or max(2, int(np.ceil(768e6 / step_bytes)))
@@ -190,6 +210,9 @@ def main():
             s.update(p=up(acc.p), qd=up(acc.q), u=up(acc.u), draft=up(acc.draft))
         if tacc is not None:
             s.update(p=up(tacc.p), u=up(tacc.u))
+        if lacc is not None:
+            s.update(tl=up(lacc.target), dl=up(lacc.draft_logits), u=up(lacc.u),
+                     draft=up(lacc.draft))
         if logits is not None:
             s["logits"] = up(logits)
         sets.append(s)
@@ -205,8 +228,12 @@ def main():
         tmask = torch.from_numpy(masks.view(np.int64)).to(dev)
         tpar, ttok = up(tacc.parent), up(tacc.token)
         ws_tacc = va.workspace(va.accept_tree_workspace_bytes(bs, B, cfg.vocab))
-    if acc is not None:
-        ws_acc = va.workspace(va.accept_workspace_bytes(bs, cfg.k_spec, cfg.vocab))
+    if lacc is not None:
+        ws_acc = va.workspace(va.accept_logits_workspace_bytes(bs, cfg.k_spec, cfg.vocab,
+                                                               cfg.sampling[1]))
+    if acc is not None or lacc is not None:
+        if acc is not None:
+            ws_acc = va.workspace(va.accept_workspace_bytes(bs, cfg.k_spec, cfg.vocab))
         acc_out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
                        commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
                        bonus=torch.empty(bs, dtype=torch.int32, device=dev),
@@ -235,6 +262,10 @@ def main():
     if acc is not None:
         tail_calls = [va.accept_call(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out,
                                      ws=ws_acc, err=err)[0] for s in sets]
+    elif lacc is not None:
+        tail_calls = [va.accept_logits_call(s["tl"], s["dl"], s["draft"], s["u"], seq,
+                                            *cfg.sampling, out=acc_out, ws=ws_acc, err=err)[0]
+                      for s in sets]
     elif logits is not None:
         tail_calls = [va.draft_argmax_call(s["logits"], out=tokens)[0] for s in sets]
 
@@ -288,10 +319,15 @@ def main():
     tokens_per_step = bs * B
     value = tokens_per_step * args.steps / wall
     extra = {}
-    if acc is not None or tree:
+    if acc is not None or tree or lacc is not None:
         al = acc_out["accept_len"].cpu().numpy()
         cl = acc_out["commit_len"].cpu().numpy()
-        ab = tree_accept_alg_bytes(cfg) if tree else accept_alg_bytes(cfg, al)
+        if tree:
+            ab = tree_accept_alg_bytes(cfg)
+        elif lacc is not None:
+            ab = logits_accept_alg_bytes(cfg)
+        else:
+            ab = accept_alg_bytes(cfg, al)
         extra["accept"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2),
                                alg_bytes=ab, achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1),
                                mean_commit_len=float(cl.mean()))
@@ -300,6 +336,21 @@ def main():
         ab = logits.nbytes
         extra["draft_argmax"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2), alg_bytes=int(ab),
                                      achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1))
+    attn_rl = {"kernel": "block_attn", "bound": "hbm",
+               "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(achieved / HBM_PEAK_GBS, 4),
+               "traffic": measured_traffic(cfg.name, kernel_sources_hash()),
+               "traffic_unit": "bytes per launch",
+               "alg_bytes_per_launch": alg_bytes, "avg_us": round(attn_ms.mean() * 1e3, 2),
+               "mfma_frac": round(alg_flops / attn_s / 1e12 / mfma_peak, 4)}
+    tail_name = ("spec_accept_tree" if tree else "spec_accept_logits" if lacc is not None else
+                 "spec_accept" if acc is not None else "spec_draft_argmax")
+    tail_s = tail_ms.mean() / 1e3
+    tail_rl = {"kernel": tail_name, "bound": "hbm", "achieved": round(ab / tail_s / 1e9, 1),
+               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ab / tail_s / 1e9 / HBM_PEAK_GBS, 4),
+               "traffic": measured_traffic(cfg.name, kernel_sources_hash(), tail_name),
+               "traffic_unit": "bytes per launch", "alg_bytes_per_launch": int(ab),
+               "avg_us": round(tail_ms.mean() * 1e3, 2)}
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -313,23 +364,22 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded N(0,1) Q/K/V, softmax-of-normal target/draft rows)",
+        "data": ("synthetic (seeded N(0,1) Q/K/V, normal target logits, draft logits = target "
+                 "+ normal noise)" if lacc is not None else
+                 "synthetic (seeded N(0,1) Q/K/V, softmax-of-normal target/draft rows)"),
         "config": {"workload": cfg.name, "bs": bs, "block": B, "hq": cfg.hq, "hkv": cfg.hkv,
                    "head_dim": cfg.d, "page": cfg.page, "mode": synth.MODE_NAMES[mode],
                    "ctx": [cfg.ctx_lo, cfg.ctx_hi], "vocab": cfg.vocab or cfg.argmax_vocab,
                    "k_spec": cfg.k_spec, "input_copies": copies},
-        "roofline": {"kernel": "block_attn", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name, kernel_sources_hash()),
-                     "traffic_unit": "bytes per launch",
-                     "alg_bytes_per_launch": alg_bytes, "avg_us": round(attn_ms.mean() * 1e3, 2),
-                     "mfma_frac": round(alg_flops / attn_s / 1e12 / mfma_peak, 4)},
+        "roofline": attn_rl,
         "kernel_src": kernel_sources_hash(),
         **extra,
     }
+    if tail_rl["avg_us"] > attn_rl["avg_us"]:
+        # the call that dominates the step carries the roofline
+        line["roofline"], line["attn_roofline"] = tail_rl, attn_rl
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, x, acc, args.cpu_seconds, masks, tacc)
+        line["cpu_baseline"] = cpu_baseline(cfg, x, acc, args.cpu_seconds, masks, tacc, lacc)
     print(json.dumps(line), flush=True)
 
 

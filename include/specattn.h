@@ -291,6 +291,76 @@ int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const int32_t*
                      int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
                      void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream);
 
+/*
+ * spec_sampling_filter -- temperature / top-k / top-p processing of logits rows.
+ *
+ * Follows the evaluation protocol of "Unlocking Lossless Speedups in LLMs via
+ * Discrete Diffusion" (reproduction section: sampling with temperature, top-p
+ * and top-k) and the I-DLM verify of "From DFlash to dLLM Self-Spec (4)",
+ * section 4.3.1 (the verify consumes logits through softmax / top-k). The
+ * pages do not fix the order or the boundary rules; this library takes:
+ *   1. rank the tokens of a row by logit, largest first; equal logits (-0 and
+ *      +0 are equal) rank the lower index first; NaN logits are never kept;
+ *   2. keep the first top_k ranks;
+ *   3. e_r = exp((l_r - l_max) / temperature) in double over the kept ranks;
+ *   4. top_p < 1: keep rank r iff (sum_{s<r} e_s) / (sum_s e_s) < top_p, the
+ *      shortest rank prefix whose mass reaches top_p; top_p >= 1 keeps all;
+ *   5. prob_r = e_r / sum_{kept} e.
+ *
+ *   rows, V        logits is [rows, V] (V <= 524288), dtype SPEC_F32 / SPEC_BF16
+ *   temperature    > 0 and finite; top_k 1..64; top_p > 0 (>= 1: no top-p);
+ *                  both are used at their float32 values, widened to double
+ * Outputs: kept_ids [rows, top_k] int32 in rank order then -1, kept_probs
+ *   [rows, top_k] double (0 past the kept ones), n_kept [rows]. A row without a
+ *   finite logit among its top ranks gives n_kept = 0.
+ * Workspace: spec_sampling_filter_workspace_bytes(rows, V) bytes (one float
+ *   per 64 logits), contents irrelevant; calls sharing it must be ordered.
+ * Errors: SPEC_EINVAL (rows <= 0, V <= 0, NULL, parameters out of range),
+ *   SPEC_ENOTSUP (dtype, V > 524288), SPEC_ENOSPC.
+ */
+size_t spec_sampling_filter_workspace_bytes(int rows, int V);
+
+int spec_sampling_filter(int rows, int V, int dtype, const void* logits, float temperature,
+                         int top_k, float top_p, int32_t* kept_ids, double* kept_probs,
+                         int32_t* n_kept, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * spec_accept_logits -- speculative accept on logits under sampling parameters.
+ *
+ * The lossless rule (as spec_accept, from "Unlocking Lossless Speedups in
+ * LLMs via Discrete Diffusion" and section 4.3.1 of "From DFlash to dLLM
+ * Self-Spec (4)") applied to processed distributions: every target row and
+ * every draft row is processed as spec_sampling_filter describes, with the
+ * same parameters, and then
+ *   test i: accept iff u[b,i] * q_i(d_i) < p_i(d_i) (double; a token outside
+ *   the kept set has probability 0; an id outside [0, V) is a reject and sets
+ *   SPEC_ERR_TOKEN); j = accept_len; r = max(p_j - q_j, 0) over p_j's kept
+ *   set (p_K's kept set when j = K); bonus = smallest kept t (vocabulary
+ *   order) whose running sum of r exceeds u[b,K] * sum r; a zero residual
+ *   draws from p_j and sets SPEC_ERR_ZERO_RESIDUAL. The outputs are those of
+ *   spec_accept. The emitted tokens are distributed as the processed target.
+ *
+ *   bs, K, V            requests, draft tokens (1..63), vocabulary (<= 524288)
+ *   dtype               SPEC_F32 or SPEC_BF16 for both logits tensors
+ *   temperature, top_k, top_p   as spec_sampling_filter
+ *   target_logits [bs, K+1, V]  row i scores block token i + 1 (row K: bonus)
+ *   draft_logits  [bs, K, V]    the drafter's logits of draft token i
+ *   draft [bs, K], u [bs, K+1] float in [0, 1), seq_lens [bs]
+ * Outputs: accept_len, commit_len, bonus, new_seq_lens [bs]; out_tokens [bs, K+1].
+ * Workspace: spec_accept_logits_workspace_bytes(bs, K, V, top_k) bytes,
+ *   16-byte aligned, contents irrelevant; calls sharing it must be ordered.
+ * Errors: SPEC_EINVAL (sizes, NULL, parameters), SPEC_ENOTSUP (dtype,
+ *   V > 524288), SPEC_ENOSPC.
+ */
+size_t spec_accept_logits_workspace_bytes(int bs, int K, int V, int top_k);
+
+int spec_accept_logits(int bs, int K, int V, int dtype, float temperature, int top_k, float top_p,
+                       const void* target_logits, const void* draft_logits, const int32_t* draft,
+                       const float* u, const int32_t* seq_lens, int32_t* accept_len,
+                       int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
+                       int32_t* new_seq_lens, void* workspace, size_t ws_bytes,
+                       int32_t* err_flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -180,3 +180,55 @@ def test_binding_fails_loudly_without_gpu_tensors(lib):
     x = torch.zeros(3, dtype=torch.int32)
     with pytest.raises(b.SpecError):
         va.prepare_block(x, x, torch.zeros((3, 2), dtype=torch.int32), 16, 4, 0, 8)
+
+
+def test_sampling_filter_rejects_bad_arguments(lib):
+    def filt(**kw):
+        a = dict(rows=8, V=151936, dt=b.F32, x=FAKE, T=1.0, k=50, p=0.95, ids=FAKE, probs=FAKE,
+                 n=FAKE, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.spec_sampling_filter(a["rows"], a["V"], a["dt"], a["x"], a["T"], a["k"], a["p"],
+                                        a["ids"], a["probs"], a["n"], a["ws"], a["ws_bytes"], None)
+    assert filt(rows=0) == b.SPEC_EINVAL
+    assert filt(V=0) == b.SPEC_EINVAL
+    assert filt(x=None) == b.SPEC_EINVAL
+    assert filt(n=None) == b.SPEC_EINVAL
+    assert filt(T=0.0) == b.SPEC_EINVAL
+    assert filt(T=float("inf")) == b.SPEC_EINVAL
+    assert filt(k=0) == b.SPEC_EINVAL
+    assert filt(k=65) == b.SPEC_EINVAL
+    assert filt(p=0.0) == b.SPEC_EINVAL
+    assert filt(p=float("nan")) == b.SPEC_EINVAL
+    assert filt(dt=7) == b.SPEC_ENOTSUP
+    assert filt(V=524289) == b.SPEC_ENOTSUP
+    need = lib.spec_sampling_filter_workspace_bytes(8, 151936)
+    assert need >= 8 * 2374 * 4
+    assert filt(ws_bytes=need - 1) == b.SPEC_ENOSPC
+    assert filt(ws=None) == b.SPEC_ENOSPC
+
+
+def test_accept_logits_rejects_bad_arguments(lib):
+    def acc(**kw):
+        a = dict(bs=4, K=15, V=151936, dt=b.F32, T=1.0, k=50, p=0.95, tl=FAKE, dl=FAKE, dr=FAKE,
+                 u=FAKE, seq=FAKE, al=FAKE, cl=FAKE, bon=FAKE, out=FAKE, nsl=FAKE, ws=FAKE,
+                 ws_bytes=1 << 30, err=None)
+        a.update(kw)
+        return lib.spec_accept_logits(a["bs"], a["K"], a["V"], a["dt"], a["T"], a["k"], a["p"],
+                                      a["tl"], a["dl"], a["dr"], a["u"], a["seq"], a["al"],
+                                      a["cl"], a["bon"], a["out"], a["nsl"], a["ws"],
+                                      a["ws_bytes"], a["err"], None)
+    assert acc(bs=0) == b.SPEC_EINVAL
+    assert acc(K=0) == b.SPEC_EINVAL
+    assert acc(K=64) == b.SPEC_EINVAL
+    assert acc(dl=None) == b.SPEC_EINVAL
+    assert acc(u=None) == b.SPEC_EINVAL
+    assert acc(nsl=None) == b.SPEC_EINVAL
+    assert acc(k=65) == b.SPEC_EINVAL
+    assert acc(T=-1.0) == b.SPEC_EINVAL
+    assert acc(dt=3) == b.SPEC_ENOTSUP
+    assert acc(V=524289) == b.SPEC_ENOTSUP
+    need = lib.spec_accept_logits_workspace_bytes(4, 15, 151936, 50)
+    # tile maxima plus kept ids, probabilities and counts of 4 * 31 rows
+    assert need >= 4 * 31 * (2374 * 4 + 50 * 12 + 4)
+    assert acc(ws_bytes=need - 1) == b.SPEC_ENOSPC
+    assert lib.spec_accept_logits_workspace_bytes(4, 15, 151936, 65) == 0

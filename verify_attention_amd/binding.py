@@ -45,6 +45,12 @@ _SIGS = {
                                   _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "spec_accept": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
+    "spec_sampling_filter_workspace_bytes": (_c_size, [_c_int] * 2),
+    "spec_sampling_filter": (_c_int, [_c_int, _c_int, _c_int, _vp, _f, _c_int, _f, _vp, _vp, _vp,
+                                      _vp, _c_size, _vp]),
+    "spec_accept_logits_workspace_bytes": (_c_size, [_c_int] * 4),
+    "spec_accept_logits": (_c_int, [_c_int, _c_int, _c_int, _c_int, _f, _c_int, _f, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
 }
 
 
@@ -407,5 +413,104 @@ def accept_tree(parent, token, p, u, seq_lens, out=None, ws=None, err=None, stre
     accept_len, commit_len, bonus, out_tokens [bs, N], path_nodes [bs, N],
     new_seq_lens."""
     enqueue, out = accept_tree_call(parent, token, p, u, seq_lens, out, ws, err, stream)
+    enqueue()
+    return out
+
+
+# ------------------------------------------------------ sampling parameters
+def sampling_filter_workspace_bytes(rows, V) -> int:
+    return int(load().spec_sampling_filter_workspace_bytes(rows, V))
+
+
+def sampling_filter_call(logits, temperature, top_k, top_p, out=None, ws=None, stream=None):
+    """Checks the arguments of spec_sampling_filter once and returns (enqueue,
+    out). logits [rows, V] float32 or bfloat16; out: kept_ids [rows, top_k]
+    int32, kept_probs [rows, top_k] float64, n_kept [rows] int32."""
+    torch = _torch()
+    rows, V = logits.shape
+    _need(logits, "logits")
+    dt = _dtype_code(logits)
+    dev = logits.device
+    if out is None:
+        out = dict(kept_ids=torch.empty((rows, top_k), dtype=torch.int32, device=dev),
+                   kept_probs=torch.empty((rows, top_k), dtype=torch.float64, device=dev),
+                   n_kept=torch.empty(rows, dtype=torch.int32, device=dev))
+    _need(out["kept_ids"], "kept_ids", torch.int32, (rows, top_k))
+    _need(out["kept_probs"], "kept_probs", torch.float64, (rows, top_k))
+    _need(out["n_kept"], "n_kept", torch.int32, (rows,))
+    if ws is None:
+        ws = workspace(sampling_filter_workspace_bytes(rows, V), dev)
+    args = (rows, V, dt, _ptr(logits), float(temperature), int(top_k), float(top_p),
+            _ptr(out["kept_ids"]), _ptr(out["kept_probs"]), _ptr(out["n_kept"]), _ptr(ws),
+            ws.numel(), _stream(stream))
+    fn = load().spec_sampling_filter
+    keep = (logits, out, ws)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_sampling_filter")
+
+    return enqueue, out
+
+
+def sampling_filter(logits, temperature, top_k, top_p, out=None, ws=None, stream=None):
+    """Temperature / top-k / top-p processing of logits rows
+    (spec_sampling_filter). Returns kept_ids, kept_probs, n_kept."""
+    enqueue, out = sampling_filter_call(logits, temperature, top_k, top_p, out, ws, stream)
+    enqueue()
+    return out
+
+
+def accept_logits_workspace_bytes(bs, K, V, top_k) -> int:
+    return int(load().spec_accept_logits_workspace_bytes(bs, K, V, top_k))
+
+
+def accept_logits_call(target_logits, draft_logits, draft, u, seq_lens, temperature, top_k,
+                       top_p, out=None, ws=None, err=None, stream=None):
+    """Checks the arguments of spec_accept_logits once and returns (enqueue,
+    out). target_logits [bs, K+1, V], draft_logits [bs, K, V] (float32 or
+    bfloat16, the same dtype), draft [bs, K] int32, u [bs, K+1] float32."""
+    torch = _torch()
+    bs, K1, V = target_logits.shape
+    K = K1 - 1
+    _need(target_logits, "target_logits")
+    dt = _dtype_code(target_logits)
+    _need(draft_logits, "draft_logits", target_logits.dtype, (bs, K, V))
+    _need(draft, "draft", torch.int32, (bs, K))
+    _need(u, "u", torch.float32, (bs, K + 1))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    dev = target_logits.device
+    if out is None:
+        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((bs, K + 1), dtype=torch.int32, device=dev),
+                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = workspace(accept_logits_workspace_bytes(bs, K, V, top_k), dev)
+    args = (bs, K, V, dt, float(temperature), int(top_k), float(top_p), _ptr(target_logits),
+            _ptr(draft_logits), _ptr(draft), _ptr(u), _ptr(seq_lens), _ptr(out["accept_len"]),
+            _ptr(out["commit_len"]), _ptr(out["bonus"]), _ptr(out["out_tokens"]),
+            _ptr(out["new_seq_lens"]), _ptr(ws), ws.numel(), _ptr(err), _stream(stream))
+    fn = load().spec_accept_logits
+    keep = (target_logits, draft_logits, draft, u, seq_lens, out, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_accept_logits")
+
+    return enqueue, out
+
+
+def accept_logits(target_logits, draft_logits, draft, u, seq_lens, temperature, top_k, top_p,
+                  out=None, ws=None, err=None, stream=None):
+    """Speculative accept on logits under sampling parameters
+    (spec_accept_logits). Returns the same dict as accept()."""
+    enqueue, out = accept_logits_call(target_logits, draft_logits, draft, u, seq_lens,
+                                      temperature, top_k, top_p, out, ws, err, stream)
     enqueue()
     return out

@@ -365,3 +365,115 @@ SPEC_API int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const
   a.chunk = plan.chunk;
   return hip_status(launch_accept_tree(a, static_cast<hipStream_t>(stream)));
 }
+
+// ------------------------------------------------ sampling parameters
+namespace {
+
+struct SampPlan {
+  int ntiles = 0;
+  size_t off_tmax = 0, off_ids = 0, off_probs = 0, off_n = 0, ws_bytes = 0;
+};
+
+// Workspace of rows processed rows: tile maxima, and (for the accept) the
+// kept ids / probabilities / counts.
+SampPlan plan_sampling(long long rows, int V, int top_k, bool kept_in_ws) {
+  SampPlan p;
+  p.ntiles = (V + 63) / 64;
+  p.off_tmax = 0;
+  p.ws_bytes = align_up((size_t)rows * p.ntiles * sizeof(float), 256);
+  if (kept_in_ws) {
+    p.off_probs = p.ws_bytes;
+    p.off_ids = align_up(p.off_probs + (size_t)rows * top_k * sizeof(double), 256);
+    p.off_n = align_up(p.off_ids + (size_t)rows * top_k * sizeof(int32_t), 256);
+    p.ws_bytes = align_up(p.off_n + (size_t)rows * sizeof(int32_t), 256);
+  }
+  return p;
+}
+
+bool sampling_params_ok(float temperature, int top_k, float top_p) {
+  return std::isfinite(temperature) && temperature > 0.0f && top_k >= 1 && top_k <= kMaxTopK &&
+         top_p > 0.0f && !std::isnan(top_p);
+}
+
+}  // namespace
+
+SPEC_API size_t spec_sampling_filter_workspace_bytes(int rows, int V) {
+  if (rows <= 0 || V <= 0) return 0;
+  return plan_sampling(rows, V, 1, false).ws_bytes;
+}
+
+SPEC_API int spec_sampling_filter(int rows, int V, int dtype, const void* logits,
+                                  float temperature, int top_k, float top_p, int32_t* kept_ids,
+                                  double* kept_probs, int32_t* n_kept, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (rows <= 0 || V <= 0 || !logits || !kept_ids || !kept_probs || !n_kept) return SPEC_EINVAL;
+  if (!sampling_params_ok(temperature, top_k, top_p)) return SPEC_EINVAL;
+  if (V > kMaxSampVocab) return SPEC_ENOTSUP;
+  const SampPlan plan = plan_sampling(rows, V, top_k, false);
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  SampArgs a{};
+  a.x0 = logits;
+  a.R1 = rows;
+  a.V = V;
+  a.ntiles = plan.ntiles;
+  a.top_k = top_k;
+  a.temperature = temperature;
+  a.top_p = top_p;
+  a.tmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_tmax);
+  a.kept_ids = kept_ids;
+  a.kept_probs = kept_probs;
+  a.n_kept = n_kept;
+  return hip_status(launch_sampling_filter(a, dtype == SPEC_BF16, static_cast<hipStream_t>(stream)));
+}
+
+SPEC_API size_t spec_accept_logits_workspace_bytes(int bs, int K, int V, int top_k) {
+  if (bs <= 0 || K < 1 || K > 63 || V <= 0 || top_k < 1 || top_k > kMaxTopK) return 0;
+  return plan_sampling((long long)bs * (2 * K + 1), V, top_k, true).ws_bytes;
+}
+
+SPEC_API int spec_accept_logits(int bs, int K, int V, int dtype, float temperature, int top_k,
+                                float top_p, const void* target_logits,
+                                const void* draft_logits, const int32_t* draft, const float* u,
+                                const int32_t* seq_lens, int32_t* accept_len,
+                                int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
+                                int32_t* new_seq_lens, void* workspace, size_t ws_bytes,
+                                int32_t* err_flags, void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (bs <= 0 || K < 1 || K > 63 || V <= 0) return SPEC_EINVAL;
+  if ((long long)bs * (2 * K + 1) > INT_MAX / 64) return SPEC_EINVAL;
+  if (!target_logits || !draft_logits || !draft || !u || !seq_lens || !accept_len ||
+      !commit_len || !bonus || !out_tokens || !new_seq_lens)
+    return SPEC_EINVAL;
+  if (!sampling_params_ok(temperature, top_k, top_p)) return SPEC_EINVAL;
+  if (V > kMaxSampVocab) return SPEC_ENOTSUP;
+  const SampPlan plan = plan_sampling((long long)bs * (2 * K + 1), V, top_k, true);
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  char* ws = static_cast<char*>(workspace);
+  SampArgs a{};
+  a.x0 = target_logits;
+  a.x1 = draft_logits;
+  a.R1 = bs * (K + 1);
+  a.R2 = bs * K;
+  a.V = V;
+  a.ntiles = plan.ntiles;
+  a.top_k = top_k;
+  a.temperature = temperature;
+  a.top_p = top_p;
+  a.tmax = reinterpret_cast<float*>(ws + plan.off_tmax);
+  a.kept_ids = reinterpret_cast<int32_t*>(ws + plan.off_ids);
+  a.kept_probs = reinterpret_cast<double*>(ws + plan.off_probs);
+  a.n_kept = reinterpret_cast<int32_t*>(ws + plan.off_n);
+  a.bs = bs;
+  a.K = K;
+  a.draft = draft;
+  a.u = u;
+  a.seq_lens = seq_lens;
+  a.accept_len = accept_len;
+  a.commit_len = commit_len;
+  a.bonus = bonus;
+  a.out_tokens = out_tokens;
+  a.new_seq_lens = new_seq_lens;
+  a.err = err_flags;
+  return hip_status(launch_accept_logits(a, dtype == SPEC_BF16, static_cast<hipStream_t>(stream)));
+}

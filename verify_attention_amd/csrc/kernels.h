@@ -79,6 +79,35 @@ struct AcceptArgs {
 constexpr int kMaxAcceptVocab = 8 * 256 * 256;
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+// Sampling parameters (temperature, top-k, top-p) in front of the accept.
+constexpr int kMaxSampVocab = 524288;  // tile maxima of a row: 32 per thread of 256
+constexpr int kMaxTopK = 64;           // one wave holds a row's top list
+
+struct SampArgs {
+  const void* x0;       // rows [0, R1): [R1][V] logits (the target rows for the accept)
+  const void* x1;       // rows [R1, R1 + R2): [R2][V] (the draft rows), may be null
+  int R1, R2, V, ntiles, top_k;
+  float temperature, top_p;
+  float* tmax;          // [R1 + R2][ntiles] tile maxima (workspace)
+  int32_t* kept_ids;    // [R1 + R2][top_k] kept ids in rank order, -1 padded
+  double* kept_probs;   // [R1 + R2][top_k] their probabilities, 0 padded
+  int32_t* n_kept;      // [R1 + R2]
+  // accept (bs requests, K drafts each)
+  int bs, K;
+  const int32_t* draft;
+  const float* u;
+  const int32_t* seq_lens;
+  int32_t* accept_len;
+  int32_t* commit_len;
+  int32_t* bonus;
+  int32_t* out_tokens;
+  int32_t* new_seq_lens;
+  int32_t* err;
+};
+
+hipError_t launch_sampling_filter(const SampArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_accept_logits(const SampArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream);
 hipError_t launch_greedy_accept(const AcceptArgs& a, hipStream_t stream);
 

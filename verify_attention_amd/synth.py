@@ -53,6 +53,9 @@ class RoundConfig:
     q_noise_sigma: float = 0.0  # >0: q-logits = p-logits + N(0, s^2); 0: independent
     argmax_vocab: int = 0      # draft pass: argmax of bf16 logits over this vocab
     tree_depth: int = 0        # TREE: the block is a token tree of this many levels at most
+    # accept from logits under (temperature, top_k, top_p); () = accept from
+    # stored probability rows
+    sampling: tuple = ()
 
 
 # The five round configurations. Sizes are the workloads the pages describe:
@@ -61,6 +64,9 @@ class RoundConfig:
 #  3 block-diffusion draft pass, ragged contexts, block 32, greedy draft ids
 #  4 high-concurrency ragged verify (batch 256)
 #  5 I-DLM style mixed layout: 8 clean causal + 8 MASK bidirectional positions
+#  7 the verify of 2 with the accept taking logits under the sampling
+#    parameters of the Uno evaluation protocol (temperature 1, top-k 50,
+#    top-p 0.95): target logits N(0, 3^2), draft logits = target + N(0, 0.5^2)
 #  6 tree verify: the Qwen3-8B-shaped verify of 2 with a 32-node token tree
 #    (at most 16 levels) as the block, one tree per request; target logits
 #    N(0, 6^2), peaked enough (top-4 mass about 2/3 at this vocabulary) that
@@ -88,6 +94,10 @@ CONFIGS = {
                    block=32, modes=(TREE,), dtype="bf16", ctx_lo=1024,
                    ctx_hi=1024, tree_depth=16, vocab=151936, k_spec=31,
                    logit_sigma=6.0, q_noise_sigma=0.5),
+    7: RoundConfig("qwen3_8b_verify_bs32_logits", bs=32, hq=32, hkv=8, d=128, page=16,
+                   block=16, modes=(CAUSAL,), dtype="bf16", ctx_lo=1024,
+                   ctx_hi=1024, vocab=151936, k_spec=15, logit_sigma=3.0,
+                   q_noise_sigma=0.5, sampling=(1.0, 50, 0.95)),
 }
 
 
@@ -353,6 +363,44 @@ def make_tree_accept_inputs(cfg: RoundConfig, seed: int, parents: np.ndarray,
             token[b, kids] = top
     u = rng_for(seed, "uniform").random((bs, N), dtype=np.float32)
     return TreeAcceptInputs(par.copy(), token, p, u)
+
+
+@dataclasses.dataclass
+class LogitsAcceptInputs:
+    target: np.ndarray  # [bs, K+1, V] target logits (row i scores block token i+1)
+    draft_logits: np.ndarray  # [bs, K, V] draft logits
+    draft: np.ndarray   # [bs, K] int32 draft tokens
+    u: np.ndarray       # [bs, K+1] float32 uniforms in [0, 1)
+
+
+def make_logits_accept_inputs(cfg: RoundConfig, seed: int, bs: int | None = None,
+                              dtype: str = "f32") -> LogitsAcceptInputs:
+    """Target logits l ~ N(0, sigma^2) per row and draft logits l + N(0, s^2)
+    (float32, or bf16 bits when dtype is "bf16"). Draft token i is the token at
+    rank R of draft row i (largest logit first, lower index first on ties),
+    R ~ Geometric(0.35) - 1 capped at 39, so drafts sit among the drafter's
+    top candidates as a sampler with top-k truncation draws them. The accept
+    step's uniforms come from a separate stream."""
+    bs = cfg.bs if bs is None else bs
+    K, V = cfg.k_spec, cfg.vocab
+    tl = np.empty((bs, K + 1, V), np.float32)
+    dl = np.empty((bs, K, V), np.float32)
+    draft = np.empty((bs, K), np.int32)
+    rp, rq, rd = rng_for(seed, "plogit"), rng_for(seed, "qnoise"), rng_for(seed, "draft")
+    for b in range(bs):
+        tl[b] = rp.standard_normal((K + 1, V), dtype=np.float32) * np.float32(cfg.logit_sigma)
+        dl[b] = tl[b, :K] + rq.standard_normal((K, V), dtype=np.float32) * np.float32(
+            cfg.q_noise_sigma)
+        if dtype == "bf16":  # the drafts are ranked on the stored values
+            tl[b] = bf16_to_f32(bf16_bits(tl[b]))
+            dl[b] = bf16_to_f32(bf16_bits(dl[b]))
+        ranks = np.minimum(rd.geometric(0.35, size=K) - 1, 39)
+        for i in range(K):
+            draft[b, i] = np.argsort(-dl[b, i], kind="stable")[ranks[i]]
+    u = rng_for(seed, "uniform").random((bs, K + 1), dtype=np.float32)
+    if dtype == "bf16":
+        return LogitsAcceptInputs(bf16_bits(tl), bf16_bits(dl), draft, u)
+    return LogitsAcceptInputs(tl, dl, draft, u)
 
 
 def make_argmax_logits(cfg: RoundConfig, seed: int, rows: int | None = None) -> np.ndarray:
