@@ -381,10 +381,11 @@ SampPlan plan_sampling(long long rows, int V, int top_k, bool kept_in_ws) {
   p.ntiles = (V + 63) / 64;
   p.off_tmax = 0;
   p.ws_bytes = align_up((size_t)rows * p.ntiles * sizeof(float), 256);
-  if (kept_in_ws) {
+  if (kept_in_ws) {  // rows padded to kMaxTopK entries
+    (void)top_k;
     p.off_probs = p.ws_bytes;
-    p.off_ids = align_up(p.off_probs + (size_t)rows * top_k * sizeof(double), 256);
-    p.off_n = align_up(p.off_ids + (size_t)rows * top_k * sizeof(int32_t), 256);
+    p.off_ids = align_up(p.off_probs + (size_t)rows * kMaxTopK * sizeof(double), 256);
+    p.off_n = align_up(p.off_ids + (size_t)rows * kMaxTopK * sizeof(int32_t), 256);
     p.ws_bytes = align_up(p.off_n + (size_t)rows * sizeof(int32_t), 256);
   }
   return p;
@@ -424,6 +425,7 @@ SPEC_API int spec_sampling_filter(int rows, int V, int dtype, const void* logits
   a.kept_ids = kept_ids;
   a.kept_probs = kept_probs;
   a.n_kept = n_kept;
+  a.stride = top_k;
   return hip_status(launch_sampling_filter(a, dtype == SPEC_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -464,6 +466,7 @@ SPEC_API int spec_accept_logits(int bs, int K, int V, int dtype, float temperatu
   a.kept_ids = reinterpret_cast<int32_t*>(ws + plan.off_ids);
   a.kept_probs = reinterpret_cast<double*>(ws + plan.off_probs);
   a.n_kept = reinterpret_cast<int32_t*>(ws + plan.off_n);
+  a.stride = kMaxTopK;
   a.bs = bs;
   a.K = K;
   a.draft = draft;

@@ -88,10 +88,11 @@ struct SampArgs {
   const void* x0;       // rows [0, R1): [R1][V] logits (the target rows for the accept)
   const void* x1;       // rows [R1, R1 + R2): [R2][V] (the draft rows), may be null
   int R1, R2, V, ntiles, top_k;
+  int stride;           // kept row stride: top_k (filter outputs) or kMaxTopK (accept workspace)
   float temperature, top_p;
   float* tmax;          // [R1 + R2][ntiles] tile maxima (workspace)
-  int32_t* kept_ids;    // [R1 + R2][top_k] kept ids in rank order, -1 padded
-  double* kept_probs;   // [R1 + R2][top_k] their probabilities, 0 padded
+  int32_t* kept_ids;    // [R1 + R2][stride] kept ids in rank order, -1 padded
+  double* kept_probs;   // [R1 + R2][stride] their probabilities, 0 padded
   int32_t* n_kept;      // [R1 + R2]
   // accept (bs requests, K drafts each)
   int bs, K;

@@ -15,13 +15,14 @@
 // Three kernels:
 //   * tile_max_kernel streams every row once (the HBM-bound pass) and stores
 //     the maximum of each 64-entry tile;
-//   * row_topk_kernel, one workgroup per row: tau = the top_k-th largest of
-//     256 per-thread maxima of tile maxima is a logit that at least top_k
-//     entries reach, so every top-k entry lies in a tile whose maximum is at
-//     least tau. Only those tiles are read again; their entries >= tau are
-//     ranked exactly by counting, and one wave applies temperature and top-p
-//     and writes the kept ids and probabilities. Rows whose candidates do not
-//     fit in LDS (massive ties) take an exact slow path;
+//   * row_topk_kernel, one workgroup per row: tau, the top_k-th largest of
+//     256 per-thread maxima of tile maxima rounded down to 16 key bits, is a
+//     logit that at least top_k entries reach, so every top-k entry lies in a
+//     tile whose maximum is at least tau. Only those tiles are read again;
+//     their entries >= tau are ranked exactly by counting, and one wave
+//     applies temperature and top-p and writes the kept ids and
+//     probabilities. Rows whose candidates do not fit in LDS (massive ties)
+//     take an exact slow path;
 //   * accept_logits_kernel, one wave per request: the tests u_i q_i(d_i) <
 //     p_i(d_i) on the kept sets, the first reject, the residual max(p_j -
 //     q_j, 0) (or the bonus row) over p_j's kept set drawn in vocabulary
@@ -35,7 +36,7 @@ constexpr int kSampThreads = 256;
 constexpr int kTilesPerThread = kMaxSampVocab / kTile / kSampThreads;
 constexpr int kMaxCandTiles = 1024;             // candidate tiles held in LDS
 constexpr int kMaxSurvivors = 2048;             // candidate entries held in LDS
-constexpr int kTileIters = 8;                   // tile-max loop iterations per workgroup
+constexpr int kTileIters = 16;                  // 16-byte loads in flight per lane (tile-max pass)
 
 static_assert(kTilesPerThread * kTile * kSampThreads == kMaxSampVocab, "vocabulary cap");
 
@@ -56,6 +57,16 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 }
 __device__ __forceinline__ float key_f(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Value of lane l (wave-uniform l) without an LDS round trip.
+__device__ __forceinline__ int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+// Number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
 // Rank order: (v, i) comes before (w, j) iff v > w, or v == w and i < j.
@@ -81,22 +92,35 @@ __global__ __launch_bounds__(kSampThreads) void tile_max_kernel(SampArgs a) {
   const int tile0 = blockIdx.y * (TPI * kTileIters) + tid / LPT;
   const int sub = (tid % LPT) * E;
   float m[kTileIters];
+  if (vec) {
+    // every load is issued before the first is used; the logits are read
+    // once, so the loads carry the non-temporal hint
+    vecT v[kTileIters];
 #pragma unroll
-  for (int it = 0; it < kTileIters; ++it) {
-    const int e0 = (tile0 + it * TPI) * kTile + sub;
-    float mx = -__builtin_inff();
-    if (vec) {
-      if (e0 < V) {
-        const vecT v = *reinterpret_cast<const vecT*>(x + e0);
+    for (int it = 0; it < kTileIters; ++it) {
+      const int e0 = (tile0 + it * TPI) * kTile + sub;
+      if (e0 < V) v[it] = __builtin_nontemporal_load(reinterpret_cast<const vecT*>(x + e0));
+      else
 #pragma unroll
-        for (int k = 0; k < E; ++k) mx = fmaxf(mx, (float)v[k]);
-      }
-    } else {
+        for (int k = 0; k < E; ++k) v[it][k] = (T)(-__builtin_inff());
+    }
+#pragma unroll
+    for (int it = 0; it < kTileIters; ++it) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int k = 0; k < E; ++k) mx = fmaxf(mx, (float)v[it][k]);
+      m[it] = mx;
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kTileIters; ++it) {
+      const int e0 = (tile0 + it * TPI) * kTile + sub;
+      float mx = -__builtin_inff();
 #pragma unroll
       for (int k = 0; k < E; ++k)
         if (e0 + k < V) mx = fmaxf(mx, load_f32(x + e0 + k));
+      m[it] = mx;
     }
-    m[it] = mx;
   }
 #pragma unroll
   for (int it = 0; it < kTileIters; ++it) {
@@ -109,21 +133,67 @@ __global__ __launch_bounds__(kSampThreads) void tile_max_kernel(SampArgs a) {
 }
 
 // ------------------------------------------------------------ exact top-k
-// The k-th largest of 256 keys held 4 per lane by one wave, by deciding one
-// key bit at a time with ballots (wave-uniform result).
-__device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&key)[4], int k) {
+// Offset of this wave's items in a workgroup-wide list, from each wave's
+// (wave-uniform) count; *total = the workgroup's count.
+__device__ __forceinline__ int wave_offset(int wcnt, int* s_w, int* total) {
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s_w[wave] = wcnt;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSampThreads / 64; ++w) {
+    const int v = s_w[w];
+    base += w < wave ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return base;
+}
+
+// A threshold for the top-k search: the key of the k-th largest of the 256
+// per-thread keys with its low 16 bits cleared, found by two rounds of an
+// 8-bit digit histogram in LDS (largest digit whose suffix count reaches the
+// rank still sought). At least k keys are >= the result.
+__device__ __forceinline__ uint32_t threshold_key(uint32_t key, int k, int* s_hist, int* s_sel) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t prefix = 0;
   int krem = k;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t hi = b == 31 ? 0u : (0xffffffffu << (b + 1));
-    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool c = ((key[i] & hi) == prefix) && ((key[i] >> b) & 1u);
-      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c));
+  for (int round = 0; round < 2; ++round) {
+    const int shift = 24 - 8 * round;
+    s_hist[tid] = 0;
+    __syncthreads();
+    const bool match = round == 0 || (key >> 24) == (prefix >> 24);
+    if (match) atomicAdd(&s_hist[(key >> shift) & 255], 1);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds digits 4l .. 4l + 3; suffix sums from the top digit down
+      const int h0 = s_hist[4 * lane], h1 = s_hist[4 * lane + 1], h2 = s_hist[4 * lane + 2],
+                h3 = s_hist[4 * lane + 3];
+      int suf = h0 + h1 + h2 + h3;  // becomes the count of digits >= 4 * lane
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += y;
+      }
+      // counts of digits >= 4l + 3, 4l + 2, 4l + 1, 4l
+      const int c3 = suf - h0 - h1 - h2, c2 = c3 + h2, c1 = c2 + h1, c0 = suf;
+      const int best = c3 >= krem ? 4 * lane + 3 : c2 >= krem ? 4 * lane + 2
+                       : c1 >= krem ? 4 * lane + 1 : c0 >= krem ? 4 * lane : -1;
+      const uint64_t ok = __builtin_amdgcn_ballot_w64(best >= 0);
+      const int top = 63 - __builtin_clzll(ok);  // the lane holding the largest such digit
+      if (lane == top) {
+        const int above = best == 4 * lane + 3 ? c3 - h3 : best == 4 * lane + 2 ? c2 - h2
+                          : best == 4 * lane + 1 ? c1 - h1 : c0 - h0;
+        s_sel[0] = best;
+        s_sel[1] = above;
+      }
     }
-    if (cnt >= krem) prefix |= 1u << b;
-    else krem -= cnt;
+    __syncthreads();
+    prefix |= (uint32_t)s_sel[0] << shift;
+    krem -= s_sel[1];
+    __syncthreads();
   }
   return prefix;
 }
@@ -192,16 +262,15 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.top_k, V = a.V, ntiles = a.ntiles;
   const T* x = row_ptr<T>(a, row);
-  __shared__ uint32_t s_key[kSampThreads];
+  constexpr int kBatch = 16;  // candidate tiles loaded together per wave
+  __shared__ int s_hist[kSampThreads];
   __shared__ int s_cand[kMaxCandTiles];
   __shared__ float s_sv[kMaxSurvivors];
   __shared__ int s_si[kMaxSurvivors];
   __shared__ float s_topv[kMaxTopK];
   __shared__ int s_topi[kMaxTopK];
   __shared__ float s_rv[4];
-  __shared__ int s_ri[4];
-  __shared__ int s_ncand, s_nsurv;
-  __shared__ float s_tau;
+  __shared__ int s_ri[4], s_w[4], s_sel[2];
 
   // per-thread maximum of its tile maxima (tiles tid, tid + 256, ...)
   const float* tm = a.tmax + (size_t)row * ntiles;
@@ -213,54 +282,86 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
     tv[j] = t < ntiles ? tm[t] : -__builtin_inff();
     lmax = fmaxf(lmax, tv[j]);
   }
-  s_key[tid] = fkey(lmax);
-  if (tid == 0) {
-    s_ncand = 0;
-    s_nsurv = 0;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t key[4] = {s_key[4 * lane], s_key[4 * lane + 1], s_key[4 * lane + 2],
-                             s_key[4 * lane + 3]};
-    const uint32_t kk = kth_largest_key(key, k);
-    if (lane == 0) s_tau = key_f(kk);
-  }
-  __syncthreads();
-  const float tau = s_tau;
-  // candidate tiles: maximum >= tau
+  float tau = key_f(threshold_key(fkey(lmax), k, s_hist, s_sel));
+  if (tau != tau) tau = -__builtin_inff();  // a prefix of the -inf key decodes to NaN
+
+  // candidate tiles (maximum >= tau), compacted with ballots: per wave a
+  // running count, the wave offsets through LDS
+  int wcnt = 0;
+#pragma unroll
+  for (int j = 0; j < kTilesPerThread; ++j)
+    wcnt += __builtin_popcountll(
+        __builtin_amdgcn_ballot_w64(tid + j * kSampThreads < ntiles && tv[j] >= tau));
+  int ncand;
+  int at = wave_offset(wcnt, s_w, &ncand);
 #pragma unroll
   for (int j = 0; j < kTilesPerThread; ++j) {
     const int t = tid + j * kSampThreads;
-    if (t < ntiles && tv[j] >= tau) {
-      const int slot = atomicAdd(&s_ncand, 1);
-      if (slot < kMaxCandTiles) s_cand[slot] = t;
-    }
+    const bool take = t < ntiles && tv[j] >= tau;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+    const int slot = at + lanes_below(m);
+    if (take && slot < kMaxCandTiles) s_cand[slot] = t;
+    at += __builtin_popcountll(m);
   }
   __syncthreads();
-  const int ncand = s_ncand;
-  int ntop;
+  int nsurv = 0;
   if (ncand <= kMaxCandTiles) {
-    // entries >= tau of the candidate tiles (one wave per tile, lane = entry)
-    for (int c = wave; c < ncand; c += kSampThreads / 64) {
-      const int e = s_cand[c] * kTile + lane;
-      const float v = e < V ? load_f32(x + e) : -__builtin_inff();
-      if (e < V && v >= tau) {
-        const int slot = atomicAdd(&s_nsurv, 1);
-        if (slot < kMaxSurvivors) {
-          s_sv[slot] = v;
-          s_si[slot] = e;
-        }
+    // entries >= tau of the candidate tiles (lane = entry of a tile); every
+    // wave loads kBatch tiles at once, the survivors are compacted by a scan
+    for (int c0 = 0; c0 < ncand; c0 += kBatch * (kSampThreads / 64)) {
+      float v[kBatch];
+      int e[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const int c = c0 + wave * kBatch + t;
+        e[t] = c < ncand ? s_cand[c] * kTile + lane : V;
+        v[t] = e[t] < V ? load_f32(x + e[t]) : -__builtin_inff();
       }
+      int wc = 0;
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t)
+        wc += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e[t] < V && v[t] >= tau));
+      int tot;
+      int o = nsurv + wave_offset(wc, s_w, &tot);
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const bool take = e[t] < V && v[t] >= tau;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+        const int slot = o + lanes_below(m);
+        if (take && slot < kMaxSurvivors) {
+          s_sv[slot] = v[t];
+          s_si[slot] = e[t];
+        }
+        o += __builtin_popcountll(m);
+      }
+      nsurv += tot;
     }
     __syncthreads();
   }
-  const int nsurv = s_nsurv;
-  if (ncand <= kMaxCandTiles && nsurv <= kMaxSurvivors) {
-    // exact ranks by counting; the first k go to the top list
-    for (int s = tid; s < nsurv; s += kSampThreads) {
-      const float v = s_sv[s];
-      const int i = s_si[s];
+  int ntop;
+  if (ncand <= kMaxCandTiles && nsurv <= 64) {
+    // exact ranks by counting in one wave (lane = survivor)
+    if (wave == 0) {
+      const bool in = lane < nsurv;
+      const float v = in ? s_sv[lane] : -__builtin_inff();
+      const int i = in ? s_si[lane] : 0x7fffffff;
       int rank = 0;
+      for (int t = 0; t < nsurv; ++t)
+        rank += ranks_before(lane_f(v, t), lane_i(i, t), v, i) ? 1 : 0;
+      if (in && rank < k) {
+        s_topv[rank] = v;
+        s_topi[rank] = i;
+      }
+    }
+    ntop = min(k, nsurv);
+    __syncthreads();
+  } else if (ncand <= kMaxCandTiles && nsurv <= kMaxSurvivors) {
+    // exact ranks by counting over LDS
+    for (int s2 = tid; s2 < nsurv; s2 += kSampThreads) {
+      const float v = s_sv[s2];
+      const int i = s_si[s2];
+      int rank = 0;
+#pragma unroll 8
       for (int t = 0; t < nsurv; ++t) rank += ranks_before(s_sv[t], s_si[t], v, i) ? 1 : 0;
       if (rank < k) {
         s_topv[rank] = v;
@@ -294,61 +395,71 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ek += __shfl_xor(ek, off, 64);
   const int nkept = __builtin_popcountll(__builtin_amdgcn_ballot_w64(keep));
-  if (lane < k) {
-    a.kept_ids[(size_t)row * k + lane] = keep ? s_topi[lane] : -1;
-    a.kept_probs[(size_t)row * k + lane] = keep ? e / ek : 0.0;
+  if (lane < a.stride) {
+    a.kept_ids[(size_t)row * a.stride + lane] = keep ? s_topi[lane] : -1;
+    a.kept_probs[(size_t)row * a.stride + lane] = keep ? e / ek : 0.0;
   }
   if (lane == 0) a.n_kept[row] = nkept;
 }
 
 // ------------------------------------------------------------ accept
-// Probability of token d in kept row r (0 when d is not kept): the row's ids
-// (padded with -1) are loaded together, then one probability.
-__device__ __forceinline__ double kept_prob(const SampArgs& a, int r, int d) {
-  const int k = a.top_k;
-  const int32_t* ids = a.kept_ids + (size_t)r * k;
+// Kept rows in the accept's workspace are padded to kMaxTopK entries (ids -1,
+// probabilities 0), so a row is read whole with unguarded 16-byte loads.
+// Position of token d in kept row r, or -1.
+__device__ __forceinline__ int kept_slot(const SampArgs& a, int r, int d) {
+  const int4* ids = reinterpret_cast<const int4*>(a.kept_ids + (size_t)r * kMaxTopK);
+  int4 w[kMaxTopK / 4];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK / 4; ++s) w[s] = ids[s];
   int at = -1;
 #pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s)
-    if (s < k && ids[s] == d) at = s;
-  return at >= 0 ? a.kept_probs[(size_t)r * k + at] : 0.0;
+  for (int s = kMaxTopK / 4 - 1; s >= 0; --s) {
+    at = w[s].w == d ? 4 * s + 3 : at;
+    at = w[s].z == d ? 4 * s + 2 : at;
+    at = w[s].y == d ? 4 * s + 1 : at;
+    at = w[s].x == d ? 4 * s : at;
+  }
+  return at;
 }
 
 // One wave per request. Rows: target row i of request b is b * (K + 1) + i,
 // draft row i is R1 + b * K + i.
 __global__ __launch_bounds__(64) void accept_logits_kernel(SampArgs a) {
   const int b = blockIdx.x;
-  const int K = a.K, V = a.V, k = a.top_k;
+  const int K = a.K, V = a.V;
   const int lane = threadIdx.x;
-  __shared__ double s_r[kMaxTopK];
-  __shared__ int s_v[kMaxTopK];
+  __shared__ double s_r[kMaxTopK], s_qp[kMaxTopK];
+  __shared__ int s_v[kMaxTopK], s_qid[kMaxTopK];
   // tests: lane i looks up p_i(d_i) and q_i(d_i) in the kept sets
   bool fail = false, bad = false;
   int d = -1;
   if (lane < K) {
     d = a.draft[(size_t)b * K + lane];
+    const double ui = a.u[(size_t)b * (K + 1) + lane];
     bad = d < 0 || d >= V;
-    if (bad) {
-      fail = true;
-    } else {
-      const double pd = kept_prob(a, b * (K + 1) + lane, d);
-      const double qd = kept_prob(a, a.R1 + b * K + lane, d);
-      const double ui = a.u[(size_t)b * (K + 1) + lane];
-      fail = !(ui * qd < pd);
-    }
+    const int rp = b * (K + 1) + lane, rq = a.R1 + b * K + lane;
+    const int ap = kept_slot(a, rp, d), aq = kept_slot(a, rq, d);
+    const double pd = ap >= 0 ? a.kept_probs[(size_t)rp * kMaxTopK + ap] : 0.0;
+    const double qd = aq >= 0 ? a.kept_probs[(size_t)rq * kMaxTopK + aq] : 0.0;
+    fail = bad || !(ui * qd < pd);
   }
   const uint64_t fails = __builtin_amdgcn_ballot_w64(fail);
   const int j = fails ? __builtin_ctzll(fails) : K;
   int errs = (j < K && ((__builtin_amdgcn_ballot_w64(bad) >> j) & 1)) ? kErrToken : 0;
   // residual over p_j's kept set (lane = rank): max(p - q_j, 0), or p_K
   const int prow = b * (K + 1) + j;
-  const int np = a.n_kept[prow];
-  const bool in = lane < np;
-  const int v = in ? a.kept_ids[(size_t)prow * k + lane] : 0x7fffffff;
-  const double pv = in ? a.kept_probs[(size_t)prow * k + lane] : 0.0;
+  const int v = a.kept_ids[(size_t)prow * kMaxTopK + lane];
+  const double pv = a.kept_probs[(size_t)prow * kMaxTopK + lane];
+  const bool in = v >= 0;
+  const int np = __builtin_popcountll(__builtin_amdgcn_ballot_w64(in));
   double r = pv;
-  if (j < K && in) {
-    const double qv = kept_prob(a, a.R1 + b * K + j, v);
+  if (j < K) {
+    const size_t qrow = (size_t)(a.R1 + b * K + j) * kMaxTopK;
+    s_qid[lane] = a.kept_ids[qrow + lane];
+    s_qp[lane] = a.kept_probs[qrow + lane];
+    __syncthreads();
+    double qv = 0.0;
+    for (int s = 0; s < kMaxTopK; ++s) qv = (in && s_qid[s] == v) ? s_qp[s] : qv;
     r = pv - qv > 0.0 ? pv - qv : 0.0;
   }
   double tot = r;
@@ -360,14 +471,15 @@ __global__ __launch_bounds__(64) void accept_logits_kernel(SampArgs a) {
   }
   // vocabulary order: position of this lane's token among the kept ids
   int pos = 0;
-  for (int s = 0; s < np; ++s) pos += __shfl(v, s, 64) < v ? 1 : 0;
+  for (int s = 0; s < np; ++s) pos += lane_i(v, s) < v ? 1 : 0;
   if (in) {
     s_r[pos] = r;
     s_v[pos] = v;
   }
   __syncthreads();
-  const double rr = in ? s_r[lane] : 0.0;
-  const int vv = in ? s_v[lane] : 0;
+  const bool inv = lane < np;
+  const double rr = inv ? s_r[lane] : 0.0;
+  const int vv = inv ? s_v[lane] : 0;
   double c = rr;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -376,8 +488,8 @@ __global__ __launch_bounds__(64) void accept_logits_kernel(SampArgs a) {
   }
   const double S = __shfl(c, max(np, 1) - 1, 64);
   const double thr = (double)a.u[(size_t)b * (K + 1) + K] * S;
-  const uint64_t hit = __builtin_amdgcn_ballot_w64(in && c > thr);
-  const uint64_t mass = __builtin_amdgcn_ballot_w64(in && rr > 0.0);
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(inv && c > thr);
+  const uint64_t mass = __builtin_amdgcn_ballot_w64(inv && rr > 0.0);
   int tok;
   if (hit) tok = __shfl(vv, __builtin_ctzll(hit), 64);
   else if (mass) tok = __shfl(vv, 63 - __builtin_clzll(mass), 64);
