@@ -17,6 +17,8 @@ Modules:
                walk (recursive rejection over deterministic candidates)
   sampling  -- temperature / top-k / top-p processing of logits rows, and the
                accept on processed target and draft rows
+  commit    -- the committed prefix's K/V after an accept (the accepted tree
+               path moved to contiguous positions) and the released slots
 
 Parity status: every function here is pinned by CPU tests against closed
 forms, library routines, brute force or exact enumeration (see the tests
@@ -29,10 +31,12 @@ from .accept import (accept_request, accept_batch, greedy_accept_request, argmax
                      tree_accept_request, tree_children)
 from .sampling import (sampling_filter, rank_order, accept_logits_request,
                        accept_logits_batch)
+from .commit import commit_kv, slot_of
 
 __all__ = [
     "prepare_block", "BIDIR", "CAUSAL", "MIXED", "TREE", "visible", "block_attn_rows",
     "block_attn_dense", "attn_row", "unpage_kv", "mask_matrix", "accept_request", "accept_batch",
     "greedy_accept_request", "argmax_lowest", "tree_accept_request", "tree_children",
     "sampling_filter", "rank_order", "accept_logits_request", "accept_logits_batch",
+    "commit_kv", "slot_of",
 ]
