@@ -3,7 +3,7 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
   verify workloads: spec_prepare_block (verify pass) -> block_attn -> spec_accept
   draft workload:   spec_prepare_block (draft pass)  -> block_attn -> spec_draft_argmax
-  tree workload:    block_attn_tree -> spec_accept_tree
+  tree workload:    block_attn_tree -> spec_accept_tree -> spec_commit_kv
   logits workload:  spec_prepare_block (verify pass) -> block_attn -> spec_accept_logits
 Inputs are resident in HBM before the timed region. Several copies of the
 per-step inputs are cycled so that every step reads its KV pages and target
@@ -251,10 +251,15 @@ def main():
     if tree:
         attn_calls = [va.block_attn_tree_call(tmask, s["q"], s["k"], s["v"], table, seq, max_kv,
                                               out=o, ws=ws_attn, err=err)[0] for s in sets]
-        tail_calls = [va.accept_tree_call(tpar, ttok, s["p"], s["u"], seq, ws=ws_tacc,
-                                          err=err) for s in sets]
-        acc_out = tail_calls[0][1]
-        tail_calls = [c[0] for c in tail_calls]
+        acc_out = None
+        tail_calls = []
+        for s in sets:
+            acc_call, acc_out = va.accept_tree_call(tpar, ttok, s["p"], s["u"], seq, out=acc_out,
+                                                    ws=ws_tacc, err=err)
+            # the accepted path becomes the committed prefix of the cache
+            com_call = va.commit_kv_call(s["k"], s["v"], table, seq, acc_out["accept_len"], B,
+                                         acc_out["path_nodes"], err=err)[0]
+            tail_calls.append(lambda a=acc_call, c=com_call: (a(), c()))
     else:
         attn_calls = [va.block_attn_call(mode, s["q"], s["k"], s["v"], table, seq, max_kv,
                                          n_causal=cfg.n_causal, out=o, ws=ws_attn, err=err)[0]
@@ -323,7 +328,9 @@ def main():
         al = acc_out["accept_len"].cpu().numpy()
         cl = acc_out["commit_len"].cpu().numpy()
         if tree:
-            ab = tree_accept_alg_bytes(cfg)
+            # plus the committed rows' K and V, read once and written once
+            esz = 2 if cfg.dtype == "bf16" else 4
+            ab = tree_accept_alg_bytes(cfg) + int(al.sum()) * cfg.hkv * cfg.d * 2 * 2 * esz
         elif lacc is not None:
             ab = logits_accept_alg_bytes(cfg)
         else:
@@ -343,7 +350,7 @@ def main():
                "traffic_unit": "bytes per launch",
                "alg_bytes_per_launch": alg_bytes, "avg_us": round(attn_ms.mean() * 1e3, 2),
                "mfma_frac": round(alg_flops / attn_s / 1e12 / mfma_peak, 4)}
-    tail_name = ("spec_accept_tree" if tree else "spec_accept_logits" if lacc is not None else
+    tail_name = ("spec_accept_tree+spec_commit_kv" if tree else "spec_accept_logits" if lacc is not None else
                  "spec_accept" if acc is not None else "spec_draft_argmax")
     tail_s = tail_ms.mean() / 1e3
     tail_rl = {"kernel": tail_name, "bound": "hbm", "achieved": round(ab / tail_s / 1e9, 1),

@@ -361,6 +361,40 @@ int spec_accept_logits(int bs, int K, int V, int dtype, float temperature, int t
                        int32_t* new_seq_lens, void* workspace, size_t ws_bytes,
                        int32_t* err_flags, void* stream);
 
+/*
+ * spec_commit_kv -- the committed prefix's K/V after an accept, and the
+ * released slots of the rejected suffix.
+ *
+ * Follows "From DFlash to dLLM Self-Spec (4)", section 4.6 (after a round the
+ * runtime releases the KV of the speculative suffix that was not accepted and
+ * advances the request by its commit length) and the recursive dynamic
+ * compaction note of section 4.4.1 (the committable path is fixed inside the
+ * candidate block, then the rejected suffix is released); for trees, the
+ * Tree sampler of "Unlocking Lossless Speedups in LLMs via Discrete
+ * Diffusion". The block of request b occupies positions L .. L + B - 1
+ * (L = seq_lens[b]) with node / block row n at L + n (node 0: the root, the
+ * last committed token). With d = accept_len[b] and path p_1 .. p_d
+ * (path_nodes[b, 0 .. d-1], as spec_accept_tree returns them):
+ *   position L + k receives the K and V of position L + p_k (k = 1 .. d,
+ *   every KV head; all sources are read before any destination is written);
+ *   path_nodes == NULL is the chain p_k = k (a linear verify: nothing moves);
+ *   freed_loc[b] = slots of positions L + d + 1 .. L + B - 1, then -1.
+ * The bonus token is not written: it becomes the next round's first block
+ * token at position L + d + 1 = new_seq_lens[b].
+ *
+ *   dtype SPEC_F32 / SPEC_BF16; D 64 or 128; page_size 16 or 32; B 1..64
+ *   k_pool, v_pool, page_table as block_attn (updated in place)
+ * Data errors (flagged, the request is left unchanged): L + B past the page
+ *   table (SPEC_ERR_CAPACITY), d outside 0..B-1 or a path that is not
+ *   increasing with k + 1 <= p_k < B (SPEC_ERR_TREE), a page id out of range
+ *   (SPEC_ERR_SLOT: that row is skipped).
+ * Errors: SPEC_EINVAL (sizes, NULL), SPEC_ENOTSUP (dtype, D, page_size).
+ */
+int spec_commit_kv(int dtype, int bs, int B, int Hkv, int D, int page_size, int max_pages,
+                   int num_pages, const int32_t* seq_lens, const int32_t* accept_len,
+                   const int32_t* path_nodes, const int32_t* page_table, void* k_pool,
+                   void* v_pool, int32_t* freed_loc, int32_t* err_flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

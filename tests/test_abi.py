@@ -232,3 +232,23 @@ def test_accept_logits_rejects_bad_arguments(lib):
     assert need >= 4 * 31 * (2374 * 4 + 50 * 12 + 4)
     assert acc(ws_bytes=need - 1) == b.SPEC_ENOSPC
     assert lib.spec_accept_logits_workspace_bytes(4, 15, 151936, 65) == 0
+
+
+def test_commit_kv_rejects_bad_arguments(lib):
+    def com(**kw):
+        a = dict(dt=b.BF16, bs=4, B=32, hkv=8, D=128, P=16, mp=70, np_=300, seq=FAKE, al=FAKE,
+                 path=None, tab=FAKE, k=FAKE, v=FAKE, freed=FAKE, err=None)
+        a.update(kw)
+        return lib.spec_commit_kv(a["dt"], a["bs"], a["B"], a["hkv"], a["D"], a["P"], a["mp"],
+                                  a["np_"], a["seq"], a["al"], a["path"], a["tab"], a["k"],
+                                  a["v"], a["freed"], a["err"], None)
+    assert com(bs=0) == b.SPEC_EINVAL
+    assert com(B=0) == b.SPEC_EINVAL
+    assert com(B=65) == b.SPEC_EINVAL
+    assert com(hkv=0) == b.SPEC_EINVAL
+    assert com(seq=None) == b.SPEC_EINVAL
+    assert com(freed=None) == b.SPEC_EINVAL
+    assert com(k=None) == b.SPEC_EINVAL
+    assert com(D=96) == b.SPEC_ENOTSUP
+    assert com(P=8) == b.SPEC_ENOTSUP
+    assert com(dt=9) == b.SPEC_ENOTSUP

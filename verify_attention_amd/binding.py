@@ -45,6 +45,7 @@ _SIGS = {
                                   _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "spec_accept": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
+    "spec_commit_kv": (_c_int, [_c_int] * 8 + [_vp] * 9),
     "spec_sampling_filter_workspace_bytes": (_c_size, [_c_int] * 2),
     "spec_sampling_filter": (_c_int, [_c_int, _c_int, _c_int, _vp, _f, _c_int, _f, _vp, _vp, _vp,
                                       _vp, _c_size, _vp]),
@@ -514,3 +515,49 @@ def accept_logits(target_logits, draft_logits, draft, u, seq_lens, temperature, 
                                       temperature, top_k, top_p, out, ws, err, stream)
     enqueue()
     return out
+
+
+# ------------------------------------------------------- committed prefix
+def commit_kv_call(k_pool, v_pool, page_table, seq_lens, accept_len, block, path_nodes=None,
+                   freed=None, err=None, stream=None):
+    """Checks the arguments of spec_commit_kv once and returns (enqueue,
+    freed): k_pool / v_pool are updated in place; freed [bs, block] int32
+    receives the released slots. path_nodes [bs, block] int32 (the accepted
+    node ids of a tree verify) or None (a linear verify)."""
+    torch = _torch()
+    num_pages, hkv, P, d = k_pool.shape
+    _need(k_pool, "k_pool")
+    dt = _dtype_code(k_pool)
+    _need(v_pool, "v_pool", k_pool.dtype, (num_pages, hkv, d, P))
+    bs = seq_lens.shape[0]
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need(accept_len, "accept_len", torch.int32, (bs,))
+    _need(page_table, "page_table", torch.int32)
+    if path_nodes is not None:
+        _need(path_nodes, "path_nodes", torch.int32, (bs, block))
+    if freed is None:
+        freed = torch.empty((bs, block), dtype=torch.int32, device=k_pool.device)
+    _need(freed, "freed", torch.int32, (bs, block))
+    args = (dt, bs, block, hkv, d, P, page_table.shape[1], num_pages, _ptr(seq_lens),
+            _ptr(accept_len), _ptr(path_nodes), _ptr(page_table), _ptr(k_pool), _ptr(v_pool),
+            _ptr(freed), _ptr(err), _stream(stream))
+    fn = load().spec_commit_kv
+    keep = (k_pool, v_pool, page_table, seq_lens, accept_len, path_nodes, freed, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_commit_kv")
+
+    return enqueue, freed
+
+
+def commit_kv(k_pool, v_pool, page_table, seq_lens, accept_len, block, path_nodes=None,
+              freed=None, err=None, stream=None):
+    """Committed prefix after an accept (spec_commit_kv): moves the accepted
+    tree path's K/V in place and returns the released slots [bs, block]."""
+    enqueue, freed = commit_kv_call(k_pool, v_pool, page_table, seq_lens, accept_len, block,
+                                    path_nodes, freed, err, stream)
+    enqueue()
+    return freed

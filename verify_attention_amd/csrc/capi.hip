@@ -480,3 +480,36 @@ SPEC_API int spec_accept_logits(int bs, int K, int V, int dtype, float temperatu
   a.err = err_flags;
   return hip_status(launch_accept_logits(a, dtype == SPEC_BF16, static_cast<hipStream_t>(stream)));
 }
+
+// ------------------------------------------------ committed prefix
+SPEC_API int spec_commit_kv(int dtype, int bs, int B, int Hkv, int D, int page_size,
+                            int max_pages, int num_pages, const int32_t* seq_lens,
+                            const int32_t* accept_len, const int32_t* path_nodes,
+                            const int32_t* page_table, void* k_pool, void* v_pool,
+                            int32_t* freed_loc, int32_t* err_flags, void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (D != 64 && D != 128) return SPEC_ENOTSUP;
+  if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
+  if (bs <= 0 || B < 1 || B > 64 || Hkv <= 0 || max_pages <= 0 || num_pages <= 0)
+    return SPEC_EINVAL;
+  if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
+  if (!seq_lens || !accept_len || !page_table || !k_pool || !v_pool || !freed_loc)
+    return SPEC_EINVAL;
+  CommitArgs a{};
+  a.k = k_pool;
+  a.v = v_pool;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.accept_len = accept_len;
+  a.path = path_nodes;
+  a.freed = freed_loc;
+  a.err = err_flags;
+  a.bs = bs;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.P = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  return hip_status(launch_commit_kv(a, dtype == SPEC_BF16, static_cast<hipStream_t>(stream)));
+}

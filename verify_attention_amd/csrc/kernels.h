@@ -107,6 +107,21 @@ struct SampArgs {
   int32_t* err;
 };
 
+// Committed-prefix K/V after an accept.
+struct CommitArgs {
+  void* k;                   // k_pool [num_pages][Hkv][P][D]
+  void* v;                   // v_pool [num_pages][Hkv][D][P]
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* accept_len;
+  const int32_t* path;       // [bs][B] accepted node ids, or null (the chain)
+  int32_t* freed;            // [bs][B] released slots, -1 padded
+  int32_t* err;
+  int bs, B, Hkv, D, P, max_pages, num_pages;
+};
+
+hipError_t launch_commit_kv(const CommitArgs& a, bool bf16, hipStream_t stream);
+
 hipError_t launch_sampling_filter(const SampArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_logits(const SampArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream);
