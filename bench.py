@@ -5,6 +5,7 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   draft workload:   spec_prepare_block (draft pass)  -> block_attn -> spec_draft_argmax
   tree workload:    block_attn_tree -> spec_accept_tree -> spec_commit_kv
   logits workload:  spec_prepare_block (verify pass) -> block_attn -> spec_accept_logits
+  quadratic layout: block_attn_tree (draft groups + verify spine) -> spec_accept
 Inputs are resident in HBM before the timed region. Several copies of the
 per-step inputs are cycled so that every step reads its KV pages and target
 rows from HBM rather than from the 256 MB last-level cache.
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="round configuration 1..7")
+    ap.add_argument("--config", type=int, default=2, help="round configuration 1..8")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="the warm-up runs at least this long (after the W steps)")
@@ -93,7 +94,8 @@ def attn_alg_bytes_flops(cfg, seq_lens, tree_masks=None):
         nc = cfg.n_causal
         intra = cfg.bs * int(np.where(i < nc, i + 1, B).sum())
     else:
-        intra = sum(bin(int(m)).count("1") for m in np.asarray(tree_masks).ravel())
+        m = np.asarray(tree_masks)
+        intra = sum(bin(int(v)).count("1") for v in m.ravel()) * (cfg.bs if m.ndim == 1 else 1)
     pairs = (seq_lens.astype(np.int64) * B).sum() + intra
     flops = 4 * cfg.d * pairs * cfg.hq
     return int(kv + qo), int(flops)
@@ -135,7 +137,8 @@ def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None, lacc=None):
         b = done % cfg.bs
         sl = slice(b, b + 1)
         oracle.block_attn_dense(q[sl], kp, vp, x.page_table[sl], x.seq_lens[sl], mode,
-                                cfg.n_causal, tree=None if masks is None else masks[sl])
+                                cfg.n_causal,
+                                tree=None if masks is None else (masks if masks.ndim == 1 else masks[sl]))
         if acc is not None:
             oracle.accept_request(acc.p[b], acc.q[b], acc.draft[b], acc.u[b], x.seq_lens[b])
         if tacc is not None:
@@ -172,7 +175,8 @@ def main():
     dev = torch.device("cuda:0")
     cfg = synth.config(args.config)
     mode = cfg.modes[-1]
-    tree = mode == synth.TREE
+    quad = cfg.quad_k > 0           # quadratic layout: bitmask attention + the linear accept
+    tree = mode == synth.TREE and not quad
     x = synth.make_attn_inputs(cfg, seed=args.seed)
     parents = masks = tacc = acc = lacc = None
     if tree:
@@ -180,6 +184,9 @@ def main():
         tacc = synth.make_tree_accept_inputs(cfg, args.seed, parents)
     elif cfg.sampling:
         lacc = synth.make_logits_accept_inputs(cfg, args.seed)
+    elif quad:
+        _, masks = synth.quadratic_layout(cfg.quad_k)
+        acc = synth.make_accept_inputs(cfg, seed=args.seed)
     elif cfg.vocab:
         acc = synth.make_accept_inputs(cfg, seed=args.seed)
     logits = synth.make_argmax_logits(cfg, seed=args.seed) if cfg.argmax_vocab else None
@@ -224,8 +231,9 @@ def main():
     ws_attn = va.workspace(va.attn_workspace_bytes(bs, B, cfg.hq, cfg.hkv, cfg.d, max_kv))
     prep_out = tuple(torch.empty((bs, B), dtype=torch.int32, device=dev) for _ in range(3))
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    if tree:
+    if tree or quad:
         tmask = torch.from_numpy(masks.view(np.int64)).to(dev)
+    if tree:
         tpar, ttok = up(tacc.parent), up(tacc.token)
         ws_tacc = va.workspace(va.accept_tree_workspace_bytes(bs, B, cfg.vocab))
     if lacc is not None:
@@ -245,7 +253,7 @@ def main():
     # every call is checked once; the timed loop re-enqueues pre-marshalled calls
     # a tree round has no linear block to prepare (node positions follow the
     # tree depths): its step is the tree attention and the tree accept
-    prep_call = None if tree else va.prepare_block_call(
+    prep_call = None if (tree or quad) else va.prepare_block_call(
         vid, seq, table, cfg.page, B, 0, x.num_pages, None if mode == synth.BIDIR else dr,
         out=prep_out, err=err)[0]
     if tree:
@@ -260,6 +268,9 @@ def main():
             com_call = va.commit_kv_call(s["k"], s["v"], table, seq, acc_out["accept_len"], B,
                                          acc_out["path_nodes"], err=err)[0]
             tail_calls.append(lambda a=acc_call, c=com_call: (a(), c()))
+    elif quad:
+        attn_calls = [va.block_attn_tree_call(tmask, s["q"], s["k"], s["v"], table, seq, max_kv,
+                                              out=o, ws=ws_attn, err=err)[0] for s in sets]
     else:
         attn_calls = [va.block_attn_call(mode, s["q"], s["k"], s["v"], table, seq, max_kv,
                                          n_causal=cfg.n_causal, out=o, ws=ws_attn, err=err)[0]
@@ -377,7 +388,8 @@ def main():
         "config": {"workload": cfg.name, "bs": bs, "block": B, "hq": cfg.hq, "hkv": cfg.hkv,
                    "head_dim": cfg.d, "page": cfg.page, "mode": synth.MODE_NAMES[mode],
                    "ctx": [cfg.ctx_lo, cfg.ctx_hi], "vocab": cfg.vocab or cfg.argmax_vocab,
-                   "k_spec": cfg.k_spec, "input_copies": copies},
+                   "k_spec": cfg.k_spec, "input_copies": copies,
+                   **({"layout": f"quadratic, k = {cfg.quad_k}"} if quad else {})},
         "roofline": attn_rl,
         "kernel_src": kernel_sources_hash(),
         **extra,

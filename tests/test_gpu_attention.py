@@ -239,7 +239,31 @@ def sampled_rows(x, n, rng):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6])
+QUADS = [
+    # (name, overrides of the quadratic workload): k drafts, (k + 1)^2 rows
+    ("k4_g4_bf16", dict(bs=3, ctx_lo=60, ctx_hi=700)),
+    ("k7_g2_d64_f32", dict(bs=2, hq=4, hkv=2, d=64, block=64, quad_k=7, dtype="f32", ctx_lo=0,
+                           ctx_hi=500)),
+    ("k3_g8_p32", dict(bs=4, hq=16, hkv=2, page=32, block=16, quad_k=3, ctx_lo=1, ctx_hi=300)),
+]
+
+
+@pytest.mark.parametrize("name,over", QUADS, ids=[q[0] for q in QUADS])
+def test_quadratic_layout_all_rows(gpu_lib, name, over):
+    """The quadratic layout (draft groups after every spine token) through the
+    bitmask mode, every output row against the dense reference."""
+    cfg = synth.config(8, **over)
+    print_case("block_attn_tree quadratic", name, cfg)
+    x = synth.make_attn_inputs(cfg, seed=33)
+    _, masks = synth.quadratic_layout(cfg.quad_k)
+    o, lse = run_tree(AttnCase(x), masks)
+    ro, rl = oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                     x.page_table, x.seq_lens, oracle.TREE, 0, tree=masks)
+    assert np.max(np.abs(o - ro)) <= TOL[cfg.dtype]
+    assert np.max(np.abs(lse - rl)) <= LSE_TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 8])
 def test_full_size_sampled_rows(gpu_lib, cid):
     """Full workload shapes in the bench's launch configuration; the reference
     computes sampled rows one at a time."""
@@ -250,7 +274,10 @@ def test_full_size_sampled_rows(gpu_lib, cid):
     mode = cfg.modes[0]
     masks = None
     if mode == synth.TREE:
-        _, masks = synth.make_trees(cfg, cid)
+        if cfg.quad_k:
+            _, masks = synth.quadratic_layout(cfg.quad_k)
+        else:
+            _, masks = synth.make_trees(cfg, cid)
         o, lse = run_tree(case, masks)
     else:
         o, lse = run(case, mode)

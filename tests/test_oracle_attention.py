@@ -302,3 +302,64 @@ def test_tree_rows_and_dense_forms_agree_and_planted_bit_matters():
 def dataclasses_replace(cfg, **kw):
     import dataclasses
     return dataclasses.replace(cfg, **kw)
+
+
+# ---------------------------------------------------------- quadratic layout
+def _separate_block(x, b, rows, L):
+    """A fresh identity-paged cache of request b holding its context and then
+    the listed block rows (positions L + r of the original block) in order."""
+    cfg = x.cfg
+    P = cfg.page
+    k64, v64 = x.as_f64("k_pool"), x.as_f64("v_pool")
+    n = L + len(rows)
+    npg = (n + P - 1) // P
+    kp = np.zeros((npg, cfg.hkv, P, cfg.d))
+    vp = np.zeros((npg, cfg.hkv, cfg.d, P))
+    for t in range(n):
+        src = t if t < L else L + rows[t - L]
+        pg, off = int(x.page_table[b, src // P]), src % P
+        kp[t // P, :, t % P, :] = k64[pg, :, off, :]
+        vp[t // P, :, :, t % P] = v64[pg, :, :, off]
+    return kp, vp, np.arange(npg)[None, :]
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 7])
+def test_quadratic_layout_rows_follow_their_definition(k):
+    """Each row of the quadratic layout, run through the bitmask mode, equals
+    the attention that defines it on a separately built block: spine token i
+    is the last row of a causal block of spine tokens 0 .. i; a member of
+    group G_j is a row of a bidirectional block made of spine tokens 0 .. j
+    and the members of G_j."""
+    n = (k + 1) ** 2
+    x = tiny(bs=2, hq=4, hkv=2, d=16, page=4, block=n, ctx=(3, 9), seed=30 + k)
+    cfg = x.cfg
+    role, masks = synth.quadratic_layout(k)
+    q64 = x.as_f64("q")
+    o_q, l_q = oracle.block_attn_rows(q64, x.as_f64("k_pool"), x.as_f64("v_pool"), x.page_table,
+                                      x.seq_lens, oracle.TREE, 0, tree=masks)
+    for b in range(cfg.bs):
+        L = int(x.seq_lens[b])
+        for pos, (kind, j, m) in enumerate(role):
+            spine = [t * (k + 1) for t in range(j + 1)]
+            if kind == "spine":
+                rows, mode, at = spine, CAUSAL, len(spine) - 1
+            else:
+                group = [j * (k + 1) + 1 + t for t in range(k)]
+                rows, mode, at = spine + group, BIDIR, len(spine) + m
+            kp, vp, tab = _separate_block(x, b, rows, L)
+            qp = np.zeros((1, len(rows), cfg.hq, cfg.d))
+            qp[0, at] = q64[b, pos]
+            o_c, l_c = oracle.block_attn_rows(qp, kp, vp, tab, np.array([L]), mode, 0,
+                                              rows=[(0, at, h) for h in range(cfg.hq)])
+            assert np.max(np.abs(o_c[0, at] - o_q[b, pos])) < 1e-12, (b, pos)
+            assert np.max(np.abs(l_c[0, at] - l_q[b, pos])) < 1e-12, (b, pos)
+
+
+def test_quadratic_layout_shape_and_limits():
+    role, masks = synth.quadratic_layout(3)
+    assert len(role) == 16 and role[0] == ("spine", 0, 0) and role[4] == ("spine", 1, 0)
+    assert int(masks[0]) == 1 and int(masks[8]) == 1 | 16 | 256
+    # group G_1 (positions 5, 6, 7) sees spine 0, 4 and itself
+    assert int(masks[6]) == 1 | 16 | (7 << 5)
+    with pytest.raises(ValueError):
+        synth.quadratic_layout(8)

@@ -56,6 +56,7 @@ class RoundConfig:
     # accept from logits under (temperature, top_k, top_p); () = accept from
     # stored probability rows
     sampling: tuple = ()
+    quad_k: int = 0            # >0: the block is the quadratic layout of quad_k drafts
 
 
 # The five round configurations. Sizes are the workloads the pages describe:
@@ -67,6 +68,9 @@ class RoundConfig:
 #  7 the verify of 2 with the accept taking logits under the sampling
 #    parameters of the Uno evaluation protocol (temperature 1, top-k 50,
 #    top-p 0.95): target logits N(0, 3^2), draft logits = target + N(0, 0.5^2)
+#  8 quadratic layout: the verify of 2 with k = 4 drafts and a group of k
+#    MASK tokens after the root and after every draft (25 positions), draft
+#    and verify in one forward; the accept checks the k drafts
 #  6 tree verify: the Qwen3-8B-shaped verify of 2 with a 32-node token tree
 #    (at most 16 levels) as the block, one tree per request; target logits
 #    N(0, 6^2), peaked enough (top-4 mass about 2/3 at this vocabulary) that
@@ -94,6 +98,9 @@ CONFIGS = {
                    block=32, modes=(TREE,), dtype="bf16", ctx_lo=1024,
                    ctx_hi=1024, tree_depth=16, vocab=151936, k_spec=31,
                    logit_sigma=6.0, q_noise_sigma=0.5),
+    8: RoundConfig("quadratic_verify_bs32", bs=32, hq=32, hkv=8, d=128, page=16,
+                   block=25, modes=(TREE,), dtype="bf16", ctx_lo=1024, ctx_hi=1024,
+                   vocab=151936, k_spec=4, logit_sigma=3.0, q_noise_sigma=0.5, quad_k=4),
     7: RoundConfig("qwen3_8b_verify_bs32_logits", bs=32, hq=32, hkv=8, d=128, page=16,
                    block=16, modes=(CAUSAL,), dtype="bf16", ctx_lo=1024,
                    ctx_hi=1024, vocab=151936, k_spec=15, logit_sigma=3.0,
@@ -271,6 +278,31 @@ def tree_row_masks(parent: np.ndarray) -> np.ndarray:
         if parent[n] >= 0:
             m[n] |= m[parent[n]]
     return m
+
+
+def quadratic_layout(k: int):
+    """The quadratic layout of k drafts as block rows: the spine (the root,
+    then drafts s_1 .. s_k) at positions i * (k + 1), and after spine token j
+    a group G_j of k MASK positions j * (k + 1) + 1 .. j * (k + 1) + k, which
+    proposes the continuation if exactly s_1 .. s_j are accepted. Returns
+    (role [n] as (kind, j, m) tuples, row masks [n] uint64) with n = (k + 1)^2:
+    spine token i sees spine tokens 0 .. i (causal); a member of G_j sees spine
+    tokens 0 .. j and every member of G_j (bidirectional inside the group)."""
+    n = (k + 1) * (k + 1)
+    if n > 64:
+        raise ValueError("the layout needs (k + 1)^2 <= 64 positions")
+    role, masks = [], np.zeros(n, dtype=np.uint64)
+    for pos in range(n):
+        j, m = divmod(pos, k + 1)
+        spine = sum(1 << (t * (k + 1)) for t in range(j + 1))
+        if m == 0:
+            role.append(("spine", j, 0))
+            masks[pos] = np.uint64(spine)
+        else:
+            group = sum(1 << (j * (k + 1) + 1 + t) for t in range(k))
+            role.append(("mask", j, m - 1))
+            masks[pos] = np.uint64(spine | group)
+    return role, masks
 
 
 def make_trees(cfg: RoundConfig, seed: int, per_request=True):
