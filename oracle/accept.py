@@ -46,9 +46,13 @@ TIE_EPS = 1e-6
 
 
 def argmax_lowest(x):
-    """Index of the maximum; the lowest index wins among equal maxima."""
+    """Index of the maximum; the lowest index wins among equal maxima; NaN
+    never wins (a row without a non-NaN entry gives 0)."""
     x = np.asarray(x)
-    m = x.max()
+    ok = ~np.isnan(x)
+    if not ok.any():
+        return 0
+    m = x[ok].max()
     return int(np.flatnonzero(x == m)[0])
 
 

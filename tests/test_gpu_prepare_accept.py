@@ -82,6 +82,33 @@ def test_argmax_with_planted_ties(gpu_lib):
         assert np.array_equal(got, ref), dt
 
 
+def test_argmax_aligned_rows_nan_inf_and_vector_ties(gpu_lib):
+    # aligned rows take the vector path: ties inside one 16-byte vector and
+    # across threads, rows of -inf and NaN (NaN never wins)
+    print_case("argmax aligned edge rows")
+    rng = np.random.default_rng(1)
+    rows, V = 12, 8192
+    x = rng.normal(0, 3, size=(rows, V)).astype(np.float32)
+    x[0, [9, 11]] = 50.0                 # same float4 / bf16x8 vector
+    x[1, [8, 8 + 4096]] = 50.0           # different threads
+    x[2, :] = -np.inf
+    x[3, :] = -np.inf
+    x[3, 0] = np.nan                     # NaN, then -inf everywhere
+    x[4, ::3] = np.nan
+    x[5, :] = np.nan
+    x[5, 7000] = -1.0
+    x[6, :] = 2.0                        # all equal
+    x[7, V - 1] = 99.0                   # the very last entry
+    ref = np.array([oracle.argmax_lowest(r) for r in x])
+    for dt in ("f32", "bf16"):
+        t = to_dev(synth.bf16_bits(x)) if dt == "bf16" else to_dev(x)
+        xv = synth.bf16_to_f32(synth.bf16_bits(x)) if dt == "bf16" else x
+        want = np.array([oracle.argmax_lowest(r) for r in xv])
+        got = va.draft_argmax(t).cpu().numpy()
+        assert np.array_equal(got, want), (dt, got, want)
+    assert ref[0] == 9 and ref[1] == 8 and ref[2] == 0 and ref[3] == 1 and ref[5] == 7000
+
+
 def test_argmax_draft_pass_full_size(gpu_lib):
     cfg = synth.config(3)
     print_case("argmax full", cfg.name)

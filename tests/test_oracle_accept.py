@@ -254,6 +254,16 @@ def test_argmax_lowest_index_matches_numpy():
     x = np.zeros(10)
     x[[3, 7]] = 1
     assert oracle.argmax_lowest(x) == 3
+    # NaN never wins: numpy's nanargmax (first maximum ignoring NaN)
+    for _ in range(200):
+        x = rng.integers(-5, 5, size=rng.integers(2, 64)).astype(np.float32)
+        x[rng.random(len(x)) < 0.3] = np.nan
+        x[rng.integers(len(x))] = -np.inf
+        if np.isnan(x).all():
+            continue
+        assert oracle.argmax_lowest(x) == int(np.nanargmax(x))
+    assert oracle.argmax_lowest(np.array([np.nan, -np.inf, -np.inf])) == 1
+    assert oracle.argmax_lowest(np.full(4, np.nan)) == 0
 
 
 # ------------------------------------------------------------------ tree walk

@@ -520,7 +520,6 @@ hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream) {
 }
 
 // ----------------------------------------------------------------- argmax
-// One workgroup per row; lowest index wins among equal maxima.
 __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) {
     bv = v;
@@ -531,34 +530,55 @@ __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
 template <typename T>
 __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 
+// One workgroup per row; lowest index wins among equal maxima, NaN never
+// wins. Aligned rows: every thread streams its 16-byte vectors (16 of them in
+// flight, non-temporal: the logits are read once) keeping only the running
+// maximum and the vector that first reached it; the winning vector is read
+// again to locate the lowest index holding the value. Then (value, index)
+// reductions over the wave and the workgroup.
 template <typename T>
 __global__ __launch_bounds__(kAccThreads) void argmax_rows_kernel(const T* x, int V, int32_t* out) {
   const T* row = x + (size_t)blockIdx.x * V;
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
   constexpr int kVec = 16 / sizeof(T);
+  constexpr int kIn = 16;
   typedef T vecT __attribute__((ext_vector_type(kVec)));
   int t = 0;
   if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {
     const int nv = V / kVec;
     const vecT* rv = reinterpret_cast<const vecT*>(row);
+    int bvec = -1;  // first vector of this thread whose maximum reached bv
     int e = threadIdx.x;
-    // four independent 16-byte loads in flight per thread
-    for (; e + 3 * kAccThreads < nv; e += 4 * kAccThreads) {
-      vecT v0 = rv[e], v1 = rv[e + kAccThreads], v2 = rv[e + 2 * kAccThreads], v3 = rv[e + 3 * kAccThreads];
+    for (; e + (kIn - 1) * kAccThreads < nv; e += kIn * kAccThreads) {
+      vecT v[kIn];
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) better(bv, bi, to_f32(v0[k]), e * kVec + k);
+      for (int k = 0; k < kIn; ++k) v[k] = __builtin_nontemporal_load(rv + e + k * kAccThreads);
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) better(bv, bi, to_f32(v1[k]), (e + kAccThreads) * kVec + k);
+      for (int k = 0; k < kIn; ++k) {
+        float m = to_f32(v[k][0]);
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) better(bv, bi, to_f32(v2[k]), (e + 2 * kAccThreads) * kVec + k);
-#pragma unroll
-      for (int k = 0; k < kVec; ++k) better(bv, bi, to_f32(v3[k]), (e + 3 * kAccThreads) * kVec + k);
+        for (int j = 1; j < kVec; ++j) m = fmaxf(m, to_f32(v[k][j]));
+        // later vectors hold larger indices: only a larger value wins (the
+        // first vector whose maximum is -inf counts when nothing larger was seen)
+        const bool up = m > bv || (bvec < 0 && m == bv);
+        bv = up ? m : bv;
+        bvec = up ? e + k * kAccThreads : bvec;
+      }
     }
     for (; e < nv; e += kAccThreads) {
-      vecT v0 = rv[e];
+      const vecT v = rv[e];
+      float m = to_f32(v[0]);
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) better(bv, bi, to_f32(v0[k]), e * kVec + k);
+      for (int j = 1; j < kVec; ++j) m = fmaxf(m, to_f32(v[j]));
+      const bool up = m > bv || (bvec < 0 && m == bv);
+      bv = up ? m : bv;
+      bvec = up ? e : bvec;
+    }
+    if (bvec >= 0) {
+      const vecT v = rv[bvec];
+#pragma unroll
+      for (int j = kVec - 1; j >= 0; --j) bi = to_f32(v[j]) == bv ? bvec * kVec + j : bi;
     }
     t = nv * kVec;
   }
