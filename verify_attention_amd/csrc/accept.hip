@@ -26,21 +26,9 @@ constexpr int kJTokenErr = 1 << 16;  // jbuf flag: the first reject was an inval
 constexpr int kSub = 256;  // vocabulary entries per sub-block (one wave, 4 per lane)
 
 // ------------------------------------------------------------ reductions
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
+__device__ __forceinline__ double wave_sum(double x) { return wave_sum_f64(x); }
 
-__device__ __forceinline__ double wave_inclusive_scan(double x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
+__device__ __forceinline__ double wave_inclusive_scan(double x) { return wave_scan_f64(x); }
 
 // Inclusive prefix sum of one double per thread over a 256-thread block, in a
 // fixed order (wave scans, then the wave totals through LDS).

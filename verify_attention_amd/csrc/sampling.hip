@@ -125,8 +125,7 @@ __global__ __launch_bounds__(kSampThreads) void tile_max_kernel(SampArgs a) {
 #pragma unroll
   for (int it = 0; it < kTileIters; ++it) {
     float mx = m[it];
-#pragma unroll
-    for (int off = LPT / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    mx = LPT == 16 ? row_max(mx) : half_row_max(mx);  // the tile's lanes
     const int tile = tile0 + it * TPI;
     if (tid % LPT == 0 && tile < a.ntiles) a.tmax[(size_t)row * a.ntiles + tile] = mx;
   }
@@ -380,20 +379,14 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   const double e = in ? exp(((double)s_topv[lane] - v0) / (double)a.temperature) : 0.0;
   bool keep = in;
   if (a.top_p < 1.0f) {
-    double incl = e;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
+    const double incl = wave_scan_f64(e);
     const double zk = __shfl(incl, 63, 64);
     const double up1 = __shfl_up(incl, 1, 64);
     const double before = lane == 0 ? 0.0 : up1;  // mass of the ranks before this one
     keep = in && before / zk < (double)a.top_p;
   }
   double ek = keep ? e : 0.0;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ek += __shfl_xor(ek, off, 64);
+  ek = wave_sum_f64(ek);
   const int nkept = __builtin_popcountll(__builtin_amdgcn_ballot_w64(keep));
   if (lane < a.stride) {
     a.kept_ids[(size_t)row * a.stride + lane] = keep ? s_topi[lane] : -1;
@@ -463,8 +456,7 @@ __global__ __launch_bounds__(64) void accept_logits_kernel(SampArgs a) {
     r = pv - qv > 0.0 ? pv - qv : 0.0;
   }
   double tot = r;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+  tot = wave_sum_f64(tot);
   if (!(tot > 0.0)) {
     errs |= kErrZeroResidual;
     r = pv;
@@ -480,12 +472,7 @@ __global__ __launch_bounds__(64) void accept_logits_kernel(SampArgs a) {
   const bool inv = lane < np;
   const double rr = inv ? s_r[lane] : 0.0;
   const int vv = inv ? s_v[lane] : 0;
-  double c = rr;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(c, off, 64);
-    if (lane >= off) c += y;
-  }
+  const double c = wave_scan_f64(rr);
   const double S = __shfl(c, max(np, 1) - 1, 64);
   const double thr = (double)a.u[(size_t)b * (K + 1) + K] * S;
   const uint64_t hit = __builtin_amdgcn_ballot_w64(inv && c > thr);
