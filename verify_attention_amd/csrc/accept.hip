@@ -230,8 +230,14 @@ __device__ int draw_from_masses(const double (&mv)[kMaxPer], int i0, int i1, con
     run += x;
     if (x > 0.0) lastm = i0 + k;
   }
-  if (hit >= 0) atomicMin(&s_int[0], hit);
-  if (lastm >= 0) atomicMax(&s_int[1], lastm);
+  // one LDS atomic per wave (same-address atomics serialise lane by lane):
+  // sub-blocks ascend with the thread index, so the lowest lane with a hit
+  // holds the wave's first hit and the highest lane with mass its last one
+  const int lane = tid & 63;
+  const uint64_t hm = __builtin_amdgcn_ballot_w64(hit >= 0);
+  const uint64_t lm = __builtin_amdgcn_ballot_w64(lastm >= 0);
+  if (hm && lane == __builtin_ctzll(hm)) atomicMin(&s_int[0], hit);
+  if (lm && lane == 63 - __builtin_clzll(lm)) atomicMax(&s_int[1], lastm);
   __syncthreads();
   const int first_hit = s_int[0];
   const int sstar = first_hit != 0x7fffffff ? first_hit : s_int[1];

@@ -471,10 +471,12 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const floatx4 s0 = st.s[0][t], s1 = st.s[1][t];
-    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    // scores are finite or -inf (masked) here: the NaN-propagating maximum
+    // is exact and needs no operand quieting
+    float mx = vmax(vmax(vmax(s0[0], s0[1]), vmax(s0[2], s0[3])),
+                    vmax(vmax(s1[0], s1[1]), vmax(s1[2], s1[3])));
     mx = group_max4(mx) * c2;
-    m_new[t] = fmaxf(ws.m_run[t], mx);
+    m_new[t] = vmax(ws.m_run[t], mx);
     need_any |= m_new[t] > ws.m_run[t] + kRescale;
   }
   if (__builtin_amdgcn_ballot_w64(need_any)) {
@@ -647,23 +649,30 @@ __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const Att
     // in registers across the barrier), then runs the front half of its new
     // one. The two waves of a SIMD thus work on different halves at once:
     // one reads LDS and issues S MFMAs while the other runs the softmax.
+    // Set 0 issues its share of the refill right after the barrier, set 1
+    // only after its back half: the per-CU queue of vector-memory requests
+    // then never holds both waves of a SIMD at once, so one of them always
+    // has compute to issue while the other's loads wait for queue space.
     StageRegs<T, D, MT> st;
     bool pending = false;
     for (int u = 0; u < npairs; ++u) {
       wait_stages<SS::PW>(max(0, min(NSP - 2, mine - 1 - u)));
       asm volatile("s_barrier" ::: "memory");
-      if (u + NSP - 1 < npairs) issue(u + NSP - 1, po_next);
-      po_next = offsets(u + NSP);
-      if (!has_rows) continue;
-      if (pending) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
-      pending = false;
-      const int t = 2 * u + set;
-      if (t < ns) {
-        const unsigned so = (u % NSP) * SS::PAIR;
-        stage_front<T, D, MT>(st, ws, c.k_lane + so, c.v_lane + so, (w0 + t) * kStep);
-        if (set == 0) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
-        else pending = true;
+      const bool more = u + NSP - 1 < npairs;
+      if (more && (set == 0 || !has_rows)) issue(u + NSP - 1, po_next);
+      if (has_rows) {
+        if (pending) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
+        pending = false;
+        if (more && set == 1) issue(u + NSP - 1, po_next);
+        const int t = 2 * u + set;
+        if (t < ns) {
+          const unsigned so = (u % NSP) * SS::PAIR;
+          stage_front<T, D, MT>(st, ws, c.k_lane + so, c.v_lane + so, (w0 + t) * kStep);
+          if (set == 0) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
+          else pending = true;
+        }
       }
+      po_next = offsets(u + NSP);
     }
     if (pending) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
   }

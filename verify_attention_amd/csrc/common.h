@@ -28,13 +28,18 @@ __device__ __forceinline__ void flag_error(int32_t* err, int bits) {
 // the same register as both operands) return the pair {x[l], x[l^16]} (resp.
 // l^32) in some order, so max / sum of the pair is the same on both partners
 // and no LDS round trip is needed.
+// IEEE 754-2019 maximum (NaN propagates): v_maximum3_f32 on gfx950, with no
+// quieting of its operands first, where fmaxf (NaN-ignoring) costs an extra
+// v_max_f32 x, x, x per operand that the compiler cannot prove canonical.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float pair16_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair16_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
