@@ -127,7 +127,9 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
  *   n_causal          MIXED: clean rows per request (0..B) when
  *   n_causal_per_req  is NULL, else per-request counts [bs] (device)
  *   dtype             SPEC_BF16 (q, pools, o in bf16) or SPEC_F32
- *   bs, B, Hq, Hkv    Hq % Hkv == 0; g = Hq / Hkv; g * B <= 128
+ *   bs, B, Hq, Hkv    Hq % Hkv == 0; g = Hq / Hkv; g * B <= 2048 (a KV
+ *                     head's g * B query rows beyond 128 run as row groups
+ *                     of at most 128 rows, each streaming the head's keys)
  *   D                 head dim: 64 or 128
  *   page_size         16 or 32
  *   max_pages, num_pages   page-table columns, pages in the pool
@@ -142,7 +144,7 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
  *   16-byte aligned, contents irrelevant. It holds per-split partial outputs
  *   between the attention kernel and the merge kernel of the same call, so
  *   calls that share a workspace must be ordered (same stream, or synchronised).
- * Errors: SPEC_EINVAL (bad counts, Hq % Hkv != 0, g * B > 128, mode, n_causal
+ * Errors: SPEC_EINVAL (bad counts, Hq % Hkv != 0, g * B > 2048, mode, n_causal
  *   outside [0, B], NULL pointers), SPEC_ENOTSUP (D, P, dtype), SPEC_ENOSPC.
  *   Kernels set SPEC_ERR_SLOT for a page id outside [0, num_pages) (physical
  *   page 0 is read in its place) and SPEC_ERR_CAPACITY for L_b < 0 or L_b + B

@@ -75,7 +75,7 @@ def test_block_attn_rejects_bad_arguments(lib):
     assert _attn(lib, dt=7) == b.SPEC_ENOTSUP
     assert _attn(lib, mode=3) == b.SPEC_EINVAL
     assert _attn(lib, hq=30) == b.SPEC_EINVAL           # Hq % Hkv != 0
-    assert _attn(lib, B=40) == b.SPEC_EINVAL            # g * B = 160 > 128
+    assert _attn(lib, B=513, max_pages=200) == b.SPEC_EINVAL  # g * B = 2052 > 2048
     assert _attn(lib, bs=0) == b.SPEC_EINVAL
     assert _attn(lib, max_pages=0) == b.SPEC_EINVAL
     assert _attn(lib, mode=2, nc=17) == b.SPEC_EINVAL   # n_causal > B
@@ -98,7 +98,7 @@ def test_block_attn_tree_rejects_bad_arguments(lib):
                                    a["lse"], a["ws"], a["ws_bytes"], a["err"], None)
     assert tree(tm=None) == b.SPEC_EINVAL
     assert tree(B=65, hq=2, hkv=2) == b.SPEC_EINVAL       # more nodes than mask bits
-    assert tree(B=40) == b.SPEC_EINVAL                    # g * B = 160 > 128
+    assert tree(B=64, hq=64, hkv=1) == b.SPEC_EINVAL      # g * B = 4096 > 2048
     assert tree(d=96) == b.SPEC_ENOTSUP
     assert tree(q=None) == b.SPEC_EINVAL
     # the mode argument of block_attn itself does not take TREE (no mask pointer)
@@ -121,6 +121,11 @@ def test_block_attn_workspace_planning(lib):
     assert lib.block_attn_workspace_bytes(128, 16, 32, 8, 128, 4112) == \
         lib.block_attn_workspace_bytes(256, 16, 32, 8, 128, 9232)
     assert lib.block_attn_workspace_bytes(0, 16, 32, 8, 128, 9232) == 0
+    # 512 rows per KV head run as 4 row groups of 128: the plan (and so the
+    # workspace) of 4 KV heads x 128 rows equals that of 16 KV heads x 128 rows
+    for kv in (8192, 2 ** 18):
+        assert lib.block_attn_workspace_bytes(2, 128, 16, 4, 128, kv) == \
+            lib.block_attn_workspace_bytes(2, 32, 64, 16, 128, kv) > 0
 
 
 def _acc(lib, **kw):

@@ -60,6 +60,14 @@ SMALL = [
     ("g1_b8_d64", 1, dict(bs=4, hq=4, hkv=4, dtype="bf16", ctx_lo=100, ctx_hi=700), synth.BIDIR),
     ("g2_b40_d128", 2, dict(bs=2, hq=4, hkv=2, block=40, ctx_lo=50, ctx_hi=400), synth.CAUSAL),
     ("f32_d128_m64", 2, dict(bs=2, dtype="f32", ctx_lo=200, ctx_hi=600), synth.CAUSAL),
+    # more than 128 query rows per KV head: row groups, each streaming the keys
+    ("rows160_g4_causal", 2, dict(bs=2, block=40, ctx_lo=50, ctx_hi=400), synth.CAUSAL),
+    ("rows512_g4_bidir_p32", 3, dict(bs=2, block=128, ctx_lo=300, ctx_hi=700), synth.BIDIR),
+    ("rows200_mixed", 5, dict(bs=2, block=50, n_causal=20, ctx_lo=100, ctx_hi=500), synth.MIXED),
+    ("rows144_f32_d64", 1, dict(bs=2, block=72, ctx_lo=40, ctx_hi=300), synth.BIDIR),
+    ("rows129_g3_ragged", 4, dict(bs=3, hq=24, hkv=8, block=43, ctx_lo=20, ctx_hi=900),
+     synth.CAUSAL),
+    ("rows2048_g8_max", 2, dict(bs=1, hq=64, hkv=8, block=256, ctx_lo=90, ctx_hi=90), synth.CAUSAL),
 ]
 
 
@@ -128,6 +136,23 @@ def test_split_kv_plans_agree(gpu_lib):
         o = va.block_attn(synth.CAUSAL, case.q, case.k, case.v, case.table, case.seq, 65536, ws=ws)
         torch.cuda.synchronize()
         assert np.max(np.abs(to_f64(o) - o4)) == 0.0
+
+
+def test_row_groups_every_schedule(gpu_lib):
+    """512 query rows per KV head (4 row groups): the split plan, a loose
+    bound that splits every unit many ways, and the balanced schedule (row
+    group teams, cut units merged per group) all match the reference."""
+    cfg = synth.config(3, bs=3, block=128, ctx_lo=900, ctx_hi=2100)
+    print_case("block_attn row groups, every schedule", cfg)
+    x = synth.make_attn_inputs(cfg, seed=21)
+    case = AttnCase(x)
+    o1, l1 = run(case, synth.BIDIR)
+    check_all(x, o1, l1, synth.BIDIR, 0)
+    o2, l2 = run(case, synth.BIDIR, max_kv=20000)
+    check_all(x, o2, l2, synth.BIDIR, 0)
+    o3, l3 = run(case, synth.BIDIR, max_kv=65536 * 4)
+    check_all(x, o3, l3, synth.BIDIR, 0)
+    assert np.max(np.abs(o1 - o3)) <= 2 ** -7 and np.max(np.abs(l1 - l3)) <= 1e-4
 
 
 def test_bad_page_id_is_flagged(gpu_lib):
@@ -245,6 +270,7 @@ QUADS = [
     ("k7_g2_d64_f32", dict(bs=2, hq=4, hkv=2, d=64, block=64, quad_k=7, dtype="f32", ctx_lo=0,
                            ctx_hi=500)),
     ("k3_g8_p32", dict(bs=4, hq=16, hkv=2, page=32, block=16, quad_k=3, ctx_lo=1, ctx_hi=300)),
+    ("k7_g4_bf16_rowgroups", dict(bs=2, block=64, quad_k=7, ctx_lo=10, ctx_hi=600)),
 ]
 
 

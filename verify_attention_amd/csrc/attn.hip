@@ -536,26 +536,48 @@ __device__ __forceinline__ WaveCtx<T, D> wave_ctx(const AttnArgs& a, const char*
   return c;
 }
 
-// Q^T operands of this wave's rows of unit (b, kvh): lane (n, grp) holds row
-// 16t + n, dims 32c + 8*grp .. +7. Row r of the group is block token r / g,
-// query head kvh * g + r % g. Both waves of a row slot hold the same rows.
+// A unit: request b, KV head kvh, and the row group whose first query row
+// (of the head's Mt = g * B) is row0; its rows are row0 .. row0 + M - 1,
+// clipped to Mt.
+struct UnitRef {
+  int b, kvh, row0;
+};
+
+__device__ __forceinline__ UnitRef unit_ref(const AttnArgs& a, int unit) {
+  const int b = unit / a.Hv;
+  const int vh = unit - b * a.Hv;
+  const int kvh = vh / a.RG;
+  return UnitRef{b, kvh, (vh - kvh * a.RG) * a.M};
+}
+
+// Whether local row r (0 .. M - 1) of a unit whose group starts at row0 exists.
+__device__ __forceinline__ bool row_exists(const AttnArgs& a, int row0, int r) {
+  return r < a.M && row0 + r < a.Mt;
+}
+
+// Q^T operands of this wave's rows of unit (b, kvh, row0): lane (n, grp)
+// holds local row 16t + n, dims 32c + 8*grp .. +7. Row r of the head is block
+// token r / g, query head kvh * g + r % g. Both waves of a row slot hold the
+// same rows.
 template <typename T, int D, int MT>
 __device__ __forceinline__ void load_q(WaveState<T, D, MT>& ws, const AttnArgs& a, int b, int kvh,
-                                       int rs, int n, int grp) {
-  const int row0 = rs * 16 * MT;
+                                       int row0, int rs, int n, int grp) {
+  const int rl0 = rs * 16 * MT;
   const T* qg = reinterpret_cast<const T*>(a.q);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    const int r = row0 + 16 * t + n;
+    const int rl = rl0 + 16 * t + n;
+    const bool in = row_exists(a, row0, rl);
+    const int r = row0 + rl;
     ws.blk_row[t] = r / a.g;
-    const int rr = r < a.M ? r : 0;
+    const int rr = in ? r : 0;
     const int ii = rr / a.g, hh = rr - ii * a.g;
     ws.tmask[t] = a.mode == 3 ? a.tree[(a.tree_per_req ? (size_t)b * a.B : 0) + ii] : 0;
     const T* src = qg + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hh) * D + 8 * grp;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       ws.qf[t][c] = Frag<T>::load(src + 32 * c);
-      if (r >= a.M) ws.qf[t][c] = Frag<T>::zero();
+      if (!in) ws.qf[t][c] = Frag<T>::zero();
     }
     ws.m_run[t] = kNegBig;
     ws.l_run[t] = 0.f;
@@ -589,8 +611,8 @@ __device__ __forceinline__ int clamped_len(const AttnArgs& a, int b, bool flag) 
 template <typename T, int D, int MT>
 __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const AttnArgs& a,
                                               const WaveCtx<T, D>& c, char* s_ring,
-                                              uint64_t* s_pgoff, int b, int kvh, int L, int s_lo,
-                                              int s_hi, int2 first) {
+                                              uint64_t* s_pgoff, int b, int kvh, int row0, int L,
+                                              int s_lo, int s_hi, int2 first) {
   using SS = StageShape<T, D>;
   constexpr int NSP = SS::NSP;
   static_assert(kPageWin == kWave * kWaves, "one thread per staged stage");
@@ -600,7 +622,7 @@ __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const Att
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
   const int n_keys = L + a.B;
   const int nc = a.nc_per_req ? a.nc_per_req[b] : a.n_causal;
-  const bool has_rows = c.rs * 16 * MT < a.M;
+  const bool has_rows = row_exists(a, row0, c.rs * 16 * MT);
   const int set = c.set;
 
   for (int w0 = s_lo; w0 < s_hi; w0 += kPageWin) {
@@ -684,12 +706,12 @@ __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const Att
 template <typename T, int D, int MT>
 __device__ __forceinline__ void finish_unit(WaveState<T, D, MT>& ws, const AttnArgs& a,
                                             const WaveCtx<T, D>& c, char* s_ring, int b, int kvh,
-                                            int part) {
+                                            int row0, int part) {
   using SS = StageShape<T, D>;
   static_assert(kRowSlots * (D / 16) * MT * 1024 + kRowSlots * MT * 512 <= SS::NSP * SS::PAIR,
                 "merge buffers fit the ring");
-  const int row0 = c.rs * 16 * MT;
-  const bool has_rows = row0 < a.M;
+  const int rl0 = c.rs * 16 * MT;
+  const bool has_rows = row_exists(a, row0, rl0);
   const int lane = c.lane;
   __syncthreads();  // every stage consumed: the ring is free
   floatx4* x_acc = reinterpret_cast<floatx4*>(s_ring) + (size_t)c.rs * (D / 16) * MT * 64;
@@ -720,8 +742,9 @@ __device__ __forceinline__ void finish_unit(WaveState<T, D, MT>& ws, const AttnA
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const float l_tot = group_sum4(ws.l_run[t]);
-    const int r = row0 + 16 * t + c.n;
-    if (r >= a.M) continue;
+    const int rl = rl0 + 16 * t + c.n;
+    if (!row_exists(a, row0, rl)) continue;
+    const int r = row0 + rl;
     const int i = r / a.g, hl = r - i * a.g;
     const size_t orow = (size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl;
     if (part < 0) {
@@ -731,7 +754,7 @@ __device__ __forceinline__ void finish_unit(WaveState<T, D, MT>& ws, const AttnA
       for (int dt = 0; dt < D / 16; ++dt) Frag<T>::store4(dst + 16 * dt, ws.acc[dt][t] * inv);
       if (a.lse && c.grp == 0) a.lse[orow] = (ws.m_run[t] + __log2f(l_tot)) * kLn2;
     } else {
-      const size_t prow = (size_t)part * a.M + r;
+      const size_t prow = (size_t)part * a.M + rl;
       float* dst = a.part_o + prow * D + 4 * c.grp;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<floatx4*>(dst + 16 * dt) = ws.acc[dt][t];
@@ -746,6 +769,15 @@ __device__ __forceinline__ void finish_unit(WaveState<T, D, MT>& ws, const AttnA
 // One workgroup per (request, KV head, split): the split is stages
 // [split * steps_per_split, ...) of the unit. With one split the rows are
 // written normalised, otherwise as partial state for the split merge.
+//
+// Workgroups are dealt to the 8 XCDs round robin. With row groups, hardware
+// block x runs logical block (x % 8) * (n / 8) + x / 8 (n blocks, n % 8 == 0),
+// so that each XCD takes a contiguous run of logical blocks: the row groups
+// of one KV head then run side by side on one XCD and share its keys in L2.
+__device__ __forceinline__ int logical_block(const AttnArgs& a, int x, int n) {
+  return (a.RG > 1 && n % 8 == 0) ? (x % 8) * (n / 8) + x / 8 : x;
+}
+
 template <typename T, int D, int MT>
 __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs a) {
   using SS = StageShape<T, D>;
@@ -753,22 +785,23 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
   __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];  // (lo, hi) per stage
 
   const WaveCtx<T, D> c = wave_ctx<T, D>(a, s_ring);
-  const int unit = blockIdx.x / a.splits;
-  const int split = blockIdx.x - unit * a.splits;
-  const int b = unit / a.Hkv;
-  const int kvh = unit - b * a.Hkv;
+  const int lb = logical_block(a, blockIdx.x, gridDim.x);
+  const int unit = lb / a.splits;
+  const int split = lb - unit * a.splits;
+  const UnitRef u = unit_ref(a, unit);
+  const int b = u.b, kvh = u.kvh;
   const int s_lo = split * a.steps_per_split;
 
   // loads that do not depend on the sequence length go out first, so that
   // their latency overlaps the length's
   WaveState<T, D, MT> ws;
-  load_q<T, D, MT>(ws, a, b, kvh, c.rs, c.n, c.grp);
+  load_q<T, D, MT>(ws, a, b, kvh, u.row0, c.rs, c.n, c.grp);
   const int2 first = table_pair(a, a.page_table + (size_t)b * a.max_pages, s_lo + c.tid);
   const int L = clamped_len(a, b, c.tid == 0 && split == 0);
   const int n_steps = (L + a.B + kStep - 1) / kStep;
   const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
-  stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, L, s_lo, s_hi, first);
-  finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, a.splits == 1 ? -1 : (int)blockIdx.x);
+  stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, u.row0, L, s_lo, s_hi, first);
+  finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, u.row0, a.splits == 1 ? -1 : lb);
 }
 
 // ------------------------------------------------------- balanced schedule
@@ -780,6 +813,17 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
 // cuts is written as partial states by the workgroups that share it -- into
 // slot 2w when it is workgroup w's first unit, else 2w + 1 -- and merged by
 // the boundary-combine kernel; every other unit is written normalised.
+//
+// With row groups the G workgroups form T = G / RG teams of RG: the ranges
+// are cut over the teams (a unit here is a (request, KV head) pair), and each
+// member streams its team's range for its own row group. A team's members sit
+// on one XCD, dealt out one after the other, so they share the keys in L2.
+// Partial slots are (2 team + {0, 1}) * RG + rg.
+__device__ __forceinline__ int2 team_of(const AttnArgs& a, int x, int G) {
+  if (a.RG == 1) return int2{x, 0};
+  const int per_xcd = G / 8, j = x / 8;
+  return int2{(x % 8) * (per_xcd / a.RG) + j / a.RG, j % a.RG};
+}
 
 __device__ __forceinline__ int unit_pairs(const AttnArgs& a, int L) {
   const int n_steps = (L + a.B + kStep - 1) / kStep;
@@ -850,9 +894,10 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   __shared__ int s_tmp[kWaves];
 
   const WaveCtx<T, D> c = wave_ctx<T, D>(a, s_ring);
-  const int G = gridDim.x, w = blockIdx.x;
-  const int total = balanced_prefix(a, s_pre, s_tmp, w == 0);
-  const int start = range_start(total, w, G), end = range_start(total, w + 1, G);
+  const int2 tr = team_of(a, blockIdx.x, gridDim.x);
+  const int T_ = gridDim.x / a.RG, w = tr.x, rg = tr.y, row0 = rg * a.M;
+  const int total = balanced_prefix(a, s_pre, s_tmp, blockIdx.x == 0);
+  const int start = range_start(total, w, T_), end = range_start(total, w + 1, T_);
   if (start >= end) return;
   int b = request_of(s_pre, a.bs, start);
   int L = clamped_len(a, b, false);
@@ -862,14 +907,14 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   for (int cur = start; cur < end;) {
     const int seg = min(np - off, end - cur);
     const bool whole = off == 0 && seg == np;
-    const int part = whole ? -1 : (cur == start ? 2 * w : 2 * w + 1);
+    const int part = whole ? -1 : (cur == start ? 2 * w : 2 * w + 1) * a.RG + rg;
     const int s_lo = 2 * off;
     const int s_hi = min((L + a.B + kStep - 1) / kStep, 2 * (off + seg));
     WaveState<T, D, MT> ws;
-    load_q<T, D, MT>(ws, a, b, kvh, c.rs, c.n, c.grp);
+    load_q<T, D, MT>(ws, a, b, kvh, row0, c.rs, c.n, c.grp);
     const int2 first = table_pair(a, a.page_table + (size_t)b * a.max_pages, s_lo + c.tid);
-    stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, L, s_lo, s_hi, first);
-    finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, part);
+    stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, row0, L, s_lo, s_hi, first);
+    finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, row0, part);
     cur += seg;
     off += seg;
     if (off == np) {  // next unit
@@ -885,10 +930,10 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   }
 }
 
-// Merge of the units cut by range boundaries. Boundary k (k = 1 .. G - 1)
-// merges the unit containing pair start(k) if that unit began inside
-// workgroup k - 1's range (so each cut unit is merged once); each boundary's
-// rows are spread over kCombineRowGroups blocks.
+// Merge of the units cut by range boundaries. Boundary k (k = 1 .. T - 1,
+// between teams) merges the unit containing pair start(k) if that unit began
+// inside team k - 1's range (so each cut unit is merged once); each
+// boundary's rows are spread over RG x kCombineRowGroups blocks.
 constexpr int kCombineRowGroups = 4;
 constexpr int kCombineMaxPieces = 256;  // a unit is shared by at most G workgroups
 
@@ -899,7 +944,9 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
   __shared__ int s_slot[kCombineMaxPieces];
   constexpr int RPB = 128 / kCombineRowGroups;  // rows per block at most
   __shared__ float s_w[RPB * 33];               // per row: weight of each of <= 32 pieces
-  const int G = a.G, k = blockIdx.x / kCombineRowGroups + 1, rg = blockIdx.x % kCombineRowGroups;
+  const int G = a.G / a.RG, per_k = a.RG * kCombineRowGroups;
+  const int k = blockIdx.x / per_k + 1, grp = (blockIdx.x % per_k) / kCombineRowGroups;
+  const int rg = blockIdx.x % kCombineRowGroups, row0 = grp * a.M;
   const int total = balanced_prefix(a, s_pre, s_tmp, false);
   const int sk = range_start(total, k, G), sk1 = range_start(total, k - 1, G);
   if (sk >= total || sk1 >= sk) return;
@@ -914,15 +961,18 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
     int n = 0;
     for (int wg = k - 1; wg < G && range_start(total, wg, G) < u1; ++wg) {
       if (range_start(total, wg, G) >= range_start(total, wg + 1, G)) continue;
-      if (n < kCombineMaxPieces) s_slot[n] = wg == k - 1 && u0 > sk1 ? 2 * wg + 1 : 2 * wg;
+      if (n < kCombineMaxPieces)
+        s_slot[n] = (wg == k - 1 && u0 > sk1 ? 2 * wg + 1 : 2 * wg) * a.RG + grp;
       ++n;
     }
     s_tmp[0] = min(n, kCombineMaxPieces);
   }
   __syncthreads();
   const int npc = s_tmp[0];
-  const int rpb = (a.M + kCombineRowGroups - 1) / kCombineRowGroups;
-  const int r0 = rg * rpb, r1 = min(a.M, r0 + rpb);
+  // local rows [r0, r1) of the unit's row group (rows past Mt do not exist)
+  const int rows = min(a.M, a.Mt - row0);
+  const int rpb = (rows + kCombineRowGroups - 1) / kCombineRowGroups;
+  const int r0 = rg * rpb, r1 = min(rows, r0 + rpb);
   if (r0 >= r1) return;
   // weights in chunks of 32 pieces: w_i = 2^(m_i - max m) / sum_j 2^(m_j - max m) l_j
   const int n4 = (r1 - r0) * (D / 4);
@@ -945,7 +995,7 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
         s_w[(r - r0) * 33 + i] = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - mm) * inv;
       }
       if (p0 == 0 && a.lse) {
-        const int ii = r / a.g, hl = r - ii * a.g;
+        const int ii = (row0 + r) / a.g, hl = row0 + r - ii * a.g;
         a.lse[(size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hl] = (mm + __log2f(ll)) * kLn2;
       }
     }
@@ -968,7 +1018,7 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
     const int e = threadIdx.x + j * blockDim.x;
     if (e >= n4) break;
     const int rl = e / (D / 4), d4 = e - rl * (D / 4);
-    const int r = r0 + rl, ii = r / a.g, hl = r - ii * a.g;
+    const int r = row0 + r0 + rl, ii = r / a.g, hl = r - ii * a.g;
     T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hl) * D + 4 * d4;
     Frag<T>::store4(dst, sum[j]);
   }
@@ -979,12 +1029,13 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
 template <typename T, int D>
 __global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
   const int unit = blockIdx.x;
-  const int b = unit / a.Hkv;
-  const int kvh = unit - b * a.Hkv;
+  const UnitRef u = unit_ref(a, unit);
+  const int b = u.b, kvh = u.kvh;
   const int S = a.splits;
+  const int rows = min(a.M, a.Mt - u.row0);  // local rows of the unit's row group
   const size_t part0 = (size_t)unit * S;
   __shared__ float wts[128 * 65];  // M <= 128 rows x (splits <= 64, + 1/L)
-  for (int r = threadIdx.x; r < a.M; r += blockDim.x) {
+  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
     float mm = kNegBig;
     for (int s2 = 0; s2 < S; ++s2) mm = fmaxf(mm, a.part_ml[((part0 + s2) * a.M + r) * 2]);
     float ll = 0.f;
@@ -996,12 +1047,12 @@ __global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
     }
     wts[r * (S + 1) + S] = 1.0f / ll;
     if (a.lse) {
-      const int i = r / a.g, hl = r - i * a.g;
+      const int i = (u.row0 + r) / a.g, hl = u.row0 + r - i * a.g;
       a.lse[(size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl] = (mm + __log2f(ll)) * kLn2;
     }
   }
   __syncthreads();
-  const int n4 = a.M * (D / 4);
+  const int n4 = rows * (D / 4);
   for (int e = threadIdx.x; e < n4; e += blockDim.x) {
     const int r = e / (D / 4), d4 = e - r * (D / 4);
     floatx4 sum = {0.f, 0.f, 0.f, 0.f};
@@ -1009,7 +1060,7 @@ __global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
       sum += wts[r * (S + 1) + s2] *
              *reinterpret_cast<const floatx4*>(a.part_o + ((part0 + s2) * a.M + r) * D + 4 * d4);
     sum *= wts[r * (S + 1) + S];
-    const int i = r / a.g, hl = r - i * a.g;
+    const int i = (u.row0 + r) / a.g, hl = u.row0 + r - i * a.g;
     T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl) * D + 4 * d4;
     Frag<T>::store4(dst, sum);
   }
@@ -1026,9 +1077,10 @@ static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t str
     else
       hipLaunchKernelGGL((block_attn_balanced_kernel<T, D, 1>), grid, block, 0, stream, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.G < 2) return e;
+    const int teams = a.G / a.RG;
+    if (e != hipSuccess || teams < 2) return e;
     hipLaunchKernelGGL((block_attn_boundary_combine_kernel<T, D>),
-                       dim3((a.G - 1) * kCombineRowGroups), dim3(256), 0, stream, a);
+                       dim3((teams - 1) * a.RG * kCombineRowGroups), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 grid(total_blocks);
@@ -1038,7 +1090,7 @@ static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t str
     hipLaunchKernelGGL((block_attn_kernel<T, D, 1>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((block_attn_combine_kernel<T, D>), dim3(a.bs * a.Hkv), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((block_attn_combine_kernel<T, D>), dim3(a.bs * a.Hv), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@ namespace {
 constexpr int kStepKeys = 32;
 constexpr int kMaxSplits = 64;  // the merge weights (M x (splits+1) floats) fit the LDS output tile
 constexpr int kMaxChunks = 256;
+constexpr int kMaxUnitRows = 128;   // query rows one workgroup holds (8 MFMA row tiles)
+constexpr int kMaxQueryRows = 2048; // g * B: at most 16 row groups
 constexpr int kCUs = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -43,7 +45,7 @@ int env_schedule() {
 }
 
 struct AttnPlan {
-  int M = 0, units = 0, splits = 1, steps_per_split = 1;
+  int M = 0, Mt = 0, RG = 1, units = 0, splits = 1, steps_per_split = 1;
   bool balanced = false;
   int grid = 0;
   size_t off_ml = 0, off_o = 0, ws_bytes = 0;
@@ -59,17 +61,25 @@ struct AttnPlan {
 // 8 stages of 32 keys.
 constexpr long long kBalancedMinStages = 32768;
 
+// Query rows per KV head beyond kMaxUnitRows are cut into row groups of at
+// most kMaxUnitRows (equal sizes, rounded up to the 16-row MFMA tile); each
+// group streams the head's keys on its own. The balanced schedule keeps the
+// RG workgroups of a group team on one XCD so that they share the keys in L2.
 AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   AttnPlan p;
-  p.M = (Hq / Hkv) * B;
-  p.units = bs * Hkv;
+  p.Mt = (Hq / Hkv) * B;
+  p.RG = (p.Mt + kMaxUnitRows - 1) / kMaxUnitRows;
+  p.M = p.RG == 1 ? p.Mt : (int)align_up((size_t)((p.Mt + p.RG - 1) / p.RG), 16);
+  p.RG = (p.Mt + p.M - 1) / p.M;  // no empty group after the rounding
+  p.units = bs * Hkv * p.RG;
   const int max_steps = std::max(1, (max_kv_len + kStepKeys - 1) / kStepKeys);
   const int sched = env_schedule();
   p.balanced = bs <= kMaxBalancedBatch &&
                (sched == 2 || (sched != 1 && (long long)p.units * max_steps >= kBalancedMinStages));
   if (p.balanced) {
-    p.grid = kCUs;
-    const size_t slots = 2 * (size_t)kCUs;
+    // G = teams x RG workgroups, a multiple of 8 * RG (one team per XCD slot)
+    p.grid = p.RG == 1 ? kCUs : std::max(1, kCUs / (8 * p.RG)) * 8 * p.RG;
+    const size_t slots = 2 * (size_t)p.grid;
     p.off_ml = 0;
     p.off_o = align_up(slots * p.M * 2 * sizeof(float), 256);
     p.ws_bytes = p.off_o + slots * p.M * D * sizeof(float);
@@ -187,7 +197,7 @@ int attn_common(int mode, int n_causal, const int32_t* n_causal_per_req, const u
   if (D != 64 && D != 128) return SPEC_ENOTSUP;
   if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
   if (bs <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return SPEC_EINVAL;
-  if ((Hq / Hkv) * B > 128) return SPEC_EINVAL;
+  if ((long long)(Hq / Hkv) * B > kMaxQueryRows) return SPEC_EINVAL;
   if (max_pages <= 0 || num_pages <= 0 || max_kv_len <= 0) return SPEC_EINVAL;
   if ((long long)max_pages * page_size < B) return SPEC_EINVAL;
   if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
@@ -219,6 +229,9 @@ int attn_common(int mode, int n_causal, const int32_t* n_causal_per_req, const u
   a.Hkv = Hkv;
   a.g = Hq / Hkv;
   a.M = plan.M;
+  a.Mt = plan.Mt;
+  a.RG = plan.RG;
+  a.Hv = Hkv * plan.RG;
   a.P = page_size;
   a.p_shift = ilog2_exact(page_size);
   a.max_pages = max_pages;

@@ -18,7 +18,10 @@ struct AttnArgs {
   float* part_o;      // [slots][M][D] partial outputs (unnormalised): split or cut-unit pieces
   float* part_ml;     // [slots][M][2] partial (max, sum), log2 domain
   int32_t* err;
-  int bs, B, Hq, Hkv, g, M;  // M = g * B query rows per KV head
+  // The Mt = g * B query rows of a KV head are cut into RG row groups of M
+  // rows (the last may be short); a unit is (request, KV head, row group),
+  // Hv = Hkv * RG units per request, unit = b * Hv + kvh * RG + rg.
+  int bs, B, Hq, Hkv, g, M, Mt, RG, Hv;
   int P, p_shift, max_pages, num_pages;
   int mode, n_causal;
   int tree_per_req;
