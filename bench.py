@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="round configuration 1..8")
+    ap.add_argument("--config", type=int, default=2, help="round configuration 1..9")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="the warm-up runs at least this long (after the W steps)")
@@ -157,7 +157,8 @@ def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None, lacc=None):
     return dict(value=done * cfg.block / el, unit="verified tokens/s", cores=int(threads),
                 kind="oracle",
                 sample=f"{done} requests of this workload (attention over all {cfg.hq} query "
-                       f"heads + accept), one after another, {el:.1f} s; host has "
+                       f"heads{' + accept' if acc is not None or tacc is not None or lacc is not None else ''}"
+                       f"), one after another, {el:.1f} s; host has "
                        f"{len(os.sched_getaffinity(0))} cores")
 
 
@@ -247,7 +248,7 @@ def main():
                        bonus=torch.empty(bs, dtype=torch.int32, device=dev),
                        out_tokens=torch.empty((bs, cfg.k_spec + 1), dtype=torch.int32, device=dev),
                        new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
-    elif not tree:
+    elif not tree and logits is not None:
         tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     # every call is checked once; the timed loop re-enqueues pre-marshalled calls
@@ -284,6 +285,8 @@ def main():
                       for s in sets]
     elif logits is not None:
         tail_calls = [va.draft_argmax_call(s["logits"], out=tokens)[0] for s in sets]
+    else:
+        tail_calls = [lambda: None] * copies  # attention-only workload
 
     def step(i, ev=None):
         if prep_call is not None:
@@ -350,7 +353,7 @@ def main():
                                alg_bytes=ab, achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1),
                                mean_commit_len=float(cl.mean()))
         extra["committed_tokens_per_s"] = float(cl.sum() * args.steps / wall)
-    else:
+    elif logits is not None:
         ab = logits.nbytes
         extra["draft_argmax"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2), alg_bytes=int(ab),
                                      achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1))
@@ -361,14 +364,24 @@ def main():
                "traffic_unit": "bytes per launch",
                "alg_bytes_per_launch": alg_bytes, "avg_us": round(attn_ms.mean() * 1e3, 2),
                "mfma_frac": round(alg_flops / attn_s / 1e12 / mfma_peak, 4)}
-    tail_name = ("spec_accept_tree+spec_commit_kv" if tree else "spec_accept_logits" if lacc is not None else
-                 "spec_accept" if acc is not None else "spec_draft_argmax")
-    tail_s = tail_ms.mean() / 1e3
-    tail_rl = {"kernel": tail_name, "bound": "hbm", "achieved": round(ab / tail_s / 1e9, 1),
-               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ab / tail_s / 1e9 / HBM_PEAK_GBS, 4),
-               "traffic": measured_traffic(cfg.name, kernel_sources_hash(), tail_name),
-               "traffic_unit": "bytes per launch", "alg_bytes_per_launch": int(ab),
-               "avg_us": round(tail_ms.mean() * 1e3, 2)}
+    if alg_flops / alg_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        # flops per byte above the ridge: the matrix cores bound the kernel
+        tflops = alg_flops / attn_s / 1e12
+        attn_rl.update(bound="mfma", achieved=round(tflops, 1), peak=mfma_peak, unit="TFLOP/s",
+                       frac=round(tflops / mfma_peak, 4), alg_flops_per_launch=alg_flops,
+                       hbm_frac=round(achieved / HBM_PEAK_GBS, 4))
+    tail_rl = None
+    if acc is not None or tree or lacc is not None or logits is not None:
+        tail_name = ("spec_accept_tree+spec_commit_kv" if tree else "spec_accept_logits"
+                     if lacc is not None else "spec_accept" if acc is not None else
+                     "spec_draft_argmax")
+        tail_s = tail_ms.mean() / 1e3
+        tail_rl = {"kernel": tail_name, "bound": "hbm", "achieved": round(ab / tail_s / 1e9, 1),
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(ab / tail_s / 1e9 / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic(cfg.name, kernel_sources_hash(), tail_name),
+                   "traffic_unit": "bytes per launch", "alg_bytes_per_launch": int(ab),
+                   "avg_us": round(tail_ms.mean() * 1e3, 2)}
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -384,7 +397,10 @@ def main():
         "dtype": cfg.dtype,
         "data": ("synthetic (seeded N(0,1) Q/K/V, normal target logits, draft logits = target "
                  "+ normal noise)" if lacc is not None else
-                 "synthetic (seeded N(0,1) Q/K/V, softmax-of-normal target/draft rows)"),
+                 "synthetic (seeded N(0,1) Q/K/V, softmax-of-normal target/draft rows)"
+                 if acc is not None or tree else
+                 "synthetic (seeded N(0,1) Q/K/V, N(0, 3^2) bf16 draft logits)"
+                 if logits is not None else "synthetic (seeded N(0,1) Q/K/V)"),
         "config": {"workload": cfg.name, "bs": bs, "block": B, "hq": cfg.hq, "hkv": cfg.hkv,
                    "head_dim": cfg.d, "page": cfg.page, "mode": synth.MODE_NAMES[mode],
                    "ctx": [cfg.ctx_lo, cfg.ctx_hi], "vocab": cfg.vocab or cfg.argmax_vocab,
@@ -394,7 +410,7 @@ def main():
         "kernel_src": kernel_sources_hash(),
         **extra,
     }
-    if tail_rl["avg_us"] > attn_rl["avg_us"]:
+    if tail_rl is not None and tail_rl["avg_us"] > attn_rl["avg_us"]:
         # the call that dominates the step carries the roofline
         line["roofline"], line["attn_roofline"] = tail_rl, attn_rl
     if not args.no_cpu:

@@ -71,6 +71,10 @@ class RoundConfig:
 #  8 quadratic layout: the verify of 2 with k = 4 drafts and a group of k
 #    MASK tokens after the root and after every draft (25 positions), draft
 #    and verify in one forward; the accept checks the k drafts
+#  9 the draft pass of 3 with a 128-position block: g * B = 512 query rows
+#    per KV head put the attention's flops per KV byte (about 470) above the
+#    MI355X ridge (2.5 PFLOP/s / 8 TB/s = 312.5), the matrix-core-bound
+#    shape; attention only (no argmax tail)
 #  6 tree verify: the Qwen3-8B-shaped verify of 2 with a 32-node token tree
 #    (at most 16 levels) as the block, one tree per request; target logits
 #    N(0, 6^2), peaked enough (top-4 mass about 2/3 at this vocabulary) that
@@ -105,6 +109,8 @@ CONFIGS = {
                    block=16, modes=(CAUSAL,), dtype="bf16", ctx_lo=1024,
                    ctx_hi=1024, vocab=151936, k_spec=15, logit_sigma=3.0,
                    q_noise_sigma=0.5, sampling=(1.0, 50, 0.95)),
+    9: RoundConfig("draft_bidir_b128_bs64", bs=64, hq=16, hkv=4, d=128, page=32,
+                   block=128, modes=(BIDIR,), dtype="bf16", ctx_lo=1024, ctx_hi=9216),
 }
 
 
