@@ -285,7 +285,7 @@ def main():
                       for s in sets]
     elif logits is not None:
         tail_calls = [va.draft_argmax_call(s["logits"], out=tokens)[0] for s in sets]
-    else:
+    elif not tree:
         tail_calls = [lambda: None] * copies  # attention-only workload
 
     def step(i, ev=None):

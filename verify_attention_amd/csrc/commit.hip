@@ -32,40 +32,39 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
   __shared__ long long s_src[64], s_dst[64];  // element offsets of K rows (-1: skipped)
   __shared__ long long s_vsrc[64], s_vdst[64];
   __shared__ int s_d, s_err;
-  if (tid == 0) {
+  // wave 0, lane k = accepted row k: the length, the depth and every path
+  // entry are loaded at once, the path is checked by a ballot, then each lane
+  // looks up its row's pages (two dependent loads in all)
+  if (tid < 64) {
     const int L = a.seq_lens[b];
     int d = a.accept_len[b];
+    const int p = a.path ? (tid < B ? a.path[(size_t)b * B + tid] : 0) : tid + 1;
     int err = 0;
     if (L < 0 || (long long)L + B > (long long)a.max_pages * P) {
-      err |= kErrCapacity;
+      err = kErrCapacity;
       d = -1;
     } else if (d < 0 || d > B - 1) {
-      err |= kErrTree;
+      err = kErrTree;
       d = -1;
     } else if (a.path) {
       // node p_k has depth k + 1: k + 1 <= p_k < B, increasing
-      for (int k = 0; k < d; ++k) {
-        const int p = a.path[(size_t)b * B + k];
-        if (p < k + 1 || p >= B || (k > 0 && p <= a.path[(size_t)b * B + k - 1])) err |= kErrTree;
+      const int prev = __shfl_up(p, 1, 64);
+      const bool bad = tid < d && (p < tid + 1 || p >= B || (tid > 0 && p <= prev));
+      if (__builtin_amdgcn_ballot_w64(bad)) {
+        err = kErrTree;
+        d = -1;
       }
-      if (err) d = -1;
     }
-    s_d = d;
-    s_err = err;
-  }
-  __syncthreads();
-  const int d = s_d;
-  const int L = a.seq_lens[b];
-  // row bases: K element (page, h, off, i) at ((page * Hkv + h) * P + off) * D + i,
-  // V element (page, h, i, off) at ((page * Hkv + h) * D + i) * P + off
-  if (tid < 64) {
+    // row bases: K element (page, h, off, i) at ((page * Hkv + h) * P + off) * D + i,
+    // V element (page, h, i, off) at ((page * Hkv + h) * D + i) * P + off
     long long ks = -1, kd = -1, vs = -1, vd = -1;
+    bool bad_slot = false;
     if (tid < d) {
-      const int src = L + (a.path ? a.path[(size_t)b * B + tid] : tid + 1);
+      const int src = L + p;
       const int dst = L + 1 + tid;
       const int ps = tab[src / P], pd = tab[dst / P];
       const bool ok = (unsigned)ps < (unsigned)a.num_pages && (unsigned)pd < (unsigned)a.num_pages;
-      if (!ok) atomicOr(&s_err, kErrSlot);
+      bad_slot = !ok;
       if (ok && src != dst) {
         ks = (((long long)ps * Hkv + h) * P + src % P) * D;
         kd = (((long long)pd * Hkv + h) * P + dst % P) * D;
@@ -73,11 +72,19 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
         vd = ((long long)pd * Hkv + h) * D * P + dst % P;
       }
     }
+    if (__builtin_amdgcn_ballot_w64(bad_slot)) err |= kErrSlot;
     s_src[tid] = ks;
     s_dst[tid] = kd;
     s_vsrc[tid] = vs;
     s_vdst[tid] = vd;
+    if (tid == 0) {
+      s_d = d;
+      s_err = err;
+    }
   }
+  __syncthreads();
+  const int d = s_d;
+  const int L = a.seq_lens[b];
   __syncthreads();
   T* K = reinterpret_cast<T*>(a.k);
   T* V = reinterpret_cast<T*>(a.v);
