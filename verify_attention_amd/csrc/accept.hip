@@ -342,13 +342,24 @@ __device__ __forceinline__ double wave_exclusive_scan(double x) {
   return wave_inclusive_scan(x) - x;
 }
 
+// Lane n's node: parent and token (loaded once, shared by the walk and the
+// excluded set).
+struct TreeNode {
+  int par, tok;
+};
+
+__device__ __forceinline__ TreeNode tree_node(const AcceptArgs& a, int b) {
+  const int N = a.K, n = threadIdx.x & 63;
+  const bool in = n < N;
+  return TreeNode{in ? a.parent[(size_t)b * N + n] : -2, in ? a.token[(size_t)b * N + n] : -1};
+}
+
 // Wave 0 only. path[] (LDS) receives the accepted node ids.
-__device__ TreeWalk tree_walk(const AcceptArgs& a, int b, int* path) {
+__device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNode& nd, int* path) {
   const int N = a.K, V = a.V;
   const int n = threadIdx.x & 63;
   const bool in = n < N;
-  const int par = in ? a.parent[(size_t)b * N + n] : -2;
-  const int tok = in ? a.token[(size_t)b * N + n] : -1;
+  const int par = nd.par, tok = nd.tok;
   const double un = in ? (double)a.u[(size_t)b * N + n] : 0.0;
   const bool vpar = in && n >= 1 && par >= 0 && par < n;
   const bool vtok = tok >= 0 && tok < V;
@@ -363,7 +374,7 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, int* path) {
     bool dup = false;
     for (uint64_t rest = kids; rest; rest &= rest - 1) {
       const int k = __builtin_ctzll(rest);
-      const int tk = __shfl(tok, k, 64);
+      const int tk = __builtin_amdgcn_readlane(tok, k);  // k is wave-uniform
       dup |= kid && n > k && tk == tok;
     }
     const double pres = (kid && vtok && !dup) ? pv : 0.0;
@@ -382,12 +393,11 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, int* path) {
 
 // The final node's children tokens (valid ids) into excl[]; returns the count.
 // Wave 0 only.
-__device__ int tree_excluded(const AcceptArgs& a, int b, int x, int* excl) {
+__device__ int tree_excluded(const AcceptArgs& a, const TreeNode& nd, int x, int* excl) {
   const int N = a.K, V = a.V;
   const int n = threadIdx.x & 63;
   const bool in = n < N;
-  const int par = in ? a.parent[(size_t)b * N + n] : -2;
-  const int tok = in ? a.token[(size_t)b * N + n] : -1;
+  const int par = nd.par, tok = nd.tok;
   const bool ex = in && n >= 1 && par == x && par < n && tok >= 0 && tok < V;
   const uint64_t m = __builtin_amdgcn_ballot_w64(ex);
   if (ex) excl[__builtin_popcountll(m & ((1ull << n) - 1))] = tok;
@@ -404,8 +414,9 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(Accept
   __shared__ int s_path[64], s_excl[64], s_fexcl[64];
   __shared__ int s_x, s_nex, s_nf;
   if (wave == 0) {
-    const TreeWalk w = tree_walk(a, b, s_path);
-    const int nex = tree_excluded(a, b, w.x, s_excl);
+    const TreeNode nd = tree_node(a, b);
+    const TreeWalk w = tree_walk(a, b, nd, s_path);
+    const int nex = tree_excluded(a, nd, w.x, s_excl);
     if (lane == 0) {
       s_x = w.x;
       s_nex = nex;
@@ -413,7 +424,10 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(Accept
         a.jbuf[b] = w.x | (w.depth << 8) | ((w.errs & kErrToken) ? kJTreeTokErr : 0) |
                     ((w.errs & kErrTree) ? kJTreeErr : 0);
     }
-    if (c == 0 && lane < w.depth) a.pathbuf[(size_t)b * N + lane] = s_path[lane];
+    // the accepted nodes with their tokens (node | token << 8) for the select
+    const int pn = lane < w.depth ? s_path[lane] : 0;
+    const int pt = __shfl(nd.tok, pn, 64);
+    if (c == 0 && lane < w.depth) a.pathbuf[(size_t)b * N + lane] = pn | (pt << 8);
   }
   __syncthreads();
   const int nsb = (V + kSub - 1) / kSub;
@@ -461,10 +475,11 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_select_kernel(AcceptA
   const double ub = (double)a.u[(size_t)b * N];
   const int jw = a.jbuf[b];
   const int x = jw & 0xff, depth = (jw >> 8) & 0xff;
-  const int pnode = tid < depth ? a.pathbuf[(size_t)b * N + tid] : -1;
-  const int ptok = pnode >= 0 ? a.token[(size_t)b * N + pnode] : -1;
+  const int pw = tid < depth ? a.pathbuf[(size_t)b * N + tid] : -1;
+  const int pnode = pw >= 0 ? (pw & 0xff) : -1;
+  const int ptok = pw >= 0 ? (int)((unsigned)pw >> 8) : -1;
   if (tid < 64) {
-    const int nex = tree_excluded(a, b, x, s_excl);
+    const int nex = tree_excluded(a, tree_node(a, b), x, s_excl);
     if (tid == 0) s_nex = nex;
   }
   __syncthreads();
