@@ -151,50 +151,31 @@ __device__ __forceinline__ int wave_offset(int wcnt, int* s_w, int* total) {
 }
 
 // A threshold for the top-k search: the key of the k-th largest of the 256
-// per-thread keys with its low 16 bits cleared, found by two rounds of an
-// 8-bit digit histogram in LDS (largest digit whose suffix count reaches the
-// rank still sought). At least k keys are >= the result.
+// per-thread keys with its low 16 bits cleared, i.e. the largest multiple P of
+// 2^16 with at least k keys >= P. Wave 0 holds all 256 keys (4 per lane) and
+// decides the 16 high bits from the top down, each by a count of the keys
+// reaching the candidate (ballots; no LDS atomics, one barrier each way).
 __device__ __forceinline__ uint32_t threshold_key(uint32_t key, int k, int* s_hist, int* s_sel) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t prefix = 0;
-  int krem = k;
+  s_hist[tid] = (int)key;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t k0 = (uint32_t)s_hist[lane], k1 = (uint32_t)s_hist[64 + lane],
+                   k2 = (uint32_t)s_hist[128 + lane], k3 = (uint32_t)s_hist[192 + lane];
+    uint32_t prefix = 0;  // every key reaches 0
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int shift = 24 - 8 * round;
-    s_hist[tid] = 0;
-    __syncthreads();
-    const bool match = round == 0 || (key >> 24) == (prefix >> 24);
-    if (match) atomicAdd(&s_hist[(key >> shift) & 255], 1);
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds digits 4l .. 4l + 3; suffix sums from the top digit down
-      const int h0 = s_hist[4 * lane], h1 = s_hist[4 * lane + 1], h2 = s_hist[4 * lane + 2],
-                h3 = s_hist[4 * lane + 3];
-      int suf = h0 + h1 + h2 + h3;  // becomes the count of digits >= 4 * lane
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(suf, off, 64);
-        if (lane + off < 64) suf += y;
-      }
-      // counts of digits >= 4l + 3, 4l + 2, 4l + 1, 4l
-      const int c3 = suf - h0 - h1 - h2, c2 = c3 + h2, c1 = c2 + h1, c0 = suf;
-      const int best = c3 >= krem ? 4 * lane + 3 : c2 >= krem ? 4 * lane + 2
-                       : c1 >= krem ? 4 * lane + 1 : c0 >= krem ? 4 * lane : -1;
-      const uint64_t ok = __builtin_amdgcn_ballot_w64(best >= 0);
-      const int top = 63 - __builtin_clzll(ok);  // the lane holding the largest such digit
-      if (lane == top) {
-        const int above = best == 4 * lane + 3 ? c3 - h3 : best == 4 * lane + 2 ? c2 - h2
-                          : best == 4 * lane + 1 ? c1 - h1 : c0 - h0;
-        s_sel[0] = best;
-        s_sel[1] = above;
-      }
+    for (int bit = 31; bit >= 16; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(k0 >= cand)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(k1 >= cand)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(k2 >= cand)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(k3 >= cand));
+      if (cnt >= k) prefix = cand;
     }
-    __syncthreads();
-    prefix |= (uint32_t)s_sel[0] << shift;
-    krem -= s_sel[1];
-    __syncthreads();
+    if (lane == 0) s_sel[0] = (int)prefix;
   }
-  return prefix;
+  __syncthreads();
+  return (uint32_t)s_sel[0];
 }
 
 // Exact slow path for one row (candidates overflow LDS): top_k rounds, each
@@ -271,12 +252,16 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   __shared__ float s_rv[4];
   __shared__ int s_ri[4], s_w[4], s_sel[2];
 
-  // per-thread maximum of its tile maxima (tiles tid, tid + 256, ...)
+  // per-thread maximum of its tile maxima (tiles tid, tid + 256, ...); the
+  // register loops are unrolled for the largest vocabulary and leave at the
+  // row's own tile count (a uniform branch)
   const float* tm = a.tmax + (size_t)row * ntiles;
+  const int jn = (ntiles + kSampThreads - 1) / kSampThreads;
   float tv[kTilesPerThread];
   float lmax = -__builtin_inff();
 #pragma unroll
   for (int j = 0; j < kTilesPerThread; ++j) {
+    if (j >= jn) break;
     const int t = tid + j * kSampThreads;
     tv[j] = t < ntiles ? tm[t] : -__builtin_inff();
     lmax = fmaxf(lmax, tv[j]);
@@ -288,13 +273,16 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   // running count, the wave offsets through LDS
   int wcnt = 0;
 #pragma unroll
-  for (int j = 0; j < kTilesPerThread; ++j)
+  for (int j = 0; j < kTilesPerThread; ++j) {
+    if (j >= jn) break;
     wcnt += __builtin_popcountll(
         __builtin_amdgcn_ballot_w64(tid + j * kSampThreads < ntiles && tv[j] >= tau));
+  }
   int ncand;
   int at = wave_offset(wcnt, s_w, &ncand);
 #pragma unroll
   for (int j = 0; j < kTilesPerThread; ++j) {
+    if (j >= jn) break;
     const int t = tid + j * kSampThreads;
     const bool take = t < ntiles && tv[j] >= tau;
     const uint64_t m = __builtin_amdgcn_ballot_w64(take);
@@ -339,14 +327,19 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   }
   int ntop;
   if (ncand <= kMaxCandTiles && nsurv <= 64) {
-    // exact ranks by counting in one wave (lane = survivor)
+    // exact ranks by counting (lane = survivor): each wave counts the
+    // survivors of its quarter that rank before the lane's, wave 0 adds
+    const bool in = lane < nsurv;
+    const float v = in ? s_sv[lane] : -__builtin_inff();
+    const int i = in ? s_si[lane] : 0x7fffffff;
+    int rank = 0;
+    const int t1 = min(nsurv, 16 * (wave + 1));
+    for (int t = 16 * wave; t < t1; ++t)
+      rank += ranks_before(lane_f(v, t), lane_i(i, t), v, i) ? 1 : 0;
+    s_hist[tid] = rank;
+    __syncthreads();
     if (wave == 0) {
-      const bool in = lane < nsurv;
-      const float v = in ? s_sv[lane] : -__builtin_inff();
-      const int i = in ? s_si[lane] : 0x7fffffff;
-      int rank = 0;
-      for (int t = 0; t < nsurv; ++t)
-        rank += ranks_before(lane_f(v, t), lane_i(i, t), v, i) ? 1 : 0;
+      rank += s_hist[64 + lane] + s_hist[128 + lane] + s_hist[192 + lane];
       if (in && rank < k) {
         s_topv[rank] = v;
         s_topi[rank] = i;
