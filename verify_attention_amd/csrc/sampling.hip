@@ -242,8 +242,9 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.top_k, V = a.V, ntiles = a.ntiles;
   const T* x = row_ptr<T>(a, row);
-  constexpr int kBatch = 16;  // candidate tiles loaded together per wave
+  constexpr int kBatch = 24;  // candidate tiles loaded together per wave
   __shared__ int s_hist[kSampThreads];
+  __shared__ int s_rank2[kSampThreads];
   __shared__ int s_cand[kMaxCandTiles];
   __shared__ float s_sv[kMaxSurvivors];
   __shared__ int s_si[kMaxSurvivors];
@@ -260,10 +261,14 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   float tv[kTilesPerThread];
   float lmax = -__builtin_inff();
 #pragma unroll
-  for (int j = 0; j < kTilesPerThread; ++j) {
+  for (int j = 0; j < kTilesPerThread; ++j) {  // every load goes out before any use
     if (j >= jn) break;
     const int t = tid + j * kSampThreads;
     tv[j] = t < ntiles ? tm[t] : -__builtin_inff();
+  }
+#pragma unroll
+  for (int j = 0; j < kTilesPerThread; ++j) {
+    if (j >= jn) break;
     lmax = fmaxf(lmax, tv[j]);
   }
   float tau = key_f(threshold_key(fkey(lmax), k, s_hist, s_sel));
@@ -294,13 +299,15 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
   int nsurv = 0;
   if (ncand <= kMaxCandTiles) {
     // entries >= tau of the candidate tiles (lane = entry of a tile); every
-    // wave loads kBatch tiles at once, the survivors are compacted by a scan
+    // wave loads up to kBatch tiles at once (tiles dealt to the waves in
+    // turn, so that a short list keeps all four busy), the survivors are
+    // compacted by a scan
     for (int c0 = 0; c0 < ncand; c0 += kBatch * (kSampThreads / 64)) {
       float v[kBatch];
       int e[kBatch];
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
-        const int c = c0 + wave * kBatch + t;
+        const int c = c0 + t * (kSampThreads / 64) + wave;
         e[t] = c < ncand ? s_cand[c] * kTile + lane : V;
         v[t] = e[t] < V ? load_f32(x + e[t]) : -__builtin_inff();
       }
@@ -326,23 +333,36 @@ __global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
     __syncthreads();
   }
   int ntop;
-  if (ncand <= kMaxCandTiles && nsurv <= 64) {
-    // exact ranks by counting (lane = survivor): each wave counts the
-    // survivors of its quarter that rank before the lane's, wave 0 adds
-    const bool in = lane < nsurv;
-    const float v = in ? s_sv[lane] : -__builtin_inff();
-    const int i = in ? s_si[lane] : 0x7fffffff;
-    int rank = 0;
-    const int t1 = min(nsurv, 16 * (wave + 1));
-    for (int t = 16 * wave; t < t1; ++t)
-      rank += ranks_before(lane_f(v, t), lane_i(i, t), v, i) ? 1 : 0;
-    s_hist[tid] = rank;
+  if (ncand <= kMaxCandTiles && nsurv <= 128) {
+    // exact ranks by counting: every wave holds survivors lane and 64 + lane
+    // in registers and counts, for both, the survivors t of its quarter of
+    // the list that rank before them (t read by readlane); wave 0 adds
+    const bool ina = lane < nsurv, inb = 64 + lane < nsurv;
+    const float va = ina ? s_sv[lane] : -__builtin_inff();
+    const int ia = ina ? s_si[lane] : 0x7fffffff;
+    const float vb = inb ? s_sv[64 + lane] : -__builtin_inff();
+    const int ib = inb ? s_si[64 + lane] : 0x7fffffff;
+    const int q = (nsurv + 3) >> 2, t0 = wave * q, t1 = min(nsurv, t0 + q);
+    int ra = 0, rb = 0;
+    for (int t = t0; t < t1; ++t) {
+      const float vt = lane_f(t < 64 ? va : vb, t & 63);
+      const int it = lane_i(t < 64 ? ia : ib, t & 63);
+      ra += ranks_before(vt, it, va, ia) ? 1 : 0;
+      rb += ranks_before(vt, it, vb, ib) ? 1 : 0;
+    }
+    s_hist[tid] = ra;
+    s_rank2[tid] = rb;
     __syncthreads();
     if (wave == 0) {
-      rank += s_hist[64 + lane] + s_hist[128 + lane] + s_hist[192 + lane];
-      if (in && rank < k) {
-        s_topv[rank] = v;
-        s_topi[rank] = i;
+      ra += s_hist[64 + lane] + s_hist[128 + lane] + s_hist[192 + lane];
+      rb += s_rank2[64 + lane] + s_rank2[128 + lane] + s_rank2[192 + lane];
+      if (ina && ra < k) {
+        s_topv[ra] = va;
+        s_topi[ra] = ia;
+      }
+      if (inb && rb < k) {
+        s_topv[rb] = vb;
+        s_topi[rb] = ib;
       }
     }
     ntop = min(k, nsurv);
