@@ -194,7 +194,8 @@ int block_attn_tree(const uint64_t* tree_mask, int tree_per_request, int dtype, 
  *
  *   rows, V   logits is [rows, V] (for a draft pass, rows = bs * (B - 1))
  *   dtype     SPEC_BF16 or SPEC_F32
- * Output: tokens [rows]. Rows holding NaN give an unspecified id in [0, V).
+ * Output: tokens [rows]. NaN entries never win; a row without a non-NaN
+ * entry gives 0.
  * Errors: SPEC_EINVAL (rows <= 0, V <= 0, NULL), SPEC_ENOTSUP (dtype).
  */
 int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* tokens,
