@@ -958,6 +958,48 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   }
 }
 
+constexpr int kCombineFastPieces = 8;  // partial states loaded together per merge step
+
+// Merge of n partial states (unnormalised output, max m and sum l in the
+// log2 domain) for the 4 output dims 4 d4 .. 4 d4 + 3 of one row: piece i's
+// state sits at partial row prow(i). Pieces are taken kCombineFastPieces at
+// a time, every load of a chunk issued before any is used; the running
+// (max, sum, output) is rescaled when a chunk raises the maximum. Returns the
+// unnormalised output acc, its max mm and sum ll.
+template <int D, typename F>
+__device__ __forceinline__ void merge_pieces(const AttnArgs& a, int n, F prow, int d4, float& mm,
+                                             float& ll, floatx4& acc) {
+  mm = kNegBig;
+  ll = 0.f;
+  acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < n; c0 += kCombineFastPieces) {
+    float2 ml[kCombineFastPieces];
+    floatx4 po[kCombineFastPieces];
+#pragma unroll
+    for (int i = 0; i < kCombineFastPieces; ++i) {
+      if (c0 + i >= n) break;
+      const size_t pr = prow(c0 + i);
+      ml[i] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+      po[i] = *reinterpret_cast<const floatx4*>(a.part_o + pr * D + 4 * d4);
+    }
+    float mc = mm;
+#pragma unroll
+    for (int i = 0; i < kCombineFastPieces; ++i)
+      if (c0 + i < n) mc = fmaxf(mc, ml[i].x);
+    const float sc = __builtin_amdgcn_exp2f(mm - mc);
+    ll *= sc;
+    acc *= sc;
+    mm = mc;
+#pragma unroll
+    for (int i = 0; i < kCombineFastPieces; ++i) {
+      if (c0 + i >= n) break;
+      const float w = __builtin_amdgcn_exp2f(ml[i].x - mm);
+      ll += w * ml[i].y;
+      acc += w * po[i];
+    }
+  }
+}
+
 // Merge of the units cut by range boundaries. Boundary k (k = 1 .. T - 1,
 // between teams) merges the unit containing pair start(k) if that unit began
 // inside team k - 1's range (so each cut unit is merged once); each
@@ -970,8 +1012,6 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
   __shared__ int s_pre[kMaxBalancedBatch + 1];
   __shared__ int s_tmp[4];
   __shared__ int s_slot[kCombineMaxPieces];
-  constexpr int RPB = 128 / kCombineRowGroups;  // rows per block at most
-  __shared__ float s_w[RPB * 33];               // per row: weight of each of <= 32 pieces
   const int G = a.G / a.RG, per_k = a.RG * kCombineRowGroups;
   const int k = blockIdx.x / per_k + 1, grp = (blockIdx.x % per_k) / kCombineRowGroups;
   const int rg = blockIdx.x % kCombineRowGroups, row0 = grp * a.M;
@@ -1002,53 +1042,16 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
   const int rpb = (rows + kCombineRowGroups - 1) / kCombineRowGroups;
   const int r0 = rg * rpb, r1 = min(rows, r0 + rpb);
   if (r0 >= r1) return;
-  // weights in chunks of 32 pieces: w_i = 2^(m_i - max m) / sum_j 2^(m_j - max m) l_j
   const int n4 = (r1 - r0) * (D / 4);
-  floatx4 sum[4];
-  for (int j = 0; j < 4; ++j) sum[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < npc; p0 += 32) {
-    const int pn = min(32, npc - p0);
-    __syncthreads();
-    for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
-      float mm = kNegBig;
-      for (int i = 0; i < npc; ++i) mm = fmaxf(mm, a.part_ml[((size_t)s_slot[i] * a.M + r) * 2]);
-      float ll = 0.f;
-      for (int i = 0; i < npc; ++i) {
-        const size_t pr = (size_t)s_slot[i] * a.M + r;
-        ll += __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - mm) * a.part_ml[pr * 2 + 1];
-      }
-      const float inv = 1.0f / ll;
-      for (int i = 0; i < pn; ++i) {
-        const size_t pr = (size_t)s_slot[p0 + i] * a.M + r;
-        s_w[(r - r0) * 33 + i] = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - mm) * inv;
-      }
-      if (p0 == 0 && a.lse) {
-        const int ii = (row0 + r) / a.g, hl = row0 + r - ii * a.g;
-        a.lse[(size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hl] = (mm + __log2f(ll)) * kLn2;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = threadIdx.x + j * blockDim.x;
-      if (e >= n4) break;
-      const int rl = e / (D / 4), d4 = e - rl * (D / 4);
-      floatx4 acc = sum[j];
-      for (int i = 0; i < pn; ++i) {
-        const size_t pr = (size_t)s_slot[p0 + i] * a.M + r0 + rl;
-        acc += s_w[rl * 33 + i] * *reinterpret_cast<const floatx4*>(a.part_o + pr * D + 4 * d4);
-      }
-      sum[j] = acc;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = threadIdx.x + j * blockDim.x;
-    if (e >= n4) break;
-    const int rl = e / (D / 4), d4 = e - rl * (D / 4);
-    const int r = row0 + r0 + rl, ii = r / a.g, hl = r - ii * a.g;
-    T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hl) * D + 4 * d4;
-    Frag<T>::store4(dst, sum[j]);
+  for (int e = threadIdx.x; e < n4; e += blockDim.x) {
+    const int rl = e / (D / 4), d4 = e - rl * (D / 4), r = r0 + rl;
+    float mm, ll;
+    floatx4 acc;
+    merge_pieces<D>(a, npc, [&](int i) { return (size_t)s_slot[i] * a.M + r; }, d4, mm, ll, acc);
+    const int rr = row0 + r, ii = rr / a.g, hl = rr - ii * a.g;
+    const size_t orow = (size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hl;
+    if (d4 == 0 && a.lse) a.lse[orow] = (mm + __log2f(ll)) * kLn2;
+    Frag<T>::store4(reinterpret_cast<T*>(a.o) + orow * D + 4 * d4, acc * (1.0f / ll));
   }
 }
 
@@ -1062,35 +1065,16 @@ __global__ __launch_bounds__(256) void block_attn_combine_kernel(AttnArgs a) {
   const int S = a.splits;
   const int rows = min(a.M, a.Mt - u.row0);  // local rows of the unit's row group
   const size_t part0 = (size_t)unit * S;
-  __shared__ float wts[128 * 65];  // M <= 128 rows x (splits <= 64, + 1/L)
-  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-    float mm = kNegBig;
-    for (int s2 = 0; s2 < S; ++s2) mm = fmaxf(mm, a.part_ml[((part0 + s2) * a.M + r) * 2]);
-    float ll = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const size_t pr = (part0 + s2) * a.M + r;
-      const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - mm);
-      wts[r * (S + 1) + s2] = w;
-      ll += w * a.part_ml[pr * 2 + 1];
-    }
-    wts[r * (S + 1) + S] = 1.0f / ll;
-    if (a.lse) {
-      const int i = (u.row0 + r) / a.g, hl = u.row0 + r - i * a.g;
-      a.lse[(size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl] = (mm + __log2f(ll)) * kLn2;
-    }
-  }
-  __syncthreads();
   const int n4 = rows * (D / 4);
   for (int e = threadIdx.x; e < n4; e += blockDim.x) {
     const int r = e / (D / 4), d4 = e - r * (D / 4);
-    floatx4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < S; ++s2)
-      sum += wts[r * (S + 1) + s2] *
-             *reinterpret_cast<const floatx4*>(a.part_o + ((part0 + s2) * a.M + r) * D + 4 * d4);
-    sum *= wts[r * (S + 1) + S];
-    const int i = (u.row0 + r) / a.g, hl = u.row0 + r - i * a.g;
-    T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl) * D + 4 * d4;
-    Frag<T>::store4(dst, sum);
+    float mm, ll;
+    floatx4 acc;
+    merge_pieces<D>(a, S, [&](int s2) { return (part0 + s2) * a.M + r; }, d4, mm, ll, acc);
+    const int rr = u.row0 + r, i = rr / a.g, hl = rr - i * a.g;
+    const size_t orow = (size_t)(b * a.B + i) * a.Hq + kvh * a.g + hl;
+    if (d4 == 0 && a.lse) a.lse[orow] = (mm + __log2f(ll)) * kLn2;
+    Frag<T>::store4(reinterpret_cast<T*>(a.o) + orow * D + 4 * d4, acc * (1.0f / ll));
   }
 }
 

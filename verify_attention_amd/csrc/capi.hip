@@ -15,7 +15,7 @@ using namespace specattn;
 namespace {
 
 constexpr int kStepKeys = 32;
-constexpr int kMaxSplits = 64;  // the merge weights (M x (splits+1) floats) fit the LDS output tile
+constexpr int kMaxSplits = 64;  // splits per unit (each keeps at least 8 stages when planned)
 constexpr int kMaxChunks = 256;
 constexpr int kMaxUnitRows = 128;   // query rows one workgroup holds (8 MFMA row tiles)
 constexpr int kMaxQueryRows = 2048; // g * B: at most 16 row groups
