@@ -263,12 +263,12 @@ def main():
         acc_out = None
         tail_calls = []
         for s in sets:
-            acc_call, acc_out = va.accept_tree_call(tpar, ttok, s["p"], s["u"], seq, out=acc_out,
-                                                    ws=ws_tacc, err=err)
-            # the accepted path becomes the committed prefix of the cache
-            com_call = va.commit_kv_call(s["k"], s["v"], table, seq, acc_out["accept_len"], B,
-                                         acc_out["path_nodes"], err=err)[0]
-            tail_calls.append(lambda a=acc_call, c=com_call: (a(), c()))
+            # the tree accept, whose accepted path becomes the committed
+            # prefix of the cache in the same call
+            acc_call, acc_out = va.accept_tree_commit_call(tpar, ttok, s["p"], s["u"], seq,
+                                                           s["k"], s["v"], table, out=acc_out,
+                                                           ws=ws_tacc, err=err)
+            tail_calls.append(acc_call)
     elif quad:
         attn_calls = [va.block_attn_tree_call(tmask, s["q"], s["k"], s["v"], table, seq, max_kv,
                                               out=o, ws=ws_attn, err=err)[0] for s in sets]
@@ -372,7 +372,7 @@ def main():
                        hbm_frac=round(achieved / HBM_PEAK_GBS, 4))
     tail_rl = None
     if acc is not None or tree or lacc is not None or logits is not None:
-        tail_name = ("spec_accept_tree+spec_commit_kv" if tree else "spec_accept_logits"
+        tail_name = ("spec_accept_tree_commit" if tree else "spec_accept_logits"
                      if lacc is not None else "spec_accept" if acc is not None else
                      "spec_draft_argmax")
         tail_s = tail_ms.mean() / 1e3

@@ -398,6 +398,33 @@ int spec_commit_kv(int dtype, int bs, int B, int Hkv, int D, int page_size, int 
                    const int32_t* path_nodes, const int32_t* page_table, void* k_pool,
                    void* v_pool, int32_t* freed_loc, int32_t* err_flags, void* stream);
 
+/*
+ * spec_accept_tree_commit -- spec_accept_tree and spec_commit_kv in one call.
+ *
+ * The tree accept (spec_accept_tree) followed by the commit of its accepted
+ * path (spec_commit_kv with B = N, accept_len and path_nodes as the accept
+ * returns them): every output, both pools and freed_loc are exactly those of
+ * the two calls in order. One launch fewer: the path is fixed by the walk of
+ * the accept's first kernel (the bonus draw of the second does not change
+ * it), so the first kernel also moves the rows and lists the released slots.
+ *
+ *   bs, N, V, parent, token, p, u, seq_lens and the outputs: as
+ *   spec_accept_tree (same workspace: spec_accept_tree_workspace_bytes)
+ *   dtype, Hkv, D, page_size, max_pages, num_pages, page_table, k_pool,
+ *   v_pool, freed_loc [bs, N]: as spec_commit_kv with B = N
+ * Data errors: those of both calls (a request whose block lies past its page
+ *   table keeps its rows in place and releases nothing).
+ * Errors: those of both calls.
+ */
+int spec_accept_tree_commit(int bs, int N, int V, const int32_t* parent, const int32_t* token,
+                            const float* p, const float* u, const int32_t* seq_lens,
+                            int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                            int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
+                            int dtype, int Hkv, int D, int page_size, int max_pages,
+                            int num_pages, const int32_t* page_table, void* k_pool, void* v_pool,
+                            int32_t* freed_loc, void* workspace, size_t ws_bytes,
+                            int32_t* err_flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

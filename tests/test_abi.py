@@ -257,3 +257,34 @@ def test_commit_kv_rejects_bad_arguments(lib):
     assert com(D=96) == b.SPEC_ENOTSUP
     assert com(P=8) == b.SPEC_ENOTSUP
     assert com(dt=9) == b.SPEC_ENOTSUP
+
+
+def test_accept_tree_commit_rejects_bad_arguments(lib):
+    ws = lib.spec_accept_tree_workspace_bytes(4, 32, 151936)
+
+    def atc(**kw):
+        a = dict(bs=4, N=32, V=151936, par=FAKE, tok=FAKE, p=FAKE, u=FAKE, seq=FAKE, al=FAKE,
+                 cl=FAKE, bon=FAKE, ot=FAKE, pn=FAKE, nsl=FAKE, dt=b.BF16, hkv=8, D=128, P=16,
+                 mp=70, np_=300, tab=FAKE, k=FAKE, v=FAKE, freed=FAKE, ws=FAKE, ws_bytes=ws,
+                 err=None)
+        a.update(kw)
+        return lib.spec_accept_tree_commit(
+            a["bs"], a["N"], a["V"], a["par"], a["tok"], a["p"], a["u"], a["seq"], a["al"],
+            a["cl"], a["bon"], a["ot"], a["pn"], a["nsl"], a["dt"], a["hkv"], a["D"], a["P"],
+            a["mp"], a["np_"], a["tab"], a["k"], a["v"], a["freed"], a["ws"], a["ws_bytes"],
+            a["err"], None)
+    # the commit's arguments
+    assert atc(dt=9) == b.SPEC_ENOTSUP
+    assert atc(D=96) == b.SPEC_ENOTSUP
+    assert atc(P=8) == b.SPEC_ENOTSUP
+    assert atc(hkv=0) == b.SPEC_EINVAL
+    assert atc(mp=0) == b.SPEC_EINVAL
+    assert atc(tab=None) == b.SPEC_EINVAL
+    assert atc(k=None) == b.SPEC_EINVAL
+    assert atc(freed=None) == b.SPEC_EINVAL
+    # the accept's arguments
+    assert atc(N=65) == b.SPEC_EINVAL
+    assert atc(bs=0) == b.SPEC_EINVAL
+    assert atc(par=None) == b.SPEC_EINVAL
+    assert atc(V=600000) == b.SPEC_ENOTSUP
+    assert atc(ws_bytes=ws - 1) == b.SPEC_ENOSPC

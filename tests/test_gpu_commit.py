@@ -114,3 +114,79 @@ def test_commit_flags_bad_requests_and_leaves_them_unchanged():
                                       np.array([2, 0, 0, 0]), path, cfg.block)
     assert np.array_equal(k, rk) and np.array_equal(v, rv)
     assert np.array_equal(freed[0], rfreed[0])
+
+
+def _tree_case(cfg, seed):
+    x = synth.make_attn_inputs(cfg, seed=seed)
+    par, _ = synth.make_trees(cfg, seed)
+    ti = synth.make_tree_accept_inputs(cfg, seed, par)
+    return x, ti
+
+
+def _pools(x):
+    return to_dev(x.k_pool), to_dev(x.v_pool)
+
+
+def _host(t, bf16):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("cid,over", [(6, {}), (6, dict(bs=5, block=12, hq=4, hkv=2, d=64, page=32,
+                                                          dtype="f32", ctx_lo=17, ctx_hi=70,
+                                                          tree_depth=6, vocab=300))])
+def test_accept_tree_commit_equals_the_two_calls(cid, over):
+    """spec_accept_tree_commit gives exactly the outputs, pools and released
+    slots of spec_accept_tree followed by spec_commit_kv, and the pools equal
+    the reference commit of the reference accept's path."""
+    cfg = synth.config(cid, **over)
+    print_case("accept_tree_commit", cfg.name, over)
+    x, ti = _tree_case(cfg, 2)
+    bf16 = x.k_pool.dtype == np.uint16
+    args = [to_dev(a) for a in (ti.parent, ti.token, ti.p, ti.u)]
+    seq, tab = to_dev(x.seq_lens), to_dev(x.page_table)
+    # two calls
+    k1, v1 = _pools(x)
+    out1 = va.accept_tree(*args, seq)
+    freed1 = va.commit_kv(k1, v1, tab, seq, out1["accept_len"], cfg.block, out1["path_nodes"])
+    # one call
+    k2, v2 = _pools(x)
+    out2 = va.accept_tree_commit(*args, seq, k2, v2, tab)
+    torch.cuda.synchronize()
+    for key in ("accept_len", "commit_len", "bonus", "out_tokens", "path_nodes", "new_seq_lens"):
+        assert torch.equal(out1[key], out2[key]), key
+    assert torch.equal(freed1, out2["freed"])
+    assert np.array_equal(_host(k1, bf16), _host(k2, bf16))
+    assert np.array_equal(_host(v1, bf16), _host(v2, bf16))
+    # and the reference: commit of the reference accept's path
+    acc = [oracle.tree_accept_request(ti.parent[b], ti.token[b], ti.p[b], ti.u[b], x.seq_lens[b])
+           for b in range(cfg.bs)]
+    depth = np.array([a["accept_len"] for a in acc], np.int32)
+    path = np.stack([a["path_nodes"] for a in acc]).astype(np.int32)
+    assert np.array_equal(out2["accept_len"].cpu().numpy(), depth)
+    rk, rv, rfreed = oracle.commit_kv(x.k_pool, x.v_pool, x.page_table, x.seq_lens, depth, path,
+                                      cfg.block)
+    assert np.array_equal(_host(k2, bf16), rk) and np.array_equal(_host(v2, bf16), rv)
+    assert np.array_equal(out2["freed"].cpu().numpy(), rfreed)
+    print(f"accept_tree_commit: depths {depth.tolist()[:8]}...", flush=True)
+
+
+def test_accept_tree_commit_flags_a_block_past_the_table():
+    cfg = synth.config(6, bs=4, block=8, hq=4, hkv=2, d=64, dtype="f32", ctx_lo=20, ctx_hi=20,
+                       tree_depth=5, vocab=64)
+    print_case("accept_tree_commit capacity")
+    x, ti = _tree_case(cfg, 9)
+    x.seq_lens[2] = x.page_table.shape[1] * cfg.page   # request 2: block past its table
+    args = [to_dev(a) for a in (ti.parent, ti.token, ti.p, ti.u)]
+    seq, tab = to_dev(x.seq_lens), to_dev(x.page_table)
+    e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    k1, v1 = _pools(x)
+    out1 = va.accept_tree(*args, seq, err=e1)
+    freed1 = va.commit_kv(k1, v1, tab, seq, out1["accept_len"], cfg.block, out1["path_nodes"],
+                          err=e1)
+    k2, v2 = _pools(x)
+    out2 = va.accept_tree_commit(*args, seq, k2, v2, tab, err=e2)
+    torch.cuda.synchronize()
+    assert int(e2.item()) & va.ERR_CAPACITY and int(e1.item()) == int(e2.item())
+    assert torch.equal(freed1, out2["freed"]) and (out2["freed"][2] == -1).all()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)

@@ -46,6 +46,8 @@ _SIGS = {
     "spec_accept": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "spec_commit_kv": (_c_int, [_c_int] * 8 + [_vp] * 9),
+    "spec_accept_tree_commit": (_c_int, [_c_int] * 3 + [_vp] * 11 + [_c_int] * 6 +
+                                [_vp] * 5 + [_c_size, _vp, _vp]),
     "spec_sampling_filter_workspace_bytes": (_c_size, [_c_int] * 2),
     "spec_sampling_filter": (_c_int, [_c_int, _c_int, _c_int, _vp, _f, _c_int, _f, _vp, _vp, _vp,
                                       _vp, _c_size, _vp]),
@@ -407,6 +409,62 @@ def accept_tree_call(parent, token, p, u, seq_lens, out=None, ws=None, err=None,
             _check(st, "spec_accept_tree")
 
     return enqueue, out
+
+
+def accept_tree_commit_call(parent, token, p, u, seq_lens, k_pool, v_pool, page_table, out=None,
+                            ws=None, err=None, stream=None):
+    """Checks the arguments of spec_accept_tree_commit once and returns
+    (enqueue, out): the tree accept of accept_tree_call plus the commit of its
+    path (k_pool / v_pool updated in place); out also holds freed [bs, N]."""
+    torch = _torch()
+    bs, N, V = p.shape
+    _need(p, "p", torch.float32)
+    _need(parent, "parent", torch.int32, (bs, N))
+    _need(token, "token", torch.int32, (bs, N))
+    _need(u, "u", torch.float32, (bs, N))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    num_pages, hkv, P, d = k_pool.shape
+    _need(k_pool, "k_pool")
+    dt = _dtype_code(k_pool)
+    _need(v_pool, "v_pool", k_pool.dtype, (num_pages, hkv, d, P))
+    _need(page_table, "page_table", torch.int32)
+    dev = p.device
+    if out is None:
+        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((bs, N), dtype=torch.int32, device=dev),
+                   path_nodes=torch.empty((bs, N), dtype=torch.int32, device=dev),
+                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev),
+                   freed=torch.empty((bs, N), dtype=torch.int32, device=dev))
+    _need(out["freed"], "freed", torch.int32, (bs, N))
+    if ws is None:
+        ws = workspace(accept_tree_workspace_bytes(bs, N, V), dev)
+    args = (bs, N, V, _ptr(parent), _ptr(token), _ptr(p), _ptr(u), _ptr(seq_lens),
+            _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
+            _ptr(out["out_tokens"]), _ptr(out["path_nodes"]), _ptr(out["new_seq_lens"]),
+            dt, hkv, d, P, page_table.shape[1], num_pages, _ptr(page_table), _ptr(k_pool),
+            _ptr(v_pool), _ptr(out["freed"]), _ptr(ws), ws.numel(), _ptr(err), _stream(stream))
+    fn = load().spec_accept_tree_commit
+    keep = (parent, token, p, u, seq_lens, k_pool, v_pool, page_table, out, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_accept_tree_commit")
+
+    return enqueue, out
+
+
+def accept_tree_commit(parent, token, p, u, seq_lens, k_pool, v_pool, page_table, out=None,
+                       ws=None, err=None, stream=None):
+    """Tree accept and commit in one call (spec_accept_tree_commit): the
+    outputs of accept_tree plus freed [bs, N]; the pools are updated in place."""
+    enqueue, out = accept_tree_commit_call(parent, token, p, u, seq_lens, k_pool, v_pool,
+                                           page_table, out, ws, err, stream)
+    enqueue()
+    return out
 
 
 def accept_tree(parent, token, p, u, seq_lens, out=None, ws=None, err=None, stream=None):

@@ -16,6 +16,7 @@
 //     boundary orders the two phases; no device-scope fences or counters).
 // Only the residual (or bonus) row pair is streamed from HBM; the other target
 // rows are touched at one gathered element each.
+#include "commit_rows.h"
 #include "kernels.h"
 
 namespace specattn {
@@ -453,10 +454,9 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(Accept
   }
 }
 
-// Kernel 2, one workgroup per request: the bonus from the sub-block masses,
-// then every output.
-__global__ __launch_bounds__(kAccThreads) void accept_tree_select_kernel(AcceptArgs a) {
-  const int b = blockIdx.x;
+// Kernel 2, request b: the bonus from the sub-block masses, then every
+// output (all threads of the workgroup).
+__device__ void tree_select(const AcceptArgs& a, int b) {
   const int N = a.K, V = a.V;
   const int tid = threadIdx.x;
   __shared__ double s_wave[4];
@@ -519,12 +519,62 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_select_kernel(AcceptA
   if (tid == 0 && errs) flag_error(a.err, errs);
 }
 
+// The commit of KV head h of request b in the same call: the accepted path
+// (fixed by the walk of kernel 1, which the draw does not change) from the
+// workspace; head 0 also lists the released slots. A block past the page
+// table keeps its rows and releases nothing.
+template <typename KVT>
+__device__ void tree_commit_head(const AcceptArgs& a, int b, int h) {
+  __shared__ long long s_ksrc[64], s_kdst[64], s_vsrc[64], s_vdst[64];
+  __shared__ int s_cerr;
+  const CommitRows rows{s_ksrc, s_kdst, s_vsrc, s_vdst};
+  const int tid = threadIdx.x, N = a.K, P = a.commit_P;
+  const int32_t* tab = a.commit_tab + (size_t)b * a.commit_max_pages;
+  const int L = a.seq_lens[b];
+  const bool cap_ok = L >= 0 && (long long)L + N <= (long long)a.commit_max_pages * P;
+  const int d = cap_ok ? (a.jbuf[b] >> 8) & 0xff : -1;
+  if (tid < 64) {
+    const int pw = tid < N ? a.pathbuf[(size_t)b * N + tid] : 0;  // lanes < d hold the path
+    const bool bad = commit_row_bases(rows, tab, P, a.commit_D, a.commit_Hkv, a.commit_num_pages,
+                                      h, L, d, pw & 0xff);
+    if (tid == 0) s_cerr = (cap_ok ? 0 : kErrCapacity) | (bad ? kErrSlot : 0);
+  }
+  __syncthreads();
+  commit_move_rows<KVT>(rows, reinterpret_cast<KVT*>(a.commit_k),
+                        reinterpret_cast<KVT*>(a.commit_v), P, a.commit_D, d);
+  if (h == 0) {
+    if (commit_freed(a.commit_freed + (size_t)b * N, tab, P, N, a.commit_num_pages, L, d))
+      atomicOr(&s_cerr, kErrSlot);
+    __syncthreads();
+  }
+  if (tid == 0 && s_cerr) flag_error(a.err, s_cerr);
+}
+
+// Kernel 2, one workgroup per request; with the commit, Hkv + 1 per request:
+// workgroup h < Hkv commits KV head h while the last one draws the bonus and
+// writes the accept's outputs, side by side.
+template <bool COMMIT, typename KVT>
+__global__ __launch_bounds__(kAccThreads) void accept_tree_select_kernel(AcceptArgs a) {
+  const int H1 = COMMIT ? a.commit_Hkv + 1 : 1;
+  const int b = blockIdx.x / H1, h = blockIdx.x - b * H1;
+  if (h == H1 - 1) tree_select(a, b);
+  else if constexpr (COMMIT) tree_commit_head<KVT>(a, b, h);
+}
+
 hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(accept_tree_partial_kernel, dim3(a.bs * a.nchunk), dim3(kAccThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_tree_select_kernel, dim3(a.bs), dim3(kAccThreads), 0, stream, a);
+  const dim3 block(kAccThreads);
+  if (!a.commit_k)
+    hipLaunchKernelGGL((accept_tree_select_kernel<false, float>), dim3(a.bs), block, 0, stream, a);
+  else if (a.commit_bf16)
+    hipLaunchKernelGGL((accept_tree_select_kernel<true, __bf16>), dim3(a.bs * (a.commit_Hkv + 1)),
+                       block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((accept_tree_select_kernel<true, float>), dim3(a.bs * (a.commit_Hkv + 1)),
+                       block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -337,12 +337,14 @@ SPEC_API size_t spec_accept_tree_workspace_bytes(int bs, int N, int V) {
   return plan_accept_tree(bs, N, V).ws_bytes;
 }
 
-SPEC_API int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const int32_t* token,
-                              const float* p, const float* u, const int32_t* seq_lens,
-                              int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
-                              int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
-                              void* workspace, size_t ws_bytes, int32_t* err_flags,
-                              void* stream) {
+namespace {
+
+int accept_tree_common(int bs, int N, int V, const int32_t* parent, const int32_t* token,
+                       const float* p, const float* u, const int32_t* seq_lens,
+                       int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                       int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
+                       void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream,
+                       const AcceptArgs* commit) {
   if (bs <= 0 || N < 1 || N > 64 || V <= 0) return SPEC_EINVAL;
   if ((long long)bs * N > INT_MAX) return SPEC_EINVAL;
   if (!parent || !token || !p || !u || !seq_lens || !accept_len || !commit_len || !bonus ||
@@ -352,7 +354,7 @@ SPEC_API int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const
   const AccPlan plan = plan_accept_tree(bs, N, V);
   if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
   char* ws = static_cast<char*>(workspace);
-  AcceptArgs a{};
+  AcceptArgs a = commit ? *commit : AcceptArgs{};
   a.p = p;
   a.q = nullptr;
   a.draft = nullptr;
@@ -377,6 +379,50 @@ SPEC_API int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const
   a.nchunk = plan.nchunk;
   a.chunk = plan.chunk;
   return hip_status(launch_accept_tree(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+SPEC_API int spec_accept_tree(int bs, int N, int V, const int32_t* parent, const int32_t* token,
+                              const float* p, const float* u, const int32_t* seq_lens,
+                              int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                              int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
+                              void* workspace, size_t ws_bytes, int32_t* err_flags,
+                              void* stream) {
+  return accept_tree_common(bs, N, V, parent, token, p, u, seq_lens, accept_len, commit_len,
+                            bonus, out_tokens, path_nodes, new_seq_lens, workspace, ws_bytes,
+                            err_flags, stream, nullptr);
+}
+
+SPEC_API int spec_accept_tree_commit(int bs, int N, int V, const int32_t* parent,
+                                     const int32_t* token, const float* p, const float* u,
+                                     const int32_t* seq_lens, int32_t* accept_len,
+                                     int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
+                                     int32_t* path_nodes, int32_t* new_seq_lens, int dtype,
+                                     int Hkv, int D, int page_size, int max_pages, int num_pages,
+                                     const int32_t* page_table, void* k_pool, void* v_pool,
+                                     int32_t* freed_loc, void* workspace, size_t ws_bytes,
+                                     int32_t* err_flags, void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (D != 64 && D != 128) return SPEC_ENOTSUP;
+  if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
+  if (Hkv <= 0 || max_pages <= 0 || num_pages <= 0) return SPEC_EINVAL;
+  if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
+  if (!page_table || !k_pool || !v_pool || !freed_loc) return SPEC_EINVAL;
+  AcceptArgs c{};
+  c.commit_k = k_pool;
+  c.commit_v = v_pool;
+  c.commit_tab = page_table;
+  c.commit_freed = freed_loc;
+  c.commit_bf16 = dtype == SPEC_BF16 ? 1 : 0;
+  c.commit_Hkv = Hkv;
+  c.commit_D = D;
+  c.commit_P = page_size;
+  c.commit_max_pages = max_pages;
+  c.commit_num_pages = num_pages;
+  return accept_tree_common(bs, N, V, parent, token, p, u, seq_lens, accept_len, commit_len,
+                            bonus, out_tokens, path_nodes, new_seq_lens, workspace, ws_bytes,
+                            err_flags, stream, &c);
 }
 
 // ------------------------------------------------ sampling parameters

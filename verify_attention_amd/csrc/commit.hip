@@ -15,23 +15,19 @@
 // separates the reads from the writes (a destination may be another row's
 // source), then they are stored. The request's first workgroup lists the
 // released slots.
-#include "kernels.h"
+#include "commit_rows.h"
 
 namespace specattn {
-
-constexpr int kCommitThreads = 256;
-constexpr int kCommitPer = 32;  // elements per thread: 63 rows x 128 dims fit
-static_assert(kCommitThreads * kCommitPer >= 63 * 128, "one round of loads");
 
 template <typename T>
 __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a) {
   const int b = blockIdx.x / a.Hkv, h = blockIdx.x - (blockIdx.x / a.Hkv) * a.Hkv;
   const int tid = threadIdx.x;
-  const int P = a.P, D = a.D, B = a.B, Hkv = a.Hkv;
+  const int P = a.P, B = a.B;
   const int32_t* tab = a.page_table + (size_t)b * a.max_pages;
-  __shared__ long long s_src[64], s_dst[64];  // element offsets of K rows (-1: skipped)
-  __shared__ long long s_vsrc[64], s_vdst[64];
+  __shared__ long long s_ksrc[64], s_kdst[64], s_vsrc[64], s_vdst[64];
   __shared__ int s_d, s_err;
+  const CommitRows rows{s_ksrc, s_kdst, s_vsrc, s_vdst};
   // wave 0, lane k = accepted row k: the length, the depth and every path
   // entry are loaded at once, the path is checked by a ballot, then each lane
   // looks up its row's pages (two dependent loads in all)
@@ -55,28 +51,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
         d = -1;
       }
     }
-    // row bases: K element (page, h, off, i) at ((page * Hkv + h) * P + off) * D + i,
-    // V element (page, h, i, off) at ((page * Hkv + h) * D + i) * P + off
-    long long ks = -1, kd = -1, vs = -1, vd = -1;
-    bool bad_slot = false;
-    if (tid < d) {
-      const int src = L + p;
-      const int dst = L + 1 + tid;
-      const int ps = tab[src / P], pd = tab[dst / P];
-      const bool ok = (unsigned)ps < (unsigned)a.num_pages && (unsigned)pd < (unsigned)a.num_pages;
-      bad_slot = !ok;
-      if (ok && src != dst) {
-        ks = (((long long)ps * Hkv + h) * P + src % P) * D;
-        kd = (((long long)pd * Hkv + h) * P + dst % P) * D;
-        vs = ((long long)ps * Hkv + h) * D * P + src % P;
-        vd = ((long long)pd * Hkv + h) * D * P + dst % P;
-      }
-    }
-    if (__builtin_amdgcn_ballot_w64(bad_slot)) err |= kErrSlot;
-    s_src[tid] = ks;
-    s_dst[tid] = kd;
-    s_vsrc[tid] = vs;
-    s_vdst[tid] = vd;
+    if (commit_row_bases(rows, tab, P, a.D, a.Hkv, a.num_pages, h, L, d, p)) err |= kErrSlot;
     if (tid == 0) {
       s_d = d;
       s_err = err;
@@ -84,47 +59,13 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
   }
   __syncthreads();
   const int d = s_d;
-  const int L = a.seq_lens[b];
-  __syncthreads();
-  T* K = reinterpret_cast<T*>(a.k);
-  T* V = reinterpret_cast<T*>(a.v);
-  T kr[kCommitPer], vr[kCommitPer];
-#pragma unroll
-  for (int i = 0; i < kCommitPer; ++i) {
-    const int e = tid + i * kCommitThreads;
-    const int k = e / D, dd = e - (e / D) * D;
-    if (k < d && s_src[k] >= 0) {
-      kr[i] = K[s_src[k] + dd];
-      vr[i] = V[s_vsrc[k] + (long long)dd * P];
-    }
-  }
-  __syncthreads();  // every source element is read before any is overwritten
-#pragma unroll
-  for (int i = 0; i < kCommitPer; ++i) {
-    const int e = tid + i * kCommitThreads;
-    const int k = e / D, dd = e - (e / D) * D;
-    if (k < d && s_src[k] >= 0) {
-      K[s_dst[k] + dd] = kr[i];
-      V[s_vdst[k] + (long long)dd * P] = vr[i];
-    }
-  }
+  commit_move_rows<T>(rows, reinterpret_cast<T*>(a.k), reinterpret_cast<T*>(a.v), P, a.D, d);
   if (h == 0) {
-    // released slots: positions L + d + 1 .. L + B - 1 in order, then -1
-    if (tid < B) {
-      const int pos = L + d + 1 + tid;
-      int slot = -1;
-      if (d >= 0 && pos < L + B) {
-        const int pg = tab[pos / P];
-        if ((unsigned)pg < (unsigned)a.num_pages) slot = pg * P + pos % P;
-        else atomicOr(&s_err, kErrSlot);
-      }
-      a.freed[(size_t)b * B + tid] = slot;
-    }
+    if (commit_freed(a.freed + (size_t)b * B, tab, P, B, a.num_pages, a.seq_lens[b], d))
+      atomicOr(&s_err, kErrSlot);
     __syncthreads();
-    if (tid == 0 && s_err) flag_error(a.err, s_err);
-  } else if (tid == 0 && s_err) {
-    flag_error(a.err, s_err);
   }
+  if (tid == 0 && s_err) flag_error(a.err, s_err);
 }
 
 hipError_t launch_commit_kv(const CommitArgs& a, bool bf16, hipStream_t stream) {

@@ -74,6 +74,13 @@ struct AcceptArgs {
   const int32_t* token;
   int32_t* path_nodes;  // [bs][N] output
   int32_t* pathbuf;     // [bs][N] accepted nodes passed between the two kernels
+  // tree verify with the commit in the same call (commit_k null: no commit):
+  // the accepted path's K/V rows moved, the rest of the block released
+  void* commit_k;                 // k_pool [num_pages][Hkv][P][D]
+  void* commit_v;                 // v_pool [num_pages][Hkv][D][P]
+  const int32_t* commit_tab;      // page_table [bs][commit_max_pages]
+  int32_t* commit_freed;          // [bs][N] released slots
+  int commit_bf16, commit_Hkv, commit_D, commit_P, commit_max_pages, commit_num_pages;
   int bs, K, V, nchunk, chunk;
 };
 
