@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference leg")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="HIP events bracket the calls of every n-th timed step (an event "
+                         "record drains the stream: on every step they would slow it)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MB (a known-size "
                          "kernel for scaling HBM byte counters)")
@@ -319,7 +322,10 @@ def main():
         if warm_steps % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # per-call durations: events around the calls of every n-th timed step
+    every = max(1, args.event_every)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] if i % every == 0 else None
+           for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -329,6 +335,7 @@ def main():
     if int(err.item()) != 0:
         raise RuntimeError(f"kernels reported data errors: {int(err.item())}")
 
+    evs = [e for e in evs if e is not None]
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     tail_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     alg_bytes, alg_flops = attn_alg_bytes_flops(cfg, x.seq_lens, masks)
@@ -390,6 +397,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_steps_run": warm_steps,
+        "event_steps": len(evs),
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
