@@ -15,7 +15,10 @@
 //     that sub-block to locate the token, and writes every output (a kernel
 //     boundary orders the two phases; no device-scope fences or counters).
 // Only the residual (or bonus) row pair is streamed from HBM; the other target
-// rows are touched at one gathered element each.
+// rows are touched at one gathered element each. The tree accept has the same
+// two kernels (the walk in the first); when it also commits the accepted path
+// (spec_accept_tree_commit), its second kernel adds one workgroup per KV head
+// that moves that head's rows beside the one drawing the bonus.
 #include "commit_rows.h"
 #include "kernels.h"
 

@@ -10,12 +10,16 @@
 // per-row bitmask over the block keys for tree verification (the Tree
 // sampler of "Unlocking Lossless Speedups in LLMs via Discrete Diffusion").
 //
-// Work decomposition: one 8-wave workgroup per (request, KV head, split).
+// Work decomposition: one 8-wave workgroup per (request, KV head, row group,
+// split).
 //   * All g * B query rows that share a KV head (the GQA group's query heads
 //     times the block tokens) are the MFMA N dimension, so each K/V page is
-//     read from HBM once per KV head. The rows are cut into 4 row slots of 16
-//     (or 32 when g * B > 64) rows; each row slot has two waves, one per key
-//     half: the split's keys stream through in 32-key stages taken in pairs,
+//     read from HBM once per KV head; beyond 128 rows they are cut into row
+//     groups (each streaming the head's keys; the groups of a head run on one
+//     XCD and share them in its L2). A group's rows are cut into 4 row slots
+//     of 16 (or 32 when the group has more than 64) rows; each row slot has
+//     two waves, one per key half: the split's keys stream through in 32-key
+//     stages taken in pairs,
 //     wave set 0 consuming the even stage of a pair and set 1 the odd one.
 //     The two sets' softmax states are merged through LDS at the end, so two
 //     waves share every SIMD and one wave's MFMAs overlap the other's VALU.
@@ -35,15 +39,16 @@
 //     a stage so that the accumulator layout of S^T is directly the B operand
 //     of the PV product and the dim-major V page gives the A operand as one
 //     contiguous 16-byte run: no shuffles between the two products.
-//   * Online softmax in fp32 (exp2 domain), row max across the 4 lane groups
-//     via permlane swaps, lazy rescaling (the reference max only moves when a
+//   * Online softmax in fp32 (exp2 domain), row max (IEEE maximum) across
+//     the 4 lane groups via permlane swaps, lazy rescaling (the reference max
+//     only moves when a
 //     new max exceeds it by 2^8), masks applied only on stages that reach the
 //     block; keys past the sequence end load zeros (K) or are zeroed by the
 //     reader (V).
-//   * With several splits per (request, KV head) each workgroup stores its
-//     partial state and a second, small kernel merges the splits (a kernel
-//     boundary instead of device-scope fences, which on gfx950 write back and
-//     invalidate the L2 of the issuing XCD).
+//   * With several splits per unit (or units cut by the balanced schedule's
+//     ranges) each workgroup stores its partial state and a second, small
+//     kernel merges them (a kernel boundary instead of device-scope fences,
+//     which on gfx950 write back and invalidate the L2 of the issuing XCD).
 #include "kernels.h"
 
 namespace specattn {
