@@ -168,7 +168,7 @@ def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None, lacc=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build runs on a single MI355X); "
+        print(f"bench.py measures one GPU only (the hot path runs on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import torch

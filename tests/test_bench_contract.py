@@ -1,0 +1,66 @@
+"""The bench's host logic (CPU only): the one-GPU contract and the algorithmic
+byte and flop counts its roofline divides by, checked against counts written
+out by hand for small shapes."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from verify_attention_amd import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single" in r.stderr
+
+
+def test_attention_bytes_and_flops_by_hand():
+    cfg = synth.config(2, bs=2, block=4, hq=4, hkv=2, d=8, ctx_lo=3, ctx_hi=3)
+    seq = np.array([3, 5])
+    kv_bytes = 2 * ((3 + 4) + (5 + 4)) * 2 * 8 * 2      # K and V, 2 KV heads, D 8, bf16
+    qo_bytes = 2 * 2 * 4 * 4 * 8 * 2                    # Q read + O written
+    # CAUSAL: row i sees L keys of context and i + 1 block keys
+    pairs = sum(L * 4 + (1 + 2 + 3 + 4) for L in (3, 5))
+    b, f = bench.attn_alg_bytes_flops(cfg, seq)
+    assert b == kv_bytes + qo_bytes
+    assert f == 4 * 8 * pairs * 4
+    # BIDIR and MIXED (2 clean rows, then rows that see the whole block)
+    cb = synth.config(2, bs=2, block=4, hq=4, hkv=2, d=8, modes=(synth.BIDIR,))
+    assert bench.attn_alg_bytes_flops(cb, seq)[1] == 4 * 8 * sum(L * 4 + 16 for L in (3, 5)) * 4
+    cm = synth.config(2, bs=2, block=4, hq=4, hkv=2, d=8, modes=(synth.MIXED,), n_causal=2)
+    assert bench.attn_alg_bytes_flops(cm, seq)[1] == 4 * 8 * sum(L * 4 + (1 + 2 + 4 + 4)
+                                                                   for L in (3, 5)) * 4
+    # TREE: the set bits of the row masks
+    ct = synth.config(2, bs=2, block=4, hq=4, hkv=2, d=8, modes=(synth.TREE,))
+    masks = np.array([0b1, 0b11, 0b101, 0b1011], dtype=np.uint64)
+    assert bench.attn_alg_bytes_flops(ct, seq, masks)[1] == \
+        4 * 8 * sum(L * 4 + 1 + 2 + 2 + 3 for L in (3, 5)) * 4
+
+
+def test_accept_bytes_by_hand():
+    cfg = synth.config(2, bs=3, vocab=100, k_spec=5)
+    al = np.array([0, 5, 2])         # the all-accepted request streams the bonus row only
+    assert bench.accept_alg_bytes(cfg, al) == (2 + 1 + 2) * 100 * 4 + 3 * (2 * 5 + 1) * 4
+    assert bench.logits_accept_alg_bytes(cfg) == 3 * 11 * 100 * 4
+    assert bench.tree_accept_alg_bytes(synth.config(6, bs=2, vocab=100, block=8)) == \
+        2 * (100 + 8) * 4
+
+
+def test_traffic_table_matches_its_sources():
+    t = bench.measured_traffic("qwen3_8b_verify_bs32", "not-these-sources")
+    assert t is None
+    import json
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(path):
+        tj = json.load(open(path))
+        for key, w in tj["workloads"].items():
+            name, _, call = key.partition("/")
+            got = bench.measured_traffic(name, tj["kernel_src"], call or "block_attn")
+            assert got == int(w["traffic_bytes"])
