@@ -149,8 +149,16 @@ struct StageShape {
 __device__ __attribute__((aligned(64))) int g_zero16[16];
 
 constexpr int wait_vm_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (3 << 14);  // lgkmcnt(0) alone
 
-// s_waitcnt vmcnt(per * m) for a small runtime m (the immediate must be static).
+// s_waitcnt vmcnt(per * m) for a small runtime m (the immediate must be
+// static), then lgkmcnt(0). The lgkm wait, taken before the barrier that
+// licenses a ring slot's refill, (1) completes this wave's V fragment reads
+// of that slot, which set 1 leaves in flight across the barrier, and (2)
+// retires the compiler-visible LDS read of the next page offsets on every
+// path; left pending on any path, that read makes the compiler wait for all
+// LDS reads (the in-flight V fragments included) where its registers are
+// next written.
 template <int PER>
 __device__ __forceinline__ void wait_stages(int m) {
   switch (m) {
@@ -158,6 +166,7 @@ __device__ __forceinline__ void wait_stages(int m) {
     case 1: __builtin_amdgcn_s_waitcnt(wait_vm_imm(PER)); break;
     default: __builtin_amdgcn_s_waitcnt(wait_vm_imm(2 * PER)); break;
   }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 }
 
 // Per-lane constants of one wave's DMA pieces: the byte offset of the lane's
@@ -375,6 +384,16 @@ __device__ __forceinline__ void lds_read8_nowait(intx4* o, unsigned addr) {
       : "memory");
 }
 
+// Waits for reads issued by lds_read8_nowait. The parts pass through the
+// wait as operands, so no use of them can be scheduled above it.
+__device__ __forceinline__ void lds_wait8(intx4* o) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]),
+                 "+v"(o[6]), "+v"(o[7])
+               :
+               : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void lds_read(intx4* o, unsigned addr) {
   static_assert(N == 4 || N == 8 || N == 16, "part counts");
@@ -477,7 +496,7 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
   // mask and softmax below); wait for them before V is first touched
   constexpr bool vdefer = MT == 2 && StageShape<T, D>::NVP == 8;
   if (key0 + kStep > n_keys) {
-    if constexpr (vdefer) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (vdefer) lds_wait8(st.vp);
     zero_v_tail<T, D>(st.vp, key0, n_keys, grp);
   }
 
@@ -534,7 +553,7 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
     ws.l_run[t] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     pf[t] = Frag<T>::pack(pv);
   }
-  if constexpr (vdefer) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if constexpr (vdefer) lds_wait8(st.vp);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
