@@ -263,6 +263,13 @@ __device__ __forceinline__ void issue_stage(char* slot, int r, const DmaLanes<T,
     issue_dma<T, D, true>(slot, r, dl, hb, key0, n_keys);
 }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only, so its vector-memory loads and stores stay in flight across it
+// (__syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------------- LDS reads
 // N 16-byte fragment parts at lane-relative LDS address addr + 512 * i, then
 // one s_waitcnt. Inline asm keeps the compiler's LDS-DMA tracking from
@@ -611,9 +618,23 @@ __device__ __forceinline__ bool row_exists(const AttnArgs& a, int row0, int r) {
 // holds local row 16t + n, dims 32c + 8*grp .. +7. Row r of the head is block
 // token r / g, query head kvh * g + r % g. Both waves of a row slot hold the
 // same rows.
+// Empty softmax state: running max, sum and output of every row tile.
+template <typename T, int D, int MT>
+__device__ __forceinline__ void reset_state(WaveState<T, D, MT>& ws) {
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    ws.m_run[t] = kNegBig;
+    ws.l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) ws.acc[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Q fragments of the wave's row tiles (and each row's block row and tree
+// mask); with reset, an empty softmax state as well.
 template <typename T, int D, int MT>
 __device__ __forceinline__ void load_q(WaveState<T, D, MT>& ws, const AttnArgs& a, int b, int kvh,
-                                       int row0, int rs, int n, int grp) {
+                                       int row0, int rs, int n, int grp, bool reset = true) {
   const int rl0 = rs * 16 * MT;
   const T* qg = reinterpret_cast<const T*>(a.q);
 #pragma unroll
@@ -625,17 +646,13 @@ __device__ __forceinline__ void load_q(WaveState<T, D, MT>& ws, const AttnArgs& 
     const int rr = in ? r : 0;
     const int ii = rr / a.g, hh = rr - ii * a.g;
     ws.tmask[t] = a.mode == 3 ? a.tree[(a.tree_per_req ? (size_t)b * a.B : 0) + ii] : 0;
+    // a row past the group's end reads the head's first row: its scores stay
+    // finite, its softmax state is its own and its output is never written
     const T* src = qg + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hh) * D + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      ws.qf[t][c] = Frag<T>::load(src + 32 * c);
-      if (!in) ws.qf[t][c] = Frag<T>::zero();
-    }
-    ws.m_run[t] = kNegBig;
-    ws.l_run[t] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) ws.acc[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < D / 32; ++c) ws.qf[t][c] = Frag<T>::load(src + 32 * c);
   }
+  if (reset) reset_state(ws);
 }
 
 // Page-table entries of stage t of a request: the pages of keys 32 t and
@@ -647,6 +664,32 @@ __device__ __forceinline__ int2 table_pair(const AttnArgs& a, const int32_t* pta
 }
 
 // Sequence length of request b clamped to the page-table capacity.
+// Clean (causal) rows of request b's block in MIXED mode. b is wave-uniform:
+// the per-request count is read with a scalar load, whose wait (lgkmcnt)
+// does not drain the vector-memory queue.
+__device__ __forceinline__ int causal_rows(const AttnArgs& a, int b) {
+  if (!a.nc_per_req) return a.n_causal;
+  const auto* p = (const __attribute__((address_space(4))) int32_t*)a.nc_per_req;
+  return p[__builtin_amdgcn_readfirstlane(b)];
+}
+
+// Byte offsets of the (lo, hi) pages of stage t into window entry `slot`;
+// hi = lo when the stage has one page (P = 32) or its second page lies past
+// the sequence end. A page id outside the pool flags kErrSlot and reads page 0.
+template <typename T, int D>
+__device__ __forceinline__ void put_offsets(const AttnArgs& a, uint64_t* s_pgoff, int slot, int t,
+                                            int2 pg, int n_keys) {
+  const uint64_t page_bytes = (uint64_t)a.P * D * a.Hkv * sizeof(T);
+  const bool second = a.P == 16 && t * kStep + 16 < n_keys;
+  const bool bad_lo = (unsigned)pg.x >= (unsigned)a.num_pages;
+  const bool bad_hi = second && (unsigned)pg.y >= (unsigned)a.num_pages;
+  if (bad_lo || bad_hi) flag_error(a.err, kErrSlot);
+  const uint64_t lo = (uint64_t)(bad_lo ? 0 : pg.x) * page_bytes;
+  const uint64_t hi = second ? (uint64_t)(bad_hi ? 0 : pg.y) * page_bytes : lo;
+  reinterpret_cast<uint4*>(s_pgoff)[slot] =
+      uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+
 __device__ __forceinline__ int clamped_len(const AttnArgs& a, int b, bool flag) {
   int L = a.seq_lens[b];
   const int cap = a.max_pages * a.P - a.B;
@@ -660,45 +703,36 @@ __device__ __forceinline__ int clamped_len(const AttnArgs& a, int b, bool flag) 
 // Streams stages [s_lo, s_hi) of unit (b, kvh), length L, through the ring
 // into this wave's softmax state. Thread tid stages the page offsets of
 // stage tid of each window (first window: the prefetched `first` entries).
-template <typename T, int D, int MT>
+template <typename T, int D, int MT, bool STAGED = false>
 __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const AttnArgs& a,
                                               const WaveCtx<T, D>& c, char* s_ring,
                                               uint64_t* s_pgoff, int b, int kvh, int row0, int L,
-                                              int s_lo, int s_hi, int2 first) {
+                                              int nc, int s_lo, int s_hi, int2 first) {
   using SS = StageShape<T, D>;
   constexpr int NSP = SS::NSP;
   static_assert(kPageWin == kWave * kWaves, "one thread per staged stage");
   const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)kvh * a.P * D * sizeof(T);
   const char* vbase = reinterpret_cast<const char*>(a.v) + (size_t)kvh * a.P * D * sizeof(T);
-  const uint64_t page_bytes = (uint64_t)a.P * D * a.Hkv * sizeof(T);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
   const int n_keys = L + a.B;
-  const int nc = a.nc_per_req ? a.nc_per_req[b] : a.n_causal;
   const bool has_rows = row_exists(a, row0, c.rs * 16 * MT);
   const int set = c.set;
 
   for (int w0 = s_lo; w0 < s_hi; w0 += kPageWin) {
     const int w1 = min(s_hi, w0 + kPageWin);
     const int ns = w1 - w0;
-    __syncthreads();  // the previous window (or unit) is fully consumed
-    // byte offsets of the (lo, hi) pages of every stage of the window; hi = lo
-    // when the stage has one page (P = 32) or its second page lies past the
-    // sequence end
-    if (c.tid < ns) {
-      const int2 pg = w0 == s_lo ? first : table_pair(a, ptab, w0 + c.tid);
-      const bool second = a.P == 16 && (w0 + c.tid) * kStep + 16 < n_keys;
-      const bool bad_lo = (unsigned)pg.x >= (unsigned)a.num_pages;
-      const bool bad_hi = second && (unsigned)pg.y >= (unsigned)a.num_pages;
-      if (bad_lo || bad_hi) flag_error(a.err, kErrSlot);
-      const uint64_t lo = (uint64_t)(bad_lo ? 0 : pg.x) * page_bytes;
-      const uint64_t hi = second ? (uint64_t)(bad_hi ? 0 : pg.y) * page_bytes : lo;
-      reinterpret_cast<uint4*>(s_pgoff)[c.tid] =
-          uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-    }
-    // Q and the page ids are in: from here on the only vector-memory loads in
-    // flight are the ring's DMAs, which the waits below count by hand
-    __builtin_amdgcn_s_waitcnt(wait_vm_imm(0));
-    __syncthreads();
+    lds_barrier();  // the previous window (or unit) is fully consumed
+    // the page offsets of every stage of the window (STAGED: the caller has
+    // already written the first window's)
+    if (c.tid < ns && !(STAGED && w0 == s_lo))
+      put_offsets<T, D>(a, s_pgoff, c.tid, w0 + c.tid,
+                        w0 == s_lo ? first : table_pair(a, ptab, w0 + c.tid), n_keys);
+    // The waits below count this wave's ring DMAs by hand. Older vector-memory
+    // operations may still be in flight here (the Q loads, the previous
+    // piece's output stores); they only make those waits longer: loads
+    // complete in issue order and every older operation counts against a
+    // wait, so none can pass before the DMAs it waits for have landed.
+    lds_barrier();
 
     // pair u holds window stages 2u (set 0) and 2u + 1 (set 1) in ring slot u % NSP
     const int npairs = (ns + 1) >> 1;
@@ -755,17 +789,18 @@ __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const Att
 // Merges the two key halves of every row slot through LDS, then writes the
 // unit's rows: normalised output (part < 0) or the unnormalised partial
 // state into partial slot `part`.
-template <typename T, int D, int MT>
+template <typename T, int D, int MT, typename F>
 __device__ __forceinline__ void finish_unit(WaveState<T, D, MT>& ws, const AttnArgs& a,
                                             const WaveCtx<T, D>& c, char* s_ring, int b, int kvh,
-                                            int row0, int part) {
+                                            int row0, int part, F&& between) {
   using SS = StageShape<T, D>;
   static_assert(kRowSlots * (D / 16) * MT * 1024 + kRowSlots * MT * 512 <= SS::NSP * SS::PAIR,
                 "merge buffers fit the ring");
   const int rl0 = c.rs * 16 * MT;
   const bool has_rows = row_exists(a, row0, rl0);
   const int lane = c.lane;
-  __syncthreads();  // every stage consumed: the ring is free
+  lds_barrier();  // every stage consumed: the ring and the page offsets are free
+  between();
   floatx4* x_acc = reinterpret_cast<floatx4*>(s_ring) + (size_t)c.rs * (D / 16) * MT * 64;
   float2* x_ml = reinterpret_cast<float2*>(s_ring + kRowSlots * (D / 16) * MT * 1024) +
                  (size_t)c.rs * MT * 64;
@@ -777,7 +812,7 @@ __device__ __forceinline__ void finish_unit(WaveState<T, D, MT>& ws, const AttnA
       x_ml[t * 64 + lane] = float2{ws.m_run[t], ws.l_run[t]};
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (c.set == 1 || !has_rows) return;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -852,8 +887,9 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
   const int L = clamped_len(a, b, c.tid == 0 && split == 0);
   const int n_steps = (L + a.B + kStep - 1) / kStep;
   const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
-  stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, u.row0, L, s_lo, s_hi, first);
-  finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, u.row0, a.splits == 1 ? -1 : lb);
+  const int nc = causal_rows(a, b);
+  stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, u.row0, L, nc, s_lo, s_hi, first);
+  finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, u.row0, a.splits == 1 ? -1 : lb, [] {});
 }
 
 // ------------------------------------------------------- balanced schedule
@@ -904,8 +940,10 @@ __device__ __forceinline__ int block_exclusive_scan_int(int x, int* s_tmp, int* 
 }
 
 // s_pre[b] = pairs of all units of requests before b (b = 0 .. bs); returns
-// the total. Thread tid covers a contiguous run of requests.
-__device__ int balanced_prefix(const AttnArgs& a, int* s_pre, int* s_tmp, bool flag) {
+// the total. Thread tid covers a contiguous run of requests. With s_len, the
+// clamped lengths are kept there too.
+__device__ int balanced_prefix(const AttnArgs& a, int* s_pre, int* s_tmp, bool flag,
+                               int* s_len = nullptr) {
   const int nthr = blockDim.x, tid = threadIdx.x;
   const int per = (a.bs + nthr - 1) / nthr;
   const int b0 = min(a.bs, tid * per), b1 = min(a.bs, b0 + per);
@@ -915,7 +953,9 @@ __device__ int balanced_prefix(const AttnArgs& a, int* s_pre, int* s_tmp, bool f
   int run = block_exclusive_scan_int(sum, s_tmp, &total);
   for (int b = b0; b < b1; ++b) {
     s_pre[b] = run;
-    run += a.Hkv * unit_pairs(a, clamped_len(a, b, false));
+    const int L = clamped_len(a, b, false);
+    if (s_len) s_len[b] = L;
+    run += a.Hkv * unit_pairs(a, L);
   }
   if (tid == 0) s_pre[a.bs] = total;
   __syncthreads();
@@ -943,30 +983,42 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   __shared__ __attribute__((aligned(1024))) char s_ring[SS::NSP * SS::PAIR];
   __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];
   __shared__ int s_pre[kMaxBalancedBatch + 1];
+  __shared__ int s_len[kMaxBalancedBatch];
   __shared__ int s_tmp[kWaves];
 
   const WaveCtx<T, D> c = wave_ctx<T, D>(a, s_ring);
   const int2 tr = team_of(a, blockIdx.x, gridDim.x);
   const int T_ = gridDim.x / a.RG, w = tr.x, rg = tr.y, row0 = rg * a.M;
-  const int total = balanced_prefix(a, s_pre, s_tmp, blockIdx.x == 0);
+  const int total = balanced_prefix(a, s_pre, s_tmp, blockIdx.x == 0, s_len);
   const int start = range_start(total, w, T_), end = range_start(total, w + 1, T_);
   if (start >= end) return;
   int b = request_of(s_pre, a.bs, start);
-  int L = clamped_len(a, b, false);
+  int L = s_len[b];
   int np = unit_pairs(a, L);
   int kvh = (start - s_pre[b]) / np;
   int off = start - s_pre[b] - kvh * np;  // first pair inside the unit
+  // stages [x, y) of the piece that starts at global pair cur
+  auto stage_range = [&](int cur) {
+    return int2{2 * off, min((L + a.B + kStep - 1) / kStep, 2 * (off + min(np - off, end - cur)))};
+  };
+  // the page offsets of the first window of a piece (stages r.x ..) from
+  // its page ids pg (thread tid: stage r.x + tid)
+  auto stage_first = [&](int2 r, int2 pg) {
+    if (c.tid < min(r.y, r.x + kPageWin) - r.x)
+      put_offsets<T, D>(a, s_pgoff, c.tid, r.x + c.tid, pg, L + a.B);
+  };
+  WaveState<T, D, MT> ws;
+  load_q<T, D, MT>(ws, a, b, kvh, row0, c.rs, c.n, c.grp);
+  int nc = causal_rows(a, b);
+  int2 range = stage_range(start);
+  stage_first(range, table_pair(a, a.page_table + (size_t)b * a.max_pages, range.x + c.tid));
   for (int cur = start; cur < end;) {
     const int seg = min(np - off, end - cur);
     const bool whole = off == 0 && seg == np;
     const int part = whole ? -1 : (cur == start ? 2 * w : 2 * w + 1) * a.RG + rg;
-    const int s_lo = 2 * off;
-    const int s_hi = min((L + a.B + kStep - 1) / kStep, 2 * (off + seg));
-    WaveState<T, D, MT> ws;
-    load_q<T, D, MT>(ws, a, b, kvh, row0, c.rs, c.n, c.grp);
-    const int2 first = table_pair(a, a.page_table + (size_t)b * a.max_pages, s_lo + c.tid);
-    stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, row0, L, s_lo, s_hi, first);
-    finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, row0, part);
+    stream_stages<T, D, MT, true>(ws, a, c, s_ring, s_pgoff, b, kvh, row0, L, nc, range.x, range.y,
+                                  int2{0, 0});
+    const int fb = b, fkvh = kvh;
     cur += seg;
     off += seg;
     if (off == np) {  // next unit
@@ -974,11 +1026,29 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
       if (++kvh == a.Hkv) {
         kvh = 0;
         if (++b < a.bs) {
-          L = clamped_len(a, b, false);
+          L = s_len[b];
           np = unit_pairs(a, L);
         }
       }
     }
+    // The next piece's page ids, Q fragments and causal-row count are
+    // requested before this piece's rows are merged and stored, and its
+    // first window's page offsets are written during the merge, before any
+    // store is issued: the next piece then starts its DMAs at once, their
+    // latency overlapping that of the stores (the Q registers are free once
+    // the stages are streamed).
+    const bool next = cur < end;
+    int2 pg{0, 0};
+    if (next) {
+      range = stage_range(cur);
+      pg = table_pair(a, a.page_table + (size_t)b * a.max_pages, range.x + c.tid);
+      load_q<T, D, MT>(ws, a, b, kvh, row0, c.rs, c.n, c.grp, false);
+      nc = causal_rows(a, b);
+    }
+    finish_unit<T, D, MT>(ws, a, c, s_ring, fb, fkvh, row0, part, [&] {
+      if (next) stage_first(range, pg);
+    });
+    reset_state(ws);
   }
 }
 
