@@ -611,13 +611,16 @@ __global__ __launch_bounds__(kAccThreads) void argmax_rows_kernel(const T* x, in
     const int nv = V / kVec;
     const vecT* rv = reinterpret_cast<const vecT*>(row);
     int bvec = -1;  // first vector of this thread whose maximum reached bv
-    int e = threadIdx.x;
-    for (; e + (kIn - 1) * kAccThreads < nv; e += kIn * kAccThreads) {
+    // the last batch is partial: its loads past the row end are skipped, so
+    // the tail keeps kIn loads in flight per lane like the rest
+    for (int e = threadIdx.x; e < nv; e += kIn * kAccThreads) {
       vecT v[kIn];
 #pragma unroll
-      for (int k = 0; k < kIn; ++k) v[k] = __builtin_nontemporal_load(rv + e + k * kAccThreads);
+      for (int k = 0; k < kIn; ++k)
+        if (e + k * kAccThreads < nv) v[k] = __builtin_nontemporal_load(rv + e + k * kAccThreads);
 #pragma unroll
       for (int k = 0; k < kIn; ++k) {
+        if (e + k * kAccThreads >= nv) break;
         float m = to_f32(v[k][0]);
 #pragma unroll
         for (int j = 1; j < kVec; ++j) m = fmaxf(m, to_f32(v[k][j]));
@@ -627,15 +630,6 @@ __global__ __launch_bounds__(kAccThreads) void argmax_rows_kernel(const T* x, in
         bv = up ? m : bv;
         bvec = up ? e + k * kAccThreads : bvec;
       }
-    }
-    for (; e < nv; e += kAccThreads) {
-      const vecT v = rv[e];
-      float m = to_f32(v[0]);
-#pragma unroll
-      for (int j = 1; j < kVec; ++j) m = fmaxf(m, to_f32(v[j]));
-      const bool up = m > bv || (bvec < 0 && m == bv);
-      bv = up ? m : bv;
-      bvec = up ? e : bvec;
     }
     if (bvec >= 0) {
       const vecT v = rv[bvec];

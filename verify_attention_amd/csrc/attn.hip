@@ -49,6 +49,12 @@
 //     ranges) each workgroup stores its partial state and a second, small
 //     kernel merges them (a kernel boundary instead of device-scope fences,
 //     which on gfx950 write back and invalidate the L2 of the issuing XCD).
+//   * The balanced schedule hands each workgroup a run of unit pieces. At a
+//     piece boundary the next piece's page ids and Q fragments are requested
+//     before the finished piece's rows are merged and stored, and the next
+//     piece's first page offsets are staged during the merge; the barriers
+//     there wait for LDS traffic only, so the next piece's DMAs go out while
+//     the stores are still in flight.
 #include "kernels.h"
 
 namespace specattn {
