@@ -315,3 +315,58 @@ def test_full_size_sampled_rows(gpu_lib, cid):
     for (b, i, h) in rows:
         assert np.max(np.abs(o[b, i, h] - ro[b, i, h])) <= TOL[cfg.dtype], (b, i, h)
         assert abs(lse[b, i, h] - rl[b, i, h]) <= LSE_TOL[cfg.dtype], (b, i, h)
+
+
+def compact_for_requests(x, reqs):
+    """The inputs of requests `reqs` alone, over a pool holding only their
+    pages (the page table renumbered), so that a float64 copy stays small."""
+    need = [-(-(int(x.seq_lens[b]) + x.cfg.block) // x.cfg.page) for b in reqs]
+    pages = np.unique(np.concatenate([x.page_table[b, :n] for b, n in zip(reqs, need)]))
+    remap = np.full(x.num_pages, -1, dtype=np.int64)
+    remap[pages] = np.arange(len(pages))
+    table = np.zeros((len(reqs), x.max_pages), dtype=np.int32)
+    for r, (b, n) in enumerate(zip(reqs, need)):
+        table[r, :n] = remap[x.page_table[b, :n]]
+    return synth.AttnInputs(x.cfg, x.seq_lens[reqs], table, len(pages), x.q[reqs],
+                            x.k_pool[pages], x.v_pool[pages], x.n_causal[reqs])
+
+
+SPANS = [
+    # (name, config id, overrides, mode): requests of 17-18k keys (more than
+    # one 512-stage window of staged page offsets) and batches whose balanced
+    # shares (units x stages / 256) exceed 512 stages, so that pieces cross
+    # windows; one and two row tiles per wave
+    ("g2_b16_d64_causal", 2, dict(bs=64, hq=8, hkv=4, d=64, ctx_lo=17000, ctx_hi=18000),
+     synth.CAUSAL),
+    ("g4_b32_d64_bidir", 3, dict(bs=32, hq=32, hkv=8, d=64, ctx_lo=17000, ctx_hi=18000),
+     synth.BIDIR),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,mode", SPANS, ids=[s[0] for s in SPANS])
+def test_balanced_pieces_span_page_windows(gpu_lib, name, cid, over, mode):
+    """A balanced piece's first window of page offsets is staged during the
+    previous piece's merge, its later windows in place; sampled rows (every
+    request's first and last block row included) against the reference."""
+    cfg = synth.config(cid, **over)
+    print_case("block_attn balanced, multi-window pieces", name, cfg)
+    x = synth.make_attn_inputs(cfg, seed=41 + cid)
+    case = AttnCase(x)
+    units = cfg.bs * cfg.hkv
+    assert units * ((case.max_kv + 31) // 32) >= 32768
+    assert units * ((int(x.seq_lens.min()) + cfg.block) // 32) // 256 > 512
+    o, lse = run(case, mode)
+    assert np.isfinite(o).all()
+    rng = np.random.default_rng(41 + cid)
+    reqs = sorted({int(b) for b in rng.choice(cfg.bs, size=4, replace=False)} |
+                  {int(np.argmax(x.seq_lens))})
+    sub = compact_for_requests(x, reqs)
+    rows = [(r, i, h) for r in range(len(reqs)) for i in (0, cfg.block - 1)
+            for h in (0, cfg.hq - 1)]
+    rows += [(r, int(rng.integers(cfg.block)), int(rng.integers(cfg.hq))) for r in range(len(reqs))]
+    ro, rl = oracle.block_attn_rows(sub.as_f64("q"), sub.as_f64("k_pool"), sub.as_f64("v_pool"),
+                                    sub.page_table, sub.seq_lens, mode, cfg.n_causal, rows=rows)
+    for (r, i, h) in rows:
+        b = reqs[r]
+        assert np.max(np.abs(o[b, i, h] - ro[r, i, h])) <= TOL[cfg.dtype], (b, i, h)
+        assert abs(lse[b, i, h] - rl[r, i, h]) <= LSE_TOL[cfg.dtype], (b, i, h)
