@@ -12,10 +12,12 @@
 // exp((l - l_max) / T) and keeping the shortest rank prefix whose mass reaches
 // top_p; the linear accept rule then runs on the processed rows.
 //
-// Three kernels:
-//   * tile_max_kernel streams every row once (the HBM-bound pass) and stores
-//     the maximum of each 64-entry tile;
-//   * row_topk_kernel, one workgroup per row: tau, the top_k-th largest of
+// Three passes, launched over the rows in two halves (the second half's
+// tile maxima computed in the launch that ranks the first half, so that the
+// latency-bound ranking runs beside the HBM-bound stream):
+//   * tile maxima stream every row once (the HBM-bound pass) and store the
+//     maximum of each 64-entry tile;
+//   * the ranking, one workgroup per row: tau, the top_k-th largest of
 //     256 per-thread maxima of tile maxima rounded down to 16 key bits, is a
 //     logit that at least top_k entries reach, so every top-k entry lies in a
 //     tile whose maximum is at least tau. Only those tiles are read again;
@@ -79,17 +81,16 @@ __device__ __forceinline__ bool ranks_before(float v, int i, float w, int j) {
 // tile (16 for float, 8 for bf16) reduce with xor shuffles; NaN entries and
 // entries past V count as -inf. kTileIters loads per lane are in flight.
 template <typename T>
-__global__ __launch_bounds__(kSampThreads) void tile_max_kernel(SampArgs a) {
+__device__ __forceinline__ void tile_max_block(const SampArgs& a, int row, int part) {
   constexpr int E = 16 / sizeof(T);
   constexpr int LPT = kTile / E;
   constexpr int TPI = kSampThreads / LPT;
   typedef T vecT __attribute__((ext_vector_type(E)));
-  const int row = blockIdx.x;
   const T* x = row_ptr<T>(a, row);
   const int V = a.V;
   const bool vec = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (V % E == 0);
   const int tid = threadIdx.x;
-  const int tile0 = blockIdx.y * (TPI * kTileIters) + tid / LPT;
+  const int tile0 = part * (TPI * kTileIters) + tid / LPT;
   const int sub = (tid % LPT) * E;
   float m[kTileIters];
   if (vec) {
@@ -237,8 +238,7 @@ __device__ int topk_by_rounds(const T* x, int V, int k, float* s_v, int* s_i, fl
 // One workgroup per row: exact top-k, then temperature and top-p (wave 0),
 // written as kept ids / probabilities in rank order and the kept count.
 template <typename T>
-__global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a) {
-  const int row = blockIdx.x;
+__device__ __forceinline__ void row_topk_block(const SampArgs& a, int row) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.top_k, V = a.V, ntiles = a.ntiles;
   const T* x = row_ptr<T>(a, row);
@@ -505,16 +505,51 @@ __global__ __launch_bounds__(64) void accept_logits_kernel(SampArgs a) {
     a.out_tokens[(size_t)b * (K + 1) + lane] = lane < j ? d : (lane == j ? tok : -1);
 }
 
+// Grid (rows, blocks per row): tile maxima of rows t0 ...
+template <typename T>
+__global__ __launch_bounds__(kSampThreads) void tile_max_kernel(SampArgs a, int t0) {
+  tile_max_block<T>(a, t0 + blockIdx.x, blockIdx.y);
+}
+
+// One block per row: the ranks of rows k0 ...
+template <typename T>
+__global__ __launch_bounds__(kSampThreads) void row_topk_kernel(SampArgs a, int k0) {
+  row_topk_block<T>(a, k0 + blockIdx.x);
+}
+
+// Blocks [0, nk) rank rows k0 .., one per block, whose tile maxima an earlier
+// launch stored; the blocks after them compute tile maxima of rows t0 ..,
+// bpr blocks per row. One launch thus ranks one part of the rows while
+// streaming another (the ranking blocks, dispatched first, start at once).
+template <typename T>
+__global__ __launch_bounds__(kSampThreads) void tile_max_topk_kernel(SampArgs a, int k0, int nk,
+                                                                     int t0, int bpr) {
+  const int x = blockIdx.x;
+  if (x < nk) row_topk_block<T>(a, k0 + x);
+  else tile_max_block<T>(a, t0 + (x - nk) / bpr, (x - nk) % bpr);
+}
+
 // ------------------------------------------------------------ launch
+// The rows are streamed in two halves: the second half's tile maxima are
+// computed in the same launch that ranks the first half, so the ranking's
+// latency-bound blocks run beside the HBM-bound stream.
 template <typename T>
 static hipError_t launch_filter_t(const SampArgs& a, hipStream_t stream) {
   constexpr int TPB = kSampThreads / (kTile / (16 / sizeof(T))) * kTileIters;  // tiles per block
-  const int rows = a.R1 + a.R2;
-  hipLaunchKernelGGL(tile_max_kernel<T>, dim3(rows, (a.ntiles + TPB - 1) / TPB),
-                     dim3(kSampThreads), 0, stream, a);
+  const int rows = a.R1 + a.R2, h = (rows + 1) / 2;
+  const int bpr = (a.ntiles + TPB - 1) / TPB;
+  // tile maxima of rows [0, h)
+  hipLaunchKernelGGL(tile_max_kernel<T>, dim3(h, bpr), dim3(kSampThreads), 0, stream, a, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(row_topk_kernel<T>, dim3(rows), dim3(kSampThreads), 0, stream, a);
+  // the ranks of rows [0, h) beside the tile maxima of rows [h, rows)
+  hipLaunchKernelGGL(tile_max_topk_kernel<T>, dim3(h + (rows - h) * bpr), dim3(kSampThreads), 0,
+                     stream, a, 0, h, h, bpr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // ranks of rows [h, rows)
+  if (rows > h)
+    hipLaunchKernelGGL(row_topk_kernel<T>, dim3(rows - h), dim3(kSampThreads), 0, stream, a, h);
   return hipGetLastError();
 }
 
