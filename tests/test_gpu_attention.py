@@ -370,3 +370,43 @@ def test_balanced_pieces_span_page_windows(gpu_lib, name, cid, over, mode):
         b = reqs[r]
         assert np.max(np.abs(o[b, i, h] - ro[r, i, h])) <= TOL[cfg.dtype], (b, i, h)
         assert abs(lse[b, i, h] - rl[r, i, h]) <= LSE_TOL[cfg.dtype], (b, i, h)
+
+
+ROW_GROUPS = [
+    # (name, config id, overrides, mode, per-request clean counts): 256 query
+    # rows per KV head (two row groups of 128) in the other element types and
+    # head sizes
+    ("f32_d64_g2_b128_causal", 1, dict(bs=3, hq=4, hkv=2, block=128, ctx_lo=200, ctx_hi=700),
+     synth.CAUSAL, False),
+    ("bf16_d64_g4_b64_mixed_nc", 3, dict(bs=3, hq=8, hkv=2, d=64, block=64, n_causal=20,
+                                         ctx_lo=100, ctx_hi=900), synth.MIXED, True),
+    ("f32_d128_g8_b32_bidir", 1, dict(bs=2, hq=8, hkv=1, d=128, block=32, ctx_lo=100,
+                                      ctx_hi=400), synth.BIDIR, False),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,mode,nc_req", ROW_GROUPS, ids=[r[0] for r in ROW_GROUPS])
+def test_row_groups_types_and_sizes(gpu_lib, name, cid, over, mode, nc_req):
+    """Row groups under the split plan, a bound loose enough to split every
+    unit many ways, and the balanced schedule, every row against the
+    reference."""
+    cfg = synth.config(cid, **over)
+    print_case("block_attn row groups", name, cfg)
+    assert (cfg.hq // cfg.hkv) * cfg.block > 128
+    x = synth.make_attn_inputs(cfg, seed=51 + cid, n_causal_per_req=nc_req)
+    case = AttnCase(x)
+    outs = []
+    for max_kv in (None, 20000, 65536 * 4):
+        o, lse = run(case, mode, max_kv=max_kv, nc_per_req=nc_req)
+        if nc_req:
+            for b in range(cfg.bs):
+                one = synth.AttnInputs(cfg, x.seq_lens[b:b + 1], x.page_table[b:b + 1],
+                                       x.num_pages, x.q[b:b + 1], x.k_pool, x.v_pool,
+                                       x.n_causal[b:b + 1])
+                ro, rl = ref_dense(one, mode, int(x.n_causal[b]))
+                assert np.max(np.abs(o[b:b + 1] - ro)) <= TOL[cfg.dtype]
+                assert np.max(np.abs(lse[b:b + 1] - rl)) <= LSE_TOL[cfg.dtype]
+        else:
+            check_all(x, o, lse, mode, cfg.n_causal)
+        outs.append(o)
+    assert np.max(np.abs(outs[0] - outs[2])) <= (1e-5 if cfg.dtype == "f32" else 2 ** -7)
