@@ -288,3 +288,14 @@ def test_accept_tree_commit_rejects_bad_arguments(lib):
     assert atc(par=None) == b.SPEC_EINVAL
     assert atc(V=600000) == b.SPEC_ENOTSUP
     assert atc(ws_bytes=ws - 1) == b.SPEC_ENOSPC
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library the entry points raise: there is no other
+    implementation behind the names."""
+    monkeypatch.setattr(b, "_LIB", None)
+    monkeypatch.setattr(b, "lib_path", lambda: str(tmp_path / "libspecattn.so"))
+    with pytest.raises(b.SpecError, match="not built"):
+        b.load()
+    with pytest.raises(b.SpecError, match="not built"):
+        va.attn_workspace_bytes(2, 16, 32, 8, 128, 1024)
