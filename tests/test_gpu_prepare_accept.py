@@ -167,6 +167,24 @@ def test_accept_matches_reference(gpu_lib, cid, bs):
     assert differ <= ties
 
 
+def test_accept_at_the_largest_k(gpu_lib):
+    """K = 63, the largest the call takes: half of the requests have q = p, so
+    every test passes and the bonus comes from the 64th row of p; the others
+    reject early."""
+    cfg = synth.config(1, k_spec=63)
+    print_case("accept K = 63")
+    x = synth.make_accept_inputs(cfg, seed=63, bs=64)
+    x.q[:32] = x.p[:32, :63]
+    seq = synth.context_lengths(synth.config(1, bs=64), 63)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = run_accept(x, seq, err=err)
+    ref = oracle.accept_batch(x.p, x.q, x.draft, x.u, seq)
+    assert (ref["accept_len"][:32] == 63).all()
+    ties, differ = compare_accept(got, ref)
+    assert int(err.item()) == 0
+    assert differ <= ties
+
+
 def test_accept_all_accepted_and_workspace_reuse(gpu_lib):
     cfg = synth.config(2, bs=8)
     print_case("accept all accepted")

@@ -54,7 +54,7 @@ PARAMS = [(1.0, 50, 0.95), (0.7, 64, 0.9), (1.3, 1, 0.5), (1.0, 20, 1.0), (2.0, 
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [151936, 5003, 64, 30])
+@pytest.mark.parametrize("V", [524288, 151936, 5003, 64, 30])
 def test_filter_matches_reference(V, dtype):
     rng = np.random.default_rng(V)
     rows = 12
