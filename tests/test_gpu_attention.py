@@ -410,3 +410,22 @@ def test_row_groups_types_and_sizes(gpu_lib, name, cid, over, mode, nc_req):
             check_all(x, o, lse, mode, cfg.n_causal)
         outs.append(o)
     assert np.max(np.abs(outs[0] - outs[2])) <= (1e-5 if cfg.dtype == "f32" else 2 ** -7)
+
+
+def test_single_token_block_modes_agree(gpu_lib):
+    """B = 1 is single-token decode in every mask mode: the outputs agree bit
+    for bit; with an empty context the output is the block's own V row."""
+    cfg = synth.config(2, bs=4, block=1, ctx_lo=1, ctx_hi=300)
+    print_case("block_attn single-token block, every mode", cfg)
+    x = synth.make_attn_inputs(cfg, seed=61)
+    x.seq_lens[0] = 0
+    case = AttnCase(x)
+    outs = [run(case, m) for m in (synth.BIDIR, synth.CAUSAL, synth.MIXED)]
+    for o, lse in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(lse, outs[0][1])
+    check_all(x, outs[0][0], outs[0][1], synth.CAUSAL, 0)
+    v = x.as_f64("v_pool")[x.page_table[0, 0], :, :, 0]     # [Hkv, D]: key 0 of request 0
+    g = cfg.hq // cfg.hkv
+    for h in range(cfg.hq):
+        assert np.array_equal(outs[0][0][0, 0, h], v[h // g]), h
+
