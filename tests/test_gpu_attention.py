@@ -429,3 +429,28 @@ def test_single_token_block_modes_agree(gpu_lib):
     for h in range(cfg.hq):
         assert np.array_equal(outs[0][0][0, 0, h], v[h // g]), h
 
+
+@pytest.mark.parametrize("cid,over", [(5, dict(bs=3, ctx_lo=50, ctx_hi=600)),
+                                      (3, dict(bs=2, hq=8, hkv=2, block=64, ctx_lo=10,
+                                               ctx_hi=500))],
+                         ids=["one_tile", "two_tiles_row_groups"])
+def test_mixed_limits_are_bidir_and_causal(gpu_lib, cid, over):
+    """MIXED with no clean row is BIDIR and with every row clean is CAUSAL,
+    bit for bit."""
+    cfg = synth.config(cid, **over)
+    print_case("block_attn MIXED limits", cid, cfg)
+    x = synth.make_attn_inputs(cfg, seed=71)
+    case = AttnCase(x)
+
+    def attn(mode, nc):
+        lse = torch.empty((cfg.bs, cfg.block, cfg.hq), dtype=torch.float32, device="cuda")
+        o = va.block_attn(mode, case.q, case.k, case.v, case.table, case.seq, case.max_kv,
+                          n_causal=nc, lse=lse)
+        torch.cuda.synchronize()
+        return to_f64(o), lse.cpu().numpy()
+
+    for nc, mode in ((0, synth.BIDIR), (cfg.block, synth.CAUSAL)):
+        om, lm = attn(synth.MIXED, nc)
+        oo, lo = attn(mode, 0)
+        assert np.array_equal(om, oo) and np.array_equal(lm, lo), (nc, mode)
+
