@@ -454,3 +454,23 @@ def test_mixed_limits_are_bidir_and_causal(gpu_lib, cid, over):
         oo, lo = attn(mode, 0)
         assert np.array_equal(om, oo) and np.array_equal(lm, lo), (nc, mode)
 
+
+def test_page_permutation_changes_nothing(gpu_lib):
+    """Moving the physical pages, with their page-table entries, changes no
+    bit of the output (default plan and balanced schedule)."""
+    cfg = synth.config(4, bs=6, ctx_lo=100, ctx_hi=1500)
+    print_case("block_attn page permutation", cfg)
+    x = synth.make_attn_inputs(cfg, seed=81)
+    perm = np.random.default_rng(81).permutation(x.num_pages)
+    k2 = np.empty_like(x.k_pool)
+    v2 = np.empty_like(x.v_pool)
+    k2[perm] = x.k_pool
+    v2[perm] = x.v_pool
+    t2 = np.where(x.page_table >= 0, perm[np.maximum(x.page_table, 0)], x.page_table)
+    y = synth.AttnInputs(cfg, x.seq_lens, t2.astype(np.int32), x.num_pages, x.q, k2, v2,
+                         x.n_causal)
+    for max_kv in (None, 65536):
+        o1, l1 = run(AttnCase(x), synth.CAUSAL, max_kv=max_kv)
+        o2, l2 = run(AttnCase(y), synth.CAUSAL, max_kv=max_kv)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), max_kv
+
