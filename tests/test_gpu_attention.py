@@ -474,3 +474,16 @@ def test_page_permutation_changes_nothing(gpu_lib):
         o2, l2 = run(AttnCase(y), synth.CAUSAL, max_kv=max_kv)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2), max_kv
 
+
+def test_last_block_row_is_the_same_in_causal_and_bidir(gpu_lib):
+    """The block's last row sees the whole block under both masks: its output
+    and LSE agree bit for bit."""
+    cfg = synth.config(3, bs=3, ctx_lo=20, ctx_hi=700)
+    print_case("block_attn last row, CAUSAL vs BIDIR", cfg)
+    x = synth.make_attn_inputs(cfg, seed=93)
+    case = AttnCase(x)
+    oc, lc = run(case, synth.CAUSAL)
+    ob, lb = run(case, synth.BIDIR)
+    assert np.array_equal(oc[:, -1], ob[:, -1]) and np.array_equal(lc[:, -1], lb[:, -1])
+    assert not np.array_equal(oc[:, 0], ob[:, 0])
+

@@ -245,3 +245,29 @@ def test_greedy_accept(gpu_lib):
     got = run_accept(x, s2, greedy=True)
     ref = oracle.accept_batch(x.p, x.q, x.draft, x.u, s2, greedy=True)
     compare_accept(got, ref, allow_ties=False)
+
+
+def test_one_hot_rejection_sampling_is_the_greedy_rule(gpu_lib):
+    """With one-hot p and q (q at the drafted token) the rejection-sampling
+    accept reproduces the greedy rule exactly, whatever the uniforms: a test
+    passes iff the draft is p's token, and the residual (or the bonus row) is
+    one-hot at p's token."""
+    rng = np.random.default_rng(91)
+    bs, K, V = 64, 15, 1000
+    print_case("accept one-hot = greedy", bs, K, V)
+    tgt = rng.integers(V, size=(bs, K + 1))
+    draft = np.where(rng.random((bs, K)) < 0.7, tgt[:, :K],
+                     rng.integers(V, size=(bs, K))).astype(np.int32)
+    p = np.zeros((bs, K + 1, V), np.float32)
+    p[np.arange(bs)[:, None], np.arange(K + 1), tgt] = 1.0
+    q = np.zeros((bs, K, V), np.float32)
+    q[np.arange(bs)[:, None], np.arange(K), draft] = 1.0
+    u = rng.random((bs, K + 1), dtype=np.float32)
+    seq = rng.integers(1, 500, size=bs).astype(np.int32)
+    st = va.accept(to_dev(p), to_dev(q), to_dev(draft), to_dev(u), to_dev(seq))
+    gr = va.accept(to_dev(p), None, to_dev(draft), None, to_dev(seq), greedy=True)
+    torch.cuda.synchronize()
+    for key in ("accept_len", "commit_len", "bonus", "out_tokens", "new_seq_lens"):
+        assert torch.equal(st[key], gr[key]), key
+    assert (st["accept_len"] < K).any() and (st["accept_len"] == K).any()
+
