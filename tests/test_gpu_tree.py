@@ -107,3 +107,41 @@ def test_linear_accept_zero_rows(gpu_lib):
     r = oracle.accept_request(acc.p[2], acc.q[2], acc.draft[2], acc.u[2], 0)
     assert int(got["bonus"][2]) == r["bonus"] == 0 and int(got["accept_len"][2]) == r["accept_len"]
     assert int(err.item()) & va.ERR_ZERO_RESIDUAL
+
+
+def test_chain_tree_matches_the_linear_accept(gpu_lib):
+    """A chain tree through spec_accept_tree gives what spec_accept gives for
+    the same block with one-hot draft rows (test uniforms u[1..K], final draw
+    u[0]), bit for bit; requests the reference marks as ties are excluded
+    (the two kernels sum the residual masses in different orders)."""
+    rng = np.random.default_rng(97)
+    bs, K, V = 32, 15, 4096
+    print_case("chain tree = linear accept", bs, K, V)
+    dev = lambda a: to_dev(np.ascontiguousarray(a))
+    N = K + 1
+    parent = np.tile(np.arange(-1, K, dtype=np.int32), (bs, 1))
+    lg = rng.standard_normal((bs, N, V)) * 10.0
+    p = np.exp(lg - lg.max(-1, keepdims=True))
+    p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+    token = np.zeros((bs, N), np.int32)
+    best = p[:, :K].argmax(-1)
+    token[:, 1:] = np.where(rng.random((bs, K)) < 0.85, best, rng.integers(V, size=(bs, K)))
+    u = rng.random((bs, N), dtype=np.float32)
+    token[:8, 1:] = best[:8]        # the first requests accept every draft:
+    u[:8, 1:] = 1e-4                # the bonus comes from the last row
+    seq = rng.integers(1, 900, size=bs).astype(np.int32)
+    tr = va.accept_tree(dev(parent), dev(token), dev(p), dev(u), dev(seq))
+    q = np.zeros((bs, K, V), np.float32)
+    q[np.arange(bs)[:, None], np.arange(K), token[:, 1:]] = 1.0
+    ul = np.ascontiguousarray(np.concatenate([u[:, 1:], u[:, :1]], axis=1))
+    draft = np.ascontiguousarray(token[:, 1:])
+    lin = va.accept(dev(p), dev(q), dev(draft), dev(ul), dev(seq))
+    torch.cuda.synchronize()
+    ref = oracle.accept_batch(p, q, draft, ul, seq)
+    keep = ~ref["tie"]
+    for key in ("accept_len", "commit_len", "bonus", "new_seq_lens", "out_tokens"):
+        a, b = tr[key].cpu().numpy(), lin[key].cpu().numpy()
+        assert np.array_equal(a[keep], b[keep]), key
+    assert (ref["accept_len"][:8] == K).all() and (ref["accept_len"][8:] < K).all()
+    assert (ref["accept_len"][8:] > 0).any()
+
