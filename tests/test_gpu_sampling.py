@@ -160,3 +160,37 @@ def test_accept_logits_error_paths():
     assert e & va.ERR_TOKEN and e & va.ERR_ZERO_RESIDUAL
     assert got["accept_len"][0] == 0 and got["accept_len"][1] == 2
     assert ref["err"][1] & va.ERR_ZERO_RESIDUAL
+
+
+def test_untruncated_logits_accept_is_the_accept_on_softmax_rows():
+    """With nothing truncated (V = top-k = 64, top-p 1, temperature 1) the
+    logits accept equals spec_accept fed the softmax rows (float32), request by
+    request; ties of either reference are excluded (the two paths round the
+    probabilities differently)."""
+    rng = np.random.default_rng(101)
+    bs, K, V = 48, 7, 64
+    print_case("accept_logits untruncated = accept", bs, K, V)
+    tl = (rng.standard_normal((bs, K + 1, V)) * 2.0).astype(np.float32)
+    dl = (tl[:, :K] + rng.standard_normal((bs, K, V)) * 0.5).astype(np.float32)
+
+    def softmax(a):
+        e = np.exp(a.astype(np.float64) - a.max(-1, keepdims=True))
+        return e / e.sum(-1, keepdims=True)
+
+    q64 = softmax(dl)
+    draft = np.array([[rng.choice(V, p=q64[b, i]) for i in range(K)] for b in range(bs)], np.int32)
+    u = rng.random((bs, K + 1), dtype=np.float32)
+    seq = rng.integers(1, 900, size=bs).astype(np.int32)
+    got_l = va.accept_logits(to_dev(tl), to_dev(dl), to_dev(draft), to_dev(u), to_dev(seq),
+                             1.0, V, 1.0)
+    p32, q32 = softmax(tl).astype(np.float32), q64.astype(np.float32)
+    got_a = va.accept(to_dev(p32), to_dev(q32), to_dev(draft), to_dev(u), to_dev(seq))
+    torch.cuda.synchronize()
+    ref_l = oracle.accept_logits_batch(tl, dl, draft, u, seq, np.float32(1.0), V, np.float32(1.0))
+    ref_a = oracle.accept_batch(p32, q32, draft, u, seq)
+    keep = ~(ref_l["tie"] | ref_a["tie"])
+    for key in ("accept_len", "commit_len", "bonus", "new_seq_lens", "out_tokens"):
+        a, b = got_l[key].cpu().numpy(), got_a[key].cpu().numpy()
+        assert np.array_equal(a[keep], b[keep]), key
+    assert keep.sum() >= bs - 2 and (ref_a["accept_len"] > 0).any()
+
