@@ -144,6 +144,9 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
  *   16-byte aligned, contents irrelevant. It holds per-split partial outputs
  *   between the attention kernel and the merge kernel of the same call, so
  *   calls that share a workspace must be ordered (same stream, or synchronised).
+ *   The plan (and so the size) depends on the compute-unit count of the
+ *   current HIP device: size the workspace with the device current that the
+ *   call will run on.
  * Errors: SPEC_EINVAL (bad counts, Hq % Hkv != 0, g * B > 2048, mode, n_causal
  *   outside [0, B], NULL pointers), SPEC_ENOTSUP (D, P, dtype), SPEC_ENOSPC.
  *   Kernels set SPEC_ERR_SLOT for a page id outside [0, num_pages) (physical

@@ -42,7 +42,27 @@ import numpy as np
 
 ERR_TOKEN = 4          # a draft token id is outside [0, V)
 ERR_ZERO_RESIDUAL = 8  # residual mass was zero; the draw used p_j instead
-TIE_EPS = 1e-6
+TIE_EPS = 1e-6         # accept-test ties: |u - min(1, p/q)| below this
+
+
+def sample_tie_band(V, S, resid_abs_err=0.0):
+    """Half-width of the band around the draw's threshold inside which two
+    correct float64 evaluations of the inverse CDF may pick different tokens.
+
+    Both sides hold the same float64 residual entries (each is a float32
+    value, or the difference of two float32 values, rounded once, a
+    deterministic operation) and differ only in the order of their sums. A
+    running sum of n non-negative terms is within (n - 1) * 2^-53 * S of its
+    exact value (first-order bound; S = the total), this reference's running
+    sum has n <= V, and a summation tree or scan of depth below 256 (the
+    kernels' sub-block sums and scans) stays within 256 * 2^-53 * S. The
+    threshold u * S moves with S and adds one rounding. Together the running
+    sum at the chosen boundary and the threshold differ between the two
+    sides by at most (2V + 512) * 2^-53 * S = (V + 256) * 2^-52 * S.
+    resid_abs_err bounds sum_v |r_v - r'_v| when the two sides compute the
+    residual entries themselves (the logits accept); it moves both the
+    running sum and S, so it counts twice."""
+    return (V + 256) * 2.0 ** -52 * S + 2.0 * resid_abs_err
 
 
 def argmax_lowest(x):
@@ -70,14 +90,14 @@ def _inverse_cdf(r, u):
     return t, S, thr, C
 
 
-def accept_request(p, q, draft, u, seq_len):
+def accept_request(p, q, draft, u, seq_len, resid_abs_err=0.0):
     """One request. p [K+1, V], q [K, V] float32 rows; draft [K]; u [K+1].
 
     Returns a dict with accept_len, commit_len, bonus, out_tokens [K+1]
     (accepted drafts, then the bonus, then -1), new_seq_len, err, and the
     tie flags: tie_accept when a reached test has |u - min(1, p/q)| < 1e-6,
-    tie_sample when u_K * S lies within 1e-6 * S of the chosen token's
-    interval ends, tie = either."""
+    tie_sample when u_K * S lies within sample_tie_band(V, S, resid_abs_err)
+    of the chosen token's interval ends, tie = either."""
     K, V = q.shape
     err = 0
     tie_accept = False
@@ -106,7 +126,8 @@ def accept_request(p, q, draft, u, seq_len):
         r = p[j].astype(np.float64)
     t, S, thr, C = _inverse_cdf(r, u[K])
     lo = C[t - 1] if t > 0 else 0.0
-    tie_sample = bool(abs(thr - C[t]) < TIE_EPS * S or abs(thr - lo) < TIE_EPS * S)
+    band = sample_tie_band(V, S, resid_abs_err)
+    tie_sample = bool(abs(thr - C[t]) <= band or abs(thr - lo) <= band)
     out = np.full(K + 1, -1, np.int64)
     out[:n_acc] = draft[:n_acc]
     out[n_acc] = t
@@ -161,7 +182,8 @@ def tree_accept_request(parent, token, p, u, seq_len):
     path_nodes [N] (accepted node ids, then -1), out_tokens [N] (their
     tokens, then the bonus, then -1), bonus, commit_len, new_seq_len, err and
     tie flags as accept_request (tie_accept: a test with |u - p/(1 - T)| <
-    1e-6; tie_sample: the final threshold within 1e-6 * S of an interval end).
+    1e-6, T being a sum whose order may differ; tie_sample: the final
+    threshold within sample_tie_band(V, S) of an interval end).
     """
     N, V = p.shape
     err = 0
@@ -202,7 +224,8 @@ def tree_accept_request(parent, token, p, u, seq_len):
         r = p[x].astype(np.float64)
     t, S, thr, C = _inverse_cdf(r, u[0])
     lo = C[t - 1] if t > 0 else 0.0
-    tie_sample = bool(abs(thr - C[t]) < TIE_EPS * S or abs(thr - lo) < TIE_EPS * S)
+    band = sample_tie_band(V, S)
+    tie_sample = bool(abs(thr - C[t]) <= band or abs(thr - lo) <= band)
     k = len(path)
     nodes = np.full(N, -1, np.int64)
     nodes[:k] = path

@@ -33,6 +33,11 @@ stacks apply them):
 * A top-p decision whose prefix mass lies within 1e-9 of top_p is a tie: a
   request that uses such a row is excluded from bit-exact comparisons, like
   the accept and sampling ties of accept_request.
+* Two correct evaluations of a processed row agree to PROB_REL_ERR relative
+  per probability (exponentials and sums in float64, in different orders),
+  so the residual entries of the two sides differ by at most
+  PROB_REL_ERR * (p + q) each, 2 * PROB_REL_ERR in total; the draw's tie band
+  widens by that (accept.sample_tie_band's resid_abs_err).
 """
 import math
 
@@ -41,6 +46,7 @@ import numpy as np
 from .accept import accept_request
 
 TOPP_TIE_EPS = 1e-9
+PROB_REL_ERR = 1e-12
 
 
 def rank_order(logits):
@@ -99,7 +105,8 @@ def accept_logits_request(target_logits, draft_logits, draft, u, seq_len, temper
                   for i in range(K + 1)])
     q, tq = zip(*[sampling_filter(draft_logits[i], temperature, top_k, top_p)[::2]
                   for i in range(K)])
-    res = accept_request(np.stack(p), np.stack(q), draft, u, seq_len)
+    res = accept_request(np.stack(p), np.stack(q), draft, u, seq_len,
+                         resid_abs_err=2.0 * PROB_REL_ERR)
     j = res["accept_len"]
     used = any(tp[: j + 1]) or any(tq[: min(j + 1, K)])
     res["tie_topp"] = bool(used)

@@ -34,3 +34,17 @@ class AttnCase:
 
 def print_case(*parts):
     print("CASE", *parts, flush=True)
+
+
+# Share of a test's requests that may be left out of a bit-exact comparison
+# as ties (a decision within the tie band of its threshold, where two correct
+# float64 evaluations may differ).
+MAX_TIE_SHARE = 0.01
+
+
+def check_tie_share(n_excluded, n, what=""):
+    """Report the tie count and fail if more than 1 % of the requests were
+    left out of the bit-exact comparison."""
+    print(f"TIES {what}: {n_excluded} of {n} requests excluded", flush=True)
+    assert n_excluded <= MAX_TIE_SHARE * n, (
+        f"{n_excluded} of {n} requests excluded as ties (more than {MAX_TIE_SHARE:.0%})")

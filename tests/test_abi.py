@@ -299,3 +299,46 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         b.load()
     with pytest.raises(b.SpecError, match="not built"):
         va.attn_workspace_bytes(2, 16, 32, 8, 128, 1024)
+
+
+def test_binding_rejects_bad_buffers_before_any_launch():
+    """The binding's checks on the buffers it passes on: the error word must
+    be an int32 GPU tensor with at least one element, a workspace must be a GPU
+    tensor of at least the planned bytes (counted in bytes, whatever its
+    dtype), the page table must have one row per request, and every tensor of
+    a call must live on one device. All of them raise before a pointer
+    reaches the library."""
+    import torch
+    with pytest.raises(TypeError):
+        b._need_err(torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        b._need_err(torch.zeros(0, dtype=torch.int32))
+    with pytest.raises(b.SpecError, match="GPU"):
+        b._need_err(torch.zeros(1, dtype=torch.int32))      # a host error word
+    assert b._need_err(None) is None
+    with pytest.raises(b.SpecError, match="needs a workspace"):
+        b._need_ws(None, 64)
+    assert b._need_ws(None, 0) == 0
+    with pytest.raises(b.SpecError, match="smaller"):
+        b._need_ws(torch.empty(15, dtype=torch.float32), 61)  # 60 bytes, not 15
+    with pytest.raises(b.SpecError, match="GPU"):
+        b._need_ws(torch.empty(16, dtype=torch.float32), 61)  # big enough, but host memory
+    with pytest.raises(ValueError, match="page_table"):
+        b._need_table(torch.zeros((3, 8), dtype=torch.int32), 4)
+    with pytest.raises(TypeError):
+        b._need_table(torch.zeros((4, 8), dtype=torch.int64), 4)
+    with pytest.raises(b.SpecError, match="GPU"):
+        b._need_table(torch.zeros((4, 8), dtype=torch.int32), 4)
+    with pytest.raises(b.SpecError, match="different devices"):
+        b._same_device(torch.zeros(1), torch.zeros(1, device="meta"))
+    out = b._need_out(None, b._accept_outputs(3, 5), "cpu")
+    assert out["out_tokens"].shape == (3, 5) and out["bonus"].dtype == torch.int32
+    with pytest.raises(ValueError):
+        b._need_out(dict(out, bonus=torch.zeros(2, dtype=torch.int32)), b._accept_outputs(3, 5),
+                    "cpu")
+    # a whole call on host tensors stops at its first check
+    q = torch.zeros((2, 4, 2, 64), dtype=torch.float32)
+    with pytest.raises(b.SpecError, match="GPU"):
+        b.block_attn_call(1, q, torch.zeros((4, 1, 16, 64)), torch.zeros((4, 1, 64, 16)),
+                          torch.zeros((2, 2), dtype=torch.int32),
+                          torch.zeros(2, dtype=torch.int32), 64)

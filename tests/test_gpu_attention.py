@@ -253,6 +253,49 @@ def test_tree_chain_is_bitwise_causal(gpu_lib):
     assert np.array_equal(o_t, o_c) and np.array_equal(l_t, l_c)
 
 
+F32_P32 = [
+    # (name, config id, overrides, mode): fp32 inputs in 32-token pages (both
+    # halves of a DMA stage from one page, the V tail of a 32-token page), D 64
+    # and 128, every mask mode; ragged lengths end inside a page
+    ("f32_p32_d64_causal", 2, dict(bs=3, hq=4, hkv=2, d=64, page=32, dtype="f32", ctx_lo=1,
+                                   ctx_hi=1700), synth.CAUSAL),
+    ("f32_p32_d128_bidir", 3, dict(bs=2, hq=8, hkv=2, page=32, dtype="f32", ctx_lo=200,
+                                   ctx_hi=1300), synth.BIDIR),
+    ("f32_p32_d128_mixed", 5, dict(bs=3, hq=8, hkv=2, page=32, dtype="f32", n_causal=5,
+                                   ctx_lo=30, ctx_hi=900), synth.MIXED),
+    ("f32_p32_d64_mixed", 5, dict(bs=2, hq=4, hkv=1, d=64, page=32, dtype="f32", n_causal=11,
+                                  ctx_lo=500, ctx_hi=1500), synth.MIXED),
+    ("f32_p32_d128_tree", 6, dict(bs=3, hq=8, hkv=2, page=32, dtype="f32", block=24,
+                                  tree_depth=9, ctx_lo=50, ctx_hi=1100), synth.TREE),
+    ("f32_p32_d64_tree", 6, dict(bs=2, hq=4, hkv=2, d=64, page=32, dtype="f32", block=40,
+                                 tree_depth=12, ctx_lo=0, ctx_hi=800), synth.TREE),
+]
+
+
+@pytest.mark.parametrize("name,cid,over,mode", F32_P32, ids=[c[0] for c in F32_P32])
+def test_f32_page32_every_schedule(gpu_lib, name, cid, over, mode):
+    """fp32 with 32-token pages under the default plan, a loose bound that
+    splits every unit many ways, and a bound loose enough for the balanced
+    schedule: every output row against the dense reference at 1e-5."""
+    cfg = synth.config(cid, **over)
+    print_case("block_attn f32 page 32", name, cfg)
+    x = synth.make_attn_inputs(cfg, seed=61)
+    case = AttnCase(x)
+    masks = synth.make_trees(cfg, 61)[1] if mode == synth.TREE else None
+    units = cfg.bs * cfg.hkv
+    balanced = 32 * (-(-32768 // units))      # units x stages >= 32768
+    ref = oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                  x.page_table, x.seq_lens, mode, cfg.n_causal, tree=masks)
+    for max_kv in (case.max_kv, 4 * case.max_kv + 3000, balanced):
+        if mode == synth.TREE:
+            o, lse = run_tree(case, masks, max_kv=max_kv)
+        else:
+            o, lse = run(case, mode, max_kv=max_kv)
+        assert np.max(np.abs(o - ref[0])) <= TOL["f32"], max_kv
+        assert np.max(np.abs(lse - ref[1])) <= LSE_TOL["f32"], max_kv
+    assert va.attn_workspace_bytes(cfg.bs, cfg.block, cfg.hq, cfg.hkv, cfg.d, balanced) > 0
+
+
 def sampled_rows(x, n, rng):
     rows = set()
     B, hq = x.cfg.block, x.cfg.hq

@@ -1,7 +1,10 @@
 """GPU parity of spec_prepare_block, spec_draft_argmax and spec_accept
-against the float64 CPU reference. Integer outputs must match bit for bit;
-accept decisions are exact in double on both sides, and requests whose
-decision lies within 1e-6 of its threshold (ties) are counted and excluded."""
+against the float64 CPU reference. Integer outputs must match bit for bit.
+The accept tests u * q < p are exact in double on both sides (the same float32
+inputs), so requests with an accept tie (|u - min(1, p/q)| < 1e-6) are counted
+and still compared; only a draw whose threshold lies within the derived
+float64 band of an interval end (oracle.accept.sample_tie_band) is left out,
+and at most 1 % of a test's requests may be."""
 import json
 import os
 
@@ -12,7 +15,7 @@ import torch
 import oracle
 import verify_attention_amd as va
 from verify_attention_amd import synth
-from _support import print_case, to_dev
+from _support import check_tie_share, print_case, to_dev
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -130,11 +133,10 @@ def run_accept(x, seq, greedy=False, err=None, ws=None):
 
 
 def compare_accept(got, ref, allow_ties=True):
-    """Requests without a tie must match bit for bit. Ties (a reached accept
-    test within 1e-6 of min(1, p/q), or the sampling threshold within 1e-6 * S
-    of the chosen token's interval) are excluded, counted and reported,
-    together with how many of them matched anyway."""
-    tie = ref["tie"] if allow_ties else np.zeros(len(ref["tie"]), bool)
+    """Every request must match bit for bit except draws within the float64
+    tie band of the sampling threshold (at most 1 % of the requests); accept
+    ties are counted and reported, and compared like every other request."""
+    tie = ref["tie_sample"] if allow_ties else np.zeros(len(ref["tie"]), bool)
     same = np.ones(len(tie), bool)
     for k_got, k_ref in (("accept_len", "accept_len"), ("commit_len", "commit_len"),
                          ("bonus", "bonus"), ("new_seq_lens", "new_seq_len"),
@@ -144,9 +146,9 @@ def compare_accept(got, ref, allow_ties=True):
     bad = np.flatnonzero(~same & ~tie)
     assert len(bad) == 0, f"requests differing without a tie: {bad}"
     n_tie = int(tie.sum())
-    print(f"ties excluded: {n_tie} (accept-test {int(ref['tie_accept'].sum())}, "
-          f"sampling {int(ref['tie_sample'].sum())}); tied requests that matched anyway: "
-          f"{int((same & tie).sum())}")
+    print(f"accept ties (compared): {int(ref['tie_accept'].sum())}; sampling ties excluded: "
+          f"{n_tie}, of which matched anyway: {int((same & tie).sum())}")
+    check_tie_share(n_tie, len(tie), "spec_accept")
     return n_tie, int((~same).sum())
 
 

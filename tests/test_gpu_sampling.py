@@ -11,7 +11,7 @@ import torch
 import oracle
 import verify_attention_amd as va
 from verify_attention_amd import synth
-from _support import print_case, to_dev
+from _support import check_tie_share, print_case, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def check_filter(logits, got, T, k, top_p):
         assert n == len(kept), (r, n, len(kept))
         assert list(got["kept_ids"][r, :n]) == kept, r
         assert (got["kept_ids"][r, n:] == -1).all() and (got["kept_probs"][r, n:] == 0).all()
-        np.testing.assert_allclose(got["kept_probs"][r, :n], p[kept], rtol=1e-12, atol=0)
+        np.testing.assert_allclose(got["kept_probs"][r, :n], p[kept], rtol=oracle.sampling.PROB_REL_ERR, atol=0)
     print(f"filter rows {vals.shape[0]}: top-p ties excluded {ties}", flush=True)
     return ties
 
@@ -115,6 +115,7 @@ def compare_accept_logits(x, seq, got, T, k, top_p):
           f"(accept {int(ref['tie_accept'].sum())}, sampling {int(ref['tie_sample'].sum())}, "
           f"top-p {int(ref['tie_topp'].sum())}), tied that matched {int((same & ref['tie']).sum())}, "
           f"mean accept {ref['accept_len'].mean():.2f}", flush=True)
+    check_tie_share(int(ref["tie"].sum()), len(seq), "spec_accept_logits")
     return ref
 
 
@@ -192,5 +193,6 @@ def test_untruncated_logits_accept_is_the_accept_on_softmax_rows():
     for key in ("accept_len", "commit_len", "bonus", "new_seq_lens", "out_tokens"):
         a, b = got_l[key].cpu().numpy(), got_a[key].cpu().numpy()
         assert np.array_equal(a[keep], b[keep]), key
-    assert keep.sum() >= bs - 2 and (ref_a["accept_len"] > 0).any()
+    check_tie_share(int((~keep).sum()), bs, "untruncated logits accept vs accept")
+    assert (ref_a["accept_len"] > 0).any()
 

@@ -1,6 +1,9 @@
 """GPU parity of the tree verify path: spec_accept_tree against the float64
-tree walk of the CPU reference (bit-exact outputs for every request whose
-walk has no tie within 1e-6; ties are counted and reported)."""
+tree walk of the CPU reference: bit-exact outputs for every request except
+ties, counted, reported and at most 1 % of a test's requests. A tie is a
+child test within 1e-6 of its threshold (the tried mass T is a sum whose
+order differs between the two sides) or a draw within the derived float64
+band of an interval end."""
 import numpy as np
 import pytest
 import torch
@@ -8,7 +11,7 @@ import torch
 import oracle
 import verify_attention_amd as va
 from verify_attention_amd import synth
-from _support import print_case, to_dev
+from _support import check_tie_share, print_case, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +40,7 @@ def compare(ti, seq, got):
             continue
         assert same, (b, {k: got[k][b] for k in got}, r)
     print(f"ties {ties} of {bs} requests ({differ} of them differ)", flush=True)
+    check_tie_share(ties, bs, "spec_accept_tree")
     return ties
 
 
@@ -49,7 +53,7 @@ def test_tree_accept_full_vocab(gpu_lib):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     got = run_tree_accept(ti, seq, err=err)
     assert int(err.item()) == 0
-    assert compare(ti, seq, got) <= 2
+    compare(ti, seq, got)
     assert got["accept_len"].max() >= 1   # the workload does accept children
 
 
@@ -65,8 +69,7 @@ def test_tree_accept_small_vocab_many_requests(gpu_lib, N, V, depth, seed):
     ti = synth.make_tree_accept_inputs(cfg, seed, par)
     seq = np.random.default_rng(seed).integers(0, 5000, size=cfg.bs).astype(np.int32)
     got = run_tree_accept(ti, seq)
-    ties = compare(ti, seq, got)
-    assert ties <= cfg.bs // 20
+    compare(ti, seq, got)
     if N > 1:
         assert got["accept_len"].max() >= 2
 
@@ -112,7 +115,8 @@ def test_linear_accept_zero_rows(gpu_lib):
 def test_chain_tree_matches_the_linear_accept(gpu_lib):
     """A chain tree through spec_accept_tree gives what spec_accept gives for
     the same block with one-hot draft rows (test uniforms u[1..K], final draw
-    u[0]), bit for bit; requests the reference marks as ties are excluded
+    u[0]), bit for bit: a chain node has one child, so both kernels test
+    u * 1 < p exactly; only draws within the float64 tie band are excluded
     (the two kernels sum the residual masses in different orders)."""
     rng = np.random.default_rng(97)
     bs, K, V = 32, 15, 4096
@@ -138,10 +142,11 @@ def test_chain_tree_matches_the_linear_accept(gpu_lib):
     lin = va.accept(dev(p), dev(q), dev(draft), dev(ul), dev(seq))
     torch.cuda.synchronize()
     ref = oracle.accept_batch(p, q, draft, ul, seq)
-    keep = ~ref["tie"]
+    keep = ~ref["tie_sample"]
     for key in ("accept_len", "commit_len", "bonus", "new_seq_lens", "out_tokens"):
         a, b = tr[key].cpu().numpy(), lin[key].cpu().numpy()
         assert np.array_equal(a[keep], b[keep]), key
+    check_tie_share(int((~keep).sum()), bs, "chain tree vs linear accept")
     assert (ref["accept_len"][:8] == K).all() and (ref["accept_len"][8:] < K).all()
     assert (ref["accept_len"][8:] > 0).any()
 

@@ -419,3 +419,44 @@ def test_tree_walk_flags_bad_tokens_and_parents():
     # u = 0 accepts the first valid child (node 2), a leaf; bonus from p[2]
     assert r["accept_len"] == 1 and r["path_nodes"][0] == 2 and r["out_tokens"][0] == 1
     assert r["new_seq_len"] == 12
+
+
+def test_sample_tie_band_covers_other_summation_orders():
+    """oracle.accept.sample_tie_band(V, S) bounds how far two correct float64
+    evaluations of the draw's running sums may be apart. On a full-vocabulary
+    residual row, the reference's sequential running sum, a blocked order
+    (pairwise sums of four entries, a reduction over 256-entry sub-blocks, a
+    running sum over the sub-block totals, then a running sum inside the
+    sub-block, as a GPU reduction orders it) and a reversed accumulation all
+    agree to well inside half the band at every index, and against exactly
+    rounded prefix sums (math.fsum) at sampled indices."""
+    import math
+    rng = np.random.default_rng(7)
+    V = 151936
+    lp = rng.standard_normal(V) * 3.0
+    lq = lp + rng.standard_normal(V) * 0.5
+    p = np.exp(lp - lp.max()); p = (p / p.sum()).astype(np.float32)
+    q = np.exp(lq - lq.max()); q = (q / q.sum()).astype(np.float32)
+    r = np.maximum(p.astype(np.float64) - q.astype(np.float64), 0.0)
+    C = np.cumsum(r)
+    S = C[-1]
+    band = oracle.accept.sample_tie_band(V, S)
+    pad = np.zeros(-(-V // 256) * 256)
+    pad[:V] = r
+    quads = pad.reshape(-1, 4)
+    lane = (quads[:, 0] + quads[:, 1]) + (quads[:, 2] + quads[:, 3])
+    sub = lane.reshape(-1, 64)
+    while sub.shape[1] > 1:          # pairwise tree inside each sub-block
+        sub = sub[:, 0::2] + sub[:, 1::2]
+    base = np.concatenate([[0.0], np.cumsum(sub[:, 0])[:-1]])
+    inner = np.cumsum(pad.reshape(-1, 256), axis=1)
+    C_blocked = (base[:, None] + inner).ravel()[:V]
+    C_rev = S - np.concatenate([np.cumsum(r[::-1])[::-1][1:], [0.0]])
+    assert np.max(np.abs(C_blocked - C)) <= band / 2
+    assert np.max(np.abs(C_rev - C)) <= band / 2
+    for t in rng.integers(0, V, size=64):
+        exact = math.fsum(r[:t + 1])
+        assert abs(C[t] - exact) <= band / 4 and abs(C_blocked[t] - exact) <= band / 4
+    # the band is a rounding bound, orders of magnitude below the accept-test
+    # tie width
+    assert band < 1e-9 * S

@@ -114,18 +114,83 @@ def _ptr(t):
 
 
 def _need(t, name, dtype=None, shape=None, device=True):
+    """Type, dtype, shape and contiguity, then (device=True) that the tensor
+    lives on a GPU."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if device and not t.is_cuda:
-        raise SpecError(f"{name} must live on the GPU")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise SpecError(f"{name} must live on the GPU")
     return t
+
+
+def _need_err(err):
+    """The device error word: int32 on the GPU with at least one element (or None)."""
+    torch = _torch()
+    if err is None:
+        return None
+    _need(err, "err", torch.int32, device=False)
+    if err.numel() < 1:
+        raise ValueError("err needs at least one int32 element")
+    return _need(err, "err")
+
+
+def _need_ws(ws, need):
+    """A workspace on the GPU (contiguous) of at least `need` bytes; returns its
+    size in bytes (0 for None)."""
+    if ws is None:
+        if need > 0:
+            raise SpecError(f"the call needs a workspace of {need} bytes")
+        return 0
+    _need(ws, "ws", device=False)
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise SpecError(f"workspace of {nbytes} bytes is smaller than the {need} the call needs")
+    _need(ws, "ws")
+    return nbytes
+
+
+def _need_table(page_table, bs):
+    """page_table [bs, max_pages] int32 on the GPU."""
+    torch = _torch()
+    _need(page_table, "page_table", torch.int32, device=False)
+    if page_table.dim() != 2 or page_table.shape[0] != bs:
+        raise ValueError(f"page_table must have shape ({bs}, max_pages), got "
+                         f"{tuple(page_table.shape)}")
+    return _need(page_table, "page_table")
+
+
+def _need_out(out, specs, dev):
+    """Creates (out None) or checks the output tensors of an accept-style call:
+    specs maps name -> shape (int32 unless a dtype is given as a third entry)."""
+    torch = _torch()
+    if out is None:
+        out = {}
+        for name, spec in specs.items():
+            dt = spec[1] if len(spec) > 1 else torch.int32
+            out[name] = torch.empty(spec[0], dtype=dt, device=dev)
+        return out
+    for name, spec in specs.items():
+        if name not in out:
+            raise KeyError(f"out is missing {name}")
+        dt = spec[1] if len(spec) > 1 else torch.int32
+        _need(out[name], name, dt, spec[0], device=False)
+    for name in specs:
+        _need(out[name], name)
+    return out
+
+
+def _same_device(*ts):
+    """Every tensor given lives on one GPU."""
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise SpecError(f"tensors live on different devices: {sorted(map(str, devs))}")
 
 
 def _dtype_code(t):
@@ -160,7 +225,8 @@ def prepare_block_call(verified_id, seq_lens, page_table, page_size, block, mask
     bs = verified_id.shape[0]
     _need(verified_id, "verified_id", torch.int32, (bs,))
     _need(seq_lens, "seq_lens", torch.int32, (bs,))
-    _need(page_table, "page_table", torch.int32)
+    _need_table(page_table, bs)
+    _need_err(err)
     if draft_tokens is not None:
         _need(draft_tokens, "draft_tokens", torch.int32, (bs, block - 1))
     if out is None:
@@ -168,6 +234,7 @@ def prepare_block_call(verified_id, seq_lens, page_table, page_size, block, mask
                     for _ in range(3))
     for t, nm in zip(out, ("block_ids", "positions", "cache_loc")):
         _need(t, nm, torch.int32, (bs, block))
+    _same_device(verified_id, seq_lens, page_table, draft_tokens, *out, err)
     args = (bs, block, page_size, page_table.shape[1], num_pages, mask_token_id, _ptr(verified_id),
             _ptr(seq_lens), _ptr(page_table), _ptr(draft_tokens), _ptr(out[0]), _ptr(out[1]),
             _ptr(out[2]), _ptr(err), _stream(stream))
@@ -206,8 +273,9 @@ def block_attn_call(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n
     _need(v_pool, "v_pool", q.dtype, (num_pages, hkv, d, P))
     if d2 != d:
         raise ValueError("k_pool head dim differs from q")
-    _need(page_table, "page_table", torch.int32)
+    _need_table(page_table, bs)
     _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need_err(err)
     if n_causal_per_req is not None:
         _need(n_causal_per_req, "n_causal_per_req", torch.int32, (bs,))
     if out is None:
@@ -218,10 +286,12 @@ def block_attn_call(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n
     need = attn_workspace_bytes(bs, B, hq, hkv, d, max_kv_len)
     if ws is None and need > 0:
         ws = workspace(need, q.device)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(q, k_pool, v_pool, page_table, seq_lens, n_causal_per_req, out, lse, ws, err)
     args = (mode, n_causal, _ptr(n_causal_per_req), dt, bs, B, hq, hkv, d, P, page_table.shape[1],
             num_pages, max_kv_len, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
-            _ptr(seq_lens), sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
-            0 if ws is None else ws.numel(), _ptr(err), _stream(stream))
+            _ptr(seq_lens), sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(err),
+            _stream(stream))
     fn = load().block_attn
     keep = (q, k_pool, v_pool, page_table, seq_lens, n_causal_per_req, out, lse, ws, err)
 
@@ -248,8 +318,9 @@ def block_attn_tree_call(tree_mask, q, k_pool, v_pool, page_table, seq_lens, max
     _need(v_pool, "v_pool", q.dtype, (num_pages, hkv, d, P))
     if d2 != d:
         raise ValueError("k_pool head dim differs from q")
-    _need(page_table, "page_table", torch.int32)
+    _need_table(page_table, bs)
     _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need_err(err)
     _need(tree_mask, "tree_mask", torch.int64)
     if tuple(tree_mask.shape) not in ((B,), (bs, B)):
         raise ValueError(f"tree_mask must have shape ({B},) or ({bs}, {B})")
@@ -262,10 +333,12 @@ def block_attn_tree_call(tree_mask, q, k_pool, v_pool, page_table, seq_lens, max
     need = attn_workspace_bytes(bs, B, hq, hkv, d, max_kv_len)
     if ws is None and need > 0:
         ws = workspace(need, q.device)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(tree_mask, q, k_pool, v_pool, page_table, seq_lens, out, lse, ws, err)
     args = (_ptr(tree_mask), int(per_request), dt, bs, B, hq, hkv, d, P, page_table.shape[1],
             num_pages, max_kv_len, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
-            _ptr(seq_lens), sm_scale, _ptr(out), _ptr(lse), _ptr(ws),
-            0 if ws is None else ws.numel(), _ptr(err), _stream(stream))
+            _ptr(seq_lens), sm_scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(err),
+            _stream(stream))
     fn = load().block_attn_tree
     keep = (tree_mask, q, k_pool, v_pool, page_table, seq_lens, out, lse, ws, err)
 
@@ -307,6 +380,7 @@ def draft_argmax_call(logits, out=None, stream=None):
     if out is None:
         out = torch.empty(rows, dtype=torch.int32, device=logits.device)
     _need(out, "tokens", torch.int32, (rows,))
+    _same_device(logits, out)
     args = (rows, V, _dtype_code(logits), _ptr(logits), _ptr(out), _stream(stream))
     fn = load().spec_draft_argmax
     keep = (logits, out)
@@ -327,6 +401,12 @@ def draft_argmax(logits, out=None, stream=None):
     return out
 
 
+def _accept_outputs(bs, n_tok):
+    """Output shapes shared by the accept calls (int32)."""
+    return dict(accept_len=((bs,),), commit_len=((bs,),), bonus=((bs,),),
+                out_tokens=((bs, n_tok),), new_seq_lens=((bs,),))
+
+
 def accept_call(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, stream=None):
     """Checks the arguments of spec_accept once and returns (enqueue, out)."""
     torch = _torch()
@@ -338,18 +418,18 @@ def accept_call(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=N
     if not greedy:
         _need(q, "q", torch.float32, (bs, K, V))
         _need(u, "u", torch.float32, (bs, K + 1))
+    _need_err(err)
     dev = p.device
-    if out is None:
-        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((bs, K + 1), dtype=torch.int32, device=dev),
-                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
+    out = _need_out(out, _accept_outputs(bs, K + 1), dev)
+    need = accept_workspace_bytes(bs, K, V, greedy)
     if ws is None:
-        ws = workspace(accept_workspace_bytes(bs, K, V, greedy), dev)
+        ws = workspace(need, dev)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(p, None if greedy else q, draft, None if greedy else u, seq_lens, ws, err,
+                 *out.values())
     args = (bs, K, V, int(bool(greedy)), _ptr(p), _ptr(q), _ptr(draft), _ptr(u), _ptr(seq_lens),
             _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
-            _ptr(out["out_tokens"]), _ptr(out["new_seq_lens"]), _ptr(ws), ws.numel(), _ptr(err),
+            _ptr(out["out_tokens"]), _ptr(out["new_seq_lens"]), _ptr(ws), ws_bytes, _ptr(err),
             _stream(stream))
     fn = load().spec_accept
     keep = (p, q, draft, u, seq_lens, out, ws, err)
@@ -385,20 +465,18 @@ def accept_tree_call(parent, token, p, u, seq_lens, out=None, ws=None, err=None,
     _need(token, "token", torch.int32, (bs, N))
     _need(u, "u", torch.float32, (bs, N))
     _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need_err(err)
     dev = p.device
-    if out is None:
-        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((bs, N), dtype=torch.int32, device=dev),
-                   path_nodes=torch.empty((bs, N), dtype=torch.int32, device=dev),
-                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
+    out = _need_out(out, dict(_accept_outputs(bs, N), path_nodes=((bs, N),)), dev)
+    need = accept_tree_workspace_bytes(bs, N, V)
     if ws is None:
-        ws = workspace(accept_tree_workspace_bytes(bs, N, V), dev)
+        ws = workspace(need, dev)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(parent, token, p, u, seq_lens, ws, err, *out.values())
     args = (bs, N, V, _ptr(parent), _ptr(token), _ptr(p), _ptr(u), _ptr(seq_lens),
             _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
             _ptr(out["out_tokens"]), _ptr(out["path_nodes"]), _ptr(out["new_seq_lens"]),
-            _ptr(ws), ws.numel(), _ptr(err), _stream(stream))
+            _ptr(ws), ws_bytes, _ptr(err), _stream(stream))
     fn = load().spec_accept_tree
     keep = (parent, token, p, u, seq_lens, out, ws, err)
 
@@ -427,24 +505,22 @@ def accept_tree_commit_call(parent, token, p, u, seq_lens, k_pool, v_pool, page_
     _need(k_pool, "k_pool")
     dt = _dtype_code(k_pool)
     _need(v_pool, "v_pool", k_pool.dtype, (num_pages, hkv, d, P))
-    _need(page_table, "page_table", torch.int32)
+    _need_table(page_table, bs)
+    _need_err(err)
     dev = p.device
-    if out is None:
-        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((bs, N), dtype=torch.int32, device=dev),
-                   path_nodes=torch.empty((bs, N), dtype=torch.int32, device=dev),
-                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev),
-                   freed=torch.empty((bs, N), dtype=torch.int32, device=dev))
-    _need(out["freed"], "freed", torch.int32, (bs, N))
+    out = _need_out(out, dict(_accept_outputs(bs, N), path_nodes=((bs, N),),
+                              freed=((bs, N),)), dev)
+    need = accept_tree_workspace_bytes(bs, N, V)
     if ws is None:
-        ws = workspace(accept_tree_workspace_bytes(bs, N, V), dev)
+        ws = workspace(need, dev)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(parent, token, p, u, seq_lens, k_pool, v_pool, page_table, ws, err,
+                 *out.values())
     args = (bs, N, V, _ptr(parent), _ptr(token), _ptr(p), _ptr(u), _ptr(seq_lens),
             _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
             _ptr(out["out_tokens"]), _ptr(out["path_nodes"]), _ptr(out["new_seq_lens"]),
             dt, hkv, d, P, page_table.shape[1], num_pages, _ptr(page_table), _ptr(k_pool),
-            _ptr(v_pool), _ptr(out["freed"]), _ptr(ws), ws.numel(), _ptr(err), _stream(stream))
+            _ptr(v_pool), _ptr(out["freed"]), _ptr(ws), ws_bytes, _ptr(err), _stream(stream))
     fn = load().spec_accept_tree_commit
     keep = (parent, token, p, u, seq_lens, k_pool, v_pool, page_table, out, ws, err)
 
@@ -490,18 +566,17 @@ def sampling_filter_call(logits, temperature, top_k, top_p, out=None, ws=None, s
     _need(logits, "logits")
     dt = _dtype_code(logits)
     dev = logits.device
-    if out is None:
-        out = dict(kept_ids=torch.empty((rows, top_k), dtype=torch.int32, device=dev),
-                   kept_probs=torch.empty((rows, top_k), dtype=torch.float64, device=dev),
-                   n_kept=torch.empty(rows, dtype=torch.int32, device=dev))
-    _need(out["kept_ids"], "kept_ids", torch.int32, (rows, top_k))
-    _need(out["kept_probs"], "kept_probs", torch.float64, (rows, top_k))
-    _need(out["n_kept"], "n_kept", torch.int32, (rows,))
+    out = _need_out(out, dict(kept_ids=((rows, top_k),),
+                              kept_probs=((rows, top_k), torch.float64),
+                              n_kept=((rows,),)), dev)
+    need = sampling_filter_workspace_bytes(rows, V)
     if ws is None:
-        ws = workspace(sampling_filter_workspace_bytes(rows, V), dev)
+        ws = workspace(need, dev)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(logits, ws, *out.values())
     args = (rows, V, dt, _ptr(logits), float(temperature), int(top_k), float(top_p),
             _ptr(out["kept_ids"]), _ptr(out["kept_probs"]), _ptr(out["n_kept"]), _ptr(ws),
-            ws.numel(), _stream(stream))
+            ws_bytes, _stream(stream))
     fn = load().spec_sampling_filter
     keep = (logits, out, ws)
 
@@ -540,19 +615,18 @@ def accept_logits_call(target_logits, draft_logits, draft, u, seq_lens, temperat
     _need(draft, "draft", torch.int32, (bs, K))
     _need(u, "u", torch.float32, (bs, K + 1))
     _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need_err(err)
     dev = target_logits.device
-    if out is None:
-        out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                   bonus=torch.empty(bs, dtype=torch.int32, device=dev),
-                   out_tokens=torch.empty((bs, K + 1), dtype=torch.int32, device=dev),
-                   new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
+    out = _need_out(out, _accept_outputs(bs, K + 1), dev)
+    need = accept_logits_workspace_bytes(bs, K, V, top_k)
     if ws is None:
-        ws = workspace(accept_logits_workspace_bytes(bs, K, V, top_k), dev)
+        ws = workspace(need, dev)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(target_logits, draft_logits, draft, u, seq_lens, ws, err, *out.values())
     args = (bs, K, V, dt, float(temperature), int(top_k), float(top_p), _ptr(target_logits),
             _ptr(draft_logits), _ptr(draft), _ptr(u), _ptr(seq_lens), _ptr(out["accept_len"]),
             _ptr(out["commit_len"]), _ptr(out["bonus"]), _ptr(out["out_tokens"]),
-            _ptr(out["new_seq_lens"]), _ptr(ws), ws.numel(), _ptr(err), _stream(stream))
+            _ptr(out["new_seq_lens"]), _ptr(ws), ws_bytes, _ptr(err), _stream(stream))
     fn = load().spec_accept_logits
     keep = (target_logits, draft_logits, draft, u, seq_lens, out, ws, err)
 
@@ -590,12 +664,14 @@ def commit_kv_call(k_pool, v_pool, page_table, seq_lens, accept_len, block, path
     bs = seq_lens.shape[0]
     _need(seq_lens, "seq_lens", torch.int32, (bs,))
     _need(accept_len, "accept_len", torch.int32, (bs,))
-    _need(page_table, "page_table", torch.int32)
+    _need_table(page_table, bs)
+    _need_err(err)
     if path_nodes is not None:
         _need(path_nodes, "path_nodes", torch.int32, (bs, block))
     if freed is None:
         freed = torch.empty((bs, block), dtype=torch.int32, device=k_pool.device)
     _need(freed, "freed", torch.int32, (bs, block))
+    _same_device(k_pool, v_pool, page_table, seq_lens, accept_len, path_nodes, freed, err)
     args = (dt, bs, block, hkv, d, P, page_table.shape[1], num_pages, _ptr(seq_lens),
             _ptr(accept_len), _ptr(path_nodes), _ptr(page_table), _ptr(k_pool), _ptr(v_pool),
             _ptr(freed), _ptr(err), _stream(stream))

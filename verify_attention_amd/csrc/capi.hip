@@ -3,7 +3,6 @@
 // Every entry point only enqueues work on the caller's stream.
 #include <climits>
 #include <cmath>
-#include <cstdlib>
 
 #include "specattn.h"
 #include "kernels.h"
@@ -19,7 +18,8 @@ constexpr int kMaxSplits = 64;  // splits per unit (each keeps at least 8 stages
 constexpr int kMaxChunks = 256;
 constexpr int kMaxUnitRows = 128;   // query rows one workgroup holds (8 MFMA row tiles)
 constexpr int kMaxQueryRows = 2048; // g * B: at most 16 row groups
-constexpr int kCUs = 256;
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCUs = 256;    // MI355X; used only if the device cannot be queried
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -29,19 +29,21 @@ int ilog2_exact(int x) {
   return (1 << s) == x ? s : -1;
 }
 
-// Optional overrides read once (tuning knobs): the split count of the
-// per-unit schedule, and the schedule itself (1: per unit, 2: balanced).
-int env_int(const char* name) {
-  const char* s = std::getenv(name);
-  return s ? std::atoi(s) : 0;
-}
-int env_splits() {
-  static int v = env_int("SPECATTN_SPLITS");
-  return v;
-}
-int env_schedule() {
-  static int v = env_int("SPECATTN_SCHEDULE");
-  return v;
+// Compute units of the current device, queried once per device: the
+// attention plan sizes its grids (one workgroup per CU for the balanced
+// schedule, enough splits to cover the CUs otherwise) from it, so the
+// workspace size and the call must be planned on the same device.
+int device_cus() {
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = kDefaultCUs;
+  __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  return n;
 }
 
 struct AttnPlan {
@@ -73,23 +75,19 @@ AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   p.RG = (p.Mt + p.M - 1) / p.M;  // no empty group after the rounding
   p.units = bs * Hkv * p.RG;
   const int max_steps = std::max(1, (max_kv_len + kStepKeys - 1) / kStepKeys);
-  const int sched = env_schedule();
-  p.balanced = bs <= kMaxBalancedBatch &&
-               (sched == 2 || (sched != 1 && (long long)p.units * max_steps >= kBalancedMinStages));
+  const int cus = device_cus();
+  p.balanced = bs <= kMaxBalancedBatch && (long long)p.units * max_steps >= kBalancedMinStages;
   if (p.balanced) {
     // G = teams x RG workgroups, a multiple of 8 * RG (one team per XCD slot)
-    p.grid = p.RG == 1 ? kCUs : std::max(1, kCUs / (8 * p.RG)) * 8 * p.RG;
+    p.grid = p.RG == 1 ? cus : std::max(1, cus / (8 * p.RG)) * 8 * p.RG;
     const size_t slots = 2 * (size_t)p.grid;
     p.off_ml = 0;
     p.off_o = align_up(slots * p.M * 2 * sizeof(float), 256);
     p.ws_bytes = p.off_o + slots * p.M * D * sizeof(float);
     return p;
   }
-  int splits = env_splits();
-  if (splits <= 0) {
-    splits = (kCUs + p.units - 1) / p.units;
-    splits = std::min(splits, std::max(1, max_steps / 8));
-  }
+  int splits = (cus + p.units - 1) / p.units;
+  splits = std::min(splits, std::max(1, max_steps / 8));
   splits = std::max(1, std::min(splits, std::min(kMaxSplits, max_steps)));
   p.steps_per_split = (max_steps + splits - 1) / splits;
   p.splits = (max_steps + p.steps_per_split - 1) / p.steps_per_split;
