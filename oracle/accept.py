@@ -65,6 +65,18 @@ def sample_tie_band(V, S, resid_abs_err=0.0):
     return (V + 256) * 2.0 ** -52 * S + 2.0 * resid_abs_err
 
 
+def draw_is_tie(thr, C, t, band):
+    """Whether the draw's threshold thr lies strictly inside the tie band of
+    an end of the chosen token's interval (C[t-1], C[t]]. A zero threshold
+    (u = 0) is not a tie: it is exactly 0 on both sides and every running sum
+    before the first entry with mass is a sum of zeros, exact in any order,
+    so both pick the first entry with mass."""
+    if thr == 0.0:
+        return False
+    lo = C[t - 1] if t > 0 else 0.0
+    return bool(abs(thr - C[t]) < band or abs(thr - lo) < band)
+
+
 def argmax_lowest(x):
     """Index of the maximum; the lowest index wins among equal maxima; NaN
     never wins (a row without a non-NaN entry gives 0)."""
@@ -97,7 +109,7 @@ def accept_request(p, q, draft, u, seq_len, resid_abs_err=0.0):
     (accepted drafts, then the bonus, then -1), new_seq_len, err, and the
     tie flags: tie_accept when a reached test has |u - min(1, p/q)| < 1e-6,
     tie_sample when u_K * S lies within sample_tie_band(V, S, resid_abs_err)
-    of the chosen token's interval ends, tie = either."""
+    of the chosen token's interval ends (draw_is_tie), tie = either."""
     K, V = q.shape
     err = 0
     tie_accept = False
@@ -125,9 +137,7 @@ def accept_request(p, q, draft, u, seq_len, resid_abs_err=0.0):
         err |= ERR_ZERO_RESIDUAL
         r = p[j].astype(np.float64)
     t, S, thr, C = _inverse_cdf(r, u[K])
-    lo = C[t - 1] if t > 0 else 0.0
-    band = sample_tie_band(V, S, resid_abs_err)
-    tie_sample = bool(abs(thr - C[t]) <= band or abs(thr - lo) <= band)
+    tie_sample = draw_is_tie(thr, C, t, sample_tie_band(V, S, resid_abs_err))
     out = np.full(K + 1, -1, np.int64)
     out[:n_acc] = draft[:n_acc]
     out[n_acc] = t
@@ -223,9 +233,7 @@ def tree_accept_request(parent, token, p, u, seq_len):
         err |= ERR_ZERO_RESIDUAL
         r = p[x].astype(np.float64)
     t, S, thr, C = _inverse_cdf(r, u[0])
-    lo = C[t - 1] if t > 0 else 0.0
-    band = sample_tie_band(V, S)
-    tie_sample = bool(abs(thr - C[t]) <= band or abs(thr - lo) <= band)
+    tie_sample = draw_is_tie(thr, C, t, sample_tie_band(V, S))
     k = len(path)
     nodes = np.full(N, -1, np.int64)
     nodes[:k] = path

@@ -460,3 +460,18 @@ def test_sample_tie_band_covers_other_summation_orders():
     # the band is a rounding bound, orders of magnitude below the accept-test
     # tie width
     assert band < 1e-9 * S
+
+
+def test_zero_threshold_is_not_a_tie():
+    """u = 0 draws the first entry with mass on both sides exactly (the
+    threshold and every earlier running sum are exact zeros): no tie, while a
+    threshold a rounding step away from a boundary is one."""
+    C = np.cumsum(np.array([0.0, 0.0, 0.25, 0.75]))
+    band = oracle.accept.sample_tie_band(4, 1.0)
+    assert not oracle.accept.draw_is_tie(0.0, C, 2, band)
+    assert oracle.accept.draw_is_tie(0.25 + band / 2, C, 3, band)
+    assert not oracle.accept.draw_is_tie(0.5, C, 3, band)
+    p = np.array([[0.0, 0.0, 0.25, 0.75], [0.1, 0.2, 0.3, 0.4]], np.float32)
+    q = np.array([[0.0, 0.0, 0.25, 0.75]], np.float32)
+    r = oracle.accept_request(p, q, np.array([3]), np.array([0.0, 0.0], np.float32), 0)
+    assert r["accept_len"] == 1 and r["bonus"] == 0 and not r["tie"]
