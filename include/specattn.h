@@ -54,6 +54,7 @@ extern "C" {
 #define SPEC_ENOTSUP (-2) /* dtype, head_dim or page size not supported    */
 #define SPEC_ENOSPC (-3)  /* workspace smaller than the *_workspace_bytes  */
 #define SPEC_EHIP (-4)    /* the HIP runtime refused the launch            */
+#define SPEC_ESCRATCH (-5) /* sizes exceed an allocation-free call's fixed scratch */
 
 /* err_flags bits, set by kernels */
 #define SPEC_ERR_SLOT 1           /* a page-table entry the call needed is outside [0, num_pages) */
@@ -247,6 +248,35 @@ int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q
                 int32_t* accept_len, int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
                 int32_t* new_seq_lens, void* workspace, size_t ws_bytes, int32_t* err_flags,
                 void* stream);
+
+/*
+ * spec_accept_static -- spec_accept without a workspace argument.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and outputs as spec_accept, bit for bit, with the workspace
+ * taken from a fixed device array the library owns, one copy per GPU, kept
+ * until the process ends. The call allocates nothing and frees nothing.
+ *
+ *   arguments and outputs: as spec_accept, without workspace / ws_bytes
+ * Limit: spec_accept_workspace_bytes(bs, K, V, greedy) must not exceed
+ *   SPEC_ACCEPT_STATIC_SCRATCH_BYTES (4 MiB: for V = 151936 about 880
+ *   requests of the stochastic accept); larger calls return SPEC_ESCRATCH and
+ *   launch nothing.
+ * Concurrency: every call on one GPU uses that GPU's one array, so calls that
+ *   may run at the same time on one GPU (unordered streams) race on it and
+ *   must be ordered by the caller. Its contents persist between calls; no
+ *   call depends on them.
+ * Errors: those of spec_accept (SPEC_ENOSPC excepted), SPEC_ESCRATCH, and
+ *   SPEC_EHIP when the array's device address cannot be obtained.
+ */
+#define SPEC_ACCEPT_STATIC_SCRATCH_BYTES (4u << 20)
+
+int spec_accept_static(int bs, int K, int V, int greedy, const float* p, const float* q,
+                       const int32_t* draft, const float* u, const int32_t* seq_lens,
+                       int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                       int32_t* out_tokens, int32_t* new_seq_lens, int32_t* err_flags,
+                       void* stream);
 
 /*
  * spec_accept_tree -- speculative accept for a token tree (tree verify).

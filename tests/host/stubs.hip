@@ -63,6 +63,7 @@ hipError_t launch_accept_logits(const SampArgs& a, bool, hipStream_t) {
   require(a.tmax && a.kept_ids && a.kept_probs && a.n_kept, "logits accept workspace");
   return hipErrorInvalidValue;
 }
+hipError_t scratch_on_current_device(void**, size_t*) { return hipErrorNoDevice; }
 hipError_t launch_commit_kv(const CommitArgs& a, bool, hipStream_t) {
   require(a.B >= 1 && a.B <= 64, "commit block");
   return hipErrorInvalidValue;

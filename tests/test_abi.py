@@ -342,3 +342,22 @@ def test_binding_rejects_bad_buffers_before_any_launch():
         b.block_attn_call(1, q, torch.zeros((4, 1, 16, 64)), torch.zeros((4, 1, 64, 16)),
                           torch.zeros((2, 2), dtype=torch.int32),
                           torch.zeros(2, dtype=torch.int32), 64)
+
+
+def test_static_accept_rejects_before_any_launch(lib):
+    """spec_accept_static checks like spec_accept, and refuses sizes whose
+    workspace would not fit its fixed per-GPU scratch (SPEC_ESCRATCH), all
+    on the host."""
+    def call(bs=4, K=15, V=151936, greedy=0, p=FAKE, q=FAKE):
+        return lib.spec_accept_static(bs, K, V, greedy, p, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, None, None)
+    assert call(bs=0) == b.SPEC_EINVAL
+    assert call(K=64) == b.SPEC_EINVAL
+    assert call(p=None) == b.SPEC_EINVAL
+    assert call(q=None) == b.SPEC_EINVAL
+    assert call(V=(1 << 19) + 1) == b.SPEC_ENOTSUP
+    big = 1024
+    assert lib.spec_accept_workspace_bytes(big, 15, 151936, 0) > b.ACCEPT_STATIC_SCRATCH_BYTES
+    assert call(bs=big) == b.SPEC_ESCRATCH
+    assert lib.spec_accept_workspace_bytes(256, 15, 151936, 0) <= b.ACCEPT_STATIC_SCRATCH_BYTES
+    assert b"scratch" in lib.spec_status_string(b.SPEC_ESCRATCH)

@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 _LIB = None
 
-SPEC_OK, SPEC_EINVAL, SPEC_ENOTSUP, SPEC_ENOSPC, SPEC_EHIP = 0, -1, -2, -3, -4
+SPEC_OK, SPEC_EINVAL, SPEC_ENOTSUP, SPEC_ENOSPC, SPEC_EHIP, SPEC_ESCRATCH = 0, -1, -2, -3, -4, -5
+ACCEPT_STATIC_SCRATCH_BYTES = 4 << 20  # SPEC_ACCEPT_STATIC_SCRATCH_BYTES
 ERR_SLOT, ERR_CAPACITY, ERR_TOKEN, ERR_ZERO_RESIDUAL, ERR_TREE = 1, 2, 4, 8, 16
 BIDIR, CAUSAL, MIXED, TREE = 0, 1, 2, 3
 F32, BF16 = 0, 1
@@ -45,6 +46,7 @@ _SIGS = {
                                   _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "spec_accept": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _c_size, _vp, _vp]),
+    "spec_accept_static": (_c_int, [_c_int] * 4 + [_vp] * 12),
     "spec_commit_kv": (_c_int, [_c_int] * 8 + [_vp] * 9),
     "spec_accept_tree_commit": (_c_int, [_c_int] * 3 + [_vp] * 11 + [_c_int] * 6 +
                                 [_vp] * 5 + [_c_size, _vp, _vp]),
@@ -447,6 +449,51 @@ def accept(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, 
     """Speculative accept / bonus (spec_accept). Returns a dict of int32 tensors:
     accept_len, commit_len, bonus, out_tokens [bs, K+1], new_seq_lens."""
     enqueue, out = accept_call(p, q, draft, u, seq_lens, greedy, out, ws, err, stream)
+    enqueue()
+    return out
+
+
+def accept_static_call(p, q, draft, u, seq_lens, greedy=False, out=None, err=None,
+                       stream=None):
+    """Checks the arguments of spec_accept_static once and returns (enqueue,
+    out): the accept of accept_call with its workspace in the library's fixed
+    per-GPU array (no workspace tensor; calls on one GPU must be ordered)."""
+    torch = _torch()
+    bs, K1, V = p.shape
+    K = K1 - 1
+    _need(p, "p", torch.float32)
+    _need(draft, "draft", torch.int32, (bs, K))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    if not greedy:
+        _need(q, "q", torch.float32, (bs, K, V))
+        _need(u, "u", torch.float32, (bs, K + 1))
+    _need_err(err)
+    dev = p.device
+    out = _need_out(out, _accept_outputs(bs, K + 1), dev)
+    if accept_workspace_bytes(bs, K, V, greedy) > ACCEPT_STATIC_SCRATCH_BYTES:
+        raise SpecError(f"spec_accept_static: bs {bs}, K {K}, V {V} need more than the "
+                        f"{ACCEPT_STATIC_SCRATCH_BYTES} bytes of fixed scratch")
+    _same_device(p, None if greedy else q, draft, None if greedy else u, seq_lens, err,
+                 *out.values())
+    args = (bs, K, V, int(bool(greedy)), _ptr(p), _ptr(q), _ptr(draft), _ptr(u), _ptr(seq_lens),
+            _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
+            _ptr(out["out_tokens"]), _ptr(out["new_seq_lens"]), _ptr(err), _stream(stream))
+    fn = load().spec_accept_static
+    keep = (p, q, draft, u, seq_lens, out, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_accept_static")
+
+    return enqueue, out
+
+
+def accept_static(p, q, draft, u, seq_lens, greedy=False, out=None, err=None, stream=None):
+    """Speculative accept / bonus without a workspace (spec_accept_static):
+    the outputs of accept()."""
+    enqueue, out = accept_static_call(p, q, draft, u, seq_lens, greedy, out, err, stream)
     enqueue()
     return out
 

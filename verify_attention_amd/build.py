@@ -10,7 +10,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["capi.hip", "attn.hip", "prepare.hip", "accept.hip", "sampling.hip", "commit.hip"]
+SOURCES = ["capi.hip", "attn.hip", "prepare.hip", "accept.hip", "sampling.hip", "commit.hip",
+           "scratch.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -146,6 +146,7 @@ SPEC_API const char* spec_status_string(int status) {
     case SPEC_ENOTSUP: return "unsupported dtype, head dim or page size";
     case SPEC_ENOSPC: return "workspace too small";
     case SPEC_EHIP: return "HIP launch failed";
+    case SPEC_ESCRATCH: return "sizes exceed the fixed scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -285,11 +286,15 @@ SPEC_API size_t spec_accept_workspace_bytes(int bs, int K, int V, int greedy) {
   return plan_accept(bs, K, V, greedy).ws_bytes;
 }
 
-SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q,
-                         const int32_t* draft, const float* u, const int32_t* seq_lens,
-                         int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
-                         int32_t* out_tokens, int32_t* new_seq_lens, void* workspace,
-                         size_t ws_bytes, int32_t* err_flags, void* stream) {
+namespace {
+
+// Checks shared by the linear accept entry points; fills the kernels'
+// arguments (workspace pointers excepted) and the plan.
+int accept_check_args(int bs, int K, int V, int greedy, const float* p, const float* q,
+                        const int32_t* draft, const float* u, const int32_t* seq_lens,
+                        int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                        int32_t* out_tokens, int32_t* new_seq_lens, int32_t* err_flags,
+                        AcceptArgs* a, AccPlan* plan) {
   if (bs <= 0 || K < 1 || K > 63 || V <= 0) return SPEC_EINVAL;
   if ((long long)bs * (K + 1) > INT_MAX) return SPEC_EINVAL;
   if (!p || !draft || !seq_lens || !accept_len || !commit_len || !bonus || !out_tokens ||
@@ -297,26 +302,29 @@ SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const
     return SPEC_EINVAL;
   if (!greedy && (!q || !u)) return SPEC_EINVAL;
   if (!greedy && V > kMaxAcceptVocab) return SPEC_ENOTSUP;
-  const AccPlan plan = plan_accept(bs, K, V, greedy);
-  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
-  char* ws = static_cast<char*>(workspace);
-  AcceptArgs a;
-  a.p = p;
-  a.q = q;
-  a.draft = draft;
-  a.u = u;
-  a.seq_lens = seq_lens;
-  a.accept_len = accept_len;
-  a.commit_len = commit_len;
-  a.bonus = bonus;
-  a.out_tokens = out_tokens;
-  a.new_seq_lens = new_seq_lens;
-  a.err = err_flags;
-  a.bs = bs;
-  a.K = K;
-  a.V = V;
-  a.nchunk = plan.nchunk;
-  a.chunk = plan.chunk;
+  *plan = plan_accept(bs, K, V, greedy);
+  *a = AcceptArgs{};
+  a->p = p;
+  a->q = q;
+  a->draft = draft;
+  a->u = u;
+  a->seq_lens = seq_lens;
+  a->accept_len = accept_len;
+  a->commit_len = commit_len;
+  a->bonus = bonus;
+  a->out_tokens = out_tokens;
+  a->new_seq_lens = new_seq_lens;
+  a->err = err_flags;
+  a->bs = bs;
+  a->K = K;
+  a->V = V;
+  a->nchunk = plan->nchunk;
+  a->chunk = plan->chunk;
+  return SPEC_OK;
+}
+
+// Launches the linear accept with its workspace at ws (plan.ws_bytes bytes).
+int accept_launch(AcceptArgs a, const AccPlan& plan, char* ws, int greedy, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (greedy) {
     a.partial = nullptr;
@@ -328,6 +336,23 @@ SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const
   a.partial = reinterpret_cast<double*>(ws + plan.off_partial);
   a.greedy_ids = nullptr;
   return hip_status(launch_accept(a, s));
+}
+
+}  // namespace
+
+SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q,
+                         const int32_t* draft, const float* u, const int32_t* seq_lens,
+                         int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                         int32_t* out_tokens, int32_t* new_seq_lens, void* workspace,
+                         size_t ws_bytes, int32_t* err_flags, void* stream) {
+  AcceptArgs a;
+  AccPlan plan;
+  const int st = accept_check_args(bs, K, V, greedy, p, q, draft, u, seq_lens, accept_len,
+                                     commit_len, bonus, out_tokens, new_seq_lens, err_flags, &a,
+                                     &plan);
+  if (st != SPEC_OK) return st;
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  return accept_launch(a, plan, static_cast<char*>(workspace), greedy, stream);
 }
 
 SPEC_API size_t spec_accept_tree_workspace_bytes(int bs, int N, int V) {
@@ -569,4 +594,27 @@ SPEC_API int spec_commit_kv(int dtype, int bs, int B, int Hkv, int D, int page_s
   a.max_pages = max_pages;
   a.num_pages = num_pages;
   return hip_status(launch_commit_kv(a, dtype == SPEC_BF16, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------ accept without a workspace
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the linear accept with its workspace in the library's fixed per-GPU
+// scratch array (scratch.hip) instead of a caller's buffer.
+SPEC_API int spec_accept_static(int bs, int K, int V, int greedy, const float* p, const float* q,
+                                const int32_t* draft, const float* u, const int32_t* seq_lens,
+                                int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                                int32_t* out_tokens, int32_t* new_seq_lens, int32_t* err_flags,
+                                void* stream) {
+  AcceptArgs a;
+  AccPlan plan;
+  const int st = accept_check_args(bs, K, V, greedy, p, q, draft, u, seq_lens, accept_len,
+                                     commit_len, bonus, out_tokens, new_seq_lens, err_flags, &a,
+                                     &plan);
+  if (st != SPEC_OK) return st;
+  if (plan.ws_bytes > SPEC_ACCEPT_STATIC_SCRATCH_BYTES) return SPEC_ESCRATCH;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (scratch_on_current_device(&ws, &ws_bytes) != hipSuccess) return SPEC_EHIP;
+  if (ws_bytes < plan.ws_bytes) return SPEC_ESCRATCH;
+  return accept_launch(a, plan, static_cast<char*>(ws), greedy, stream);
 }

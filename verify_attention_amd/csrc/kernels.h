@@ -132,6 +132,10 @@ struct CommitArgs {
 
 hipError_t launch_commit_kv(const CommitArgs& a, bool bf16, hipStream_t stream);
 
+// Device address and size of the current GPU's copy of the library's fixed
+// scratch array (scratch.hip), for the allocation-free entry points.
+hipError_t scratch_on_current_device(void** ptr, size_t* bytes);
+
 hipError_t launch_sampling_filter(const SampArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_logits(const SampArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream);
