@@ -19,12 +19,14 @@ Modules:
                accept on processed target and draft rows
   commit    -- the committed prefix's K/V after an accept (the accepted tree
                path moved to contiguous positions) and the released slots
+  quadratic -- the quadratic layout's hand-off: the next round's drafts from
+               the MASK group after the last accepted spine token
 
 Parity status: every function here is pinned by CPU tests against closed
 forms, library routines, brute force or exact enumeration (see the tests
 named test_oracle_*). None is "parity unpinned".
 """
-from .prepare import prepare_block
+from .prepare import prepare_block, prepare_tree, tree_depths
 from .attention import (BIDIR, CAUSAL, MIXED, TREE, visible, block_attn_rows,
                         block_attn_dense, attn_row, unpage_kv, mask_matrix)
 from .accept import (accept_request, accept_batch, greedy_accept_request, argmax_lowest,
@@ -32,9 +34,10 @@ from .accept import (accept_request, accept_batch, greedy_accept_request, argmax
 from .sampling import (sampling_filter, rank_order, accept_logits_request,
                        accept_logits_batch)
 from .commit import commit_kv, slot_of
+from . import quadratic
 
 __all__ = [
-    "prepare_block", "BIDIR", "CAUSAL", "MIXED", "TREE", "visible", "block_attn_rows",
+    "prepare_block", "prepare_tree", "tree_depths", "quadratic", "BIDIR", "CAUSAL", "MIXED", "TREE", "visible", "block_attn_rows",
     "block_attn_dense", "attn_row", "unpage_kv", "mask_matrix", "accept_request", "accept_batch",
     "greedy_accept_request", "argmax_lowest", "tree_accept_request", "tree_children",
     "sampling_filter", "rank_order", "accept_logits_request", "accept_logits_batch",

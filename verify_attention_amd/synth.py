@@ -311,6 +311,23 @@ def quadratic_layout(k: int):
     return role, masks
 
 
+def quadratic_parents(k: int) -> np.ndarray:
+    """Position order of the quadratic layout as parents: spine token i
+    follows spine token i - 1; member 0 of group G_j follows spine token j and
+    member m follows member m - 1 (the layout's tokens after spine token j).
+    Only the positions come from this; the attention masks are those of
+    quadratic_layout."""
+    n = (k + 1) * (k + 1)
+    parent = np.full(n, -1, dtype=np.int32)
+    for pos in range(1, n):
+        j, m = divmod(pos, k + 1)
+        if m == 0:
+            parent[pos] = (j - 1) * (k + 1)
+        else:
+            parent[pos] = j * (k + 1) if m == 1 else pos - 1
+    return parent
+
+
 def make_trees(cfg: RoundConfig, seed: int, per_request=True):
     """Token trees for a TREE round: parents [bs, B] and row masks [bs, B]
     (per_request), or one tree shared by the batch ([B] each)."""
