@@ -6,6 +6,7 @@
  * HIP stream and without any host/device synchronisation:
  *
  *   spec_prepare_block  (draft pass)  -> block ids / positions / KV slots
+ *                        (spec_prepare_tree for a tree or quadratic block)
  *   [caller writes the block's K/V at the slots]
  *   block_attn(SPEC_BIDIR)            -> draft-pass attention
  *   spec_draft_argmax                 -> greedy draft tokens
@@ -13,6 +14,8 @@
  *   block_attn(SPEC_CAUSAL | SPEC_MIXED), or block_attn_tree for a token tree
  *   [caller produces target rows p]
  *   spec_accept (or spec_accept_tree) -> accepted prefix, bonus, new lengths
+ *                        (spec_accept_prepare also prepares the next block)
+ *   spec_commit_kv / spec_quadratic_handoff -> committed K/V, next drafts
  *
  * Conventions shared by every call
  * --------------------------------
@@ -103,6 +106,44 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
                        const int32_t* seq_lens, const int32_t* page_table,
                        const int32_t* draft_tokens, int32_t* block_ids, int32_t* positions,
                        int32_t* cache_loc, int32_t* err_flags, void* stream);
+
+/*
+ * spec_prepare_tree -- the block of one round when its tokens form a tree
+ * (or any layout given as parents in position order), for every request.
+ *
+ * Follows the block preparation of "From DFlash to dLLM Self-Spec (2): SGLang
+ * Spec V2", section 2.2.2 (ids, positions and KV locations of the block in one
+ * step), for a block laid out as the Tree sampler of "Unlocking Lossless
+ * Speedups in LLMs via Discrete Diffusion" verifies it (method steps: top
+ * candidates kept as a tree of prefixes) or as the quadratic layout of "From
+ * DFlash to dLLM Self-Spec (4)", section 4.4.1 (MASK groups after every
+ * speculative token). Node n sits at block row n (node 0, the root, is the
+ * previous round's verified token):
+ *   block_ids[b,0] = verified_id[b]; block_ids[b,n] = node_tokens[b,n] (or
+ *   mask_token_id when node_tokens is NULL);
+ *   positions[b,n] = L_b + depth(n), depth(0) = 0, depth(n) = depth(parent) + 1
+ *   (a node continues its parent's sequence: siblings share a position);
+ *   cache_loc[b,n] = the slot of position L_b + n (node n's K/V go to the
+ *   n-th slot after the committed prefix, as block_attn_tree reads them).
+ *
+ *   bs, N           requests and block nodes (1..64)
+ *   page_size, max_pages, num_pages, mask_token_id, verified_id, seq_lens,
+ *   page_table      as spec_prepare_block
+ *   parent          [N] (parent_per_request == 0) or [bs, N]; parent[0] is not
+ *                   read; node n >= 1 needs 0 <= parent < n
+ *   node_tokens     [bs, N] or NULL (node_tokens[b,0] is not read)
+ * Outputs: block_ids, positions, cache_loc [bs, N]. A node whose parent is
+ *   not an earlier node, or that descends from one, gets position -1 and sets
+ *   SPEC_ERR_TREE; missing slots give -1 with SPEC_ERR_SLOT, and L_b + N past
+ *   the page-table row sets SPEC_ERR_CAPACITY.
+ * Errors: SPEC_EINVAL for bs <= 0, N outside 1..64, page_size, max_pages or
+ *   num_pages <= 0, or a NULL required pointer.
+ */
+int spec_prepare_tree(int bs, int N, int page_size, int max_pages, int num_pages,
+                      int32_t mask_token_id, const int32_t* verified_id, const int32_t* seq_lens,
+                      const int32_t* page_table, const int32_t* parent, int parent_per_request,
+                      const int32_t* node_tokens, int32_t* block_ids, int32_t* positions,
+                      int32_t* cache_loc, int32_t* err_flags, void* stream);
 
 /*
  * block_attn -- block-query attention over the paged KV cache.
@@ -206,6 +247,41 @@ int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* t
                       void* stream);
 
 /*
+ * spec_quadratic_handoff -- the next round's drafts from a quadratic block.
+ *
+ * Follows "From DFlash to dLLM Self-Spec (4)", section 4.4.1 (the paragraph
+ * comparing recursive compaction with Quadratic Decoding: MASK tokens among
+ * the speculative tokens keep supplying speculative tokens for the next step
+ * after a speculative position fails) and "Unlocking Lossless Speedups in LLMs
+ * via Discrete Diffusion", future work (2) (draft and verify in one forward).
+ * The block of k drafts has n = (k + 1)^2 rows: the spine (root, s_1 .. s_k)
+ * at rows i * (k + 1), and after spine token j the group G_j of k MASK rows
+ * j * (k + 1) + 1 + m. When the accept keeps a = accept_len[b] drafts, the
+ * correction takes the position after s_a and G_a's members propose the k
+ * tokens after it:
+ *   next_draft[b,m] = smallest index among the maxima of
+ *   logits[b, a * (k + 1) + 1 + m, :] (NaN never wins), m = 0 .. k-1;
+ *   next_block[b] (nullable) = the next round's quadratic block tokens:
+ *   row 0 = bonus[b], row (m + 1) * (k + 1) = next_draft[b,m], every group
+ *   row = mask_token_id.
+ * Only the k rows of G_a are read per request.
+ *
+ *   bs, k, V        requests, drafts per block (1..7), vocabulary
+ *   dtype           SPEC_BF16 or SPEC_F32 logits [bs, (k + 1)^2, V]
+ *   accept_len [bs] as spec_accept returns it (0..k); bonus [bs] (needed only
+ *   with next_block)
+ * Outputs: next_draft [bs, k], next_block [bs, (k + 1)^2] or NULL. An
+ *   accept_len outside 0..k gives drafts of -1 and sets SPEC_ERR_TREE.
+ * The accepted spine becomes contiguous with spec_commit_kv(B = (k + 1)^2,
+ *   path_nodes[b, i] = (i + 1) * (k + 1)).
+ * Errors: SPEC_EINVAL (sizes, NULL), SPEC_ENOTSUP (dtype).
+ */
+int spec_quadratic_handoff(int bs, int k, int V, int dtype, const void* logits,
+                           const int32_t* accept_len, const int32_t* bonus,
+                           int32_t mask_token_id, int32_t* next_draft, int32_t* next_block,
+                           int32_t* err_flags, void* stream);
+
+/*
  * spec_accept -- speculative accept / bonus epilogue.
  *
  * Follows "Unlocking Lossless Speedups in LLMs via Discrete Diffusion"
@@ -248,6 +324,36 @@ int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q
                 int32_t* accept_len, int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
                 int32_t* new_seq_lens, void* workspace, size_t ws_bytes, int32_t* err_flags,
                 void* stream);
+
+/*
+ * spec_accept_prepare -- spec_accept, then the next round's block in the same
+ * call.
+ *
+ * The accept outputs are the next round's inputs ("From DFlash to dLLM
+ * Self-Spec (2)", section 2.2.5: the bonus becomes the next verified id and
+ * the new lengths the next committed lengths; section 2.2.2: the next round
+ * starts by preparing its block from them). Every output equals that of
+ * spec_accept followed by spec_prepare_block(bs, B_next, page_size,
+ * max_pages, num_pages, mask_token_id, verified_id = bonus, seq_lens =
+ * new_seq_lens, page_table, draft_tokens = NULL): the next draft pass's block
+ * (token 0 = the bonus, the rest the mask token), its positions and slots.
+ * One launch fewer: the accept's last kernel writes the block.
+ *
+ *   the accept's arguments and outputs: as spec_accept (same workspace)
+ *   B_next, page_size, max_pages, num_pages, mask_token_id, page_table: as
+ *   spec_prepare_block
+ * Outputs also: block_ids, positions, cache_loc [bs, B_next], with the data
+ *   errors spec_prepare_block reports.
+ * Errors: those of both calls.
+ */
+int spec_accept_prepare(int bs, int K, int V, int greedy, const float* p, const float* q,
+                        const int32_t* draft, const float* u, const int32_t* seq_lens,
+                        int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                        int32_t* out_tokens, int32_t* new_seq_lens, int B_next, int page_size,
+                        int max_pages, int num_pages, int32_t mask_token_id,
+                        const int32_t* page_table, int32_t* block_ids, int32_t* positions,
+                        int32_t* cache_loc, void* workspace, size_t ws_bytes, int32_t* err_flags,
+                        void* stream);
 
 /*
  * spec_accept_static -- spec_accept without a workspace argument.

@@ -35,6 +35,15 @@ hipError_t launch_prepare_block(const PrepareArgs& a, hipStream_t) {
   require(a.bs > 0 && a.B > 0, "prepare sizes");
   return hipErrorInvalidValue;
 }
+hipError_t launch_prepare_tree(const PrepareTreeArgs& a, hipStream_t) {
+  require(a.bs > 0 && a.N >= 1 && a.N <= 64 && a.parent, "prepare_tree sizes");
+  return hipErrorInvalidValue;
+}
+hipError_t launch_quadratic_handoff(const HandoffArgs& h, bool, hipStream_t) {
+  require(h.k >= 1 && h.k <= 7 && h.n == (h.k + 1) * (h.k + 1), "handoff layout");
+  require(!h.next_block || h.bonus, "handoff block needs the bonus");
+  return hipErrorInvalidValue;
+}
 hipError_t launch_argmax_rows(const void*, bool, int rows, int V, int32_t*, hipStream_t) {
   require(rows > 0 && V > 0, "argmax sizes");
   return hipErrorInvalidValue;
@@ -42,6 +51,7 @@ hipError_t launch_argmax_rows(const void*, bool, int rows, int V, int32_t*, hipS
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t) {
   require(a.nchunk >= 1 && (long long)a.nchunk * a.chunk >= a.V, "chunks cover V");
   require(a.partial && a.jbuf, "accept workspace");
+  require(!a.next_ids || (a.next_pos && a.next_loc && a.next_tab && a.next_B > 0), "next block");
   return hipErrorInvalidValue;
 }
 hipError_t launch_greedy_accept(const AcceptArgs& a, hipStream_t) {

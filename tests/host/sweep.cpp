@@ -64,6 +64,29 @@ int main() {
   // prepare, argmax
   EXPECT(spec_prepare_block(32, 16, 16, 80, 300, 7, I, I, I, I, I, I, I, I, nullptr), SPEC_EHIP);
   EXPECT(spec_prepare_block(0, 16, 16, 80, 300, 7, I, I, I, I, I, I, I, I, nullptr), SPEC_EINVAL);
+  for (int N : {1, 5, 25, 64})
+    for (int per : {0, 1}) {
+      EXPECT(spec_prepare_tree(32, N, 16, 80, 300, 7, I, I, I, I, per, I, I, I, I, I, nullptr),
+             SPEC_EHIP);
+      EXPECT(spec_prepare_tree(32, N, 16, 80, 300, 7, I, I, I, I, per, nullptr, I, I, I, nullptr,
+                               nullptr),
+             SPEC_EHIP);
+    }
+  EXPECT(spec_prepare_tree(32, 65, 16, 80, 300, 7, I, I, I, I, 0, I, I, I, I, I, nullptr),
+         SPEC_EINVAL);
+  EXPECT(spec_prepare_tree(32, 8, 16, 80, 300, 7, I, I, I, nullptr, 0, I, I, I, I, I, nullptr),
+         SPEC_EINVAL);
+  for (int k = 1; k <= 7; ++k) {
+    EXPECT(spec_quadratic_handoff(32, k, 151936, SPEC_BF16, F, I, I, 9, I, I, I, nullptr),
+           SPEC_EHIP);
+    EXPECT(spec_quadratic_handoff(32, k, 151936, SPEC_F32, F, I, nullptr, 9, I, nullptr, I,
+                                  nullptr),
+           SPEC_EHIP);
+  }
+  EXPECT(spec_quadratic_handoff(32, 8, 151936, SPEC_BF16, F, I, I, 9, I, I, I, nullptr),
+         SPEC_EINVAL);
+  EXPECT(spec_quadratic_handoff(32, 4, 151936, SPEC_BF16, F, I, nullptr, 9, I, I, I, nullptr),
+         SPEC_EINVAL);  // a next block needs the bonus
   EXPECT(spec_draft_argmax(1984, 157184, SPEC_BF16, F, I, nullptr), SPEC_EHIP);
   EXPECT(spec_draft_argmax(0, 157184, SPEC_BF16, F, I, nullptr), SPEC_EINVAL);
 
@@ -75,6 +98,24 @@ int main() {
           const size_t ws = spec_accept_workspace_bytes(bs, K, V, greedy);
           EXPECT(spec_accept(bs, K, V, greedy, FL, FL, I, FL, I, I, I, I, I, I, F, ws, I, nullptr),
                  SPEC_EHIP);
+        }
+        for (int Bn : {1, 16, 300}) {
+          const size_t ws = spec_accept_workspace_bytes(bs, K, V, 0);
+          EXPECT(spec_accept_prepare(bs, K, V, 0, FL, FL, I, FL, I, I, I, I, I, I, Bn, 16, 80,
+                                     300, 7, I, I, I, I, F, ws, I, nullptr),
+                 V > 524288 ? SPEC_ENOTSUP : SPEC_EHIP);
+          EXPECT(spec_accept_prepare(bs, K, V, 0, FL, FL, I, FL, I, I, I, I, I, I, Bn, 16, 80,
+                                     300, 7, nullptr, I, I, I, F, ws, I, nullptr),
+                 SPEC_EINVAL);
+          if (ws > 0)
+            EXPECT(spec_accept_prepare(bs, K, V, 0, FL, FL, I, FL, I, I, I, I, I, I, Bn, 16, 80,
+                                       300, 7, I, I, I, I, F, ws - 1, I, nullptr),
+                   SPEC_ENOSPC);
+        }
+        {
+          const size_t ws = spec_accept_workspace_bytes(bs, K, V, 0);
+          EXPECT(spec_accept_static(bs, K, V, 0, FL, FL, I, FL, I, I, I, I, I, I, I, nullptr),
+                 ws > SPEC_ACCEPT_STATIC_SCRATCH_BYTES ? SPEC_ESCRATCH : SPEC_EHIP);
         }
         const int N = K + 1;
         const size_t wt = spec_accept_tree_workspace_bytes(bs, N, V);
@@ -112,7 +153,7 @@ int main() {
   EXPECT(spec_commit_kv(SPEC_BF16, 32, 65, 8, 128, 16, 80, 300, I, I, I, I, F, F, I, I, nullptr),
          SPEC_EINVAL);
 
-  for (int st : {0, -1, -2, -3, -4, -99}) (void)spec_status_string(st);
+  for (int st : {0, -1, -2, -3, -4, -5, -99}) (void)spec_status_string(st);
   std::printf(fails ? "sweep: %d failures\n" : "sweep ok (%d failures)\n", fails);
   return fails ? 1 : 0;
 }

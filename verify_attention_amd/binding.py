@@ -32,6 +32,12 @@ _SIGS = {
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_prepare_block": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_int32,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "spec_prepare_tree": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_int32,
+                                   _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "spec_quadratic_handoff": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                        ctypes.c_int32, _vp, _vp, _vp, _vp]),
+    "spec_accept_prepare": (_c_int, [_c_int] * 4 + [_vp] * 10 + [_c_int] * 4 +
+                            [ctypes.c_int32] + [_vp] * 5 + [_c_size, _vp, _vp]),
     "block_attn_workspace_bytes": (_c_size, [_c_int] * 6),
     "block_attn": (_c_int, [_c_int, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _f, _vp,
@@ -261,6 +267,56 @@ def prepare_block(verified_id, seq_lens, page_table, page_size, block, mask_toke
     return out
 
 
+def prepare_tree_call(verified_id, seq_lens, page_table, page_size, parent, mask_token_id,
+                      num_pages, node_tokens=None, out=None, err=None, stream=None):
+    """Checks the arguments of spec_prepare_tree once and returns (enqueue,
+    out). parent: int32 [N] (one layout for the batch) or [bs, N];
+    node_tokens: int32 [bs, N] or None (mask fill); out: block_ids,
+    positions, cache_loc [bs, N]."""
+    torch = _torch()
+    bs = verified_id.shape[0]
+    N = parent.shape[-1]
+    _need(verified_id, "verified_id", torch.int32, (bs,))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need_table(page_table, bs)
+    _need(parent, "parent", torch.int32)
+    if tuple(parent.shape) not in ((N,), (bs, N)):
+        raise ValueError(f"parent must have shape ({N},) or ({bs}, {N})")
+    _need_err(err)
+    if node_tokens is not None:
+        _need(node_tokens, "node_tokens", torch.int32, (bs, N))
+    if out is None:
+        out = tuple(torch.empty((bs, N), dtype=torch.int32, device=verified_id.device)
+                    for _ in range(3))
+    for t, nm in zip(out, ("block_ids", "positions", "cache_loc")):
+        _need(t, nm, torch.int32, (bs, N))
+    _same_device(verified_id, seq_lens, page_table, parent, node_tokens, *out, err)
+    args = (bs, N, page_size, page_table.shape[1], num_pages, mask_token_id, _ptr(verified_id),
+            _ptr(seq_lens), _ptr(page_table), _ptr(parent), int(parent.dim() == 2),
+            _ptr(node_tokens), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(err),
+            _stream(stream))
+    fn = load().spec_prepare_tree
+    keep = (verified_id, seq_lens, page_table, parent, node_tokens, out, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_prepare_tree")
+
+    return enqueue, out
+
+
+def prepare_tree(verified_id, seq_lens, page_table, page_size, parent, mask_token_id, num_pages,
+                 node_tokens=None, out=None, err=None, stream=None):
+    """Block ids, positions (committed length + depth) and KV slots of a tree
+    or quadratic block (spec_prepare_tree)."""
+    enqueue, out = prepare_tree_call(verified_id, seq_lens, page_table, page_size, parent,
+                                     mask_token_id, num_pages, node_tokens, out, err, stream)
+    enqueue()
+    return out
+
+
 def block_attn_call(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n_causal=0,
                     n_causal_per_req=None, sm_scale=0.0, out=None, lse=None, ws=None, err=None,
                     stream=None):
@@ -396,6 +452,50 @@ def draft_argmax_call(logits, out=None, stream=None):
     return enqueue, out
 
 
+def quadratic_handoff_call(logits, accept_len, k, bonus=None, mask_token_id=0, out=None,
+                           err=None, stream=None):
+    """Checks the arguments of spec_quadratic_handoff once and returns
+    (enqueue, out). logits [bs, (k + 1)^2, V] float32 or bfloat16; out:
+    next_draft [bs, k] and, when bonus is given, next_block [bs, (k + 1)^2]."""
+    torch = _torch()
+    bs, n, V = logits.shape
+    if n != (k + 1) * (k + 1):
+        raise ValueError(f"logits must hold (k + 1)^2 = {(k + 1) ** 2} rows per request")
+    _need(logits, "logits")
+    dt = _dtype_code(logits)
+    _need(accept_len, "accept_len", torch.int32, (bs,))
+    if bonus is not None:
+        _need(bonus, "bonus", torch.int32, (bs,))
+    _need_err(err)
+    specs = dict(next_draft=((bs, k),))
+    if bonus is not None:
+        specs["next_block"] = ((bs, n),)
+    out = _need_out(out, specs, logits.device)
+    _same_device(logits, accept_len, bonus, err, *out.values())
+    args = (bs, k, V, dt, _ptr(logits), _ptr(accept_len), _ptr(bonus), mask_token_id,
+            _ptr(out["next_draft"]), _ptr(out.get("next_block")), _ptr(err), _stream(stream))
+    fn = load().spec_quadratic_handoff
+    keep = (logits, accept_len, bonus, out, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_quadratic_handoff")
+
+    return enqueue, out
+
+
+def quadratic_handoff(logits, accept_len, k, bonus=None, mask_token_id=0, out=None, err=None,
+                      stream=None):
+    """Next round's drafts (and block tokens) from a quadratic block
+    (spec_quadratic_handoff)."""
+    enqueue, out = quadratic_handoff_call(logits, accept_len, k, bonus, mask_token_id, out, err,
+                                          stream)
+    enqueue()
+    return out
+
+
 def draft_argmax(logits, out=None, stream=None):
     """Greedy draft tokens: lowest-index argmax of each row of logits [rows, V]."""
     enqueue, out = draft_argmax_call(logits, out, stream)
@@ -443,6 +543,62 @@ def accept_call(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=N
             _check(st, "spec_accept")
 
     return enqueue, out
+
+
+def accept_prepare_call(p, q, draft, u, seq_lens, page_table, page_size, block_next,
+                        mask_token_id, num_pages, greedy=False, out=None, ws=None, err=None,
+                        stream=None):
+    """Checks the arguments of spec_accept_prepare once and returns (enqueue,
+    out): the outputs of accept_call plus block_ids, positions, cache_loc
+    [bs, block_next] of the next round's draft-pass block."""
+    torch = _torch()
+    bs, K1, V = p.shape
+    K = K1 - 1
+    _need(p, "p", torch.float32)
+    _need(draft, "draft", torch.int32, (bs, K))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    if not greedy:
+        _need(q, "q", torch.float32, (bs, K, V))
+        _need(u, "u", torch.float32, (bs, K + 1))
+    _need_table(page_table, bs)
+    _need_err(err)
+    dev = p.device
+    out = _need_out(out, dict(_accept_outputs(bs, K + 1), block_ids=((bs, block_next),),
+                              positions=((bs, block_next),), cache_loc=((bs, block_next),)),
+                    dev)
+    need = accept_workspace_bytes(bs, K, V, greedy)
+    if ws is None:
+        ws = workspace(need, dev)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(p, None if greedy else q, draft, None if greedy else u, seq_lens, page_table, ws,
+                 err, *out.values())
+    args = (bs, K, V, int(bool(greedy)), _ptr(p), _ptr(q), _ptr(draft), _ptr(u), _ptr(seq_lens),
+            _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
+            _ptr(out["out_tokens"]), _ptr(out["new_seq_lens"]), block_next, page_size,
+            page_table.shape[1], num_pages, mask_token_id, _ptr(page_table),
+            _ptr(out["block_ids"]), _ptr(out["positions"]), _ptr(out["cache_loc"]), _ptr(ws),
+            ws_bytes, _ptr(err), _stream(stream))
+    fn = load().spec_accept_prepare
+    keep = (p, q, draft, u, seq_lens, page_table, out, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_accept_prepare")
+
+    return enqueue, out
+
+
+def accept_prepare(p, q, draft, u, seq_lens, page_table, page_size, block_next, mask_token_id,
+                   num_pages, greedy=False, out=None, ws=None, err=None, stream=None):
+    """Speculative accept followed by the next round's draft-pass block in
+    one call (spec_accept_prepare)."""
+    enqueue, out = accept_prepare_call(p, q, draft, u, seq_lens, page_table, page_size,
+                                       block_next, mask_token_id, num_pages, greedy, out, ws, err,
+                                       stream)
+    enqueue()
+    return out
 
 
 def accept(p, q, draft, u, seq_lens, greedy=False, out=None, ws=None, err=None, stream=None):

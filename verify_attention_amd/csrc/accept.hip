@@ -261,6 +261,36 @@ __device__ int draw_from_masses(const double (&mv)[kMaxPer], int i0, int i1, con
   return tok;
 }
 
+// The next round's draft-pass block of request b (spec_accept_prepare): token
+// 0 is the bonus and the others the mask token; positions continue the new
+// committed length; slots come through the page table, as spec_prepare_block
+// forms them (-1 with SPEC_ERR_SLOT when the page is missing, SPEC_ERR_CAPACITY
+// when the block does not fit the table row).
+__device__ void write_next_block(const AcceptArgs& a, int b, int tok, int newL, int tid,
+                                 int nthreads) {
+  const int B = a.next_B, P = a.next_P;
+  if (tid == 0 && (newL < 0 || (long long)newL + B > (long long)a.next_max_pages * P))
+    flag_error(a.err, kErrCapacity);
+  int errs = 0;
+  for (int i = tid; i < B; i += nthreads) {
+    const long long pos = (long long)newL + i;
+    int32_t slot = -1;
+    if (pos >= 0) {
+      const long long n = pos / P;
+      if (n < a.next_max_pages) {
+        const int32_t page = a.next_tab[(size_t)b * a.next_max_pages + n];
+        if (page >= 0 && page < a.next_num_pages) slot = page * P + (int32_t)(pos % P);
+      }
+    }
+    if (slot < 0) errs |= kErrSlot;
+    const size_t e = (size_t)b * B + i;
+    a.next_ids[e] = i == 0 ? tok : a.next_mask;
+    a.next_pos[e] = (int32_t)pos;
+    a.next_loc[e] = slot;
+  }
+  if (errs) flag_error(a.err, errs);
+}
+
 // Kernel 2, one workgroup per request: scan the sub-block masses, find the
 // sub-block where the running mass passes u_K * S, locate the token inside it,
 // write every output. Every load that does not depend on the accept length
@@ -318,6 +348,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a
   if (tid <= K)
     a.out_tokens[(size_t)b * (K + 1) + tid] = tid < j ? dtok : (tid == j ? tok : -1);
   if (tid == 0 && errs) flag_error(a.err, errs);
+  if (a.next_ids) write_next_block(a, b, tok, L + j + 1, tid, kAccThreads);
 }
 
 // ------------------------------------------------------------- tree verify
@@ -598,9 +629,9 @@ __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 // maximum and the vector that first reached it; the winning vector is read
 // again to locate the lowest index holding the value. Then (value, index)
 // reductions over the wave and the workgroup.
+// The whole workgroup scans `row`; the result is valid in thread 0.
 template <typename T>
-__global__ __launch_bounds__(kAccThreads) void argmax_rows_kernel(const T* x, int V, int32_t* out) {
-  const T* row = x + (size_t)blockIdx.x * V;
+__device__ __forceinline__ int argmax_row(const T* row, int V) {
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
   constexpr int kVec = 16 / sizeof(T);
@@ -654,10 +685,62 @@ __global__ __launch_bounds__(kAccThreads) void argmax_rows_kernel(const T* x, in
     s_i[wave] = bi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0)
     for (int w = 1; w < 4; ++w) better(bv, bi, s_v[w], s_i[w]);
-    out[blockIdx.x] = bi == 0x7fffffff ? 0 : bi;
+  return bi == 0x7fffffff ? 0 : bi;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kAccThreads) void argmax_rows_kernel(const T* x, int V, int32_t* out) {
+  const int bi = argmax_row(x + (size_t)blockIdx.x * V, V);
+  if (threadIdx.x == 0) out[blockIdx.x] = bi;
+}
+
+// The quadratic layout's hand-off, one workgroup per (request b, member m):
+// with a = accept_len[b] drafts accepted, member m of the group after spine
+// token a (block row a * (k + 1) + 1 + m) proposes the next round's draft m,
+// its greedy token. The workgroup also writes its share of the next round's
+// block tokens: spine position (m + 1) * (k + 1) = the draft and the group
+// after it = the mask token; member 0's workgroup writes position 0 (the
+// bonus) and group G_0. An accept length outside 0 .. k gives -1 drafts and
+// SPEC_ERR_TREE.
+template <typename T>
+__global__ __launch_bounds__(kAccThreads) void quadratic_handoff_kernel(HandoffArgs h) {
+  const int b = blockIdx.x / h.k;
+  const int m = blockIdx.x - b * h.k;
+  const int k = h.k, tid = threadIdx.x;
+  const int acc = h.accept_len[b];
+  const bool ok = acc >= 0 && acc <= k;  // uniform over the workgroup
+  int tok = -1;
+  if (ok) {
+    const T* row = reinterpret_cast<const T*>(h.logits) +
+                   ((size_t)b * h.n + (size_t)acc * (k + 1) + 1 + m) * h.V;
+    tok = argmax_row(row, h.V);
   }
+  if (tid == 0) {
+    h.next_draft[(size_t)b * k + m] = tok;
+    if (!ok && m == 0) flag_error(h.err, kErrTree);
+  }
+  if (h.next_block) {
+    int32_t* nb = h.next_block + (size_t)b * h.n;
+    const int spine = (m + 1) * (k + 1);
+    if (tid == 0) nb[spine] = tok;
+    else if (tid <= k) nb[spine + tid] = h.mask_token_id;
+    if (m == 0) {
+      if (tid == 0) nb[0] = h.bonus[b];
+      else if (tid <= k) nb[tid] = h.mask_token_id;
+    }
+  }
+}
+
+hipError_t launch_quadratic_handoff(const HandoffArgs& h, bool bf16, hipStream_t stream) {
+  if (bf16)
+    hipLaunchKernelGGL(quadratic_handoff_kernel<__bf16>, dim3(h.bs * h.k), dim3(kAccThreads), 0,
+                       stream, h);
+  else
+    hipLaunchKernelGGL(quadratic_handoff_kernel<float>, dim3(h.bs * h.k), dim3(kAccThreads), 0,
+                       stream, h);
+  return hipGetLastError();
 }
 
 hipError_t launch_argmax_rows(const void* x, bool bf16, int rows, int V, int32_t* out,
@@ -691,6 +774,7 @@ __global__ __launch_bounds__(64) void greedy_commit_kernel(AcceptArgs a) {
   }
   for (int i = lane; i <= K; i += 64)
     a.out_tokens[(size_t)b * (K + 1) + i] = i < j ? a.draft[(size_t)b * K + i] : (i == j ? tok : -1);
+  if (a.next_ids) write_next_block(a, b, tok, a.seq_lens[b] + j + 1, lane, 64);
 }
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {

@@ -179,6 +179,39 @@ SPEC_API int spec_prepare_block(int bs, int B, int page_size, int max_pages, int
   return hip_status(launch_prepare_block(a, static_cast<hipStream_t>(stream)));
 }
 
+SPEC_API int spec_prepare_tree(int bs, int N, int page_size, int max_pages, int num_pages,
+                               int32_t mask_token_id, const int32_t* verified_id,
+                               const int32_t* seq_lens, const int32_t* page_table,
+                               const int32_t* parent, int parent_per_request,
+                               const int32_t* node_tokens, int32_t* block_ids,
+                               int32_t* positions, int32_t* cache_loc, int32_t* err_flags,
+                               void* stream) {
+  if (bs <= 0 || N < 1 || N > 64 || page_size <= 0 || max_pages <= 0 || num_pages <= 0)
+    return SPEC_EINVAL;
+  if ((long long)bs * N > INT_MAX) return SPEC_EINVAL;
+  if (!verified_id || !seq_lens || !page_table || !parent || !block_ids || !positions ||
+      !cache_loc)
+    return SPEC_EINVAL;
+  PrepareTreeArgs a{};
+  a.verified_id = verified_id;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.parent = parent;
+  a.parent_per_req = parent_per_request ? 1 : 0;
+  a.node_tokens = node_tokens;
+  a.block_ids = block_ids;
+  a.positions = positions;
+  a.cache_loc = cache_loc;
+  a.err = err_flags;
+  a.bs = bs;
+  a.N = N;
+  a.P = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.mask_token_id = mask_token_id;
+  return hip_status(launch_prepare_tree(a, static_cast<hipStream_t>(stream)));
+}
+
 SPEC_API size_t block_attn_workspace_bytes(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   if (bs <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || max_kv_len <= 0) return 0;
   return plan_attn(bs, B, Hq, Hkv, D, max_kv_len).ws_bytes;
@@ -281,6 +314,31 @@ SPEC_API int spec_draft_argmax(int rows, int V, int dtype, const void* logits, i
                                        static_cast<hipStream_t>(stream)));
 }
 
+SPEC_API int spec_quadratic_handoff(int bs, int k, int V, int dtype, const void* logits,
+                                    const int32_t* accept_len, const int32_t* bonus,
+                                    int32_t mask_token_id, int32_t* next_draft,
+                                    int32_t* next_block, int32_t* err_flags, void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (bs <= 0 || k < 1 || k > 7 || V <= 0) return SPEC_EINVAL;
+  const int n = (k + 1) * (k + 1);
+  if ((long long)bs * n > INT_MAX) return SPEC_EINVAL;
+  if (!logits || !accept_len || !next_draft || (next_block && !bonus)) return SPEC_EINVAL;
+  HandoffArgs h{};
+  h.logits = logits;
+  h.accept_len = accept_len;
+  h.bonus = bonus;
+  h.next_draft = next_draft;
+  h.next_block = next_block;
+  h.err = err_flags;
+  h.bs = bs;
+  h.k = k;
+  h.n = n;
+  h.V = V;
+  h.mask_token_id = mask_token_id;
+  return hip_status(launch_quadratic_handoff(h, dtype == SPEC_BF16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 SPEC_API size_t spec_accept_workspace_bytes(int bs, int K, int V, int greedy) {
   if (bs <= 0 || K < 1 || K > 63 || V <= 0) return 0;
   return plan_accept(bs, K, V, greedy).ws_bytes;
@@ -352,6 +410,37 @@ SPEC_API int spec_accept(int bs, int K, int V, int greedy, const float* p, const
                                      &plan);
   if (st != SPEC_OK) return st;
   if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  return accept_launch(a, plan, static_cast<char*>(workspace), greedy, stream);
+}
+
+SPEC_API int spec_accept_prepare(int bs, int K, int V, int greedy, const float* p,
+                                 const float* q, const int32_t* draft, const float* u,
+                                 const int32_t* seq_lens, int32_t* accept_len,
+                                 int32_t* commit_len, int32_t* bonus, int32_t* out_tokens,
+                                 int32_t* new_seq_lens, int B_next, int page_size, int max_pages,
+                                 int num_pages, int32_t mask_token_id, const int32_t* page_table,
+                                 int32_t* block_ids, int32_t* positions, int32_t* cache_loc,
+                                 void* workspace, size_t ws_bytes, int32_t* err_flags,
+                                 void* stream) {
+  AcceptArgs a;
+  AccPlan plan;
+  const int st = accept_check_args(bs, K, V, greedy, p, q, draft, u, seq_lens, accept_len,
+                                     commit_len, bonus, out_tokens, new_seq_lens, err_flags, &a,
+                                     &plan);
+  if (st != SPEC_OK) return st;
+  if (B_next <= 0 || page_size <= 0 || max_pages <= 0 || num_pages <= 0) return SPEC_EINVAL;
+  if ((long long)bs * B_next > INT_MAX) return SPEC_EINVAL;
+  if (!page_table || !block_ids || !positions || !cache_loc) return SPEC_EINVAL;
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  a.next_ids = block_ids;
+  a.next_pos = positions;
+  a.next_loc = cache_loc;
+  a.next_tab = page_table;
+  a.next_B = B_next;
+  a.next_P = page_size;
+  a.next_max_pages = max_pages;
+  a.next_num_pages = num_pages;
+  a.next_mask = mask_token_id;
   return accept_launch(a, plan, static_cast<char*>(workspace), greedy, stream);
 }
 

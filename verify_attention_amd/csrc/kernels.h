@@ -51,6 +51,39 @@ struct PrepareArgs {
 
 hipError_t launch_prepare_block(const PrepareArgs& a, hipStream_t stream);
 
+// A block given as parents in position order (a token tree, or the quadratic
+// layout's position order): ids, positions L + depth(n), slots of L + n.
+struct PrepareTreeArgs {
+  const int32_t* verified_id;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  const int32_t* parent;       // [N] or [bs][N]
+  const int32_t* node_tokens;  // [bs][N] or null (mask fill)
+  int32_t* block_ids;
+  int32_t* positions;
+  int32_t* cache_loc;
+  int32_t* err;
+  int bs, N, P, max_pages, num_pages, parent_per_req;
+  int32_t mask_token_id;
+};
+
+hipError_t launch_prepare_tree(const PrepareTreeArgs& a, hipStream_t stream);
+
+// The quadratic layout's hand-off: the greedy tokens of the group after the
+// last accepted spine token become the next round's drafts.
+struct HandoffArgs {
+  const void* logits;          // [bs][n][V], n = (k + 1)^2
+  const int32_t* accept_len;   // [bs]
+  const int32_t* bonus;        // [bs] (next block's root), may be null without next_block
+  int32_t* next_draft;         // [bs][k]
+  int32_t* next_block;         // [bs][n] or null
+  int32_t* err;
+  int bs, k, n, V;
+  int32_t mask_token_id;
+};
+
+hipError_t launch_quadratic_handoff(const HandoffArgs& a, bool bf16, hipStream_t stream);
+
 hipError_t launch_argmax_rows(const void* x, bool bf16, int rows, int V, int32_t* out,
                               hipStream_t stream);
 
@@ -81,6 +114,14 @@ struct AcceptArgs {
   const int32_t* commit_tab;      // page_table [bs][commit_max_pages]
   int32_t* commit_freed;          // [bs][N] released slots
   int commit_bf16, commit_Hkv, commit_D, commit_P, commit_max_pages, commit_num_pages;
+  // linear accept with the next round's block (spec_accept_prepare; next_ids
+  // null: none): the draft-pass block of B_next tokens at the new lengths
+  int32_t* next_ids;              // [bs][next_B]
+  int32_t* next_pos;              // [bs][next_B]
+  int32_t* next_loc;              // [bs][next_B]
+  const int32_t* next_tab;        // page_table [bs][next_max_pages]
+  int next_B, next_P, next_max_pages, next_num_pages;
+  int32_t next_mask;
   int bs, K, V, nchunk, chunk;
 };
 
