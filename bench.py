@@ -1,19 +1,23 @@
 """Benchmark of one self-speculative decoding round on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-  verify workloads: spec_prepare_block (verify pass) -> block_attn -> spec_accept
-  draft workload:   spec_prepare_block (draft pass)  -> block_attn -> spec_draft_argmax
-  tree workload:    block_attn_tree -> spec_accept_tree -> spec_commit_kv
+  verify workloads: block_attn -> spec_accept_prepare (the accept, then the
+                    next round's block: the block preparation of every round
+                    runs inside the previous round's accept call)
+  draft workload:   spec_prepare_block (draft pass) -> block_attn -> spec_draft_argmax
+  tree workload:    spec_prepare_tree -> block_attn_tree -> spec_accept_tree_commit
   logits workload:  spec_prepare_block (verify pass) -> block_attn -> spec_accept_logits
-  quadratic layout: block_attn_tree (draft groups + verify spine) -> spec_accept
+  quadratic layout: spec_prepare_tree -> block_attn_tree -> spec_accept (spine
+                    drafts) -> spec_quadratic_handoff -> spec_commit_kv (spine)
 Inputs are resident in HBM before the timed region. Several copies of the
 per-step inputs are cycled so that every step reads its KV pages and target
 rows from HBM rather than from the 256 MB last-level cache.
 
-Prints ONE JSON line: verified tokens/s (bs * B per step), the roofline
-position of the call that dominates the step (block_attn, or the accept /
-argmax call when it takes longer: algorithmic bytes over its event-timed
-average duration) and the float64 CPU reference timed on a bounded sample.
+Prints ONE JSON line: verified tokens/s, the roofline position of the call
+that dominates the step (algorithmic bytes over its average duration from
+HIP events on the launch stream), the whole step against its own roofline,
+and the float64 CPU reference timed on a bounded sample of requests (which
+also re-checks the GPU's outputs for those requests and counts ties).
 """
 from __future__ import annotations
 
@@ -34,23 +38,27 @@ METRIC = "verified tokens/s per round (attn+accept) and % HBM roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
+DEFAULT_CONFIG = 4   # the high-concurrency ragged verify, the largest single-GPU workload
+MASK_TOKEN = 151669  # any id works: the block's ids are outputs only
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="round configuration 1..9")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, help="round configuration 1..9")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="the warm-up runs at least this long (after the W steps)")
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0: auto)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference leg")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="HIP events bracket the calls of every n-th timed step (an event "
-                         "record drains the stream: on every step they would slow it)")
+    ap.add_argument("--event-launches", type=int, default=24,
+                    help="after the timed region, each call of the step is launched this many "
+                         "times back to back between two HIP events on its stream, three times "
+                         "over, for its average duration (the timed region carries no events: "
+                         "an event record drains the stream)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MB (a known-size "
                          "kernel for scaling HBM byte counters)")
@@ -118,6 +126,11 @@ def accept_alg_bytes(cfg, accept_len):
     return int((rows * V * 4).sum() + cfg.bs * (2 * K + 1) * 4)
 
 
+def block_prep_bytes(bs, B):
+    """Block preparation: block ids, positions and slots written (int32)."""
+    return int(3 * bs * B * 4)
+
+
 def logits_accept_alg_bytes(cfg, esz=4):
     """Logits accept: every target and draft logits row streamed once (the
     top-k needs each row whole); the candidate re-reads, kept sets and the
@@ -125,44 +138,125 @@ def logits_accept_alg_bytes(cfg, esz=4):
     return int(cfg.bs * (2 * cfg.k_spec + 1) * cfg.vocab * esz)
 
 
-def cpu_baseline(cfg, x, acc, seconds, masks=None, tacc=None, lacc=None):
-    """The float64 reference, as it stands, on the host cores: dense attention
-    per (request, KV head) plus the sequential accept (or tree accept),
-    request after request, until `seconds` have elapsed (at least one
-    request)."""
+def handoff_alg_bytes(cfg, esz=2):
+    """Quadratic hand-off: the k logits rows of the chosen group per request
+    read once, the drafts and the next block's tokens written."""
+    k, n = cfg.quad_k, (cfg.quad_k + 1) ** 2
+    return int(cfg.bs * (k * cfg.vocab * esz + (k + n) * 4))
+
+
+def commit_alg_bytes(cfg, accept_len):
+    """Committed prefix: every moved row's K and V read once and written once."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    return int(accept_len.sum()) * cfg.hkv * cfg.d * 2 * 2 * esz
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _sample_inputs(x, reqs):
+    """The attention inputs of requests `reqs` alone over a pool holding only
+    their pages (page table renumbered), so that the float64 copies stay small
+    at any batch size."""
+    from verify_attention_amd import synth
+    cfg = x.cfg
+    need = [-(-(int(x.seq_lens[b]) + cfg.block) // cfg.page) for b in reqs]
+    pages = np.unique(np.concatenate([x.page_table[b, :n] for b, n in zip(reqs, need)]))
+    remap = np.full(x.num_pages, -1, dtype=np.int64)
+    remap[pages] = np.arange(len(pages))
+    table = np.full((len(reqs), x.max_pages), -1, dtype=np.int32)
+    for r, (b, n) in enumerate(zip(reqs, need)):
+        table[r, :n] = remap[x.page_table[b, :n]]
+    return synth.AttnInputs(cfg, x.seq_lens[reqs], table, len(pages), x.q[reqs],
+                            x.k_pool[pages], x.v_pool[pages], x.n_causal[reqs])
+
+
+def cpu_baseline(cfg, x, seconds, gpu, masks=None, acc=None, tacc=None, lacc=None,
+                 quad=None):
+    """The float64 reference, as it stands, on the host cores, over a bounded
+    sample of this workload: requests taken in a seeded random order, each one
+    its dense attention over all query heads plus its accept (or tree /
+    logits accept, or the quadratic hand-off), until `seconds` have elapsed.
+    The same requests' GPU outputs from the last timed step (`gpu`) are
+    compared with the reference's: integer outputs bit for bit except draws
+    within the float64 tie band, attention to the workload's tolerance (not
+    for workloads whose step commits into the pools it reads). Returns the
+    baseline entry with that check and its tie counts."""
     import oracle
+    from oracle import quadratic
     from threadpoolctl import threadpool_info
-    q, kp, vp = x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool")
-    mode = cfg.modes[0]
+    order = np.random.default_rng(12345).permutation(cfg.bs)
+    mode = cfg.modes[-1]
+    tol = 1e-2 if cfg.dtype == "bf16" else 1e-5
+    check = dict(requests=0, mismatched_requests=0, accept_ties=0, sampling_ties=0,
+                 attn_max_abs_err=0.0, attn_checked=gpu.get("o") is not None)
     t0 = time.perf_counter()
     done = 0
-    while True:
-        b = done % cfg.bs
-        sl = slice(b, b + 1)
-        oracle.block_attn_dense(q[sl], kp, vp, x.page_table[sl], x.seq_lens[sl], mode,
-                                cfg.n_causal,
-                                tree=None if masks is None else (masks if masks.ndim == 1 else masks[sl]))
+    while done < cfg.bs:
+        b = int(order[done])
+        one = _sample_inputs(x, [b])
+        tree = None if masks is None else (masks if masks.ndim == 1 else masks[b:b + 1])
+        ro, _ = oracle.block_attn_dense(one.as_f64("q"), one.as_f64("k_pool"),
+                                        one.as_f64("v_pool"), one.page_table, one.seq_lens, mode,
+                                        cfg.n_causal, tree=tree)
+        r = None
         if acc is not None:
-            oracle.accept_request(acc.p[b], acc.q[b], acc.draft[b], acc.u[b], x.seq_lens[b])
-        if tacc is not None:
-            oracle.tree_accept_request(tacc.parent[b], tacc.token[b], tacc.p[b], tacc.u[b],
-                                       x.seq_lens[b])
-        if lacc is not None:
+            r = oracle.accept_request(acc.p[b], acc.q[b], acc.draft[b], acc.u[b], x.seq_lens[b])
+        elif tacc is not None:
+            r = oracle.tree_accept_request(tacc.parent[b], tacc.token[b], tacc.p[b], tacc.u[b],
+                                           x.seq_lens[b])
+        elif lacc is not None:
             T, k, top_p = cfg.sampling
-            oracle.accept_logits_request(lacc.target[b], lacc.draft_logits[b], lacc.draft[b],
-                                         lacc.u[b], x.seq_lens[b], float(np.float32(T)), k,
-                                         float(np.float32(top_p)))
-        done += 1
+            r = oracle.accept_logits_request(lacc.target[b], lacc.draft_logits[b], lacc.draft[b],
+                                             lacc.u[b], x.seq_lens[b], float(np.float32(T)), k,
+                                             float(np.float32(top_p)))
+        hand = None
+        if quad is not None and r is not None:
+            hand = quadratic.handoff(quad["logits_f32"](b), r["accept_len"], cfg.quad_k,
+                                     r["bonus"], MASK_TOKEN)
         el = time.perf_counter() - t0
+        done += 1
+        # the check of the GPU's outputs (not timed)
+        if gpu.get("o") is not None:
+            e = float(np.max(np.abs(gpu["o"](b) - ro[0])))
+            check["attn_max_abs_err"] = max(check["attn_max_abs_err"], e)
+            bad = e > tol
+        else:
+            bad = False
+        if r is not None:
+            check["accept_ties"] += int(r["tie_accept"])
+            check["sampling_ties"] += int(r["tie_sample"])
+            if not r["tie_sample"]:
+                got = gpu["accept"](b)
+                bad |= got["accept_len"] != r["accept_len"] or got["bonus"] != r["bonus"]
+                bad |= got["new_seq_lens"] != r["new_seq_len"]
+                bad |= not np.array_equal(got["out_tokens"], r["out_tokens"])
+                if hand is not None:
+                    bad |= not np.array_equal(gpu["handoff"](b), hand[0])
+        check["requests"] += 1
+        check["mismatched_requests"] += int(bad)
         if el >= seconds:
             break
+    el = time.perf_counter() - t0
+    check["attn_max_abs_err"] = float(f"{check['attn_max_abs_err']:.3e}")
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    return dict(value=done * cfg.block / el, unit="verified tokens/s", cores=int(threads),
-                kind="oracle",
-                sample=f"{done} requests of this workload (attention over all {cfg.hq} query "
-                       f"heads{' + accept' if acc is not None or tacc is not None or lacc is not None else ''}"
-                       f"), one after another, {el:.1f} s; host has "
-                       f"{len(os.sched_getaffinity(0))} cores")
+    tok_per_req = cfg.quad_k + 1 if cfg.quad_k else cfg.block
+    what = ("tree accept" if tacc is not None else "logits accept" if lacc is not None else
+            "accept" + (" + hand-off" if quad is not None else "") if acc is not None else None)
+    return dict(value=done * tok_per_req / el, unit="verified tokens/s", cores=int(threads),
+                kind="oracle", cpu_model=cpu_model(),
+                sample=f"{done} of the {cfg.bs} requests of this workload (seeded order): dense "
+                       f"float64 attention over all {cfg.hq} query heads"
+                       f"{' + ' + what if what else ''}, one request after another, {el:.1f} s; "
+                       f"host has {len(os.sched_getaffinity(0))} cores",
+                parity_sample=check)
 
 
 def main():
@@ -182,7 +276,7 @@ def main():
     quad = cfg.quad_k > 0           # quadratic layout: bitmask attention + the linear accept
     tree = mode == synth.TREE and not quad
     x = synth.make_attn_inputs(cfg, seed=args.seed)
-    parents = masks = tacc = acc = lacc = None
+    parents = masks = tacc = acc = lacc = qlogits = None
     if tree:
         parents, masks = synth.make_trees(cfg, args.seed)
         tacc = synth.make_tree_accept_inputs(cfg, args.seed, parents)
@@ -190,7 +284,12 @@ def main():
         lacc = synth.make_logits_accept_inputs(cfg, args.seed)
     elif quad:
         _, masks = synth.quadratic_layout(cfg.quad_k)
+        parents = synth.quadratic_parents(cfg.quad_k)
         acc = synth.make_accept_inputs(cfg, seed=args.seed)
+        # the layout's logits rows (draft and verify in one forward), bf16
+        qlogits = synth.make_argmax_logits(synth.config(args.config, argmax_vocab=cfg.vocab),
+                                           args.seed, rows=cfg.bs * cfg.block).reshape(
+            cfg.bs, cfg.block, cfg.vocab)
     elif cfg.vocab:
         acc = synth.make_accept_inputs(cfg, seed=args.seed)
     logits = synth.make_argmax_logits(cfg, seed=args.seed) if cfg.argmax_vocab else None
@@ -213,6 +312,8 @@ def main():
         step_bytes += logits_accept_alg_bytes(cfg)
     if logits is not None:
         step_bytes += logits.nbytes
+    if qlogits is not None:
+        step_bytes += handoff_alg_bytes(cfg)
     copies = args.copies or max(2, int(np.ceil(768e6 / step_bytes)))
     sets = []
     for _ in range(copies):
@@ -226,6 +327,8 @@ def main():
                      draft=up(lacc.draft))
         if logits is not None:
             s["logits"] = up(logits)
+        if qlogits is not None:
+            s["qlogits"] = up(qlogits)
         sets.append(s)
     table, seq = up(x.page_table), up(x.seq_lens)
     vid, dr = up(verified), up(drafts)
@@ -237,71 +340,93 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     if tree or quad:
         tmask = torch.from_numpy(masks.view(np.int64)).to(dev)
+        tpar = up(np.ascontiguousarray(parents, dtype=np.int32))
+    if quad:
+        node_tokens = np.full((bs, B), MASK_TOKEN, np.int32)
+        node_tokens[:, [i * (cfg.quad_k + 1) for i in range(1, cfg.quad_k + 1)]] = acc.draft
+        ntok = up(node_tokens)
+        spine = np.full((bs, B), -1, np.int32)
+        spine[:, :cfg.quad_k] = [i * (cfg.quad_k + 1) for i in range(1, cfg.quad_k + 1)]
+        spine = up(spine)
     if tree:
-        tpar, ttok = up(tacc.parent), up(tacc.token)
+        ttok = up(tacc.token)
         ws_tacc = va.workspace(va.accept_tree_workspace_bytes(bs, B, cfg.vocab))
     if lacc is not None:
         ws_acc = va.workspace(va.accept_logits_workspace_bytes(bs, cfg.k_spec, cfg.vocab,
                                                                cfg.sampling[1]))
-    if acc is not None or lacc is not None:
-        if acc is not None:
-            ws_acc = va.workspace(va.accept_workspace_bytes(bs, cfg.k_spec, cfg.vocab))
-        acc_out = dict(accept_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                       commit_len=torch.empty(bs, dtype=torch.int32, device=dev),
-                       bonus=torch.empty(bs, dtype=torch.int32, device=dev),
-                       out_tokens=torch.empty((bs, cfg.k_spec + 1), dtype=torch.int32, device=dev),
-                       new_seq_lens=torch.empty(bs, dtype=torch.int32, device=dev))
-    elif not tree and logits is not None:
-        tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
+    if acc is not None:
+        ws_acc = va.workspace(va.accept_workspace_bytes(bs, cfg.k_spec, cfg.vocab))
     # every call is checked once; the timed loop re-enqueues pre-marshalled calls
-    # a tree round has no linear block to prepare (node positions follow the
-    # tree depths): its step is the tree attention and the tree accept
-    prep_call = None if (tree or quad) else va.prepare_block_call(
-        vid, seq, table, cfg.page, B, 0, x.num_pages, None if mode == synth.BIDIR else dr,
-        out=prep_out, err=err)[0]
+    calls = []      # per step: list of (name, [enqueue per input copy])
+    acc_out = None
+    if tree or quad:
+        calls.append(("spec_prepare_tree", [va.prepare_tree_call(
+            vid, seq, table, cfg.page, tpar, MASK_TOKEN, x.num_pages, ttok if tree else ntok,
+            out=prep_out, err=err)[0]] * copies))
+        calls.append(("block_attn_tree", [va.block_attn_tree_call(
+            tmask, s["q"], s["k"], s["v"], table, seq, max_kv, out=o, ws=ws_attn,
+            err=err)[0] for s in sets]))
+    else:
+        if acc is None:   # the draft pass and the logits verify prepare their own block
+            calls.append(("spec_prepare_block", [va.prepare_block_call(
+                vid, seq, table, cfg.page, B, MASK_TOKEN, x.num_pages,
+                None if mode == synth.BIDIR else dr, out=prep_out, err=err)[0]] * copies))
+        calls.append(("block_attn", [va.block_attn_call(
+            mode, s["q"], s["k"], s["v"], table, seq, max_kv, n_causal=cfg.n_causal, out=o,
+            ws=ws_attn, err=err)[0] for s in sets]))
     if tree:
-        attn_calls = [va.block_attn_tree_call(tmask, s["q"], s["k"], s["v"], table, seq, max_kv,
-                                              out=o, ws=ws_attn, err=err)[0] for s in sets]
-        acc_out = None
-        tail_calls = []
+        lst = []
         for s in sets:
             # the tree accept, whose accepted path becomes the committed
             # prefix of the cache in the same call
-            acc_call, acc_out = va.accept_tree_commit_call(tpar, ttok, s["p"], s["u"], seq,
-                                                           s["k"], s["v"], table, out=acc_out,
-                                                           ws=ws_tacc, err=err)
-            tail_calls.append(acc_call)
+            c, acc_out = va.accept_tree_commit_call(tpar, ttok, s["p"], s["u"], seq, s["k"],
+                                                    s["v"], table, out=acc_out, ws=ws_tacc,
+                                                    err=err)
+            lst.append(c)
+        calls.append(("spec_accept_tree_commit", lst))
     elif quad:
-        attn_calls = [va.block_attn_tree_call(tmask, s["q"], s["k"], s["v"], table, seq, max_kv,
-                                              out=o, ws=ws_attn, err=err)[0] for s in sets]
-    else:
-        attn_calls = [va.block_attn_call(mode, s["q"], s["k"], s["v"], table, seq, max_kv,
-                                         n_causal=cfg.n_causal, out=o, ws=ws_attn, err=err)[0]
-                      for s in sets]
-    if acc is not None:
-        tail_calls = [va.accept_call(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out,
-                                     ws=ws_acc, err=err)[0] for s in sets]
+        lst = []
+        for s in sets:
+            c, acc_out = va.accept_call(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out,
+                                        ws=ws_acc, err=err)
+            lst.append(c)
+        calls.append(("spec_accept", lst))
+        ho_out = None
+        lst = []
+        for s in sets:
+            c, ho_out = va.quadratic_handoff_call(s["qlogits"], acc_out["accept_len"],
+                                                  cfg.quad_k, acc_out["bonus"], MASK_TOKEN,
+                                                  out=ho_out, err=err)
+            lst.append(c)
+        calls.append(("spec_quadratic_handoff", lst))
+        freed = torch.empty((bs, B), dtype=torch.int32, device=dev)
+        calls.append(("spec_commit_kv", [va.commit_kv_call(
+            s["k"], s["v"], table, seq, acc_out["accept_len"], B, spine, freed=freed,
+            err=err)[0] for s in sets]))
+    elif acc is not None:
+        lst = []
+        for s in sets:
+            c, acc_out = va.accept_prepare_call(s["p"], s["qd"], s["draft"], s["u"], seq, table,
+                                                cfg.page, B, MASK_TOKEN, x.num_pages,
+                                                out=acc_out, ws=ws_acc, err=err)
+            lst.append(c)
+        calls.append(("spec_accept_prepare", lst))
     elif lacc is not None:
-        tail_calls = [va.accept_logits_call(s["tl"], s["dl"], s["draft"], s["u"], seq,
-                                            *cfg.sampling, out=acc_out, ws=ws_acc, err=err)[0]
-                      for s in sets]
+        lst = []
+        for s in sets:
+            c, acc_out = va.accept_logits_call(s["tl"], s["dl"], s["draft"], s["u"], seq,
+                                               *cfg.sampling, out=acc_out, ws=ws_acc, err=err)
+            lst.append(c)
+        calls.append(("spec_accept_logits", lst))
     elif logits is not None:
-        tail_calls = [va.draft_argmax_call(s["logits"], out=tokens)[0] for s in sets]
-    elif not tree:
-        tail_calls = [lambda: None] * copies  # attention-only workload
+        tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
+        calls.append(("spec_draft_argmax", [va.draft_argmax_call(s["logits"], out=tokens)[0]
+                                            for s in sets]))
+    stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        if prep_call is not None:
-            prep_call()
-        if ev is not None:
-            ev[0].record(stream)
-        attn_calls[i % copies]()
-        if ev is not None:
-            ev[1].record(stream)
-        tail_calls[i % copies]()
-        if ev is not None:
-            ev[2].record(stream)
+    def step(i):
+        for _, fns in calls:
+            fns[i % copies]()
 
     if args.copy_calib_mb:
         n = args.copy_calib_mb << 20
@@ -322,73 +447,97 @@ def main():
         if warm_steps % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    # per-call durations: events around the calls of every n-th timed step
-    every = max(1, args.event_every)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] if i % every == 0 else None
-           for i in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if int(err.item()) != 0:
         raise RuntimeError(f"kernels reported data errors: {int(err.item())}")
+    # outputs of the last timed step, for the CPU leg's check
+    last = (args.steps - 1) % copies
+    gpu = {}
+    if not (tree or quad):
+        o_last = o.float().cpu().numpy().astype(np.float64)
+        gpu["o"] = lambda b: o_last[b]
+    if acc_out is not None:
+        snap = {k: v.cpu().numpy() for k, v in acc_out.items()}
+        gpu["accept"] = lambda b: {k: v[b] for k, v in snap.items()}
+    if quad:
+        hsnap = ho_out["next_draft"].cpu().numpy()
+        gpu["handoff"] = lambda b: hsnap[b]
+    al = acc_out["accept_len"].cpu().numpy() if acc_out is not None else None
+    cl = acc_out["commit_len"].cpu().numpy() if acc_out is not None else None
 
-    evs = [e for e in evs if e is not None]
-    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    tail_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    # per-call durations (after the timed region, whose steps carry no
+    # events): each call launched --event-launches times back to back between
+    # two events recorded on the launch stream, three such batches per call,
+    # input copies cycled as in the steps; the average includes the dispatch
+    # between consecutive launches, as a serving loop issues them
+    n_ev = max(20, args.event_launches)
+    per_call_us = {}
+    for name, fns in calls:
+        batches = []
+        for rep_ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for r in range(n_ev):
+                fns[r % copies]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            batches.append(e0.elapsed_time(e1) / n_ev * 1e3)
+        per_call_us[name] = float(np.mean(batches))
+
+    # algorithmic bytes per call
     alg_bytes, alg_flops = attn_alg_bytes_flops(cfg, x.seq_lens, masks)
-    attn_s = attn_ms.mean() / 1e3
-    achieved = alg_bytes / attn_s / 1e9
-    mfma_peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
-    tokens_per_step = bs * B
-    value = tokens_per_step * args.steps / wall
-    extra = {}
-    if acc is not None or tree or lacc is not None:
-        al = acc_out["accept_len"].cpu().numpy()
-        cl = acc_out["commit_len"].cpu().numpy()
+    esz = 2 if cfg.dtype == "bf16" else 4
+    call_bytes = {"block_attn": alg_bytes, "block_attn_tree": alg_bytes,
+                  "spec_prepare_block": block_prep_bytes(bs, B),
+                  "spec_prepare_tree": block_prep_bytes(bs, B)}
+    if al is not None:
         if tree:
-            # plus the committed rows' K and V, read once and written once
-            esz = 2 if cfg.dtype == "bf16" else 4
-            ab = tree_accept_alg_bytes(cfg) + int(al.sum()) * cfg.hkv * cfg.d * 2 * 2 * esz
+            call_bytes["spec_accept_tree_commit"] = tree_accept_alg_bytes(cfg) + \
+                int(al.sum()) * cfg.hkv * cfg.d * 2 * 2 * esz
         elif lacc is not None:
-            ab = logits_accept_alg_bytes(cfg)
+            call_bytes["spec_accept_logits"] = logits_accept_alg_bytes(cfg)
+        elif quad:
+            call_bytes["spec_accept"] = accept_alg_bytes(cfg, al)
+            call_bytes["spec_quadratic_handoff"] = handoff_alg_bytes(cfg)
+            call_bytes["spec_commit_kv"] = commit_alg_bytes(cfg, al)
         else:
-            ab = accept_alg_bytes(cfg, al)
-        extra["accept"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2),
-                               alg_bytes=ab, achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1),
-                               mean_commit_len=float(cl.mean()))
-        extra["committed_tokens_per_s"] = float(cl.sum() * args.steps / wall)
-    elif logits is not None:
-        ab = logits.nbytes
-        extra["draft_argmax"] = dict(avg_us=round(tail_ms.mean() * 1e3, 2), alg_bytes=int(ab),
-                                     achieved_gbs=round(ab / (tail_ms.mean() / 1e3) / 1e9, 1))
-    attn_rl = {"kernel": "block_attn", "bound": "hbm",
-               "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-               "frac": round(achieved / HBM_PEAK_GBS, 4),
-               "traffic": measured_traffic(cfg.name, kernel_sources_hash()),
-               "traffic_unit": "bytes per launch",
-               "alg_bytes_per_launch": alg_bytes, "avg_us": round(attn_ms.mean() * 1e3, 2),
-               "mfma_frac": round(alg_flops / attn_s / 1e12 / mfma_peak, 4)}
-    if alg_flops / alg_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
-        # flops per byte above the ridge: the matrix cores bound the kernel
-        tflops = alg_flops / attn_s / 1e12
-        attn_rl.update(bound="mfma", achieved=round(tflops, 1), peak=mfma_peak, unit="TFLOP/s",
-                       frac=round(tflops / mfma_peak, 4), alg_flops_per_launch=alg_flops,
-                       hbm_frac=round(achieved / HBM_PEAK_GBS, 4))
-    tail_rl = None
-    if acc is not None or tree or lacc is not None or logits is not None:
-        tail_name = ("spec_accept_tree_commit" if tree else "spec_accept_logits"
-                     if lacc is not None else "spec_accept" if acc is not None else
-                     "spec_draft_argmax")
-        tail_s = tail_ms.mean() / 1e3
-        tail_rl = {"kernel": tail_name, "bound": "hbm", "achieved": round(ab / tail_s / 1e9, 1),
-                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                   "frac": round(ab / tail_s / 1e9 / HBM_PEAK_GBS, 4),
-                   "traffic": measured_traffic(cfg.name, kernel_sources_hash(), tail_name),
-                   "traffic_unit": "bytes per launch", "alg_bytes_per_launch": int(ab),
-                   "avg_us": round(tail_ms.mean() * 1e3, 2)}
+            call_bytes["spec_accept_prepare"] = accept_alg_bytes(cfg, al) + block_prep_bytes(bs, B)
+    if logits is not None:
+        call_bytes["spec_draft_argmax"] = int(logits.nbytes)
+    src_hash = kernel_sources_hash()
+    mfma_peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS
+
+    def roofline(name):
+        us = per_call_us[name]
+        ab = call_bytes[name]
+        gbs = ab / (us * 1e-6) / 1e9
+        rl = {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+              "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+              "traffic": measured_traffic(cfg.name, src_hash,
+                                          "block_attn" if name.startswith("block_attn") else name),
+              "traffic_unit": "bytes per launch", "alg_bytes_per_launch": int(ab),
+              "avg_us": round(us, 2), "timed_launches": 3 * n_ev}
+        if name.startswith("block_attn"):
+            tflops = alg_flops / (us * 1e-6) / 1e12
+            rl["mfma_frac"] = round(tflops / mfma_peak, 4)
+            if alg_flops / alg_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+                # flops per byte above the ridge: the matrix cores bound the kernel
+                rl.update(bound="mfma", achieved=round(tflops, 1), peak=mfma_peak,
+                          unit="TFLOP/s", frac=round(tflops / mfma_peak, 4),
+                          alg_flops_per_launch=alg_flops, hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        return rl
+
+    dominant = max(per_call_us, key=per_call_us.get)
+    tokens_per_step = bs * (cfg.quad_k + 1 if quad else B)
+    value = tokens_per_step * args.steps / wall
+    step_bytes_alg = sum(call_bytes[n] for n, _ in calls)
+    step_roof_us = max(step_bytes_alg / (HBM_PEAK_GBS * 1e9),
+                       alg_flops / (mfma_peak * 1e12)) * 1e6
+    ms = wall / args.steps * 1e3
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -397,15 +546,15 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_steps_run": warm_steps,
-        "event_steps": len(evs),
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": ("synthetic (seeded N(0,1) Q/K/V, normal target logits, draft logits = target "
                  "+ normal noise)" if lacc is not None else
-                 "synthetic (seeded N(0,1) Q/K/V, softmax-of-normal target/draft rows)"
+                 "synthetic (seeded N(0,1) Q/K/V, softmax-of-normal target/draft rows"
+                 + (", N(0, 3^2) bf16 layout logits)" if quad else ")")
                  if acc is not None or tree else
                  "synthetic (seeded N(0,1) Q/K/V, N(0, 3^2) bf16 draft logits)"
                  if logits is not None else "synthetic (seeded N(0,1) Q/K/V)"),
@@ -413,16 +562,27 @@ def main():
                    "head_dim": cfg.d, "page": cfg.page, "mode": synth.MODE_NAMES[mode],
                    "ctx": [cfg.ctx_lo, cfg.ctx_hi], "vocab": cfg.vocab or cfg.argmax_vocab,
                    "k_spec": cfg.k_spec, "input_copies": copies,
-                   **({"layout": f"quadratic, k = {cfg.quad_k}"} if quad else {})},
-        "roofline": attn_rl,
-        "kernel_src": kernel_sources_hash(),
-        **extra,
+                   "step": [n for n, _ in calls],
+                   **({"layout": f"quadratic, k = {cfg.quad_k}",
+                       "verified_tokens_per_request": cfg.quad_k + 1} if quad else {})},
+        "roofline": roofline(dominant),
+        "step_roofline": {"alg_bytes": int(step_bytes_alg), "roofline_us": round(step_roof_us, 2),
+                          "measured_us": round(ms * 1e3, 2),
+                          "frac": round(step_roof_us / (ms * 1e3), 4)},
+        "calls": {n: roofline(n) for n, _ in calls if n != dominant},
+        "kernel_src": src_hash,
     }
-    if tail_rl is not None and tail_rl["avg_us"] > attn_rl["avg_us"]:
-        # the call that dominates the step carries the roofline
-        line["roofline"], line["attn_roofline"] = tail_rl, attn_rl
+    if cl is not None:
+        line["committed_tokens_per_s"] = round(float(cl.sum() * args.steps / wall), 1)
+        line["mean_commit_len"] = float(cl.mean())
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, x, acc, args.cpu_seconds, masks, tacc, lacc)
+        quad_in = None
+        if quad:
+            qf = lambda b: synth.bf16_to_f32(qlogits[b])
+            quad_in = {"logits_f32": qf}
+        line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds, gpu, masks,
+                                            acc if acc is not None else None, tacc, lacc,
+                                            quad_in)
     print(json.dumps(line), flush=True)
 
 

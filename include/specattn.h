@@ -272,14 +272,19 @@ int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* t
  *   with next_block)
  * Outputs: next_draft [bs, k], next_block [bs, (k + 1)^2] or NULL. An
  *   accept_len outside 0..k gives drafts of -1 and sets SPEC_ERR_TREE.
+ * Workspace: spec_quadratic_handoff_workspace_bytes(bs, k, V) bytes of device
+ *   memory, contents irrelevant (per-segment maxima passed between the call's
+ *   two kernels); calls sharing it must be ordered.
  * The accepted spine becomes contiguous with spec_commit_kv(B = (k + 1)^2,
  *   path_nodes[b, i] = (i + 1) * (k + 1)).
- * Errors: SPEC_EINVAL (sizes, NULL), SPEC_ENOTSUP (dtype).
+ * Errors: SPEC_EINVAL (sizes, NULL), SPEC_ENOTSUP (dtype), SPEC_ENOSPC.
  */
+size_t spec_quadratic_handoff_workspace_bytes(int bs, int k, int V);
+
 int spec_quadratic_handoff(int bs, int k, int V, int dtype, const void* logits,
                            const int32_t* accept_len, const int32_t* bonus,
                            int32_t mask_token_id, int32_t* next_draft, int32_t* next_block,
-                           int32_t* err_flags, void* stream);
+                           void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream);
 
 /*
  * spec_accept -- speculative accept / bonus epilogue.

@@ -42,6 +42,9 @@ hipError_t launch_prepare_tree(const PrepareTreeArgs& a, hipStream_t) {
 hipError_t launch_quadratic_handoff(const HandoffArgs& h, bool, hipStream_t) {
   require(h.k >= 1 && h.k <= 7 && h.n == (h.k + 1) * (h.k + 1), "handoff layout");
   require(!h.next_block || h.bonus, "handoff block needs the bonus");
+  require(h.part_v && h.part_i && h.S >= 1 && h.S <= 16 && h.seg_len % 8 == 0 &&
+              (long long)h.S * h.seg_len >= h.V && (long long)(h.S - 1) * h.seg_len < h.V,
+          "handoff segments cover the row");
   return hipErrorInvalidValue;
 }
 hipError_t launch_argmax_rows(const void*, bool, int rows, int V, int32_t*, hipStream_t) {

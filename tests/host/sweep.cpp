@@ -76,16 +76,24 @@ int main() {
          SPEC_EINVAL);
   EXPECT(spec_prepare_tree(32, 8, 16, 80, 300, 7, I, I, I, nullptr, 0, I, I, I, I, I, nullptr),
          SPEC_EINVAL);
-  for (int k = 1; k <= 7; ++k) {
-    EXPECT(spec_quadratic_handoff(32, k, 151936, SPEC_BF16, F, I, I, 9, I, I, I, nullptr),
-           SPEC_EHIP);
-    EXPECT(spec_quadratic_handoff(32, k, 151936, SPEC_F32, F, I, nullptr, 9, I, nullptr, I,
-                                  nullptr),
-           SPEC_EHIP);
-  }
-  EXPECT(spec_quadratic_handoff(32, 8, 151936, SPEC_BF16, F, I, I, 9, I, I, I, nullptr),
+  for (int bs : {1, 5, 32, 1000})
+    for (int k = 1; k <= 7; ++k)
+      for (int V : {1, 7, 1000, 151936}) {
+        const size_t wh = spec_quadratic_handoff_workspace_bytes(bs, k, V);
+        EXPECT(spec_quadratic_handoff(bs, k, V, SPEC_BF16, F, I, I, 9, I, I, F, wh, I, nullptr),
+               SPEC_EHIP);
+        EXPECT(spec_quadratic_handoff(bs, k, V, SPEC_F32, F, I, nullptr, 9, I, nullptr, F, wh, I,
+                                      nullptr),
+               SPEC_EHIP);
+        EXPECT(spec_quadratic_handoff(bs, k, V, SPEC_F32, F, I, nullptr, 9, I, nullptr, F, wh - 1,
+                                      I, nullptr),
+               SPEC_ENOSPC);
+      }
+  EXPECT(spec_quadratic_handoff(32, 8, 151936, SPEC_BF16, F, I, I, 9, I, I, F, 1 << 30, I,
+                                nullptr),
          SPEC_EINVAL);
-  EXPECT(spec_quadratic_handoff(32, 4, 151936, SPEC_BF16, F, I, nullptr, 9, I, I, I, nullptr),
+  EXPECT(spec_quadratic_handoff(32, 4, 151936, SPEC_BF16, F, I, nullptr, 9, I, I, F, 1 << 30, I,
+                                nullptr),
          SPEC_EINVAL);  // a next block needs the bonus
   EXPECT(spec_draft_argmax(1984, 157184, SPEC_BF16, F, I, nullptr), SPEC_EHIP);
   EXPECT(spec_draft_argmax(0, 157184, SPEC_BF16, F, I, nullptr), SPEC_EINVAL);

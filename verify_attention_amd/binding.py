@@ -34,8 +34,9 @@ _SIGS = {
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "spec_prepare_tree": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_int32,
                                    _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "spec_quadratic_handoff_workspace_bytes": (_c_size, [_c_int] * 3),
     "spec_quadratic_handoff": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
-                                        ctypes.c_int32, _vp, _vp, _vp, _vp]),
+                                        ctypes.c_int32, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "spec_accept_prepare": (_c_int, [_c_int] * 4 + [_vp] * 10 + [_c_int] * 4 +
                             [ctypes.c_int32] + [_vp] * 5 + [_c_size, _vp, _vp]),
     "block_attn_workspace_bytes": (_c_size, [_c_int] * 6),
@@ -452,8 +453,12 @@ def draft_argmax_call(logits, out=None, stream=None):
     return enqueue, out
 
 
+def quadratic_handoff_workspace_bytes(bs, k, V) -> int:
+    return int(load().spec_quadratic_handoff_workspace_bytes(bs, k, V))
+
+
 def quadratic_handoff_call(logits, accept_len, k, bonus=None, mask_token_id=0, out=None,
-                           err=None, stream=None):
+                           ws=None, err=None, stream=None):
     """Checks the arguments of spec_quadratic_handoff once and returns
     (enqueue, out). logits [bs, (k + 1)^2, V] float32 or bfloat16; out:
     next_draft [bs, k] and, when bonus is given, next_block [bs, (k + 1)^2]."""
@@ -471,11 +476,16 @@ def quadratic_handoff_call(logits, accept_len, k, bonus=None, mask_token_id=0, o
     if bonus is not None:
         specs["next_block"] = ((bs, n),)
     out = _need_out(out, specs, logits.device)
-    _same_device(logits, accept_len, bonus, err, *out.values())
+    need = quadratic_handoff_workspace_bytes(bs, k, V)
+    if ws is None:
+        ws = workspace(need, logits.device)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(logits, accept_len, bonus, ws, err, *out.values())
     args = (bs, k, V, dt, _ptr(logits), _ptr(accept_len), _ptr(bonus), mask_token_id,
-            _ptr(out["next_draft"]), _ptr(out.get("next_block")), _ptr(err), _stream(stream))
+            _ptr(out["next_draft"]), _ptr(out.get("next_block")), _ptr(ws), ws_bytes, _ptr(err),
+            _stream(stream))
     fn = load().spec_quadratic_handoff
-    keep = (logits, accept_len, bonus, out, err)
+    keep = (logits, accept_len, bonus, out, ws, err)
 
     def enqueue():
         _ = keep
@@ -486,12 +496,12 @@ def quadratic_handoff_call(logits, accept_len, k, bonus=None, mask_token_id=0, o
     return enqueue, out
 
 
-def quadratic_handoff(logits, accept_len, k, bonus=None, mask_token_id=0, out=None, err=None,
-                      stream=None):
+def quadratic_handoff(logits, accept_len, k, bonus=None, mask_token_id=0, out=None, ws=None,
+                      err=None, stream=None):
     """Next round's drafts (and block tokens) from a quadratic block
     (spec_quadratic_handoff)."""
-    enqueue, out = quadratic_handoff_call(logits, accept_len, k, bonus, mask_token_id, out, err,
-                                          stream)
+    enqueue, out = quadratic_handoff_call(logits, accept_len, k, bonus, mask_token_id, out, ws,
+                                          err, stream)
     enqueue()
     return out
 

@@ -28,6 +28,8 @@ constexpr int kAccThreads = 256;
 constexpr int kJTokenErr = 1 << 16;  // jbuf flag: the first reject was an invalid token id
 
 constexpr int kSub = 256;  // vocabulary entries per sub-block (one wave, 4 per lane)
+constexpr int kSubInFlight = 4;  // sub-blocks whose loads a wave keeps in flight
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------ reductions
 __device__ __forceinline__ double wave_sum(double x) { return wave_sum_f64(x); }
@@ -152,12 +154,46 @@ __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs 
   const int sb0 = c * (a.chunk / kSub);
   const int sb1 = min(nsb, sb0 + a.chunk / kSub);
   double* out = a.partial + (size_t)b * nsb;
-#pragma unroll 2
-  for (int sb = sb0 + wave; sb < sb1; sb += kAccThreads / 64) {
-    double r[4];
-    resid4(prow, qrow, sb * kSub + 4 * lane, V, vec, r);
-    const double t = wave_sum((r[0] + r[1]) + (r[2] + r[3]));
-    if (lane == 0) out[sb] = t;
+  // each wave streams its sub-blocks (every 4th of the chunk) in batches of
+  // kSubInFlight: all of a batch's 16-byte loads of p and q are issued (non-
+  // temporal: the rows are read once) before the first is used
+  constexpr int kWaves = kAccThreads / 64;
+  for (int base = sb0 + wave; base < sb1; base += kSubInFlight * kWaves) {
+    f32x4 pv[kSubInFlight], qv[kSubInFlight];
+#pragma unroll
+    for (int t = 0; t < kSubInFlight; ++t) {
+      const int sb = base + t * kWaves;
+      const int e = sb * kSub + 4 * lane;
+      pv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      qv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (sb < sb1 && vec && e + 4 <= V) {
+        pv[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(prow + e));
+        if (qrow) qv[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(qrow + e));
+      } else if (sb < sb1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[t][i] = e + i < V ? prow[e + i] : 0.f;
+          if (qrow) qv[t][i] = e + i < V ? qrow[e + i] : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kSubInFlight; ++t) {
+      const int sb = base + t * kWaves;
+      if (sb >= sb1) break;
+      double r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!qrow) {
+          r[i] = (double)pv[t][i];
+        } else {
+          const double d = (double)pv[t][i] - (double)qv[t][i];
+          r[i] = d > 0.0 ? d : 0.0;
+        }
+      }
+      const double sum = wave_sum((r[0] + r[1]) + (r[2] + r[3]));
+      if (lane == 0) out[sb] = sum;
+    }
   }
 }
 
@@ -629,9 +665,11 @@ __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 // maximum and the vector that first reached it; the winning vector is read
 // again to locate the lowest index holding the value. Then (value, index)
 // reductions over the wave and the workgroup.
-// The whole workgroup scans `row`; the result is valid in thread 0.
+// The whole workgroup scans `row`: the largest non-NaN value and the lowest
+// index holding it (index 0x7fffffff when the row holds only NaN), valid in
+// thread 0.
 template <typename T>
-__device__ __forceinline__ int argmax_row(const T* row, int V) {
+__device__ __forceinline__ void argmax_row_pair(const T* row, int V, float& out_v, int& out_i) {
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
   constexpr int kVec = 16 / sizeof(T);
@@ -687,6 +725,17 @@ __device__ __forceinline__ int argmax_row(const T* row, int V) {
   __syncthreads();
   if (threadIdx.x == 0)
     for (int w = 1; w < 4; ++w) better(bv, bi, s_v[w], s_i[w]);
+  out_v = bv;
+  out_i = bi;
+}
+
+// Lowest index among the maxima of `row` (0 for a row without a non-NaN
+// entry), valid in thread 0.
+template <typename T>
+__device__ __forceinline__ int argmax_row(const T* row, int V) {
+  float bv;
+  int bi;
+  argmax_row_pair(row, V, bv, bi);
   return bi == 0x7fffffff ? 0 : bi;
 }
 
@@ -696,50 +745,74 @@ __global__ __launch_bounds__(kAccThreads) void argmax_rows_kernel(const T* x, in
   if (threadIdx.x == 0) out[blockIdx.x] = bi;
 }
 
-// The quadratic layout's hand-off, one workgroup per (request b, member m):
-// with a = accept_len[b] drafts accepted, member m of the group after spine
-// token a (block row a * (k + 1) + 1 + m) proposes the next round's draft m,
-// its greedy token. The workgroup also writes its share of the next round's
-// block tokens: spine position (m + 1) * (k + 1) = the draft and the group
-// after it = the mask token; member 0's workgroup writes position 0 (the
-// bonus) and group G_0. An accept length outside 0 .. k gives -1 drafts and
-// SPEC_ERR_TREE.
+// The quadratic layout's hand-off. With a = accept_len[b] drafts accepted,
+// member m of the group after spine token a (block row a * (k + 1) + 1 + m)
+// proposes the next round's draft m, its greedy token. The k rows of a request
+// are cut into S segments so that the scan keeps the whole GPU busy
+// (bs * k rows alone would leave CUs idle at serving batch sizes): kernel 1,
+// one workgroup per (request, member, segment), stores the segment's largest
+// value and lowest index holding it; kernel 2, one wave per request, merges
+// the S segments of each member in index order (largest value, then lowest
+// index: the whole-row rule) and writes the drafts and the next block's
+// tokens. An accept length outside 0 .. k gives -1 drafts and SPEC_ERR_TREE.
 template <typename T>
-__global__ __launch_bounds__(kAccThreads) void quadratic_handoff_kernel(HandoffArgs h) {
-  const int b = blockIdx.x / h.k;
-  const int m = blockIdx.x - b * h.k;
-  const int k = h.k, tid = threadIdx.x;
+__global__ __launch_bounds__(kAccThreads) void handoff_partial_kernel(HandoffArgs h) {
+  const int seg = blockIdx.x % h.S;
+  const int r = blockIdx.x / h.S;  // b * k + m
+  const int b = r / h.k, m = r - b * h.k;
+  const int k = h.k;
   const int acc = h.accept_len[b];
   const bool ok = acc >= 0 && acc <= k;  // uniform over the workgroup
-  int tok = -1;
-  if (ok) {
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  const int e0 = seg * h.seg_len;
+  const int n = min(h.V - e0, h.seg_len);
+  if (ok && n > 0) {
     const T* row = reinterpret_cast<const T*>(h.logits) +
-                   ((size_t)b * h.n + (size_t)acc * (k + 1) + 1 + m) * h.V;
-    tok = argmax_row(row, h.V);
+                   ((size_t)b * h.n + (size_t)acc * (k + 1) + 1 + m) * h.V + e0;
+    argmax_row_pair(row, n, bv, bi);
   }
-  if (tid == 0) {
-    h.next_draft[(size_t)b * k + m] = tok;
-    if (!ok && m == 0) flag_error(h.err, kErrTree);
+  if (threadIdx.x == 0) {
+    h.part_v[blockIdx.x] = bv;
+    h.part_i[blockIdx.x] = bi == 0x7fffffff ? bi : bi + e0;
   }
-  if (h.next_block) {
-    int32_t* nb = h.next_block + (size_t)b * h.n;
-    const int spine = (m + 1) * (k + 1);
-    if (tid == 0) nb[spine] = tok;
-    else if (tid <= k) nb[spine + tid] = h.mask_token_id;
-    if (m == 0) {
-      if (tid == 0) nb[0] = h.bonus[b];
-      else if (tid <= k) nb[tid] = h.mask_token_id;
-    }
+}
+
+__global__ __launch_bounds__(64) void handoff_select_kernel(HandoffArgs h) {
+  const int b = blockIdx.x, lane = threadIdx.x, k = h.k;
+  const int acc = h.accept_len[b];
+  const bool ok = acc >= 0 && acc <= k;
+  int tok = -1;
+  if (lane < k && ok) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    const size_t base = ((size_t)b * k + lane) * h.S;
+    for (int s = 0; s < h.S; ++s) better(bv, bi, h.part_v[base + s], h.part_i[base + s]);
+    tok = bi == 0x7fffffff ? 0 : bi;
+  }
+  if (lane < k) h.next_draft[(size_t)b * k + lane] = tok;
+  if (lane == 0 && !ok) flag_error(h.err, kErrTree);
+  // row 0: the bonus (the next root); spine rows (m + 1) * (k + 1): the
+  // drafts; every group row: the mask token (lane = row, n <= 64)
+  const int j = lane / (k + 1), rem = lane - j * (k + 1);
+  const int draft = __shfl(tok, j > 0 && j <= k ? j - 1 : 0, 64);  // every lane takes part
+  if (h.next_block && lane < h.n) {
+    int32_t v = h.mask_token_id;
+    if (lane == 0) v = h.bonus[b];
+    else if (rem == 0) v = draft;
+    h.next_block[(size_t)b * h.n + lane] = v;
   }
 }
 
 hipError_t launch_quadratic_handoff(const HandoffArgs& h, bool bf16, hipStream_t stream) {
+  const dim3 grid(h.bs * h.k * h.S);
   if (bf16)
-    hipLaunchKernelGGL(quadratic_handoff_kernel<__bf16>, dim3(h.bs * h.k), dim3(kAccThreads), 0,
-                       stream, h);
+    hipLaunchKernelGGL(handoff_partial_kernel<__bf16>, grid, dim3(kAccThreads), 0, stream, h);
   else
-    hipLaunchKernelGGL(quadratic_handoff_kernel<float>, dim3(h.bs * h.k), dim3(kAccThreads), 0,
-                       stream, h);
+    hipLaunchKernelGGL(handoff_partial_kernel<float>, grid, dim3(kAccThreads), 0, stream, h);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(handoff_select_kernel, dim3(h.bs), dim3(64), 0, stream, h);
   return hipGetLastError();
 }
 

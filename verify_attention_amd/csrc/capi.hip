@@ -314,15 +314,48 @@ SPEC_API int spec_draft_argmax(int rows, int V, int dtype, const void* logits, i
                                        static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// The hand-off's segments: enough workgroups (about 1024) to keep every CU
+// streaming, each segment a multiple of 8 entries (16-byte vectors stay
+// aligned), at most 16 segments per row.
+struct HandoffPlan {
+  int S = 1, seg_len = 0;
+  size_t off_i = 0, ws_bytes = 0;
+};
+
+HandoffPlan plan_handoff(int bs, int k, int V) {
+  HandoffPlan p;
+  const long long rows = (long long)bs * k;
+  p.S = (int)std::max(1LL, std::min(16LL, (1024 + rows - 1) / rows));
+  p.seg_len = (int)align_up((size_t)((V + p.S - 1) / p.S), 8);
+  p.S = (V + p.seg_len - 1) / p.seg_len;
+  const size_t parts = (size_t)rows * p.S;
+  p.off_i = align_up(parts * sizeof(float), 256);
+  p.ws_bytes = p.off_i + parts * sizeof(int32_t);
+  return p;
+}
+
+}  // namespace
+
+SPEC_API size_t spec_quadratic_handoff_workspace_bytes(int bs, int k, int V) {
+  if (bs <= 0 || k < 1 || k > 7 || V <= 0) return 0;
+  return plan_handoff(bs, k, V).ws_bytes;
+}
+
 SPEC_API int spec_quadratic_handoff(int bs, int k, int V, int dtype, const void* logits,
                                     const int32_t* accept_len, const int32_t* bonus,
                                     int32_t mask_token_id, int32_t* next_draft,
-                                    int32_t* next_block, int32_t* err_flags, void* stream) {
+                                    int32_t* next_block, void* workspace, size_t ws_bytes,
+                                    int32_t* err_flags, void* stream) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
   if (bs <= 0 || k < 1 || k > 7 || V <= 0) return SPEC_EINVAL;
   const int n = (k + 1) * (k + 1);
-  if ((long long)bs * n > INT_MAX) return SPEC_EINVAL;
+  if ((long long)bs * n > INT_MAX / 16) return SPEC_EINVAL;
   if (!logits || !accept_len || !next_draft || (next_block && !bonus)) return SPEC_EINVAL;
+  const HandoffPlan plan = plan_handoff(bs, k, V);
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  char* ws = static_cast<char*>(workspace);
   HandoffArgs h{};
   h.logits = logits;
   h.accept_len = accept_len;
@@ -330,10 +363,14 @@ SPEC_API int spec_quadratic_handoff(int bs, int k, int V, int dtype, const void*
   h.next_draft = next_draft;
   h.next_block = next_block;
   h.err = err_flags;
+  h.part_v = reinterpret_cast<float*>(ws);
+  h.part_i = reinterpret_cast<int32_t*>(ws + plan.off_i);
   h.bs = bs;
   h.k = k;
   h.n = n;
   h.V = V;
+  h.S = plan.S;
+  h.seg_len = plan.seg_len;
   h.mask_token_id = mask_token_id;
   return hip_status(launch_quadratic_handoff(h, dtype == SPEC_BF16,
                                              static_cast<hipStream_t>(stream)));

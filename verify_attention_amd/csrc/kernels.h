@@ -78,7 +78,10 @@ struct HandoffArgs {
   int32_t* next_draft;         // [bs][k]
   int32_t* next_block;         // [bs][n] or null
   int32_t* err;
+  float* part_v;               // [bs][k][S] segment maxima (workspace)
+  int32_t* part_i;             // [bs][k][S] their lowest indices
   int bs, k, n, V;
+  int S, seg_len;              // segments per row and their length (a multiple of 8)
   int32_t mask_token_id;
 };
 
