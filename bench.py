@@ -54,11 +54,11 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference leg")
-    ap.add_argument("--event-launches", type=int, default=24,
-                    help="after the timed region, each call of the step is launched this many "
-                         "times back to back between two HIP events on its stream, three times "
-                         "over, for its average duration (the timed region carries no events: "
-                         "an event record drains the stream)")
+    ap.add_argument("--event-steps", type=int, default=24,
+                    help="steps at the end of the warm-up (right before the timed region) with "
+                         "HIP events recorded on the launch stream around every call, for the "
+                         "per-call average durations (at least 20; the timed steps carry no "
+                         "events: an event record drains the stream)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="before warmup, run one plain device copy of this many MB (a known-size "
                          "kernel for scaling HBM byte counters)")
@@ -424,9 +424,13 @@ def main():
                                             for s in sets]))
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        for _, fns in calls:
+    def step(i, ev=None):
+        for c, (_, fns) in enumerate(calls):
+            if ev is not None:
+                ev[c].record(stream)
             fns[i % copies]()
+        if ev is not None:
+            ev[-1].record(stream)
 
     if args.copy_calib_mb:
         n = args.copy_calib_mb << 20
@@ -447,6 +451,20 @@ def main():
         if warm_steps % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # per-call durations: the last --event-steps warm-up steps carry HIP events
+    # around every call (recorded on the launch stream), right before the
+    # timed region and in the same steady state; an event's time includes the
+    # dispatch that follows it
+    n_ev = max(20, args.event_steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(n_ev)]
+    for i in range(n_ev):
+        step(warm_steps + i, evs[i])
+    torch.cuda.synchronize()
+    per_call_us = {}
+    for c, (name, _) in enumerate(calls):
+        per_call_us[name] = float(np.mean([e[c].elapsed_time(e[c + 1]) for e in evs]) * 1e3)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -455,7 +473,6 @@ def main():
     if int(err.item()) != 0:
         raise RuntimeError(f"kernels reported data errors: {int(err.item())}")
     # outputs of the last timed step, for the CPU leg's check
-    last = (args.steps - 1) % copies
     gpu = {}
     if not (tree or quad):
         o_last = o.float().cpu().numpy().astype(np.float64)
@@ -468,25 +485,6 @@ def main():
         gpu["handoff"] = lambda b: hsnap[b]
     al = acc_out["accept_len"].cpu().numpy() if acc_out is not None else None
     cl = acc_out["commit_len"].cpu().numpy() if acc_out is not None else None
-
-    # per-call durations (after the timed region, whose steps carry no
-    # events): each call launched --event-launches times back to back between
-    # two events recorded on the launch stream, three such batches per call,
-    # input copies cycled as in the steps; the average includes the dispatch
-    # between consecutive launches, as a serving loop issues them
-    n_ev = max(20, args.event_launches)
-    per_call_us = {}
-    for name, fns in calls:
-        batches = []
-        for rep_ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for r in range(n_ev):
-                fns[r % copies]()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            batches.append(e0.elapsed_time(e1) / n_ev * 1e3)
-        per_call_us[name] = float(np.mean(batches))
 
     # algorithmic bytes per call
     alg_bytes, alg_flops = attn_alg_bytes_flops(cfg, x.seq_lens, masks)
@@ -520,7 +518,7 @@ def main():
               "traffic": measured_traffic(cfg.name, src_hash,
                                           "block_attn" if name.startswith("block_attn") else name),
               "traffic_unit": "bytes per launch", "alg_bytes_per_launch": int(ab),
-              "avg_us": round(us, 2), "timed_launches": 3 * n_ev}
+              "avg_us": round(us, 2), "event_samples": n_ev}
         if name.startswith("block_attn"):
             tflops = alg_flops / (us * 1e-6) / 1e12
             rl["mfma_frac"] = round(tflops / mfma_peak, 4)
@@ -545,7 +543,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_steps_run": warm_steps,
+        "warmup_steps_run": warm_steps + n_ev,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

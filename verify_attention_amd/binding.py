@@ -86,12 +86,16 @@ def header_functions() -> list:
 
 
 def load():
-    """Load the built library (raises when it is missing)."""
+    """Load the built library (raises when it is missing). torch is imported
+    first: the library's HIP runtime dependency must resolve to the runtime
+    torch already loaded (one HIP runtime per process), not load a second
+    one."""
     global _LIB
     if _LIB is None:
         path = lib_path()
         if not os.path.exists(path):
             raise SpecError(f"{path} is not built; run __graft_entry__.build() first")
+        _torch()
         lib = ctypes.CDLL(path)
         for name, (res, args) in _SIGS.items():
             fn = getattr(lib, name)
