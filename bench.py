@@ -7,8 +7,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   draft workload:   spec_prepare_block (draft pass) -> block_attn -> spec_draft_argmax
   tree workload:    spec_prepare_tree -> block_attn_tree -> spec_accept_tree_commit
   logits workload:  spec_prepare_block (verify pass) -> block_attn -> spec_accept_logits
-  quadratic layout: spec_prepare_tree -> block_attn_tree -> spec_accept (spine
-                    drafts) -> spec_quadratic_handoff -> spec_commit_kv (spine)
+  quadratic layout: spec_prepare_tree -> block_attn_tree -> spec_accept_quadratic
+                    (the spine drafts' accept, the hand-off of the next drafts
+                    and the spine's commit in one call)
 Inputs are resident in HBM before the timed region. Several copies of the
 per-step inputs are cycled so that every step reads its KV pages and target
 rows from HBM rather than from the 256 MB last-level cache.
@@ -345,9 +346,6 @@ def main():
         node_tokens = np.full((bs, B), MASK_TOKEN, np.int32)
         node_tokens[:, [i * (cfg.quad_k + 1) for i in range(1, cfg.quad_k + 1)]] = acc.draft
         ntok = up(node_tokens)
-        spine = np.full((bs, B), -1, np.int32)
-        spine[:, :cfg.quad_k] = [i * (cfg.quad_k + 1) for i in range(1, cfg.quad_k + 1)]
-        spine = up(spine)
     if tree:
         ttok = up(tacc.token)
         ws_tacc = va.workspace(va.accept_tree_workspace_bytes(bs, B, cfg.vocab))
@@ -386,23 +384,13 @@ def main():
         calls.append(("spec_accept_tree_commit", lst))
     elif quad:
         lst = []
+        ws_q = va.workspace(va.accept_quadratic_workspace_bytes(bs, cfg.quad_k, cfg.vocab))
         for s in sets:
-            c, acc_out = va.accept_call(s["p"], s["qd"], s["draft"], s["u"], seq, out=acc_out,
-                                        ws=ws_acc, err=err)
+            c, acc_out = va.accept_quadratic_call(s["p"], s["qd"], s["draft"], s["u"], seq,
+                                                  s["qlogits"], s["k"], s["v"], table,
+                                                  MASK_TOKEN, out=acc_out, ws=ws_q, err=err)
             lst.append(c)
-        calls.append(("spec_accept", lst))
-        ho_out = None
-        lst = []
-        for s in sets:
-            c, ho_out = va.quadratic_handoff_call(s["qlogits"], acc_out["accept_len"],
-                                                  cfg.quad_k, acc_out["bonus"], MASK_TOKEN,
-                                                  out=ho_out, err=err)
-            lst.append(c)
-        calls.append(("spec_quadratic_handoff", lst))
-        freed = torch.empty((bs, B), dtype=torch.int32, device=dev)
-        calls.append(("spec_commit_kv", [va.commit_kv_call(
-            s["k"], s["v"], table, seq, acc_out["accept_len"], B, spine, freed=freed,
-            err=err)[0] for s in sets]))
+        calls.append(("spec_accept_quadratic", lst))
     elif acc is not None:
         lst = []
         for s in sets:
@@ -481,7 +469,7 @@ def main():
         snap = {k: v.cpu().numpy() for k, v in acc_out.items()}
         gpu["accept"] = lambda b: {k: v[b] for k, v in snap.items()}
     if quad:
-        hsnap = ho_out["next_draft"].cpu().numpy()
+        hsnap = acc_out["next_draft"].cpu().numpy()
         gpu["handoff"] = lambda b: hsnap[b]
     al = acc_out["accept_len"].cpu().numpy() if acc_out is not None else None
     cl = acc_out["commit_len"].cpu().numpy() if acc_out is not None else None
@@ -499,9 +487,9 @@ def main():
         elif lacc is not None:
             call_bytes["spec_accept_logits"] = logits_accept_alg_bytes(cfg)
         elif quad:
-            call_bytes["spec_accept"] = accept_alg_bytes(cfg, al)
-            call_bytes["spec_quadratic_handoff"] = handoff_alg_bytes(cfg)
-            call_bytes["spec_commit_kv"] = commit_alg_bytes(cfg, al)
+            call_bytes["spec_accept_quadratic"] = (accept_alg_bytes(cfg, al) +
+                                                   handoff_alg_bytes(cfg) +
+                                                   commit_alg_bytes(cfg, al))
         else:
             call_bytes["spec_accept_prepare"] = accept_alg_bytes(cfg, al) + block_prep_bytes(bs, B)
     if logits is not None:

@@ -331,6 +331,48 @@ int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q
                 void* stream);
 
 /*
+ * spec_accept_quadratic -- one quadratic round's tail in one call: the accept
+ * of the k spine drafts, the hand-off of the next round's drafts and the
+ * spine's commit.
+ *
+ * Every output, both pools and freed_loc equal those of the three calls in
+ * order: spec_accept(bs, k, V, greedy = 0, p, q, draft, u, seq_lens, ...),
+ * spec_quadratic_handoff(bs, k, V, logits_dtype, logits, accept_len, bonus,
+ * mask_token_id, next_draft, next_block), and spec_commit_kv(kv_dtype, bs,
+ * B = (k + 1)^2, Hkv, D, page_size, max_pages, num_pages, seq_lens,
+ * accept_len, path_nodes[b, i] = (i + 1) * (k + 1), page_table, k_pool,
+ * v_pool, freed_loc) ("From DFlash to dLLM Self-Spec (4)", section 4.4.1,
+ * Quadratic Decoding and recursive compaction; section 4.6 for the released
+ * slots). Two launches instead of five: the hand-off's and the commit's
+ * workgroups ride in the accept's two kernels (each finds the accept length
+ * from the same gathered tests).
+ *
+ *   bs, k (1..7), V, p [bs, k+1, V], q [bs, k, V], draft [bs, k], u [bs, k+1],
+ *   seq_lens: as spec_accept with K = k (stochastic form only)
+ *   logits_dtype, logits [bs, (k + 1)^2, V], mask_token_id: as
+ *   spec_quadratic_handoff
+ *   kv_dtype, Hkv, D, page_size, max_pages, num_pages, page_table, k_pool,
+ *   v_pool: as spec_commit_kv (pools updated in place)
+ * Outputs: accept_len, commit_len, bonus, new_seq_lens [bs], out_tokens
+ *   [bs, k+1], next_draft [bs, k], next_block [bs, (k + 1)^2] (nullable),
+ *   freed_loc [bs, (k + 1)^2].
+ * Workspace: spec_accept_quadratic_workspace_bytes(bs, k, V) bytes, contents
+ *   irrelevant; calls sharing it must be ordered.
+ * Errors: those of the three calls.
+ */
+size_t spec_accept_quadratic_workspace_bytes(int bs, int k, int V);
+
+int spec_accept_quadratic(int bs, int k, int V, const float* p, const float* q,
+                          const int32_t* draft, const float* u, const int32_t* seq_lens,
+                          int logits_dtype, const void* logits, int32_t mask_token_id,
+                          int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                          int32_t* out_tokens, int32_t* new_seq_lens, int32_t* next_draft,
+                          int32_t* next_block, int kv_dtype, int Hkv, int D, int page_size,
+                          int max_pages, int num_pages, const int32_t* page_table, void* k_pool,
+                          void* v_pool, int32_t* freed_loc, void* workspace, size_t ws_bytes,
+                          int32_t* err_flags, void* stream);
+
+/*
  * spec_accept_prepare -- spec_accept, then the next round's block in the same
  * call.
  *

@@ -57,6 +57,16 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t) {
   require(!a.next_ids || (a.next_pos && a.next_loc && a.next_tab && a.next_B > 0), "next block");
   return hipErrorInvalidValue;
 }
+hipError_t launch_accept_quadratic(const AcceptArgs& a, bool, hipStream_t) {
+  require(a.nchunk >= 1 && (long long)a.nchunk * a.chunk >= a.V, "chunks cover V");
+  require(a.partial && a.jbuf && a.quad_part_v && a.quad_part_i, "quadratic workspace");
+  require(a.quad_n == (a.K + 1) * (a.K + 1) && a.K <= 7, "quadratic layout");
+  require(a.quad_S >= 1 && a.quad_seg % 8 == 0 && (long long)a.quad_S * a.quad_seg >= a.V,
+          "hand-off segments cover the row");
+  require(a.commit_k && a.commit_v && a.commit_tab && a.commit_freed && a.commit_Hkv > 0,
+          "commit arguments");
+  return hipErrorInvalidValue;
+}
 hipError_t launch_greedy_accept(const AcceptArgs& a, hipStream_t) {
   require(a.greedy_ids != nullptr, "greedy workspace");
   return hipErrorInvalidValue;

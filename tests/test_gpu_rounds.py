@@ -280,3 +280,79 @@ def test_two_quadratic_rounds_chain(gpu_lib):
     for g, r in zip((ids2, pos2, loc2), r2[:3]):
         assert np.array_equal(_np(g), r)
     assert set(ra["accept_len"].tolist()) >= {0, 1, k}
+
+
+@pytest.mark.parametrize("name,over,logit_dt", [
+    ("quadratic_workload", {}, "bf16"),
+    ("k7_f32_d64_p32", dict(bs=5, block=64, quad_k=7, k_spec=7, hq=4, hkv=2, d=64, page=32,
+                            dtype="f32", vocab=4099, ctx_lo=20, ctx_hi=300), "f32"),
+    ("k1_bf16", dict(bs=9, block=4, quad_k=1, k_spec=1, vocab=1000, ctx_lo=3, ctx_hi=90),
+     "bf16"),
+])
+def test_accept_quadratic_is_the_three_calls(gpu_lib, name, over, logit_dt):
+    """spec_accept_quadratic equals spec_accept, spec_quadratic_handoff and
+    spec_commit_kv (spine path) called in order -- every output, both pools
+    and the released slots, bit for bit -- and the reference chain."""
+    cfg = synth.config(8, **over)
+    k, n, V = cfg.quad_k, cfg.block, cfg.vocab
+    print_case("accept_quadratic", name, cfg.bs, k, V)
+    x = synth.make_attn_inputs(cfg, seed=12)
+    acc = synth.make_accept_inputs(cfg, seed=12)
+    for b in (0, 1):      # requests rejecting at the first / second test
+        if b < k:
+            acc.q[b, b] = 0.0
+            acc.q[b, b, acc.draft[b, b]] = 1.0
+            acc.u[b, b] = np.float32(0.99999)
+    rng = np.random.default_rng(12)
+    lg = (rng.standard_normal((cfg.bs, n, V), dtype=np.float32) * 3).astype(np.float32)
+    if logit_dt == "bf16":
+        bits = synth.bf16_bits(lg)
+        lvals, ldev = synth.bf16_to_f32(bits), to_dev(bits)
+    else:
+        lvals, ldev = lg, to_dev(lg)
+    D = lambda a: to_dev(np.ascontiguousarray(a))
+    seq, table = D(x.seq_lens), D(x.page_table)
+    p, q, d, u = D(acc.p), D(acc.q), D(acc.draft), D(acc.u)
+    # fused
+    k1, v1 = D(x.k_pool), D(x.v_pool)
+    e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = va.accept_quadratic(p, q, d, u, seq, ldev, k1, v1, table, 77, err=e1)
+    # the three calls
+    k2, v2 = D(x.k_pool), D(x.v_pool)
+    e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a2 = va.accept(p, q, d, u, seq, err=e2)
+    h2 = va.quadratic_handoff(ldev, a2["accept_len"], k, a2["bonus"], 77, err=e2)
+    spine = np.full((cfg.bs, n), -1, np.int32)
+    spine[:, :k] = quadratic.spine_path(k)
+    f2 = va.commit_kv(k2, v2, table, seq, a2["accept_len"], n, D(spine), err=e2)
+    # without the next block
+    k3, v3 = D(x.k_pool), D(x.v_pool)
+    got3 = va.accept_quadratic(p, q, d, u, seq, ldev, k3, v3, table, 77, next_block=False)
+    torch.cuda.synchronize()
+    for key in ("accept_len", "commit_len", "bonus", "out_tokens", "new_seq_lens"):
+        assert torch.equal(got[key], a2[key]), key
+        assert torch.equal(got3[key], a2[key]), key
+    assert torch.equal(got["next_draft"], h2["next_draft"])
+    assert torch.equal(got3["next_draft"], h2["next_draft"])
+    assert torch.equal(got["next_block"], h2["next_block"])
+    assert torch.equal(got["freed"], f2) and torch.equal(got3["freed"], f2)
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert torch.equal(k3, k2) and torch.equal(v3, v2)
+    assert int(e1.item()) == int(e2.item()) == 0
+    # and the reference chain
+    ra = oracle.accept_batch(acc.p, acc.q, acc.draft, acc.u, x.seq_lens)
+    keep = ~ra["tie_sample"]
+    check_tie_share(int((~keep).sum()), cfg.bs, "accept_quadratic")
+    al = _np(got["accept_len"])
+    assert np.array_equal(al[keep], ra["accept_len"][keep])
+    assert np.array_equal(_np(got["bonus"])[keep], ra["bonus"][keep])
+    for b in np.flatnonzero(keep):
+        r_d, r_b = quadratic.handoff(lvals[b], ra["accept_len"][b], k, ra["bonus"][b], 77)
+        assert _np(got["next_draft"][b]).tolist() == r_d.tolist(), b
+        assert _np(got["next_block"][b]).tolist() == r_b.tolist(), b
+    rk, rv, rfreed = oracle.commit_kv(x.k_pool, x.v_pool, x.page_table, x.seq_lens, al, spine, n)
+    view = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) \
+        if x.k_pool.dtype == np.uint16 else _np
+    assert np.array_equal(view(k1), rk) and np.array_equal(view(v1), rv)
+    assert np.array_equal(_np(got["freed"]), rfreed)
+    assert (al == 0).any() and (al > 0).any()

@@ -37,6 +37,9 @@ _SIGS = {
     "spec_quadratic_handoff_workspace_bytes": (_c_size, [_c_int] * 3),
     "spec_quadratic_handoff": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp, _c_size, _vp, _vp]),
+    "spec_accept_quadratic_workspace_bytes": (_c_size, [_c_int] * 3),
+    "spec_accept_quadratic": (_c_int, [_c_int] * 3 + [_vp] * 5 + [_c_int, _vp, ctypes.c_int32] +
+                              [_vp] * 7 + [_c_int] * 6 + [_vp] * 5 + [_c_size, _vp, _vp]),
     "spec_accept_prepare": (_c_int, [_c_int] * 4 + [_vp] * 10 + [_c_int] * 4 +
                             [ctypes.c_int32] + [_vp] * 5 + [_c_size, _vp, _vp]),
     "block_attn_workspace_bytes": (_c_size, [_c_int] * 6),
@@ -611,6 +614,73 @@ def accept_prepare(p, q, draft, u, seq_lens, page_table, page_size, block_next, 
     enqueue, out = accept_prepare_call(p, q, draft, u, seq_lens, page_table, page_size,
                                        block_next, mask_token_id, num_pages, greedy, out, ws, err,
                                        stream)
+    enqueue()
+    return out
+
+
+def accept_quadratic_workspace_bytes(bs, k, V) -> int:
+    return int(load().spec_accept_quadratic_workspace_bytes(bs, k, V))
+
+
+def accept_quadratic_call(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page_table,
+                          mask_token_id=0, next_block=True, out=None, ws=None, err=None,
+                          stream=None):
+    """Checks the arguments of spec_accept_quadratic once and returns
+    (enqueue, out): the outputs of accept_call plus next_draft [bs, k],
+    next_block [bs, (k + 1)^2] (unless next_block is False) and freed [bs,
+    (k + 1)^2]; k_pool / v_pool are updated in place."""
+    torch = _torch()
+    bs, K1, V = p.shape
+    k = K1 - 1
+    n = (k + 1) * (k + 1)
+    _need(p, "p", torch.float32)
+    _need(q, "q", torch.float32, (bs, k, V))
+    _need(draft, "draft", torch.int32, (bs, k))
+    _need(u, "u", torch.float32, (bs, k + 1))
+    _need(seq_lens, "seq_lens", torch.int32, (bs,))
+    _need(logits, "logits", shape=(bs, n, V))
+    ldt = _dtype_code(logits)
+    num_pages, hkv, P, d = k_pool.shape
+    _need(k_pool, "k_pool")
+    kdt = _dtype_code(k_pool)
+    _need(v_pool, "v_pool", k_pool.dtype, (num_pages, hkv, d, P))
+    _need_table(page_table, bs)
+    _need_err(err)
+    specs = dict(_accept_outputs(bs, k + 1), next_draft=((bs, k),), freed=((bs, n),))
+    if next_block:
+        specs["next_block"] = ((bs, n),)
+    out = _need_out(out, specs, p.device)
+    need = accept_quadratic_workspace_bytes(bs, k, V)
+    if ws is None:
+        ws = workspace(need, p.device)
+    ws_bytes = _need_ws(ws, need)
+    _same_device(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page_table, ws, err,
+                 *out.values())
+    args = (bs, k, V, _ptr(p), _ptr(q), _ptr(draft), _ptr(u), _ptr(seq_lens), ldt, _ptr(logits),
+            mask_token_id, _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
+            _ptr(out["out_tokens"]), _ptr(out["new_seq_lens"]), _ptr(out["next_draft"]),
+            _ptr(out.get("next_block")), kdt, hkv, d, P, page_table.shape[1], num_pages,
+            _ptr(page_table), _ptr(k_pool), _ptr(v_pool), _ptr(out["freed"]), _ptr(ws), ws_bytes,
+            _ptr(err), _stream(stream))
+    fn = load().spec_accept_quadratic
+    keep = (p, q, draft, u, seq_lens, logits, k_pool, v_pool, page_table, out, ws, err)
+
+    def enqueue():
+        _ = keep
+        st = fn(*args)
+        if st != SPEC_OK:
+            _check(st, "spec_accept_quadratic")
+
+    return enqueue, out
+
+
+def accept_quadratic(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page_table,
+                     mask_token_id=0, next_block=True, out=None, ws=None, err=None, stream=None):
+    """A quadratic round's accept, hand-off and spine commit in one call
+    (spec_accept_quadratic)."""
+    enqueue, out = accept_quadratic_call(p, q, draft, u, seq_lens, logits, k_pool, v_pool,
+                                         page_table, mask_token_id, next_block, out, ws, err,
+                                         stream)
     enqueue()
     return out
 

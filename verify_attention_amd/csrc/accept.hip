@@ -111,18 +111,14 @@ struct ResidExcl {
   }
 };
 
-// Kernel 1, one workgroup per (request, vocabulary chunk): the accept length,
-// then the residual (or bonus) mass of every 256-entry sub-block of the chunk
-// (one wave per sub-block, 4 entries per lane).
-__global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs a) {
-  const int b = blockIdx.x / a.nchunk;
-  const int c = blockIdx.x - b * a.nchunk;
+// The accept length of request b, computed by wave 0 and returned to every
+// thread of the workgroup: lane i runs test i; a ballot of the failures gives
+// the first reject (an invalid token id counts as a reject and is flagged in
+// jbuf when write_jbuf).
+__device__ int accept_len_of(const AcceptArgs& a, int b, bool write_jbuf) {
   const int K = a.K, V = a.V;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int s_j;
-
-  // accept length: lane i runs test i; a ballot of the failures gives the
-  // first reject (an invalid token id counts as a reject and is flagged)
   if (wave == 0) {
     bool fail = false, bad = false;
     if (lane < K) {
@@ -142,11 +138,20 @@ __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs 
     const uint64_t bads = __builtin_amdgcn_ballot_w64(bad);
     if (lane == 0) {
       s_j = j;
-      if (c == 0) a.jbuf[b] = j | ((((bads >> j) & 1) && j < K) ? kJTokenErr : 0);
+      if (write_jbuf) a.jbuf[b] = j | ((((bads >> j) & 1) && j < K) ? kJTokenErr : 0);
     }
   }
   __syncthreads();
-  const int j = s_j;
+  return s_j;
+}
+
+// Kernel 1's work for (request b, vocabulary chunk c): the accept length,
+// then the residual (or bonus) mass of every 256-entry sub-block of the chunk
+// (one wave per sub-block, 4 entries per lane).
+__device__ void accept_partial_body(const AcceptArgs& a, int b, int c) {
+  const int K = a.K, V = a.V;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = accept_len_of(a, b, c == 0);
   const float* prow = a.p + ((size_t)b * (K + 1) + j) * V;
   const float* qrow = j < K ? a.q + ((size_t)b * K + j) * V : nullptr;
   const bool vec = rows_aligned(prow, qrow);
@@ -195,6 +200,11 @@ __global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs 
       if (lane == 0) out[sb] = sum;
     }
   }
+}
+
+// Kernel 1, one workgroup per (request, vocabulary chunk).
+__global__ __launch_bounds__(kAccThreads) void accept_partial_kernel(AcceptArgs a) {
+  accept_partial_body(a, blockIdx.x / a.nchunk, blockIdx.x % a.nchunk);
 }
 
 // Smallest index t of sub-block sb with base + sum_{v<=t} r_v > thr, found by
@@ -327,12 +337,11 @@ __device__ void write_next_block(const AcceptArgs& a, int b, int tok, int newL, 
   if (errs) flag_error(a.err, errs);
 }
 
-// Kernel 2, one workgroup per request: scan the sub-block masses, find the
+// Kernel 2's work for request b: scan the sub-block masses, find the
 // sub-block where the running mass passes u_K * S, locate the token inside it,
 // write every output. Every load that does not depend on the accept length
-// goes out first.
-__global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a) {
-  const int b = blockIdx.x;
+// goes out first. Returns the drawn token to every thread.
+__device__ int accept_select_body(const AcceptArgs& a, int b) {
   const int K = a.K, V = a.V;
   const int tid = threadIdx.x;
   __shared__ double s_wave[4];
@@ -385,6 +394,12 @@ __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a
     a.out_tokens[(size_t)b * (K + 1) + tid] = tid < j ? dtok : (tid == j ? tok : -1);
   if (tid == 0 && errs) flag_error(a.err, errs);
   if (a.next_ids) write_next_block(a, b, tok, L + j + 1, tid, kAccThreads);
+  return tok;
+}
+
+// Kernel 2, one workgroup per request.
+__global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a) {
+  accept_select_body(a, blockIdx.x);
 }
 
 // ------------------------------------------------------------- tree verify
@@ -802,6 +817,124 @@ __global__ __launch_bounds__(64) void handoff_select_kernel(HandoffArgs h) {
     else if (rem == 0) v = draft;
     h.next_block[(size_t)b * h.n + lane] = v;
   }
+}
+
+// ------------------------------------------------- quadratic round in one call
+// spec_accept_quadratic: the accept of a quadratic block's k spine drafts, the
+// hand-off of the next round's drafts and the spine's commit, as two kernels.
+// Kernel 1 holds the accept's chunk workgroups and the hand-off's segment
+// workgroups (each of which finds the accept length itself, from the same
+// gathered tests, before scanning its segment of the chosen group's row).
+// Kernel 2 holds, per request, the accept's draw (which then merges the
+// hand-off's segments and writes the drafts and the next block) and one
+// workgroup per KV head moving that head's accepted spine rows.
+template <typename T>
+__global__ __launch_bounds__(kAccThreads) void accept_quad_partial_kernel(AcceptArgs a) {
+  const int nacc = a.bs * a.nchunk;
+  if ((int)blockIdx.x < nacc) {
+    accept_partial_body(a, blockIdx.x / a.nchunk, blockIdx.x % a.nchunk);
+    return;
+  }
+  const int idx = blockIdx.x - nacc;
+  const int k = a.K, S = a.quad_S;
+  const int seg = idx % S, r = idx / S;
+  const int b = r / k, m = r - b * k;
+  const int j = accept_len_of(a, b, false);
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  const int e0 = seg * a.quad_seg;
+  const int n = min(a.V - e0, a.quad_seg);
+  if (n > 0) {
+    const T* row = reinterpret_cast<const T*>(a.quad_logits) +
+                   ((size_t)b * a.quad_n + (size_t)j * (k + 1) + 1 + m) * a.V + e0;
+    argmax_row_pair(row, n, bv, bi);
+  }
+  if (threadIdx.x == 0) {
+    a.quad_part_v[idx] = bv;
+    a.quad_part_i[idx] = bi == 0x7fffffff ? bi : bi + e0;
+  }
+}
+
+// Wave 0 of the drawing workgroup: the drafts from the segments of group
+// G_j, and the next block (bonus, drafts on the spine rows, mask elsewhere).
+__device__ void quad_handoff_merge(const AcceptArgs& a, int b, int j, int bonus) {
+  const int lane = threadIdx.x, k = a.K, n = a.quad_n, S = a.quad_S;
+  int tok = -1;
+  if (lane < k) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    const size_t base = ((size_t)b * k + lane) * S;
+    for (int s = 0; s < S; ++s) better(bv, bi, a.quad_part_v[base + s], a.quad_part_i[base + s]);
+    tok = bi == 0x7fffffff ? 0 : bi;
+    a.quad_next_draft[(size_t)b * k + lane] = tok;
+  }
+  const int jj = lane / (k + 1), rem = lane - jj * (k + 1);
+  const int draft = __shfl(tok, jj > 0 && jj <= k ? jj - 1 : 0, 64);  // every lane takes part
+  if (a.quad_next_block && lane < n) {
+    int32_t v = a.quad_mask;
+    if (lane == 0) v = bonus;
+    else if (rem == 0) v = draft;
+    a.quad_next_block[(size_t)b * n + lane] = v;
+  }
+  (void)j;
+}
+
+// One KV head's share of the spine commit: the accepted spine drafts (rows
+// i * (k + 1), i = 1 .. d) move to positions L + 1 .. L + d; KV head 0 also
+// lists the released slots of the n-row block.
+template <typename KVT>
+__device__ void quad_commit_head(const AcceptArgs& a, int b, int h) {
+  __shared__ long long s_ksrc[64], s_kdst[64], s_vsrc[64], s_vdst[64];
+  __shared__ int s_cerr;
+  const CommitRows rows{s_ksrc, s_kdst, s_vsrc, s_vdst};
+  const int tid = threadIdx.x, n = a.quad_n, k = a.K, P = a.commit_P;
+  const int32_t* tab = a.commit_tab + (size_t)b * a.commit_max_pages;
+  const int L = a.seq_lens[b];
+  const bool cap_ok = L >= 0 && (long long)L + n <= (long long)a.commit_max_pages * P;
+  const int d = cap_ok ? a.jbuf[b] & 0xffff : -1;
+  if (tid < 64) {
+    const bool bad = commit_row_bases(rows, tab, P, a.commit_D, a.commit_Hkv, a.commit_num_pages,
+                                      h, L, d, (tid + 1) * (k + 1));
+    if (tid == 0) s_cerr = (cap_ok ? 0 : kErrCapacity) | (bad ? kErrSlot : 0);
+  }
+  __syncthreads();
+  commit_move_rows<KVT>(rows, reinterpret_cast<KVT*>(a.commit_k),
+                        reinterpret_cast<KVT*>(a.commit_v), P, a.commit_D, d);
+  if (h == 0) {
+    if (commit_freed(a.commit_freed + (size_t)b * n, tab, P, n, a.commit_num_pages, L, d))
+      atomicOr(&s_cerr, kErrSlot);
+    __syncthreads();
+  }
+  if (tid == 0 && s_cerr) flag_error(a.err, s_cerr);
+}
+
+template <typename KVT>
+__global__ __launch_bounds__(kAccThreads) void accept_quad_select_kernel(AcceptArgs a) {
+  const int H1 = a.commit_Hkv + 1;
+  const int b = blockIdx.x / H1, h = blockIdx.x - b * H1;
+  if (h == H1 - 1) {
+    const int tok = accept_select_body(a, b);
+    if (threadIdx.x < 64) quad_handoff_merge(a, b, a.jbuf[b] & 0xffff, tok);
+  } else {
+    quad_commit_head<KVT>(a, b, h);
+  }
+}
+
+hipError_t launch_accept_quadratic(const AcceptArgs& a, bool logits_bf16, hipStream_t stream) {
+  const dim3 block(kAccThreads);
+  const dim3 g1(a.bs * a.nchunk + a.bs * a.K * a.quad_S);
+  if (logits_bf16)
+    hipLaunchKernelGGL(accept_quad_partial_kernel<__bf16>, g1, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(accept_quad_partial_kernel<float>, g1, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2(a.bs * (a.commit_Hkv + 1));
+  if (a.commit_bf16)
+    hipLaunchKernelGGL(accept_quad_select_kernel<__bf16>, g2, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(accept_quad_select_kernel<float>, g2, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_quadratic_handoff(const HandoffArgs& h, bool bf16, hipStream_t stream) {

@@ -481,6 +481,86 @@ SPEC_API int spec_accept_prepare(int bs, int K, int V, int greedy, const float* 
   return accept_launch(a, plan, static_cast<char*>(workspace), greedy, stream);
 }
 
+namespace {
+
+// spec_accept_quadratic's workspace: the accept's (accept lengths, sub-block
+// masses) followed by the hand-off's segment maxima.
+struct QuadPlan {
+  AccPlan acc;
+  HandoffPlan ho;
+  size_t off_ho = 0, ws_bytes = 0;
+};
+
+QuadPlan plan_quadratic(int bs, int k, int V) {
+  QuadPlan p;
+  p.acc = plan_accept(bs, k, V, 0);
+  p.ho = plan_handoff(bs, k, V);
+  p.off_ho = align_up(p.acc.ws_bytes, 256);
+  p.ws_bytes = p.off_ho + p.ho.ws_bytes;
+  return p;
+}
+
+}  // namespace
+
+SPEC_API size_t spec_accept_quadratic_workspace_bytes(int bs, int k, int V) {
+  if (bs <= 0 || k < 1 || k > 7 || V <= 0) return 0;
+  return plan_quadratic(bs, k, V).ws_bytes;
+}
+
+SPEC_API int spec_accept_quadratic(int bs, int k, int V, const float* p, const float* q,
+                                   const int32_t* draft, const float* u, const int32_t* seq_lens,
+                                   int logits_dtype, const void* logits, int32_t mask_token_id,
+                                   int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
+                                   int32_t* out_tokens, int32_t* new_seq_lens,
+                                   int32_t* next_draft, int32_t* next_block, int kv_dtype,
+                                   int Hkv, int D, int page_size, int max_pages, int num_pages,
+                                   const int32_t* page_table, void* k_pool, void* v_pool,
+                                   int32_t* freed_loc, void* workspace, size_t ws_bytes,
+                                   int32_t* err_flags, void* stream) {
+  if (logits_dtype != SPEC_F32 && logits_dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (kv_dtype != SPEC_F32 && kv_dtype != SPEC_BF16) return SPEC_ENOTSUP;
+  if (D != 64 && D != 128) return SPEC_ENOTSUP;
+  if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
+  if (k < 1 || k > 7) return SPEC_EINVAL;
+  AcceptArgs a;
+  AccPlan acc_plan;
+  const int st = accept_check_args(bs, k, V, 0, p, q, draft, u, seq_lens, accept_len, commit_len,
+                                   bonus, out_tokens, new_seq_lens, err_flags, &a, &acc_plan);
+  if (st != SPEC_OK) return st;
+  const int n = (k + 1) * (k + 1);
+  if ((long long)bs * n > INT_MAX / 16) return SPEC_EINVAL;
+  if (Hkv <= 0 || max_pages <= 0 || num_pages <= 0) return SPEC_EINVAL;
+  if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
+  if (!logits || !next_draft || !page_table || !k_pool || !v_pool || !freed_loc)
+    return SPEC_EINVAL;
+  const QuadPlan plan = plan_quadratic(bs, k, V);
+  if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
+  char* ws = static_cast<char*>(workspace);
+  a.jbuf = reinterpret_cast<int32_t*>(ws + plan.acc.off_jbuf);
+  a.partial = reinterpret_cast<double*>(ws + plan.acc.off_partial);
+  a.quad_logits = logits;
+  a.quad_next_draft = next_draft;
+  a.quad_next_block = next_block;
+  a.quad_part_v = reinterpret_cast<float*>(ws + plan.off_ho);
+  a.quad_part_i = reinterpret_cast<int32_t*>(ws + plan.off_ho + plan.ho.off_i);
+  a.quad_n = n;
+  a.quad_S = plan.ho.S;
+  a.quad_seg = plan.ho.seg_len;
+  a.quad_mask = mask_token_id;
+  a.commit_k = k_pool;
+  a.commit_v = v_pool;
+  a.commit_tab = page_table;
+  a.commit_freed = freed_loc;
+  a.commit_bf16 = kv_dtype == SPEC_BF16 ? 1 : 0;
+  a.commit_Hkv = Hkv;
+  a.commit_D = D;
+  a.commit_P = page_size;
+  a.commit_max_pages = max_pages;
+  a.commit_num_pages = num_pages;
+  return hip_status(launch_accept_quadratic(a, logits_dtype == SPEC_BF16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 SPEC_API size_t spec_accept_tree_workspace_bytes(int bs, int N, int V) {
   if (bs <= 0 || N < 1 || N > 64 || V <= 0) return 0;
   return plan_accept_tree(bs, N, V).ws_bytes;

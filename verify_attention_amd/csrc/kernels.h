@@ -125,6 +125,16 @@ struct AcceptArgs {
   const int32_t* next_tab;        // page_table [bs][next_max_pages]
   int next_B, next_P, next_max_pages, next_num_pages;
   int32_t next_mask;
+  // quadratic round in one call (spec_accept_quadratic): the hand-off of the
+  // next drafts from the layout's logits [bs][quad_n][V] and the spine commit
+  // (the commit_* fields above, with quad_n rows per block)
+  const void* quad_logits;
+  int32_t* quad_next_draft;       // [bs][K]
+  int32_t* quad_next_block;       // [bs][quad_n] or null
+  float* quad_part_v;             // [bs][K][quad_S] segment maxima (workspace)
+  int32_t* quad_part_i;           // [bs][K][quad_S] their lowest indices
+  int quad_n, quad_S, quad_seg;
+  int32_t quad_mask;
   int bs, K, V, nchunk, chunk;
 };
 
@@ -133,6 +143,7 @@ struct AcceptArgs {
 constexpr int kMaxAcceptVocab = 8 * 256 * 256;
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+hipError_t launch_accept_quadratic(const AcceptArgs& a, bool logits_bf16, hipStream_t stream);
 
 // Sampling parameters (temperature, top-k, top-p) in front of the accept.
 constexpr int kMaxSampVocab = 524288;  // tile maxima of a row: 32 per thread of 256
