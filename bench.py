@@ -7,9 +7,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   draft workload:   spec_prepare_block (draft pass) -> block_attn -> spec_draft_argmax
   tree workload:    spec_prepare_tree -> block_attn_tree -> spec_accept_tree_commit
   logits workload:  spec_prepare_block (verify pass) -> block_attn -> spec_accept_logits
-  quadratic layout: spec_prepare_tree -> block_attn_tree -> spec_accept_quadratic
-                    (the spine drafts' accept, the hand-off of the next drafts
-                    and the spine's commit in one call)
+  quadratic layout: block_attn_tree -> spec_accept_quadratic (the spine
+                    drafts' accept, the hand-off of the next drafts, the
+                    spine's commit and the next round's block in one call)
 Inputs are resident in HBM before the timed region. Several copies of the
 per-step inputs are cycled so that every step reads its KV pages and target
 rows from HBM rather than from the 256 MB last-level cache.
@@ -342,10 +342,6 @@ def main():
     if tree or quad:
         tmask = torch.from_numpy(masks.view(np.int64)).to(dev)
         tpar = up(np.ascontiguousarray(parents, dtype=np.int32))
-    if quad:
-        node_tokens = np.full((bs, B), MASK_TOKEN, np.int32)
-        node_tokens[:, [i * (cfg.quad_k + 1) for i in range(1, cfg.quad_k + 1)]] = acc.draft
-        ntok = up(node_tokens)
     if tree:
         ttok = up(tacc.token)
         ws_tacc = va.workspace(va.accept_tree_workspace_bytes(bs, B, cfg.vocab))
@@ -358,9 +354,10 @@ def main():
     calls = []      # per step: list of (name, [enqueue per input copy])
     acc_out = None
     if tree or quad:
-        calls.append(("spec_prepare_tree", [va.prepare_tree_call(
-            vid, seq, table, cfg.page, tpar, MASK_TOKEN, x.num_pages, ttok if tree else ntok,
-            out=prep_out, err=err)[0]] * copies))
+        if tree:  # a quadratic round's block is prepared by the previous round's accept
+            calls.append(("spec_prepare_tree", [va.prepare_tree_call(
+                vid, seq, table, cfg.page, tpar, MASK_TOKEN, x.num_pages, ttok,
+                out=prep_out, err=err)[0]] * copies))
         calls.append(("block_attn_tree", [va.block_attn_tree_call(
             tmask, s["q"], s["k"], s["v"], table, seq, max_kv, out=o, ws=ws_attn,
             err=err)[0] for s in sets]))
@@ -388,7 +385,8 @@ def main():
         for s in sets:
             c, acc_out = va.accept_quadratic_call(s["p"], s["qd"], s["draft"], s["u"], seq,
                                                   s["qlogits"], s["k"], s["v"], table,
-                                                  MASK_TOKEN, out=acc_out, ws=ws_q, err=err)
+                                                  MASK_TOKEN, prepare_next=True, out=acc_out,
+                                                  ws=ws_q, err=err)
             lst.append(c)
         calls.append(("spec_accept_quadratic", lst))
     elif acc is not None:
@@ -489,7 +487,8 @@ def main():
         elif quad:
             call_bytes["spec_accept_quadratic"] = (accept_alg_bytes(cfg, al) +
                                                    handoff_alg_bytes(cfg) +
-                                                   commit_alg_bytes(cfg, al))
+                                                   commit_alg_bytes(cfg, al) +
+                                                   2 * bs * B * 4)
         else:
             call_bytes["spec_accept_prepare"] = accept_alg_bytes(cfg, al) + block_prep_bytes(bs, B)
     if logits is not None:

@@ -343,9 +343,14 @@ int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q
  * accept_len, path_nodes[b, i] = (i + 1) * (k + 1), page_table, k_pool,
  * v_pool, freed_loc) ("From DFlash to dLLM Self-Spec (4)", section 4.4.1,
  * Quadratic Decoding and recursive compaction; section 4.6 for the released
- * slots). Two launches instead of five: the hand-off's and the commit's
- * workgroups ride in the accept's two kernels (each finds the accept length
- * from the same gathered tests).
+ * slots). With next_positions / next_cache_loc, the call also prepares the
+ * next round's block: they equal spec_prepare_tree's positions and cache_loc
+ * for verified_id = bonus, seq_lens = new_seq_lens and the layout's position
+ * order (row j' (k + 1) + m' at depth j' + m'), the same page table (so the
+ * next round needs no preparation launch; next_block holds its tokens). Two
+ * launches instead of five (six with the preparation): the hand-off's and the
+ * commit's workgroups ride in the accept's two kernels (each finds the accept
+ * length from the same gathered tests).
  *
  *   bs, k (1..7), V, p [bs, k+1, V], q [bs, k, V], draft [bs, k], u [bs, k+1],
  *   seq_lens: as spec_accept with K = k (stochastic form only)
@@ -355,7 +360,9 @@ int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q
  *   v_pool: as spec_commit_kv (pools updated in place)
  * Outputs: accept_len, commit_len, bonus, new_seq_lens [bs], out_tokens
  *   [bs, k+1], next_draft [bs, k], next_block [bs, (k + 1)^2] (nullable),
- *   freed_loc [bs, (k + 1)^2].
+ *   next_positions, next_cache_loc [bs, (k + 1)^2] (both or neither; missing
+ *   slots give -1 with SPEC_ERR_SLOT, a block past the table row
+ *   SPEC_ERR_CAPACITY), freed_loc [bs, (k + 1)^2].
  * Workspace: spec_accept_quadratic_workspace_bytes(bs, k, V) bytes, contents
  *   irrelevant; calls sharing it must be ordered.
  * Errors: those of the three calls.
@@ -367,7 +374,8 @@ int spec_accept_quadratic(int bs, int k, int V, const float* p, const float* q,
                           int logits_dtype, const void* logits, int32_t mask_token_id,
                           int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
                           int32_t* out_tokens, int32_t* new_seq_lens, int32_t* next_draft,
-                          int32_t* next_block, int kv_dtype, int Hkv, int D, int page_size,
+                          int32_t* next_block, int32_t* next_positions, int32_t* next_cache_loc,
+                          int kv_dtype, int Hkv, int D, int page_size,
                           int max_pages, int num_pages, const int32_t* page_table, void* k_pool,
                           void* v_pool, int32_t* freed_loc, void* workspace, size_t ws_bytes,
                           int32_t* err_flags, void* stream);

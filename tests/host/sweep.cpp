@@ -100,19 +100,25 @@ int main() {
       for (int V : {9, 4099, 151936}) {
         const size_t wq = spec_accept_quadratic_workspace_bytes(bs, k, V);
         EXPECT(spec_accept_quadratic(bs, k, V, FL, FL, I, FL, I, SPEC_BF16, F, 7, I, I, I, I, I, I,
-                                     I, SPEC_BF16, 8, 128, 16, 80, 300, I, F, F, I, F, wq, I,
+                                     I, I, I, SPEC_BF16, 8, 128, 16, 80, 300, I, F, F, I, F, wq, I,
                                      nullptr),
                SPEC_EHIP);
         EXPECT(spec_accept_quadratic(bs, k, V, FL, FL, I, FL, I, SPEC_F32, F, 7, I, I, I, I, I, I,
-                                     nullptr, SPEC_F32, 2, 64, 32, 80, 300, I, F, F, I, F, wq - 1,
-                                     I, nullptr),
+                                     nullptr, nullptr, nullptr, SPEC_F32, 2, 64, 32, 80, 300, I, F,
+                                     F, I, F, wq - 1, I, nullptr),
                SPEC_ENOSPC);
+        EXPECT(spec_accept_quadratic(bs, k, V, FL, FL, I, FL, I, SPEC_F32, F, 7, I, I, I, I, I, I,
+                                     nullptr, I, nullptr, SPEC_F32, 2, 64, 32, 80, 300, I, F, F, I,
+                                     F, wq, I, nullptr),
+               SPEC_EINVAL);  // positions without slots
       }
   EXPECT(spec_accept_quadratic(4, 8, 512, FL, FL, I, FL, I, SPEC_BF16, F, 7, I, I, I, I, I, I, I,
-                               SPEC_BF16, 8, 128, 16, 80, 300, I, F, F, I, F, 1 << 30, I, nullptr),
+                               I, I, SPEC_BF16, 8, 128, 16, 80, 300, I, F, F, I, F, 1 << 30, I,
+                               nullptr),
          SPEC_EINVAL);
   EXPECT(spec_accept_quadratic(4, 4, 512, FL, FL, I, FL, I, SPEC_BF16, F, 7, I, I, I, I, I, I, I,
-                               SPEC_BF16, 8, 96, 16, 80, 300, I, F, F, I, F, 1 << 30, I, nullptr),
+                               I, I, SPEC_BF16, 8, 96, 16, 80, 300, I, F, F, I, F, 1 << 30, I,
+                               nullptr),
          SPEC_ENOTSUP);
   EXPECT(spec_draft_argmax(1984, 157184, SPEC_BF16, F, I, nullptr), SPEC_EHIP);
   EXPECT(spec_draft_argmax(0, 157184, SPEC_BF16, F, I, nullptr), SPEC_EINVAL);

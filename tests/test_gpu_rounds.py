@@ -290,9 +290,11 @@ def test_two_quadratic_rounds_chain(gpu_lib):
      "bf16"),
 ])
 def test_accept_quadratic_is_the_three_calls(gpu_lib, name, over, logit_dt):
-    """spec_accept_quadratic equals spec_accept, spec_quadratic_handoff and
-    spec_commit_kv (spine path) called in order -- every output, both pools
-    and the released slots, bit for bit -- and the reference chain."""
+    """spec_accept_quadratic equals spec_accept, spec_quadratic_handoff,
+    spec_commit_kv (spine path) and spec_prepare_tree of the next block
+    called in order -- every output, both pools, the released slots and the
+    next block's positions and slots, bit for bit -- and the reference
+    chain."""
     cfg = synth.config(8, **over)
     k, n, V = cfg.quad_k, cfg.block, cfg.vocab
     print_case("accept_quadratic", name, cfg.bs, k, V)
@@ -316,7 +318,8 @@ def test_accept_quadratic_is_the_three_calls(gpu_lib, name, over, logit_dt):
     # fused
     k1, v1 = D(x.k_pool), D(x.v_pool)
     e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
-    got = va.accept_quadratic(p, q, d, u, seq, ldev, k1, v1, table, 77, err=e1)
+    got = va.accept_quadratic(p, q, d, u, seq, ldev, k1, v1, table, 77, prepare_next=True,
+                              err=e1)
     # the three calls
     k2, v2 = D(x.k_pool), D(x.v_pool)
     e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -325,6 +328,9 @@ def test_accept_quadratic_is_the_three_calls(gpu_lib, name, over, logit_dt):
     spine = np.full((cfg.bs, n), -1, np.int32)
     spine[:, :k] = quadratic.spine_path(k)
     f2 = va.commit_kv(k2, v2, table, seq, a2["accept_len"], n, D(spine), err=e2)
+    par = D(synth.quadratic_parents(k))
+    p2 = va.prepare_tree(a2["bonus"], a2["new_seq_lens"], table, cfg.page, par, 77, x.num_pages,
+                         h2["next_block"], err=e2)
     # without the next block
     k3, v3 = D(x.k_pool), D(x.v_pool)
     got3 = va.accept_quadratic(p, q, d, u, seq, ldev, k3, v3, table, 77, next_block=False)
@@ -336,6 +342,8 @@ def test_accept_quadratic_is_the_three_calls(gpu_lib, name, over, logit_dt):
     assert torch.equal(got3["next_draft"], h2["next_draft"])
     assert torch.equal(got["next_block"], h2["next_block"])
     assert torch.equal(got["freed"], f2) and torch.equal(got3["freed"], f2)
+    assert torch.equal(got["positions"], p2[1]) and torch.equal(got["cache_loc"], p2[2])
+    assert "positions" not in got3
     assert torch.equal(k1, k2) and torch.equal(v1, v2)
     assert torch.equal(k3, k2) and torch.equal(v3, v2)
     assert int(e1.item()) == int(e2.item()) == 0
@@ -355,4 +363,11 @@ def test_accept_quadratic_is_the_three_calls(gpu_lib, name, over, logit_dt):
         if x.k_pool.dtype == np.uint16 else _np
     assert np.array_equal(view(k1), rk) and np.array_equal(view(v1), rv)
     assert np.array_equal(_np(got["freed"]), rfreed)
+    _, r_pos, r_loc, r_err = oracle.prepare_tree(_np(got["bonus"]), _np(got["new_seq_lens"]),
+                                                 x.page_table, cfg.page,
+                                                 synth.quadratic_parents(k), 77, None,
+                                                 x.num_pages)
+    assert r_err == 0
+    assert np.array_equal(_np(got["positions"]), r_pos)
+    assert np.array_equal(_np(got["cache_loc"]), r_loc)
     assert (al == 0).any() and (al > 0).any()

@@ -39,7 +39,7 @@ _SIGS = {
                                         ctypes.c_int32, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "spec_accept_quadratic_workspace_bytes": (_c_size, [_c_int] * 3),
     "spec_accept_quadratic": (_c_int, [_c_int] * 3 + [_vp] * 5 + [_c_int, _vp, ctypes.c_int32] +
-                              [_vp] * 7 + [_c_int] * 6 + [_vp] * 5 + [_c_size, _vp, _vp]),
+                              [_vp] * 9 + [_c_int] * 6 + [_vp] * 5 + [_c_size, _vp, _vp]),
     "spec_accept_prepare": (_c_int, [_c_int] * 4 + [_vp] * 10 + [_c_int] * 4 +
                             [ctypes.c_int32] + [_vp] * 5 + [_c_size, _vp, _vp]),
     "block_attn_workspace_bytes": (_c_size, [_c_int] * 6),
@@ -623,12 +623,13 @@ def accept_quadratic_workspace_bytes(bs, k, V) -> int:
 
 
 def accept_quadratic_call(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page_table,
-                          mask_token_id=0, next_block=True, out=None, ws=None, err=None,
-                          stream=None):
+                          mask_token_id=0, next_block=True, prepare_next=False, out=None,
+                          ws=None, err=None, stream=None):
     """Checks the arguments of spec_accept_quadratic once and returns
     (enqueue, out): the outputs of accept_call plus next_draft [bs, k],
-    next_block [bs, (k + 1)^2] (unless next_block is False) and freed [bs,
-    (k + 1)^2]; k_pool / v_pool are updated in place."""
+    next_block [bs, (k + 1)^2] (unless next_block is False), with
+    prepare_next the next round's positions and cache_loc [bs, (k + 1)^2],
+    and freed [bs, (k + 1)^2]; k_pool / v_pool are updated in place."""
     torch = _torch()
     bs, K1, V = p.shape
     k = K1 - 1
@@ -649,6 +650,9 @@ def accept_quadratic_call(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page
     specs = dict(_accept_outputs(bs, k + 1), next_draft=((bs, k),), freed=((bs, n),))
     if next_block:
         specs["next_block"] = ((bs, n),)
+    if prepare_next:
+        specs["positions"] = ((bs, n),)
+        specs["cache_loc"] = ((bs, n),)
     out = _need_out(out, specs, p.device)
     need = accept_quadratic_workspace_bytes(bs, k, V)
     if ws is None:
@@ -659,7 +663,8 @@ def accept_quadratic_call(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page
     args = (bs, k, V, _ptr(p), _ptr(q), _ptr(draft), _ptr(u), _ptr(seq_lens), ldt, _ptr(logits),
             mask_token_id, _ptr(out["accept_len"]), _ptr(out["commit_len"]), _ptr(out["bonus"]),
             _ptr(out["out_tokens"]), _ptr(out["new_seq_lens"]), _ptr(out["next_draft"]),
-            _ptr(out.get("next_block")), kdt, hkv, d, P, page_table.shape[1], num_pages,
+            _ptr(out.get("next_block")), _ptr(out.get("positions")), _ptr(out.get("cache_loc")),
+            kdt, hkv, d, P, page_table.shape[1], num_pages,
             _ptr(page_table), _ptr(k_pool), _ptr(v_pool), _ptr(out["freed"]), _ptr(ws), ws_bytes,
             _ptr(err), _stream(stream))
     fn = load().spec_accept_quadratic
@@ -675,12 +680,14 @@ def accept_quadratic_call(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page
 
 
 def accept_quadratic(p, q, draft, u, seq_lens, logits, k_pool, v_pool, page_table,
-                     mask_token_id=0, next_block=True, out=None, ws=None, err=None, stream=None):
+                     mask_token_id=0, next_block=True, prepare_next=False, out=None, ws=None,
+                     err=None, stream=None):
     """A quadratic round's accept, hand-off and spine commit in one call
-    (spec_accept_quadratic)."""
+    (spec_accept_quadratic); with prepare_next also the next round's block
+    positions and slots."""
     enqueue, out = accept_quadratic_call(p, q, draft, u, seq_lens, logits, k_pool, v_pool,
-                                         page_table, mask_token_id, next_block, out, ws, err,
-                                         stream)
+                                         page_table, mask_token_id, next_block, prepare_next,
+                                         out, ws, err, stream)
     enqueue()
     return out
 

@@ -856,7 +856,11 @@ __global__ __launch_bounds__(kAccThreads) void accept_quad_partial_kernel(Accept
 }
 
 // Wave 0 of the drawing workgroup: the drafts from the segments of group
-// G_j, and the next block (bonus, drafts on the spine rows, mask elsewhere).
+// G_j, and the next block (bonus, drafts on the spine rows, mask elsewhere);
+// with next_pos, also the next block's positions and slots (the quadratic
+// layout's position order: row r = j' (k + 1) + m' sits at depth j' + m'
+// after the new committed length, and its K/V at slot L' + r), as
+// spec_prepare_tree writes them.
 __device__ void quad_handoff_merge(const AcceptArgs& a, int b, int j, int bonus) {
   const int lane = threadIdx.x, k = a.K, n = a.quad_n, S = a.quad_S;
   int tok = -1;
@@ -876,7 +880,24 @@ __device__ void quad_handoff_merge(const AcceptArgs& a, int b, int j, int bonus)
     else if (rem == 0) v = draft;
     a.quad_next_block[(size_t)b * n + lane] = v;
   }
-  (void)j;
+  if (a.next_pos) {
+    // the next round's block starts at the new committed length
+    const int L2 = a.seq_lens[b] + j + 1;
+    const int P = a.commit_P;
+    if (lane == 0 && (L2 < 0 || (long long)L2 + n > (long long)a.commit_max_pages * P))
+      flag_error(a.err, kErrCapacity);
+    if (lane < n) {
+      const long long pos = (long long)L2 + lane;
+      int32_t slot = -1;
+      if (pos >= 0 && pos / P < a.commit_max_pages) {
+        const int32_t page = a.commit_tab[(size_t)b * a.commit_max_pages + pos / P];
+        if (page >= 0 && page < a.commit_num_pages) slot = page * P + (int32_t)(pos % P);
+      }
+      if (slot < 0) flag_error(a.err, kErrSlot);
+      a.next_pos[(size_t)b * n + lane] = L2 + jj + rem;
+      a.next_loc[(size_t)b * n + lane] = slot;
+    }
+  }
 }
 
 // One KV head's share of the spine commit: the accepted spine drafts (rows

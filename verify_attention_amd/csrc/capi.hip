@@ -512,7 +512,8 @@ SPEC_API int spec_accept_quadratic(int bs, int k, int V, const float* p, const f
                                    int logits_dtype, const void* logits, int32_t mask_token_id,
                                    int32_t* accept_len, int32_t* commit_len, int32_t* bonus,
                                    int32_t* out_tokens, int32_t* new_seq_lens,
-                                   int32_t* next_draft, int32_t* next_block, int kv_dtype,
+                                   int32_t* next_draft, int32_t* next_block,
+                                   int32_t* next_positions, int32_t* next_cache_loc, int kv_dtype,
                                    int Hkv, int D, int page_size, int max_pages, int num_pages,
                                    const int32_t* page_table, void* k_pool, void* v_pool,
                                    int32_t* freed_loc, void* workspace, size_t ws_bytes,
@@ -533,6 +534,7 @@ SPEC_API int spec_accept_quadratic(int bs, int k, int V, const float* p, const f
   if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
   if (!logits || !next_draft || !page_table || !k_pool || !v_pool || !freed_loc)
     return SPEC_EINVAL;
+  if (!next_positions != !next_cache_loc) return SPEC_EINVAL;
   const QuadPlan plan = plan_quadratic(bs, k, V);
   if (!workspace || ws_bytes < plan.ws_bytes) return SPEC_ENOSPC;
   char* ws = static_cast<char*>(workspace);
@@ -547,6 +549,8 @@ SPEC_API int spec_accept_quadratic(int bs, int k, int V, const float* p, const f
   a.quad_S = plan.ho.S;
   a.quad_seg = plan.ho.seg_len;
   a.quad_mask = mask_token_id;
+  a.next_pos = next_positions;
+  a.next_loc = next_cache_loc;
   a.commit_k = k_pool;
   a.commit_v = v_pool;
   a.commit_tab = page_table;
