@@ -694,7 +694,6 @@ __device__ __forceinline__ void argmax_row_pair(const T* row, int V, float& out_
   if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {
     const int nv = V / kVec;
     const vecT* rv = reinterpret_cast<const vecT*>(row);
-    int bvec = -1;  // first vector of this thread whose maximum reached bv
     // the last batch is partial: its loads past the row end are skipped, so
     // the tail keeps kIn loads in flight per lane like the rest
     for (int e = threadIdx.x; e < nv; e += kIn * kAccThreads) {
@@ -709,16 +708,17 @@ __device__ __forceinline__ void argmax_row_pair(const T* row, int V, float& out_
 #pragma unroll
         for (int j = 1; j < kVec; ++j) m = fmaxf(m, to_f32(v[k][j]));
         // later vectors hold larger indices: only a larger value wins (the
-        // first vector whose maximum is -inf counts when nothing larger was seen)
-        const bool up = m > bv || (bvec < 0 && m == bv);
-        bv = up ? m : bv;
-        bvec = up ? e + k * kAccThreads : bvec;
-      }
-    }
-    if (bvec >= 0) {
-      const vecT v = rv[bvec];
+        // first vector whose maximum is -inf counts when nothing was seen);
+        // the winner's lowest index holding the value is found from the
+        // registers, so the (non-temporal, evicted) vector is never re-read
+        if (m > bv || (bi == 0x7fffffff && m == bv)) {
+          int jf = kVec - 1;
 #pragma unroll
-      for (int j = kVec - 1; j >= 0; --j) bi = to_f32(v[j]) == bv ? bvec * kVec + j : bi;
+          for (int j = kVec - 2; j >= 0; --j) jf = to_f32(v[k][j]) == m ? j : jf;
+          bv = m;
+          bi = (e + k * kAccThreads) * kVec + jf;
+        }
+      }
     }
     t = nv * kVec;
   }
