@@ -203,10 +203,17 @@ def _need_out(out, specs, dev):
 
 
 def _same_device(*ts):
-    """Every tensor given lives on one GPU."""
+    """Every tensor given lives on one GPU, the current one (the library
+    launches on the current device and plans for its compute units)."""
     devs = {t.device for t in ts if t is not None}
     if len(devs) > 1:
         raise SpecError(f"tensors live on different devices: {sorted(map(str, devs))}")
+    dev = next(iter(devs), None)
+    if dev is not None and dev.type == "cuda":
+        torch = _torch()
+        cur = torch.cuda.current_device()
+        if (dev.index if dev.index is not None else cur) != cur:
+            raise SpecError(f"tensors live on {dev}, but the current device is cuda:{cur}")
 
 
 def _dtype_code(t):
