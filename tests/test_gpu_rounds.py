@@ -100,7 +100,7 @@ def test_prepare_tree_error_flags(gpu_lib):
 
 
 # -------------------------------------------------------- accept_prepare
-@pytest.mark.parametrize("cid,bs,B_next,greedy", [(2, None, 16, False), (4, 64, 16, False),
+@pytest.mark.parametrize("cid,bs,B_next,greedy", [(2, None, 16, False), (4, None, 16, False),
                                                   (1, 40, 300, False), (2, 8, 32, True)])
 def test_accept_prepare_is_accept_then_prepare(gpu_lib, cid, bs, B_next, greedy):
     """Every output equals spec_accept followed by spec_prepare_block on the
