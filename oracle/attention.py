@@ -50,14 +50,20 @@ def visible(mode, i, jb, n_causal, tree_row=0):
 
 
 def _tree_rows(tree, bs, B):
-    """Per-request row masks [bs][B] (Python ints) from a [B] shared or
-    [bs, B] per-request array of uint64 masks (or None)."""
+    """Per-request row masks [bs][B] (Python ints of B bits) from uint64 mask
+    words: [B] (one tree, one word per row), [bs, B] (one tree per request),
+    or, for blocks of any size, [bs, B, W] / [1, B, W] with W = ceil(B / 64)
+    words per row, word w holding bits 64 w .. 64 w + 63 (or None)."""
     if tree is None:
         return [[0] * B for _ in range(bs)]
     t = np.asarray(tree, dtype=np.uint64)
     if t.ndim == 1:
         t = np.broadcast_to(t, (bs, B))
-    return [[int(x) for x in t[b]] for b in range(bs)]
+    if t.ndim == 2:
+        t = t[:, :, None]
+    t = np.broadcast_to(t, (bs, B, t.shape[-1]))
+    return [[sum(int(w) << (64 * k) for k, w in enumerate(t[b, i])) for i in range(B)]
+            for b in range(bs)]
 
 
 def unpage_kv(k_pool, v_pool, page_table_row, n_tokens, kvh):
@@ -94,7 +100,8 @@ def block_attn_rows(q, k_pool, v_pool, page_table, seq_lens, mode, n_causal, sca
     """Per-row loop form. q [bs, B, Hq, D] float64. Returns o [bs, B, Hq, D]
     and lse [bs, B, Hq]; with `rows` (an iterable of (b, i, h)) only those rows
     are computed and the rest stay NaN. `tree`: TREE-mode row masks, [B]
-    shared or [bs, B] per request."""
+    shared or [bs, B] per request (one word per row), or [bs or 1, B, W]
+    words per row for any block size."""
     bs, B, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     g = Hq // Hkv

@@ -475,3 +475,28 @@ def test_zero_threshold_is_not_a_tie():
     q = np.array([[0.0, 0.0, 0.25, 0.75]], np.float32)
     r = oracle.accept_request(p, q, np.array([3]), np.array([0.0, 0.0], np.float32), 0)
     assert r["accept_len"] == 1 and r["bonus"] == 0 and not r["tie"]
+
+
+def test_long_chain_tree_is_the_linear_accept():
+    """The same identity for chains longer than one 64-bit mask word (up to
+    200 nodes), with targets peaked at the drafts so that deep acceptance
+    happens: the tree walk has no node limit of its own."""
+    rng = np.random.default_rng(71)
+    deepest = 0
+    for trial in range(20):
+        K, V = int(rng.integers(65, 200)), 7
+        parent = np.arange(-1, K, dtype=np.int64)
+        token = np.concatenate([[0], rng.integers(0, V, size=K)])
+        p = np.stack([_dist(rng, V, floor=0.001) for _ in range(K + 1)])
+        p[np.arange(K), token[1:]] += 40.0           # mostly accepted
+        p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+        u = rng.random(K + 1).astype(np.float32)
+        q = np.zeros((K, V), np.float32)
+        q[np.arange(K), token[1:]] = 1.0
+        lin = oracle.accept_request(p, q, token[1:], np.concatenate([u[1:], u[:1]]), 5)
+        tr = oracle.tree_accept_request(parent, token, p, u, 5)
+        for key in ("accept_len", "commit_len", "bonus", "new_seq_len", "err"):
+            assert lin[key] == tr[key], (trial, key)
+        assert np.array_equal(lin["out_tokens"], tr["out_tokens"])
+        deepest = max(deepest, tr["accept_len"])
+    assert deepest > 64

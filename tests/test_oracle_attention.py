@@ -235,16 +235,21 @@ def test_tree_mode_chain_and_full_masks_reduce_to_causal_and_bidir():
         assert np.max(np.abs(o_t - o_m)) < 1e-12 and np.max(np.abs(l_t - l_m)) < 1e-12
 
 
-def test_tree_node_equals_causal_attention_over_its_root_path():
+@pytest.mark.parametrize("block,depth,hq,page", [(9, 6, 4, 4), (80, 12, 2, 16), (150, 20, 2, 16)])
+def test_tree_node_equals_causal_attention_over_its_root_path(block, depth, hq, page):
     """Defining property of tree attention: node n's output equals ordinary
     causal attention of the last row of a block laid out as the node's root
     path (ancestors in order, then n) after the same context. The path block
     is built as a separate paged cache, so this does not go through the tree
-    mask at all."""
-    x = tiny(bs=2, hq=4, hkv=2, d=16, page=4, block=9, ctx=(2, 10), seed=22)
+    mask at all. Blocks of 80 and 150 nodes take their masks as two and three
+    64-bit words per row."""
+    x = tiny(bs=2, hq=hq, hkv=2 if hq >= 2 else 1, d=16, page=page, block=block, ctx=(2, 10),
+             seed=22)
     cfg = x.cfg
     B, P = cfg.block, cfg.page
-    par, masks = synth.make_trees(dataclasses_replace(cfg, tree_depth=6), 3)
+    par, masks = synth.make_trees(dataclasses_replace(cfg, tree_depth=depth), 3)
+    if B > 64:
+        assert masks.shape == (cfg.bs, B, (B + 63) // 64)
     q64, k64, v64 = x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool")
     o_t, l_t = oracle.block_attn_rows(q64, k64, v64, x.page_table, x.seq_lens, oracle.TREE, 0,
                                       tree=masks)
@@ -363,3 +368,48 @@ def test_quadratic_layout_shape_and_limits():
     assert int(masks[6]) == 1 | 16 | (7 << 5)
     with pytest.raises(ValueError):
         synth.quadratic_layout(8)
+
+
+def test_mask_words_agree_with_one_word_rows_and_wide_chains_are_causal():
+    """Up to 64 nodes the word layout [bs, B, 1] is the one-word layout; past
+    64 nodes a chain tree in words is the causal triangle and all-ones words
+    the rectangle (B = 70 and 129: the second and third words carry the last
+    rows' bits)."""
+    x = tiny(seed=24, block=40, ctx=(0, 9))
+    par, masks = synth.make_trees(dataclasses_replace(x.cfg, tree_depth=10), 5)
+    words = np.stack([synth.tree_row_words(p) for p in par])
+    assert words.shape == (x.cfg.bs, 40, 1) and np.array_equal(words[:, :, 0], masks)
+    args = (x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"), x.page_table, x.seq_lens,
+            oracle.TREE, 0)
+    o1, _ = oracle.block_attn_dense(*args, tree=masks)
+    o2, _ = oracle.block_attn_dense(*args, tree=words)
+    assert np.max(np.abs(o1 - o2)) == 0.0
+    for B in (70, 129):
+        xw = tiny(seed=25, hq=2, hkv=1, d=8, page=16, block=B, ctx=(0, 20))
+        chain = synth.tree_row_words(np.arange(-1, B - 1, dtype=np.int32))[None]
+        W = (B + 63) // 64
+        full = np.zeros((1, B, W), dtype=np.uint64)
+        for w in range(W):
+            nb = min(64, B - 64 * w)
+            full[:, :, w] = np.uint64((1 << nb) - 1)
+        a = (xw.as_f64("q"), xw.as_f64("k_pool"), xw.as_f64("v_pool"), xw.page_table,
+             xw.seq_lens)
+        for tree, mode in ((chain, CAUSAL), (full, BIDIR)):
+            o_t, l_t = oracle.block_attn_dense(*a, oracle.TREE, 0, tree=tree)
+            o_m, l_m = oracle.block_attn_dense(*a, mode, 0)
+            assert np.max(np.abs(o_t - o_m)) < 1e-12 and np.max(np.abs(l_t - l_m)) < 1e-12
+
+
+def test_planted_bit_in_a_later_word_matters():
+    """Clearing one ancestor bit held in the second word of a row changes that
+    node's rows only."""
+    x = tiny(bs=1, seed=26, hq=2, hkv=1, d=8, page=16, block=100, ctx=(5, 6))
+    par = np.arange(-1, 99, dtype=np.int32)          # a chain: node n sees 0 .. n
+    words = synth.tree_row_words(par)[None].copy()
+    args = (x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"), x.page_table, x.seq_lens,
+            oracle.TREE, 0)
+    o1, _ = oracle.block_attn_dense(*args, tree=words)
+    words[0, 90, 1] &= ~np.uint64(1 << (70 - 64))   # row 90 loses ancestor 70
+    o2, _ = oracle.block_attn_dense(*args, tree=words)
+    diff = np.abs(o2 - o1).max(axis=(2, 3))[0]
+    assert diff[90] > 1e-6 and np.delete(diff, 90).max() == 0.0

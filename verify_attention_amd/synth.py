@@ -276,14 +276,28 @@ def random_tree_parents(rng, n_nodes: int, max_depth: int) -> np.ndarray:
 
 
 def tree_row_masks(parent: np.ndarray) -> np.ndarray:
-    """uint64 row masks of a tree in topological order: bit j of row n is set
-    iff node j is node n or one of its ancestors."""
-    m = np.zeros(len(parent), dtype=np.uint64)
-    for n in range(len(parent)):
-        m[n] = np.uint64(1) << np.uint64(n)
+    """uint64 row masks of a tree of at most 64 nodes in topological order:
+    bit j of row n is set iff node j is node n or one of its ancestors."""
+    if len(parent) > 64:
+        raise ValueError("one word per row holds at most 64 nodes; use tree_row_words")
+    return tree_row_words(parent)[:, 0].copy()
+
+
+def tree_row_words(parent: np.ndarray) -> np.ndarray:
+    """The same row masks for a tree of any size as W = ceil(N / 64) uint64
+    words per row, [N, W]: bit j of the mask is bit j % 64 of word j // 64."""
+    n_nodes = len(parent)
+    W = (n_nodes + 63) // 64
+    rows = [0] * n_nodes
+    for n in range(n_nodes):
+        rows[n] = 1 << n
         if parent[n] >= 0:
-            m[n] |= m[parent[n]]
-    return m
+            rows[n] |= rows[parent[n]]
+    out = np.zeros((n_nodes, W), dtype=np.uint64)
+    for n in range(n_nodes):
+        for w in range(W):
+            out[n, w] = np.uint64((rows[n] >> (64 * w)) & ((1 << 64) - 1))
+    return out
 
 
 def quadratic_layout(k: int):
@@ -330,14 +344,18 @@ def quadratic_parents(k: int) -> np.ndarray:
 
 def make_trees(cfg: RoundConfig, seed: int, per_request=True):
     """Token trees for a TREE round: parents [bs, B] and row masks [bs, B]
-    (per_request), or one tree shared by the batch ([B] each)."""
+    (per_request), or one tree shared by the batch ([B] each). Blocks of more
+    than 64 nodes get their masks as words: [bs, B, W] (or [1, B, W] for one
+    shared tree)."""
     r = rng_for(seed, "tree")
     depth = cfg.tree_depth or cfg.block
+    wide = cfg.block > 64
+    masks = tree_row_words if wide else tree_row_masks
     if not per_request:
         par = random_tree_parents(r, cfg.block, depth)
-        return par, tree_row_masks(par)
+        return par, (masks(par)[None] if wide else masks(par))
     par = np.stack([random_tree_parents(r, cfg.block, depth) for _ in range(cfg.bs)])
-    return par, np.stack([tree_row_masks(p) for p in par])
+    return par, np.stack([masks(p) for p in par])
 
 
 # --------------------------------------------------------------- accept step
