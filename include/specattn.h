@@ -210,17 +210,18 @@ int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req, int dtyp
  * Discrete Diffusion" (method steps: candidate prefixes verified in parallel
  * with tree attention): the B block tokens are tree nodes, and a node must see
  * the context and its own root path only. Row i's visibility over the block
- * is a bitmask: block key j' (0 <= j' < B) is visible to block row i iff bit
- * j' of tree_mask[i] (shared tree) or tree_mask[b * B + i] (one tree per
- * request) is set; context keys are always visible. Callers set, for node i,
- * the bits of node i and of its ancestors; a row whose mask and context are
- * both empty has no defined output.
+ * is a bitmask of W = ceil(B / 64) uint64 words: block key j' (0 <= j' < B)
+ * is visible to block row i iff bit j' % 64 of word j' / 64 of row i is set,
+ * the row being tree_mask[i * W ..] (shared tree) or tree_mask[(b * B + i) *
+ * W ..] (one tree per request); context keys are always visible. Callers
+ * set, for node i, the bits of node i and of its ancestors; a row whose mask
+ * and context are both empty has no defined output.
  *
- *   tree_mask         uint64 row masks (device): [B] when tree_per_request
- *                     is 0, else [bs, B]; B <= 64
- *   other arguments, outputs, workspace (block_attn_workspace_bytes) and
- *   errors as for block_attn; SPEC_EINVAL also for tree_mask == NULL or
- *   B > 64.
+ *   tree_mask         uint64 row masks (device): [B, W] when tree_per_request
+ *                     is 0, else [bs, B, W]; B <= 512 (W = 1 for B <= 64)
+ *   other arguments, outputs, workspace (block_attn_workspace_bytes, which
+ *   for B > 64 covers the schedule these trees take) and errors as for
+ *   block_attn; SPEC_EINVAL also for tree_mask == NULL or B > 512.
  */
 int block_attn_tree(const uint64_t* tree_mask, int tree_per_request, int dtype, int bs, int B,
                     int Hq, int Hkv, int D, int page_size, int max_pages, int num_pages,

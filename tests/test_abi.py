@@ -97,12 +97,19 @@ def test_block_attn_tree_rejects_bad_arguments(lib):
                                    a["q"], a["k"], a["v"], a["tab"], a["seq"], a["scale"], a["o"],
                                    a["lse"], a["ws"], a["ws_bytes"], a["err"], None)
     assert tree(tm=None) == b.SPEC_EINVAL
-    assert tree(B=65, hq=2, hkv=2) == b.SPEC_EINVAL       # more nodes than mask bits
+    assert tree(B=513, hq=2, hkv=2) == b.SPEC_EINVAL      # more nodes than 8 mask words
     assert tree(B=64, hq=64, hkv=1) == b.SPEC_EINVAL      # g * B = 4096 > 2048
     assert tree(d=96) == b.SPEC_ENOTSUP
     assert tree(q=None) == b.SPEC_EINVAL
     # the mode argument of block_attn itself does not take TREE (no mask pointer)
     assert _attn(lib, mode=3) == b.SPEC_EINVAL
+
+
+def test_block_attn_workspace_covers_wide_trees(lib):
+    # a block of more than 64 nodes takes the split schedule even where the
+    # balanced one would run: the size covers both
+    for bs, B in ((256, 80), (2, 150), (64, 481)):
+        assert lib.block_attn_workspace_bytes(bs, B, 32, 8, 128, 8192) > 0
 
 
 def test_block_attn_workspace_planning(lib):

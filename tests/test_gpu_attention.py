@@ -208,7 +208,9 @@ def test_balanced_schedule_all_rows(gpu_lib, name, cid, over, mode, nc_req):
 
 def run_tree(case, masks, max_kv=None):
     x = case.x
-    tm = torch.from_numpy(masks.view(np.int64)).to("cuda")
+    if masks.ndim == 3 and masks.shape[0] == 1 and x.cfg.bs > 1:
+        masks = masks[0]     # one shared tree of mask words: [B, W]
+    tm = torch.from_numpy(np.ascontiguousarray(masks).view(np.int64)).to("cuda")
     lse = torch.empty((x.cfg.bs, x.cfg.block, x.cfg.hq), dtype=torch.float32, device="cuda")
     o = va.block_attn_tree(tm, case.q, case.k, case.v, case.table, case.seq,
                            max_kv or case.max_kv, lse=lse)
@@ -224,6 +226,17 @@ TREES = [
     ("b16_g4_f32_d64", 6, dict(bs=3, hq=8, hkv=2, d=64, block=16, tree_depth=8, dtype="f32",
                                ctx_lo=40, ctx_hi=500), True),
     ("b32_p32_balanced", 6, dict(bs=128, hq=8, hkv=2, page=32, ctx_lo=1, ctx_hi=4200), True),
+    # more than 64 nodes: W = ceil(B / 64) mask words per row, staged in LDS
+    ("b80_g4_d128_rowgroups", 6, dict(bs=3, block=80, tree_depth=20, ctx_lo=50, ctx_hi=700),
+     True),
+    ("b150_g2_d64_shared", 6, dict(bs=3, hq=4, hkv=2, d=64, block=150, tree_depth=40, ctx_lo=0,
+                                   ctx_hi=500), False),
+    ("b200_g1_p32", 6, dict(bs=2, hq=2, hkv=2, page=32, block=200, tree_depth=30, ctx_lo=1,
+                            ctx_hi=400), True),
+    ("b100_f32_d128_two_tiles", 6, dict(bs=2, hq=8, hkv=2, block=100, tree_depth=16,
+                                        dtype="f32", ctx_lo=20, ctx_hi=300), True),
+    ("b512_g4_max", 6, dict(bs=2, hq=8, hkv=2, block=512, tree_depth=16, ctx_lo=0, ctx_hi=200),
+     True),
 ]
 
 
@@ -248,6 +261,19 @@ def test_tree_chain_is_bitwise_causal(gpu_lib):
     x = synth.make_attn_inputs(cfg, seed=32)
     case = AttnCase(x)
     chain = synth.tree_row_masks(np.arange(-1, cfg.block - 1, dtype=np.int32))
+    o_t, l_t = run_tree(case, chain)
+    o_c, l_c = run(case, synth.CAUSAL)
+    assert np.array_equal(o_t, o_c) and np.array_equal(l_t, l_c)
+
+
+def test_wide_chain_tree_is_bitwise_causal(gpu_lib):
+    """A chain of 150 nodes (three mask words per row, read from LDS) gives
+    the causal mask's outputs bit for bit; both take the split schedule."""
+    cfg = synth.config(2, bs=2, hq=8, hkv=2, block=150, ctx_lo=100, ctx_hi=600)
+    print_case("block_attn_tree wide chain", cfg)
+    x = synth.make_attn_inputs(cfg, seed=34)
+    case = AttnCase(x)
+    chain = synth.tree_row_words(np.arange(-1, cfg.block - 1, dtype=np.int32))
     o_t, l_t = run_tree(case, chain)
     o_c, l_c = run(case, synth.CAUSAL)
     assert np.array_equal(o_t, o_c) and np.array_equal(l_t, l_c)

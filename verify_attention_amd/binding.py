@@ -380,8 +380,9 @@ def block_attn_call(mode, q, k_pool, v_pool, page_table, seq_lens, max_kv_len, n
 def block_attn_tree_call(tree_mask, q, k_pool, v_pool, page_table, seq_lens, max_kv_len,
                          sm_scale=0.0, out=None, lse=None, ws=None, err=None, stream=None):
     """Checks the arguments of block_attn_tree once and returns (enqueue, out).
-    tree_mask: int64 tensor of uint64 row bit patterns, [B] (one tree for the
-    batch) or [bs, B] (one tree per request)."""
+    tree_mask: int64 tensor of uint64 row bit patterns, W = ceil(B / 64) words
+    per row: [B, W] (one tree for the batch) or [bs, B, W] (one tree per
+    request); for B <= 64 also [B] or [bs, B]."""
     torch = _torch()
     bs, B, hq, d = q.shape
     num_pages, hkv, P, d2 = k_pool.shape
@@ -395,9 +396,14 @@ def block_attn_tree_call(tree_mask, q, k_pool, v_pool, page_table, seq_lens, max
     _need(seq_lens, "seq_lens", torch.int32, (bs,))
     _need_err(err)
     _need(tree_mask, "tree_mask", torch.int64)
-    if tuple(tree_mask.shape) not in ((B,), (bs, B)):
-        raise ValueError(f"tree_mask must have shape ({B},) or ({bs}, {B})")
-    per_request = tree_mask.dim() == 2
+    W = (B + 63) // 64
+    shapes = {(B, W): False, (bs, B, W): True}
+    if W == 1:
+        shapes.update({(B,): False, (bs, B): True})
+    if tuple(tree_mask.shape) not in shapes:
+        raise ValueError(f"tree_mask must have shape ({B}, {W}) or ({bs}, {B}, {W})"
+                         + (f", ({B},) or ({bs}, {B})" if W == 1 else ""))
+    per_request = shapes[tuple(tree_mask.shape)]
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, q.shape)

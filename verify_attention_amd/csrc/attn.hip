@@ -458,6 +458,17 @@ struct WaveState {
   uint64_t tmask[MT];  // TREE mode: the row's visibility bits over the block keys
 };
 
+// TREE blocks of more than 64 nodes: each row's visibility over the block is
+// W = ceil(B / 64) words, staged in LDS for the block rows of the workgroup's
+// row group (block rows ibase .. ilast), word w of row i at rows[(i - ibase)
+// * W + w].
+constexpr int kMaxTreeWords = 8;                            // B <= 512
+constexpr int kWideMaskWords = (128 + 1) * kMaxTreeWords;   // row group rows + 1
+struct WideMask {
+  const uint64_t* rows;
+  int ibase, ilast, W;
+};
+
 // A stage is consumed in two halves so that the two waves sharing a SIMD can
 // run them out of phase:
 //   front: read the stage's K and V fragments from the ring, S^T = K Q^T;
@@ -500,9 +511,10 @@ __device__ __forceinline__ void stage_front(StageRegs<T, D, MT>& st, const WaveS
   st.key0 = key0;
 }
 
-template <typename T, int D, int MT>
+template <typename T, int D, int MT, bool WIDE = false>
 __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T, D, MT>& ws,
-                                           const AttnArgs& a, int L, int n_keys, int nc, int grp) {
+                                           const AttnArgs& a, int L, int n_keys, int nc, int grp,
+                                           const WideMask& wm) {
   using SS = StageShape<T, D>;
   const int key0 = st.key0;
   // two row tiles: the front left its V reads in flight (they overlap the
@@ -522,8 +534,17 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
         for (int j = 0; j < 4; ++j) {
           const int key = key0 + 8 * grp + 4 * t2 + j;
           const int jb = key - L, i = ws.blk_row[t];
-          const bool intra = a.mode == 3 ? ((ws.tmask[t] >> (jb & 63)) & 1) != 0
-                                         : (a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc));
+          bool intra;
+          if constexpr (WIDE) {
+            // LDS words of the row (rows past the group's end read a neighbour:
+            // their outputs are never written); keys outside the block are
+            // context (always visible) or past the end (never visible)
+            const int ic = min(max(i, wm.ibase), wm.ilast) - wm.ibase;
+            intra = jb >= 0 && jb < a.B && ((wm.rows[ic * wm.W + (jb >> 6)] >> (jb & 63)) & 1);
+          } else {
+            intra = a.mode == 3 ? ((ws.tmask[t] >> (jb & 63)) & 1) != 0
+                                : (a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc));
+          }
           const bool vis = (key < L) | ((key < n_keys) & intra);
           st.s[t2][t][j] = vis ? st.s[t2][t][j] : -__builtin_inff();
         }
@@ -651,7 +672,8 @@ __device__ __forceinline__ void load_q(WaveState<T, D, MT>& ws, const AttnArgs& 
     ws.blk_row[t] = r / a.g;
     const int rr = in ? r : 0;
     const int ii = rr / a.g, hh = rr - ii * a.g;
-    ws.tmask[t] = a.mode == 3 ? a.tree[(a.tree_per_req ? (size_t)b * a.B : 0) + ii] : 0;
+    ws.tmask[t] = a.mode == 3 ? a.tree[((a.tree_per_req ? (size_t)b * a.B : 0) + ii) * a.tree_words]
+                              : 0;
     // a row past the group's end reads the head's first row: its scores stay
     // finite, its softmax state is its own and its output is never written
     const T* src = qg + ((size_t)(b * a.B + ii) * a.Hq + kvh * a.g + hh) * D + 8 * grp;
@@ -709,11 +731,12 @@ __device__ __forceinline__ int clamped_len(const AttnArgs& a, int b, bool flag) 
 // Streams stages [s_lo, s_hi) of unit (b, kvh), length L, through the ring
 // into this wave's softmax state. Thread tid stages the page offsets of
 // stage tid of each window (first window: the prefetched `first` entries).
-template <typename T, int D, int MT, bool STAGED = false>
+template <typename T, int D, int MT, bool STAGED = false, bool WIDE = false>
 __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const AttnArgs& a,
                                               const WaveCtx<T, D>& c, char* s_ring,
                                               uint64_t* s_pgoff, int b, int kvh, int row0, int L,
-                                              int nc, int s_lo, int s_hi, int2 first) {
+                                              int nc, int s_lo, int s_hi, int2 first,
+                                              const WideMask& wm = WideMask{}) {
   using SS = StageShape<T, D>;
   constexpr int NSP = SS::NSP;
   static_assert(kPageWin == kWave * kWaves, "one thread per staged stage");
@@ -775,20 +798,20 @@ __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const Att
       const bool more = u + NSP - 1 < npairs;
       if (more && (set == 0 || !has_rows)) issue(u + NSP - 1, po_next);
       if (has_rows) {
-        if (pending) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
+        if (pending) stage_back<T, D, MT, WIDE>(st, ws, a, L, n_keys, nc, c.grp, wm);
         pending = false;
         if (more && set == 1) issue(u + NSP - 1, po_next);
         const int t = 2 * u + set;
         if (t < ns) {
           const unsigned so = (u % NSP) * SS::PAIR;
           stage_front<T, D, MT>(st, ws, c.k_lane + so, c.v_lane + so, (w0 + t) * kStep);
-          if (set == 0) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
+          if (set == 0) stage_back<T, D, MT, WIDE>(st, ws, a, L, n_keys, nc, c.grp, wm);
           else pending = true;
         }
       }
       po_next = offsets(u + NSP);
     }
-    if (pending) stage_back<T, D, MT>(st, ws, a, L, n_keys, nc, c.grp);
+    if (pending) stage_back<T, D, MT, WIDE>(st, ws, a, L, n_keys, nc, c.grp, wm);
   }
 }
 
@@ -871,11 +894,12 @@ __device__ __forceinline__ int logical_block(const AttnArgs& a, int x, int n) {
   return (a.RG > 1 && n % 8 == 0) ? (x % 8) * (n / 8) + x / 8 : x;
 }
 
-template <typename T, int D, int MT>
+template <typename T, int D, int MT, bool WIDE = false>
 __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs a) {
   using SS = StageShape<T, D>;
   __shared__ __attribute__((aligned(1024))) char s_ring[SS::NSP * SS::PAIR];
   __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];  // (lo, hi) per stage
+  __shared__ uint64_t s_tm[WIDE ? kWideMaskWords : 1];
 
   const WaveCtx<T, D> c = wave_ctx<T, D>(a, s_ring);
   const int lb = logical_block(a, blockIdx.x, gridDim.x);
@@ -894,7 +918,20 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
   const int n_steps = (L + a.B + kStep - 1) / kStep;
   const int s_hi = (split == a.splits - 1) ? n_steps : min(n_steps, s_lo + a.steps_per_split);
   const int nc = causal_rows(a, b);
-  stream_stages<T, D, MT>(ws, a, c, s_ring, s_pgoff, b, kvh, u.row0, L, nc, s_lo, s_hi, first);
+  WideMask wm{s_tm, 0, 0, 1};
+  if constexpr (WIDE) {
+    // the row group's block rows' mask words into LDS (the streaming loop
+    // starts with a barrier, which publishes them)
+    wm.ibase = u.row0 / a.g;
+    wm.ilast = min(a.B - 1, (u.row0 + a.M - 1) / a.g);
+    wm.W = a.tree_words;
+    const int n = (wm.ilast - wm.ibase + 1) * wm.W;
+    const uint64_t* src =
+        a.tree + ((a.tree_per_req ? (size_t)b * a.B : 0) + wm.ibase) * (size_t)wm.W;
+    for (int e = c.tid; e < n; e += kWave * kWaves) s_tm[e] = src[e];
+  }
+  stream_stages<T, D, MT, false, WIDE>(ws, a, c, s_ring, s_pgoff, b, kvh, u.row0, L, nc, s_lo,
+                                       s_hi, first, wm);
   finish_unit<T, D, MT>(ws, a, c, s_ring, b, kvh, u.row0, a.splits == 1 ? -1 : lb, [] {});
 }
 
@@ -1196,10 +1233,16 @@ static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t str
     return hipGetLastError();
   }
   const dim3 grid(total_blocks);
-  if (a.M > 64)
+  if (a.tree_words > 1) {  // TREE blocks of more than 64 nodes
+    if (a.M > 64)
+      hipLaunchKernelGGL((block_attn_kernel<T, D, 2, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((block_attn_kernel<T, D, 1, true>), grid, block, 0, stream, a);
+  } else if (a.M > 64) {
     hipLaunchKernelGGL((block_attn_kernel<T, D, 2>), grid, block, 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL((block_attn_kernel<T, D, 1>), grid, block, 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL((block_attn_combine_kernel<T, D>), dim3(a.bs * a.Hv), dim3(256), 0, stream, a);

@@ -18,6 +18,7 @@ constexpr int kMaxSplits = 64;  // splits per unit (each keeps at least 8 stages
 constexpr int kMaxChunks = 256;
 constexpr int kMaxUnitRows = 128;   // query rows one workgroup holds (8 MFMA row tiles)
 constexpr int kMaxQueryRows = 2048; // g * B: at most 16 row groups
+constexpr int kMaxTreeNodes = 512;  // tree blocks: 8 mask words per row
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultCUs = 256;    // MI355X; used only if the device cannot be queried
 
@@ -67,7 +68,8 @@ constexpr long long kBalancedMinStages = 32768;
 // most kMaxUnitRows (equal sizes, rounded up to the 16-row MFMA tile); each
 // group streams the head's keys on its own. The balanced schedule keeps the
 // RG workgroups of a group team on one XCD so that they share the keys in L2.
-AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
+AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len,
+                   bool allow_balanced = true) {
   AttnPlan p;
   p.Mt = (Hq / Hkv) * B;
   p.RG = (p.Mt + kMaxUnitRows - 1) / kMaxUnitRows;
@@ -76,7 +78,8 @@ AttnPlan plan_attn(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   p.units = bs * Hkv * p.RG;
   const int max_steps = std::max(1, (max_kv_len + kStepKeys - 1) / kStepKeys);
   const int cus = device_cus();
-  p.balanced = bs <= kMaxBalancedBatch && (long long)p.units * max_steps >= kBalancedMinStages;
+  p.balanced = allow_balanced && bs <= kMaxBalancedBatch &&
+               (long long)p.units * max_steps >= kBalancedMinStages;
   if (p.balanced) {
     // G = teams x RG workgroups, a multiple of 8 * RG (one team per XCD slot)
     p.grid = p.RG == 1 ? cus : std::max(1, cus / (8 * p.RG)) * 8 * p.RG;
@@ -214,7 +217,10 @@ SPEC_API int spec_prepare_tree(int bs, int N, int page_size, int max_pages, int 
 
 SPEC_API size_t block_attn_workspace_bytes(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   if (bs <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || max_kv_len <= 0) return 0;
-  return plan_attn(bs, B, Hq, Hkv, D, max_kv_len).ws_bytes;
+  const size_t ws = plan_attn(bs, B, Hq, Hkv, D, max_kv_len).ws_bytes;
+  // tree blocks of more than 64 nodes always take the split schedule
+  if (B <= 64) return ws;
+  return std::max(ws, plan_attn(bs, B, Hq, Hkv, D, max_kv_len, false).ws_bytes);
 }
 
 namespace {
@@ -234,10 +240,11 @@ int attn_common(int mode, int n_causal, const int32_t* n_causal_per_req, const u
   if ((long long)max_pages * page_size < B) return SPEC_EINVAL;
   if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
   if (mode == SPEC_MIXED && !n_causal_per_req && (n_causal < 0 || n_causal > B)) return SPEC_EINVAL;
-  if (mode == SPEC_TREE && (!tree || B > 64)) return SPEC_EINVAL;
+  if (mode == SPEC_TREE && (!tree || B > kMaxTreeNodes)) return SPEC_EINVAL;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return SPEC_EINVAL;
   if (!(std::isfinite(sm_scale))) return SPEC_EINVAL;
-  const AttnPlan plan = plan_attn(bs, B, Hq, Hkv, D, max_kv_len);
+  const int tree_words = mode == SPEC_TREE ? (B + 63) / 64 : 1;
+  const AttnPlan plan = plan_attn(bs, B, Hq, Hkv, D, max_kv_len, tree_words == 1);
   if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes)) return SPEC_ENOSPC;
 
   AttnArgs a;
@@ -249,6 +256,7 @@ int attn_common(int mode, int n_causal, const int32_t* n_causal_per_req, const u
   a.nc_per_req = mode == SPEC_MIXED ? n_causal_per_req : nullptr;
   a.tree = mode == SPEC_TREE ? tree : nullptr;
   a.tree_per_req = tree_per_request ? 1 : 0;
+  a.tree_words = tree_words;
   a.o = o;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);

@@ -12,7 +12,8 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* seq_lens;
   const int32_t* nc_per_req;
-  const uint64_t* tree;  // TREE mode: row masks over the block keys, [B] or [bs][B]
+  const uint64_t* tree;  // TREE mode: row masks over the block keys, [B][W] or [bs][B][W]
+  int tree_words;        // W = ceil(B / 64) (1 for the other modes)
   void* o;
   float* lse;
   float* part_o;      // [slots][M][D] partial outputs (unnormalised): split or cut-unit pieces
