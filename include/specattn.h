@@ -126,7 +126,7 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
  *   cache_loc[b,n] = the slot of position L_b + n (node n's K/V go to the
  *   n-th slot after the committed prefix, as block_attn_tree reads them).
  *
- *   bs, N           requests and block nodes (1..64)
+ *   bs, N           requests and block nodes (1..512)
  *   page_size, max_pages, num_pages, mask_token_id, verified_id, seq_lens,
  *   page_table      as spec_prepare_block
  *   parent          [N] (parent_per_request == 0) or [bs, N]; parent[0] is not
@@ -136,7 +136,7 @@ int spec_prepare_block(int bs, int B, int page_size, int max_pages, int num_page
  *   not an earlier node, or that descends from one, gets position -1 and sets
  *   SPEC_ERR_TREE; missing slots give -1 with SPEC_ERR_SLOT, and L_b + N past
  *   the page-table row sets SPEC_ERR_CAPACITY.
- * Errors: SPEC_EINVAL for bs <= 0, N outside 1..64, page_size, max_pages or
+ * Errors: SPEC_EINVAL for bs <= 0, N outside 1..512, page_size, max_pages or
  *   num_pages <= 0, or a NULL required pointer.
  */
 int spec_prepare_tree(int bs, int N, int page_size, int max_pages, int num_pages,
@@ -462,7 +462,7 @@ int spec_accept_static(int bs, int K, int V, int greedy, const float* p, const f
  * Every emitted token is then distributed as the target's next-token
  * distribution at its position, as for the linear rule.
  *
- *   bs, N, V          requests, tree nodes per request (1..64), vocabulary
+ *   bs, N, V          requests, tree nodes per request (1..512), vocabulary
  *                     (<= 524288)
  *   parent [bs, N]    parent node; parent[b,0] = -1 (the root is the last
  *                     committed token); a node n >= 1 needs 0 <= parent < n
@@ -478,7 +478,7 @@ int spec_accept_static(int bs, int K, int V, int greedy, const float* p, const f
  *   bonus, commit_len = accept_len + 1, new_seq_lens = seq_lens + commit_len.
  * Workspace: spec_accept_tree_workspace_bytes(bs, N, V) bytes, 16-byte
  *   aligned, contents irrelevant; calls sharing it must be ordered.
- * Errors: SPEC_EINVAL (bs <= 0, N outside 1..64, V <= 0, NULL), SPEC_ENOSPC,
+ * Errors: SPEC_EINVAL (bs <= 0, N outside 1..512, V <= 0, NULL), SPEC_ENOSPC,
  *   SPEC_ENOTSUP (V > 524288).
  */
 size_t spec_accept_tree_workspace_bytes(int bs, int N, int V);
@@ -580,7 +580,7 @@ int spec_accept_logits(int bs, int K, int V, int dtype, float temperature, int t
  * The bonus token is not written: it becomes the next round's first block
  * token at position L + d + 1 = new_seq_lens[b].
  *
- *   dtype SPEC_F32 / SPEC_BF16; D 64 or 128; page_size 16 or 32; B 1..64
+ *   dtype SPEC_F32 / SPEC_BF16; D 64 or 128; page_size 16 or 32; B 1..512
  *   k_pool, v_pool, page_table as block_attn (updated in place)
  * Data errors (flagged, the request is left unchanged): L + B past the page
  *   table (SPEC_ERR_CAPACITY), d outside 0..B-1 or a path that is not

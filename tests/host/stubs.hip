@@ -21,6 +21,12 @@ hipError_t launch_block_attn(const AttnArgs& a, bool, int D, int total_blocks, h
   require((a.RG - 1) * a.M < a.Mt, "no empty row group");
   require(a.Hv == a.Hkv * a.RG, "Hv");
   require(D == 64 || D == 128, "D");
+  if (a.mode == 3) {
+    require(a.tree && a.tree_words == (a.B + 63) / 64 && a.tree_words <= 8, "tree mask words");
+    require(a.tree_words == 1 || !a.balanced, "wide trees take the split schedule");
+  } else {
+    require(a.tree_words == 1, "one mask word outside TREE mode");
+  }
   if (a.balanced) {
     require(a.G >= 1 && (a.RG == 1 || a.G % (8 * a.RG) == 0), "balanced grid of teams");
     require(a.part_o && a.part_ml, "balanced workspace");
@@ -36,7 +42,7 @@ hipError_t launch_prepare_block(const PrepareArgs& a, hipStream_t) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_prepare_tree(const PrepareTreeArgs& a, hipStream_t) {
-  require(a.bs > 0 && a.N >= 1 && a.N <= 64 && a.parent, "prepare_tree sizes");
+  require(a.bs > 0 && a.N >= 1 && a.N <= kMaxTreeNodes && a.parent, "prepare_tree sizes");
   return hipErrorInvalidValue;
 }
 hipError_t launch_quadratic_handoff(const HandoffArgs& h, bool, hipStream_t) {
@@ -88,7 +94,7 @@ hipError_t launch_accept_logits(const SampArgs& a, bool, hipStream_t) {
 }
 hipError_t scratch_on_current_device(void**, size_t*) { return hipErrorNoDevice; }
 hipError_t launch_commit_kv(const CommitArgs& a, bool, hipStream_t) {
-  require(a.B >= 1 && a.B <= 64, "commit block");
+  require(a.B >= 1 && a.B <= kMaxTreeNodes, "commit block");
   return hipErrorInvalidValue;
 }
 

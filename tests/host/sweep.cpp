@@ -27,7 +27,7 @@ int main() {
 
   // block attention: planner and host path over a grid of shapes
   const int bss[] = {1, 2, 7, 32, 64, 256, 1000, 2048, 3000};
-  const int Bs[] = {1, 8, 16, 25, 32, 64, 128, 256};
+  const int Bs[] = {1, 8, 16, 25, 32, 64, 128, 256, 481, 512};
   const int heads[][2] = {{32, 8}, {16, 4}, {64, 8}, {8, 8}, {24, 8}, {2, 1}};
   const int kvs[] = {1, 100, 1040, 9232, 65536, 1 << 20};
   for (int bs : bss)
@@ -43,11 +43,10 @@ int main() {
                               max_pages, 1 << 20, kv, F, F, F, I, I, 0.0f, F, nullptr, F, ws,
                               nullptr, nullptr),
                    want);
-            if (B <= 64)
-              EXPECT(block_attn_tree(M, 1, SPEC_F32, bs, B, hh[0], hh[1], D, 32, max_pages,
-                                     1 << 20, kv, F, F, F, I, I, 0.5f, F, nullptr,
-                                     F, ws, I, nullptr),
-                     want);
+            EXPECT(block_attn_tree(M, 1, SPEC_F32, bs, B, hh[0], hh[1], D, 32, max_pages,
+                                   1 << 20, kv, F, F, F, I, I, 0.5f, F, nullptr,
+                                   F, ws, I, nullptr),
+                   want);
             if (ws > 0)
               EXPECT(block_attn(SPEC_BIDIR, 0, nullptr, SPEC_BF16, bs, B, hh[0], hh[1], D, 16,
                                 max_pages, 1 << 20, kv, F, F, F, I, I, 0.0f, F, nullptr, F,
@@ -64,7 +63,7 @@ int main() {
   // prepare, argmax
   EXPECT(spec_prepare_block(32, 16, 16, 80, 300, 7, I, I, I, I, I, I, I, I, nullptr), SPEC_EHIP);
   EXPECT(spec_prepare_block(0, 16, 16, 80, 300, 7, I, I, I, I, I, I, I, I, nullptr), SPEC_EINVAL);
-  for (int N : {1, 5, 25, 64})
+  for (int N : {1, 5, 25, 64, 65, 481, 512})
     for (int per : {0, 1}) {
       EXPECT(spec_prepare_tree(32, N, 16, 80, 300, 7, I, I, I, I, per, I, I, I, I, I, nullptr),
              SPEC_EHIP);
@@ -72,7 +71,7 @@ int main() {
                                nullptr),
              SPEC_EHIP);
     }
-  EXPECT(spec_prepare_tree(32, 65, 16, 80, 300, 7, I, I, I, I, 0, I, I, I, I, I, nullptr),
+  EXPECT(spec_prepare_tree(32, 513, 16, 80, 300, 7, I, I, I, I, 0, I, I, I, I, I, nullptr),
          SPEC_EINVAL);
   EXPECT(spec_prepare_tree(32, 8, 16, 80, 300, 7, I, I, I, nullptr, 0, I, I, I, I, I, nullptr),
          SPEC_EINVAL);
@@ -160,6 +159,17 @@ int main() {
         EXPECT(spec_accept_tree(bs, N, V, I, I, FL, FL, I, I, I, I, I, I, I, F, wt - 1, I, nullptr),
                SPEC_ENOSPC);
       }
+  for (int bs : {1, 32})
+    for (int N : {65, 481, 512})
+      for (int V : {5, 151936}) {
+        const size_t wt = spec_accept_tree_workspace_bytes(bs, N, V);
+        EXPECT(spec_accept_tree(bs, N, V, I, I, FL, FL, I, I, I, I, I, I, I, F, wt, I, nullptr),
+               SPEC_EHIP);
+        EXPECT(spec_accept_tree(bs, N, V, I, I, FL, FL, I, I, I, I, I, I, I, F, wt - 1, I, nullptr),
+               SPEC_ENOSPC);
+      }
+  EXPECT(spec_accept_tree(4, 513, 512, I, I, FL, FL, I, I, I, I, I, I, I, F, 1 << 30, I, nullptr),
+         SPEC_EINVAL);
   EXPECT(spec_accept(4, 64, 512, 0, FL, FL, I, FL, I, I, I, I, I, I, F, 1 << 30, I, nullptr),
          SPEC_EINVAL);
 
@@ -180,10 +190,10 @@ int main() {
          SPEC_EINVAL);
 
   // commit
-  for (int B : {1, 8, 32, 64})
+  for (int B : {1, 8, 32, 64, 65, 481, 512})
     EXPECT(spec_commit_kv(SPEC_BF16, 32, B, 8, 128, 16, 80, 300, I, I, I, I, F, F, I, I, nullptr),
            SPEC_EHIP);
-  EXPECT(spec_commit_kv(SPEC_BF16, 32, 65, 8, 128, 16, 80, 300, I, I, I, I, F, F, I, I, nullptr),
+  EXPECT(spec_commit_kv(SPEC_BF16, 32, 513, 8, 128, 16, 80, 300, I, I, I, I, F, F, I, I, nullptr),
          SPEC_EINVAL);
 
   for (int st : {0, -1, -2, -3, -4, -5, -99}) (void)spec_status_string(st);

@@ -171,7 +171,7 @@ def test_accept_tree_rejects_bad_arguments(lib):
                                     a["nsl"], a["ws"], a["ws_bytes"], a["err"], None)
     assert acc(bs=0) == b.SPEC_EINVAL
     assert acc(N=0) == b.SPEC_EINVAL
-    assert acc(N=65) == b.SPEC_EINVAL
+    assert acc(N=513) == b.SPEC_EINVAL
     assert acc(par=None) == b.SPEC_EINVAL
     assert acc(path=None) == b.SPEC_EINVAL
     assert acc(V=524289) == b.SPEC_ENOTSUP
@@ -256,7 +256,7 @@ def test_commit_kv_rejects_bad_arguments(lib):
                                   a["v"], a["freed"], a["err"], None)
     assert com(bs=0) == b.SPEC_EINVAL
     assert com(B=0) == b.SPEC_EINVAL
-    assert com(B=65) == b.SPEC_EINVAL
+    assert com(B=513) == b.SPEC_EINVAL
     assert com(hkv=0) == b.SPEC_EINVAL
     assert com(seq=None) == b.SPEC_EINVAL
     assert com(freed=None) == b.SPEC_EINVAL
@@ -290,7 +290,7 @@ def test_accept_tree_commit_rejects_bad_arguments(lib):
     assert atc(k=None) == b.SPEC_EINVAL
     assert atc(freed=None) == b.SPEC_EINVAL
     # the accept's arguments
-    assert atc(N=65) == b.SPEC_EINVAL
+    assert atc(N=513) == b.SPEC_EINVAL
     assert atc(bs=0) == b.SPEC_EINVAL
     assert atc(par=None) == b.SPEC_EINVAL
     assert atc(V=600000) == b.SPEC_ENOTSUP

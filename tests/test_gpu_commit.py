@@ -83,6 +83,35 @@ def test_commit_small_shapes_and_overlapping_moves(dtype, d, page):
     check(x, depth, path, cfg.block)
 
 
+@pytest.mark.parametrize("cid,over", [
+    (10, dict(bs=3, vocab=64)),
+    (6, dict(bs=2, block=512, tree_depth=512, hq=8, hkv=2, d=64, dtype="f32", ctx_lo=3,
+             ctx_hi=300, page=32)),
+])
+def test_commit_wide_blocks(cid, over):
+    """Blocks of 481 and 512 nodes: the deepest first-child chains, every
+    other node (rows k <- 2k, more than one round of 64 rows), and random
+    increasing paths of up to 511 rows."""
+    cfg = synth.config(cid, **over)
+    print_case("commit wide", cid, cfg.block, cfg.dtype)
+    x = synth.make_attn_inputs(cfg, seed=4)
+    par, _ = synth.make_trees(cfg, 4)
+    B = cfg.block
+    depth, path = deepest_paths(par, B)
+    check(x, depth, path, B)
+    rng = np.random.default_rng(cid)
+    depth = np.zeros(cfg.bs, np.int32)
+    path = np.full((cfg.bs, B), -1, np.int32)
+    for b in range(cfg.bs):
+        if b == 0:
+            d, p = (B - 1) // 2, 2 * np.arange(1, (B - 1) // 2 + 1)
+        else:
+            d = int(rng.integers(65, B))
+            p = np.sort(rng.choice(np.arange(1, B), size=d, replace=False))
+        depth[b], path[b, :d] = d, p
+    check(x, depth, path, B)
+
+
 def test_commit_linear_verify_moves_nothing():
     cfg = synth.config(2, bs=8)
     print_case("commit linear")
@@ -133,7 +162,8 @@ def _host(t, bf16):
 
 @pytest.mark.parametrize("cid,over", [(6, {}), (6, dict(bs=5, block=12, hq=4, hkv=2, d=64, page=32,
                                                           dtype="f32", ctx_lo=17, ctx_hi=70,
-                                                          tree_depth=6, vocab=300))])
+                                                          tree_depth=6, vocab=300)),
+                                      (10, dict(bs=4, vocab=500))])
 def test_accept_tree_commit_equals_the_two_calls(cid, over):
     """spec_accept_tree_commit gives exactly the outputs, pools and released
     slots of spec_accept_tree followed by spec_commit_kv, and the pools equal

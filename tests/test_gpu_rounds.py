@@ -68,6 +68,11 @@ def _tree_case(cfg, seed, per_request=True, quad=False):
      True, False),
     ("quadratic_k4", 8, {}, False, True),
     ("quadratic_k7_per_request", 8, dict(bs=6, block=64, quad_k=7), True, True),
+    # more than 64 nodes: a workgroup per request, pointer jumping through LDS
+    ("tree_sampler_481", 10, dict(bs=4, vocab=64), True, False),
+    ("tree_65_shared", 6, dict(bs=5, block=65, tree_depth=64), False, False),
+    ("deep_512", 6, dict(bs=3, block=512, tree_depth=512, ctx_lo=1, ctx_hi=900, page=32),
+     True, False),
 ])
 def test_prepare_tree_matches_reference(gpu_lib, name, cid, over, per_req, quad):
     cfg = synth.config(cid, **over)
@@ -82,6 +87,26 @@ def test_prepare_tree_matches_reference(gpu_lib, name, cid, over, per_req, quad)
             assert np.array_equal(_np(g), r)
         assert ref[3] == 0
     assert int(err.item()) == 0
+
+
+def test_prepare_tree_wide_error_flags(gpu_lib):
+    """A 300-node block: a bad edge deep in the tree marks every descendant
+    (position -1, SPEC_ERR_TREE), as the reference does."""
+    print_case("prepare_tree wide errors")
+    rng = np.random.default_rng(3)
+    par = synth.random_tree_parents(rng, 300, 120)[None].repeat(2, 0)
+    par[1, 150] = 200                           # not an earlier node
+    seq = np.array([7, 100], np.int32)
+    table = np.arange(2 * 30, dtype=np.int32).reshape(2, 30)
+    verified = np.array([5, 6], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = va.prepare_tree(to_dev(verified), to_dev(seq), to_dev(table), 16, to_dev(par), 9, 60,
+                          err=err)
+    ref = oracle.prepare_tree(verified, seq, table, 16, par, 9, None, 60)
+    for g, r in zip(got, ref[:3]):
+        assert np.array_equal(_np(g), r)
+    assert (ref[1][1] == -1).sum() >= 1 and (ref[1][0] >= 0).all()
+    assert int(err.item()) == ref[3] == va.ERR_TREE
 
 
 def test_prepare_tree_error_flags(gpu_lib):

@@ -150,3 +150,60 @@ def test_chain_tree_matches_the_linear_accept(gpu_lib):
     assert (ref["accept_len"][:8] == K).all() and (ref["accept_len"][8:] < K).all()
     assert (ref["accept_len"][8:] > 0).any()
 
+
+
+@pytest.mark.parametrize("name,over,seed", [
+    ("tree_sampler_481_v2000", dict(bs=24, vocab=2000), 5),
+    ("tree_sampler_481_v4099_flat", dict(bs=16, vocab=4099, logit_sigma=2.0), 6),
+])
+def test_tree_sampler_shape_accept(gpu_lib, name, over, seed):
+    """The Tree sampler's (16, 32, 32) tree (481 nodes in chunks of 64 per
+    lane, the children of a node spread over several chunks) against the
+    reference walk."""
+    cfg = synth.config(10, **over)
+    print_case("spec_accept_tree tree sampler", name, cfg.bs, cfg.vocab)
+    par, _ = synth.make_trees(cfg, seed)
+    ti = synth.make_tree_accept_inputs(cfg, seed, par)
+    seq = np.random.default_rng(seed).integers(0, 5000, size=cfg.bs).astype(np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = run_tree_accept(ti, seq, err=err)
+    assert int(err.item()) == 0
+    compare(ti, seq, got)
+    assert got["accept_len"].max() >= 1
+
+
+@pytest.mark.parametrize("N", [65, 200, 512])
+def test_wide_chain_tree_matches_the_reference(gpu_lib, N):
+    """Chains of up to 512 nodes (walks across every 64-node chunk) with
+    test uniforms small enough that most requests accept deep, and siblings
+    placed in other chunks than their first brother: node 1's children are
+    nodes 2 and N - 1 (a repeat of node 2's token and a fresh one)."""
+    rng = np.random.default_rng(N)
+    bs, V = 12, 300
+    print_case("spec_accept_tree wide chain", N)
+    parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (bs, 1))
+    parent[:, N - 1] = 1
+    lg = rng.standard_normal((bs, N, V)) * 4.0
+    p = np.exp(lg - lg.max(-1, keepdims=True))
+    p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+    token = p.argmax(-1).astype(np.int32)
+    token = np.concatenate([np.zeros((bs, 1), np.int32), token[:, :-1]], axis=1)  # child of n: argmax p_n
+    token[:, N - 1] = token[:, 2]
+    token[6:, N - 1] = np.argsort(-p[6:, 1], axis=-1, kind="stable")[:, 1]   # p_1's second best
+    u = (rng.random((bs, N), dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
+    u[:, 0] = rng.random(bs, dtype=np.float32)
+    u[3:6, 5 + (N // 3)] = np.float32(0.9999)     # an early stop at different depths
+    u[0:2, 2] = u[6:9, 2] = np.float32(0.9999)    # node 2 rejected: its sibling N - 1 is tried
+    u[6:9, N - 1] = 0.0
+    tokdirty = token.copy()
+    tokdirty[9, 7] = V + 5                          # an invalid token: a reject, flagged
+    u[9, 1:7] = 0.0                                 # (reached: nodes 1..6 are accepted)
+    ti = synth.TreeAcceptInputs(parent, tokdirty, p, u)
+    seq = rng.integers(0, 900, size=bs).astype(np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = run_tree_accept(ti, seq, err=err)
+    compare(ti, seq, got)
+    assert int(err.item()) & va.ERR_TOKEN
+    assert got["accept_len"].max() == N - 2        # the whole chain below node 1
+    assert (got["accept_len"][0:2] == 1).all()          # the sibling repeats node 2's token
+    assert (got["path_nodes"][6:9, 1] == N - 1).all()   # the fresh sibling is accepted

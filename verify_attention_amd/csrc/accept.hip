@@ -25,6 +25,7 @@
 namespace specattn {
 
 constexpr int kAccThreads = 256;
+static_assert(kAccThreads == kCommitThreads, "the accept kernels run the commit helpers");
 constexpr int kJTokenErr = 1 << 16;  // jbuf flag: the first reject was an invalid token id
 
 constexpr int kSub = 256;  // vocabulary entries per sub-block (one wave, 4 per lane)
@@ -410,84 +411,130 @@ __global__ __launch_bounds__(kAccThreads) void accept_select_kernel(AcceptArgs a
 // next node; with none (or at a leaf) the bonus is drawn from p_x with the
 // tried tokens set to 0.
 //
-// One wave, lane n = node n (N <= 64). Every value a test may need,
-// p[parent(n)][token(n)], is gathered in one round before the walk, so the
-// walk itself is register work: the children of x are a ballot, T an
-// exclusive wave scan of their target masses, the accepted child the lowest
-// set bit of a second ballot.
+// One wave; lane l holds nodes l, l + 64, ... (chunks of 64 nodes, N <= 512).
+// Every value a test may need, p[parent(n)][token(n)], is gathered in one
+// round before the walk, so the walk itself is register work: per chunk the
+// children of x are a ballot, T the mass of earlier chunks plus an exclusive
+// wave scan, the accepted child the lowest set bit of a second ballot; the
+// tokens of children in earlier chunks sit in LDS for the repeat test.
+constexpr int kTreeChunks = kMaxTreeNodes / 64;
+
 struct TreeWalk {
   int x;          // final node
   int depth;      // accepted nodes
   int errs;       // kErrToken / kErrTree
 };
 
-constexpr int kJTreeTokErr = 1 << 16;
-constexpr int kJTreeErr = 1 << 17;
+// jbuf of a tree request: final node | depth << 10 | error bits
+constexpr int kJTreeDepthShift = 10;
+constexpr int kJTreeMask = (1 << kJTreeDepthShift) - 1;
+constexpr int kJTreeTokErr = 1 << 20;
+constexpr int kJTreeErr = 1 << 21;
+static_assert(kMaxTreeNodes <= kJTreeMask + 1, "node ids fit the jbuf fields");
 
 __device__ __forceinline__ double wave_exclusive_scan(double x) {
   return wave_inclusive_scan(x) - x;
 }
 
-// Lane n's node: parent and token (loaded once, shared by the walk and the
-// excluded set).
-struct TreeNode {
-  int par, tok;
+// Lane l's nodes l + 64 c: parent and token (loaded once, shared by the walk
+// and the excluded set).
+struct TreeNodes {
+  int par[kTreeChunks], tok[kTreeChunks];
 };
 
-__device__ __forceinline__ TreeNode tree_node(const AcceptArgs& a, int b) {
-  const int N = a.K, n = threadIdx.x & 63;
-  const bool in = n < N;
-  return TreeNode{in ? a.parent[(size_t)b * N + n] : -2, in ? a.token[(size_t)b * N + n] : -1};
+__device__ __forceinline__ TreeNodes tree_nodes(const AcceptArgs& a, int b) {
+  const int N = a.K, lane = threadIdx.x & 63;
+  TreeNodes t;
+#pragma unroll
+  for (int c = 0; c < kTreeChunks; ++c) {
+    const int n = c * 64 + lane;
+    const bool in = n < N;
+    t.par[c] = in ? a.parent[(size_t)b * N + n] : -2;
+    t.tok[c] = in ? a.token[(size_t)b * N + n] : -1;
+  }
+  return t;
 }
 
-// Wave 0 only. path[] (LDS) receives the accepted node ids.
-__device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNode& nd, int* path) {
+// Wave 0 only. path[] (LDS) receives the accepted node ids; sib[] (LDS, N
+// entries) is scratch for the tokens of the children already tried.
+__device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes& nd, int* path,
+                              int* sib) {
   const int N = a.K, V = a.V;
-  const int n = threadIdx.x & 63;
-  const bool in = n < N;
-  const int par = nd.par, tok = nd.tok;
-  const double un = in ? (double)a.u[(size_t)b * N + n] : 0.0;
-  const bool vpar = in && n >= 1 && par >= 0 && par < n;
-  const bool vtok = tok >= 0 && tok < V;
-  const double pv = (vpar && vtok) ? (double)a.p[((size_t)b * N + par) * V + tok] : 0.0;
+  const int lane = threadIdx.x & 63, nch = (N + 63) >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  double un[kTreeChunks], pv[kTreeChunks];
+  bool vpar[kTreeChunks], vtok[kTreeChunks];
   TreeWalk w{0, 0, 0};
-  if (__builtin_amdgcn_ballot_w64(in && n >= 1 && !vpar)) w.errs |= kErrTree;
-  for (int level = 0; level < 64; ++level) {
-    const bool kid = vpar && par == w.x;
-    const uint64_t kids = __builtin_amdgcn_ballot_w64(kid);
-    if (!kids) break;
-    // a child repeating an earlier sibling's token has residual 0
-    bool dup = false;
-    for (uint64_t rest = kids; rest; rest &= rest - 1) {
-      const int k = __builtin_ctzll(rest);
-      const int tk = __builtin_amdgcn_readlane(tok, k);  // k is wave-uniform
-      dup |= kid && n > k && tk == tok;
+#pragma unroll
+  for (int c = 0; c < kTreeChunks; ++c) {
+    const int n = c * 64 + lane;
+    const bool in = n < N;
+    const int par = nd.par[c], tok = nd.tok[c];
+    un[c] = in ? (double)a.u[(size_t)b * N + n] : 0.0;
+    vpar[c] = in && n >= 1 && par >= 0 && par < n;
+    vtok[c] = tok >= 0 && tok < V;
+    pv[c] = (vpar[c] && vtok[c]) ? (double)a.p[((size_t)b * N + par) * V + tok] : 0.0;
+    if (__builtin_amdgcn_ballot_w64(in && n >= 1 && !vpar[c])) w.errs |= kErrTree;
+  }
+  for (int level = 0; level < N; ++level) {
+    double T0 = 0.0;  // mass of the distinct tokens tried in earlier chunks
+    int nsib = 0, next = -1;
+#pragma unroll
+    for (int c = 0; c < kTreeChunks; ++c) {
+      // children come after their parent: chunks before x's hold none
+      if (c >= nch || c < (w.x + 1) >> 6) continue;
+      const bool kid = vpar[c] && nd.par[c] == w.x;
+      const uint64_t kids = __builtin_amdgcn_ballot_w64(kid);
+      if (!kids) continue;
+      const int tok = nd.tok[c];
+      // a child repeating an earlier sibling's token has residual 0
+      bool dup = false;
+      for (uint64_t rest = kids; rest; rest &= rest - 1) {
+        const int k = __builtin_ctzll(rest);
+        const int tk = __builtin_amdgcn_readlane(tok, k);  // k is wave-uniform
+        dup |= kid && lane > k && tk == tok;
+      }
+      for (int i = 0; i < nsib; ++i) dup |= kid && sib[i] == tok;
+      const double pres = (kid && vtok[c] && !dup) ? pv[c] : 0.0;
+      const double incl = wave_inclusive_scan(pres);
+      const double T = T0 + (incl - pres);
+      const bool acc = kid && vtok[c] && !dup && un[c] * (1.0 - T) < pres;
+      const uint64_t accm = __builtin_amdgcn_ballot_w64(acc);
+      const int limit = accm ? __builtin_ctzll(accm) : 64;
+      if (__builtin_amdgcn_ballot_w64(kid && !vtok[c] && lane < limit)) w.errs |= kErrToken;
+      if (accm) {
+        next = c * 64 + limit;
+        break;
+      }
+      T0 += __shfl(incl, 63, 64);
+      if (kid) sib[nsib + __builtin_popcountll(kids & below)] = tok;
+      nsib += __builtin_popcountll(kids);
     }
-    const double pres = (kid && vtok && !dup) ? pv : 0.0;
-    const double T = wave_exclusive_scan(pres);
-    const bool acc = kid && vtok && !dup && un * (1.0 - T) < pres;
-    const uint64_t accm = __builtin_amdgcn_ballot_w64(acc);
-    const int limit = accm ? __builtin_ctzll(accm) : 64;
-    if (__builtin_amdgcn_ballot_w64(kid && !vtok && n < limit)) w.errs |= kErrToken;
-    if (!accm) break;
-    w.x = limit;
-    if (n == 0) path[w.depth] = limit;
+    if (next < 0) break;
+    w.x = next;
+    if (lane == 0) path[w.depth] = next;
     ++w.depth;
   }
   return w;
 }
 
-// The final node's children tokens (valid ids) into excl[]; returns the count.
-// Wave 0 only.
-__device__ int tree_excluded(const AcceptArgs& a, const TreeNode& nd, int x, int* excl) {
+// The final node's children tokens (valid ids) into excl[] in node order;
+// returns the count. Wave 0 only.
+__device__ int tree_excluded(const AcceptArgs& a, const TreeNodes& nd, int x, int* excl) {
   const int N = a.K, V = a.V;
-  const int n = threadIdx.x & 63;
-  const bool in = n < N;
-  const int par = nd.par, tok = nd.tok;
-  const bool ex = in && n >= 1 && par == x && par < n && tok >= 0 && tok < V;
-  const uint64_t m = __builtin_amdgcn_ballot_w64(ex);
-  if (ex) excl[__builtin_popcountll(m & ((1ull << n) - 1))] = tok;
-  return __builtin_popcountll(m);
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1;
+  int cnt = 0;
+#pragma unroll
+  for (int c = 0; c < kTreeChunks; ++c) {
+    const int n = c * 64 + lane;
+    const int par = nd.par[c], tok = nd.tok[c];
+    const bool ex = n < N && n >= 1 && par == x && par < n && tok >= 0 && tok < V;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ex);
+    if (ex) excl[cnt + __builtin_popcountll(m & below)] = tok;
+    cnt += __builtin_popcountll(m);
+  }
+  return cnt;
 }
 
 // Kernel 1, one workgroup per (request, vocabulary chunk): the walk, then
@@ -497,23 +544,24 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(Accept
   const int c = blockIdx.x - b * a.nchunk;
   const int N = a.K, V = a.V;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ int s_path[64], s_excl[64], s_fexcl[64];
+  __shared__ int s_path[kMaxTreeNodes], s_excl[kMaxTreeNodes], s_fexcl[kMaxTreeNodes];
+  __shared__ int s_sib[kMaxTreeNodes];
   __shared__ int s_x, s_nex, s_nf;
   if (wave == 0) {
-    const TreeNode nd = tree_node(a, b);
-    const TreeWalk w = tree_walk(a, b, nd, s_path);
+    const TreeNodes nd = tree_nodes(a, b);
+    const TreeWalk w = tree_walk(a, b, nd, s_path, s_sib);
     const int nex = tree_excluded(a, nd, w.x, s_excl);
     if (lane == 0) {
       s_x = w.x;
       s_nex = nex;
       if (c == 0)
-        a.jbuf[b] = w.x | (w.depth << 8) | ((w.errs & kErrToken) ? kJTreeTokErr : 0) |
+        a.jbuf[b] = w.x | (w.depth << kJTreeDepthShift) |
+                    ((w.errs & kErrToken) ? kJTreeTokErr : 0) |
                     ((w.errs & kErrTree) ? kJTreeErr : 0);
     }
-    // the accepted nodes with their tokens (node | token << 8) for the select
-    const int pn = lane < w.depth ? s_path[lane] : 0;
-    const int pt = __shfl(nd.tok, pn, 64);
-    if (c == 0 && lane < w.depth) a.pathbuf[(size_t)b * N + lane] = pn | (pt << 8);
+    // the accepted nodes for the select and the commit
+    if (c == 0)
+      for (int k = lane; k < w.depth; k += 64) a.pathbuf[(size_t)b * N + k] = s_path[k];
   }
   __syncthreads();
   const int nsb = (V + kSub - 1) / kSub;
@@ -547,7 +595,7 @@ __device__ void tree_select(const AcceptArgs& a, int b) {
   __shared__ double s_wave[4];
   __shared__ double s_dbl[2];
   __shared__ int s_int[2];
-  __shared__ int s_excl[64];
+  __shared__ int s_excl[kMaxTreeNodes];
   __shared__ int s_nex;
   const int nsb = (V + kSub - 1) / kSub;
   const int per = (nsb + kAccThreads - 1) / kAccThreads;
@@ -559,12 +607,9 @@ __device__ void tree_select(const AcceptArgs& a, int b) {
   const int L = a.seq_lens[b];
   const double ub = (double)a.u[(size_t)b * N];
   const int jw = a.jbuf[b];
-  const int x = jw & 0xff, depth = (jw >> 8) & 0xff;
-  const int pw = tid < depth ? a.pathbuf[(size_t)b * N + tid] : -1;
-  const int pnode = pw >= 0 ? (pw & 0xff) : -1;
-  const int ptok = pw >= 0 ? (int)((unsigned)pw >> 8) : -1;
+  const int x = jw & kJTreeMask, depth = (jw >> kJTreeDepthShift) & kJTreeMask;
   if (tid < 64) {
-    const int nex = tree_excluded(a, tree_node(a, b), x, s_excl);
+    const int nex = tree_excluded(a, tree_nodes(a, b), x, s_excl);
     if (tid == 0) s_nex = nex;
   }
   __syncthreads();
@@ -597,9 +642,11 @@ __device__ void tree_select(const AcceptArgs& a, int b) {
     a.bonus[b] = tok;
     a.new_seq_lens[b] = L + depth + 1;
   }
-  if (tid < N) {
-    a.path_nodes[(size_t)b * N + tid] = pnode;
-    a.out_tokens[(size_t)b * N + tid] = tid < depth ? ptok : (tid == depth ? tok : -1);
+  for (int t = tid; t < N; t += kAccThreads) {
+    const int node = t < depth ? a.pathbuf[(size_t)b * N + t] : -1;
+    a.path_nodes[(size_t)b * N + t] = node;
+    a.out_tokens[(size_t)b * N + t] =
+        t < depth ? a.token[(size_t)b * N + node] : (t == depth ? tok : -1);
   }
   if (tid == 0 && errs) flag_error(a.err, errs);
 }
@@ -610,28 +657,23 @@ __device__ void tree_select(const AcceptArgs& a, int b) {
 // table keeps its rows and releases nothing.
 template <typename KVT>
 __device__ void tree_commit_head(const AcceptArgs& a, int b, int h) {
-  __shared__ long long s_ksrc[64], s_kdst[64], s_vsrc[64], s_vdst[64];
+  SPEC_COMMIT_ROWS(rows);
   __shared__ int s_cerr;
-  const CommitRows rows{s_ksrc, s_kdst, s_vsrc, s_vdst};
   const int tid = threadIdx.x, N = a.K, P = a.commit_P;
   const int32_t* tab = a.commit_tab + (size_t)b * a.commit_max_pages;
   const int L = a.seq_lens[b];
   const bool cap_ok = L >= 0 && (long long)L + N <= (long long)a.commit_max_pages * P;
-  const int d = cap_ok ? (a.jbuf[b] >> 8) & 0xff : -1;
-  if (tid < 64) {
-    const int pw = tid < N ? a.pathbuf[(size_t)b * N + tid] : 0;  // lanes < d hold the path
-    const bool bad = commit_row_bases(rows, tab, P, a.commit_D, a.commit_Hkv, a.commit_num_pages,
-                                      h, L, d, pw & 0xff);
-    if (tid == 0) s_cerr = (cap_ok ? 0 : kErrCapacity) | (bad ? kErrSlot : 0);
-  }
-  __syncthreads();
+  const int d = cap_ok ? (a.jbuf[b] >> kJTreeDepthShift) & kJTreeMask : -1;
+  if (tid == 0) s_cerr = cap_ok ? 0 : kErrCapacity;  // published by the barrier below
+  const int32_t* path = a.pathbuf + (size_t)b * N;
+  bool bad = commit_row_bases(rows, [&](int k) { return path[k]; }, tab, P, a.commit_D,
+                              a.commit_Hkv, a.commit_num_pages, h, L, d);
   commit_move_rows<KVT>(rows, reinterpret_cast<KVT*>(a.commit_k),
                         reinterpret_cast<KVT*>(a.commit_v), P, a.commit_D, d);
-  if (h == 0) {
-    if (commit_freed(a.commit_freed + (size_t)b * N, tab, P, N, a.commit_num_pages, L, d))
-      atomicOr(&s_cerr, kErrSlot);
-    __syncthreads();
-  }
+  if (h == 0) bad |= commit_freed(a.commit_freed + (size_t)b * N, tab, P, N, a.commit_num_pages,
+                                  L, d);
+  if (bad) atomicOr(&s_cerr, kErrSlot);
+  __syncthreads();
   if (tid == 0 && s_cerr) flag_error(a.err, s_cerr);
 }
 
@@ -905,27 +947,22 @@ __device__ void quad_handoff_merge(const AcceptArgs& a, int b, int j, int bonus)
 // lists the released slots of the n-row block.
 template <typename KVT>
 __device__ void quad_commit_head(const AcceptArgs& a, int b, int h) {
-  __shared__ long long s_ksrc[64], s_kdst[64], s_vsrc[64], s_vdst[64];
+  SPEC_COMMIT_ROWS(rows);
   __shared__ int s_cerr;
-  const CommitRows rows{s_ksrc, s_kdst, s_vsrc, s_vdst};
   const int tid = threadIdx.x, n = a.quad_n, k = a.K, P = a.commit_P;
   const int32_t* tab = a.commit_tab + (size_t)b * a.commit_max_pages;
   const int L = a.seq_lens[b];
   const bool cap_ok = L >= 0 && (long long)L + n <= (long long)a.commit_max_pages * P;
   const int d = cap_ok ? a.jbuf[b] & 0xffff : -1;
-  if (tid < 64) {
-    const bool bad = commit_row_bases(rows, tab, P, a.commit_D, a.commit_Hkv, a.commit_num_pages,
-                                      h, L, d, (tid + 1) * (k + 1));
-    if (tid == 0) s_cerr = (cap_ok ? 0 : kErrCapacity) | (bad ? kErrSlot : 0);
-  }
-  __syncthreads();
+  if (tid == 0) s_cerr = cap_ok ? 0 : kErrCapacity;  // published by the barrier below
+  bool bad = commit_row_bases(rows, [&](int r) { return (r + 1) * (k + 1); }, tab, P, a.commit_D,
+                              a.commit_Hkv, a.commit_num_pages, h, L, d);
   commit_move_rows<KVT>(rows, reinterpret_cast<KVT*>(a.commit_k),
                         reinterpret_cast<KVT*>(a.commit_v), P, a.commit_D, d);
-  if (h == 0) {
-    if (commit_freed(a.commit_freed + (size_t)b * n, tab, P, n, a.commit_num_pages, L, d))
-      atomicOr(&s_cerr, kErrSlot);
-    __syncthreads();
-  }
+  if (h == 0) bad |= commit_freed(a.commit_freed + (size_t)b * n, tab, P, n, a.commit_num_pages,
+                                  L, d);
+  if (bad) atomicOr(&s_cerr, kErrSlot);
+  __syncthreads();
   if (tid == 0 && s_cerr) flag_error(a.err, s_cerr);
 }
 

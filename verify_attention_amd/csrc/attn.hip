@@ -462,7 +462,7 @@ struct WaveState {
 // W = ceil(B / 64) words, staged in LDS for the block rows of the workgroup's
 // row group (block rows ibase .. ilast), word w of row i at rows[(i - ibase)
 // * W + w].
-constexpr int kMaxTreeWords = 8;                            // B <= 512
+constexpr int kMaxTreeWords = kMaxTreeNodes / 64;
 constexpr int kWideMaskWords = (128 + 1) * kMaxTreeWords;   // row group rows + 1
 struct WideMask {
   const uint64_t* rows;

@@ -18,7 +18,6 @@ constexpr int kMaxSplits = 64;  // splits per unit (each keeps at least 8 stages
 constexpr int kMaxChunks = 256;
 constexpr int kMaxUnitRows = 128;   // query rows one workgroup holds (8 MFMA row tiles)
 constexpr int kMaxQueryRows = 2048; // g * B: at most 16 row groups
-constexpr int kMaxTreeNodes = 512;  // tree blocks: 8 mask words per row
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultCUs = 256;    // MI355X; used only if the device cannot be queried
 
@@ -189,7 +188,8 @@ SPEC_API int spec_prepare_tree(int bs, int N, int page_size, int max_pages, int 
                                const int32_t* node_tokens, int32_t* block_ids,
                                int32_t* positions, int32_t* cache_loc, int32_t* err_flags,
                                void* stream) {
-  if (bs <= 0 || N < 1 || N > 64 || page_size <= 0 || max_pages <= 0 || num_pages <= 0)
+  if (bs <= 0 || N < 1 || N > kMaxTreeNodes || page_size <= 0 || max_pages <= 0 ||
+      num_pages <= 0)
     return SPEC_EINVAL;
   if ((long long)bs * N > INT_MAX) return SPEC_EINVAL;
   if (!verified_id || !seq_lens || !page_table || !parent || !block_ids || !positions ||
@@ -574,7 +574,7 @@ SPEC_API int spec_accept_quadratic(int bs, int k, int V, const float* p, const f
 }
 
 SPEC_API size_t spec_accept_tree_workspace_bytes(int bs, int N, int V) {
-  if (bs <= 0 || N < 1 || N > 64 || V <= 0) return 0;
+  if (bs <= 0 || N < 1 || N > kMaxTreeNodes || V <= 0) return 0;
   return plan_accept_tree(bs, N, V).ws_bytes;
 }
 
@@ -586,7 +586,7 @@ int accept_tree_common(int bs, int N, int V, const int32_t* parent, const int32_
                        int32_t* out_tokens, int32_t* path_nodes, int32_t* new_seq_lens,
                        void* workspace, size_t ws_bytes, int32_t* err_flags, void* stream,
                        const AcceptArgs* commit) {
-  if (bs <= 0 || N < 1 || N > 64 || V <= 0) return SPEC_EINVAL;
+  if (bs <= 0 || N < 1 || N > kMaxTreeNodes || V <= 0) return SPEC_EINVAL;
   if ((long long)bs * N > INT_MAX) return SPEC_EINVAL;
   if (!parent || !token || !p || !u || !seq_lens || !accept_len || !commit_len || !bonus ||
       !out_tokens || !path_nodes || !new_seq_lens)
@@ -790,7 +790,7 @@ SPEC_API int spec_commit_kv(int dtype, int bs, int B, int Hkv, int D, int page_s
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
   if (D != 64 && D != 128) return SPEC_ENOTSUP;
   if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
-  if (bs <= 0 || B < 1 || B > 64 || Hkv <= 0 || max_pages <= 0 || num_pages <= 0)
+  if (bs <= 0 || B < 1 || B > kMaxTreeNodes || Hkv <= 0 || max_pages <= 0 || num_pages <= 0)
     return SPEC_EINVAL;
   if ((long long)max_pages * page_size > INT_MAX / 2) return SPEC_EINVAL;
   if (!seq_lens || !accept_len || !page_table || !k_pool || !v_pool || !freed_loc)

@@ -10,11 +10,11 @@
 // they are moved to L + 1 + k so that the next round sees a contiguous
 // causal prefix.
 //
-// One workgroup per (request, KV head): every accepted row's K and V
-// elements (at most 63 rows of D <= 128) are read into registers, a barrier
-// separates the reads from the writes (a destination may be another row's
-// source), then they are stored. The request's first workgroup lists the
-// released slots.
+// One workgroup per (request, KV head): the accepted rows' K and V elements
+// (D <= 128) move in rounds of 64 rows (128 at D 64): a round reads its rows
+// into registers, a barrier separates the reads from the writes (a
+// destination may be another row's source), then they are stored. The
+// request's first workgroup lists the released slots.
 #include "commit_rows.h"
 
 namespace specattn {
@@ -25,47 +25,45 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
   const int tid = threadIdx.x;
   const int P = a.P, B = a.B;
   const int32_t* tab = a.page_table + (size_t)b * a.max_pages;
-  __shared__ long long s_ksrc[64], s_kdst[64], s_vsrc[64], s_vdst[64];
-  __shared__ int s_d, s_err;
-  const CommitRows rows{s_ksrc, s_kdst, s_vsrc, s_vdst};
-  // wave 0, lane k = accepted row k: the length, the depth and every path
-  // entry are loaded at once, the path is checked by a ballot, then each lane
-  // looks up its row's pages (two dependent loads in all)
-  if (tid < 64) {
-    const int L = a.seq_lens[b];
-    int d = a.accept_len[b];
-    const int p = a.path ? (tid < B ? a.path[(size_t)b * B + tid] : 0) : tid + 1;
-    int err = 0;
-    if (L < 0 || (long long)L + B > (long long)a.max_pages * P) {
-      err = kErrCapacity;
-      d = -1;
-    } else if (d < 0 || d > B - 1) {
-      err = kErrTree;
-      d = -1;
-    } else if (a.path) {
-      // node p_k has depth k + 1: k + 1 <= p_k < B, increasing
-      const int prev = __shfl_up(p, 1, 64);
-      const bool bad = tid < d && (p < tid + 1 || p >= B || (tid > 0 && p <= prev));
-      if (__builtin_amdgcn_ballot_w64(bad)) {
-        err = kErrTree;
-        d = -1;
-      }
-    }
-    if (commit_row_bases(rows, tab, P, a.D, a.Hkv, a.num_pages, h, L, d, p)) err |= kErrSlot;
-    if (tid == 0) {
-      s_d = d;
-      s_err = err;
-    }
+  SPEC_COMMIT_ROWS(rows);
+  __shared__ int s_path[kMaxCommitRows];
+  __shared__ int s_err;
+  // the length and depth (every thread), the path entries into LDS, then
+  // the path check: node p_k has depth k + 1, so k + 1 <= p_k < B, increasing
+  const int L = a.seq_lens[b];
+  int d = a.accept_len[b];
+  int err = 0;
+  if (L < 0 || (long long)L + B > (long long)a.max_pages * P) {
+    err = kErrCapacity;
+    d = -1;
+  } else if (d < 0 || d > B - 1) {
+    err = kErrTree;
+    d = -1;
   }
+  for (int k = tid; k < d; k += kCommitThreads)
+    s_path[k] = a.path ? a.path[(size_t)b * B + k] : k + 1;
+  if (tid == 0) s_err = 0;
   __syncthreads();
-  const int d = s_d;
+  bool bad = false;
+  if (a.path)
+    for (int k = tid; k < d; k += kCommitThreads) {
+      const int p = s_path[k];
+      bad |= p < k + 1 || p >= B || (k > 0 && p <= s_path[k - 1]);
+    }
+  if (__syncthreads_or(bad)) {
+    err = kErrTree;
+    d = -1;
+  }
+  if (commit_row_bases(rows, [&](int k) { return s_path[k]; }, tab, P, a.D, a.Hkv, a.num_pages,
+                       h, L, d))
+    err |= kErrSlot;
   commit_move_rows<T>(rows, reinterpret_cast<T*>(a.k), reinterpret_cast<T*>(a.v), P, a.D, d);
   if (h == 0) {
-    if (commit_freed(a.freed + (size_t)b * B, tab, P, B, a.num_pages, a.seq_lens[b], d))
+    if (commit_freed(a.freed + (size_t)b * B, tab, P, B, a.num_pages, L, d))
       atomicOr(&s_err, kErrSlot);
     __syncthreads();
   }
-  if (tid == 0 && s_err) flag_error(a.err, s_err);
+  if (tid == 0 && (err | s_err)) flag_error(a.err, err | s_err);
 }
 
 hipError_t launch_commit_kv(const CommitArgs& a, bool bf16, hipStream_t stream) {

@@ -5,6 +5,9 @@
 
 namespace specattn {
 
+// Token-tree blocks hold at most 512 nodes (8 uint64 mask words per row).
+constexpr int kMaxTreeNodes = 512;
+
 struct AttnArgs {
   const void* q;
   const void* k;

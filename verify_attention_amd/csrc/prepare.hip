@@ -101,8 +101,62 @@ __global__ __launch_bounds__(256) void prepare_tree_kernel(PrepareTreeArgs a) {
   a.cache_loc[e] = slot;
 }
 
+// Blocks of more than 64 nodes: one workgroup of kMaxTreeNodes threads per
+// request, thread n = node n, the same pointer jumping through LDS (nine
+// rounds reach 511 ancestors).
+__global__ __launch_bounds__(kMaxTreeNodes) void prepare_tree_wide_kernel(PrepareTreeArgs a) {
+  __shared__ int s_depth[kMaxTreeNodes], s_up[kMaxTreeNodes], s_bad[kMaxTreeNodes];
+  const int n = threadIdx.x, b = blockIdx.x, N = a.N;
+  const bool live = n < N;
+  const int32_t* par = a.parent + (a.parent_per_req ? (size_t)b * N : 0);
+  const int p = live && n > 0 ? par[n] : -1;
+  const bool edge_ok = n == 0 || (p >= 0 && p < n);
+  int depth = live && n > 0 ? 1 : 0;
+  int up = live && n > 0 && edge_ok ? p : -1;
+  int bad = live && !edge_ok ? 1 : 0;
+  for (int it = 0; it < 9; ++it) {
+    s_depth[n] = depth;
+    s_up[n] = up;
+    s_bad[n] = bad;
+    __syncthreads();
+    if (up >= 0) {
+      depth += s_depth[up];
+      bad |= s_bad[up];
+      up = s_up[up];
+    }
+    __syncthreads();
+  }
+  const int L = a.seq_lens[b];
+  if (n == 0 && (L < 0 || (long long)L + N > (long long)a.max_pages * a.P))
+    flag_error(a.err, kErrCapacity);
+  if (!live) return;
+  int32_t id;
+  if (n == 0) id = a.verified_id[b];
+  else if (a.node_tokens) id = a.node_tokens[(size_t)b * N + n];
+  else id = a.mask_token_id;
+  const long long pos = (long long)L + n;
+  int32_t slot = -1;
+  if (pos >= 0) {
+    const long long pg = pos / a.P;
+    if (pg < a.max_pages) {
+      const int32_t page = a.page_table[(size_t)b * a.max_pages + pg];
+      if (page >= 0 && page < a.num_pages) slot = page * a.P + (int32_t)(pos % a.P);
+    }
+  }
+  int err = slot < 0 ? kErrSlot : 0;
+  if (bad) err |= kErrTree;
+  if (err) flag_error(a.err, err);
+  const size_t e = (size_t)b * N + n;
+  a.block_ids[e] = id;
+  a.positions[e] = bad ? -1 : (int32_t)(L + depth);
+  a.cache_loc[e] = slot;
+}
+
 hipError_t launch_prepare_tree(const PrepareTreeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(prepare_tree_kernel, dim3((a.bs + 3) / 4), dim3(256), 0, stream, a);
+  if (a.N > 64)
+    hipLaunchKernelGGL(prepare_tree_wide_kernel, dim3(a.bs), dim3(kMaxTreeNodes), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prepare_tree_kernel, dim3((a.bs + 3) / 4), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ class RoundConfig:
     q_noise_sigma: float = 0.0  # >0: q-logits = p-logits + N(0, s^2); 0: independent
     argmax_vocab: int = 0      # draft pass: argmax of bf16 logits over this vocab
     tree_depth: int = 0        # TREE: the block is a token tree of this many levels at most
+    tree_width: int = 0        # TREE: >0: a beam-shaped tree, tree_depth levels of this many nodes
     # accept from logits under (temperature, top_k, top_p); () = accept from
     # stored probability rows
     sampling: tuple = ()
@@ -79,6 +80,11 @@ class RoundConfig:
 #    (at most 16 levels) as the block, one tree per request; target logits
 #    N(0, 6^2), peaked enough (top-4 mass about 2/3 at this vocabulary) that
 #    top-candidate children are accepted at useful rates
+# 10 the Tree sampler's own setting, (B, K, V) = (16, 32, 32): 15 drafted
+#    positions, top-32 candidates per position, the best 32 prefixes kept per
+#    length, so a beam-shaped tree of 1 + 15 * 32 = 481 nodes (8 mask words a
+#    row; g * B = 1924 query rows per KV head); the Qwen3-8B-shaped verify of
+#    6 otherwise, at 8 requests
 CONFIGS = {
     1: RoundConfig("tiny_f32", bs=1, hq=2, hkv=1, d=64, page=16, block=8,
                    modes=(BIDIR, CAUSAL), dtype="f32", ctx_lo=256, ctx_hi=256,
@@ -109,6 +115,10 @@ CONFIGS = {
                    block=16, modes=(CAUSAL,), dtype="bf16", ctx_lo=1024,
                    ctx_hi=1024, vocab=151936, k_spec=15, logit_sigma=3.0,
                    q_noise_sigma=0.5, sampling=(1.0, 50, 0.95)),
+    10: RoundConfig("tree_sampler_b481_bs8", bs=8, hq=32, hkv=8, d=128, page=16,
+                    block=481, modes=(TREE,), dtype="bf16", ctx_lo=1024, ctx_hi=1024,
+                    tree_depth=15, tree_width=32, vocab=151936, k_spec=480,
+                    logit_sigma=6.0, q_noise_sigma=0.5),
     9: RoundConfig("draft_bidir_b128_bs64", bs=64, hq=16, hkv=4, d=128, page=32,
                    block=128, modes=(BIDIR,), dtype="bf16", ctx_lo=1024, ctx_hi=9216),
 }
@@ -275,6 +285,53 @@ def random_tree_parents(rng, n_nodes: int, max_depth: int) -> np.ndarray:
     return parent
 
 
+def _node_logits(cfg: "RoundConfig", rp, N: int) -> np.ndarray:
+    """Target logits of one request's N nodes, l ~ N(0, sigma^2) (one row per
+    node, drawn in node order from the request's share of the stream)."""
+    return rp.standard_normal((N, cfg.vocab)) * cfg.logit_sigma
+
+
+def _draft_logits(cfg: "RoundConfig", lp_row: np.ndarray, rq) -> np.ndarray:
+    """The drafter's logits for the token after a node: its target logits
+    plus N(0, s^2) noise."""
+    return lp_row + rq.standard_normal(len(lp_row)) * max(cfg.q_noise_sigma, 1e-3)
+
+
+def beam_tree_parents(cfg: "RoundConfig", lp: np.ndarray, rq) -> np.ndarray:
+    """parent[n] of the tree the Tree sampler keeps: per position the top
+    tree_width candidates of the drafter, and of all extensions of the kept
+    prefixes the tree_width with the largest summed draft log-probability
+    (ties: earlier prefix, then the higher-ranked candidate), for tree_depth
+    positions: the root, then tree_depth levels of tree_width nodes, a level's
+    nodes grouped by parent in level order and, under one parent, by rank.
+    The drafter's distribution is taken per prefix (node x's children are
+    candidates of softmax(_draft_logits(lp[x]))). One draft row is drawn per
+    node in node order, leaves included, as make_tree_accept_inputs draws
+    them."""
+    W, N = cfg.tree_width, cfg.block
+    parent = np.full(N, -1, dtype=np.int32)
+    score = np.zeros(N)
+    level = [0]
+    nxt = 1
+    for _ in range(cfg.tree_depth):
+        cands = []                        # (-score, prefix order, rank, prefix)
+        for order, x in enumerate(level):
+            lq = _draft_logits(cfg, lp[x], rq)
+            m = lq.max()
+            logq = lq - (m + np.log(np.exp(lq - m).sum()))
+            top = _top_indices(lq, W)
+            cands += [(-(score[x] + logq[t]), order, r, x) for r, t in enumerate(top)]
+        kept = sorted(sorted(cands)[:W], key=lambda c: (c[1], c[2]))
+        level = []
+        for negs, _, _, x in kept:
+            parent[nxt], score[nxt] = x, -negs
+            level.append(nxt)
+            nxt += 1
+    for _ in level:                       # the last level's draft rows (unused here)
+        rq.standard_normal(cfg.vocab)
+    return parent
+
+
 def tree_row_masks(parent: np.ndarray) -> np.ndarray:
     """uint64 row masks of a tree of at most 64 nodes in topological order:
     bit j of row n is set iff node j is node n or one of its ancestors."""
@@ -351,10 +408,19 @@ def make_trees(cfg: RoundConfig, seed: int, per_request=True):
     depth = cfg.tree_depth or cfg.block
     wide = cfg.block > 64
     masks = tree_row_words if wide else tree_row_masks
+    if cfg.tree_width:
+        if 1 + depth * cfg.tree_width != cfg.block:
+            raise ValueError("a beam tree has 1 + tree_depth * tree_width nodes")
+        # the beam follows the round's own target and draft rows (the streams
+        # of make_tree_accept_inputs, request by request)
+        rp, rq = rng_for(seed, "plogit"), rng_for(seed, "qnoise")
+        draw = lambda: beam_tree_parents(cfg, _node_logits(cfg, rp, cfg.block), rq)
+    else:
+        draw = lambda: random_tree_parents(r, cfg.block, depth)
     if not per_request:
-        par = random_tree_parents(r, cfg.block, depth)
+        par = draw()
         return par, (masks(par)[None] if wide else masks(par))
-    par = np.stack([random_tree_parents(r, cfg.block, depth) for _ in range(cfg.bs)])
+    par = np.stack([draw() for _ in range(cfg.bs)])
     return par, np.stack([masks(p) for p in par])
 
 
@@ -411,6 +477,17 @@ class TreeAcceptInputs:
     u: np.ndarray       # [bs, N] float32 uniforms in [0, 1)
 
 
+def _top_indices(x: np.ndarray, k: int) -> np.ndarray:
+    """The indices of the k largest entries of x, largest first, the lower
+    index first among equal values (a stable descending sort's first k)."""
+    if k >= len(x):
+        return np.argsort(-x, kind="stable")
+    cand = np.argpartition(-x, k - 1)[:k]
+    kth = x[cand].min()
+    cand = np.flatnonzero(x >= kth)            # every entry tied with the k-th
+    return cand[np.lexsort((cand, -x[cand]))][:k]
+
+
 def make_tree_accept_inputs(cfg: RoundConfig, seed: int, parents: np.ndarray,
                             bs: int | None = None) -> TreeAcceptInputs:
     """Target rows p = softmax(l), l ~ N(0, sigma^2), one per node. The
@@ -425,15 +502,15 @@ def make_tree_accept_inputs(cfg: RoundConfig, seed: int, parents: np.ndarray,
     token = np.zeros((bs, N), np.int32)
     rp, rq = rng_for(seed, "plogit"), rng_for(seed, "qnoise")
     for b in range(bs):
-        lp = rp.standard_normal((N, V)) * cfg.logit_sigma
+        lp = _node_logits(cfg, rp, N)
         p[b] = _softmax_rows64(lp)
         for x in range(N):
             kids = np.flatnonzero(par[b] == x)
-            if len(kids) == 0:
-                continue
-            lq = lp[x] + rq.standard_normal(V) * max(cfg.q_noise_sigma, 1e-3)
-            top = np.argsort(-lq, kind="stable")[:len(kids)]
-            token[b, kids] = top
+            if len(kids) == 0 and not cfg.tree_width:
+                continue      # (a beam tree's rows are drawn for every node)
+            lq = _draft_logits(cfg, lp[x], rq)
+            if len(kids):
+                token[b, kids] = _top_indices(lq, len(kids))
     u = rng_for(seed, "uniform").random((bs, N), dtype=np.float32)
     return TreeAcceptInputs(par.copy(), token, p, u)
 
