@@ -267,7 +267,7 @@ int spec_draft_argmax(int rows, int V, int dtype, const void* logits, int32_t* t
  *   row = mask_token_id.
  * Only the k rows of G_a are read per request.
  *
- *   bs, k, V        requests, drafts per block (1..7), vocabulary
+ *   bs, k, V        requests, drafts per block (1..21), vocabulary
  *   dtype           SPEC_BF16 or SPEC_F32 logits [bs, (k + 1)^2, V]
  *   accept_len [bs] as spec_accept returns it (0..k); bonus [bs] (needed only
  *   with next_block)
@@ -353,7 +353,7 @@ int spec_accept(int bs, int K, int V, int greedy, const float* p, const float* q
  * commit's workgroups ride in the accept's two kernels (each finds the accept
  * length from the same gathered tests).
  *
- *   bs, k (1..7), V, p [bs, k+1, V], q [bs, k, V], draft [bs, k], u [bs, k+1],
+ *   bs, k (1..21), V, p [bs, k+1, V], q [bs, k, V], draft [bs, k], u [bs, k+1],
  *   seq_lens: as spec_accept with K = k (stochastic form only)
  *   logits_dtype, logits [bs, (k + 1)^2, V], mask_token_id: as
  *   spec_quadratic_handoff

@@ -46,7 +46,7 @@ hipError_t launch_prepare_tree(const PrepareTreeArgs& a, hipStream_t) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_quadratic_handoff(const HandoffArgs& h, bool, hipStream_t) {
-  require(h.k >= 1 && h.k <= 7 && h.n == (h.k + 1) * (h.k + 1), "handoff layout");
+  require(h.k >= 1 && h.k <= kMaxQuadK && h.n == (h.k + 1) * (h.k + 1), "handoff layout");
   require(!h.next_block || h.bonus, "handoff block needs the bonus");
   require(h.part_v && h.part_i && h.S >= 1 && h.S <= 16 && h.seg_len % 8 == 0 &&
               (long long)h.S * h.seg_len >= h.V && (long long)(h.S - 1) * h.seg_len < h.V,
@@ -66,7 +66,7 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t) {
 hipError_t launch_accept_quadratic(const AcceptArgs& a, bool, hipStream_t) {
   require(a.nchunk >= 1 && (long long)a.nchunk * a.chunk >= a.V, "chunks cover V");
   require(a.partial && a.jbuf && a.quad_part_v && a.quad_part_i, "quadratic workspace");
-  require(a.quad_n == (a.K + 1) * (a.K + 1) && a.K <= 7, "quadratic layout");
+  require(a.quad_n == (a.K + 1) * (a.K + 1) && a.K <= kMaxQuadK, "quadratic layout");
   require(a.quad_S >= 1 && a.quad_seg % 8 == 0 && (long long)a.quad_S * a.quad_seg >= a.V,
           "hand-off segments cover the row");
   require(a.commit_k && a.commit_v && a.commit_tab && a.commit_freed && a.commit_Hkv > 0,

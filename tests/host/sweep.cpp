@@ -76,7 +76,7 @@ int main() {
   EXPECT(spec_prepare_tree(32, 8, 16, 80, 300, 7, I, I, I, nullptr, 0, I, I, I, I, I, nullptr),
          SPEC_EINVAL);
   for (int bs : {1, 5, 32, 1000})
-    for (int k = 1; k <= 7; ++k)
+    for (int k : {1, 2, 4, 7, 8, 15, 21})
       for (int V : {1, 7, 1000, 151936}) {
         const size_t wh = spec_quadratic_handoff_workspace_bytes(bs, k, V);
         EXPECT(spec_quadratic_handoff(bs, k, V, SPEC_BF16, F, I, I, 9, I, I, F, wh, I, nullptr),
@@ -88,14 +88,14 @@ int main() {
                                       I, nullptr),
                SPEC_ENOSPC);
       }
-  EXPECT(spec_quadratic_handoff(32, 8, 151936, SPEC_BF16, F, I, I, 9, I, I, F, 1 << 30, I,
+  EXPECT(spec_quadratic_handoff(32, 22, 151936, SPEC_BF16, F, I, I, 9, I, I, F, 1 << 30, I,
                                 nullptr),
          SPEC_EINVAL);
   EXPECT(spec_quadratic_handoff(32, 4, 151936, SPEC_BF16, F, I, nullptr, 9, I, I, F, 1 << 30, I,
                                 nullptr),
          SPEC_EINVAL);  // a next block needs the bonus
   for (int bs : {1, 32, 600})
-    for (int k = 1; k <= 7; ++k)
+    for (int k : {1, 2, 4, 7, 8, 15, 21})
       for (int V : {9, 4099, 151936}) {
         const size_t wq = spec_accept_quadratic_workspace_bytes(bs, k, V);
         EXPECT(spec_accept_quadratic(bs, k, V, FL, FL, I, FL, I, SPEC_BF16, F, 7, I, I, I, I, I, I,
@@ -111,7 +111,7 @@ int main() {
                                      F, wq, I, nullptr),
                SPEC_EINVAL);  // positions without slots
       }
-  EXPECT(spec_accept_quadratic(4, 8, 512, FL, FL, I, FL, I, SPEC_BF16, F, 7, I, I, I, I, I, I, I,
+  EXPECT(spec_accept_quadratic(4, 22, 512, FL, FL, I, FL, I, SPEC_BF16, F, 7, I, I, I, I, I, I, I,
                                I, I, SPEC_BF16, 8, 128, 16, 80, 300, I, F, F, I, F, 1 << 30, I,
                                nullptr),
          SPEC_EINVAL);

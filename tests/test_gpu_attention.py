@@ -340,6 +340,10 @@ QUADS = [
                            ctx_hi=500)),
     ("k3_g8_p32", dict(bs=4, hq=16, hkv=2, page=32, block=16, quad_k=3, ctx_lo=1, ctx_hi=300)),
     ("k7_g4_bf16_rowgroups", dict(bs=2, block=64, quad_k=7, ctx_lo=10, ctx_hi=600)),
+    # past 64 rows: mask words (a block of 16 drafted positions has k = 15)
+    ("k15_g4_bf16_words", dict(bs=2, block=256, quad_k=15, ctx_lo=10, ctx_hi=400)),
+    ("k21_g2_d64_f32_words", dict(bs=1, hq=4, hkv=2, d=64, block=484, quad_k=21, dtype="f32",
+                                  ctx_lo=0, ctx_hi=200)),
 ]
 
 
@@ -358,7 +362,7 @@ def test_quadratic_layout_all_rows(gpu_lib, name, over):
     assert np.max(np.abs(lse - rl)) <= LSE_TOL[cfg.dtype]
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 8, 9])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 8, 9, 10])
 def test_full_size_sampled_rows(gpu_lib, cid):
     """Full workload shapes in the bench's launch configuration; the reference
     computes sampled rows one at a time."""

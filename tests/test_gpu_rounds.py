@@ -204,11 +204,13 @@ def test_quadratic_handoff_golden(gpu_lib):
 
 
 @pytest.mark.parametrize("k,bs,V,dt", [(4, 32, 151936, "bf16"), (7, 5, 4099, "f32"),
-                                       (1, 17, 1000, "bf16")])
+                                       (1, 17, 1000, "bf16"), (15, 3, 5003, "f32"),
+                                       (21, 2, 2000, "bf16")])
 def test_quadratic_handoff_matches_reference(gpu_lib, k, bs, V, dt):
     """The quadratic workload's size (k = 4, bs 32, bf16 logits of V =
-    151936: real equal maxima occur), the largest layout (k = 7) and k = 1;
-    every accept length from 0 to k, and one out of range."""
+    151936: real equal maxima occur), k = 7, 15 (a 256-row next block) and
+    21 (the largest layout, 484 rows) and k = 1; every accept length from 0
+    to k, and one out of range."""
     print_case("handoff", k, bs, V, dt)
     rng = np.random.default_rng(k * 100 + bs)
     n = (k + 1) ** 2
@@ -313,6 +315,8 @@ def test_two_quadratic_rounds_chain(gpu_lib):
                             dtype="f32", vocab=4099, ctx_lo=20, ctx_hi=300), "f32"),
     ("k1_bf16", dict(bs=9, block=4, quad_k=1, k_spec=1, vocab=1000, ctx_lo=3, ctx_hi=90),
      "bf16"),
+    ("k15_bf16_block256", dict(bs=4, block=256, quad_k=15, k_spec=15, vocab=3001, ctx_lo=10,
+                               ctx_hi=400), "bf16"),
 ])
 def test_accept_quadratic_is_the_three_calls(gpu_lib, name, over, logit_dt):
     """spec_accept_quadratic equals spec_accept, spec_quadratic_handoff,

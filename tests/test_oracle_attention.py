@@ -328,7 +328,7 @@ def _separate_block(x, b, rows, L):
     return kp, vp, np.arange(npg)[None, :]
 
 
-@pytest.mark.parametrize("k", [1, 2, 4, 7])
+@pytest.mark.parametrize("k", [1, 2, 4, 7, 8])
 def test_quadratic_layout_rows_follow_their_definition(k):
     """Each row of the quadratic layout, run through the bitmask mode, equals
     the attention that defines it on a separately built block: spine token i
@@ -366,8 +366,18 @@ def test_quadratic_layout_shape_and_limits():
     assert int(masks[0]) == 1 and int(masks[8]) == 1 | 16 | 256
     # group G_1 (positions 5, 6, 7) sees spine 0, 4 and itself
     assert int(masks[6]) == 1 | 16 | (7 << 5)
+    # past 64 positions the rows are words: k = 8 has 81 rows of two words,
+    # spine token 8 (position 72) sees spine positions 0, 9, .., 63 and itself;
+    # member 7 of G_8 (position 80) also sees the members 73 .. 80
+    role, masks = synth.quadratic_layout(8)
+    assert masks.shape == (1, 81, 2) and role[72] == ("spine", 8, 0)
+    row = lambda r: int(masks[0, r, 0]) | (int(masks[0, r, 1]) << 64)
+    assert row(72) == sum(1 << (9 * t) for t in range(9))
+    assert role[80] == ("mask", 8, 7) and row(80) == row(72) | sum(1 << t for t in range(73, 81))
+    role, masks = synth.quadratic_layout(21)
+    assert masks.shape == (1, 484, 8)
     with pytest.raises(ValueError):
-        synth.quadratic_layout(8)
+        synth.quadratic_layout(22)
 
 
 def test_mask_words_agree_with_one_word_rows_and_wide_chains_are_causal():

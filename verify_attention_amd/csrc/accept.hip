@@ -850,14 +850,17 @@ __global__ __launch_bounds__(64) void handoff_select_kernel(HandoffArgs h) {
   if (lane < k) h.next_draft[(size_t)b * k + lane] = tok;
   if (lane == 0 && !ok) flag_error(h.err, kErrTree);
   // row 0: the bonus (the next root); spine rows (m + 1) * (k + 1): the
-  // drafts; every group row: the mask token (lane = row, n <= 64)
-  const int j = lane / (k + 1), rem = lane - j * (k + 1);
-  const int draft = __shfl(tok, j > 0 && j <= k ? j - 1 : 0, 64);  // every lane takes part
-  if (h.next_block && lane < h.n) {
-    int32_t v = h.mask_token_id;
-    if (lane == 0) v = h.bonus[b];
-    else if (rem == 0) v = draft;
-    h.next_block[(size_t)b * h.n + lane] = v;
+  // drafts; every group row: the mask token (row e = e0 + lane)
+  if (!h.next_block) return;
+  for (int e0 = 0; e0 < h.n; e0 += 64) {
+    const int e = e0 + lane, j = e / (k + 1), rem = e - j * (k + 1);
+    const int draft = __shfl(tok, j > 0 && j <= k ? j - 1 : 0, 64);  // every lane takes part
+    if (e < h.n) {
+      int32_t v = h.mask_token_id;
+      if (e == 0) v = h.bonus[b];
+      else if (rem == 0) v = draft;
+      h.next_block[(size_t)b * h.n + e] = v;
+    }
   }
 }
 
@@ -914,30 +917,33 @@ __device__ void quad_handoff_merge(const AcceptArgs& a, int b, int j, int bonus)
     tok = bi == 0x7fffffff ? 0 : bi;
     a.quad_next_draft[(size_t)b * k + lane] = tok;
   }
-  const int jj = lane / (k + 1), rem = lane - jj * (k + 1);
-  const int draft = __shfl(tok, jj > 0 && jj <= k ? jj - 1 : 0, 64);  // every lane takes part
-  if (a.quad_next_block && lane < n) {
-    int32_t v = a.quad_mask;
-    if (lane == 0) v = bonus;
-    else if (rem == 0) v = draft;
-    a.quad_next_block[(size_t)b * n + lane] = v;
-  }
-  if (a.next_pos) {
-    // the next round's block starts at the new committed length
-    const int L2 = a.seq_lens[b] + j + 1;
-    const int P = a.commit_P;
-    if (lane == 0 && (L2 < 0 || (long long)L2 + n > (long long)a.commit_max_pages * P))
-      flag_error(a.err, kErrCapacity);
-    if (lane < n) {
-      const long long pos = (long long)L2 + lane;
+  // the next round's block, row e = e0 + lane (row e of the layout is
+  // member rem of group jj, or spine token jj when rem = 0)
+  const int L2 = a.seq_lens[b] + j + 1;  // the next block starts at the new committed length
+  const int P = a.commit_P;
+  if (a.next_pos && lane == 0 &&
+      (L2 < 0 || (long long)L2 + n > (long long)a.commit_max_pages * P))
+    flag_error(a.err, kErrCapacity);
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane, jj = e / (k + 1), rem = e - jj * (k + 1);
+    const int draft = __shfl(tok, jj > 0 && jj <= k ? jj - 1 : 0, 64);  // every lane takes part
+    if (e >= n) continue;
+    if (a.quad_next_block) {
+      int32_t v = a.quad_mask;
+      if (e == 0) v = bonus;
+      else if (rem == 0) v = draft;
+      a.quad_next_block[(size_t)b * n + e] = v;
+    }
+    if (a.next_pos) {
+      const long long pos = (long long)L2 + e;
       int32_t slot = -1;
       if (pos >= 0 && pos / P < a.commit_max_pages) {
         const int32_t page = a.commit_tab[(size_t)b * a.commit_max_pages + pos / P];
         if (page >= 0 && page < a.commit_num_pages) slot = page * P + (int32_t)(pos % P);
       }
       if (slot < 0) flag_error(a.err, kErrSlot);
-      a.next_pos[(size_t)b * n + lane] = L2 + jj + rem;
-      a.next_loc[(size_t)b * n + lane] = slot;
+      a.next_pos[(size_t)b * n + e] = L2 + jj + rem;
+      a.next_loc[(size_t)b * n + e] = slot;
     }
   }
 }

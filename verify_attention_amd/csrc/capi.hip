@@ -347,7 +347,7 @@ HandoffPlan plan_handoff(int bs, int k, int V) {
 }  // namespace
 
 SPEC_API size_t spec_quadratic_handoff_workspace_bytes(int bs, int k, int V) {
-  if (bs <= 0 || k < 1 || k > 7 || V <= 0) return 0;
+  if (bs <= 0 || k < 1 || k > kMaxQuadK || V <= 0) return 0;
   return plan_handoff(bs, k, V).ws_bytes;
 }
 
@@ -357,7 +357,7 @@ SPEC_API int spec_quadratic_handoff(int bs, int k, int V, int dtype, const void*
                                     int32_t* next_block, void* workspace, size_t ws_bytes,
                                     int32_t* err_flags, void* stream) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ENOTSUP;
-  if (bs <= 0 || k < 1 || k > 7 || V <= 0) return SPEC_EINVAL;
+  if (bs <= 0 || k < 1 || k > kMaxQuadK || V <= 0) return SPEC_EINVAL;
   const int n = (k + 1) * (k + 1);
   if ((long long)bs * n > INT_MAX / 16) return SPEC_EINVAL;
   if (!logits || !accept_len || !next_draft || (next_block && !bonus)) return SPEC_EINVAL;
@@ -511,7 +511,7 @@ QuadPlan plan_quadratic(int bs, int k, int V) {
 }  // namespace
 
 SPEC_API size_t spec_accept_quadratic_workspace_bytes(int bs, int k, int V) {
-  if (bs <= 0 || k < 1 || k > 7 || V <= 0) return 0;
+  if (bs <= 0 || k < 1 || k > kMaxQuadK || V <= 0) return 0;
   return plan_quadratic(bs, k, V).ws_bytes;
 }
 
@@ -530,7 +530,7 @@ SPEC_API int spec_accept_quadratic(int bs, int k, int V, const float* p, const f
   if (kv_dtype != SPEC_F32 && kv_dtype != SPEC_BF16) return SPEC_ENOTSUP;
   if (D != 64 && D != 128) return SPEC_ENOTSUP;
   if (page_size != 16 && page_size != 32) return SPEC_ENOTSUP;
-  if (k < 1 || k > 7) return SPEC_EINVAL;
+  if (k < 1 || k > kMaxQuadK) return SPEC_EINVAL;
   AcceptArgs a;
   AccPlan acc_plan;
   const int st = accept_check_args(bs, k, V, 0, p, q, draft, u, seq_lens, accept_len, commit_len,

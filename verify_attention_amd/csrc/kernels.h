@@ -7,6 +7,9 @@ namespace specattn {
 
 // Token-tree blocks hold at most 512 nodes (8 uint64 mask words per row).
 constexpr int kMaxTreeNodes = 512;
+// Quadratic layouts of k drafts take (k + 1)^2 block rows.
+constexpr int kMaxQuadK = 21;
+static_assert((kMaxQuadK + 1) * (kMaxQuadK + 1) <= kMaxTreeNodes, "a quadratic block is a tree block");
 
 struct AttnArgs {
   const void* q;

@@ -362,24 +362,30 @@ def quadratic_layout(k: int):
     then drafts s_1 .. s_k) at positions i * (k + 1), and after spine token j
     a group G_j of k MASK positions j * (k + 1) + 1 .. j * (k + 1) + k, which
     proposes the continuation if exactly s_1 .. s_j are accepted. Returns
-    (role [n] as (kind, j, m) tuples, row masks [n] uint64) with n = (k + 1)^2:
-    spine token i sees spine tokens 0 .. i (causal); a member of G_j sees spine
-    tokens 0 .. j and every member of G_j (bidirectional inside the group)."""
+    (role [n] as (kind, j, m) tuples, row masks) with n = (k + 1)^2: spine
+    token i sees spine tokens 0 .. i (causal); a member of G_j sees spine
+    tokens 0 .. j and every member of G_j (bidirectional inside the group).
+    The masks are [n] uint64 for n <= 64, else W = ceil(n / 64) words per row
+    of the one shared layout, [1, n, W] (bit j of a row is bit j % 64 of word
+    j // 64); n <= 512."""
     n = (k + 1) * (k + 1)
-    if n > 64:
-        raise ValueError("the layout needs (k + 1)^2 <= 64 positions")
-    role, masks = [], np.zeros(n, dtype=np.uint64)
+    if n > 512:
+        raise ValueError("the layout needs (k + 1)^2 <= 512 positions")
+    role, rows = [], []
     for pos in range(n):
         j, m = divmod(pos, k + 1)
         spine = sum(1 << (t * (k + 1)) for t in range(j + 1))
         if m == 0:
             role.append(("spine", j, 0))
-            masks[pos] = np.uint64(spine)
+            rows.append(spine)
         else:
             group = sum(1 << (j * (k + 1) + 1 + t) for t in range(k))
             role.append(("mask", j, m - 1))
-            masks[pos] = np.uint64(spine | group)
-    return role, masks
+            rows.append(spine | group)
+    W = (n + 63) // 64
+    words = np.array([[(r >> (64 * w)) & ((1 << 64) - 1) for w in range(W)] for r in rows],
+                     dtype=np.uint64)
+    return role, (words[:, 0].copy() if W == 1 else words[None])
 
 
 def quadratic_parents(k: int) -> np.ndarray:
