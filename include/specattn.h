@@ -219,9 +219,9 @@ int block_attn(int mode, int n_causal, const int32_t* n_causal_per_req, int dtyp
  *
  *   tree_mask         uint64 row masks (device): [B, W] when tree_per_request
  *                     is 0, else [bs, B, W]; B <= 512 (W = 1 for B <= 64)
- *   other arguments, outputs, workspace (block_attn_workspace_bytes, which
- *   for B > 64 covers the schedule these trees take) and errors as for
- *   block_attn; SPEC_EINVAL also for tree_mask == NULL or B > 512.
+ *   other arguments, outputs, workspace (block_attn_workspace_bytes) and
+ *   errors as for block_attn; SPEC_EINVAL also for tree_mask == NULL or
+ *   B > 512.
  */
 int block_attn_tree(const uint64_t* tree_mask, int tree_per_request, int dtype, int bs, int B,
                     int Hq, int Hkv, int D, int page_size, int max_pages, int num_pages,

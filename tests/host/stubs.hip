@@ -15,7 +15,8 @@ static void require(bool ok, const char* what) {
   }
 }
 
-hipError_t launch_block_attn(const AttnArgs& a, bool, int D, int total_blocks, hipStream_t) {
+hipError_t launch_block_attn(const AttnArgs& a, bool bf16, int D, int total_blocks, hipStream_t) {
+  const bool f32 = !bf16;
   require(a.g * a.B == a.Mt, "Mt = g * B");
   require(a.M >= 1 && a.M <= 128 && a.RG >= 1 && (long long)a.RG * a.M >= a.Mt, "row groups cover Mt");
   require((a.RG - 1) * a.M < a.Mt, "no empty row group");
@@ -23,7 +24,8 @@ hipError_t launch_block_attn(const AttnArgs& a, bool, int D, int total_blocks, h
   require(D == 64 || D == 128, "D");
   if (a.mode == 3) {
     require(a.tree && a.tree_words == (a.B + 63) / 64 && a.tree_words <= 8, "tree mask words");
-    require(a.tree_words == 1 || !a.balanced, "wide trees take the split schedule");
+    require(a.tree_words == 1 || !a.balanced || !(f32 && D == 128),
+            "fp32 D 128 wide trees take the split schedule");
   } else {
     require(a.tree_words == 1, "one mask word outside TREE mode");
   }

@@ -237,6 +237,14 @@ TREES = [
                                         dtype="f32", ctx_lo=20, ctx_hi=300), True),
     ("b512_g4_max", 6, dict(bs=2, hq=8, hkv=2, block=512, tree_depth=16, ctx_lo=0, ctx_hi=200),
      True),
+    # the balanced schedule (a workgroup's pieces span requests: the mask
+    # words are restaged per request)
+    ("b72_g4_balanced", 6, dict(bs=96, hq=8, hkv=2, block=72, tree_depth=20, ctx_lo=1,
+                                ctx_hi=3000), True),
+    ("b200_g1_shared_balanced", 6, dict(bs=128, hq=2, hkv=2, block=200, tree_depth=30, ctx_lo=1,
+                                        ctx_hi=4000), False),
+    ("b66_f32_d64_balanced", 6, dict(bs=96, hq=4, hkv=2, d=64, block=66, tree_depth=12,
+                                     dtype="f32", ctx_lo=1, ctx_hi=3000), True),
 ]
 
 

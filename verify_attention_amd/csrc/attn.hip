@@ -469,6 +469,20 @@ struct WideMask {
   int ibase, ilast, W;
 };
 
+// The block rows of the row group starting at query row row0, for LDS words s.
+__device__ __forceinline__ WideMask wide_mask(const AttnArgs& a, uint64_t* s, int row0) {
+  return WideMask{s, row0 / a.g, min(a.B - 1, (row0 + a.M - 1) / a.g), a.tree_words};
+}
+
+// Every thread: request b's mask words of the group's rows into LDS (the
+// caller publishes them with a barrier).
+__device__ __forceinline__ void stage_wide_mask(const AttnArgs& a, uint64_t* s,
+                                                const WideMask& wm, int b, int tid) {
+  const int n = (wm.ilast - wm.ibase + 1) * wm.W;
+  const uint64_t* src = a.tree + ((a.tree_per_req ? (size_t)b * a.B : 0) + wm.ibase) * (size_t)wm.W;
+  for (int e = tid; e < n; e += kWave * kWaves) s[e] = src[e];
+}
+
 // A stage is consumed in two halves so that the two waves sharing a SIMD can
 // run them out of phase:
 //   front: read the stage's K and V fragments from the ring, S^T = K Q^T;
@@ -526,6 +540,22 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
   }
 
   if (key0 + kStep > L) {
+    // WIDE: bits key0 - L .. key0 - L + 31 of each row's mask, from at most
+    // two LDS words (rows past the group's end read a neighbour: their
+    // outputs are never written; bits outside the block read as 0, and the
+    // keys there are context, always visible, or past the end, never)
+    uint32_t win[MT];
+    if constexpr (WIDE) {
+      const int jb0 = key0 - L, wi = jb0 >> 6, sh = jb0 & 63;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int ic = min(max(ws.blk_row[t], wm.ibase), wm.ilast) - wm.ibase;
+        const uint64_t* row = wm.rows + ic * wm.W;
+        const uint64_t lo = wi >= 0 && wi < wm.W ? row[wi] : 0;
+        const uint64_t hi = wi + 1 >= 0 && wi + 1 < wm.W ? row[wi + 1] : 0;
+        win[t] = (uint32_t)(sh ? (lo >> sh) | (hi << (64 - sh)) : lo);
+      }
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -536,11 +566,7 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
           const int jb = key - L, i = ws.blk_row[t];
           bool intra;
           if constexpr (WIDE) {
-            // LDS words of the row (rows past the group's end read a neighbour:
-            // their outputs are never written); keys outside the block are
-            // context (always visible) or past the end (never visible)
-            const int ic = min(max(i, wm.ibase), wm.ilast) - wm.ibase;
-            intra = jb >= 0 && jb < a.B && ((wm.rows[ic * wm.W + (jb >> 6)] >> (jb & 63)) & 1);
+            intra = (win[t] >> (8 * grp + 4 * t2 + j)) & 1;
           } else {
             intra = a.mode == 3 ? ((ws.tmask[t] >> (jb & 63)) & 1) != 0
                                 : (a.mode == 0) | (jb <= i) | ((a.mode == 2) & (i >= nc));
@@ -920,15 +946,10 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
   const int nc = causal_rows(a, b);
   WideMask wm{s_tm, 0, 0, 1};
   if constexpr (WIDE) {
-    // the row group's block rows' mask words into LDS (the streaming loop
-    // starts with a barrier, which publishes them)
-    wm.ibase = u.row0 / a.g;
-    wm.ilast = min(a.B - 1, (u.row0 + a.M - 1) / a.g);
-    wm.W = a.tree_words;
-    const int n = (wm.ilast - wm.ibase + 1) * wm.W;
-    const uint64_t* src =
-        a.tree + ((a.tree_per_req ? (size_t)b * a.B : 0) + wm.ibase) * (size_t)wm.W;
-    for (int e = c.tid; e < n; e += kWave * kWaves) s_tm[e] = src[e];
+    // the row group's mask words into LDS (the streaming loop starts with a
+    // barrier, which publishes them)
+    wm = wide_mask(a, s_tm, u.row0);
+    stage_wide_mask(a, s_tm, wm, b, c.tid);
   }
   stream_stages<T, D, MT, false, WIDE>(ws, a, c, s_ring, s_pgoff, b, kvh, u.row0, L, nc, s_lo,
                                        s_hi, first, wm);
@@ -1020,11 +1041,12 @@ __device__ __forceinline__ int range_start(int total, int w, int G) {
   return (int)((long long)total * w / G);
 }
 
-template <typename T, int D, int MT>
+template <typename T, int D, int MT, bool WIDE = false>
 __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(AttnArgs a) {
   using SS = StageShape<T, D>;
   __shared__ __attribute__((aligned(1024))) char s_ring[SS::NSP * SS::PAIR];
   __shared__ __attribute__((aligned(16))) uint64_t s_pgoff[2 * kPageWin];
+  __shared__ uint64_t s_tm[WIDE ? kWideMaskWords : 1];
   __shared__ int s_pre[kMaxBalancedBatch + 1];
   __shared__ int s_len[kMaxBalancedBatch];
   __shared__ int s_tmp[kWaves];
@@ -1055,12 +1077,17 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   int nc = causal_rows(a, b);
   int2 range = stage_range(start);
   stage_first(range, table_pair(a, a.page_table + (size_t)b * a.max_pages, range.x + c.tid));
+  // TREE blocks of more than 64 nodes: the workgroup's row group is fixed,
+  // so its mask words change only with the request (restaged with the next
+  // piece's page offsets, after the barrier that ends their last reads)
+  const WideMask wm = WIDE ? wide_mask(a, s_tm, row0) : WideMask{s_tm, 0, 0, 1};
+  if constexpr (WIDE) stage_wide_mask(a, s_tm, wm, b, c.tid);
   for (int cur = start; cur < end;) {
     const int seg = min(np - off, end - cur);
     const bool whole = off == 0 && seg == np;
     const int part = whole ? -1 : (cur == start ? 2 * w : 2 * w + 1) * a.RG + rg;
-    stream_stages<T, D, MT, true>(ws, a, c, s_ring, s_pgoff, b, kvh, row0, L, nc, range.x, range.y,
-                                  int2{0, 0});
+    stream_stages<T, D, MT, true, WIDE>(ws, a, c, s_ring, s_pgoff, b, kvh, row0, L, nc, range.x,
+                                        range.y, int2{0, 0}, wm);
     const int fb = b, fkvh = kvh;
     cur += seg;
     off += seg;
@@ -1090,6 +1117,8 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
     }
     finish_unit<T, D, MT>(ws, a, c, s_ring, fb, fkvh, row0, part, [&] {
       if (next) stage_first(range, pg);
+      if constexpr (WIDE)
+        if (next && b != fb && a.tree_per_req) stage_wide_mask(a, s_tm, wm, b, c.tid);
     });
     reset_state(ws);
   }
@@ -1221,10 +1250,19 @@ static hipError_t launch_dt(const AttnArgs& a, int total_blocks, hipStream_t str
   const dim3 block(kWave * kWaves);
   if (a.balanced) {
     const dim3 grid(a.G);
-    if (a.M > 64)
+    if (a.tree_words > 1) {  // TREE blocks of more than 64 nodes
+      if constexpr (sizeof(T) == 4 && D == 128) {
+        return hipErrorInvalidValue;  // no LDS room for the mask words: the planner never asks
+      } else if (a.M > 64) {
+        hipLaunchKernelGGL((block_attn_balanced_kernel<T, D, 2, true>), grid, block, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((block_attn_balanced_kernel<T, D, 1, true>), grid, block, 0, stream, a);
+      }
+    } else if (a.M > 64) {
       hipLaunchKernelGGL((block_attn_balanced_kernel<T, D, 2>), grid, block, 0, stream, a);
-    else
+    } else {
       hipLaunchKernelGGL((block_attn_balanced_kernel<T, D, 1>), grid, block, 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     const int teams = a.G / a.RG;
     if (e != hipSuccess || teams < 2) return e;

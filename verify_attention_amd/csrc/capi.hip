@@ -218,8 +218,9 @@ SPEC_API int spec_prepare_tree(int bs, int N, int page_size, int max_pages, int 
 SPEC_API size_t block_attn_workspace_bytes(int bs, int B, int Hq, int Hkv, int D, int max_kv_len) {
   if (bs <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || max_kv_len <= 0) return 0;
   const size_t ws = plan_attn(bs, B, Hq, Hkv, D, max_kv_len).ws_bytes;
-  // tree blocks of more than 64 nodes always take the split schedule
-  if (B <= 64) return ws;
+  // fp32 trees of more than 64 nodes at D = 128 take the split schedule (the
+  // balanced kernel's LDS has no room for their mask words): cover both
+  if (B <= 64 || D != 128) return ws;
   return std::max(ws, plan_attn(bs, B, Hq, Hkv, D, max_kv_len, false).ws_bytes);
 }
 
@@ -244,7 +245,8 @@ int attn_common(int mode, int n_causal, const int32_t* n_causal_per_req, const u
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return SPEC_EINVAL;
   if (!(std::isfinite(sm_scale))) return SPEC_EINVAL;
   const int tree_words = mode == SPEC_TREE ? (B + 63) / 64 : 1;
-  const AttnPlan plan = plan_attn(bs, B, Hq, Hkv, D, max_kv_len, tree_words == 1);
+  const bool split_only = tree_words > 1 && dtype == SPEC_F32 && D == 128;
+  const AttnPlan plan = plan_attn(bs, B, Hq, Hkv, D, max_kv_len, !split_only);
   if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes)) return SPEC_ENOSPC;
 
   AttnArgs a;
