@@ -32,8 +32,9 @@
 //     it with one conflict-free ds_read_b128. A ring of three stage pairs
 //     keeps two pairs (64 KB for bf16, 128 dims) in flight per CU; the loads
 //     carry the non-temporal cache policy (the KV stream is read once), which
-//     measurably raises the HBM read rate. vmcnt waits are counted by hand and
-//     one barrier per pair publishes a pair to both sets.
+//     measurably raises the HBM read rate, except where a head's row groups
+//     re-read its keys from L2. vmcnt waits are counted by hand and one
+//     barrier per pair publishes a pair to both sets.
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16
 //     (eight v_mfma_f32_16x16x4f32 for fp32 inputs). Keys are permuted inside
 //     a stage so that the accumulator layout of S^T is directly the B operand
@@ -67,7 +68,8 @@ constexpr int kRowSlots = 4;          // row slots per workgroup
 constexpr int kSets = 2;              // key halves (stage parity) per row slot
 constexpr int kWaves = kRowSlots * kSets;
 constexpr int kRingBytes = 128 * 1024;  // ring capacity; at most 3 stage pairs are used
-constexpr int kNonTemporal = 2;       // cache policy of the KV loads: streamed, read once
+constexpr int kNonTemporal = 2;       // cache policy of KV loads read once (streamed)
+constexpr int kTemporal = 0;          // ... and of KV loads the row-group team re-reads from L2
 constexpr int kPageWin = 512;         // stages whose page offsets are staged at once
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
@@ -233,7 +235,7 @@ __device__ __forceinline__ HalfBases half_bases(const char* kbase, const char* v
 // wave r is r + 4 j; its half, hence its page base, is wave-uniform. TAIL:
 // K lanes whose key lies at or past n_keys read zeros instead; V elements past
 // n_keys are zeroed by their reader.
-template <typename T, int D, bool TAIL>
+template <typename T, int D, bool TAIL, int CPOL>
 __device__ __forceinline__ void issue_dma(char* slot, int r, const DmaLanes<T, D>& dl,
                                           const HalfBases& hb, int key0, int n_keys) {
   using SS = StageShape<T, D>;
@@ -244,7 +246,7 @@ __device__ __forceinline__ void issue_dma(char* slot, int r, const DmaLanes<T, D
     const char* src = base + dl.off[j];
     if (TAIL && key0 + dl.key[j] >= n_keys) src = reinterpret_cast<const char*>(g_zero16);
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(slot + p * 1024),
-                                     16, 0, kNonTemporal);
+                                     16, 0, CPOL);
   }
 #pragma unroll
   for (int j = 0; j < SS::VPW; ++j) {
@@ -252,21 +254,29 @@ __device__ __forceinline__ void issue_dma(char* slot, int r, const DmaLanes<T, D
     const char* base = p >= SS::NVP / 2 ? hb.v1 : hb.v0;
     __builtin_amdgcn_global_load_lds(base + dl.off[SS::KPW + j],
                                      (__attribute__((address_space(3))) void*)(slot + (SS::NKP + p) * 1024),
-                                     16, 0, kNonTemporal);
+                                     16, 0, CPOL);
   }
 }
 
 // Issues one stage (when it exists) whose first key is key0; the stage that
-// crosses n_keys takes the zero-filling path.
+// crosses n_keys takes the zero-filling path. A head's keys are streamed once
+// (non-temporal loads) unless its query rows are cut into row groups, whose
+// workgroups run side by side on one XCD and read the same keys: then the
+// loads keep the lines in that XCD's L2 for the other groups (at the
+// draft-pass shape with 128-position blocks, four groups per head, HBM reads
+// 764 -> 712 MB per launch for 701 MB of K, V and Q, same time).
 template <typename T, int D>
 __device__ __forceinline__ void issue_stage(char* slot, int r, const DmaLanes<T, D>& dl,
                                             const HalfBases& hb, int key0, int n_keys,
-                                            bool exists) {
+                                            bool exists, bool shared) {
   if (!exists) return;
-  if (key0 + kStep <= n_keys)
-    issue_dma<T, D, false>(slot, r, dl, hb, key0, n_keys);
-  else
-    issue_dma<T, D, true>(slot, r, dl, hb, key0, n_keys);
+  if (key0 + kStep <= n_keys) {
+    if (shared) issue_dma<T, D, false, kTemporal>(slot, r, dl, hb, key0, n_keys);
+    else issue_dma<T, D, false, kNonTemporal>(slot, r, dl, hb, key0, n_keys);
+  } else {
+    if (shared) issue_dma<T, D, true, kTemporal>(slot, r, dl, hb, key0, n_keys);
+    else issue_dma<T, D, true, kNonTemporal>(slot, r, dl, hb, key0, n_keys);
+  }
 }
 
 // Workgroup barrier for LDS traffic: waits for this wave's LDS operations
@@ -799,7 +809,7 @@ __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const Att
     auto issue = [&](int u, uint4 po) {
       issue_stage<T, D>(s_ring + (u % NSP) * SS::PAIR + set * SS::BYTES, c.rs, c.dl,
                         half_bases(kbase, vbase, po), (w0 + 2 * u + set) * kStep, n_keys,
-                        2 * u + set < ns);
+                        2 * u + set < ns, a.RG > 1);
     };
     // NSP - 1 pairs in flight. Each wave waits for its own DMA share of pair
     // u (vmcnt counts this wave's loads in issue order), the barrier
