@@ -389,34 +389,6 @@ __device__ __forceinline__ void lds_read8_8(intx4* k, intx4* v, unsigned ka, uns
       : "memory");
 }
 
-// The same 8 reads without the wait: the caller waits (s_waitcnt lgkmcnt(0))
-// before it first touches the parts, so their latency overlaps other work.
-__device__ __forceinline__ void lds_read8_nowait(intx4* o, unsigned addr) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:0\n\t"
-      "ds_read_b128 %1, %8 offset:512\n\t"
-      "ds_read_b128 %2, %8 offset:1024\n\t"
-      "ds_read_b128 %3, %8 offset:1536\n\t"
-      "ds_read_b128 %4, %8 offset:2048\n\t"
-      "ds_read_b128 %5, %8 offset:2560\n\t"
-      "ds_read_b128 %6, %8 offset:3072\n\t"
-      "ds_read_b128 %7, %8 offset:3584"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
-        "=&v"(o[6]), "=&v"(o[7])
-      : "v"(addr)
-      : "memory");
-}
-
-// Waits for reads issued by lds_read8_nowait. The parts pass through the
-// wait as operands, so no use of them can be scheduled above it.
-__device__ __forceinline__ void lds_wait8(intx4* o) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]),
-                 "+v"(o[6]), "+v"(o[7])
-               :
-               : "memory");
-}
-
 template <int N>
 __device__ __forceinline__ void lds_read(intx4* o, unsigned addr) {
   static_assert(N == 4 || N == 8 || N == 16, "part counts");
@@ -528,10 +500,7 @@ __device__ __forceinline__ void stage_front(StageRegs<T, D, MT>& st, const WaveS
         c = Frag<T>::mma(frag_of<T>(kp + (t2 * SS::KC + cc) * SS::H), ws.qf[t][cc], c);
       st.s[t2][t] = c;
     }
-  if constexpr (!together) {
-    if constexpr (SS::NVP == 8) lds_read8_nowait(st.vp, vaddr);
-    else lds_read<SS::NVP>(st.vp, vaddr);
-  }
+  if constexpr (!together) lds_read<SS::NVP>(st.vp, vaddr);
   st.key0 = key0;
 }
 
@@ -541,13 +510,7 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
                                            const WideMask& wm) {
   using SS = StageShape<T, D>;
   const int key0 = st.key0;
-  // two row tiles: the front left its V reads in flight (they overlap the
-  // mask and softmax below); wait for them before V is first touched
-  constexpr bool vdefer = MT == 2 && StageShape<T, D>::NVP == 8;
-  if (key0 + kStep > n_keys) {
-    if constexpr (vdefer) lds_wait8(st.vp);
-    zero_v_tail<T, D>(st.vp, key0, n_keys, grp);
-  }
+  if (key0 + kStep > n_keys) zero_v_tail<T, D>(st.vp, key0, n_keys, grp);
 
   if (key0 + kStep > L) {
     // WIDE: bits key0 - L .. key0 - L + 31 of each row's mask, from at most
@@ -623,7 +586,6 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
     ws.l_run[t] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     pf[t] = Frag<T>::pack(pv);
   }
-  if constexpr (vdefer) lds_wait8(st.vp);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
