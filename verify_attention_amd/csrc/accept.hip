@@ -431,22 +431,25 @@ constexpr int kJTreeMask = (1 << kJTreeDepthShift) - 1;
 constexpr int kJTreeTokErr = 1 << 20;
 constexpr int kJTreeErr = 1 << 21;
 static_assert(kMaxTreeNodes <= kJTreeMask + 1, "node ids fit the jbuf fields");
+static_assert(kMaxAcceptVocab <= (1 << (31 - kJTreeDepthShift)), "node | token << 10 fits an int");
 
 __device__ __forceinline__ double wave_exclusive_scan(double x) {
   return wave_inclusive_scan(x) - x;
 }
 
-// Lane l's nodes l + 64 c: parent and token (loaded once, shared by the walk
-// and the excluded set).
+// Lane l's nodes l + 64 c, c < NC: parent and token (loaded once, shared by
+// the walk and the excluded set). NC = 1 for trees of at most 64 nodes.
+template <int NC>
 struct TreeNodes {
-  int par[kTreeChunks], tok[kTreeChunks];
+  int par[NC], tok[NC];
 };
 
-__device__ __forceinline__ TreeNodes tree_nodes(const AcceptArgs& a, int b) {
+template <int NC>
+__device__ __forceinline__ TreeNodes<NC> tree_nodes(const AcceptArgs& a, int b) {
   const int N = a.K, lane = threadIdx.x & 63;
-  TreeNodes t;
+  TreeNodes<NC> t;
 #pragma unroll
-  for (int c = 0; c < kTreeChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int n = c * 64 + lane;
     const bool in = n < N;
     t.par[c] = in ? a.parent[(size_t)b * N + n] : -2;
@@ -455,18 +458,20 @@ __device__ __forceinline__ TreeNodes tree_nodes(const AcceptArgs& a, int b) {
   return t;
 }
 
-// Wave 0 only. path[] (LDS) receives the accepted node ids; sib[] (LDS, N
-// entries) is scratch for the tokens of the children already tried.
-__device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes& nd, int* path,
+// Wave 0 only. path[] (LDS) receives the accepted nodes as node | token << 10
+// (accepted tokens are valid ids, V <= 2^19); sib[] (LDS, N entries) is
+// scratch for the tokens of the children already tried.
+template <int NC>
+__device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes<NC>& nd, int* path,
                               int* sib) {
   const int N = a.K, V = a.V;
   const int lane = threadIdx.x & 63, nch = (N + 63) >> 6;
   const uint64_t below = (1ull << lane) - 1;
-  double un[kTreeChunks], pv[kTreeChunks];
-  bool vpar[kTreeChunks], vtok[kTreeChunks];
+  double un[NC], pv[NC];
+  bool vpar[NC], vtok[NC];
   TreeWalk w{0, 0, 0};
 #pragma unroll
-  for (int c = 0; c < kTreeChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int n = c * 64 + lane;
     const bool in = n < N;
     const int par = nd.par[c], tok = nd.tok[c];
@@ -478,9 +483,9 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes& nd, i
   }
   for (int level = 0; level < N; ++level) {
     double T0 = 0.0;  // mass of the distinct tokens tried in earlier chunks
-    int nsib = 0, next = -1;
+    int nsib = 0, next = -1, ntok = 0;
 #pragma unroll
-    for (int c = 0; c < kTreeChunks; ++c) {
+    for (int c = 0; c < NC; ++c) {
       // children come after their parent: chunks before x's hold none
       if (c >= nch || c < (w.x + 1) >> 6) continue;
       const bool kid = vpar[c] && nd.par[c] == w.x;
@@ -494,7 +499,8 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes& nd, i
         const int tk = __builtin_amdgcn_readlane(tok, k);  // k is wave-uniform
         dup |= kid && lane > k && tk == tok;
       }
-      for (int i = 0; i < nsib; ++i) dup |= kid && sib[i] == tok;
+      if constexpr (NC > 1)
+        for (int i = 0; i < nsib; ++i) dup |= kid && sib[i] == tok;
       const double pres = (kid && vtok[c] && !dup) ? pv[c] : 0.0;
       const double incl = wave_inclusive_scan(pres);
       const double T = T0 + (incl - pres);
@@ -504,15 +510,18 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes& nd, i
       if (__builtin_amdgcn_ballot_w64(kid && !vtok[c] && lane < limit)) w.errs |= kErrToken;
       if (accm) {
         next = c * 64 + limit;
+        ntok = __builtin_amdgcn_readlane(tok, limit);  // limit is wave-uniform
         break;
       }
-      T0 += __shfl(incl, 63, 64);
-      if (kid) sib[nsib + __builtin_popcountll(kids & below)] = tok;
-      nsib += __builtin_popcountll(kids);
+      if constexpr (NC > 1) {
+        T0 += __shfl(incl, 63, 64);
+        if (kid) sib[nsib + __builtin_popcountll(kids & below)] = tok;
+        nsib += __builtin_popcountll(kids);
+      }
     }
     if (next < 0) break;
     w.x = next;
-    if (lane == 0) path[w.depth] = next;
+    if (lane == 0) path[w.depth] = next | (ntok << kJTreeDepthShift);
     ++w.depth;
   }
   return w;
@@ -520,13 +529,14 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes& nd, i
 
 // The final node's children tokens (valid ids) into excl[] in node order;
 // returns the count. Wave 0 only.
-__device__ int tree_excluded(const AcceptArgs& a, const TreeNodes& nd, int x, int* excl) {
+template <int NC>
+__device__ int tree_excluded(const AcceptArgs& a, const TreeNodes<NC>& nd, int x, int* excl) {
   const int N = a.K, V = a.V;
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1;
   int cnt = 0;
 #pragma unroll
-  for (int c = 0; c < kTreeChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int n = c * 64 + lane;
     const int par = nd.par[c], tok = nd.tok[c];
     const bool ex = n < N && n >= 1 && par == x && par < n && tok >= 0 && tok < V;
@@ -539,6 +549,7 @@ __device__ int tree_excluded(const AcceptArgs& a, const TreeNodes& nd, int x, in
 
 // Kernel 1, one workgroup per (request, vocabulary chunk): the walk, then
 // the residual mass of every 256-entry sub-block of the chunk.
+template <int NC>
 __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(AcceptArgs a) {
   const int b = blockIdx.x / a.nchunk;
   const int c = blockIdx.x - b * a.nchunk;
@@ -548,8 +559,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(Accept
   __shared__ int s_sib[kMaxTreeNodes];
   __shared__ int s_x, s_nex, s_nf;
   if (wave == 0) {
-    const TreeNodes nd = tree_nodes(a, b);
-    const TreeWalk w = tree_walk(a, b, nd, s_path, s_sib);
+    const TreeNodes<NC> nd = tree_nodes<NC>(a, b);
+    const TreeWalk w = tree_walk<NC>(a, b, nd, s_path, s_sib);
     const int nex = tree_excluded(a, nd, w.x, s_excl);
     if (lane == 0) {
       s_x = w.x;
@@ -559,7 +570,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(Accept
                     ((w.errs & kErrToken) ? kJTreeTokErr : 0) |
                     ((w.errs & kErrTree) ? kJTreeErr : 0);
     }
-    // the accepted nodes for the select and the commit
+    // the accepted nodes (node | token << 10) for the select and the commit
     if (c == 0)
       for (int k = lane; k < w.depth; k += 64) a.pathbuf[(size_t)b * N + k] = s_path[k];
   }
@@ -589,6 +600,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree_partial_kernel(Accept
 
 // Kernel 2, request b: the bonus from the sub-block masses, then every
 // output (all threads of the workgroup).
+template <int NC>
 __device__ void tree_select(const AcceptArgs& a, int b) {
   const int N = a.K, V = a.V;
   const int tid = threadIdx.x;
@@ -609,7 +621,7 @@ __device__ void tree_select(const AcceptArgs& a, int b) {
   const int jw = a.jbuf[b];
   const int x = jw & kJTreeMask, depth = (jw >> kJTreeDepthShift) & kJTreeMask;
   if (tid < 64) {
-    const int nex = tree_excluded(a, tree_nodes(a, b), x, s_excl);
+    const int nex = tree_excluded<NC>(a, tree_nodes<NC>(a, b), x, s_excl);
     if (tid == 0) s_nex = nex;
   }
   __syncthreads();
@@ -643,10 +655,9 @@ __device__ void tree_select(const AcceptArgs& a, int b) {
     a.new_seq_lens[b] = L + depth + 1;
   }
   for (int t = tid; t < N; t += kAccThreads) {
-    const int node = t < depth ? a.pathbuf[(size_t)b * N + t] : -1;
-    a.path_nodes[(size_t)b * N + t] = node;
-    a.out_tokens[(size_t)b * N + t] =
-        t < depth ? a.token[(size_t)b * N + node] : (t == depth ? tok : -1);
+    const int pw = t < depth ? a.pathbuf[(size_t)b * N + t] : -1;
+    a.path_nodes[(size_t)b * N + t] = pw < 0 ? -1 : pw & kJTreeMask;
+    a.out_tokens[(size_t)b * N + t] = pw >= 0 ? pw >> kJTreeDepthShift : (t == depth ? tok : -1);
   }
   if (tid == 0 && errs) flag_error(a.err, errs);
 }
@@ -666,7 +677,8 @@ __device__ void tree_commit_head(const AcceptArgs& a, int b, int h) {
   const int d = cap_ok ? (a.jbuf[b] >> kJTreeDepthShift) & kJTreeMask : -1;
   if (tid == 0) s_cerr = cap_ok ? 0 : kErrCapacity;  // published by the barrier below
   const int32_t* path = a.pathbuf + (size_t)b * N;
-  bool bad = commit_row_bases(rows, [&](int k) { return path[k]; }, tab, P, a.commit_D,
+  bool bad = commit_row_bases(rows, [&](int k) { return path[k] & kJTreeMask; }, tab, P,
+                              a.commit_D,
                               a.commit_Hkv, a.commit_num_pages, h, L, d);
   commit_move_rows<KVT>(rows, reinterpret_cast<KVT*>(a.commit_k),
                         reinterpret_cast<KVT*>(a.commit_v), P, a.commit_D, d);
@@ -680,29 +692,37 @@ __device__ void tree_commit_head(const AcceptArgs& a, int b, int h) {
 // Kernel 2, one workgroup per request; with the commit, Hkv + 1 per request:
 // workgroup h < Hkv commits KV head h while the last one draws the bonus and
 // writes the accept's outputs, side by side.
-template <bool COMMIT, typename KVT>
+template <bool COMMIT, typename KVT, int NC>
 __global__ __launch_bounds__(kAccThreads) void accept_tree_select_kernel(AcceptArgs a) {
   const int H1 = COMMIT ? a.commit_Hkv + 1 : 1;
   const int b = blockIdx.x / H1, h = blockIdx.x - b * H1;
-  if (h == H1 - 1) tree_select(a, b);
+  if (h == H1 - 1) tree_select<NC>(a, b);
   else if constexpr (COMMIT) tree_commit_head<KVT>(a, b, h);
 }
 
-hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_tree_partial_kernel, dim3(a.bs * a.nchunk), dim3(kAccThreads), 0,
+template <int NC>
+static hipError_t launch_accept_tree_nc(const AcceptArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_tree_partial_kernel<NC>, dim3(a.bs * a.nchunk), dim3(kAccThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 block(kAccThreads);
   if (!a.commit_k)
-    hipLaunchKernelGGL((accept_tree_select_kernel<false, float>), dim3(a.bs), block, 0, stream, a);
+    hipLaunchKernelGGL((accept_tree_select_kernel<false, float, NC>), dim3(a.bs), block, 0, stream,
+                       a);
   else if (a.commit_bf16)
-    hipLaunchKernelGGL((accept_tree_select_kernel<true, __bf16>), dim3(a.bs * (a.commit_Hkv + 1)),
-                       block, 0, stream, a);
+    hipLaunchKernelGGL((accept_tree_select_kernel<true, __bf16, NC>),
+                       dim3(a.bs * (a.commit_Hkv + 1)), block, 0, stream, a);
   else
-    hipLaunchKernelGGL((accept_tree_select_kernel<true, float>), dim3(a.bs * (a.commit_Hkv + 1)),
-                       block, 0, stream, a);
+    hipLaunchKernelGGL((accept_tree_select_kernel<true, float, NC>),
+                       dim3(a.bs * (a.commit_Hkv + 1)), block, 0, stream, a);
   return hipGetLastError();
+}
+
+// Trees of at most 64 nodes take the one-chunk walk (one node per lane).
+hipError_t launch_accept_tree(const AcceptArgs& a, hipStream_t stream) {
+  return a.K <= 64 ? launch_accept_tree_nc<1>(a, stream)
+                   : launch_accept_tree_nc<kTreeChunks>(a, stream);
 }
 
 // ----------------------------------------------------------------- argmax
