@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
   const int32_t* tab = a.page_table + (size_t)b * a.max_pages;
   SPEC_COMMIT_ROWS(rows);
   __shared__ int s_path[kMaxCommitRows];
-  __shared__ int s_err;
+  __shared__ int s_err, s_bad;
   // the length and depth (every thread), the path entries into LDS, then
   // the path check: node p_k has depth k + 1, so k + 1 <= p_k < B, increasing
   const int L = a.seq_lens[b];
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
   }
   for (int k = tid; k < d; k += kCommitThreads)
     s_path[k] = a.path ? a.path[(size_t)b * B + k] : k + 1;
-  if (tid == 0) s_err = 0;
+  if (tid == 0) s_err = s_bad = 0;
   __syncthreads();
   bool bad = false;
   if (a.path)
@@ -50,19 +50,16 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kv_kernel(CommitArgs a)
       const int p = s_path[k];
       bad |= p < k + 1 || p >= B || (k > 0 && p <= s_path[k - 1]);
     }
-  if (__syncthreads_or(bad)) {
+  if (block_any(bad, &s_bad)) {
     err = kErrTree;
     d = -1;
   }
-  if (commit_row_bases(rows, [&](int k) { return s_path[k]; }, tab, P, a.D, a.Hkv, a.num_pages,
-                       h, L, d))
-    err |= kErrSlot;
+  bool bad_slot = commit_row_bases(rows, [&](int k) { return s_path[k]; }, tab, P, a.D, a.Hkv,
+                                   a.num_pages, h, L, d);
   commit_move_rows<T>(rows, reinterpret_cast<T*>(a.k), reinterpret_cast<T*>(a.v), P, a.D, d);
-  if (h == 0) {
-    if (commit_freed(a.freed + (size_t)b * B, tab, P, B, a.num_pages, L, d))
-      atomicOr(&s_err, kErrSlot);
-    __syncthreads();
-  }
+  if (h == 0) bad_slot |= commit_freed(a.freed + (size_t)b * B, tab, P, B, a.num_pages, L, d);
+  if (bad_slot) atomicOr(&s_err, kErrSlot);
+  __syncthreads();
   if (tid == 0 && (err | s_err)) flag_error(a.err, err | s_err);
 }
 

@@ -32,11 +32,20 @@ struct CommitRows {
       name##_vs[kMaxCommitRows], name##_vd[kMaxCommitRows];                    \
   const CommitRows name{name##_ks, name##_kd, name##_vs, name##_vd}
 
+// Whether p holds on any thread of the workgroup (every thread calls it):
+// one LDS atomic per wave whose ballot is not empty. flag is an LDS int
+// cleared before a barrier that precedes the call; ends with a barrier.
+__device__ __forceinline__ bool block_any(bool p, int* flag) {
+  if (__builtin_amdgcn_ballot_w64(p) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+  __syncthreads();
+  return *flag != 0;
+}
+
 // Every thread of the workgroup: rows k = tid, tid + kCommitThreads, ... below
 // d look up the pages of row k's source L + path(k) and destination L + 1 + k.
-// Ends with a barrier (which publishes the row bases) and returns, on every
-// thread, whether a page id lay outside [0, num_pages) (those rows stay in
-// place).
+// Ends with a barrier (which publishes the row bases) and returns whether a
+// page id of this thread's rows lay outside [0, num_pages) (those rows stay
+// in place).
 template <typename PathFn>
 __device__ __forceinline__ bool commit_row_bases(const CommitRows& s, PathFn path,
                                                  const int32_t* tab, int P, int D, int Hkv,
@@ -62,7 +71,8 @@ __device__ __forceinline__ bool commit_row_bases(const CommitRows& s, PathFn pat
     s.vsrc[k] = vs;
     s.vdst[k] = vd;
   }
-  return __syncthreads_or(bad) != 0;
+  __syncthreads();
+  return bad;
 }
 
 // Every thread of the workgroup, in rounds of kCommitThreads * kCommitPer / D
