@@ -317,10 +317,7 @@ def main():
         step_bytes += handoff_alg_bytes(cfg)
     copies = args.copies or max(2, int(np.ceil(768e6 / step_bytes)))
     sets = []
-    for c in range(copies):
-        if c:   # further copies are cloned on the device (no second upload)
-            sets.append({k: t.clone() for k, t in sets[0].items()})
-            continue
+    for _ in range(copies):
         s = dict(q=up(x.q), k=up(x.k_pool), v=up(x.v_pool))
         if acc is not None:
             s.update(p=up(acc.p), qd=up(acc.q), u=up(acc.u), draft=up(acc.draft))
