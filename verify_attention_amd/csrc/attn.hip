@@ -593,6 +593,29 @@ __device__ __forceinline__ void stage_back(StageRegs<T, D, MT>& st, WaveState<T,
       ws.acc[dt][t] = Frag<T>::mma(frag_of<T>(st.vp + dt * SS::H), pf[t], ws.acc[dt][t]);
 }
 
+// WIDE: whether none of the wave's rows sees a key of the stage starting at
+// key0, which lies wholly inside the block (the window test of stage_back,
+// over the wave's rows; padding rows read a neighbour's words, so the answer
+// errs on the side of computing). Such a stage changes no running state
+// (every score is -inf: the maximum, the row sum and the output stay as they
+// are), so the wave skips its products.
+template <typename T, int D, int MT>
+__device__ __forceinline__ bool wide_stage_masked(const WaveState<T, D, MT>& ws,
+                                                  const WideMask& wm, int key0, int L) {
+  if (key0 < L) return false;
+  const int jb0 = key0 - L, wi = jb0 >> 6, sh = jb0 & 63;
+  uint32_t any = 0;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int ic = min(max(ws.blk_row[t], wm.ibase), wm.ilast) - wm.ibase;
+    const uint64_t* row = wm.rows + ic * wm.W;
+    const uint64_t lo = wi < wm.W ? row[wi] : 0;
+    const uint64_t hi = wi + 1 < wm.W ? row[wi + 1] : 0;
+    any |= (uint32_t)(sh ? (lo >> sh) | (hi << (64 - sh)) : lo);
+  }
+  return __builtin_amdgcn_ballot_w64(any != 0) == 0;
+}
+
 // Per-wave constants of the stage pipeline.
 template <typename T, int D>
 struct WaveCtx {
@@ -800,7 +823,9 @@ __device__ __forceinline__ void stream_stages(WaveState<T, D, MT>& ws, const Att
         pending = false;
         if (more && set == 1) issue(u + NSP - 1, po_next);
         const int t = 2 * u + set;
-        if (t < ns) {
+        bool skip = false;
+        if constexpr (WIDE) skip = t < ns && wide_stage_masked(ws, wm, (w0 + t) * kStep, L);
+        if (t < ns && !skip) {
           const unsigned so = (u % NSP) * SS::PAIR;
           stage_front<T, D, MT>(st, ws, c.k_lane + so, c.v_lane + so, (w0 + t) * kStep);
           if (set == 0) stage_back<T, D, MT, WIDE>(st, ws, a, L, n_keys, nc, c.grp, wm);
