@@ -203,7 +203,8 @@ def cpu_baseline(cfg, x, seconds, gpu, masks=None, acc=None, tacc=None, lacc=Non
     while done < cfg.bs:
         b = int(order[done])
         one = _sample_inputs(x, [b])
-        tree = None if masks is None else (masks if masks.ndim == 1 else masks[b:b + 1])
+        shared = masks is not None and (masks.ndim == 1 or (masks.ndim == 3 and len(masks) == 1))
+        tree = None if masks is None else (masks if shared else masks[b:b + 1])
         ro, _ = oracle.block_attn_dense(one.as_f64("q"), one.as_f64("k_pool"),
                                         one.as_f64("v_pool"), one.page_table, one.seq_lens, mode,
                                         cfg.n_causal, tree=tree)
@@ -462,7 +463,13 @@ def main():
     gpu = {}
     if not (tree or quad):
         o_last = o.float().cpu().numpy().astype(np.float64)
-        gpu["o"] = lambda b: o_last[b]
+    else:
+        # the step's commit moved rows inside the cycled pools: the check's
+        # attention runs once more, untimed, over a fresh copy of the inputs
+        o_chk = va.block_attn_tree(tmask, sets[0]["q"], up(x.k_pool), up(x.v_pool), table, seq,
+                                   max_kv)
+        o_last = o_chk.float().cpu().numpy().astype(np.float64)
+    gpu["o"] = lambda b: o_last[b]
     if acc_out is not None:
         snap = {k: v.cpu().numpy() for k, v in acc_out.items()}
         gpu["accept"] = lambda b: {k: v[b] for k, v in snap.items()}
