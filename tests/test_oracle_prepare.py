@@ -83,7 +83,7 @@ def test_tree_golden():
     assert ids.tolist() == e["block_ids_mask_fill"]
 
 
-@pytest.mark.parametrize("B,seed", [(1, 0), (8, 1), (16, 2), (64, 3)])
+@pytest.mark.parametrize("B,seed", [(1, 0), (8, 1), (16, 2), (64, 3), (300, 4)])
 def test_chain_tree_is_the_linear_block(B, seed):
     """A chain (parent n - 1) is a linear block: ids, positions and slots
     equal spec_prepare_block's, for both passes."""
@@ -113,11 +113,11 @@ def test_tree_positions_are_root_path_lengths():
     counted by walking up), for random trees; siblings share a position."""
     from verify_attention_amd import synth
     rng = np.random.default_rng(5)
-    for _ in range(20):
-        N = int(rng.integers(2, 65))
+    for i in range(20):
+        N = int(rng.integers(2, 65)) if i % 4 else int(rng.integers(65, 513))
         par = synth.random_tree_parents(rng, N, int(rng.integers(2, N + 1)))
         _, pos, _, err = oracle.prepare_tree(np.zeros(1), np.array([1000]),
-                                             np.arange(80)[None, :], 16, par, 0)
+                                             np.arange(160)[None, :], 16, par, 0)
         assert err == 0
         for n in range(N):
             up, x = 0, n
@@ -146,12 +146,12 @@ def test_quadratic_positions():
     m of the group after spine token j at L + j + 1 + m (the role table of the
     layout, built separately, names every position)."""
     from verify_attention_amd import synth
-    for k in (1, 2, 4, 7):
+    for k in (1, 2, 4, 7, 15, 21):
         roles, _ = synth.quadratic_layout(k)
         par = synth.quadratic_parents(k)
         n = (k + 1) ** 2
         _, pos, _, err = oracle.prepare_tree(np.zeros(1), np.array([50]),
-                                             np.arange(8)[None, :], 32, par, 0)
+                                             np.arange(20)[None, :], 32, par, 0)
         assert err == 0
         for p_, (kind, j, m) in enumerate(roles):
             assert pos[0, p_] == (50 + j if kind == "spine" else 50 + j + 1 + m)

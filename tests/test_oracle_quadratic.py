@@ -26,7 +26,7 @@ def test_handoff_golden():
         assert block.tolist() == c["next_block"]
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 7, 8, 15])
 def test_handoff_reads_the_group_the_role_table_names(k):
     """For every accept length a, the drafts are the greedy tokens of the
     rows whose layout role is (mask, group a, member m), in member order;
@@ -62,7 +62,7 @@ def test_handoff_ties_and_range():
     assert nxt.tolist() == [-1] * k and block is None
 
 
-@pytest.mark.parametrize("k,seed", [(2, 0), (4, 1), (7, 2)])
+@pytest.mark.parametrize("k,seed", [(2, 0), (4, 1), (7, 2), (9, 3)])
 def test_spine_compaction_keeps_the_causal_view(k, seed):
     """After the accept of a spine drafts, the commit with path
     p_i = i (k + 1) makes the accepted spine contiguous: the last accepted
