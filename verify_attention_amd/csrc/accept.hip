@@ -467,6 +467,10 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes<NC>& n
   const int N = a.K, V = a.V;
   const int lane = threadIdx.x & 63, nch = (N + 63) >> 6;
   const uint64_t below = (1ull << lane) - 1;
+  // one chunk: every p[parent(n)][token(n)] gathered at once; more chunks:
+  // gathered per level, only for the children of the current node (one row,
+  // where the up-front gather of every node would touch N rows per
+  // workgroup)
   double un[NC], pv[NC];
   bool vpar[NC], vtok[NC];
   TreeWalk w{0, 0, 0};
@@ -478,7 +482,8 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes<NC>& n
     un[c] = in ? (double)a.u[(size_t)b * N + n] : 0.0;
     vpar[c] = in && n >= 1 && par >= 0 && par < n;
     vtok[c] = tok >= 0 && tok < V;
-    pv[c] = (vpar[c] && vtok[c]) ? (double)a.p[((size_t)b * N + par) * V + tok] : 0.0;
+    if constexpr (NC == 1)
+      pv[c] = (vpar[c] && vtok[c]) ? (double)a.p[((size_t)b * N + par) * V + tok] : 0.0;
     if (__builtin_amdgcn_ballot_w64(in && n >= 1 && !vpar[c])) w.errs |= kErrTree;
   }
   for (int level = 0; level < N; ++level) {
@@ -499,8 +504,10 @@ __device__ TreeWalk tree_walk(const AcceptArgs& a, int b, const TreeNodes<NC>& n
         const int tk = __builtin_amdgcn_readlane(tok, k);  // k is wave-uniform
         dup |= kid && lane > k && tk == tok;
       }
-      if constexpr (NC > 1)
+      if constexpr (NC > 1) {
         for (int i = 0; i < nsib; ++i) dup |= kid && sib[i] == tok;
+        pv[c] = (kid && vtok[c]) ? (double)a.p[((size_t)b * N + w.x) * V + tok] : 0.0;
+      }
       const double pres = (kid && vtok[c] && !dup) ? pv[c] : 0.0;
       const double incl = wave_inclusive_scan(pres);
       const double T = T0 + (incl - pres);
