@@ -274,6 +274,28 @@ def test_tree_chain_is_bitwise_causal(gpu_lib):
     assert np.array_equal(o_t, o_c) and np.array_equal(l_t, l_c)
 
 
+@pytest.mark.parametrize("B", [127, 128, 129, 256, 257])
+def test_tree_mask_word_boundaries(gpu_lib, B):
+    """Blocks at and around mask-word boundaries (W = 2, 3, 4, 5), random
+    per-request trees and a chain: every row against the dense reference,
+    the chain also bitwise equal to CAUSAL."""
+    cfg = synth.config(6, bs=2, hq=4, hkv=2, d=64, block=B, tree_depth=B // 3, ctx_lo=5,
+                       ctx_hi=90)
+    print_case("block_attn_tree word boundaries", B)
+    x = synth.make_attn_inputs(cfg, seed=B)
+    case = AttnCase(x)
+    _, masks = synth.make_trees(cfg, B)
+    o, lse = run_tree(case, masks)
+    ro, rl = oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                     x.page_table, x.seq_lens, oracle.TREE, 0, tree=masks)
+    assert np.max(np.abs(o - ro)) <= TOL[cfg.dtype]
+    assert np.max(np.abs(lse - rl)) <= LSE_TOL[cfg.dtype]
+    chain = synth.tree_row_words(np.arange(-1, B - 1, dtype=np.int32))
+    o_t, l_t = run_tree(case, chain)
+    o_c, l_c = run(case, synth.CAUSAL)
+    assert np.array_equal(o_t, o_c) and np.array_equal(l_t, l_c)
+
+
 def test_wide_chain_tree_is_bitwise_causal(gpu_lib):
     """A chain of 150 nodes (three mask words per row, read from LDS) gives
     the causal mask's outputs bit for bit; both take the split schedule."""
