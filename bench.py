@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference leg")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as HIP graph replays (one graph per input copy)")
     ap.add_argument("--event-steps", type=int, default=24,
                     help="steps at the end of the warm-up (right before the timed region) with "
                          "HIP events recorded on the launch stream around every call, for the "
@@ -351,25 +353,28 @@ def main():
                                                                cfg.sampling[1]))
     if acc is not None:
         ws_acc = va.workspace(va.accept_workspace_bytes(bs, cfg.k_spec, cfg.vocab))
-    # every call is checked once; the timed loop re-enqueues pre-marshalled calls
+    # every call is checked once; the timed loop re-enqueues pre-marshalled
+    # calls, all on one stream of their own (which a graph capture can use)
+    rs = torch.cuda.Stream(device=dev)
     calls = []      # per step: list of (name, [enqueue per input copy])
     acc_out = None
     if tree or quad:
         if tree:  # a quadratic round's block is prepared by the previous round's accept
             calls.append(("spec_prepare_tree", [va.prepare_tree_call(
                 vid, seq, table, cfg.page, tpar, MASK_TOKEN, x.num_pages, ttok,
-                out=prep_out, err=err)[0]] * copies))
+                out=prep_out, err=err, stream=rs)[0]] * copies))
         calls.append(("block_attn_tree", [va.block_attn_tree_call(
             tmask, s["q"], s["k"], s["v"], table, seq, max_kv, out=o, ws=ws_attn,
-            err=err)[0] for s in sets]))
+            err=err, stream=rs)[0] for s in sets]))
     else:
         if acc is None:   # the draft pass and the logits verify prepare their own block
             calls.append(("spec_prepare_block", [va.prepare_block_call(
                 vid, seq, table, cfg.page, B, MASK_TOKEN, x.num_pages,
-                None if mode == synth.BIDIR else dr, out=prep_out, err=err)[0]] * copies))
+                None if mode == synth.BIDIR else dr, out=prep_out, err=err,
+                stream=rs)[0]] * copies))
         calls.append(("block_attn", [va.block_attn_call(
             mode, s["q"], s["k"], s["v"], table, seq, max_kv, n_causal=cfg.n_causal, out=o,
-            ws=ws_attn, err=err)[0] for s in sets]))
+            ws=ws_attn, err=err, stream=rs)[0] for s in sets]))
     if tree:
         lst = []
         for s in sets:
@@ -377,7 +382,7 @@ def main():
             # prefix of the cache in the same call
             c, acc_out = va.accept_tree_commit_call(tpar, ttok, s["p"], s["u"], seq, s["k"],
                                                     s["v"], table, out=acc_out, ws=ws_tacc,
-                                                    err=err)
+                                                    err=err, stream=rs)
             lst.append(c)
         calls.append(("spec_accept_tree_commit", lst))
     elif quad:
@@ -387,7 +392,7 @@ def main():
             c, acc_out = va.accept_quadratic_call(s["p"], s["qd"], s["draft"], s["u"], seq,
                                                   s["qlogits"], s["k"], s["v"], table,
                                                   MASK_TOKEN, prepare_next=True, out=acc_out,
-                                                  ws=ws_q, err=err)
+                                                  ws=ws_q, err=err, stream=rs)
             lst.append(c)
         calls.append(("spec_accept_quadratic", lst))
     elif acc is not None:
@@ -395,21 +400,24 @@ def main():
         for s in sets:
             c, acc_out = va.accept_prepare_call(s["p"], s["qd"], s["draft"], s["u"], seq, table,
                                                 cfg.page, B, MASK_TOKEN, x.num_pages,
-                                                out=acc_out, ws=ws_acc, err=err)
+                                                out=acc_out, ws=ws_acc, err=err, stream=rs)
             lst.append(c)
         calls.append(("spec_accept_prepare", lst))
     elif lacc is not None:
         lst = []
         for s in sets:
             c, acc_out = va.accept_logits_call(s["tl"], s["dl"], s["draft"], s["u"], seq,
-                                               *cfg.sampling, out=acc_out, ws=ws_acc, err=err)
+                                               *cfg.sampling, out=acc_out, ws=ws_acc, err=err,
+                                               stream=rs)
             lst.append(c)
         calls.append(("spec_accept_logits", lst))
     elif logits is not None:
         tokens = torch.empty(logits.shape[0], dtype=torch.int32, device=dev)
-        calls.append(("spec_draft_argmax", [va.draft_argmax_call(s["logits"], out=tokens)[0]
+        calls.append(("spec_draft_argmax", [va.draft_argmax_call(s["logits"], out=tokens,
+                                                                 stream=rs)[0]
                                             for s in sets]))
-    stream = torch.cuda.current_stream()
+    stream = rs
+    torch.cuda.synchronize()
 
     def step(i, ev=None):
         for c, (_, fns) in enumerate(calls):
@@ -452,9 +460,25 @@ def main():
     for c, (name, _) in enumerate(calls):
         per_call_us[name] = float(np.mean([e[c].elapsed_time(e[c + 1]) for e in evs]) * 1e3)
     torch.cuda.synchronize()
+    graphs = []
+    if args.graph:
+        # one HIP graph per input copy, captured on the calls' own stream (the
+        # library allocates, clears and synchronises nothing), then replayed
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=rs):
+                for _, fns in calls:
+                    fns[c]()
+            graphs.append(g)
+        for i in range(2 * copies):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if int(err.item()) != 0:
@@ -554,7 +578,7 @@ def main():
                    "head_dim": cfg.d, "page": cfg.page, "mode": synth.MODE_NAMES[mode],
                    "ctx": [cfg.ctx_lo, cfg.ctx_hi], "vocab": cfg.vocab or cfg.argmax_vocab,
                    "k_spec": cfg.k_spec, "input_copies": copies,
-                   "step": [n for n, _ in calls],
+                   "step": [n for n, _ in calls], "launch": "hip_graph" if graphs else "eager",
                    **({"layout": f"quadratic, k = {cfg.quad_k}",
                        "verified_tokens_per_request": cfg.quad_k + 1} if quad else {})},
         "roofline": roofline(dominant),
