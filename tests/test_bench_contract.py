@@ -42,6 +42,14 @@ def test_attention_bytes_and_flops_by_hand():
     masks = np.array([0b1, 0b11, 0b101, 0b1011], dtype=np.uint64)
     assert bench.attn_alg_bytes_flops(ct, seq, masks)[1] == \
         4 * 8 * sum(L * 4 + 1 + 2 + 2 + 3 for L in (3, 5)) * 4
+    # trees past 64 nodes: mask words per row ([bs, B, W]); a 70-node chain
+    # per request sees 1 + 2 + ... + 70 block pairs
+    cw = synth.config(2, bs=2, block=70, hq=4, hkv=2, d=8, modes=(synth.TREE,))
+    chain = synth.tree_row_words(np.arange(-1, 69, dtype=np.int32))
+    words = np.stack([chain, chain])
+    assert words.shape == (2, 70, 2)
+    assert bench.attn_alg_bytes_flops(cw, seq, words)[1] == \
+        4 * 8 * sum(L * 70 + 70 * 71 // 2 for L in (3, 5)) * 4
 
 
 def test_accept_bytes_by_hand():
