@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, help="round configuration 1..9")
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, help="round configuration 1..11")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="the warm-up runs at least this long (after the W steps)")
@@ -109,7 +109,8 @@ def attn_alg_bytes_flops(cfg, seq_lens, tree_masks=None):
         intra = cfg.bs * int(np.where(i < nc, i + 1, B).sum())
     else:
         m = np.asarray(tree_masks)
-        intra = sum(bin(int(v)).count("1") for v in m.ravel()) * (cfg.bs if m.ndim == 1 else 1)
+        shared = m.ndim == 1 or (m.ndim == 3 and len(m) == 1)   # one tree for the batch
+        intra = sum(bin(int(v)).count("1") for v in m.ravel()) * (cfg.bs if shared else 1)
     pairs = (seq_lens.astype(np.int64) * B).sum() + intra
     flops = 4 * cfg.d * pairs * cfg.hq
     return int(kv + qo), int(flops)
@@ -343,7 +344,10 @@ def main():
     prep_out = tuple(torch.empty((bs, B), dtype=torch.int32, device=dev) for _ in range(3))
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     if tree or quad:
-        tmask = torch.from_numpy(masks.view(np.int64)).to(dev)
+        # one shared tree of mask words, [1, B, W], goes to the call as [B, W]
+        shared_words = masks.ndim == 3 and len(masks) == 1 and bs > 1
+        tmask = torch.from_numpy(np.ascontiguousarray(masks[0] if shared_words else masks)
+                                 .view(np.int64)).to(dev)
         tpar = up(np.ascontiguousarray(parents, dtype=np.int32))
     if tree:
         ttok = up(tacc.token)

@@ -392,7 +392,7 @@ def test_quadratic_layout_all_rows(gpu_lib, name, over):
     assert np.max(np.abs(lse - rl)) <= LSE_TOL[cfg.dtype]
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 8, 9, 10])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 8, 9, 10, 11])
 def test_full_size_sampled_rows(gpu_lib, cid):
     """Full workload shapes in the bench's launch configuration; the reference
     computes sampled rows one at a time."""

@@ -85,6 +85,10 @@ class RoundConfig:
 #    length, so a beam-shaped tree of 1 + 15 * 32 = 481 nodes (8 mask words a
 #    row; g * B = 1924 query rows per KV head); the Qwen3-8B-shaped verify of
 #    6 otherwise, at 8 requests
+# 11 the quadratic layout of 8 at the verify's own block of 16: k = 15
+#    drafts and a group of 15 MASK tokens after the root and after every
+#    draft, 256 positions (4 mask words a row, g * B = 1024 query rows per KV
+#    head)
 CONFIGS = {
     1: RoundConfig("tiny_f32", bs=1, hq=2, hkv=1, d=64, page=16, block=8,
                    modes=(BIDIR, CAUSAL), dtype="f32", ctx_lo=256, ctx_hi=256,
@@ -119,6 +123,9 @@ CONFIGS = {
                     block=481, modes=(TREE,), dtype="bf16", ctx_lo=1024, ctx_hi=1024,
                     tree_depth=15, tree_width=32, vocab=151936, k_spec=480,
                     logit_sigma=6.0, q_noise_sigma=0.5),
+    11: RoundConfig("quadratic_k15_verify_bs32", bs=32, hq=32, hkv=8, d=128, page=16,
+                    block=256, modes=(TREE,), dtype="bf16", ctx_lo=1024, ctx_hi=1024,
+                    vocab=151936, k_spec=15, logit_sigma=3.0, q_noise_sigma=0.5, quad_k=15),
     9: RoundConfig("draft_bidir_b128_bs64", bs=64, hq=16, hkv=4, d=128, page=32,
                    block=128, modes=(BIDIR,), dtype="bf16", ctx_lo=1024, ctx_hi=9216),
 }
