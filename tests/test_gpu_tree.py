@@ -74,13 +74,18 @@ def test_tree_accept_small_vocab_many_requests(gpu_lib, N, V, depth, seed):
         assert got["accept_len"].max() >= 2
 
 
-def test_tree_accept_workspace_reuse_and_error_paths(gpu_lib):
-    cfg = synth.config(6, bs=6, block=8, tree_depth=4, vocab=300, logit_sigma=2.0)
+@pytest.mark.parametrize("N", [8, 150])
+def test_tree_accept_workspace_reuse_and_error_paths(gpu_lib, N):
+    """Invalid token ids, a parent that is not an earlier node and rows
+    without mass, flagged and resolved as the reference does, in the
+    one-chunk walk (8 nodes) and the chunked one (150 nodes)."""
+    cfg = synth.config(6, bs=6, block=N, tree_depth=4 if N == 8 else 30, vocab=300,
+                       logit_sigma=2.0)
     print_case("spec_accept_tree error paths", cfg)
     par, _ = synth.make_trees(cfg, 5)
     ti = synth.make_tree_accept_inputs(cfg, 5, par)
     ti.token[1, np.flatnonzero(ti.parent[1] == 0)[0]] = cfg.vocab + 3    # invalid token id
-    ti.parent[2, 5] = 7                                                  # parent not earlier
+    ti.parent[2, 5] = 7 if N == 8 else 140                               # parent not earlier
     ti.p[3] = 0.0                                                        # rows without mass
     seq = np.arange(cfg.bs, dtype=np.int32) * 10
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
