@@ -177,6 +177,22 @@ def test_tree_sampler_shape_accept(gpu_lib, name, over, seed):
     assert got["accept_len"].max() >= 1
 
 
+def test_tree_sampler_workload_full_size(gpu_lib):
+    """The Tree sampler's workload at its full size, in the bench's launch
+    configuration: 8 requests, 481-node beam trees over the full vocabulary
+    (151936), target rows N(0, 6^2)."""
+    cfg = synth.config(10)
+    print_case("spec_accept_tree full Tree sampler workload", cfg.bs, cfg.block, cfg.vocab)
+    par, _ = synth.make_trees(cfg, 0)
+    ti = synth.make_tree_accept_inputs(cfg, 0, par)
+    seq = np.full(cfg.bs, 1024, np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = run_tree_accept(ti, seq, err=err)
+    assert int(err.item()) == 0
+    compare(ti, seq, got)
+    print(f"accept lengths {got['accept_len'].tolist()}", flush=True)
+
+
 @pytest.mark.parametrize("N", [65, 200, 512])
 def test_wide_chain_tree_matches_the_reference(gpu_lib, N):
     """Chains of up to 512 nodes (walks across every 64-node chunk) with
