@@ -1000,7 +1000,15 @@ __device__ __forceinline__ int block_exclusive_scan_int(int x, int* s_tmp, int* 
   return base + inc - x;
 }
 
-// s_pre[b] = pairs of all units of requests before b (b = 0 .. bs); returns
+// The balanced schedule deals out weighted pairs: unit (b, kvh) weighs its
+// stage pairs np plus a.piece_cost leading pairs that stand for the fixed
+// cost of a piece and hold no stages. A range that covers only some of a
+// unit's leading pairs takes none of its stages.
+__device__ __forceinline__ int unit_weight(const AttnArgs& a, int L) {
+  return unit_pairs(a, L) + a.piece_cost;
+}
+
+// s_pre[b] = weight of all units of requests before b (b = 0 .. bs); returns
 // the total. Thread tid covers a contiguous run of requests. With s_len, the
 // clamped lengths are kept there too.
 __device__ int balanced_prefix(const AttnArgs& a, int* s_pre, int* s_tmp, bool flag,
@@ -1009,21 +1017,21 @@ __device__ int balanced_prefix(const AttnArgs& a, int* s_pre, int* s_tmp, bool f
   const int per = (a.bs + nthr - 1) / nthr;
   const int b0 = min(a.bs, tid * per), b1 = min(a.bs, b0 + per);
   int sum = 0;
-  for (int b = b0; b < b1; ++b) sum += a.Hkv * unit_pairs(a, clamped_len(a, b, flag));
+  for (int b = b0; b < b1; ++b) sum += a.Hkv * unit_weight(a, clamped_len(a, b, flag));
   int total;
   int run = block_exclusive_scan_int(sum, s_tmp, &total);
   for (int b = b0; b < b1; ++b) {
     s_pre[b] = run;
     const int L = clamped_len(a, b, false);
     if (s_len) s_len[b] = L;
-    run += a.Hkv * unit_pairs(a, L);
+    run += a.Hkv * unit_weight(a, L);
   }
   if (tid == 0) s_pre[a.bs] = total;
   __syncthreads();
   return total;
 }
 
-// Request holding global pair x: the largest b with s_pre[b] <= x.
+// Request holding weighted pair x: the largest b with s_pre[b] <= x.
 __device__ __forceinline__ int request_of(const int* s_pre, int bs, int x) {
   int lo = 0, hi = bs - 1;
   while (lo < hi) {
@@ -1054,14 +1062,19 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   const int total = balanced_prefix(a, s_pre, s_tmp, blockIdx.x == 0, s_len);
   const int start = range_start(total, w, T_), end = range_start(total, w + 1, T_);
   if (start >= end) return;
+  const int X = a.piece_cost;
   int b = request_of(s_pre, a.bs, start);
   int L = s_len[b];
   int np = unit_pairs(a, L);
-  int kvh = (start - s_pre[b]) / np;
-  int off = start - s_pre[b] - kvh * np;  // first pair inside the unit
-  // stages [x, y) of the piece that starts at global pair cur
-  auto stage_range = [&](int cur) {
-    return int2{2 * off, min((L + a.B + kStep - 1) / kStep, 2 * (off + min(np - off, end - cur)))};
+  int kvh = (start - s_pre[b]) / (np + X);
+  int ustart = s_pre[b] + kvh * (np + X);  // weighted start of unit (b, kvh)
+  // the unit's stage pairs [off, lim) inside this workgroup's range
+  int off = max(0, start - ustart - X);
+  int lim = max(0, min(np + X, end - ustart) - X);
+  if (lim <= off) return;  // the range holds only leading pairs of one unit
+  // stages [x, y) of the piece
+  auto stage_range = [&]() {
+    return int2{2 * off, min((L + a.B + kStep - 1) / kStep, 2 * lim)};
   };
   // the page offsets of the first window of a piece (stages r.x ..) from
   // its page ids pg (thread tid: stage r.x + tid)
@@ -1072,31 +1085,34 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
   WaveState<T, D, MT> ws;
   load_q<T, D, MT>(ws, a, b, kvh, row0, c.rs, c.n, c.grp);
   int nc = causal_rows(a, b);
-  int2 range = stage_range(start);
+  int2 range = stage_range();
   stage_first(range, table_pair(a, a.page_table + (size_t)b * a.max_pages, range.x + c.tid));
   // TREE blocks of more than 64 nodes: the workgroup's row group is fixed,
   // so its mask words change only with the request (restaged with the next
   // piece's page offsets, after the barrier that ends their last reads)
   const WideMask wm = WIDE ? wide_mask(a, s_tm, row0) : WideMask{s_tm, 0, 0, 1};
   if constexpr (WIDE) stage_wide_mask(a, s_tm, wm, b, c.tid);
-  for (int cur = start; cur < end;) {
-    const int seg = min(np - off, end - cur);
-    const bool whole = off == 0 && seg == np;
-    const int part = whole ? -1 : (cur == start ? 2 * w : 2 * w + 1) * a.RG + rg;
+  for (bool first = true, next = true; next; first = false) {
+    const bool whole = off == 0 && lim == np;
+    const int part = whole ? -1 : (first ? 2 * w : 2 * w + 1) * a.RG + rg;
     stream_stages<T, D, MT, true, WIDE>(ws, a, c, s_ring, s_pgoff, b, kvh, row0, L, nc, range.x,
                                         range.y, int2{0, 0}, wm);
     const int fb = b, fkvh = kvh;
-    cur += seg;
-    off += seg;
-    if (off == np) {  // next unit
-      off = 0;
+    // the next unit, if the range reaches past its leading pairs (the range
+    // ends at or before the total, so the next unit exists when it starts
+    // inside the range)
+    next = false;
+    if (lim == np && ustart + np + X < end) {
+      ustart += np + X;
       if (++kvh == a.Hkv) {
         kvh = 0;
-        if (++b < a.bs) {
-          L = s_len[b];
-          np = unit_pairs(a, L);
-        }
+        ++b;
+        L = s_len[b];
+        np = unit_pairs(a, L);
       }
+      off = 0;
+      lim = max(0, min(np + X, end - ustart) - X);
+      next = lim > 0;
     }
     // The next piece's page ids, Q fragments and causal-row count are
     // requested before this piece's rows are merged and stored, and its
@@ -1104,10 +1120,9 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_balanced_kernel(
     // store is issued: the next piece then starts its DMAs at once, their
     // latency overlapping that of the stores (the Q registers are free once
     // the stages are streamed).
-    const bool next = cur < end;
     int2 pg{0, 0};
     if (next) {
-      range = stage_range(cur);
+      range = stage_range();
       pg = table_pair(a, a.page_table + (size_t)b * a.max_pages, range.x + c.tid);
       load_q<T, D, MT>(ws, a, b, kvh, row0, c.rs, c.n, c.grp, false);
       nc = causal_rows(a, b);
@@ -1164,9 +1179,10 @@ __device__ __forceinline__ void merge_pieces(const AttnArgs& a, int n, F prow, i
 }
 
 // Merge of the units cut by range boundaries. Boundary k (k = 1 .. T - 1,
-// between teams) merges the unit containing pair start(k) if that unit began
-// inside team k - 1's range (so each cut unit is merged once); each
-// boundary's rows are spread over RG x kCombineRowGroups blocks.
+// between teams) merges the unit containing weighted pair start(k) if the
+// boundary splits the unit's stage pairs and no earlier boundary does (so
+// each cut unit is merged once); each boundary's rows are spread over RG x
+// kCombineRowGroups blocks.
 constexpr int kCombineRowGroups = 4;
 constexpr int kCombineMaxPieces = 256;  // a unit is shared by at most G workgroups
 
@@ -1182,10 +1198,11 @@ __global__ __launch_bounds__(256) void block_attn_boundary_combine_kernel(AttnAr
   const int sk = range_start(total, k, G), sk1 = range_start(total, k - 1, G);
   if (sk >= total || sk1 >= sk) return;
   const int b = request_of(s_pre, a.bs, sk);
-  const int np = unit_pairs(a, clamped_len(a, b, false));
-  const int kvh = (sk - s_pre[b]) / np;
-  const int u0 = s_pre[b] + kvh * np, u1 = u0 + np;  // the unit's pairs [u0, u1)
-  if (u0 >= sk || u0 < sk1) return;  // not cut here, or cut at an earlier boundary
+  const int nw = unit_weight(a, clamped_len(a, b, false));
+  const int kvh = (sk - s_pre[b]) / nw;
+  const int u0 = s_pre[b] + kvh * nw, u1 = u0 + nw;  // the unit's weighted pairs [u0, u1)
+  const int s0 = u0 + a.piece_cost;                   // its first stage pair
+  if (sk <= s0 || sk1 > s0) return;  // no stage pair before the cut, or cut at an earlier boundary
   // pieces: workgroups k - 1 .. wb with a non-empty range; the first one's
   // piece sits in its second slot unless the unit is that workgroup's first
   if (threadIdx.x == 0) {

@@ -62,6 +62,12 @@ struct AttnPlan {
 // workgroup per CU when the batch has few units, every split keeping at least
 // 8 stages of 32 keys.
 constexpr long long kBalancedMinStages = 32768;
+// A workgroup pays a fixed cost per piece it streams (the Q and page-table
+// loads, the first DMA round trip, the merge of the two sets and the output
+// stores: about 4 stage pairs of streaming). The balanced schedule weighs
+// each unit as its stage pairs plus this many, so ranges that hold many
+// short units get fewer pairs.
+constexpr int kPieceCostPairs = 4;
 
 // Query rows per KV head beyond kMaxUnitRows are cut into row groups of at
 // most kMaxUnitRows (equal sizes, rounded up to the 16-row MFMA tile); each
@@ -284,6 +290,7 @@ int attn_common(int mode, int n_causal, const int32_t* n_causal_per_req, const u
   a.steps_per_split = plan.steps_per_split;
   a.balanced = plan.balanced ? 1 : 0;
   a.G = plan.grid;
+  a.piece_cost = kPieceCostPairs;
   const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt((float)D) : sm_scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(launch_block_attn(a, dtype == SPEC_BF16, D, plan.grid,

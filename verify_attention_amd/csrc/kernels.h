@@ -34,6 +34,7 @@ struct AttnArgs {
   int tree_per_req;
   int splits, steps_per_split;
   int balanced, G;   // balanced schedule: G persistent workgroups
+  int piece_cost;    // balanced schedule: a unit's weight is its stage pairs + piece_cost
   float scale_log2;  // sm_scale * log2(e)
 };
 
