@@ -955,13 +955,15 @@ __global__ __launch_bounds__(kWave * kWaves, 1) void block_attn_kernel(AttnArgs 
 
 // ------------------------------------------------------- balanced schedule
 // For batches whose lengths may differ widely, a fixed grid of G workgroups
-// shares the work evenly: the stage pairs of all units, taken in unit order
-// (unit = b * Hkv + kvh, each unit ceil(ceil((L_b + B) / 32) / 2) pairs), are
-// cut into G equal contiguous ranges, workgroup w taking pairs
-// [floor(TP * w / G), floor(TP * (w + 1) / G)). A unit that a range boundary
-// cuts is written as partial states by the workgroups that share it -- into
-// slot 2w when it is workgroup w's first unit, else 2w + 1 -- and merged by
-// the boundary-combine kernel; every other unit is written normalised.
+// shares the work evenly: the weighted pairs of all units, taken in unit
+// order (unit = b * Hkv + kvh; each unit ceil(ceil((L_b + B) / 32) / 2) stage
+// pairs behind piece_cost leading pairs that stand for a piece's fixed cost),
+// are cut into G equal contiguous ranges, workgroup w taking weighted pairs
+// [floor(TP * w / G), floor(TP * (w + 1) / G)). A unit whose stage pairs a
+// range boundary cuts is written as partial states by the workgroups that
+// share it -- into slot 2w when it is workgroup w's first unit, else 2w + 1 --
+// and merged by the boundary-combine kernel; every other unit is written
+// normalised.
 //
 // With row groups the G workgroups form T = G / RG teams of RG: the ranges
 // are cut over the teams (a unit here is a (request, KV head) pair), and each

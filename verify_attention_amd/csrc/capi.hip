@@ -55,8 +55,9 @@ struct AttnPlan {
 
 // Two schedules. Large batches (units x stages of the longest request at
 // least kBalancedMinStages) use the balanced schedule: one workgroup per CU,
-// each taking an equal share of all units' stage pairs, so that lengths that
-// differ widely do not leave CUs idle; units cut by a share boundary leave
+// each taking an equal share of all units' weight (stage pairs plus a fixed
+// per-piece cost), so that lengths that differ widely do not leave CUs idle;
+// units cut by a share boundary leave
 // partial states in the workspace (two slots per workgroup). Smaller batches
 // use one workgroup per (request, KV head, split): enough splits for one
 // workgroup per CU when the batch has few units, every split keeping at least
