@@ -1,10 +1,13 @@
-"""One verify round captured in a HIP graph through the C ABI. The calls
-allocate nothing, clear nothing and never synchronise with the host, so the
-round — the verify pass's block preparation, block attention and the accept
-that also prepares the next round's block — can be recorded once and replayed.
-Every replay is checked against the same calls run eagerly on the same
-inputs, bit for bit, with eager work (new uniforms, new draft tokens) between
-the replays; the eager results are also checked against the CPU reference."""
+"""Rounds captured in HIP graphs through the C ABI. The calls allocate
+nothing, clear nothing and never synchronise with the host, so a round can be
+recorded once and replayed: the linear verify round (the verify pass's block
+preparation, block attention and the accept that also prepares the next
+round's block) and the tree round (the tree block's preparation, attention
+under the tree masks, and the tree accept that commits its path into the K/V
+pools). Every replay is checked against the same calls run eagerly on the same
+inputs, bit for bit, with eager work (new uniforms, new draft tokens, restored
+pools) between the replays; the eager results are also checked against the
+CPU reference."""
 import numpy as np
 import pytest
 import torch
@@ -106,3 +109,102 @@ def test_verify_round_replays_as_a_hip_graph(gpu_lib):
         assert np.array_equal(want["accept_len"].cpu().numpy()[keep], ra["accept_len"][keep])
         assert np.array_equal(want["bonus"].cpu().numpy()[keep], ra["bonus"][keep])
         print(f"replay {rep}: accept lengths {want['accept_len'].tolist()}", flush=True)
+
+
+def _tree_round(x, ti, case, tmask, dev_in, outs, pools, stream=None):
+    """A tree round's three calls: the tree block's ids, positions and slots,
+    the attention under the tree masks, the tree accept with the commit of its
+    path into the pools (which it changes in place)."""
+    cfg = x.cfg
+    max_kv = int(x.seq_lens.max()) + cfg.block
+    e1, _ = va.prepare_tree_call(dev_in["vid"], case.seq, case.table, cfg.page, dev_in["par"],
+                                 MASK, x.num_pages, dev_in["tok"], out=outs["prep"],
+                                 err=outs["err"], stream=stream)
+    e2, _ = va.block_attn_tree_call(tmask, case.q, pools[0], pools[1], case.table, case.seq,
+                                    max_kv, out=outs["o"], ws=outs["ws_attn"], err=outs["err"],
+                                    stream=stream)
+    e3, _ = va.accept_tree_commit_call(dev_in["par"], dev_in["tok"], dev_in["p"], dev_in["u"],
+                                       case.seq, pools[0], pools[1], case.table, out=outs["acc"],
+                                       ws=outs["ws_acc"], err=outs["err"], stream=stream)
+    return (e1, e2, e3)
+
+
+def _tree_outputs(x, case):
+    cfg = x.cfg
+    bs, N = cfg.bs, cfg.block
+    max_kv = int(x.seq_lens.max()) + N
+    i32 = dict(dtype=torch.int32, device="cuda")
+    acc = dict(accept_len=torch.empty(bs, **i32), commit_len=torch.empty(bs, **i32),
+               bonus=torch.empty(bs, **i32), out_tokens=torch.empty((bs, N), **i32),
+               path_nodes=torch.empty((bs, N), **i32), new_seq_lens=torch.empty(bs, **i32),
+               freed=torch.empty((bs, N), **i32))
+    return dict(prep=tuple(torch.empty((bs, N), **i32) for _ in range(3)),
+                o=torch.empty_like(case.q),
+                ws_attn=va.workspace(max(1, va.attn_workspace_bytes(bs, N, cfg.hq, cfg.hkv, cfg.d,
+                                                                    max_kv))),
+                ws_acc=va.workspace(va.accept_tree_workspace_bytes(bs, N, cfg.vocab)),
+                acc=acc, err=torch.zeros(1, **i32))
+
+
+def test_tree_round_replays_as_a_hip_graph(gpu_lib):
+    """The tree round, whose accept also commits the accepted path into the
+    K/V pools, captured once and replayed: before every replay the pools are
+    restored and the uniforms redrawn (eager work), and each replay's outputs
+    and pools must equal the same calls run eagerly on their own copies."""
+    cfg = synth.config(6, bs=8, vocab=4000)
+    print_case("tree round as a HIP graph", cfg.bs, cfg.block, cfg.vocab)
+    x = synth.make_attn_inputs(cfg, seed=8)
+    case = AttnCase(x)
+    par, masks = synth.make_trees(cfg, 8)
+    ti = synth.make_tree_accept_inputs(cfg, 8, par)
+    tmask = torch.from_numpy(np.ascontiguousarray(masks).view(np.int64)).to("cuda")
+    verified = np.random.default_rng(80).integers(0, cfg.vocab, size=cfg.bs).astype(np.int32)
+    dev_in = dict(vid=to_dev(verified), par=to_dev(ti.parent), tok=to_dev(ti.token),
+                  p=to_dev(ti.p), u=to_dev(ti.u))
+    k0, v0 = to_dev(x.k_pool), to_dev(x.v_pool)       # pristine pools
+    g_pools = (k0.clone(), v0.clone())
+    e_pools = (k0.clone(), v0.clone())
+    g_out, e_out = _tree_outputs(x, case), _tree_outputs(x, case)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # one eager pass before the capture
+        for e in _tree_round(x, ti, case, tmask, dev_in, g_out, g_pools):
+            e()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for e in _tree_round(x, ti, case, tmask, dev_in, g_out, g_pools):
+            e()
+    eager = _tree_round(x, ti, case, tmask, dev_in, e_out, e_pools)
+    rng = np.random.default_rng(81)
+    for rep in range(3):
+        u = rng.random(ti.u.shape, dtype=np.float32)
+        dev_in["u"].copy_(torch.from_numpy(u))
+        for pl in (g_pools, e_pools):
+            pl[0].copy_(k0)
+            pl[1].copy_(v0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for e in eager:
+            e()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(g_out["prep"][i], e_out["prep"][i]), (rep, "prep", i)
+        assert torch.equal(g_out["o"], e_out["o"]), (rep, "o")
+        for k in e_out["acc"]:
+            assert torch.equal(g_out["acc"][k], e_out["acc"][k]), (rep, k)
+        for a, b in zip(g_pools, e_pools):
+            assert torch.equal(a, b), (rep, "pools")
+        assert int(g_out["err"].item()) == 0 and int(e_out["err"].item()) == 0
+        # the eager accept against the CPU reference
+        depth = e_out["acc"]["accept_len"].cpu().numpy()
+        bonus = e_out["acc"]["bonus"].cpu().numpy()
+        for b in range(cfg.bs):
+            ra = oracle.tree_accept_request(ti.parent[b], ti.token[b], ti.p[b], u[b],
+                                            x.seq_lens[b])
+            if ra.get("tie_sample") or ra.get("tie_accept"):
+                continue
+            assert depth[b] == ra["accept_len"] and bonus[b] == ra["bonus"], (rep, b)
+        print(f"replay {rep}: tree depths {depth.tolist()}", flush=True)
