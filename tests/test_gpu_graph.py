@@ -2,9 +2,10 @@
 nothing, clear nothing and never synchronise with the host, so a round can be
 recorded once and replayed: the linear verify round (the verify pass's block
 preparation, block attention and the accept that also prepares the next
-round's block) and the tree round (the tree block's preparation, attention
+round's block), the tree round (the tree block's preparation, attention
 under the tree masks, and the tree accept that commits its path into the K/V
-pools). Every replay is checked against the same calls run eagerly on the same
+pools) and the quadratic round (attention under the layout's masks, then the
+spine accept with the hand-off, the spine commit and the next block). Every replay is checked against the same calls run eagerly on the same
 inputs, bit for bit, with eager work (new uniforms, new draft tokens, restored
 pools) between the replays; the eager results are also checked against the
 CPU reference."""
@@ -208,3 +209,88 @@ def test_tree_round_replays_as_a_hip_graph(gpu_lib):
                 continue
             assert depth[b] == ra["accept_len"] and bonus[b] == ra["bonus"], (rep, b)
         print(f"replay {rep}: tree depths {depth.tolist()}", flush=True)
+
+
+def test_quadratic_round_replays_as_a_hip_graph(gpu_lib):
+    """The quadratic round -- attention under the layout's masks, then the
+    spine accept that also hands over the next drafts, commits the spine's
+    K/V and prepares the next block -- captured once and replayed with pools
+    restored and uniforms redrawn before every replay: outputs and pools equal
+    the same calls run eagerly, and the accept equals the CPU reference."""
+    cfg = synth.config(8, bs=8, vocab=3000)
+    k, n, V = cfg.quad_k, cfg.block, cfg.vocab
+    print_case("quadratic round as a HIP graph", cfg.bs, k, V)
+    x = synth.make_attn_inputs(cfg, seed=10)
+    case = AttnCase(x)
+    _, masks = synth.quadratic_layout(k)
+    tmask = torch.from_numpy(np.ascontiguousarray(masks).view(np.int64)).to("cuda")
+    acc = synth.make_accept_inputs(cfg, seed=10)
+    lg = np.random.default_rng(10).standard_normal((cfg.bs, n, V), dtype=np.float32) * 3
+    logits = to_dev(synth.bf16_bits(lg))
+    dev_in = dict(p=to_dev(acc.p), q=to_dev(acc.q), d=to_dev(acc.draft), u=to_dev(acc.u))
+    max_kv = int(x.seq_lens.max()) + n
+    k0, v0 = to_dev(x.k_pool), to_dev(x.v_pool)       # pristine pools
+
+    def outputs(pools):
+        o = torch.empty_like(case.q)
+        ws_attn = va.workspace(max(1, va.attn_workspace_bytes(cfg.bs, n, cfg.hq, cfg.hkv, cfg.d,
+                                                              max_kv)))
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        # marshalled once outside any capture, for its outputs and workspace
+        _, acc_out = va.accept_quadratic_call(dev_in["p"], dev_in["q"], dev_in["d"], dev_in["u"],
+                                              case.seq, logits, pools[0], pools[1], case.table,
+                                              MASK, prepare_next=True, err=err)
+        ws_q = va.workspace(va.accept_quadratic_workspace_bytes(cfg.bs, k, V))
+        return dict(o=o, ws_attn=ws_attn, err=err, acc=acc_out, ws_q=ws_q)
+
+    def round_calls(outs, pools):
+        e1, _ = va.block_attn_tree_call(tmask, case.q, pools[0], pools[1], case.table, case.seq,
+                                        max_kv, out=outs["o"], ws=outs["ws_attn"],
+                                        err=outs["err"])
+        e2, _ = va.accept_quadratic_call(dev_in["p"], dev_in["q"], dev_in["d"], dev_in["u"],
+                                         case.seq, logits, pools[0], pools[1], case.table, MASK,
+                                         prepare_next=True, out=outs["acc"], ws=outs["ws_q"],
+                                         err=outs["err"])
+        return (e1, e2)
+
+    g_pools, e_pools = (k0.clone(), v0.clone()), (k0.clone(), v0.clone())
+    g_out, e_out = outputs(g_pools), outputs(e_pools)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # one eager pass before the capture
+        for e in round_calls(g_out, g_pools):
+            e()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for e in round_calls(g_out, g_pools):
+            e()
+    eager = round_calls(e_out, e_pools)
+    rng = np.random.default_rng(101)
+    for rep in range(3):
+        u = rng.random(acc.u.shape, dtype=np.float32)
+        dev_in["u"].copy_(torch.from_numpy(u))
+        for pl in (g_pools, e_pools):
+            pl[0].copy_(k0)
+            pl[1].copy_(v0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for e in eager:
+            e()
+        torch.cuda.synchronize()
+        assert torch.equal(g_out["o"], e_out["o"]), (rep, "o")
+        for key in e_out["acc"]:
+            assert torch.equal(g_out["acc"][key], e_out["acc"][key]), (rep, key)
+        for a, b in zip(g_pools, e_pools):
+            assert torch.equal(a, b), (rep, "pools")
+        assert int(g_out["err"].item()) == 0 and int(e_out["err"].item()) == 0
+        ra = oracle.accept_batch(acc.p, acc.q, acc.draft, u, x.seq_lens)
+        keep = ~ra["tie_sample"]
+        check_tie_share(int((~keep).sum()), cfg.bs, "graph quadratic accept")
+        got_len = e_out["acc"]["accept_len"].cpu().numpy()
+        got_bonus = e_out["acc"]["bonus"].cpu().numpy()
+        assert np.array_equal(got_len[keep], ra["accept_len"][keep])
+        assert np.array_equal(got_bonus[keep], ra["bonus"][keep])
+        print(f"replay {rep}: spine accept lengths {got_len.tolist()}", flush=True)
