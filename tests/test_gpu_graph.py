@@ -4,8 +4,11 @@ recorded once and replayed: the linear verify round (the verify pass's block
 preparation, block attention and the accept that also prepares the next
 round's block), the tree round (the tree block's preparation, attention
 under the tree masks, and the tree accept that commits its path into the K/V
-pools) and the quadratic round (attention under the layout's masks, then the
-spine accept with the hand-off, the spine commit and the next block). Every replay is checked against the same calls run eagerly on the same
+pools), the quadratic round (attention under the layout's masks, then the
+spine accept with the hand-off, the spine commit and the next block), the
+draft pass round (MASK block, bidirectional attention, greedy draft argmax)
+and the logits verify round (accept over logits with temperature, top-k and
+top-p). Every replay is checked against the same calls run eagerly on the same
 inputs, bit for bit, with eager work (new uniforms, new draft tokens, restored
 pools) between the replays; the eager results are also checked against the
 CPU reference."""
@@ -294,3 +297,140 @@ def test_quadratic_round_replays_as_a_hip_graph(gpu_lib):
         assert np.array_equal(got_len[keep], ra["accept_len"][keep])
         assert np.array_equal(got_bonus[keep], ra["bonus"][keep])
         print(f"replay {rep}: spine accept lengths {got_len.tolist()}", flush=True)
+
+
+def _capture_and_compare(build, g_outs, e_outs, between, compare, reps=3):
+    """Captures build(g_outs) (closures marshalled on the capture stream),
+    then replays it `reps` times; before each replay between(rep) does eager
+    work, after it the eager closures build(e_outs) run and compare(rep)
+    checks both."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # one eager pass before the capture
+        for e in build(g_outs):
+            e()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for e in build(g_outs):
+            e()
+    eager = build(e_outs)
+    for rep in range(reps):
+        between(rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for e in eager:
+            e()
+        torch.cuda.synchronize()
+        compare(rep)
+
+
+def test_draft_round_replays_as_a_hip_graph(gpu_lib):
+    """The draft pass round: its block (MASK fill), bidirectional block
+    attention and the greedy draft argmax, replayed with new logits and
+    verified ids written between replays; the drafts equal the lowest-index
+    argmax of the bf16 rows."""
+    cfg = synth.config(3, bs=8, argmax_vocab=20000)
+    B = cfg.block
+    print_case("draft round as a HIP graph", cfg.bs, B, cfg.argmax_vocab)
+    x = synth.make_attn_inputs(cfg, seed=11)
+    case = AttnCase(x)
+    max_kv = int(x.seq_lens.max()) + B
+    logits = to_dev(synth.make_argmax_logits(cfg, 11))
+    vid = to_dev(np.zeros(cfg.bs, np.int32))
+    i32 = dict(dtype=torch.int32, device="cuda")
+
+    def outputs():
+        return dict(prep=tuple(torch.empty((cfg.bs, B), **i32) for _ in range(3)),
+                    o=torch.empty_like(case.q), tok=torch.empty(logits.shape[0], **i32),
+                    ws=va.workspace(max(1, va.attn_workspace_bytes(cfg.bs, B, cfg.hq, cfg.hkv,
+                                                                   cfg.d, max_kv))),
+                    err=torch.zeros(1, **i32))
+
+    def build(o):
+        e1, _ = va.prepare_block_call(vid, case.seq, case.table, cfg.page, B, MASK, x.num_pages,
+                                      None, out=o["prep"], err=o["err"])
+        e2, _ = va.block_attn_call(synth.BIDIR, case.q, case.k, case.v, case.table, case.seq,
+                                   max_kv, out=o["o"], ws=o["ws"], err=o["err"])
+        e3, _ = va.draft_argmax_call(logits, out=o["tok"])
+        return (e1, e2, e3)
+
+    g, e = outputs(), outputs()
+    rng = np.random.default_rng(111)
+    state = {}
+
+    def between(rep):
+        bits = synth.bf16_bits(rng.standard_normal(tuple(logits.shape), dtype=np.float32) * 3)
+        logits.copy_(to_dev(bits))
+        vid.copy_(torch.from_numpy(rng.integers(0, 20000, cfg.bs).astype(np.int32)))
+        state["bits"] = bits
+
+    def compare(rep):
+        for i in range(3):
+            assert torch.equal(g["prep"][i], e["prep"][i]), (rep, "prep", i)
+        assert torch.equal(g["o"], e["o"]) and torch.equal(g["tok"], e["tok"]), rep
+        assert int(g["err"].item()) == 0 and int(e["err"].item()) == 0
+        vals = synth.bf16_to_f32(state["bits"])
+        want = np.array([oracle.argmax_lowest(r) for r in vals], np.int32)
+        assert np.array_equal(e["tok"].cpu().numpy(), want), rep
+        print(f"replay {rep}: drafts {e['tok'][:6].tolist()}...", flush=True)
+
+    _capture_and_compare(build, g, e, between, compare)
+
+
+def test_logits_round_replays_as_a_hip_graph(gpu_lib):
+    """The logits verify round: the verify block, causal block attention and
+    the accept over logits (temperature, top-k, top-p), replayed with new
+    uniforms between replays; each replay equals the eager calls bit for
+    bit."""
+    cfg = synth.config(7, bs=6, vocab=20011)
+    B, K = cfg.block, cfg.k_spec
+    T, top_k, top_p = cfg.sampling
+    print_case("logits round as a HIP graph", cfg.bs, B, cfg.vocab)
+    x = synth.make_attn_inputs(cfg, seed=12)
+    case = AttnCase(x)
+    max_kv = int(x.seq_lens.max()) + B
+    li = synth.make_logits_accept_inputs(cfg, seed=12)
+    dev_in = dict(t=to_dev(li.target), dl=to_dev(li.draft_logits), d=to_dev(li.draft),
+                  u=to_dev(li.u), vid=to_dev(np.zeros(cfg.bs, np.int32)))
+    i32 = dict(dtype=torch.int32, device="cuda")
+
+    def outputs():
+        err = torch.zeros(1, **i32)
+        _, acc = va.accept_logits_call(dev_in["t"], dev_in["dl"], dev_in["d"], dev_in["u"],
+                                       case.seq, T, top_k, top_p, err=err)
+        return dict(prep=tuple(torch.empty((cfg.bs, B), **i32) for _ in range(3)),
+                    o=torch.empty_like(case.q), acc=acc, err=err,
+                    ws=va.workspace(max(1, va.attn_workspace_bytes(cfg.bs, B, cfg.hq, cfg.hkv,
+                                                                   cfg.d, max_kv))),
+                    ws_acc=va.workspace(va.accept_logits_workspace_bytes(cfg.bs, K, cfg.vocab,
+                                                                         top_k)))
+
+    def build(o):
+        e1, _ = va.prepare_block_call(dev_in["vid"], case.seq, case.table, cfg.page, B, MASK,
+                                      x.num_pages, dev_in["d"], out=o["prep"], err=o["err"])
+        e2, _ = va.block_attn_call(synth.CAUSAL, case.q, case.k, case.v, case.table, case.seq,
+                                   max_kv, out=o["o"], ws=o["ws"], err=o["err"])
+        e3, _ = va.accept_logits_call(dev_in["t"], dev_in["dl"], dev_in["d"], dev_in["u"],
+                                      case.seq, T, top_k, top_p, out=o["acc"], ws=o["ws_acc"],
+                                      err=o["err"])
+        return (e1, e2, e3)
+
+    g, e = outputs(), outputs()
+    rng = np.random.default_rng(121)
+
+    def between(rep):
+        dev_in["u"].copy_(torch.from_numpy(rng.random(li.u.shape, dtype=np.float32)))
+
+    def compare(rep):
+        for i in range(3):
+            assert torch.equal(g["prep"][i], e["prep"][i]), (rep, "prep", i)
+        assert torch.equal(g["o"], e["o"]), rep
+        for key in e["acc"]:
+            assert torch.equal(g["acc"][key], e["acc"][key]), (rep, key)
+        assert int(g["err"].item()) == 0 and int(e["err"].item()) == 0
+        print(f"replay {rep}: accept lengths {e['acc']['accept_len'].tolist()}", flush=True)
+
+    _capture_and_compare(build, g, e, between, compare)
