@@ -72,3 +72,24 @@ def test_traffic_table_matches_its_sources():
             name, _, call = key.partition("/")
             got = bench.measured_traffic(name, tj["kernel_src"], call or "block_attn")
             assert got == int(w["traffic_bytes"])
+
+
+def test_cpu_leg_sample_inputs_keep_each_requests_attention():
+    """The CPU leg runs the reference on one request at a time over a pool
+    holding only that request's pages (page table renumbered): the result
+    must equal the reference on the whole batch for that request, bit for
+    bit, whatever the page shuffle."""
+    import oracle
+    cfg = synth.config(4, bs=5, hq=4, hkv=2, d=16, ctx_lo=20, ctx_hi=90)
+    x = synth.make_attn_inputs(cfg, seed=3)
+    mode = cfg.modes[-1]
+    full, _ = oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                      x.page_table, x.seq_lens, mode, cfg.n_causal)
+    for b in (0, 3, 4):
+        one = bench._sample_inputs(x, [b])
+        assert one.num_pages < x.num_pages
+        assert np.all(one.page_table[0][one.page_table[0] >= 0] < one.num_pages)
+        got, _ = oracle.block_attn_dense(one.as_f64("q"), one.as_f64("k_pool"),
+                                         one.as_f64("v_pool"), one.page_table, one.seq_lens,
+                                         mode, cfg.n_causal)
+        assert np.array_equal(got[0], full[b]), b
