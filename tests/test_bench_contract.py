@@ -93,3 +93,32 @@ def test_cpu_leg_sample_inputs_keep_each_requests_attention():
                                          one.as_f64("v_pool"), one.page_table, one.seq_lens,
                                          mode, cfg.n_causal)
         assert np.array_equal(got[0], full[b]), b
+
+
+def test_cpu_leg_counts_a_planted_mismatch():
+    """The bench line's parity sample is not vacuous: GPU outputs equal to
+    the reference give no mismatch; one request's bonus or attention row
+    changed gives exactly one."""
+    import oracle
+    cfg = synth.config(1, bs=3)
+    x = synth.make_attn_inputs(cfg, seed=4)
+    acc = synth.make_accept_inputs(cfg, seed=4)
+    ro, _ = oracle.block_attn_dense(x.as_f64("q"), x.as_f64("k_pool"), x.as_f64("v_pool"),
+                                    x.page_table, x.seq_lens, cfg.modes[-1], cfg.n_causal)
+    ra = oracle.accept_batch(acc.p, acc.q, acc.draft, acc.u, x.seq_lens)
+
+    def gpu(bad_bonus=None, bad_attn=None):
+        def o(b):
+            return ro[b] + (0.5 if b == bad_attn else 0.0)
+
+        def accept(b):
+            return dict(accept_len=ra["accept_len"][b],
+                        bonus=ra["bonus"][b] + (1 if b == bad_bonus else 0),
+                        new_seq_lens=ra["new_seq_len"][b], out_tokens=ra["out_tokens"][b])
+        return {"o": o, "accept": accept}
+
+    for g, want in ((gpu(), 0), (gpu(bad_bonus=1), 1), (gpu(bad_attn=2), 1)):
+        r = bench.cpu_baseline(cfg, x, 60.0, g, acc=acc)
+        ps = r["parity_sample"]
+        assert ps["requests"] == cfg.bs and ps["sampling_ties"] == 0
+        assert ps["mismatched_requests"] == want, (want, ps)
